@@ -1,0 +1,104 @@
+/*
+ * orc.h -- plain CPU oracle for the polynomial activation programs of
+ * "Fast Polynomial Transcendentals for LLMs" (arXiv 2610.00049).
+ *
+ * THIS IS TEST INFRASTRUCTURE.  Only the test suite, the package smoke check
+ * and the CPU-baseline leg of the benchmark may load or call it.  The product
+ * path (the HIP library and its Python binding) never does, and this code
+ * shares nothing with it: no headers, no helpers, no tables, no generated
+ * constants.  The oracle derives every coefficient itself, by the fitting
+ * procedure the paper describes, and replays every operation of a program
+ * with an explicitly correct rounding.
+ *
+ * Everything is written for clarity, not speed: each value is decoded to an
+ * exact number, each operation is computed exactly (or with a library routine
+ * that is correctly rounded by definition, e.g. C99 fmaf), and the result is
+ * rounded once, to nearest-even, by a routine written from the definition of
+ * the binary format.
+ */
+#ifndef ORC_H
+#define ORC_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Functions (paper section 3.1 / 3.3). */
+enum { ORC_SIGMOID = 1, ORC_TANH = 2, ORC_SILU = 3, ORC_GELU = 4 };
+
+/* Rounding orders used to replay a program (paper section 3.2, steps 4-5 and
+ * the paragraph after the step list).
+ *   ORC_ORDER_F16_FMA      FP16 arithmetic, one rounding per fused multiply-add
+ *                          (packed FP16 FMA semantics);
+ *   ORC_ORDER_BF16_FMA     BF16 arithmetic, one rounding per fused multiply-add
+ *                          (the paper's packed BF16 FMA semantics);
+ *   ORC_ORDER_F32FMA_BF16  FP32 fused multiply-add rounded to FP32, then rounded
+ *                          to BF16 (how a machine without a packed BF16 FMA runs
+ *                          the same chain: two roundings per stage);
+ *   ORC_ORDER_BF16_SPLIT   BF16 arithmetic with multiply and add rounded
+ *                          separately (the paper's search emulator).          */
+enum { ORC_ORDER_F16_FMA = 1, ORC_ORDER_BF16_FMA = 2, ORC_ORDER_F32FMA_BF16 = 3,
+       ORC_ORDER_BF16_SPLIT = 4 };
+
+/* A fitted program: function, direction (deriv = 1 for a direct derivative
+ * fit), degree D, fit interval Li, runtime clamp Lc and the BF16 bit patterns
+ * of the monomial coefficients c_0..c_D in the half-domain variable t = |x|. */
+typedef struct {
+    int32_t func, deriv, degree, reserved;
+    double Li, Lc;
+    uint16_t c[8];
+} orc_prog;
+
+/* ---- binary formats (orc_fp.c) ---------------------------------------- */
+double   orc_f16_to_f64(uint16_t h);
+double   orc_bf16_to_f64(uint16_t b);
+uint16_t orc_f64_to_f16(double x);    /* round to nearest even */
+uint16_t orc_f64_to_bf16(double x);   /* round to nearest even */
+uint16_t orc_f32_to_bf16(float x);    /* round to nearest even */
+float    orc_bf16_to_f32(uint16_t b);
+uint16_t orc_fma_f16(uint16_t a, uint16_t b, uint16_t c);   /* RN(a*b+c), exact */
+uint16_t orc_fma_bf16(uint16_t a, uint16_t b, uint16_t c);  /* RN(a*b+c), exact */
+uint16_t orc_fma_f32_bf16(uint16_t a, uint16_t b, uint16_t c); /* RN16(RN32(a*b+c)) */
+float    orc_fma_f32(float a, float b, float c);            /* RN(a*b+c) */
+float    orc_add_f32(float a, float b);
+float    orc_mul_f32(float a, float b);
+
+/* ---- functions, fitting, selection (orc_fit.c) ------------------------ */
+double orc_ref(int func, int deriv, double x);        /* FP64 function value */
+double orc_residual(int func, int deriv, double t);   /* half-domain target  */
+int    orc_fit(int func, int deriv, int degree, double Li, double *coef);
+int    orc_make_prog(int func, int deriv, int degree, double Li, double Lc,
+                     orc_prog *out);
+double orc_prog_real(const orc_prog *p, double x);
+double orc_table2_metric(const orc_prog *p);
+double orc_search_objective(const orc_prog *p, int order, int *gates_ok);
+int    orc_search(int func, int deriv, int degree, double Lc_fixed, double bound,
+                  int order, orc_prog *out, double *objective, double *metric);
+
+/* ---- program replay (orc_eval.c) -------------------------------------- */
+uint16_t orc_prog_eval(const orc_prog *p, uint16_t x, int order);
+uint16_t orc_prog_bwd(const orc_prog *p, uint16_t x, uint16_t g, int order);
+void orc_act_fwd(const orc_prog *p, int order, const uint16_t *x, uint16_t *y,
+                 int64_t n);
+void orc_act_bwd(const orc_prog *p, int order, const uint16_t *x,
+                 const uint16_t *g, uint16_t *dx, int64_t n);
+void orc_swiglu_fwd(const orc_prog *sig, const uint16_t *gate, const uint16_t *up,
+                    uint16_t *h, int64_t row_begin, int64_t row_end, int64_t cols,
+                    int64_t ld_gate, int64_t ld_up, int64_t ld_h);
+void orc_swiglu_bwd(const orc_prog *sig, const uint16_t *gate, const uint16_t *up,
+                    const uint16_t *dh, uint16_t *dgate, uint16_t *dup,
+                    int64_t row_begin, int64_t row_end, int64_t cols,
+                    int64_t ld_gate, int64_t ld_up, int64_t ld_dh,
+                    int64_t ld_dgate, int64_t ld_dup);
+void orc_softcap_attn_rows(const orc_prog *tanh_prog, int poly,
+                           const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                           int32_t B, int32_t H, int32_t S, int32_t D, float cap,
+                           int32_t causal, const int64_t *rows, int64_t n_rows,
+                           double *out, double *noise);
+int orc_threads(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

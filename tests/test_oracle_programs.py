@@ -1,0 +1,225 @@
+"""Pins for the oracle's program replay, fused SwiGLU and attention.
+
+Evidence independent of the oracle's own code:
+  * the symmetry identities of the paper (Eqs. 3, 4, 9 and the odd/even forms
+    of section 3.3), which hold bit for bit for the replayed residual;
+  * a rounding-error bound around the real-arithmetic program (numpy Horner
+    on the BF16 coefficients): every replayed FP16/BF16 output lies within it;
+  * numpy / torch IEEE arithmetic for the backward product and the SwiGLU
+    combination; scipy's functions for the approximation error;
+  * a textbook FP64 softcapped attention in numpy for the attention rows.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+from scipy import special as sp
+
+GOLD = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+ALL = np.arange(65536, dtype=np.uint16)
+
+
+def _progs(orc):
+    out = {}
+    for g in json.load(open(os.path.join(GOLD, "programs.json")))["programs"]:
+        out[g["name"]] = orc.make_prog(g["func"], g["deriv"], g["degree"], g["Li"], g["Lc"])
+    return out
+
+
+@pytest.fixture(scope="module")
+def progs(orc):
+    return _progs(orc)
+
+
+def f16v(bits):
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def bf16v(bits):
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+FMT = {
+    "f16": dict(order=1, val=f16v, nan=0x7C00, quiet=0x0200, u=2.0 ** -11, tiny=2.0 ** -25),
+    "bf16": dict(order=3, val=bf16v, nan=0x7F80, quiet=0x0040, u=2.0 ** -8, tiny=2.0 ** -134),
+}
+
+
+def _finite(bits, fmt):
+    return (bits & 0x7FFF) < FMT[fmt]["nan"]
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+def test_identities_bitwise(orc, progs, fmt):
+    F = FMT[fmt]
+    pos = ALL[(ALL < 0x8000) & _finite(ALL, fmt)]
+    neg = pos | 0x8000
+    tanh_p = orc.act_fwd(progs["tanh_fwd_d4"], pos, F["order"])
+    tanh_n = orc.act_fwd(progs["tanh_fwd_d4"], neg, F["order"])
+    assert np.array_equal(tanh_n, tanh_p ^ 0x8000)           # odd: tanh~(-x) = -tanh~(x)
+    for name in ("sigmoid_bwd_d4", "tanh_bwd_d4"):              # even derivatives
+        assert np.array_equal(orc.act_fwd(progs[name], pos, F["order"]),
+                              orc.act_fwd(progs[name], neg, F["order"]))
+    # centered sigmoid: y(x) + y(-x) - 1 is only the rounding of the two 1/2 + r
+    yp = F["val"](orc.act_fwd(progs["sigmoid_fwd_d3"], pos, F["order"]))
+    yn = F["val"](orc.act_fwd(progs["sigmoid_fwd_d3"], neg, F["order"]))
+    half_ulp = lambda y: np.where(y >= 0.5, 0.5, 0.25) * F["u"] * 2  # noqa: E731
+    assert np.all(np.abs(yp + yn - 1.0) <= half_ulp(yp) / 2 + half_ulp(yn) / 2)
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+@pytest.mark.parametrize("name", ["sigmoid_fwd_d3", "tanh_fwd_d4", "silu_fwd_d3", "gelu_fwd_d5",
+                                  "sigmoid_bwd_d4", "tanh_bwd_d4"])
+def test_replay_within_rounding_bound_of_real_program(orc, progs, fmt, name):
+    """Every finite input: |replay - P(x)| <= gamma_{D+1} sum|c_j| t^j (Horner
+    with one rounding per FMA) propagated through the reconstruction, plus the
+    final rounding and underflow slack.  P(x) is evaluated here in numpy."""
+    F = FMT[fmt]
+    p = progs[name]
+    xs = ALL[_finite(ALL, fmt)]
+    x = F["val"](xs)
+    y = F["val"](orc.act_fwd(p, xs, F["order"]))
+    c = bf16v(np.array(p.coeff_bits(), dtype=np.uint16))
+    t = np.abs(x)
+    th = np.minimum(t, p.Lc)
+    v = np.polyval(c[::-1], th)
+    absv = np.polyval(np.abs(c)[::-1], th)
+    D = p.degree
+    u = F["u"] if fmt == "f16" else 2.0 ** -8 + 2.0 ** -24   # FP32 then BF16 per stage
+    gamma = (D + 1) * u / (1 - (D + 1) * u)
+    chain = gamma * absv + (D + 2) * F["tiny"]
+    sg = np.where(np.signbit(x), -1.0, 1.0)
+    if name.startswith("sigmoid_fwd"):
+        P, err = 0.5 + sg * v, chain
+    elif name.startswith("tanh_fwd") or name.endswith("bwd_d4"):
+        P, err = (sg * v if name.startswith("tanh_fwd") else v), chain
+    else:   # SiLU / GELU: x/2 + t v, t unclamped
+        P, err = 0.5 * x + t * v, t * chain + np.abs(0.5 * x) * u + 2 * F["tiny"]
+    bound = err + np.abs(P) * u + F["tiny"]
+    bad = ~(np.abs(y - P) <= bound) & np.isfinite(P)
+    assert not bad.any(), (name, fmt, x[bad][:5], y[bad][:5], P[bad][:5])
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+def test_special_values(orc, progs, fmt):
+    F = FMT[fmt]
+    inf, ninf = F["nan"], F["nan"] | 0x8000
+    nans = np.array([F["nan"] | 1, F["nan"] | F["quiet"], 0xFFFF, F["nan"] | 0x8000 | 3],
+                    dtype=np.uint16)
+    enc = (lambda v: np.array([v], np.float16).view(np.uint16)[0]) if fmt == "f16" else \
+        (lambda v: torch.tensor([v]).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)[0])
+    for name, p in progs.items():
+        y = orc.act_fwd(p, nans, F["order"])
+        assert np.array_equal(y, nans | F["quiet"]), name           # NaN -> quiet NaN
+    for name in ("sigmoid_fwd_d3", "tanh_fwd_d4", "sigmoid_bwd_d4", "tanh_bwd_d4"):
+        p = progs[name]
+        lc, nlc = enc(p.Lc), enc(-p.Lc)
+        y = orc.act_fwd(p, np.array([inf, ninf, lc, nlc], np.uint16), F["order"])
+        assert y[0] == y[2] and y[1] == y[3], name                  # clamp at +-Lc
+    for name in ("silu_fwd_d3", "gelu_fwd_d5"):
+        y = orc.act_fwd(progs[name], np.array([inf, ninf, 0, 0x8000], np.uint16), F["order"])
+        # -0: fma(+0, v, -0 * 1/2) = +0 + -0 = +0 under round-to-nearest
+        assert list(y) == [inf, 0x8000, 0, 0], name
+    y = orc.act_fwd(progs["tanh_fwd_d4"], np.array([0, 0x8000], np.uint16), F["order"])
+    assert list(y) == [0, 0x8000]
+    y = orc.act_fwd(progs["sigmoid_fwd_d3"], np.array([0, 0x8000], np.uint16), F["order"])
+    assert F["val"](y).tolist() == [0.5, 0.5]
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+def test_backward_is_rounded_product(orc, progs, fmt):
+    """dx = RN(g * q(x)): the product of two 16-bit values is exact in FP64,
+    and numpy / torch round FP64 -> FP16 and FP32 -> BF16 to nearest even."""
+    F = FMT[fmt]
+    rng = np.random.default_rng(5)
+    xs = ALL[_finite(ALL, fmt)]
+    g = rng.integers(0, 65536, xs.size).astype(np.uint16)
+    g = np.where(_finite(g, fmt), g, np.uint16(0x3C00 if fmt == "f16" else 0x3F80)).astype(np.uint16)
+    for name in ("sigmoid_bwd_d4", "tanh_bwd_d4"):
+        p = progs[name]
+        q = F["val"](orc.act_fwd(p, xs, F["order"]))
+        dx = orc.act_bwd(p, xs, g, F["order"])
+        prod = F["val"](g) * q
+        if fmt == "f16":
+            ref = prod.astype(np.float16).view(np.uint16)
+        else:   # deployed BF16 order: RN_bf16(RN_f32(g q))
+            ref = torch.from_numpy(prod).to(torch.float32).to(torch.bfloat16) \
+                .view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(dx, ref), name
+        assert np.all(q > 0), name                  # no inf * 0 can arise
+
+
+def test_swiglu_matches_ieee_float32(orc, progs):
+    rng = np.random.default_rng(6)
+    rows, cols = 37, 200
+    def bf(a):
+        return torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    g = bf(rng.standard_normal((rows, cols)) * 2)
+    u = bf(rng.standard_normal((rows, cols)) * 2)
+    dh = bf(rng.standard_normal((rows, cols)))
+    sig = progs["sigmoid_fwd_d3"]
+    h = orc.swiglu_fwd(sig, g, u)
+    dg, du = orc.swiglu_bwd(sig, g, u, dh)
+    p = bf16v(orc.act_fwd(sig, g.ravel(), 3)).reshape(rows, cols).astype(np.float32)
+    gf, uf, dhf = (bf16v(a).astype(np.float32) for a in (g, u, dh))
+    gp = gf * p
+    tob = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16) \
+        .view(torch.int16).numpy().view(np.uint16)  # noqa: E731
+    assert np.array_equal(h, tob(gp * uf))
+    ds = (gp.astype(np.float64) * (np.float32(1) - p) + p).astype(np.float32)  # one rounding
+    assert np.array_equal(du, tob(dhf * gp))
+    assert np.array_equal(dg, tob((dhf * uf) * ds))
+    # approximation: h is SiLU(g) u to within the sigmoid program's error
+    silu = gf * sp.expit(gf.astype(np.float64))
+    eps = 5.5e-3 + 2.0 ** -8
+    assert np.all(np.abs(bf16v(h) - silu * uf) <= np.abs(gf * uf) * eps + np.abs(bf16v(h)) * 2 ** -8 + 1e-30)
+
+
+def test_swiglu_row_range(orc, progs):
+    rng = np.random.default_rng(7)
+    g = rng.integers(0, 0x4000, (10, 16)).astype(np.uint16)
+    u = rng.integers(0, 0x4000, (10, 16)).astype(np.uint16)
+    h = orc.swiglu_fwd(progs["sigmoid_fwd_d3"], g, u, 3, 7)
+    full = orc.swiglu_fwd(progs["sigmoid_fwd_d3"], g, u)
+    assert np.array_equal(h[3:7], full[3:7])
+    assert not h[:3].any() and not h[7:].any()
+
+
+def _textbook_attn(q, k, v, cap, causal, score_fn):
+    B, H, S, D = q.shape
+    s = np.einsum("bhid,bhjd->bhij", q, k)
+    s = score_fn(s)
+    if causal:
+        s = np.where(np.tril(np.ones((S, S), bool)), s, -np.inf)
+    s = s - s.max(-1, keepdims=True)
+    w = np.exp(s)
+    w /= w.sum(-1, keepdims=True)
+    return np.einsum("bhij,bhjd->bhid", w, v)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_attention_rows_against_textbook(orc, progs, causal):
+    rng = np.random.default_rng(8)
+    B, H, S, D, cap = 1, 2, 70, 32, 50.0
+    def bf(a):
+        return torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    q, k, v = (bf(rng.standard_normal((B, H, S, D)) * 3) for _ in range(3))
+    qf, kf, vf = (bf16v(a) for a in (q, k, v))
+    rows = np.arange(B * H * S)
+    # exact tanh softcap: textbook softcapped softmax attention
+    o, noise = orc.softcap_attn_rows(progs["tanh_fwd_d4"], False, q, k, v, cap, causal, rows)
+    ref = _textbook_attn(qf, kf, vf, cap, causal, lambda s: cap * np.tanh(s / (cap * np.sqrt(D))))
+    np.testing.assert_allclose(o, ref.reshape(-1, D), rtol=1e-12, atol=1e-13)
+    assert np.all(noise >= 0)
+    # polynomial softcap: the score is cap * tanh~(RN16(RN32(RN32(s) * scale)))
+    tp = progs["tanh_fwd_d4"]
+    scale = np.float32(1.0 / (cap * np.sqrt(D)))
+    def poly_score(s):
+        xs = (s.astype(np.float32) * scale).astype(np.float32)
+        xb = torch.from_numpy(np.ascontiguousarray(xs)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        return cap * bf16v(orc.act_fwd(tp, xb.ravel(), 3)).reshape(s.shape)
+    o, _ = orc.softcap_attn_rows(tp, True, q, k, v, cap, causal, rows)
+    ref = _textbook_attn(qf, kf, vf, cap, causal, poly_score)
+    np.testing.assert_allclose(o, ref.reshape(-1, D), rtol=1e-12, atol=1e-13)
