@@ -1,0 +1,282 @@
+"""Benchmark: the isolated FP16 polynomial-activation sweep on one MI355X.
+
+One step = the six polynomial programs of the isolated sweep over one batch of
+268,435,456 FP16 elements (HBM resident), as in "Fast Polynomial
+Transcendentals for LLMs", section 4.2 / Table 3: sigmoid D3, tanh D4, SiLU D3
+and GELU D5 forward (y from x), sigmoid' D4 and tanh' D4 backward (dx from x
+and the upstream gradient).  Inputs: x ~ clip(N(0, 3), +-12), grad ~ N(0, 1),
+drawn on the GPU before timing (resident in HBM when the timed region starts).
+
+value   = elements processed per second over the timed steps (Gelem/s);
+roofline = the dominant kernel of the step, algorithmic bytes per launch
+          (4 B/elem forward, 6 B/elem backward) over its mean launch time,
+          measured with HIP events on the launch stream, against 8 TB/s;
+cpu_baseline = the CPU oracle replaying the same programs on a bounded
+          sample of the same arrays, on this host's cores.
+Also reported: each program's Gelem/s and share of HBM peak, the matched
+accurate-expf comparator and the speedup (alternating rounds, median of
+per-round times), the L2-resident 4,194,304-element endpoint, and the fused
+SwiGLU / softcap-attention components.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+BF16_DENSE_TFLOPS = 2500.0     # MI355X dense BF16 MFMA, vendor figure
+N_HBM = 268_435_456
+N_L2 = 4_194_304
+FWD = ["sigmoid", "tanh", "silu", "gelu"]
+BWD = ["sigmoid", "tanh"]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--rounds", type=int, default=5, help="alternating poly/native rounds")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-components", action="store_true", help="skip SwiGLU / attention")
+    ap.add_argument("--only", default="", help="profile helper: run one kernel name only")
+    return ap.parse_args()
+
+
+def kernels(pa, x, g):
+    """(name, bytes per element, launch) for every program of the step."""
+    out = []
+    y = __import__("torch").empty_like(x)
+    for f in FWD:
+        out.append((f"{f}_fwd", 4, lambda f=f: pa.poly_act_fwd(x, f, out=y),
+                    lambda f=f: pa.native_act_fwd(x, f, out=y)))
+    for f in BWD:
+        out.append((f"{f}_bwd", 6, lambda f=f: pa.poly_act_bwd(x, g, f, out=y),
+                    lambda f=f: pa.native_act_bwd(x, g, f, "native", out=y)))
+    return out, y
+
+
+def time_calls(torch, fn, reps):
+    """Mean ms per call of `reps` back-to-back calls, HIP events on the
+    current stream (the stream the library launches on)."""
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        fn()
+    e.record()
+    e.synchronize()
+    return s.elapsed_time(e) / reps
+
+
+def alternating(torch, poly, native, reps, rounds):
+    """Median per-round mean times, alternating which path goes first."""
+    tp, tn = [], []
+    for r in range(rounds):
+        if r % 2 == 0:
+            tp.append(time_calls(torch, poly, reps))
+            tn.append(time_calls(torch, native, reps))
+        else:
+            tn.append(time_calls(torch, native, reps))
+            tp.append(time_calls(torch, poly, reps))
+    return statistics.median(tp), statistics.median(tn)
+
+
+def cpu_baseline(x_t, g_t, budget_s=12.0):
+    """The oracle (OpenMP over this host's cores) on a bounded sample."""
+    import numpy as np
+
+    import oracle as orc
+    gold = json.load(open(os.path.join(ROOT, "tests", "golden", "programs.json")))["programs"]
+    byname = {e["name"]: orc.make_prog(e["func"], e["deriv"], e["degree"], e["Li"], e["Lc"])
+              for e in gold}
+    progs = {"sigmoid_fwd": byname["sigmoid_fwd_d3"], "tanh_fwd": byname["tanh_fwd_d4"],
+             "silu_fwd": byname["silu_fwd_d3"], "gelu_fwd": byname["gelu_fwd_d5"],
+             "sigmoid_bwd": byname["sigmoid_bwd_d4"], "tanh_bwd": byname["tanh_bwd_d4"]}
+    n = 1 << 21
+    xs = x_t[:n].contiguous().view(__import__("torch").int16).cpu().numpy().view(np.uint16)
+    gs = g_t[:n].contiguous().view(__import__("torch").int16).cpu().numpy().view(np.uint16)
+    done, t0 = 0, time.perf_counter()
+    while True:
+        for f in FWD:
+            orc.act_fwd(progs[f"{f}_fwd"], xs, orc.ORDER_F16_FMA)
+        for f in BWD:
+            orc.act_bwd(progs[f"{f}_bwd"], xs, gs, orc.ORDER_F16_FMA)
+        done += 1
+        el = time.perf_counter() - t0
+        if el > budget_s or done >= 64:
+            break
+    elems = done * 6 * n
+    return {"value": round(elems / el / 1e9, 5), "unit": "Gelem/s", "cores": orc.threads(),
+            "kind": "oracle",
+            "sample": f"{done} passes of the six programs over the first {n} elements "
+                      f"of the same x / grad arrays ({elems} element evaluations, {el:.1f} s)"}
+
+
+def components(torch, pa, si):
+    """Fused SwiGLU (dense 8192 x 14336; routed 131,072 x 1408) and softcap
+    attention (1 x 16 x 8192 x 128, causal), poly vs accurate comparator."""
+    res = {}
+    g, u, d = si.t_swiglu_inputs(8192, 14336)
+    h, dg, du = torch.empty_like(g), torch.empty_like(g), torch.empty_like(g)
+    n = g.numel()
+    for name, fp, fn, by in (
+            ("swiglu_dense_fwd", lambda: pa.poly_swiglu_fwd(g, u, out=h),
+             lambda: pa.native_swiglu_fwd(g, u, out=h), 6),
+            ("swiglu_dense_bwd", lambda: pa.poly_swiglu_bwd(g, u, d, out=(dg, du)),
+             lambda: pa.native_swiglu_bwd(g, u, d, out=(dg, du)), 10)):
+        fp(), fn()
+        tp, tn = alternating(torch, fp, fn, 20, 5)
+        res[name] = {"elements": n, "poly_ms": round(tp, 4), "native_ms": round(tn, 4),
+                     "speedup": round(tn / tp, 3), "gelem_s": round(n / tp / 1e6, 2),
+                     "pct_hbm": round(100 * n * by / tp / 1e6 / HBM_PEAK_GBS, 1)}
+    del g, u, d, h, dg, du
+    offsets, _ = si.zipf_routing()
+    rows = int(offsets[-1])
+    g, u, d = si.t_swiglu_inputs(rows, 1408)
+    h, dg, du = torch.empty_like(g), torch.empty_like(g), torch.empty_like(g)
+    off = torch.from_numpy(offsets).cuda()
+    n = g.numel()
+    for name, fp, fn, by in (
+            ("swiglu_routed_fwd", lambda: pa.poly_swiglu_fwd(g, u, out=h, row_offsets=off),
+             lambda: pa.native_swiglu_fwd(g, u, out=h, row_offsets=off), 6),
+            ("swiglu_routed_bwd", lambda: pa.poly_swiglu_bwd(g, u, d, out=(dg, du), row_offsets=off),
+             lambda: pa.native_swiglu_bwd(g, u, d, out=(dg, du), row_offsets=off), 10)):
+        fp(), fn()
+        tp, tn = alternating(torch, fp, fn, 20, 5)
+        res[name] = {"elements": n, "poly_ms": round(tp, 4), "native_ms": round(tn, 4),
+                     "speedup": round(tn / tp, 3), "gelem_s": round(n / tp / 1e6, 2),
+                     "pct_hbm": round(100 * n * by / tp / 1e6 / HBM_PEAK_GBS, 1)}
+    del g, u, d, h, dg, du
+    q, k, v = si.t_attn_inputs(1, 16, 8192, 128)
+    o = torch.empty_like(q)
+    fp = lambda: pa.poly_softcap_attn_fwd(q, k, v, 50.0, True, out=o)  # noqa: E731
+    fn = lambda: pa.native_softcap_attn_fwd(q, k, v, 50.0, True, out=o)  # noqa: E731
+    fp(), fn()
+    tp, tn = alternating(torch, fp, fn, 5, 5)
+    scores = 16 * 8192 * 8193 // 2
+    flops = 4 * 128 * scores
+    res["softcap_attn_fwd"] = {"causal_scores": scores, "poly_ms": round(tp, 4),
+                               "native_ms": round(tn, 4), "speedup": round(tn / tp, 3),
+                               "tflops": round(flops / tp / 1e9, 1),
+                               "pct_mfma_bf16": round(100 * flops / tp / 1e9 / BF16_DENSE_TFLOPS, 1)}
+    return res
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", flush=True)
+        sys.exit(2)
+    import torch
+
+    import elementwise_symmetry_range_amd as pa
+    import synth_inputs as si
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    pa.lib()
+
+    x, g = si.t_cfg2(N_HBM, device="cuda")
+    ks, y = kernels(pa, x, g)
+    if args.only:
+        ks = [k for k in ks if k[0] == args.only]
+    for _ in range(args.warmup):
+        for _, _, fp, _ in ks:
+            fp()
+    torch.cuda.synchronize()
+
+    # ---- timed steps, with per-kernel events on the launch stream ----------
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in ks] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for s in range(args.steps):
+        for i, (_, _, fp, _) in enumerate(ks):
+            ev[s][i][0].record()
+            fp()
+            ev[s][i][1].record()
+    t1.record()
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    ms_step = total_ms / args.steps
+    per = {name: statistics.mean(ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps))
+           for i, (name, _, _, _) in enumerate(ks)}
+    elems_step = N_HBM * len(ks)
+    value = elems_step / (ms_step * 1e-3) / 1e9
+
+    dom = max(ks, key=lambda k: per[k[0]])
+    dom_bytes = dom[1] * N_HBM
+    achieved = dom_bytes / (per[dom[0]] * 1e-3) / 1e9
+    traffic = None
+    tpath = os.path.join(ROOT, "profiles", "traffic.json")
+    if os.path.exists(tpath):
+        tr = json.load(open(tpath))
+        from elementwise_symmetry_range_amd._build import source_digest
+        if tr.get("source_digest") == source_digest() and dom[0] in tr.get("kernels", {}):
+            traffic = tr["kernels"][dom[0]]
+
+    # ---- matched comparators and the L2-resident endpoint (not in the step) --
+    detail = {}
+    for name, by, fp, fn in ks:
+        tp, tn = alternating(torch, fp, fn, 10, args.rounds)
+        detail[name] = {"poly_gelem_s": round(N_HBM / tp / 1e6, 1),
+                        "pct_hbm": round(100 * by * N_HBM / tp / 1e6 / HBM_PEAK_GBS, 1),
+                        "native_gelem_s": round(N_HBM / tn / 1e6, 1),
+                        "speedup_vs_accurate": round(tn / tp, 3)}
+    for f in BWD:   # the paper's native backward consumes the saved y
+        yy = pa.native_act_fwd(x, f)
+        tp = time_calls(torch, lambda f=f: pa.poly_act_bwd(x, g, f, out=y), 10)
+        tn = time_calls(torch, lambda f=f: pa.native_act_bwd(yy, g, f, "native_from_y", out=y), 10)
+        detail[f"{f}_bwd"]["speedup_vs_from_y"] = round(tn / tp, 3)
+        del yy
+    xs, gs = x[:N_L2].clone(), g[:N_L2].clone()
+    ys = torch.empty_like(xs)
+    l2 = {}
+    for f in FWD:
+        tp, tn = alternating(torch, lambda f=f: pa.poly_act_fwd(xs, f, out=ys),
+                             lambda f=f: pa.native_act_fwd(xs, f, out=ys), 200, args.rounds)
+        l2[f"{f}_fwd"] = {"poly_gelem_s": round(N_L2 / tp / 1e6, 1), "speedup": round(tn / tp, 3)}
+    for f in BWD:
+        tp, tn = alternating(torch, lambda f=f: pa.poly_act_bwd(xs, gs, f, out=ys),
+                             lambda f=f: pa.native_act_bwd(xs, gs, f, "native", out=ys), 200,
+                             args.rounds)
+        l2[f"{f}_bwd"] = {"poly_gelem_s": round(N_L2 / tp / 1e6, 1), "speedup": round(tn / tp, 3)}
+    del xs, gs, ys
+
+    comp = None if args.no_components else components(torch, pa, si)
+    cpu = None if args.no_cpu else cpu_baseline(x, g)
+
+    line = {
+        "metric": "Gelem/s and % of HBM roofline per poly activation vs accurate-expf kernel",
+        "value": round(value, 2), "unit": "Gelem/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": "isolated FP16 sweep, 268,435,456 elements: sigmoid D3, tanh D4, "
+                               "SiLU D3, GELU D5 forward; sigmoid' D4, tanh' D4 backward; "
+                               "x ~ clip(N(0,3), +-12), grad ~ N(0,1)",
+                   "elements_per_kernel": N_HBM, "kernels_per_step": len(ks),
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": dom[0], "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "algorithmic_bytes_per_launch": dom_bytes,
+                     "mean_launch_ms": round(per[dom[0]], 5)},
+        "cpu_baseline": cpu,
+        "per_kernel_ms": {k: round(v, 5) for k, v in per.items()},
+        "detail_hbm": detail,
+        "detail_l2_resident_4M": l2,
+        "components": comp,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,239 @@
+"""Python binding of libpolyact.so, the gfx950 polynomial activation library.
+
+Argument marshalling only: every computation runs in the HIP kernels behind
+the C ABI declared in include/polyact.h.  Tensors supply device memory and the
+current stream; there is no fallback path -- if the library is not built, or a
+call fails, an exception is raised.
+
+Programs ("Fast Polynomial Transcendentals for LLMs", arXiv 2610.00049):
+sigmoid D3, tanh D4, SiLU D3 and GELU D5 forward; sigmoid' D4 and tanh' D4
+direct derivative fits for backward; the D3 sigmoid fused into SwiGLU forward
+and backward; the D4 tanh as an attention softcap.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+from ._build import LIB as LIB_PATH
+
+__all__ = [
+    "PolyActError", "lib", "program_info", "poly_act_fwd", "poly_act_bwd", "native_act_fwd",
+    "native_act_bwd", "poly_swiglu_fwd", "poly_swiglu_bwd", "native_swiglu_fwd",
+    "native_swiglu_bwd", "poly_softcap_attn_fwd", "native_softcap_attn_fwd", "FUNCS",
+]
+
+FUNCS = {"sigmoid": 1, "tanh": 2, "silu": 3, "gelu": 4}
+IMPLS = {"poly": 0, "native": 1, "native_from_y": 2}
+_DTYPES = {torch.float16: 1, torch.bfloat16: 2}
+DTYPE_CODES = {"f16": 1, "bf16": 2}
+
+
+class PaProgram(C.Structure):
+    _fields_ = [("func", C.c_int32), ("deriv", C.c_int32), ("degree", C.c_int32),
+                ("dtype", C.c_int32), ("Li", C.c_float), ("Lc", C.c_float),
+                ("coeff_bits", C.c_uint16 * 8), ("order", C.c_int32)]
+
+
+class PolyActError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"polyact status {status}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> C.CDLL:
+    """The loaded C library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                               "(hipcc --offload-arch=gfx950)")
+        L = C.CDLL(LIB_PATH)
+        p, i32, i64, f32 = C.c_void_p, C.c_int32, C.c_int64, C.c_float
+        sigs = {
+            "poly_act_fwd": [i32, i32, p, p, i64, p],
+            "poly_act_bwd": [i32, i32, p, p, p, i64, p],
+            "native_act_fwd": [i32, i32, p, p, i64, p],
+            "native_act_bwd": [i32, i32, i32, p, p, p, i64, p],
+            "poly_swiglu_fwd": [i32, p, p, p, i64, i64, i64, i64, i64, p, i32, p],
+            "native_swiglu_fwd": [i32, p, p, p, i64, i64, i64, i64, i64, p, i32, p],
+            "poly_swiglu_bwd": [i32, p, p, p, p, p, i64, i64, i64, i64, i64, i64, i64, p, i32, p],
+            "native_swiglu_bwd": [i32, p, p, p, p, p, i64, i64, i64, i64, i64, i64, i64, p, i32,
+                                  p],
+            "poly_softcap_attn_fwd": [p, p, p, p, i32, i32, i32, i32, f32, i32, p],
+            "native_softcap_attn_fwd": [p, p, p, p, i32, i32, i32, i32, f32, i32, p],
+            "poly_program_info": [i32, i32, i32, C.POINTER(PaProgram)],
+        }
+        for name, args in sigs.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = C.c_int
+        L.pa_status_str.argtypes = [C.c_int]
+        L.pa_status_str.restype = C.c_char_p
+        L.pa_abi_version.argtypes = []
+        L.pa_abi_version.restype = C.c_int32
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise PolyActError(status, lib().pa_status_str(status).decode())
+
+
+def program_info(func: str, deriv: int, dtype: str = "f16") -> dict:
+    """The program the kernels execute (host query, no device work)."""
+    out = PaProgram()
+    _check(lib().poly_program_info(FUNCS[func], deriv, DTYPE_CODES[dtype], C.byref(out)))
+    return {"func": out.func, "deriv": out.deriv, "degree": out.degree, "dtype": out.dtype,
+            "Li": out.Li, "Lc": out.Lc, "order": out.order,
+            "coeff_bits": [int(out.coeff_bits[j]) for j in range(out.degree + 1)]}
+
+
+def _dev(t: torch.Tensor, name: str):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype not in _DTYPES:
+        raise TypeError(f"{name} must be float16 or bfloat16, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _out(out, like):
+    if out is None:
+        return torch.empty_like(like)
+    _dev(out, "out")
+    if out.dtype != like.dtype or out.numel() != like.numel():
+        raise ValueError("out must match the input's dtype and size")
+    return out
+
+
+def poly_act_fwd(x: torch.Tensor, func: str, out=None) -> torch.Tensor:
+    _dev(x, "x")
+    y = _out(out, x)
+    _check(lib().poly_act_fwd(FUNCS[func], _DTYPES[x.dtype], x.data_ptr(), y.data_ptr(),
+                              x.numel(), _stream(x)))
+    return y
+
+
+def poly_act_bwd(x: torch.Tensor, dy: torch.Tensor, func: str, out=None) -> torch.Tensor:
+    _dev(x, "x")
+    _dev(dy, "dy")
+    if dy.dtype != x.dtype or dy.numel() != x.numel():
+        raise ValueError("dy must match x")
+    dx = _out(out, x)
+    _check(lib().poly_act_bwd(FUNCS[func], _DTYPES[x.dtype], x.data_ptr(), dy.data_ptr(),
+                              dx.data_ptr(), x.numel(), _stream(x)))
+    return dx
+
+
+def native_act_fwd(x: torch.Tensor, func: str, out=None) -> torch.Tensor:
+    _dev(x, "x")
+    y = _out(out, x)
+    _check(lib().native_act_fwd(FUNCS[func], _DTYPES[x.dtype], x.data_ptr(), y.data_ptr(),
+                                x.numel(), _stream(x)))
+    return y
+
+
+def native_act_bwd(x_or_y: torch.Tensor, dy: torch.Tensor, func: str, impl: str = "native",
+                   out=None) -> torch.Tensor:
+    _dev(x_or_y, "x_or_y")
+    _dev(dy, "dy")
+    if dy.dtype != x_or_y.dtype or dy.numel() != x_or_y.numel():
+        raise ValueError("dy must match x_or_y")
+    dx = _out(out, x_or_y)
+    _check(lib().native_act_bwd(IMPLS[impl], FUNCS[func], _DTYPES[x_or_y.dtype],
+                                x_or_y.data_ptr(), dy.data_ptr(), dx.data_ptr(), x_or_y.numel(),
+                                _stream(x_or_y)))
+    return dx
+
+
+def _mat(t: torch.Tensor, name: str):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be a bfloat16 CUDA tensor")
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be 2-D with unit column stride")
+    return t.stride(0)
+
+
+def _offsets(row_offsets):
+    if row_offsets is None:
+        return None, 0
+    if not row_offsets.is_cuda or row_offsets.dtype != torch.int64 or row_offsets.dim() != 1:
+        raise TypeError("row_offsets must be a 1-D int64 CUDA tensor")
+    return row_offsets.data_ptr(), row_offsets.numel() - 1
+
+
+def _swiglu_fwd(entry, gate, up, out, row_offsets):
+    ldg, ldu = _mat(gate, "gate"), _mat(up, "up")
+    if up.shape != gate.shape:
+        raise ValueError("up must match gate")
+    h = torch.empty_like(gate) if out is None else out
+    ldh = _mat(h, "out")
+    off, ng = _offsets(row_offsets)
+    rows, cols = gate.shape
+    _check(entry(2, gate.data_ptr(), up.data_ptr(), h.data_ptr(), rows, cols, ldg, ldu, ldh, off,
+                 ng, _stream(gate)))
+    return h
+
+
+def _swiglu_bwd(entry, gate, up, dh, out, row_offsets):
+    ldg, ldu, ldd = _mat(gate, "gate"), _mat(up, "up"), _mat(dh, "dh")
+    if up.shape != gate.shape or dh.shape != gate.shape:
+        raise ValueError("up and dh must match gate")
+    dg, du = (torch.empty_like(gate), torch.empty_like(gate)) if out is None else out
+    lddg, lddu = _mat(dg, "dgate"), _mat(du, "dup")
+    off, ng = _offsets(row_offsets)
+    rows, cols = gate.shape
+    _check(entry(2, gate.data_ptr(), up.data_ptr(), dh.data_ptr(), dg.data_ptr(), du.data_ptr(),
+                 rows, cols, ldg, ldu, ldd, lddg, lddu, off, ng, _stream(gate)))
+    return dg, du
+
+
+def poly_swiglu_fwd(gate, up, out=None, row_offsets=None):
+    """h = SiLU~(gate) * up (BF16); grouped rows when row_offsets is given."""
+    return _swiglu_fwd(lib().poly_swiglu_fwd, gate, up, out, row_offsets)
+
+
+def poly_swiglu_bwd(gate, up, dh, out=None, row_offsets=None):
+    """(dgate, dup) of SwiGLU with the recomputed D3 sigmoid (BF16)."""
+    return _swiglu_bwd(lib().poly_swiglu_bwd, gate, up, dh, out, row_offsets)
+
+
+def native_swiglu_fwd(gate, up, out=None, row_offsets=None):
+    return _swiglu_fwd(lib().native_swiglu_fwd, gate, up, out, row_offsets)
+
+
+def native_swiglu_bwd(gate, up, dh, out=None, row_offsets=None):
+    return _swiglu_bwd(lib().native_swiglu_bwd, gate, up, dh, out, row_offsets)
+
+
+def _attn(entry, q, k, v, cap, causal, out):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda or t.dtype != torch.bfloat16 or t.dim() != 4 or not t.is_contiguous():
+            raise TypeError(f"{name} must be a contiguous bfloat16 CUDA tensor [B, H, S, D]")
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must have the same shape")
+    o = torch.empty_like(q) if out is None else out
+    B, H, S, D = q.shape
+    _check(entry(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), B, H, S, D, float(cap),
+                 int(bool(causal)), _stream(q)))
+    return o
+
+
+def poly_softcap_attn_fwd(q, k, v, cap: float = 50.0, causal: bool = True, out=None):
+    """Softcapped attention forward with the D4 tanh program (BF16, D = 128)."""
+    return _attn(lib().poly_softcap_attn_fwd, q, k, v, cap, causal, out)
+
+
+def native_softcap_attn_fwd(q, k, v, cap: float = 50.0, causal: bool = True, out=None):
+    return _attn(lib().native_softcap_attn_fwd, q, k, v, cap, causal, out)

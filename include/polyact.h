@@ -1,0 +1,199 @@
+/*
+ * polyact.h -- C ABI of the MI355X (gfx950) polynomial activation library.
+ *
+ * Short polynomial programs replace sigmoid, tanh, SiLU and exact GELU in the
+ * forward pass and the sigmoid / tanh derivatives in the backward pass, as in
+ * "Fast Polynomial Transcendentals for LLMs" (arXiv 2610.00049):
+ *   - range reduction t = |x|, runtime clamp t^ = min(t, Lc)   (section 3.1, Eq. 2)
+ *   - centered-odd sigmoid 1/2 + sign(x) p(t^), odd tanh        (Eq. 3)
+ *   - SiLU / GELU as x/2 + t p(t^), t unclamped                 (Eqs. 4-6)
+ *   - even direct derivative fits q(t^) for sigmoid', tanh'     (section 3.3)
+ *   - Horner chains with BF16-rounded coefficients, one rounding per
+ *     multiply-add in the target format, in deployed order     (section 3.2)
+ *   - the same D3 sigmoid inside a fused SwiGLU forward / backward
+ *     (section 3.3, section 3.4, Eq. 15) over dense or expert-grouped rows
+ *   - the D4 tanh as the softcap alpha tanh(x / alpha) on attention logits
+ *     inside a flash-attention forward (Eq. 1, section 5.2.2).
+ *
+ * Arithmetic.  FP16 programs run on packed FP16 FMA (one IEEE rounding per
+ * stage).  gfx950 has no packed BF16 FMA, so BF16 programs run each stage as
+ * an FP32 FMA followed by round-to-nearest-even to BF16 (two roundings per
+ * stage; pa_program.order = PA_ORDER_F32FMA_BF16).
+ *
+ * Special values.  NaN in -> the same NaN with its quiet bit set; +-inf is
+ * clamped like any large input (sigmoid(+inf) = 1/2 + p(Lc)); SiLU / GELU map
+ * -inf to -0 and +inf to +inf; signed zeros follow IEEE arithmetic of the
+ * deployed sequence.  Backward: NaN x or NaN upstream gradient -> that NaN,
+ * quieted.  Subnormals are preserved (no flush to zero).
+ *
+ * Conventions for every entry point below.
+ *   Ownership  all data pointers are DEVICE pointers owned by the caller; the
+ *              library never allocates, frees or retains caller memory and has
+ *              no mutable global state (the program table is read-only).
+ *   Streams    work is enqueued on `stream` (0 = the default stream) and runs
+ *              asynchronously; nothing synchronises the device.
+ *   Errors     argument errors are detected on the host before any launch and
+ *              returned synchronously; nothing is enqueued then.  A failed
+ *              launch returns PA_ERR_LAUNCH.  n == 0 (or rows == 0) returns
+ *              PA_OK without a launch; negative sizes return PA_ERR_SHAPE.
+ *   Layout     element arrays are contiguous 16-bit values (FP16 or BF16);
+ *              pointers must be 2-byte aligned (PA_ERR_ALIGN otherwise).  The
+ *              16-byte vector path runs on the aligned middle of the range;
+ *              any misaligned head or ragged tail takes a scalar path.
+ *   Aliasing   an output may alias an input exactly (same pointer); partial
+ *              overlap of an output with any other buffer is PA_ERR_OVERLAP.
+ */
+#ifndef POLYACT_H
+#define POLYACT_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* HIP's stream handle (the same typedef as hip_runtime_api.h). */
+typedef struct ihipStream_t *hipStream_t;
+
+#define PA_ABI_VERSION 1
+
+typedef enum {
+    PA_OK = 0,
+    PA_ERR_NULL = 1,     /* a required pointer is NULL                      */
+    PA_ERR_SHAPE = 2,    /* negative size, ld < cols, bad head dimension ... */
+    PA_ERR_DTYPE = 3,    /* unknown pa_dtype or dtype not supported here    */
+    PA_ERR_FUNC = 4,     /* unknown pa_func / pa_impl or no such program    */
+    PA_ERR_OVERLAP = 5,  /* an output partially overlaps another buffer     */
+    PA_ERR_LAUNCH = 6,   /* the kernel launch failed (hipGetLastError)      */
+    PA_ERR_ALIGN = 7     /* a pointer is not 2-byte aligned                 */
+} pa_status;
+
+typedef enum { PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+typedef enum { PA_SIGMOID = 1, PA_TANH = 2, PA_SILU = 3, PA_GELU = 4 } pa_func;
+
+/* Comparator implementations (the "native" path the programs replace).
+ *   PA_IMPL_NATIVE         accurate FP32 evaluation from x: expf / tanhf / erfcf
+ *                          without fast-math and an IEEE divide (for the
+ *                          backward: the derivative recomputed from x);
+ *   PA_IMPL_NATIVE_FROM_Y  backward from the saved forward output y:
+ *                          g y (1 - y) for sigmoid, g (1 - y^2) for tanh
+ *                          (Eqs. 10-11; the paper's native backward). */
+typedef enum { PA_IMPL_POLY = 0, PA_IMPL_NATIVE = 1, PA_IMPL_NATIVE_FROM_Y = 2 } pa_impl;
+
+/* Rounding order of a program (see "Arithmetic" above). */
+typedef enum { PA_ORDER_F16_FMA = 1, PA_ORDER_F32FMA_BF16 = 3 } pa_order;
+
+/* A deployed program: y = reconstruct(Horner(c_D..c_0, min(|x|, Lc))).
+ * coeff_bits[j] is the BF16 bit pattern of the monomial coefficient c_j of
+ * t^j, j = 0..degree (entries above degree are 0).  The FP16 path uses the
+ * same values, each exactly representable in FP16. */
+typedef struct {
+    int32_t func;          /* pa_func                                        */
+    int32_t deriv;         /* 0 forward program, 1 direct derivative program */
+    int32_t degree;        /* D                                              */
+    int32_t dtype;         /* pa_dtype the info was requested for            */
+    float Li;              /* fit interval [0, Li] (section 3.2)             */
+    float Lc;              /* runtime clamp                                  */
+    uint16_t coeff_bits[8];
+    int32_t order;         /* pa_order used for dtype                        */
+} pa_program;
+
+/* y[i] = f~(x[i]), i < n.  f = PA_SIGMOID (D3), PA_TANH (D4), PA_SILU (D3,
+ * reusing the sigmoid polynomial), PA_GELU (D5).  x, y: n elements of
+ * dtype t.  Paper: section 3.1, Eqs. 2-6; Table 2 programs. */
+pa_status poly_act_fwd(pa_func f, pa_dtype t, const void *x, void *y, int64_t n,
+                       hipStream_t stream);
+
+/* dx[i] = dy[i] * q(x[i]) with the direct D4 derivative fit q of f (even in
+ * x), evaluated from x.  f = PA_SIGMOID or PA_TANH.  Paper: section 3.3
+ * (direct derivative fits), section 4.2 (backward from x), Table 3. */
+pa_status poly_act_bwd(pa_func f, pa_dtype t, const void *x, const void *dy,
+                       void *dx, int64_t n, hipStream_t stream);
+
+/* Fused SwiGLU forward, BF16 only: h = SiLU~(g) * u with SiLU~(g) = g p(g)
+ * and p the D3 sigmoid program (section 3.3, Eq. 15); p in BF16 (FP32 FMA +
+ * BF16 rounding per stage), then h = RN_bf16(RN_f32(g p) * u) in FP32.
+ * Matrices are row-major [rows x cols] with leading dimensions (elements).
+ * Dense mode: row_offsets == NULL, rows [0, rows) are processed.
+ * Grouped mode: row_offsets is a DEVICE int64 array of n_groups + 1
+ * monotone offsets of an expert-sorted buffer; the kernel reads it on the
+ * device and processes rows [row_offsets[0], row_offsets[n_groups]),
+ * clipped to [0, rows): `rows` is the buffer's capacity, so the caller never
+ * synchronises to learn the routed row count.  Rows outside are untouched. */
+pa_status poly_swiglu_fwd(pa_dtype t, const void *gate, const void *up, void *h,
+                          int64_t rows, int64_t cols, int64_t ld_gate, int64_t ld_up,
+                          int64_t ld_h, const int64_t *row_offsets, int32_t n_groups,
+                          hipStream_t stream);
+
+/* Fused SwiGLU backward, BF16 only, both input gradients in one pass
+ * (section 3.3: recompute p = sigma~(g); SiLU~' = p + g p (1 - p)):
+ *   ds = RN_f32(g p (1 - p) + p),  dup = RN_bf16(dh * RN_f32(g p)),
+ *   dgate = RN_bf16(RN_f32(RN_f32(dh u) * ds)).
+ * Row selection as in poly_swiglu_fwd. */
+pa_status poly_swiglu_bwd(pa_dtype t, const void *gate, const void *up, const void *dh,
+                          void *dgate, void *dup, int64_t rows, int64_t cols,
+                          int64_t ld_gate, int64_t ld_up, int64_t ld_dh,
+                          int64_t ld_dgate, int64_t ld_dup, const int64_t *row_offsets,
+                          int32_t n_groups, hipStream_t stream);
+
+/* Softcapped attention forward, BF16 in/out, FP32 accumulation on MFMA:
+ *   S = Q K^T;  x = RN_f16(RN_f32(S) * RN_f32(1 / (cap sqrt(D))));
+ *   s = cap * tanh~(x), the D4 tanh program in packed FP16 arithmetic (the
+ *   packed 16-bit FMA of gfx950; its coefficients are the BF16 fit, exact in
+ *   FP16);  causal mask key <= query;  P = softmax(s) (FP32, online, exp2);
+ *   O = P V / l with P rounded to BF16 for the MFMA.
+ * q, k, v, o: [B, H, S, D] contiguous BF16, 16-byte aligned; D must be 128;
+ * any S >= 0; B * H <= 65535; cap > 0 and finite.  O must not overlap Q, K, V.
+ * Paper: Eq. 1 and section 5.2.2 (D4 tanh softcap inside attention). */
+pa_status poly_softcap_attn_fwd(const void *q, const void *k, const void *v, void *o,
+                                int32_t B, int32_t H, int32_t S, int32_t D, float cap,
+                                int32_t causal, hipStream_t stream);
+
+/* ---- matched comparators (same memory path, accurate FP32 math) -------- */
+
+/* y = f(x) with accurate FP32 math (sigmoid 1/(1+e^-|x|) in the overflow-safe
+ * form, tanhf, SiLU (x >= 0 ? x : x e) / (1 + e) with e = expf(-|x|), GELU
+ * x erfc(-x / sqrt 2) / 2), rounded once to dtype t. */
+pa_status native_act_fwd(pa_func f, pa_dtype t, const void *x, void *y, int64_t n,
+                         hipStream_t stream);
+
+/* Backward comparators.  impl = PA_IMPL_NATIVE: x_or_y is x and the derivative
+ * is recomputed accurately from x; impl = PA_IMPL_NATIVE_FROM_Y: x_or_y is the
+ * saved forward output y (Eqs. 10-11).  f = PA_SIGMOID or PA_TANH. */
+pa_status native_act_bwd(pa_impl impl, pa_func f, pa_dtype t, const void *x_or_y,
+                         const void *dy, void *dx, int64_t n, hipStream_t stream);
+
+/* SwiGLU with accurate FP32 SiLU (arguments as poly_swiglu_fwd / _bwd). */
+pa_status native_swiglu_fwd(pa_dtype t, const void *gate, const void *up, void *h,
+                            int64_t rows, int64_t cols, int64_t ld_gate, int64_t ld_up,
+                            int64_t ld_h, const int64_t *row_offsets, int32_t n_groups,
+                            hipStream_t stream);
+pa_status native_swiglu_bwd(pa_dtype t, const void *gate, const void *up, const void *dh,
+                            void *dgate, void *dup, int64_t rows, int64_t cols,
+                            int64_t ld_gate, int64_t ld_up, int64_t ld_dh,
+                            int64_t ld_dgate, int64_t ld_dup, const int64_t *row_offsets,
+                            int32_t n_groups, hipStream_t stream);
+
+/* Softcapped attention with accurate FP32 tanhf on the unrounded FP32 scaled
+ * score x = RN_f32(S) * RN_f32(1 / (cap sqrt(D))) (arguments as
+ * poly_softcap_attn_fwd). */
+pa_status native_softcap_attn_fwd(const void *q, const void *k, const void *v, void *o,
+                                  int32_t B, int32_t H, int32_t S, int32_t D, float cap,
+                                  int32_t causal, hipStream_t stream);
+
+/* ---- host-only queries (no device work) -------------------------------- */
+
+/* The program the kernels execute for (f, deriv, t).  Returns PA_ERR_FUNC if
+ * there is none, PA_ERR_NULL if out is NULL. */
+pa_status poly_program_info(pa_func f, int32_t deriv, pa_dtype t, pa_program *out);
+
+/* Static description of a status code. */
+const char *pa_status_str(pa_status s);
+
+/* PA_ABI_VERSION of the built library. */
+int32_t pa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* POLYACT_H */

@@ -58,7 +58,9 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
+        srcs = [os.path.join(HERE, f) for f in SOURCES + ["orc.h"]]
+        if not os.path.exists(LIB_PATH) or \
+                max(os.path.getmtime(f) for f in srcs) > os.path.getmtime(LIB_PATH):
             build()
         L = C.CDLL(LIB_PATH)
         u16, f64, i32, i64 = C.c_uint16, C.c_double, C.c_int32, C.c_int64

@@ -223,8 +223,8 @@ void orc_swiglu_bwd(const orc_prog *sig, const uint16_t *gate, const uint16_t *u
  * scale sqrt(sum_j P_j^2 V_jd^2) (the size of the output change caused by
  * relative perturbations of the probabilities; used to state tolerances).
  * Scores: S_ij = q_i . k_j exactly in FP64.
- *   poly = 1: x = RN16(RN32(RN32(S_ij) * RN32(1/(cap sqrt(D))))), the D4 tanh
- *             program in BF16 (FP32 FMA then BF16 per stage), s = cap * t~;
+ *   poly = 1: x = RN_f16(RN32(RN32(S_ij) * RN32(1/(cap sqrt(D))))), the D4 tanh
+ *             program in FP16 arithmetic (one rounding per FMA), s = cap * t~;
  *   poly = 0: s = cap * tanh(S_ij / (cap sqrt(D))) in FP64.
  * Causal: key j <= query i.  Softmax and the P V product in FP64. */
 void orc_softcap_attn_rows(const orc_prog *tp, int poly,
@@ -233,7 +233,7 @@ void orc_softcap_attn_rows(const orc_prog *tp, int poly,
                            int32_t causal, const int64_t *rows, int64_t n_rows,
                            double *out, double *noise)
 {
-    const fmt_ops f = ops_for(ORC_ORDER_F32FMA_BF16);
+    const fmt_ops f = ops_for(ORC_ORDER_F16_FMA);
     const float scale = (float)(1.0 / ((double)cap * sqrt((double)D)));
     (void)B;
 #pragma omp parallel
@@ -259,8 +259,8 @@ void orc_softcap_attn_rows(const orc_prog *tp, int poly,
                 double sc;
                 if (poly) {
                     const float xs = orc_mul_f32((float)acc, scale);
-                    const uint16_t xb = orc_f32_to_bf16(xs);
-                    sc = (double)cap * orc_bf16_to_f64(eval_one(&f, tp, xb));
+                    const uint16_t xh = orc_f64_to_f16((double)xs);
+                    sc = (double)cap * orc_f16_to_f64(eval_one(&f, tp, xh));
                 } else {
                     sc = (double)cap * tanh(acc / ((double)cap * sqrt((double)D)));
                 }

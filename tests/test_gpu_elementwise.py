@@ -1,0 +1,206 @@
+"""GPU parity of the elementwise programs against the CPU oracle.
+
+Bar: bit-exact (0 differing outputs) for every polynomial program, over all
+65,536 bit patterns of the format and over the seeded workload tensors; the
+accurate-expf comparators are within 1 ULP of the FP64 function.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth_inputs as si
+from gpu_util import (bwd_prog_name, diff_report, fwd_prog_name, note, programs, to_bits,
+                      to_dev)
+
+pytestmark = pytest.mark.gpu
+ALL = np.arange(65536, dtype=np.uint16)
+FWD = ["sigmoid", "tanh", "silu", "gelu"]
+BWD = ["sigmoid", "tanh"]
+DT = {"f16": torch.float16, "bf16": torch.bfloat16}
+ORDER = {"f16": 1, "bf16": 3}
+
+
+@pytest.fixture(scope="module")
+def pa():
+    import elementwise_symmetry_range_amd as pa
+    assert torch.cuda.is_available()
+    pa.lib()
+    return pa
+
+
+@pytest.fixture(scope="module")
+def progs(orc):
+    return programs(orc)
+
+
+def special_grads(fmt, n, rng):
+    g = rng.integers(0, 65536, n).astype(np.uint16)
+    return g
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+@pytest.mark.parametrize("func", FWD)
+def test_fwd_all_patterns(pa, orc, progs, fmt, func):
+    note(f"fwd all patterns {func} {fmt}")
+    y = to_bits(pa.poly_act_fwd(to_dev(ALL, DT[fmt]), func))
+    ref = orc.act_fwd(progs[fwd_prog_name(func)], ALL, ORDER[fmt])
+    assert np.array_equal(y, ref), diff_report(y, ref, ALL)
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+@pytest.mark.parametrize("func", BWD)
+def test_bwd_all_patterns(pa, orc, progs, fmt, func):
+    """Every x pattern against three gradient sets: random bits (NaN, inf,
+    subnormals included), ones, and seeded N(0, 1)."""
+    rng = np.random.default_rng(21)
+    one = np.uint16(0x3C00 if fmt == "f16" else 0x3F80)
+    for g in (rng.integers(0, 65536, 65536).astype(np.uint16), np.full(65536, one, np.uint16),
+              si.cfg2_grad(65536) if fmt == "f16" else si.to_bf16_bits(si.normal(3, 65536))):
+        note(f"bwd all patterns {func} {fmt}")
+        dx = to_bits(pa.poly_act_bwd(to_dev(ALL, DT[fmt]), to_dev(g, DT[fmt]), func))
+        ref = orc.act_bwd(progs[bwd_prog_name(func)], ALL, g, ORDER[fmt])
+        assert np.array_equal(dx, ref), diff_report(dx, ref, ALL)
+
+
+def test_cfg1_sigmoid_d3(pa, orc, progs):
+    """4,194,304 x ~ U(-8, 8) FP16 plus all 65,536 patterns, Lc = 5.28125."""
+    x = si.cfg1_x()
+    note(f"cfg1 sigmoid d3 n={x.size}")
+    y = to_bits(pa.poly_act_fwd(to_dev(x, torch.float16), "sigmoid"))
+    ref = orc.act_fwd(progs["sigmoid_fwd_d3"], x, 1)
+    assert np.array_equal(y, ref), diff_report(y, ref, x)
+
+
+@pytest.mark.parametrize("func", FWD)
+def test_cfg2_4m_fwd(pa, orc, progs, func):
+    n = 4_194_304
+    x = si.cfg2_x(n)
+    note(f"cfg2 4M fwd {func}")
+    y = to_bits(pa.poly_act_fwd(to_dev(x, torch.float16), func))
+    ref = orc.act_fwd(progs[fwd_prog_name(func)], x, 1)
+    assert np.array_equal(y, ref), diff_report(y, ref, x)
+
+
+@pytest.mark.parametrize("func", BWD)
+def test_cfg2_4m_bwd(pa, orc, progs, func):
+    n = 4_194_304
+    x, g = si.cfg2_x(n), si.cfg2_grad(n)
+    note(f"cfg2 4M bwd {func}")
+    dx = to_bits(pa.poly_act_bwd(to_dev(x, torch.float16), to_dev(g, torch.float16), func))
+    ref = orc.act_bwd(progs[bwd_prog_name(func)], x, g, 1)
+    assert np.array_equal(dx, ref), diff_report(dx, ref, x)
+
+
+def test_cfg2_268m_sampled(pa, orc, progs):
+    """The HBM-resident size, in the launch configuration the benchmark times:
+    inputs drawn on the GPU, every program run at full size, outputs compared
+    with the oracle on a stratified sample (every 61st element plus the last
+    4,096) of the same arrays."""
+    n = 268_435_456
+    note("cfg2 268M draw")
+    xt, gt = si.t_cfg2(n, device="cuda")
+    idx = np.concatenate([np.arange(0, n, 61), np.arange(n - 4096, n)])
+    it = torch.from_numpy(idx).cuda()
+    xs = to_bits(xt[it])
+    gs = to_bits(gt[it])
+    for func in FWD:
+        note(f"cfg2 268M fwd {func}")
+        y = pa.poly_act_fwd(xt, func)
+        got = to_bits(y[it])
+        del y
+        ref = orc.act_fwd(progs[fwd_prog_name(func)], xs, 1)
+        assert np.array_equal(got, ref), func + ": " + diff_report(got, ref, xs)
+    for func in BWD:
+        note(f"cfg2 268M bwd {func}")
+        dx = pa.poly_act_bwd(xt, gt, func)
+        got = to_bits(dx[it])
+        del dx
+        ref = orc.act_bwd(progs[bwd_prog_name(func)], xs, gs, 1)
+        assert np.array_equal(got, ref), func + ": " + diff_report(got, ref, xs)
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+def test_ragged_and_misaligned(pa, orc, progs, fmt):
+    """Scalar head / tail paths: sizes around the 8-element vector, a start
+    one element off 16-byte alignment, and input/output with different phases
+    (all-scalar path).  Exact aliasing (in place) too."""
+    rng = np.random.default_rng(22)
+    base = rng.integers(0, 65536, 5000).astype(np.uint16)
+    p = progs["gelu_fwd_d5"]
+    for n in (1, 7, 8, 9, 15, 17, 1023, 4099):
+        for off_x, off_y in ((0, 0), (1, 1), (3, 3), (1, 0), (0, 5)):
+            note(f"ragged {fmt} n={n} off=({off_x},{off_y})")
+            xb = to_dev(base, DT[fmt])
+            yb = torch.zeros(5000, dtype=DT[fmt], device="cuda")
+            x = xb[off_x:off_x + n]
+            y = yb[off_y:off_y + n]
+            pa.poly_act_fwd(x, "gelu", out=y)
+            got = to_bits(yb)
+            ref = orc.act_fwd(p, base[off_x:off_x + n], ORDER[fmt])
+            assert np.array_equal(got[off_y:off_y + n], ref), diff_report(got[off_y:off_y + n], ref)
+            assert not got[:off_y].any() and not got[off_y + n:].any()   # nothing outside
+    note(f"in place {fmt}")
+    xb = to_dev(base, DT[fmt])
+    pa.poly_act_fwd(xb, "tanh", out=xb)
+    assert np.array_equal(to_bits(xb), orc.act_fwd(progs["tanh_fwd_d4"], base, ORDER[fmt]))
+    g = rng.integers(0, 65536, 5000).astype(np.uint16)
+    for n, o in ((4099, 1), (13, 0)):
+        note(f"bwd ragged {fmt} n={n} off={o}")
+        xt, gt = to_dev(base, DT[fmt])[o:o + n], to_dev(g, DT[fmt])[o:o + n]
+        dx = to_bits(pa.poly_act_bwd(xt, gt, "sigmoid"))
+        ref = orc.act_bwd(progs["sigmoid_bwd_d4"], base[o:o + n], g[o:o + n], ORDER[fmt])
+        assert np.array_equal(dx, ref), diff_report(dx, ref)
+
+
+def _ulp_diff(a_bits, b_bits, fmt):
+    """Distance in representable values between two arrays of finite values."""
+    def key(b):
+        b = b.astype(np.int64)
+        return np.where(b & 0x8000, -(b & 0x7FFF), b & 0x7FFF)
+    return np.abs(key(a_bits) - key(b_bits))
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+@pytest.mark.parametrize("func", FWD)
+def test_native_fwd_within_one_ulp(pa, orc, fmt, func):
+    """The accurate-expf comparators round to within 1 ULP of the FP64 function."""
+    x = ALL[(ALL & 0x7FFF) < (0x7C00 if fmt == "f16" else 0x7F80)]
+    note(f"native fwd {func} {fmt}")
+    y = to_bits(pa.native_act_fwd(to_dev(x, DT[fmt]), func))
+    L = orc.lib()
+    dec = L.orc_f16_to_f64 if fmt == "f16" else L.orc_bf16_to_f64
+    enc = L.orc_f64_to_f16 if fmt == "f16" else L.orc_f64_to_bf16
+    ref = np.array([enc(L.orc_ref(orc.__dict__[func.upper()], 0, dec(int(b)))) for b in x],
+                   dtype=np.uint16)
+    d = _ulp_diff(y, ref, fmt)
+    zero_pair = ((y & 0x7FFF) == 0) & ((ref & 0x7FFF) == 0)   # +0 vs -0
+    assert np.all((d <= 1) | zero_pair), (func, fmt, int(d.max()))
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+@pytest.mark.parametrize("func", BWD)
+def test_native_bwd(pa, orc, fmt, func):
+    rng = np.random.default_rng(23)
+    fin = 0x7C00 if fmt == "f16" else 0x7F80
+    x = ALL[(ALL & 0x7FFF) < fin]
+    g = np.full(x.size, 0x3C00 if fmt == "f16" else 0x3F80, np.uint16)
+    L = orc.lib()
+    dec = L.orc_f16_to_f64 if fmt == "f16" else L.orc_bf16_to_f64
+    enc = L.orc_f64_to_f16 if fmt == "f16" else L.orc_f64_to_bf16
+    fid = orc.__dict__[func.upper()]
+    note(f"native bwd from x {func} {fmt}")
+    dx = to_bits(pa.native_act_bwd(to_dev(x, DT[fmt]), to_dev(g, DT[fmt]), func, "native"))
+    ref = np.array([enc(L.orc_ref(fid, 1, dec(int(b)))) for b in x], dtype=np.uint16)
+    assert np.all(_ulp_diff(dx, ref, fmt) <= 1), (func, fmt)
+    # from y: g y (1 - y) / g (1 - y^2) on the saved forward output
+    note(f"native bwd from y {func} {fmt}")
+    y = to_bits(pa.native_act_fwd(to_dev(x, DT[fmt]), func))
+    gr = rng.integers(0, fin, x.size).astype(np.uint16)
+    dxy = to_bits(pa.native_act_bwd(to_dev(y, DT[fmt]), to_dev(gr, DT[fmt]), func,
+                                    "native_from_y"))
+    yv = np.array([dec(int(b)) for b in y])
+    gv = np.array([dec(int(b)) for b in gr])
+    val = gv * (yv * (1 - yv)) if func == "sigmoid" else gv * (1 - yv * yv)
+    ref = np.array([enc(float(v)) for v in val], dtype=np.uint16)
+    fine = np.isfinite(val)
+    assert np.all(_ulp_diff(dxy[fine], ref[fine], fmt) <= 1), (func, fmt)

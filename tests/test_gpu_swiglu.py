@@ -1,0 +1,151 @@
+"""GPU parity of the fused SwiGLU forward / backward against the CPU oracle.
+
+Bar: bit-exact on every finite output; NaN outputs (only from NaN / inf
+inputs) must be NaN on both sides, payload free.  Dense [8192 x 14336] at full
+size (sampled rows), expert-grouped rows with Zipf routing, ragged columns,
+leading dimensions, capacity beyond the routed rows, empty groups.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth_inputs as si
+from gpu_util import diff_report, note, programs, to_bits, to_dev
+
+pytestmark = pytest.mark.gpu
+BF = torch.bfloat16
+
+
+@pytest.fixture(scope="module")
+def pa():
+    import elementwise_symmetry_range_amd as pa
+    assert torch.cuda.is_available()
+    pa.lib()
+    return pa
+
+
+@pytest.fixture(scope="module")
+def sig(orc):
+    return programs(orc)["sigmoid_fwd_d3"]
+
+
+def same(got, ref):
+    nan_g = (got & 0x7FFF) > 0x7F80
+    nan_r = (ref & 0x7FFF) > 0x7F80
+    ok = (got == ref) | (nan_g & nan_r)
+    return bool(ok.all()), diff_report(got.ravel(), ref.ravel())
+
+
+def run_both(pa, orc, sig, g, u, d, rows=None, offsets=None, ld=None):
+    """Runs forward and backward on the GPU with optional padded leading
+    dimension; returns GPU and oracle results for the processed row range."""
+    R, C = g.shape
+    ldc = ld or C
+
+    def put(a):
+        full = np.zeros((R, ldc), np.uint16)
+        full[:, :C] = a
+        return to_dev(full, BF)[:, :C]
+
+    gt, ut, dt = put(g), put(u), put(d)
+    off_t = None if offsets is None else torch.from_numpy(offsets).cuda()
+    h = pa.poly_swiglu_fwd(gt, ut, out=put(np.full_like(g, 0x7FC1)), row_offsets=off_t)
+    dg, du = pa.poly_swiglu_bwd(gt, ut, dt, out=(put(np.full_like(g, 0x7FC1)),
+                                                   put(np.full_like(g, 0x7FC1))),
+                                row_offsets=off_t)
+    r0, r1 = (0, R) if offsets is None else (int(offsets[0]), int(offsets[-1]))
+    rh = orc.swiglu_fwd(sig, g, u, r0, r1)
+    rdg, rdu = orc.swiglu_bwd(sig, g, u, d, r0, r1)
+    sent = np.full_like(g, 0x7FC1)
+    for ref in (rh, rdg, rdu):      # rows outside the range keep the sentinel
+        ref[:r0] = sent[:r0]
+        ref[r1:] = sent[r1:]
+    return (to_bits(h), to_bits(dg), to_bits(du)), (rh, rdg, rdu)
+
+
+@pytest.mark.parametrize("shape,ld", [((37, 200), None), ((16, 8), None), ((33, 13), None),
+                                      ((20, 136), 144), ((5, 7), 9), ((64, 1408), None)])
+def test_dense_small(pa, orc, sig, shape, ld):
+    g, u, d = si.swiglu_inputs(*shape)
+    note(f"swiglu dense {shape} ld={ld}")
+    got, ref = run_both(pa, orc, sig, g, u, d, ld=ld)
+    for a, b in zip(got, ref):
+        ok, msg = same(a, b)
+        assert ok, msg
+
+
+def test_special_values(pa, orc, sig):
+    """All BF16 gate patterns (NaN, inf, subnormal, signed zero) against
+    seeded up / dh values."""
+    g = np.arange(65536, dtype=np.uint16).reshape(512, 128)
+    _, u, d = si.swiglu_inputs(512, 128)
+    note("swiglu all gate patterns")
+    got, ref = run_both(pa, orc, sig, g, u, d)
+    for a, b in zip(got, ref):
+        ok, msg = same(a, b)
+        assert ok, msg
+
+
+def test_grouped_zipf(pa, orc, sig):
+    """Routed-expert rows: 16,384 tokens x top-8 over 64 experts, Zipf s = 1.1;
+    the buffer has spare capacity beyond the routed rows."""
+    offsets, counts = si.zipf_routing()
+    rows = int(offsets[-1])
+    cap = rows + 40
+    cols = 1408
+    g, u, d = si.swiglu_inputs(cap, cols)
+    note(f"swiglu grouped rows={rows} cap={cap}")
+    got, ref = run_both(pa, orc, sig, g, u, d, offsets=offsets)
+    for a, b in zip(got, ref):
+        ok, msg = same(a, b)
+        assert ok, msg
+
+
+def test_grouped_edge_offsets(pa, orc, sig):
+    """Empty groups, a nonzero first offset, an offset past the capacity."""
+    g, u, d = si.swiglu_inputs(50, 24)
+    for offs in ([0, 0, 0], [3, 3, 10, 10, 17], [7, 7], [5, 20, 80]):
+        o = np.array(offs, dtype=np.int64)
+        note(f"swiglu grouped offsets {offs}")
+        got, ref = run_both(pa, orc, sig, g, u, d, offsets=np.minimum(o, 50))
+        if offs[-1] > 50:   # the kernel clips to the capacity itself
+            off_t = torch.from_numpy(o).cuda()
+            h = pa.poly_swiglu_fwd(to_dev(g, BF), to_dev(u, BF), row_offsets=off_t)
+            torch.cuda.synchronize()
+            assert np.array_equal(to_bits(h)[5:50], orc.swiglu_fwd(sig, g, u, 5, 50)[5:50])
+        for a, b in zip(got, ref):
+            ok, msg = same(a, b)
+            assert ok, msg
+
+
+def test_dense_full_size_sampled(pa, orc, sig):
+    """[8192 x 14336] in the benchmark's launch configuration; inputs drawn on
+    the GPU, outputs compared on 96 sampled rows (first, last, random)."""
+    R, C = 8192, 14336
+    note("swiglu full size draw")
+    gt, ut, dt = si.t_swiglu_inputs(R, C)
+    note("swiglu full size fwd/bwd")
+    h = pa.poly_swiglu_fwd(gt, ut)
+    dg, du = pa.poly_swiglu_bwd(gt, ut, dt)
+    rng = np.random.default_rng(24)
+    rows = np.unique(np.concatenate([[0, 1, R - 1], rng.integers(0, R, 93)]))
+    rt = torch.from_numpy(rows).cuda()
+    g, u, d = to_bits(gt[rt]), to_bits(ut[rt]), to_bits(dt[rt])
+    rh = orc.swiglu_fwd(sig, g, u)
+    rdg, rdu = orc.swiglu_bwd(sig, g, u, d)
+    for t, r in ((h, rh), (dg, rdg), (du, rdu)):
+        ok, msg = same(to_bits(t[rt]), r)
+        assert ok, msg
+
+
+def test_native_swiglu_close(pa, orc, sig):
+    """The accurate comparator: h within 1 BF16 ULP of FP64 SiLU(g) * u."""
+    from scipy.special import expit
+    g, u, d = si.swiglu_inputs(64, 1408)
+    note("native swiglu")
+    h = to_bits(pa.native_swiglu_fwd(to_dev(g, BF), to_dev(u, BF)))
+    gv = (g.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    uv = (u.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    ref = si.to_bf16_bits(gv * expit(gv) * uv)
+    key = lambda b: np.where(b & 0x8000, -(b.astype(np.int64) & 0x7FFF), b.astype(np.int64))  # noqa: E731
+    assert np.abs(key(h) - key(ref)).max() <= 1
