@@ -24,7 +24,12 @@
 #define N_SEARCH 8000     /* section 3.2 step 6: 8,000 points on [0, 12] */
 #define N_TABLE2 20001    /* section 4.1: 20,001 points on [-Lc, Lc] */
 
-static double sigm(double x) { return 0.5 + 0.5 * tanh(0.5 * x); }
+/* sigma(x) without cancellation on either side: e = exp(-|x|) <= 1 */
+static double sigm(double x)
+{
+    const double e = exp(-fabs(x));
+    return x >= 0 ? 1.0 / (1.0 + e) : e / (1.0 + e);
+}
 static double Phi(double x) { return 0.5 * erfc(-x / sqrt(2.0)); }
 static double phi(double x) { return exp(-0.5 * x * x) / sqrt(2.0 * M_PI); }
 
@@ -42,7 +47,7 @@ double orc_ref(int func, int deriv, double x)
         switch (func) {
         case ORC_SIGMOID: return sigm(x) * sigm(-x);           /* Eq. 10 */
         case ORC_TANH: { const double c = cosh(x); return 1.0 / (c * c); }
-        case ORC_SILU:    return sigm(x) + x * sigm(x) * sigm(-x); /* Eq. 9 */
+        case ORC_SILU:    return sigm(x) * (1.0 + x * sigm(-x));   /* Eq. 9 */
         case ORC_GELU:    return Phi(x) + x * phi(x);
         }
     }
