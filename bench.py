@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-components", action="store_true", help="skip SwiGLU / attention")
     ap.add_argument("--only", default="", help="profile helper: run one kernel name only")
+    ap.add_argument("--step-only", action="store_true",
+                    help="profiling run: warm-up and timed steps, then one plain device copy "
+                         "of x (1,073,741,824 bytes moved) as the counter reference")
     return ap.parse_args()
 
 
@@ -209,6 +212,12 @@ def main():
     ms_step = total_ms / args.steps
     per = {name: statistics.mean(ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps))
            for i, (name, _, _, _) in enumerate(ks)}
+    if args.step_only:
+        y.copy_(x)      # reference kernel of known size for the traffic counters
+        torch.cuda.synchronize()
+        print(json.dumps({"step_only": True, "ms_per_step": round(ms_step, 4),
+                          "per_kernel_ms": {k: round(v, 5) for k, v in per.items()}}), flush=True)
+        return
     elems_step = N_HBM * len(ks)
     value = elems_step / (ms_step * 1e-3) / 1e9
 

@@ -20,17 +20,18 @@ HIPCC_FLAGS = [
 ]
 
 
-def source_digest() -> str:
-    """SHA-256 over the library's sources (identifies the kernels a stored
+# the sources that define the elementwise streaming kernels and their launch
+STREAM_SOURCES = ("ops.hpp", "stream.hpp", "programs.hpp", "polyact.hip")
+
+
+def source_digest(files=STREAM_SOURCES) -> str:
+    """SHA-256 over the given csrc/ files (identifies the kernels a stored
     profile was taken from)."""
     import hashlib
     h = hashlib.sha256()
-    files = sorted(os.listdir(os.path.join(PKG, "csrc")))
-    for f in files:
+    for f in sorted(files):
         with open(os.path.join(PKG, "csrc", f), "rb") as fh:
             h.update(f.encode() + b"\0" + fh.read())
-    with open(os.path.join(ROOT, "include", "polyact.h"), "rb") as fh:
-        h.update(fh.read())
     return h.hexdigest()[:16]
 
 

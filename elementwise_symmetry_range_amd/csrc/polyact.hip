@@ -17,9 +17,11 @@ using namespace pa;
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kUnroll = 4;          // 16-byte chunks in flight per thread
-constexpr int kBlocksPerCU = 8;     // persistent grid: blocks per compute unit
+constexpr int kThreads = 256;       // scalar and SwiGLU kernels
+constexpr int kMapBS = 256;         // streaming kernels: threads per block
+constexpr int kMapU = 2;            // 16-byte chunks in flight per thread
+constexpr int64_t kMaxGrid = 0x7FFFFFFF;
+constexpr int kBlocksPerCU = 8;     // scalar kernels: blocks per compute unit
 
 int cu_count()
 {
@@ -34,6 +36,13 @@ int cu_count()
         cached[dev] = n;
     }
     return cached[dev];
+}
+
+// one block per tile of tile_items work items (capped by the launch limit)
+int64_t grid_tiles(int64_t work_items, int64_t tile_items)
+{
+    const int64_t need = (work_items + tile_items - 1) / tile_items;
+    return need < 1 ? 1 : (need < kMaxGrid ? need : kMaxGrid);
 }
 
 int64_t grid_for(int64_t work_items, int per_thread)
@@ -125,8 +134,8 @@ pa_status run_map1(const void *x, void *y, int64_t n, hipStream_t st, const Op &
     const uint16_t *xs = (const uint16_t *)x;
     uint16_t *ys = (uint16_t *)y;
     if (sp.nvec > 0) {
-        const int64_t grid = grid_for(sp.nvec, kUnroll);
-        hipLaunchKernelGGL((k_map1<Op, kUnroll, true>), dim3((unsigned)grid), dim3(kThreads), 0, st,
+        const int64_t grid = grid_tiles(sp.nvec, (int64_t)kMapBS * kMapU);
+        hipLaunchKernelGGL((k_map1<Op, kMapBS, kMapU>), dim3((unsigned)grid), dim3(kMapBS), 0, st,
                            (const u32x4 *)(xs + sp.head), (u32x4 *)(ys + sp.head), sp.nvec, op);
         if (launched() != PA_OK) return PA_ERR_LAUNCH;
     }
@@ -146,8 +155,8 @@ pa_status run_map2(const void *x, const void *g, void *y, int64_t n, hipStream_t
     const uint16_t *xs = (const uint16_t *)x, *gs = (const uint16_t *)g;
     uint16_t *ys = (uint16_t *)y;
     if (sp.nvec > 0) {
-        const int64_t grid = grid_for(sp.nvec, kUnroll);
-        hipLaunchKernelGGL((k_map2<Op, kUnroll, true>), dim3((unsigned)grid), dim3(kThreads), 0, st,
+        const int64_t grid = grid_tiles(sp.nvec, (int64_t)kMapBS * kMapU);
+        hipLaunchKernelGGL((k_map2<Op, kMapBS, kMapU>), dim3((unsigned)grid), dim3(kMapBS), 0, st,
                            (const u32x4 *)(xs + sp.head), (const u32x4 *)(gs + sp.head),
                            (u32x4 *)(ys + sp.head), sp.nvec, op);
         if (launched() != PA_OK) return PA_ERR_LAUNCH;
@@ -237,13 +246,13 @@ template <class Op>
 pa_status swiglu_fwd_launch(const SwiArgs &a, hipStream_t st, const Op &op)
 {
     if (vec_ok(a, false)) {
-        const int64_t grid = grid_for(a.rows * (a.cols / 8), kUnroll);
+        const int64_t grid = grid_tiles(a.rows * (a.cols / 8), (int64_t)kMapBS * kMapU);
         if (flat(a, false))
-            hipLaunchKernelGGL((k_swiglu_fwd_vec<Op, kUnroll, true>), dim3((unsigned)grid),
-                               dim3(kThreads), 0, st, a, op);
+            hipLaunchKernelGGL((k_swiglu_fwd_vec<Op, kMapBS, kMapU, true>), dim3((unsigned)grid),
+                               dim3(kMapBS), 0, st, a, op);
         else
-            hipLaunchKernelGGL((k_swiglu_fwd_vec<Op, kUnroll, false>), dim3((unsigned)grid),
-                               dim3(kThreads), 0, st, a, op);
+            hipLaunchKernelGGL((k_swiglu_fwd_vec<Op, kMapBS, kMapU, false>), dim3((unsigned)grid),
+                               dim3(kMapBS), 0, st, a, op);
     } else {
         hipLaunchKernelGGL((k_swiglu_fwd_scalar<Op>), dim3((unsigned)grid_for(a.rows * a.cols, 1)),
                            dim3(kThreads), 0, st, a, op);
@@ -254,15 +263,14 @@ pa_status swiglu_fwd_launch(const SwiArgs &a, hipStream_t st, const Op &op)
 template <class Op>
 pa_status swiglu_bwd_launch(const SwiArgs &a, hipStream_t st, const Op &op)
 {
-    constexpr int U = 2;
     if (vec_ok(a, true)) {
-        const int64_t grid = grid_for(a.rows * (a.cols / 8), U);
+        const int64_t grid = grid_tiles(a.rows * (a.cols / 8), (int64_t)kMapBS * kMapU);
         if (flat(a, true))
-            hipLaunchKernelGGL((k_swiglu_bwd_vec<Op, U, true>), dim3((unsigned)grid),
-                               dim3(kThreads), 0, st, a, op);
+            hipLaunchKernelGGL((k_swiglu_bwd_vec<Op, kMapBS, kMapU, true>), dim3((unsigned)grid),
+                               dim3(kMapBS), 0, st, a, op);
         else
-            hipLaunchKernelGGL((k_swiglu_bwd_vec<Op, U, false>), dim3((unsigned)grid),
-                               dim3(kThreads), 0, st, a, op);
+            hipLaunchKernelGGL((k_swiglu_bwd_vec<Op, kMapBS, kMapU, false>), dim3((unsigned)grid),
+                               dim3(kMapBS), 0, st, a, op);
     } else {
         hipLaunchKernelGGL((k_swiglu_bwd_scalar<Op>), dim3((unsigned)grid_for(a.rows * a.cols, 1)),
                            dim3(kThreads), 0, st, a, op);

@@ -5,9 +5,8 @@
 // analogue of the paper's one-int4-chunk-per-thread packed path ("Fast
 // Polynomial Transcendentals for LLMs", section 3.4).  Each thread keeps U
 // independent chunks in flight (loads issued first, then compute, then
-// stores) and walks the array with a grid stride, so a grid of a few blocks
-// per compute unit covers any size.  No LDS, no MFMA: the work is bound by
-// HBM bandwidth (4 bytes per element forward, 6 backward).
+// stores).  No LDS, no MFMA: the work is bound by HBM bandwidth (4 bytes per
+// element forward, 6 backward).
 //
 // A scalar kernel handles the elements outside the 16-byte-aligned middle
 // (a misaligned head and a ragged tail), one element per thread, by feeding
@@ -51,40 +50,56 @@ __device__ __forceinline__ u32x4 map4(const Op &op, u32x4 a, u32x4 b)
     return r;
 }
 
-// y[i] = op(x[i]) over nvec 16-byte chunks.
-template <class Op, int U, bool NT>
-__global__ __launch_bounds__(256) void k_map1(const u32x4 *x, u32x4 *y, int64_t nvec, Op op)
+// Tiling.  Block b owns the tile of BS * U consecutive 16-byte chunks
+// starting at b * BS * U; chunk t0 + u * BS + threadIdx.x is thread
+// threadIdx.x's u-th chunk, so every load and store instruction of a wave
+// covers 1 KiB of contiguous memory.  The grid is one block per tile (no
+// persistent loop): blocks are spread round-robin over the eight XCDs, which
+// interleaves neighbouring tiles across the whole memory system.  Measured on
+// MI355X this beats a persistent grid-stride walk and an XCD-contiguous
+// block order by 10-25 %.  Loads and stores are nontemporal: each byte is
+// touched once.  The loop only runs again for grids capped by the launch
+// limit.
+template <class Op, int BS, int U>
+__global__ __launch_bounds__(BS) void k_map1(const u32x4 *x, u32x4 *y, int64_t nvec, Op op)
 {
-    const int64_t stride = (int64_t)gridDim.x * 256;
-    int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    for (; i + (U - 1) * stride < nvec; i += U * stride) {
+    const int64_t tile = (int64_t)BS * U;
+    for (int64_t t0 = (int64_t)blockIdx.x * tile; t0 < nvec; t0 += (int64_t)gridDim.x * tile) {
         u32x4 v[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) v[u] = ld16<NT>(x + i + u * stride);
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = t0 + u * BS + threadIdx.x;
+            if (i < nvec) v[u] = ld16<true>(x + i);
+        }
 #pragma unroll
-        for (int u = 0; u < U; ++u) st16<NT>(y + i + u * stride, map4(op, v[u]));
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = t0 + u * BS + threadIdx.x;
+            if (i < nvec) st16<true>(y + i, map4(op, v[u]));
+        }
     }
-    for (; i < nvec; i += stride) st16<NT>(y + i, map4(op, ld16<NT>(x + i)));
 }
 
-// y[i] = op(x[i], g[i]) over nvec 16-byte chunks.
-template <class Op, int U, bool NT>
-__global__ __launch_bounds__(256) void k_map2(const u32x4 *x, const u32x4 *g, u32x4 *y,
-                                              int64_t nvec, Op op)
+template <class Op, int BS, int U>
+__global__ __launch_bounds__(BS) void k_map2(const u32x4 *x, const u32x4 *g, u32x4 *y,
+                                             int64_t nvec, Op op)
 {
-    const int64_t stride = (int64_t)gridDim.x * 256;
-    int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    for (; i + (U - 1) * stride < nvec; i += U * stride) {
+    const int64_t tile = (int64_t)BS * U;
+    for (int64_t t0 = (int64_t)blockIdx.x * tile; t0 < nvec; t0 += (int64_t)gridDim.x * tile) {
         u32x4 a[U], b[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            a[u] = ld16<NT>(x + i + u * stride);
-            b[u] = ld16<NT>(g + i + u * stride);
+            const int64_t i = t0 + u * BS + threadIdx.x;
+            if (i < nvec) {
+                a[u] = ld16<true>(x + i);
+                b[u] = ld16<true>(g + i);
+            }
         }
 #pragma unroll
-        for (int u = 0; u < U; ++u) st16<NT>(y + i + u * stride, map4(op, a[u], b[u]));
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = t0 + u * BS + threadIdx.x;
+            if (i < nvec) st16<true>(y + i, map4(op, a[u], b[u]));
+        }
     }
-    for (; i < nvec; i += stride) st16<NT>(y + i, map4(op, ld16<NT>(x + i), ld16<NT>(g + i)));
 }
 
 // Elements [a0, a1) and [b0, b1), one per thread.

@@ -122,34 +122,34 @@ __device__ __forceinline__ int64_t chunk_elem(int64_t r0, int64_t c, int64_t cpr
     }
 }
 
-template <class Op, int U, bool FLAT>
-__global__ __launch_bounds__(256) void k_swiglu_fwd_vec(SwiArgs a, Op op)
+// One block per tile of BS * U chunks of the selected rows (the tiling of the
+// streaming kernels); the host sizes the grid for the capacity `rows`, and
+// blocks past the device-side row range exit at once.
+template <class Op, int BS, int U, bool FLAT>
+__global__ __launch_bounds__(BS) void k_swiglu_fwd_vec(SwiArgs a, Op op)
 {
     int64_t r0, r1;
     row_range(a, r0, r1);
     const int64_t cpr = a.cols >> 3;
     const int64_t n = (r1 - r0) * cpr;
-    const int64_t stride = (int64_t)gridDim.x * 256;
-    int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    for (; i + (U - 1) * stride < n; i += U * stride) {
+    const int64_t tile = (int64_t)BS * U;
+    for (int64_t t0 = (int64_t)blockIdx.x * tile; t0 < n; t0 += (int64_t)gridDim.x * tile) {
         u32x4 g[U], u[U];
 #pragma unroll
         for (int k = 0; k < U; ++k) {
-            const int64_t c = i + k * stride;
-            g[k] = ld16<true>((const u32x4 *)(a.g + chunk_elem<FLAT>(r0, c, cpr, a.ld_g, a.cols)));
-            u[k] = ld16<true>((const u32x4 *)(a.u + chunk_elem<FLAT>(r0, c, cpr, a.ld_u, a.cols)));
+            const int64_t c = t0 + k * BS + threadIdx.x;
+            if (c < n) {
+                g[k] = ld16<true>((const u32x4 *)(a.g + chunk_elem<FLAT>(r0, c, cpr, a.ld_g, a.cols)));
+                u[k] = ld16<true>((const u32x4 *)(a.u + chunk_elem<FLAT>(r0, c, cpr, a.ld_u, a.cols)));
+            }
         }
 #pragma unroll
         for (int k = 0; k < U; ++k) {
-            const int64_t c = i + k * stride;
-            st16<true>((u32x4 *)(a.h + chunk_elem<FLAT>(r0, c, cpr, a.ld_h, a.cols)),
-                       map4(op, g[k], u[k]));
+            const int64_t c = t0 + k * BS + threadIdx.x;
+            if (c < n)
+                st16<true>((u32x4 *)(a.h + chunk_elem<FLAT>(r0, c, cpr, a.ld_h, a.cols)),
+                           map4(op, g[k], u[k]));
         }
-    }
-    for (; i < n; i += stride) {
-        const u32x4 g = ld16<true>((const u32x4 *)(a.g + chunk_elem<FLAT>(r0, i, cpr, a.ld_g, a.cols)));
-        const u32x4 u = ld16<true>((const u32x4 *)(a.u + chunk_elem<FLAT>(r0, i, cpr, a.ld_u, a.cols)));
-        st16<true>((u32x4 *)(a.h + chunk_elem<FLAT>(r0, i, cpr, a.ld_h, a.cols)), map4(op, g, u));
     }
 }
 
@@ -164,41 +164,35 @@ __device__ __forceinline__ void bwd_chunk(const Op &op, u32x4 g, u32x4 u, u32x4 
     du = u32x4{b[0], b[1], b[2], b[3]};
 }
 
-template <class Op, int U, bool FLAT>
-__global__ __launch_bounds__(256) void k_swiglu_bwd_vec(SwiArgs a, Op op)
+template <class Op, int BS, int U, bool FLAT>
+__global__ __launch_bounds__(BS) void k_swiglu_bwd_vec(SwiArgs a, Op op)
 {
     int64_t r0, r1;
     row_range(a, r0, r1);
     const int64_t cpr = a.cols >> 3;
     const int64_t n = (r1 - r0) * cpr;
-    const int64_t stride = (int64_t)gridDim.x * 256;
-    int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    for (; i + (U - 1) * stride < n; i += U * stride) {
+    const int64_t tile = (int64_t)BS * U;
+    for (int64_t t0 = (int64_t)blockIdx.x * tile; t0 < n; t0 += (int64_t)gridDim.x * tile) {
         u32x4 g[U], u[U], d[U];
 #pragma unroll
         for (int k = 0; k < U; ++k) {
-            const int64_t c = i + k * stride;
-            g[k] = ld16<true>((const u32x4 *)(a.g + chunk_elem<FLAT>(r0, c, cpr, a.ld_g, a.cols)));
-            u[k] = ld16<true>((const u32x4 *)(a.u + chunk_elem<FLAT>(r0, c, cpr, a.ld_u, a.cols)));
-            d[k] = ld16<true>((const u32x4 *)(a.dh + chunk_elem<FLAT>(r0, c, cpr, a.ld_dh, a.cols)));
+            const int64_t c = t0 + k * BS + threadIdx.x;
+            if (c < n) {
+                g[k] = ld16<true>((const u32x4 *)(a.g + chunk_elem<FLAT>(r0, c, cpr, a.ld_g, a.cols)));
+                u[k] = ld16<true>((const u32x4 *)(a.u + chunk_elem<FLAT>(r0, c, cpr, a.ld_u, a.cols)));
+                d[k] = ld16<true>((const u32x4 *)(a.dh + chunk_elem<FLAT>(r0, c, cpr, a.ld_dh, a.cols)));
+            }
         }
 #pragma unroll
         for (int k = 0; k < U; ++k) {
-            const int64_t c = i + k * stride;
-            u32x4 dg, du;
-            bwd_chunk(op, g[k], u[k], d[k], dg, du);
-            st16<true>((u32x4 *)(a.dg + chunk_elem<FLAT>(r0, c, cpr, a.ld_dg, a.cols)), dg);
-            st16<true>((u32x4 *)(a.du + chunk_elem<FLAT>(r0, c, cpr, a.ld_du, a.cols)), du);
+            const int64_t c = t0 + k * BS + threadIdx.x;
+            if (c < n) {
+                u32x4 dg, du;
+                bwd_chunk(op, g[k], u[k], d[k], dg, du);
+                st16<true>((u32x4 *)(a.dg + chunk_elem<FLAT>(r0, c, cpr, a.ld_dg, a.cols)), dg);
+                st16<true>((u32x4 *)(a.du + chunk_elem<FLAT>(r0, c, cpr, a.ld_du, a.cols)), du);
+            }
         }
-    }
-    for (; i < n; i += stride) {
-        const u32x4 g = ld16<true>((const u32x4 *)(a.g + chunk_elem<FLAT>(r0, i, cpr, a.ld_g, a.cols)));
-        const u32x4 u = ld16<true>((const u32x4 *)(a.u + chunk_elem<FLAT>(r0, i, cpr, a.ld_u, a.cols)));
-        const u32x4 d = ld16<true>((const u32x4 *)(a.dh + chunk_elem<FLAT>(r0, i, cpr, a.ld_dh, a.cols)));
-        u32x4 dg, du;
-        bwd_chunk(op, g, u, d, dg, du);
-        st16<true>((u32x4 *)(a.dg + chunk_elem<FLAT>(r0, i, cpr, a.ld_dg, a.cols)), dg);
-        st16<true>((u32x4 *)(a.du + chunk_elem<FLAT>(r0, i, cpr, a.ld_du, a.cols)), du);
     }
 }
 
