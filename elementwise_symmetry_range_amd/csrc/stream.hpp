@@ -55,7 +55,8 @@ __device__ __forceinline__ u32x4 map4(const Op &op, u32x4 a, u32x4 b)
 // threadIdx.x's u-th chunk, so every load and store instruction of a wave
 // covers 1 KiB of contiguous memory.  The grid is one block per tile (no
 // persistent loop): blocks are spread round-robin over the eight XCDs, which
-// interleaves neighbouring tiles across the whole memory system.  Measured on
+// interleaves neighbouring tiles across the whole memory system, and the
+// occupancy of many small blocks keeps the loads in flight.  Measured on
 // MI355X this beats a persistent grid-stride walk and an XCD-contiguous
 // block order by 10-25 %.  Loads and stores are nontemporal: each byte is
 // touched once.  The loop only runs again for grids capped by the launch
