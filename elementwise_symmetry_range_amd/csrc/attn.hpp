@@ -16,9 +16,11 @@
 //   tiles of 64 rows go from HBM straight into LDS with global_load_lds_dwordx4
 //   (no register staging), double buffered with one barrier per tile: tile
 //   kt + 1 streams in while tile kt is consumed.  Rows are 256 B with the
-//   16-byte chunks XOR-swizzled by row (chunk c of row r sits at slot
-//   c ^ f(r), f(r) = 2 (r mod 8) + (r / 8 mod 2)), which keeps the K reads and
-//   the transposed V reads below free of bank conflicts.
+//   16-byte chunks XOR-swizzled by row: chunk c of row r sits at slot
+//   c ^ f(r), f(r) = 4 (r mod 4) + (r / 4 mod 4).  The K reads (16 lanes =
+//   16 consecutive rows, one chunk) and the transposed V reads (a half-wave =
+//   4 consecutive rows x 4 consecutive chunks) then each touch 16 distinct
+//   slots, i.e. all 64 banks once.
 //   S^T = K Q^T on v_mfma_f32_32x32x16_bf16: A = K rows from LDS, B = Q held
 //   in registers; the accumulator gives every lane one query (column) and 16
 //   keys of each 32-key block, so the softmax row reductions need only a
@@ -36,6 +38,8 @@
 //   almost every tile and the result is unchanged up to rounding.  P is
 //   rounded to BF16 for the MFMA, O^T accumulated in FP32, O = O^T / l.
 #pragma once
+#include <type_traits>
+
 #include "ops.hpp"
 
 namespace pa {
@@ -64,7 +68,7 @@ struct AttnArgs {
 __device__ __forceinline__ bf16x8 ld_bf16x8(const uint16_t *p) { return *(const bf16x8 *)p; }
 
 // slot of 16-byte chunk c of LDS row r (rows are 256 B, 16 chunks)
-__device__ __forceinline__ int swz(int r, int c) { return c ^ (((r & 7) << 1) | ((r >> 3) & 1)); }
+__device__ __forceinline__ int swz(int r, int c) { return c ^ (((r & 3) << 2) | ((r >> 2) & 3)); }
 
 __device__ __forceinline__ u32x2 ds_read_tr16(const uint16_t *p)
 {
@@ -135,15 +139,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     };
 
     load_tile(0, 0);
-    for (int kt = 0; kt < nkt; ++kt) {
-        const int buf = kt & 1;
+    // One tile; BUF is the LDS buffer holding it (a constant: the loop below
+    // is unrolled by two so that buffer bases become immediate offsets).
+    auto tile = [&](int kt, auto bufc) {
+        constexpr int buf = decltype(bufc)::value;
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's share of tile kt landed
         __syncthreads();   // all of tile kt landed; nobody reads buffer buf ^ 1 any more
         if (kt + 1 < nkt) load_tile(kt + 1, buf ^ 1);
 
         const int key0 = kt * AT_BN;
-        if (a.causal && key0 > q0 + 31) continue;   // tile entirely above this wave's rows
-        if (q0 >= S) continue;
+        if (a.causal && key0 > q0 + 31) return;   // tile entirely above this wave's rows
+        if (q0 >= S) return;
         const uint16_t *Kb = Ks[buf];
         const uint16_t *Vb = Vs[buf];
 
@@ -161,46 +167,61 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
 
         // ---- score transform: t = tanh(x), z = t * cap * log2(e) ------------
-        // s[kb][j*4 + i] is the score of key key0 + kb*32 + j*8 + h*4 + i
+        // s[kb][j*4 + i] is the score of key key0 + kb*32 + j*8 + h*4 + i.
+        // Masked keys (beyond the query, or beyond S) get t = -inf.  Tiles
+        // that need no mask (all but the diagonal and the ragged end) take a
+        // branch-free pass without the key arithmetic.
         const bool need_mask = (a.causal && key0 + AT_BN - 1 > q0) || key0 + AT_BN > S;
+        const int lim = a.causal ? (my_q < S - 1 ? my_q : S - 1) : S - 1;   // last visible key
         float tmax;
-        if constexpr (POLY) {
-            uint32_t mx = 0xFC00FC00u;   // packed FP16 -inf
+        auto transform = [&](auto masked) {
+            constexpr bool MASKED = decltype(masked)::value;
+            if constexpr (POLY) {
+                uint32_t mx = 0xFC00FC00u;   // packed FP16 -inf
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
+                for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-                for (int e = 0; e < 16; e += 2) {
-                    const uint32_t xw = pack_f16(s[kb][e] * a.scale, s[kb][e + 1] * a.scale);
-                    const uint32_t aw = xw & 0x7FFF7FFFu;
-                    const h2 v = horner_f16<4, true>(bc<h2>(min_u16x2(aw, a.tanh16.lc)), a.tanh16);
-                    uint32_t w = bc<uint32_t>(v) ^ (xw ^ aw);
-                    if (need_mask) {
-                        const int k0 = key0 + kb * 32 + (e >> 2) * 8 + h * 4 + (e & 3);
-                        if ((a.causal && k0 > my_q) || k0 >= S) w = (w & 0xFFFF0000u) | 0xFC00u;
-                        if ((a.causal && k0 + 1 > my_q) || k0 + 1 >= S) w = (w & 0xFFFFu) | 0xFC000000u;
+                    for (int e = 0; e < 16; e += 2) {
+                        // x = RN_f16(s * scale): the FP32 product rounded once to
+                        // FP16 equals RN_f16(RN_f32(s * scale)) (24 >= 2 * 11 + 2)
+                        h2 xh;
+                        xh[0] = (_Float16)fmaf(s[kb][e], a.scale, -0.0f);
+                        xh[1] = (_Float16)fmaf(s[kb][e + 1], a.scale, -0.0f);
+                        const uint32_t xw = bc<uint32_t>(xh);
+                        const uint32_t aw = xw & 0x7FFF7FFFu;
+                        const h2 v = horner_f16<4, true>(bc<h2>(min_u16x2(aw, a.tanh16.lc)), a.tanh16);
+                        uint32_t w = bc<uint32_t>(v) ^ (xw ^ aw);
+                        if constexpr (MASKED) {
+                            const int k0 = key0 + kb * 32 + (e >> 2) * 8 + h * 4 + (e & 3);
+                            const uint32_t mlo = k0 > lim ? 0x0000FFFFu : 0u;
+                            const uint32_t mhi = k0 + 1 > lim ? 0xFFFF0000u : 0u;
+                            w = sel(mlo | mhi, 0xFC00FC00u, w);
+                        }
+                        mx = bc<uint32_t>(__builtin_elementwise_max(bc<h2>(mx), bc<h2>(w)));
+                        s[kb][e] = f16_lo(w);
+                        s[kb][e + 1] = f16_hi(w);
                     }
-                    mx = bc<uint32_t>(__builtin_elementwise_max(bc<h2>(mx), bc<h2>(w)));
-                    s[kb][e] = f16_lo(w);
-                    s[kb][e + 1] = f16_hi(w);
+                }
+                tmax = fmaxf(f16_lo(mx), f16_hi(mx));
+            } else {
+                tmax = -INFINITY;
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        float t = tanhf(s[kb][e] * a.scale);
+                        if constexpr (MASKED) {
+                            const int k0 = key0 + kb * 32 + (e >> 2) * 8 + h * 4 + (e & 3);
+                            t = k0 > lim ? -INFINITY : t;
+                        }
+                        s[kb][e] = t;
+                        tmax = fmaxf(tmax, t);
+                    }
                 }
             }
-            tmax = fmaxf(f16_lo(mx), f16_hi(mx));
-        } else {
-            tmax = -INFINITY;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    float t = tanhf(s[kb][e] * a.scale);
-                    if (need_mask) {
-                        const int k0 = key0 + kb * 32 + (e >> 2) * 8 + h * 4 + (e & 3);
-                        if ((a.causal && k0 > my_q) || k0 >= S) t = -INFINITY;
-                    }
-                    s[kb][e] = t;
-                    tmax = fmaxf(tmax, t);
-                }
-            }
-        }
+        };
+        if (need_mask) transform(std::true_type{});
+        else transform(std::false_type{});
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
         const float zmax = tmax * a.c2;
 
@@ -247,6 +268,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bc<bf16x8>(av), pf[ks], o[db], 0, 0, 0);
             }
         }
+    };
+    for (int kt = 0; kt < nkt; kt += 2) {
+        tile(kt, std::integral_constant<int, 0>{});
+        if (kt + 1 < nkt) tile(kt + 1, std::integral_constant<int, 1>{});
     }
 
     if (my_q >= S) return;
