@@ -240,6 +240,14 @@ def main():
                         "pct_hbm": round(100 * by * N_HBM / tp / 1e6 / HBM_PEAK_GBS, 1),
                         "native_gelem_s": round(N_HBM / tn / 1e6, 1),
                         "speedup_vs_accurate": round(tn / tp, 3)}
+    for f in ("silu", "gelu"):   # centered-odd derivative programs (not in the step)
+        tp, tn = alternating(torch, lambda f=f: pa.poly_act_bwd(x, g, f, out=y),
+                             lambda f=f: pa.native_act_bwd(x, g, f, "native", out=y), 10,
+                             args.rounds)
+        detail[f"{f}_bwd"] = {"poly_gelem_s": round(N_HBM / tp / 1e6, 1),
+                              "pct_hbm": round(100 * 6 * N_HBM / tp / 1e6 / HBM_PEAK_GBS, 1),
+                              "native_gelem_s": round(N_HBM / tn / 1e6, 1),
+                              "speedup_vs_accurate": round(tn / tp, 3), "in_step": False}
     for f in BWD:   # the paper's native backward consumes the saved y
         yy = pa.native_act_fwd(x, f)
         tp = time_calls(torch, lambda f=f: pa.poly_act_bwd(x, g, f, out=y), 10)

@@ -10,6 +10,8 @@
 //   tanh     y = v xor sign(x)                                   section 3.1
 //   SiLU/GELU y = fma(t, v, x * 1/2), t unclamped               Eqs. 4-6
 //   sigmoid', tanh' (direct fits, even)  dx = g * v             section 3.3
+//   SiLU', GELU' (direct fits, centered odd)
+//            dx = g * (1/2 + (v xor sign(x)))                      Eq. 9
 //
 // FP16: one v_pk_fma_f16 / v_pk_mul_f16 / v_pk_add_f16 per stage for both
 // lanes (IEEE single rounding).  BF16: gfx950 has no packed BF16 FMA, so each
@@ -136,6 +138,20 @@ struct PolyBwdF16 {   // even direct-derivative program, dx = g * q(t^)
     }
 };
 
+template <int D>
+struct PolyBwdOddF16 {   // centered-odd direct-derivative program, dx = g (1/2 + sign q)
+    CoefF16 k;
+    __device__ __forceinline__ uint32_t operator()(uint32_t xw, uint32_t gw) const
+    {
+        const uint32_t aw = xw & 0x7FFF7FFFu;
+        const h2 v = horner_f16<D, true>(bc<h2>(min_u16x2(aw, k.lc)), k);
+        const h2 ds = bc<h2>(0x38003800u) + bc<h2>(bc<uint32_t>(v) ^ (xw ^ aw));
+        uint32_t y = bc<uint32_t>(bc<h2>(gw) * ds);
+        y = sel(nan_mask_f16(gw & 0x7FFF7FFFu), gw | 0x02000200u, y);
+        return sel(nan_mask_f16(aw), xw | 0x02000200u, y);
+    }
+};
+
 // ---- BF16 programs ----------------------------------------------------------
 // Returns the packed BF16 Horner value for the two lanes' clamped |x|.
 template <int D, bool C0_ZERO>
@@ -204,6 +220,23 @@ struct PolyBwdBF16 {
     }
 };
 
+template <int D>
+struct PolyBwdOddBF16 {
+    CoefBF16 k;
+    __device__ __forceinline__ uint32_t operator()(uint32_t xw, uint32_t gw) const
+    {
+        const uint32_t aw = xw & 0x7FFF7FFFu;
+        const uint32_t a0 = aw << 16, a1 = aw & 0xFFFF0000u;
+        const float t0 = bc<float>(a0 < k.lc ? a0 : k.lc);
+        const float t1 = bc<float>(a1 < k.lc ? a1 : k.lc);
+        const uint32_t r = horner_bf16<D, true>(t0, t1, k) ^ (xw ^ aw);
+        const uint32_t ds = pack_bf(0.5f + lo_f(r), 0.5f + hi_f(r));
+        uint32_t y = pack_bf(lo_f(gw) * lo_f(ds), hi_f(gw) * hi_f(ds));
+        y = sel(nan_mask_bf16(gw & 0x7FFF7FFFu), gw | 0x00400040u, y);
+        return sel(nan_mask_bf16(aw), xw | 0x00400040u, y);
+    }
+};
+
 // ---- accurate FP32 comparators ---------------------------------------------
 // expf / tanhf / erfcf are the device library's accurate routines (no
 // fast-math); 1.0f / d is the IEEE correctly rounded divide.
@@ -237,10 +270,19 @@ __device__ __forceinline__ float native_bwd(float xy, float g)
             const float e = expf(-fabsf(xy));
             const float r = 1.0f / (1.0f + e);
             return g * (e * r * r);
-        } else {                              // tanh' = 4 e / (1 + e)^2, e = exp(-2|x|)
+        } else if constexpr (FUNC == F_TANH) {   // tanh' = 4 e / (1 + e)^2, e = exp(-2|x|)
             const float e = expf(-2.0f * fabsf(xy));
             const float r = 1.0f / (1.0f + e);
             return g * (4.0f * e * r * r);
+        } else if constexpr (FUNC == F_SILU) {   // s' = sigma (1 + x (1 - sigma))
+            const float e = expf(-fabsf(xy));
+            const float r = 1.0f / (1.0f + e);
+            const float sg = xy >= 0.0f ? r : e * r;     // sigma(x)
+            const float sn = xy >= 0.0f ? e * r : r;     // 1 - sigma(x) = sigma(-x)
+            return g * (sg * fmaf(xy, sn, 1.0f));
+        } else {                                 // GELU' = Phi(x) + x phi(x)
+            const float phi = expf(-0.5f * xy * xy) * 0.39894228040143267794f;
+            return g * fmaf(xy, phi, 0.5f * erfcf(-xy * 0.70710678118654752440f));
         }
     }
 }

@@ -421,10 +421,22 @@ pa_status poly_act_bwd(pa_func f, pa_dtype t, const void *x, const void *dy, voi
     pa_status s = check_binary(t, x, dy, dx, n);
     if (s != PA_OK) return s;
     const ProgramDef *p = find_program((int)f, 1);
-    if (!p || p->degree != 4) return PA_ERR_FUNC;
+    if (!p) return PA_ERR_FUNC;
     if (n == 0) return PA_OK;
-    if (t == PA_F16) return run_map2(x, dy, dx, n, stream, PolyBwdF16<4>{coef_f16(*p)});
-    return run_map2(x, dy, dx, n, stream, PolyBwdBF16<4>{coef_bf16(*p)});
+    const bool h = t == PA_F16;
+    switch (f) {
+    case PA_SIGMOID:
+    case PA_TANH:   // even direct fits, D4
+        return h ? run_map2(x, dy, dx, n, stream, PolyBwdF16<4>{coef_f16(*p)})
+                 : run_map2(x, dy, dx, n, stream, PolyBwdBF16<4>{coef_bf16(*p)});
+    case PA_SILU:   // centered-odd direct fit, D3
+        return h ? run_map2(x, dy, dx, n, stream, PolyBwdOddF16<3>{coef_f16(*p)})
+                 : run_map2(x, dy, dx, n, stream, PolyBwdOddBF16<3>{coef_bf16(*p)});
+    case PA_GELU:   // centered-odd direct fit, D5
+        return h ? run_map2(x, dy, dx, n, stream, PolyBwdOddF16<5>{coef_f16(*p)})
+                 : run_map2(x, dy, dx, n, stream, PolyBwdOddBF16<5>{coef_bf16(*p)});
+    }
+    return PA_ERR_FUNC;
 }
 
 pa_status native_act_fwd(pa_func f, pa_dtype t, const void *x, void *y, int64_t n,
@@ -458,14 +470,21 @@ pa_status native_act_bwd(pa_impl impl, pa_func f, pa_dtype t, const void *x_or_y
     pa_status s = check_binary(t, x_or_y, dy, dx, n);
     if (s != PA_OK) return s;
     if (impl != PA_IMPL_NATIVE && impl != PA_IMPL_NATIVE_FROM_Y) return PA_ERR_FUNC;
-    if (f != PA_SIGMOID && f != PA_TANH) return PA_ERR_FUNC;
-    if (n == 0) return PA_OK;
+    if (f < PA_SIGMOID || f > PA_GELU) return PA_ERR_FUNC;
     const bool from_y = impl == PA_IMPL_NATIVE_FROM_Y;
-    if (f == PA_SIGMOID)
+    if (from_y && f != PA_SIGMOID && f != PA_TANH) return PA_ERR_FUNC;   // no rule from y
+    if (n == 0) return PA_OK;
+    switch (f) {
+    case PA_SIGMOID:
         return from_y ? native_bwd_dispatch<F_SIGMOID, true>(t, x_or_y, dy, dx, n, stream)
                       : native_bwd_dispatch<F_SIGMOID, false>(t, x_or_y, dy, dx, n, stream);
-    return from_y ? native_bwd_dispatch<F_TANH, true>(t, x_or_y, dy, dx, n, stream)
-                  : native_bwd_dispatch<F_TANH, false>(t, x_or_y, dy, dx, n, stream);
+    case PA_TANH:
+        return from_y ? native_bwd_dispatch<F_TANH, true>(t, x_or_y, dy, dx, n, stream)
+                      : native_bwd_dispatch<F_TANH, false>(t, x_or_y, dy, dx, n, stream);
+    case PA_SILU: return native_bwd_dispatch<F_SILU, false>(t, x_or_y, dy, dx, n, stream);
+    case PA_GELU: return native_bwd_dispatch<F_GELU, false>(t, x_or_y, dy, dx, n, stream);
+    }
+    return PA_ERR_FUNC;
 }
 
 pa_status poly_swiglu_fwd(pa_dtype t, const void *gate, const void *up, void *h, int64_t rows,

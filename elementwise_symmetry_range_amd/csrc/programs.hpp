@@ -14,6 +14,8 @@
 //   GELU    fwd D5  x/2 + t p(t^), p fitted to Phi(t) - 1/2
 //   sigmoid' D4     q(t^), direct derivative fit (even), c_0 = 1/4
 //   tanh'    D4     q(t^), direct derivative fit (even), c_0 = 1
+//   SiLU'    D3     1/2 + sign(x) q(t^), direct fit of s'(t) - 1/2 (odd, Eq. 9)
+//   GELU'    D5     1/2 + sign(x) q(t^), the same construction for Phi + x phi
 //
 // The test suite re-derives every entry with an independent CPU fitter and
 // checks the values returned by poly_program_info against it.
@@ -37,6 +39,8 @@ constexpr ProgramDef kPrograms[] = {
     {4, 0, 5, 3.75f, 2.75f, {0x0000, 0x3ECF, 0xBBEE, 0xBDA5, 0x3CDB, 0xBB2C}},
     {1, 1, 4, 4.75f, 4.75f, {0x3E80, 0xBB79, 0xBD8F, 0x3CB3, 0xBB00}},
     {2, 1, 4, 2.75f, 2.75f, {0x3F80, 0xBDE3, 0xBF65, 0x3F08, 0xBDB2}},
+    {3, 1, 3, 3.75f, 4.25f, {0x0000, 0x3F17, 0xBE3E, 0x3C93}},
+    {4, 1, 5, 4.25f, 2.75f, {0x0000, 0x3F6D, 0xBEB8, 0xBCD5, 0x3D05, 0xBB84}},
 };
 
 constexpr int kNumPrograms = sizeof(kPrograms) / sizeof(kPrograms[0]);

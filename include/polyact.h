@@ -104,9 +104,11 @@ typedef struct {
 pa_status poly_act_fwd(pa_func f, pa_dtype t, const void *x, void *y, int64_t n,
                        hipStream_t stream);
 
-/* dx[i] = dy[i] * q(x[i]) with the direct D4 derivative fit q of f (even in
- * x), evaluated from x.  f = PA_SIGMOID or PA_TANH.  Paper: section 3.3
- * (direct derivative fits), section 4.2 (backward from x), Table 3. */
+/* dx[i] = dy[i] * f~'(x[i]) with the direct derivative fit of f, evaluated
+ * from x.  f = PA_SIGMOID or PA_TANH: an even D4 polynomial q(t^) (section
+ * 3.3; section 4.2 backward from x; Table 3).  f = PA_SILU (D3) or PA_GELU
+ * (D5): the centered-odd form 1/2 + sign(x) q(t^), which keeps
+ * f~'(x) + f~'(-x) = 1 (Eq. 9); dx = RN(dy * RN(1/2 + (q xor sign))). */
 pa_status poly_act_bwd(pa_func f, pa_dtype t, const void *x, const void *dy,
                        void *dx, int64_t n, hipStream_t stream);
 
@@ -158,8 +160,9 @@ pa_status native_act_fwd(pa_func f, pa_dtype t, const void *x, void *y, int64_t 
                          hipStream_t stream);
 
 /* Backward comparators.  impl = PA_IMPL_NATIVE: x_or_y is x and the derivative
- * is recomputed accurately from x; impl = PA_IMPL_NATIVE_FROM_Y: x_or_y is the
- * saved forward output y (Eqs. 10-11).  f = PA_SIGMOID or PA_TANH. */
+ * is recomputed accurately from x (all four functions; SiLU' = sigma (1 +
+ * x sigma(-x)), GELU' = Phi + x phi); impl = PA_IMPL_NATIVE_FROM_Y: x_or_y is
+ * the saved forward output y (Eqs. 10-11), PA_SIGMOID and PA_TANH only. */
 pa_status native_act_bwd(pa_impl impl, pa_func f, pa_dtype t, const void *x_or_y,
                          const void *dy, void *dx, int64_t n, hipStream_t stream);
 

@@ -41,6 +41,13 @@ def main():
     out.append(entry("sigmoid_bwd_d4", p, obj, met, 4.465e-3))
     p, obj, met = O.search(O.TANH, 1, 4)
     out.append(entry("tanh_bwd_d4", p, obj, met, None))
+    # centered-odd derivative fits (Eq. 9): SiLU' D3 as in the B1 probe, GELU' at
+    # the forward GELU's degree D5 (its degree is not printed; D5 also has the
+    # lowest search objective among D3-D6)
+    p, obj, met = O.search(O.SILU, 1, 3)
+    out.append(entry("silu_bwd_d3", p, obj, met, None))
+    p, obj, met = O.search(O.GELU, 1, 5)
+    out.append(entry("gelu_bwd_d5", p, obj, met, None))
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "programs.json")
     with open(path, "w") as f:
         json.dump({"generator": "tests/golden/make_programs.py", "programs": out}, f,

@@ -44,7 +44,8 @@ def fwd_prog_name(func):
 
 
 def bwd_prog_name(func):
-    return {"sigmoid": "sigmoid_bwd_d4", "tanh": "tanh_bwd_d4"}[func]
+    return {"sigmoid": "sigmoid_bwd_d4", "tanh": "tanh_bwd_d4", "silu": "silu_bwd_d3",
+            "gelu": "gelu_bwd_d5"}[func]
 
 
 def diff_report(got, ref, x=None, limit=5):

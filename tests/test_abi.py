@@ -48,8 +48,9 @@ def test_program_table_matches_oracle(pa, orc):
         # and the oracle, fitting now, agrees
         p = orc.make_prog(g["func"], g["deriv"], g["degree"], g["Li"], g["Lc"])
         assert p.coeff_bits() == g["coeff_bits"]
-    with pytest.raises(pa.PolyActError):
-        pa.program_info("gelu", 1, "f16")      # no GELU derivative program
+    out = pa.PaProgram()
+    assert pa.lib().poly_program_info(9, 0, 1, C.byref(out)) == 4   # no such function
+    assert pa.lib().poly_program_info(1, 0, 5, C.byref(out)) == 3   # no such dtype
 
 
 FAKE = 0x10000  # never dereferenced: validation fails (or n == 0) first
@@ -65,7 +66,8 @@ def test_error_paths_unary(pa):
     assert L.poly_act_fwd(1, 1, FAKE + 1, FAKE + 64, 8, None) == 7   # odd address
     assert L.poly_act_fwd(1, 1, FAKE, FAKE, 0, None) == 0            # n = 0: no launch
     assert L.poly_act_fwd(1, 2, FAKE, FAKE + 64, 0, None) == 0
-    assert L.poly_act_bwd(3, 1, FAKE, FAKE + 64, FAKE + 128, 8, None) == 4   # no SiLU' D4
+    assert L.poly_act_bwd(5, 1, FAKE, FAKE + 64, FAKE + 128, 8, None) == 4   # no such function
+    assert L.native_act_bwd(2, 3, 1, FAKE, FAKE + 64, FAKE + 128, 8, None) == 4  # SiLU' from y
     assert L.poly_act_bwd(1, 1, FAKE, FAKE + 64, FAKE + 66, 8, None) == 5    # dx over dy
     assert L.native_act_bwd(5, 1, 1, FAKE, FAKE + 64, FAKE + 128, 8, None) == 4
     assert L.native_act_fwd(0, 1, FAKE, FAKE + 64, 8, None) == 4

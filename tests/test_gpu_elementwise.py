@@ -15,7 +15,7 @@ from gpu_util import (bwd_prog_name, diff_report, fwd_prog_name, note, programs,
 pytestmark = pytest.mark.gpu
 ALL = np.arange(65536, dtype=np.uint16)
 FWD = ["sigmoid", "tanh", "silu", "gelu"]
-BWD = ["sigmoid", "tanh"]
+BWD = ["sigmoid", "tanh", "silu", "gelu"]
 DT = {"f16": torch.float16, "bf16": torch.bfloat16}
 ORDER = {"f16": 1, "bf16": 3}
 
@@ -110,7 +110,7 @@ def test_cfg2_268m_sampled(pa, orc, progs):
         del y
         ref = orc.act_fwd(progs[fwd_prog_name(func)], xs, 1)
         assert np.array_equal(got, ref), func + ": " + diff_report(got, ref, xs)
-    for func in BWD:
+    for func in BWD[:2]:
         note(f"cfg2 268M bwd {func}")
         dx = pa.poly_act_bwd(xt, gt, func)
         got = to_bits(dx[it])
@@ -192,6 +192,8 @@ def test_native_bwd(pa, orc, fmt, func):
     dx = to_bits(pa.native_act_bwd(to_dev(x, DT[fmt]), to_dev(g, DT[fmt]), func, "native"))
     ref = np.array([enc(L.orc_ref(fid, 1, dec(int(b)))) for b in x], dtype=np.uint16)
     assert np.all(_ulp_diff(dx, ref, fmt) <= 1), (func, fmt)
+    if func not in ("sigmoid", "tanh"):
+        return
     # from y: g y (1 - y) / g (1 - y^2) on the saved forward output
     note(f"native bwd from y {func} {fmt}")
     y = to_bits(pa.native_act_fwd(to_dev(x, DT[fmt]), func))

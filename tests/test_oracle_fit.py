@@ -154,6 +154,8 @@ def test_golden_programs_are_oracle_output(orc):
         "gelu_fwd_d5": orc.search(orc.GELU, 0, 5, bound=1.065e-3),
         "sigmoid_bwd_d4": orc.search(orc.SIGMOID, 1, 4, bound=4.465e-3),
         "tanh_bwd_d4": orc.search(orc.TANH, 1, 4),
+        "silu_bwd_d3": orc.search(orc.SILU, 1, 3),
+        "gelu_bwd_d5": orc.search(orc.GELU, 1, 5),
     }
     for name, (p, obj, met) in sel.items():
         g = byname[name]
@@ -170,3 +172,27 @@ def test_search_replay_orders_agree_on_selection(orc):
         a = orc.search(*args, order=orc.ORDER_BF16_FMA, **kw)[0]
         b = orc.search(*args, order=orc.ORDER_F32FMA_BF16, **kw)[0]
         assert (a.Li, a.Lc, a.coeff_bits()) == (b.Li, b.Lc, b.coeff_bits())
+
+
+def test_figs_4_5_degree_is_not_monotone(orc):
+    """Appendix A (Figs. 4-5): in each of the six D3-D6 sweeps (sigmoid, tanh,
+    SiLU; forward and derivative) at least one higher-degree program has a
+    larger maximum error than a lower-degree one after BF16 replay.  Error:
+    max |replay - f| over every BF16 value in [0, 12] (the replay is odd or
+    even in x, so the positive half suffices)."""
+    import numpy as np
+    bf = (np.arange(0, 0x4141, dtype=np.uint32) << 16).view(np.float32).astype(np.float64)
+    xs = np.arange(0, 0x4141, dtype=np.uint16)[(bf >= 0) & (bf <= 12)]
+    xv = (xs.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    for func in (orc.SIGMOID, orc.TANH, orc.SILU):
+        for deriv in (0, 1):
+            errs = []
+            for degree in (3, 4, 5, 6):
+                kw = {"Lc_fixed": 5.28125} if (func != orc.TANH and deriv == 0) else {}
+                p, _, _ = orc.search(func, deriv, degree, **kw)
+                y = orc.act_fwd(p, xs, orc.ORDER_F32FMA_BF16)
+                yv = (y.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+                ref = np.array([orc.lib().orc_ref(func, deriv, float(v)) for v in xv])
+                errs.append(float(np.max(np.abs(yv - ref))))
+            inversions = [(a, b) for a in range(4) for b in range(a + 1, 4) if errs[b] > errs[a]]
+            assert inversions, (func, deriv, errs)
