@@ -52,6 +52,22 @@ class Prog(C.Structure):
                 f"c={[hex(b) for b in self.coeff_bits()]})")
 
 
+class SigProg(C.Structure):
+    """Two-region sigmoid-attention program (BF16 bit patterns)."""
+    _fields_ = [("n", C.c_int32), ("thr", C.c_uint16), ("lo", C.c_uint16),
+                ("hi", C.c_uint16), ("c", (C.c_uint16 * 4) * 2), ("a", C.c_uint16 * 2),
+                ("b", C.c_uint16 * 2)]
+
+
+class Attn(C.Structure):
+    _fields_ = [("kind", C.c_int32), ("B", C.c_int32), ("H", C.c_int32), ("Hkv", C.c_int32),
+                ("S", C.c_int32), ("D", C.c_int32), ("causal", C.c_int32),
+                ("order", C.c_int32), ("cap", C.c_float), ("tanh_prog", C.POINTER(Prog)),
+                ("sig", C.POINTER(SigProg))]
+
+
+ATTN_SOFTCAP_POLY, ATTN_SOFTCAP_EXACT, ATTN_SIGMOID_POLY, ATTN_SIGMOID_EXACT = 1, 2, 3, 4
+
 _lib = None
 
 
@@ -90,10 +106,13 @@ def lib():
             "orc_swiglu_bwd": (None, [P(Prog), C.c_void_p, C.c_void_p, C.c_void_p,
                                       C.c_void_p, C.c_void_p, i64, i64, i64, i64,
                                       i64, i64, i64, i64]),
-            "orc_softcap_attn_rows": (None, [P(Prog), C.c_int, C.c_void_p, C.c_void_p,
-                                             C.c_void_p, i32, i32, i32, i32, C.c_float,
-                                             i32, C.c_void_p, i64, C.c_void_p,
-                                             C.c_void_p]),
+            "orc_attn_fwd_rows": (C.c_int, [P(Attn), C.c_void_p, C.c_void_p, C.c_void_p,
+                                            C.c_void_p, i64, C.c_void_p, C.c_void_p,
+                                            C.c_void_p]),
+            "orc_attn_bwd_rows": (C.c_int, [P(Attn)] + [C.c_void_p] * 7 + [i64, C.c_void_p, i64]
+                                  + [C.c_void_p] * 6),
+            "orc_dtanh_prog_f16": (u16, [P(Prog), u16]),
+            "orc_sig_prog_eval": (u16, [P(SigProg), u16, C.c_int, P(u16)]),
             "orc_threads": (C.c_int, []),
         }
         for name, (res, args) in sig.items():
@@ -189,19 +208,91 @@ def swiglu_bwd(sig: Prog, gate, up, dh, row_begin=0, row_end=None):
     return dg, du
 
 
-def softcap_attn_rows(tanh_prog: Prog, poly: bool, q, k, v, cap: float, causal: bool,
-                      rows):
-    """q, k, v: uint16 (BF16 bits) [B, H, S, D].  Returns (O, noise) as float64
-    [len(rows), D] for the requested flat query rows (b*H + h)*S + i."""
-    q, k, v = _u16(q), _u16(k), _u16(v)
+def sig_prog_from_golden(d: dict) -> SigProg:
+    """SigProg from the golden description (hex strings of BF16 bit patterns)."""
+    sp = SigProg()
+    sp.n = int(d["n"])
+    sp.thr, sp.lo, sp.hi = (int(d[k], 16) for k in ("threshold", "clamp_lo", "clamp_hi"))
+    for r, name in enumerate(("region_lo", "region_hi")):
+        reg = d[name]
+        for j in range(4):
+            sp.c[r][j] = int(reg[f"c{j}"], 16)
+        sp.a[r] = int(reg["a"], 16)
+        sp.b[r] = int(reg["b"], 16)
+    return sp
+
+
+def _attn(kind, q, k, cap, causal, tanh_prog, sig, order):
     B, H, S, D = q.shape
+    a = Attn()
+    a.kind, a.B, a.H, a.Hkv, a.S, a.D = kind, B, H, k.shape[1], S, D
+    a.causal, a.order, a.cap = int(causal), order, cap
+    a._keep = (tanh_prog, sig)
+    if tanh_prog is not None:
+        a.tanh_prog = C.pointer(tanh_prog)
+    if sig is not None:
+        a.sig = C.pointer(sig)
+    return a
+
+
+def attn_fwd_rows(kind: int, q, k, v, rows, cap: float = 50.0, causal: bool = True,
+                  tanh_prog: Prog = None, sig: SigProg = None, order: int = 0):
+    """q: uint16 BF16 bits [B, H, S, D]; k, v: [B, Hkv, S, D].  Returns (O, lse,
+    noise) in float64 for the flat query rows (b H + h) S + i: O and noise
+    [len(rows), D], lse [len(rows)] (NaN for sigmoid attention)."""
+    q, k, v = _u16(q), _u16(k), _u16(v)
+    D = q.shape[3]
     rows = np.ascontiguousarray(rows, dtype=np.int64)
-    out = np.zeros((rows.size, D), dtype=np.float64)
-    noise = np.zeros((rows.size, D), dtype=np.float64)
-    lib().orc_softcap_attn_rows(C.byref(tanh_prog), int(poly), _ptr(q), _ptr(k), _ptr(v),
-                                B, H, S, D, cap, int(causal), _ptr(rows), rows.size,
-                                _ptr(out), _ptr(noise))
-    return out, noise
+    out = np.zeros((rows.size, D))
+    lse = np.zeros(rows.size)
+    noise = np.zeros((rows.size, D))
+    a = _attn(kind, q, k, cap, causal, tanh_prog, sig, order)
+    rc = lib().orc_attn_fwd_rows(C.byref(a), _ptr(q), _ptr(k), _ptr(v), _ptr(rows), rows.size,
+                                 _ptr(out), _ptr(lse), _ptr(noise))
+    if rc:
+        raise ValueError(f"orc_attn_fwd_rows: {rc}")
+    return out, lse, noise
+
+
+def attn_bwd_rows(kind: int, q, k, v, o, dout, lse, qrows, krows, cap: float = 50.0,
+                  causal: bool = True, tanh_prog: Prog = None, sig: SigProg = None,
+                  order: int = 0):
+    """Gradients of sum(O * dout) for the flat query rows (dQ) and key rows
+    (b Hkv + hk) S + j (dK, dV).  o: float64 [B, H, S, D] (the forward output
+    the backward is given), lse: float64 [B, H, S] (softcap only).  Returns
+    (dq, dk, dv, nz_dq, nz_dk, nz_dv), float64 [rows, D] each."""
+    q, k, v, dout = _u16(q), _u16(k), _u16(v), _u16(dout)
+    D = q.shape[3]
+    o = np.ascontiguousarray(o, dtype=np.float64)
+    lse = np.ascontiguousarray(np.zeros(1) if lse is None else lse, dtype=np.float64)
+    qrows = np.ascontiguousarray(qrows, dtype=np.int64)
+    krows = np.ascontiguousarray(krows, dtype=np.int64)
+    res = [np.zeros((n, D)) for n in (qrows.size, krows.size, krows.size) * 2]
+    a = _attn(kind, q, k, cap, causal, tanh_prog, sig, order)
+    rc = lib().orc_attn_bwd_rows(C.byref(a), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout),
+                                 _ptr(lse), _ptr(qrows), qrows.size, _ptr(krows), krows.size,
+                                 *[_ptr(r) for r in res])
+    if rc:
+        raise ValueError(f"orc_attn_bwd_rows: {rc}")
+    return tuple(res)
+
+
+def dtanh_prog_f16(tanh_prog: Prog, x_bits) -> np.ndarray:
+    x = np.atleast_1d(np.asarray(x_bits, dtype=np.uint16))
+    return np.array([lib().orc_dtanh_prog_f16(C.byref(tanh_prog), int(b)) for b in x],
+                    dtype=np.uint16)
+
+
+def sig_prog_eval(sp: SigProg, x_bits, order: int = ORDER_F32FMA_BF16):
+    """(P~, surrogate derivative) BF16 bit arrays at BF16 inputs x."""
+    x = np.atleast_1d(np.asarray(x_bits, dtype=np.uint16))
+    p = np.zeros(x.size, np.uint16)
+    g = np.zeros(x.size, np.uint16)
+    gb = C.c_uint16()
+    for i, b in enumerate(x):
+        p[i] = lib().orc_sig_prog_eval(C.byref(sp), int(b), order, C.byref(gb))
+        g[i] = gb.value
+    return p, g
 
 
 def threads() -> int:

@@ -20,7 +20,9 @@
  * rationals; the fit against Table 2's printed sigmoid-derivative D4 bound
  * (reproduced bit for bit) and the least-squares normal equations; replay
  * against rounding-error bounds and the symmetry identities; attention rows
- * against a textbook FP64 attention.  Parity unpinned: the selection of the
+ * against a textbook FP64 attention, attention gradients against automatic
+ * differentiation of textbook FP64 attention, the sigmoid-attention program
+ * against sigma(s - ln n).  Parity unpinned: the selection of the
  * GELU D5 program (Table 2's 1.06e-3 is not reached under any reading) and of
  * the tanh-derivative D4 program (no printed value).
  */
@@ -99,11 +101,44 @@ void orc_swiglu_bwd(const orc_prog *sig, const uint16_t *gate, const uint16_t *u
                     int64_t row_begin, int64_t row_end, int64_t cols,
                     int64_t ld_gate, int64_t ld_up, int64_t ld_dh,
                     int64_t ld_dgate, int64_t ld_dup);
-void orc_softcap_attn_rows(const orc_prog *tanh_prog, int poly,
-                           const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                           int32_t B, int32_t H, int32_t S, int32_t D, float cap,
-                           int32_t causal, const int64_t *rows, int64_t n_rows,
-                           double *out, double *noise);
+/* ---- attention with a transformed score (orc_eval.c) -------------------- */
+enum { ORC_ATTN_SOFTCAP_POLY = 1, ORC_ATTN_SOFTCAP_EXACT = 2,
+       ORC_ATTN_SIGMOID_POLY = 3, ORC_ATTN_SIGMOID_EXACT = 4 };
+
+/* The two-region sigmoid-attention program (section 3.4 and Appendix C,
+ * Listings 1-2): BF16 bit patterns of the region threshold, the clamp bounds,
+ * the cubic coefficients c[r][j] of x^j for region r (r = 1 when x >= thr) and
+ * the derivative factor a[r] + b[r] x; n is the one sequence length the
+ * coefficients hold for. */
+typedef struct {
+    int32_t n;
+    uint16_t thr, lo, hi;
+    uint16_t c[2][4];
+    uint16_t a[2], b[2];
+} orc_sig_prog;
+
+typedef struct {
+    int32_t kind;              /* ORC_ATTN_*                                   */
+    int32_t B, H, Hkv, S, D;   /* Q [B, H, S, D]; K, V [B, Hkv, S, D]          */
+    int32_t causal;
+    int32_t order;             /* replay order of the sigmoid program (0: F32FMA_BF16) */
+    float cap;                 /* softcap alpha                                 */
+    const orc_prog *tanh_prog; /* D4 tanh program (SOFTCAP_POLY)                */
+    const orc_sig_prog *sig;   /* SIGMOID_POLY                                  */
+} orc_attn;
+
+/* Returns 0, or -1 (sequence length differs from the sigmoid program's n),
+ * -2 (bad shape), -3 (unknown kind). */
+int orc_attn_fwd_rows(const orc_attn *a, const uint16_t *q, const uint16_t *k,
+                      const uint16_t *v, const int64_t *rows, int64_t n_rows,
+                      double *out, double *lse, double *noise);
+int orc_attn_bwd_rows(const orc_attn *a, const uint16_t *q, const uint16_t *k,
+                      const uint16_t *v, const double *o, const uint16_t *dout,
+                      const double *lse, const int64_t *qrows, int64_t nq,
+                      const int64_t *krows, int64_t nk, double *dq, double *dk,
+                      double *dv, double *nz_dq, double *nz_dk, double *nz_dv);
+uint16_t orc_dtanh_prog_f16(const orc_prog *tanh_prog, uint16_t x);
+uint16_t orc_sig_prog_eval(const orc_sig_prog *sp, uint16_t x, int order, uint16_t *grad);
 int orc_threads(void);
 
 #ifdef __cplusplus

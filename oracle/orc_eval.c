@@ -217,71 +217,313 @@ void orc_swiglu_bwd(const orc_prog *sig, const uint16_t *gate, const uint16_t *u
     }
 }
 
-/* ---- softcapped attention forward, selected query rows ------------------
- * Q, K, V: BF16 [B, H, S, D] contiguous.  For each requested flat row index
- * r = (b H + h) S + i, computes O[r, :] in FP64 and the per-column noise
- * scale sqrt(sum_j P_j^2 V_jd^2) (the size of the output change caused by
- * relative perturbations of the probabilities; used to state tolerances).
- * Scores: S_ij = q_i . k_j exactly in FP64.
- *   poly = 1: x = RN_f16(RN32(RN32(S_ij) * RN32(1/(cap sqrt(D))))), the D4 tanh
- *             program in FP16 arithmetic (one rounding per FMA), s = cap * t~;
- *   poly = 0: s = cap * tanh(S_ij / (cap sqrt(D))) in FP64.
- * Causal: key j <= query i.  Softmax and the P V product in FP64. */
-void orc_softcap_attn_rows(const orc_prog *tp, int poly,
-                           const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                           int32_t B, int32_t H, int32_t S, int32_t D, float cap,
-                           int32_t causal, const int64_t *rows, int64_t n_rows,
-                           double *out, double *noise)
+/* ---- attention with a transformed score ------------------------------------
+ * Layout: Q, O, dO [B, H, S, D]; K, V [B, Hkv, S, D] (grouped-query attention:
+ * query head h reads key/value head h / (H / Hkv)); BF16 bit patterns, except
+ * O and the log-sum-exp, which are passed as FP64 values.  Raw score
+ * S_ij = q_i . k_j, computed in FP64.  Causal: key j visible from query i when
+ * j <= i.
+ *
+ * Score transforms:
+ *   SOFTCAP (Eq. 1): logit s = cap tanh(S / (cap sqrt D)), P = softmax_j(s).
+ *     POLY  x = RN_f16(RN32(RN32(S) * RN32(1 / (cap sqrt D)))), tanh by the D4
+ *           program in FP16 arithmetic.  Backward (sections 3.3 and 5.2.2):
+ *           the analytic derivative of that program, i.e. the D3 polynomial
+ *           with coefficients (j + 1) c_{j+1} (exact in FP16), evaluated in
+ *           FP16 arithmetic at the same clamped |x|, so ds/dS = cap RN32(..)
+ *           q(x).
+ *     EXACT tanh in FP64; ds/dS = (1 - tanh^2) / sqrt D (Eq. 12).
+ *   SIGMOID (Eq. 14): P = sigma(s - ln n) with s = S / sqrt D and n = S, the
+ *     sequence length; no normalisation.
+ *     POLY  x = RN_bf16(RN32(RN32(S) * RN32(1 / sqrt D))); the two-region
+ *           cubic of section 3.4 / Appendix C on the clamped x, floored at 0,
+ *           with ln n and 1 / n folded into its coefficients (so it holds for
+ *           one n only); backward surrogate P~ (a + b x) per region.
+ *     EXACT FP64 sigma; dP/dS = P (1 - P) / sqrt D.
+ *
+ * Backward (chain rule through O = P V):
+ *   dV_j = sum_i P_ij dO_i;   dP_ij = dO_i . V_j;
+ *   softcap: dS_ij = P_ij (dP_ij - Delta_i) ds/dS,  Delta_i = dO_i . O_i
+ *   sigmoid: dS_ij = dP_ij dP/dS;
+ *   dQ_i = sum_j dS_ij K_j;   dK_j = sum over query heads of the group and
+ *   visible i of dS_ij Q_i.
+ * Each output also gets a noise scale sqrt(sum of squared terms): the size of
+ * the change caused by independent relative roundings of the terms (used to
+ * state the tolerance of a faster implementation). */
+
+static double stable_sigmoid(double s)
+{
+    const double e = exp(-fabs(s));
+    return s >= 0.0 ? 1.0 / (1.0 + e) : e / (1.0 + e);
+}
+
+/* Differentiated tanh program at FP16 x (see above). */
+static uint16_t dtanh_prog_f16(const orc_prog *tp, uint16_t x)
 {
     const fmt_ops f = ops_for(ORC_ORDER_F16_FMA);
-    const float scale = (float)(1.0 / ((double)cap * sqrt((double)D)));
-    (void)B;
+    uint16_t d[8];
+    for (int j = 0; j < tp->degree; j++) {
+        const double v = (double)(j + 1) * orc_bf16_to_f64(tp->c[j + 1]);
+        d[j] = orc_f64_to_f16(v);
+        if (orc_f16_to_f64(d[j]) != v) abort();
+    }
+    const uint16_t t = x & 0x7FFF;
+    const uint16_t th = orc_f16_to_f64(t) > tp->Lc ? orc_f64_to_f16(tp->Lc) : t;
+    uint16_t v = d[tp->degree - 1];
+    for (int j = tp->degree - 2; j >= 0; j--) v = t_fma(&f, v, th, d[j]);
+    return v;
+}
+
+uint16_t orc_dtanh_prog_f16(const orc_prog *tp, uint16_t x)
+{
+    return dtanh_prog_f16(tp, x);
+}
+
+/* Two-region sigmoid-attention program at BF16 x: region 1 when x >= thr;
+ * x clamped to [lo, hi]; v = c3; v = fma(x, v, c_j) for j = 2, 1, 0 in the
+ * given order; P = max(v, +0); surrogate derivative P * fma(x, b, a). */
+static uint16_t sig_eval(const fmt_ops *f, const orc_sig_prog *sp, uint16_t x,
+                         uint16_t *grad)
+{
+    const double xv = orc_bf16_to_f64(x);
+    const int r = xv >= orc_bf16_to_f64(sp->thr);
+    uint16_t xc = x;
+    if (xv > orc_bf16_to_f64(sp->hi)) xc = sp->hi;
+    if (xv < orc_bf16_to_f64(sp->lo)) xc = sp->lo;
+    uint16_t v = sp->c[r][3];
+    for (int j = 2; j >= 0; j--) v = t_fma(f, xc, v, sp->c[r][j]);
+    if (orc_bf16_to_f64(v) < 0.0) v = 0;
+    if (grad) *grad = t_mul(f, v, t_fma(f, xc, sp->b[r], sp->a[r]));
+    return v;
+}
+
+uint16_t orc_sig_prog_eval(const orc_sig_prog *sp, uint16_t x, int order, uint16_t *grad)
+{
+    const fmt_ops f = ops_for(order);
+    return sig_eval(&f, sp, x, grad);
+}
+
+typedef struct {
+    const orc_attn *a;
+    fmt_ops f16, fs;
+    float scale;      /* RN32 of the factor applied to S before rounding x */
+    double rsd;       /* 1 / sqrt(D) */
+    double logn;      /* ln S (sigmoid) */
+} actx;
+
+static int actx_init(actx *c, const orc_attn *a)
+{
+    if (a->H <= 0 || a->Hkv <= 0 || a->H % a->Hkv || a->S < 0 || a->D <= 0) return -2;
+    c->a = a;
+    c->f16 = ops_for(ORC_ORDER_F16_FMA);
+    c->fs = ops_for(a->order ? a->order : ORC_ORDER_F32FMA_BF16);
+    c->rsd = 1.0 / sqrt((double)a->D);
+    c->logn = log((double)a->S);
+    switch (a->kind) {
+    case ORC_ATTN_SOFTCAP_POLY:
+    case ORC_ATTN_SOFTCAP_EXACT:
+        if (!(a->cap > 0.0f)) return -2;
+        c->scale = (float)(1.0 / ((double)a->cap * sqrt((double)a->D)));
+        return 0;
+    case ORC_ATTN_SIGMOID_POLY:
+        if (!a->sig || a->sig->n != a->S) return -1;   /* the length guard */
+        c->scale = (float)c->rsd;
+        return 0;
+    case ORC_ATTN_SIGMOID_EXACT:
+        c->scale = (float)c->rsd;
+        return 0;
+    default:
+        return -3;
+    }
+}
+
+/* Transformed score of raw score Sr: the logit (softcap) or the probability
+ * (sigmoid), and its derivative with respect to Sr. */
+static void score(const actx *c, double Sr, double *val, double *dval)
+{
+    const orc_attn *a = c->a;
+    switch (a->kind) {
+    case ORC_ATTN_SOFTCAP_POLY: {
+        const uint16_t x = orc_f64_to_f16((double)orc_mul_f32((float)Sr, c->scale));
+        *val = (double)a->cap * orc_f16_to_f64(eval_one(&c->f16, a->tanh_prog, x));
+        *dval = (double)a->cap * (double)c->scale *
+                orc_f16_to_f64(dtanh_prog_f16(a->tanh_prog, x));
+        return;
+    }
+    case ORC_ATTN_SOFTCAP_EXACT: {
+        const double t = tanh(Sr / ((double)a->cap * sqrt((double)a->D)));
+        *val = (double)a->cap * t;
+        *dval = (1.0 - t * t) * c->rsd;
+        return;
+    }
+    case ORC_ATTN_SIGMOID_POLY: {
+        const uint16_t x = orc_f64_to_bf16((double)orc_mul_f32((float)Sr, c->scale));
+        uint16_t g;
+        *val = orc_bf16_to_f64(sig_eval(&c->fs, a->sig, x, &g));
+        *dval = orc_bf16_to_f64(g) * (double)c->scale;
+        return;
+    }
+    default: {
+        const double p = stable_sigmoid(Sr * c->rsd - c->logn);
+        *val = p;
+        *dval = p * (1.0 - p) * c->rsd;
+        return;
+    }
+    }
+}
+
+static int is_softcap(const orc_attn *a)
+{
+    return a->kind == ORC_ATTN_SOFTCAP_POLY || a->kind == ORC_ATTN_SOFTCAP_EXACT;
+}
+
+static double dot_bf16(const uint16_t *x, const uint16_t *y, int D)
+{
+    double s = 0.0;
+    for (int d = 0; d < D; d++) s += orc_bf16_to_f64(x[d]) * orc_bf16_to_f64(y[d]);
+    return s;
+}
+
+int orc_attn_fwd_rows(const orc_attn *a, const uint16_t *q, const uint16_t *k,
+                      const uint16_t *v, const int64_t *rows, int64_t n_rows,
+                      double *out, double *lse, double *noise)
+{
+    actx c;
+    const int rc = actx_init(&c, a);
+    if (rc) return rc;
+    const int64_t S = a->S, D = a->D, G = a->H / a->Hkv;
 #pragma omp parallel
     {
-        double *s = malloc(sizeof(double) * (size_t)S);
-        double *qd = malloc(sizeof(double) * (size_t)D);
+        double *w = malloc(sizeof(double) * (size_t)(S > 0 ? S : 1));
 #pragma omp for schedule(dynamic, 1)
         for (int64_t ri = 0; ri < n_rows; ri++) {
             const int64_t r = rows[ri];
-            const int64_t bh = r / S;
-            const int64_t i = r % S;
-            (void)H;
-            const uint16_t *qr = q + r * D;
-            const uint16_t *kb = k + bh * (int64_t)S * D;
-            const uint16_t *vb = v + bh * (int64_t)S * D;
-            for (int d = 0; d < D; d++) qd[d] = orc_bf16_to_f64(qr[d]);
-            const int64_t nk = causal ? i + 1 : S;
-            double m = -INFINITY;
+            const int64_t bh = r / S, i = r % S;
+            const int64_t b = bh / a->H, h = bh % a->H;
+            const int64_t kvb = (b * a->Hkv + h / G) * S * D;
+            const int64_t nk = a->causal ? i + 1 : S;
+            double m = -INFINITY, dummy;
             for (int64_t j = 0; j < nk; j++) {
-                double acc = 0.0;
-                for (int d = 0; d < D; d++)
-                    acc += qd[d] * orc_bf16_to_f64(kb[j * D + d]);
-                double sc;
-                if (poly) {
-                    const float xs = orc_mul_f32((float)acc, scale);
-                    const uint16_t xh = orc_f64_to_f16((double)xs);
-                    sc = (double)cap * orc_f16_to_f64(eval_one(&f, tp, xh));
-                } else {
-                    sc = (double)cap * tanh(acc / ((double)cap * sqrt((double)D)));
-                }
-                s[j] = sc;
-                if (sc > m) m = sc;
+                score(&c, dot_bf16(q + r * D, k + kvb + j * D, (int)D), &w[j], &dummy);
+                if (w[j] > m) m = w[j];
             }
-            double l = 0.0;
-            for (int64_t j = 0; j < nk; j++) { s[j] = exp(s[j] - m); l += s[j]; }
-            for (int d = 0; d < D; d++) {
+            if (is_softcap(a)) {
+                double l = 0.0;
+                for (int64_t j = 0; j < nk; j++) { w[j] = exp(w[j] - m); l += w[j]; }
+                for (int64_t j = 0; j < nk; j++) w[j] /= l;
+                if (lse) lse[ri] = m + log(l);
+            } else if (lse) {
+                lse[ri] = NAN;
+            }
+            for (int64_t d = 0; d < D; d++) {
                 double o = 0.0, n2 = 0.0;
                 for (int64_t j = 0; j < nk; j++) {
-                    const double pj = s[j] / l;
-                    const double vj = orc_bf16_to_f64(vb[j * D + d]);
-                    o += pj * vj;
-                    n2 += pj * pj * vj * vj;
+                    const double vj = orc_bf16_to_f64(v[kvb + j * D + d]);
+                    o += w[j] * vj;
+                    n2 += w[j] * w[j] * vj * vj;
                 }
                 out[ri * D + d] = o;
                 if (noise) noise[ri * D + d] = sqrt(n2);
             }
         }
-        free(s);
-        free(qd);
+        free(w);
     }
+    return 0;
+}
+
+/* dS_ij and P_ij of one (query row, key row) pair. */
+static void pair_grad(const actx *c, const uint16_t *qi, const uint16_t *kj,
+                      const uint16_t *vj, const uint16_t *doi, double lse_i,
+                      double delta_i, double *P, double *dS)
+{
+    const int D = c->a->D;
+    double val, dval;
+    score(c, dot_bf16(qi, kj, D), &val, &dval);
+    const double dP = dot_bf16(doi, vj, D);
+    if (is_softcap(c->a)) {
+        *P = exp(val - lse_i);
+        *dS = *P * (dP - delta_i) * dval;
+    } else {
+        *P = val;
+        *dS = dP * dval;
+    }
+}
+
+static double row_delta(const uint16_t *doi, const double *oi, int D)
+{
+    double s = 0.0;
+    for (int d = 0; d < D; d++) s += orc_bf16_to_f64(doi[d]) * oi[d];
+    return s;
+}
+
+int orc_attn_bwd_rows(const orc_attn *a, const uint16_t *q, const uint16_t *k,
+                      const uint16_t *v, const double *o, const uint16_t *dout,
+                      const double *lse, const int64_t *qrows, int64_t nq,
+                      const int64_t *krows, int64_t nk, double *dq, double *dk,
+                      double *dv, double *nz_dq, double *nz_dk, double *nz_dv)
+{
+    actx c;
+    const int rc = actx_init(&c, a);
+    if (rc) return rc;
+    const int64_t S = a->S, D = a->D, G = a->H / a->Hkv;
+    const int sc = is_softcap(a);
+    /* dQ rows */
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t ri = 0; ri < nq; ri++) {
+        const int64_t r = qrows[ri];
+        const int64_t bh = r / S, i = r % S;
+        const int64_t b = bh / a->H, h = bh % a->H;
+        const int64_t kvb = (b * a->Hkv + h / G) * S * D;
+        const double delta = sc ? row_delta(dout + r * D, o + r * D, (int)D) : 0.0;
+        const double li = sc ? lse[r] : 0.0;
+        const int64_t n = a->causal ? i + 1 : S;
+        for (int64_t d = 0; d < D; d++) { dq[ri * D + d] = 0.0; if (nz_dq) nz_dq[ri * D + d] = 0.0; }
+        for (int64_t j = 0; j < n; j++) {
+            double P, dS;
+            pair_grad(&c, q + r * D, k + kvb + j * D, v + kvb + j * D, dout + r * D, li,
+                      delta, &P, &dS);
+            for (int64_t d = 0; d < D; d++) {
+                const double t = dS * orc_bf16_to_f64(k[kvb + j * D + d]);
+                dq[ri * D + d] += t;
+                if (nz_dq) nz_dq[ri * D + d] += t * t;
+            }
+        }
+        if (nz_dq)
+            for (int64_t d = 0; d < D; d++) nz_dq[ri * D + d] = sqrt(nz_dq[ri * D + d]);
+    }
+    /* dK, dV rows: key row r = (b Hkv + hk) S + j */
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t ri = 0; ri < nk; ri++) {
+        const int64_t r = krows[ri];
+        const int64_t bk = r / S, j = r % S;
+        const int64_t b = bk / a->Hkv, hk = bk % a->Hkv;
+        for (int64_t d = 0; d < D; d++) {
+            dk[ri * D + d] = dv[ri * D + d] = 0.0;
+            if (nz_dk) nz_dk[ri * D + d] = 0.0;
+            if (nz_dv) nz_dv[ri * D + d] = 0.0;
+        }
+        for (int64_t h = hk * G; h < (hk + 1) * G; h++) {
+            const int64_t qb = (b * a->H + h) * S;
+            for (int64_t i = a->causal ? j : 0; i < S; i++) {
+                const int64_t qr = qb + i;
+                const double delta = sc ? row_delta(dout + qr * D, o + qr * D, (int)D) : 0.0;
+                double P, dS;
+                pair_grad(&c, q + qr * D, k + r * D, v + r * D, dout + qr * D,
+                          sc ? lse[qr] : 0.0, delta, &P, &dS);
+                for (int64_t d = 0; d < D; d++) {
+                    const double tk = dS * orc_bf16_to_f64(q[qr * D + d]);
+                    const double tv = P * orc_bf16_to_f64(dout[qr * D + d]);
+                    dk[ri * D + d] += tk;
+                    dv[ri * D + d] += tv;
+                    if (nz_dk) nz_dk[ri * D + d] += tk * tk;
+                    if (nz_dv) nz_dv[ri * D + d] += tv * tv;
+                }
+            }
+        }
+        for (int64_t d = 0; d < D; d++) {
+            if (nz_dk) nz_dk[ri * D + d] = sqrt(nz_dk[ri * D + d]);
+            if (nz_dv) nz_dv[ri * D + d] = sqrt(nz_dv[ri * D + d]);
+        }
+    }
+    return 0;
 }

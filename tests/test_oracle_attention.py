@@ -1,0 +1,271 @@
+"""Pins of the oracle's attention (forward rows, backward rows, the sigmoid-
+attention program) against things other than itself:
+
+* forward O and log-sum-exp against textbook FP64 attention (softmax of the
+  transformed scores, or the unnormalised sigmoid of Eq. 14);
+* every gradient against automatic differentiation (torch, FP64) of textbook
+  attention: with the exact transforms directly; for the programs, with the
+  oracle's elementwise program values wrapped as a custom autograd function
+  (checks the attention-level chain rule exactly), and, for the softcap, with
+  the real-arithmetic D4 polynomial (checks that the backward program is the
+  derivative of the forward one);
+* the printed sigmoid-attention program against sigma(s - ln 4096);
+* the differentiated tanh program against a central difference of the real
+  polynomial.
+"""
+import copy
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import synth_inputs as si
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+B3 = json.load(open(os.path.join(HERE, "golden", "sigmoid_attn_b3.json")))
+
+
+def bf16_bits(a):
+    return si.to_bf16_bits(np.asarray(a, dtype=np.float64))
+
+
+def bf16v(bits):
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def f16v(bits):
+    return bits.view(np.float16).astype(np.float64)
+
+
+@pytest.fixture(scope="module")
+def tanh_prog(orc):
+    g = [p for p in json.load(open(os.path.join(HERE, "golden", "programs.json")))["programs"]
+         if p["name"] == "tanh_fwd_d4"][0]
+    return orc.make_prog(g["func"], g["deriv"], g["degree"], g["Li"], g["Lc"])
+
+
+@pytest.fixture(scope="module")
+def sig_prog(orc):
+    return orc.sig_prog_from_golden(B3)
+
+
+def inputs(B, H, Hkv, S, D, sd_q=1.0, seed=0):
+    rng = np.random.default_rng(seed)
+    q = bf16_bits(rng.standard_normal((B, H, S, D)) * sd_q)
+    k = bf16_bits(rng.standard_normal((B, Hkv, S, D)))
+    v = bf16_bits(rng.standard_normal((B, Hkv, S, D)))
+    do = bf16_bits(rng.standard_normal((B, H, S, D)))
+    return q, k, v, do
+
+
+def textbook(q, k, v, causal, transform, softmax):
+    """FP64 torch attention; q [B, H, S, D], k, v [B, Hkv, S, D]."""
+    G = q.shape[1] // k.shape[1]
+    kk = k.repeat_interleave(G, 1)
+    vv = v.repeat_interleave(G, 1)
+    z = transform(q @ kk.transpose(-1, -2))
+    S = q.shape[2]
+    vis = torch.ones(S, S, dtype=torch.bool).tril() if causal else torch.ones(S, S, dtype=torch.bool)
+    if softmax:
+        z = z.masked_fill(~vis, -math.inf)
+        lse = torch.logsumexp(z, -1)
+        P = torch.softmax(z, -1)
+    else:
+        lse = None
+        P = z.masked_fill(~vis, 0.0)
+    return P @ vv, lse
+
+
+def table_fn(values, grads):
+    """Custom autograd function: y = values(S), dy/dS = grads(S) (numpy callables)."""
+    class F(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, s):
+            ctx.save_for_backward(s)
+            return torch.from_numpy(values(s.detach().numpy()))
+
+        @staticmethod
+        def backward(ctx, g):
+            (s,) = ctx.saved_tensors
+            return g * torch.from_numpy(grads(s.detach().numpy()))
+    return F.apply
+
+
+def run_both(orc, kind, q, k, v, do, causal, transform, softmax, **kw):
+    """Oracle forward + backward over all rows, and the autograd reference."""
+    B, H, S, D = q.shape
+    Hkv = k.shape[1]
+    qt, kt, vt = (torch.from_numpy(bf16v(a)).requires_grad_(True) for a in (q, k, v))
+    o_ref, lse_ref = textbook(qt, kt, vt, causal, transform, softmax)
+    (o_ref * torch.from_numpy(bf16v(do))).sum().backward()
+    rows = np.arange(B * H * S)
+    o, lse, noise = orc.attn_fwd_rows(kind, q, k, v, rows, causal=causal, **kw)
+    o_exact = o_ref.detach().numpy()
+    lse_exact = None if lse_ref is None else lse_ref.detach().numpy()
+    dq, dk, dv, nq, nk, nv = orc.attn_bwd_rows(kind, q, k, v, o_exact, do, lse_exact, rows,
+                                               np.arange(B * Hkv * S), causal=causal, **kw)
+    ref = dict(o=o_exact.reshape(-1, D), lse=None if lse_exact is None else lse_exact.ravel(),
+               dq=qt.grad.numpy().reshape(-1, D), dk=kt.grad.numpy().reshape(-1, D),
+               dv=vt.grad.numpy().reshape(-1, D))
+    got = dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv, noise=(noise, nq, nk, nv))
+    return got, ref
+
+
+def close(a, b, rtol):
+    scale = max(np.abs(b).max(), 1e-300)
+    err = np.abs(a - b).max() / scale
+    assert err <= rtol, f"max error {err:.3e} of max |ref| (allowed {rtol:.1e})"
+
+
+CASES = [(1, 4, 2, 37, 16, True), (2, 2, 2, 21, 8, False), (1, 3, 1, 16, 16, True)]
+
+
+@pytest.mark.parametrize("B,H,Hkv,S,D,causal", CASES)
+def test_softcap_exact_fwd_bwd_vs_autograd(orc, tanh_prog, B, H, Hkv, S, D, causal):
+    cap = 2.0
+    q, k, v, do = inputs(B, H, Hkv, S, D, sd_q=2.0, seed=S)
+    got, ref = run_both(orc, orc.ATTN_SOFTCAP_EXACT, q, k, v, do, causal,
+                        lambda s: cap * torch.tanh(s / (cap * math.sqrt(D))), True, cap=cap)
+    for name in ("o", "lse", "dq", "dk", "dv"):
+        close(got[name], ref[name], 1e-12)
+    assert all(np.all(n >= 0) for n in got["noise"])
+
+
+@pytest.mark.parametrize("B,H,Hkv,S,D,causal", CASES)
+def test_sigmoid_exact_fwd_bwd_vs_autograd(orc, B, H, Hkv, S, D, causal):
+    q, k, v, do = inputs(B, H, Hkv, S, D, sd_q=2.0, seed=S + 1)
+    got, ref = run_both(orc, orc.ATTN_SIGMOID_EXACT, q, k, v, do, causal,
+                        lambda s: torch.sigmoid(s / math.sqrt(D) - math.log(S)), False)
+    for name in ("o", "dq", "dk", "dv"):
+        close(got[name], ref[name], 1e-12)
+    assert np.all(np.isnan(got["lse"]))
+
+
+def softcap_tables(orc, tanh_prog, cap, D):
+    """The oracle's elementwise FP16 programs as functions of the raw score."""
+    scale = np.float32(1.0 / (cap * np.sqrt(D)))
+    allx = np.arange(65536, dtype=np.uint16)
+    t_tab = f16v(orc.act_fwd(tanh_prog, allx, 1))
+    d_tab = f16v(orc.dtanh_prog_f16(tanh_prog, allx))
+
+    def xbits(s):
+        return (s.astype(np.float32) * scale).astype(np.float32).astype(np.float16).view(np.uint16)
+    return (lambda s: cap * t_tab[xbits(s)],
+            lambda s: cap * np.float64(scale) * d_tab[xbits(s)])
+
+
+@pytest.mark.parametrize("B,H,Hkv,S,D,causal", CASES)
+def test_softcap_poly_chain_rule_exact(orc, tanh_prog, B, H, Hkv, S, D, causal):
+    """With the program values as the transform, the oracle's poly attention
+    equals autograd of textbook attention to rounding."""
+    cap = 1.0
+    q, k, v, do = inputs(B, H, Hkv, S, D, sd_q=0.7, seed=S + 2)
+    val, der = softcap_tables(orc, tanh_prog, cap, D)
+    got, ref = run_both(orc, orc.ATTN_SOFTCAP_POLY, q, k, v, do, causal, table_fn(val, der),
+                        True, cap=cap, tanh_prog=tanh_prog)
+    for name in ("o", "lse", "dq", "dk", "dv"):
+        close(got[name], ref[name], 1e-12)
+
+
+def test_softcap_poly_backward_is_derivative_of_forward(orc, tanh_prog):
+    """Autograd of the real-arithmetic D4 polynomial (BF16 coefficients, no
+    rounding anywhere) against the oracle's FP16 forward and differentiated
+    backward: they differ only by FP16 rounding (~1e-3), while a wrong
+    derivative coefficient moves the gradients by ~1e-1."""
+    B, H, Hkv, S, D, cap = 1, 2, 1, 48, 16, 1.0
+    q, k, v, do = inputs(B, H, Hkv, S, D, sd_q=0.45, seed=5)
+    c = [bf16v(np.array([b], np.uint16))[0] for b in tanh_prog.coeff_bits()]
+    x_all = bf16v(q).reshape(B, H, S, D) @ np.swapaxes(bf16v(k), -1, -2) / (cap * math.sqrt(D))
+    assert np.abs(x_all).max() < 0.95 * tanh_prog.Lc     # the clamp never binds
+
+    def real_tanh(s):
+        u = s / (cap * math.sqrt(D))
+        a = u.abs()
+        p = sum(cj * a ** j for j, cj in enumerate(c))
+        return cap * torch.sign(u) * p
+    got, ref = run_both(orc, orc.ATTN_SOFTCAP_POLY, q, k, v, do, True, real_tanh, True,
+                        cap=cap, tanh_prog=tanh_prog)
+    for name in ("o", "dq", "dk", "dv"):
+        close(got[name], ref[name], 1e-2)
+
+
+def sigmoid_tables(orc, sp, D):
+    scale = np.float32(1.0 / np.sqrt(D))
+    allx = np.arange(65536, dtype=np.uint16)
+    p, g = orc.sig_prog_eval(sp, allx)
+    p_tab, g_tab = bf16v(p), bf16v(g)
+
+    def xbits(s):
+        return bf16_bits((s.astype(np.float32) * scale).astype(np.float32).astype(np.float64))
+    return (lambda s: p_tab[xbits(s)], lambda s: np.float64(scale) * g_tab[xbits(s)])
+
+
+@pytest.mark.parametrize("B,H,Hkv,S,D,causal", CASES)
+def test_sigmoid_poly_chain_rule_exact(orc, sig_prog, B, H, Hkv, S, D, causal):
+    sp = copy.deepcopy(sig_prog)
+    sp.n = S          # the same coefficients, admitted at this length
+    q, k, v, do = inputs(B, H, Hkv, S, D, sd_q=2.0, seed=S + 3)
+    val, der = sigmoid_tables(orc, sp, D)
+    got, ref = run_both(orc, orc.ATTN_SIGMOID_POLY, q, k, v, do, causal, table_fn(val, der),
+                        False, sig=sp)
+    for name in ("o", "dq", "dk", "dv"):
+        close(got[name], ref[name], 1e-12)
+
+
+def test_sigmoid_poly_length_guard(orc, sig_prog):
+    q, k, v, do = inputs(1, 1, 1, 64, 8)
+    with pytest.raises(ValueError):
+        orc.attn_fwd_rows(orc.ATTN_SIGMOID_POLY, q, k, v, [0], sig=sig_prog)
+
+
+@pytest.mark.parametrize("order", [2, 3])
+def test_b3_program_against_closed_form(orc, sig_prog, order):
+    """The printed program tracks sigma(s - ln 4096) (Eq. 14 at n = 4096) where
+    attention scores live, and its factored derivative tracks sigma(1 - sigma);
+    where the true value is below ~3e-5 the floor at zero is within that."""
+    assert sig_prog.n == 4096
+    allx = np.arange(65536, dtype=np.uint16)
+    xv = bf16v(allx)
+    keep = np.isfinite(xv) & (np.abs(xv) <= 8)
+    xb, xv = allx[keep], xv[keep]
+    p, g = orc.sig_prog_eval(sig_prog, xb, order)
+    pv, gv = bf16v(p), bf16v(g)
+    ref = 1.0 / (1.0 + np.exp(-(xv - math.log(4096))))
+    dref = ref * (1.0 - ref)
+    mid = (xv >= -2) & (xv <= 4)
+    low = xv < -2
+    assert np.max(np.abs(pv[mid] - ref[mid]) / ref[mid]) < 0.10
+    assert np.max(np.abs(gv[mid] - dref[mid]) / dref[mid]) < 0.12
+    assert np.max(np.abs(pv[low] - ref[low])) < 3e-5
+    assert np.max(np.abs(gv[low] - dref[low])) < 4e-5
+    assert np.all(pv >= 0)
+    # at s = 0 the value is c_0 = 2^-12, within 0.03 % of 1 / (1 + 4096)
+    p0, _ = orc.sig_prog_eval(sig_prog, [0], order)
+    assert abs(bf16v(p0)[0] * 4097 - 1) < 3e-4
+    # the two regions meet at the threshold 1.25 to within 2 %
+    r = [bf16v(orc.sig_prog_eval(sig_prog, bf16_bits([t]), order)[0])[0]
+         for t in (1.2421875, 1.25)]
+    assert abs(r[1] - r[0]) / r[1] < 0.02
+
+
+def test_dtanh_program_is_derivative_of_tanh_program(orc, tanh_prog):
+    """q(x) = p'(min(|x|, Lc)) in FP16: against a central difference of the
+    real polynomial (orc_prog_real), to FP16 Horner accuracy."""
+    allx = np.arange(0, 0x7C00, dtype=np.uint16)
+    xv = f16v(allx)
+    keep = xv < tanh_prog.Lc
+    xb, xv = allx[keep], xv[keep]
+    q = f16v(orc.dtanh_prog_f16(tanh_prog, xb))
+    L = orc.lib()
+    h = 1e-6
+    fd = np.array([(L.orc_prog_real(tanh_prog, x + h) - L.orc_prog_real(tanh_prog, x - h)) / (2 * h)
+                   if x > h else (L.orc_prog_real(tanh_prog, x + h) - L.orc_prog_real(tanh_prog, x)) / h
+                   for x in xv])
+    assert np.max(np.abs(q - fd)) < 3e-3
+    # beyond the clamp the program holds its value at Lc
+    lc = np.float16(tanh_prog.Lc).view(np.uint16)
+    big = np.array([lc, 0x4500, 0x7BFF], np.uint16)
+    assert len(set(orc.dtanh_prog_f16(tanh_prog, big).tolist())) == 1

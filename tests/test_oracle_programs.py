@@ -193,42 +193,3 @@ def test_swiglu_row_range(orc, progs):
     full = orc.swiglu_fwd(progs["sigmoid_fwd_d3"], g, u)
     assert np.array_equal(h[3:7], full[3:7])
     assert not h[:3].any() and not h[7:].any()
-
-
-def _textbook_attn(q, k, v, cap, causal, score_fn):
-    B, H, S, D = q.shape
-    s = np.einsum("bhid,bhjd->bhij", q, k)
-    s = score_fn(s)
-    if causal:
-        s = np.where(np.tril(np.ones((S, S), bool)), s, -np.inf)
-    s = s - s.max(-1, keepdims=True)
-    w = np.exp(s)
-    w /= w.sum(-1, keepdims=True)
-    return np.einsum("bhij,bhjd->bhid", w, v)
-
-
-@pytest.mark.parametrize("causal", [True, False])
-def test_attention_rows_against_textbook(orc, progs, causal):
-    rng = np.random.default_rng(8)
-    B, H, S, D, cap = 1, 2, 70, 32, 50.0
-    def bf(a):
-        return torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
-    q, k, v = (bf(rng.standard_normal((B, H, S, D)) * 3) for _ in range(3))
-    qf, kf, vf = (bf16v(a) for a in (q, k, v))
-    rows = np.arange(B * H * S)
-    # exact tanh softcap: textbook softcapped softmax attention
-    o, noise = orc.softcap_attn_rows(progs["tanh_fwd_d4"], False, q, k, v, cap, causal, rows)
-    ref = _textbook_attn(qf, kf, vf, cap, causal, lambda s: cap * np.tanh(s / (cap * np.sqrt(D))))
-    np.testing.assert_allclose(o, ref.reshape(-1, D), rtol=1e-12, atol=1e-13)
-    assert np.all(noise >= 0)
-    # polynomial softcap: the score is cap * tanh~(RN_f16(RN32(RN32(s) * scale))),
-    # the D4 tanh program in FP16 arithmetic
-    tp = progs["tanh_fwd_d4"]
-    scale = np.float32(1.0 / (cap * np.sqrt(D)))
-    def poly_score(s):
-        xs = (s.astype(np.float32) * scale).astype(np.float32)
-        xh = xs.astype(np.float16).view(np.uint16)
-        return cap * f16v(orc.act_fwd(tp, xh.ravel(), 1)).reshape(s.shape)
-    o, _ = orc.softcap_attn_rows(tp, True, q, k, v, cap, causal, rows)
-    ref = _textbook_attn(qf, kf, vf, cap, causal, poly_score)
-    np.testing.assert_allclose(o, ref.reshape(-1, D), rtol=1e-12, atol=1e-13)
