@@ -15,8 +15,8 @@ cpu_baseline = the CPU oracle replaying the same programs on a bounded
           sample of the same arrays, on this host's cores.
 Also reported: each program's Gelem/s and share of HBM peak, the matched
 accurate-expf comparator and the speedup (alternating rounds, median of
-per-round times), the L2-resident 4,194,304-element endpoint, and the fused
-SwiGLU / softcap-attention components.
+per-round times), the L2-resident 4,194,304-element endpoint, the fused
+SwiGLU components, and softcap / sigmoid attention forward and backward.
 """
 from __future__ import annotations
 
@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-components", action="store_true", help="skip SwiGLU / attention")
     ap.add_argument("--only", default="", help="profile helper: run one kernel name only")
+    ap.add_argument("--components-only", action="store_true",
+                    help="profiling run: only the SwiGLU and attention components")
     ap.add_argument("--step-only", action="store_true",
                     help="profiling run: warm-up and timed steps, then one plain device copy "
                          "of x (1,073,741,824 bytes moved) as the counter reference")
@@ -123,8 +125,10 @@ def cpu_baseline(x_t, g_t, budget_s=12.0):
 
 
 def components(torch, pa, si):
-    """Fused SwiGLU (dense 8192 x 14336; routed 131,072 x 1408) and softcap
-    attention (1 x 16 x 8192 x 128, causal), poly vs accurate comparator."""
+    """Fused SwiGLU (dense 8192 x 14336; routed 131,072 x 1408), softcap
+    attention forward and backward (1 x 16 x 8192 x 128, causal) and sigmoid
+    attention forward and backward (1 x 32 (8 kv) x 4096 x 128, causal),
+    poly vs accurate comparator."""
     res = {}
     g, u, d = si.t_swiglu_inputs(8192, 14336)
     h, dg, du = torch.empty_like(g), torch.empty_like(g), torch.empty_like(g)
@@ -157,18 +161,59 @@ def components(torch, pa, si):
                      "speedup": round(tn / tp, 3), "gelem_s": round(n / tp / 1e6, 2),
                      "pct_hbm": round(100 * n * by / tp / 1e6 / HBM_PEAK_GBS, 1)}
     del g, u, d, h, dg, du
+
+    def attn_row(tp, tn, flops, extra):
+        row = dict(extra)
+        row.update({"poly_ms": round(tp, 4), "native_ms": round(tn, 4), "speedup": round(tn / tp, 3),
+                    "tflops": round(flops / tp / 1e9, 1),
+                    "pct_mfma_bf16": round(100 * flops / tp / 1e9 / BF16_DENSE_TFLOPS, 1)})
+        return row
+
+    # softcap attention, 1 x 16 x 8192 x 128 causal: forward, and backward
+    # from the forward's O and lse.  MFMA FLOP: forward 2 products of 2 D
+    # flop per visible score; backward 5 (dV, dP, dQ, dK and the recomputed
+    # S), i.e. 2.5x the forward.
     q, k, v = si.t_attn_inputs(1, 16, 8192, 128)
+    dout = si.t_attn_grad(1, 16, 8192, 128)
     o = torch.empty_like(q)
+    scores = 16 * 8192 * 8193 // 2
+    flops = 4 * 128 * scores
     fp = lambda: pa.poly_softcap_attn_fwd(q, k, v, 50.0, True, out=o)  # noqa: E731
     fn = lambda: pa.native_softcap_attn_fwd(q, k, v, 50.0, True, out=o)  # noqa: E731
     fp(), fn()
     tp, tn = alternating(torch, fp, fn, 5, 5)
-    scores = 16 * 8192 * 8193 // 2
+    res["softcap_attn_fwd"] = attn_row(tp, tn, flops, {"causal_scores": scores})
+    op, lp = pa.poly_softcap_attn_fwd(q, k, v, 50.0, True, with_lse=True)
+    on, ln = pa.native_softcap_attn_fwd(q, k, v, 50.0, True, with_lse=True)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty((1, 16, 8192), dtype=torch.float32, device=q.device)
+    fp = lambda: pa.poly_softcap_attn_bwd(q, k, v, op, dout, lp, 50.0, True, dq=dq, dk=dk, dv=dv,  # noqa: E731
+                                          workspace=ws)
+    fn = lambda: pa.native_softcap_attn_bwd(q, k, v, on, dout, ln, 50.0, True, dq=dq, dk=dk,  # noqa: E731
+                                            dv=dv, workspace=ws)
+    fp(), fn()
+    tp, tn = alternating(torch, fp, fn, 5, 5)
+    res["softcap_attn_bwd"] = attn_row(tp, tn, 2.5 * flops, {"causal_scores": scores})
+    del q, k, v, dout, o, op, on, lp, ln, dq, dk, dv, ws
+
+    # sigmoid attention at the program's fitted length: B = 1, 32 query heads
+    # on 8 key/value heads, S = 4096, D = 128, causal
+    q, k, v = si.t_attn_inputs(1, 32, 4096, 128, Hkv=8)
+    dout = si.t_attn_grad(1, 32, 4096, 128)
+    o = torch.empty_like(q)
+    scores = 32 * 4096 * 4097 // 2
     flops = 4 * 128 * scores
-    res["softcap_attn_fwd"] = {"causal_scores": scores, "poly_ms": round(tp, 4),
-                               "native_ms": round(tn, 4), "speedup": round(tn / tp, 3),
-                               "tflops": round(flops / tp / 1e9, 1),
-                               "pct_mfma_bf16": round(100 * flops / tp / 1e9 / BF16_DENSE_TFLOPS, 1)}
+    fp = lambda: pa.poly_sigmoid_attn_fwd(q, k, v, True, out=o)  # noqa: E731
+    fn = lambda: pa.native_sigmoid_attn_fwd(q, k, v, True, out=o)  # noqa: E731
+    fp(), fn()
+    tp, tn = alternating(torch, fp, fn, 5, 5)
+    res["sigmoid_attn_fwd"] = attn_row(tp, tn, flops, {"causal_scores": scores})
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    fp = lambda: pa.poly_sigmoid_attn_bwd(q, k, v, dout, True, dq=dq, dk=dk, dv=dv)  # noqa: E731
+    fn = lambda: pa.native_sigmoid_attn_bwd(q, k, v, dout, True, dq=dq, dk=dk, dv=dv)  # noqa: E731
+    fp(), fn()
+    tp, tn = alternating(torch, fp, fn, 5, 5)
+    res["sigmoid_attn_bwd"] = attn_row(tp, tn, 2.5 * flops, {"causal_scores": scores})
     return res
 
 
@@ -184,6 +229,10 @@ def main():
     import synth_inputs as si
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     pa.lib()
+    if args.components_only:
+        print(json.dumps({"components_only": True, "components": components(torch, pa, si)}),
+              flush=True)
+        return
 
     x, g = si.t_cfg2(N_HBM, device="cuda")
     ks, y = kernels(pa, x, g)

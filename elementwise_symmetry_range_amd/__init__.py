@@ -8,7 +8,9 @@ call fails, an exception is raised.
 Programs ("Fast Polynomial Transcendentals for LLMs", arXiv 2610.00049):
 sigmoid D3, tanh D4, SiLU D3 and GELU D5 forward; sigmoid' D4 and tanh' D4
 direct derivative fits for backward; the D3 sigmoid fused into SwiGLU forward
-and backward; the D4 tanh as an attention softcap.
+and backward; the D4 tanh as an attention softcap (forward) and its analytic
+derivative (backward); the two-region sigmoid-attention cubic and its
+factored derivative surrogate.
 """
 from __future__ import annotations
 
@@ -22,7 +24,10 @@ from ._build import LIB as LIB_PATH
 __all__ = [
     "PolyActError", "lib", "program_info", "poly_act_fwd", "poly_act_bwd", "native_act_fwd",
     "native_act_bwd", "poly_swiglu_fwd", "poly_swiglu_bwd", "native_swiglu_fwd",
-    "native_swiglu_bwd", "poly_softcap_attn_fwd", "native_softcap_attn_fwd", "FUNCS",
+    "native_swiglu_bwd", "poly_softcap_attn_fwd", "native_softcap_attn_fwd",
+    "poly_softcap_attn_bwd", "native_softcap_attn_bwd", "poly_sigmoid_attn_fwd",
+    "native_sigmoid_attn_fwd", "poly_sigmoid_attn_bwd", "native_sigmoid_attn_bwd",
+    "sigmoid_attn_program", "FUNCS",
 ]
 
 FUNCS = {"sigmoid": 1, "tanh": 2, "silu": 3, "gelu": 4}
@@ -35,6 +40,12 @@ class PaProgram(C.Structure):
     _fields_ = [("func", C.c_int32), ("deriv", C.c_int32), ("degree", C.c_int32),
                 ("dtype", C.c_int32), ("Li", C.c_float), ("Lc", C.c_float),
                 ("coeff_bits", C.c_uint16 * 8), ("order", C.c_int32)]
+
+
+class PaSigmoidAttnProgram(C.Structure):
+    _fields_ = [("n", C.c_int32), ("thr", C.c_uint16), ("clamp_lo", C.c_uint16),
+                ("clamp_hi", C.c_uint16), ("coeff_bits", (C.c_uint16 * 4) * 2),
+                ("a_bits", C.c_uint16 * 2), ("b_bits", C.c_uint16 * 2), ("order", C.c_int32)]
 
 
 class PolyActError(RuntimeError):
@@ -65,8 +76,15 @@ def lib() -> C.CDLL:
             "poly_swiglu_bwd": [i32, p, p, p, p, p, i64, i64, i64, i64, i64, i64, i64, p, i32, p],
             "native_swiglu_bwd": [i32, p, p, p, p, p, i64, i64, i64, i64, i64, i64, i64, p, i32,
                                   p],
-            "poly_softcap_attn_fwd": [p, p, p, p, i32, i32, i32, i32, f32, i32, p],
-            "native_softcap_attn_fwd": [p, p, p, p, i32, i32, i32, i32, f32, i32, p],
+            "poly_softcap_attn_fwd": [p, p, p, p, p, i32, i32, i32, i32, i32, f32, i32, p],
+            "native_softcap_attn_fwd": [p, p, p, p, p, i32, i32, i32, i32, i32, f32, i32, p],
+            "poly_softcap_attn_bwd": [p] * 10 + [i32] * 5 + [f32, i32, p],
+            "native_softcap_attn_bwd": [p] * 10 + [i32] * 5 + [f32, i32, p],
+            "poly_sigmoid_attn_fwd": [p] * 4 + [i32] * 6 + [p],
+            "native_sigmoid_attn_fwd": [p] * 4 + [i32] * 6 + [p],
+            "poly_sigmoid_attn_bwd": [p] * 7 + [i32] * 6 + [p],
+            "native_sigmoid_attn_bwd": [p] * 7 + [i32] * 6 + [p],
+            "poly_sigmoid_attn_program": [C.POINTER(PaSigmoidAttnProgram)],
             "poly_program_info": [i32, i32, i32, C.POINTER(PaProgram)],
         }
         for name, args in sigs.items():
@@ -217,23 +235,134 @@ def native_swiglu_bwd(gate, up, dh, out=None, row_offsets=None):
     return _swiglu_bwd(lib().native_swiglu_bwd, gate, up, dh, out, row_offsets)
 
 
-def _attn(entry, q, k, v, cap, causal, out):
+def _bf16_4d(t, name):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.bfloat16 \
+            or t.dim() != 4 or not t.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous bfloat16 CUDA tensor [B, H, S, D]")
+
+
+def _attn_shapes(q, k, v):
     for name, t in (("q", q), ("k", k), ("v", v)):
-        if not t.is_cuda or t.dtype != torch.bfloat16 or t.dim() != 4 or not t.is_contiguous():
-            raise TypeError(f"{name} must be a contiguous bfloat16 CUDA tensor [B, H, S, D]")
-    if k.shape != q.shape or v.shape != q.shape:
-        raise ValueError("q, k, v must have the same shape")
-    o = torch.empty_like(q) if out is None else out
+        _bf16_4d(t, name)
     B, H, S, D = q.shape
-    _check(entry(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), B, H, S, D, float(cap),
+    if k.shape != v.shape or k.shape[0] != B or k.shape[2:] != q.shape[2:]:
+        raise ValueError("k and v must be [B, Hkv, S, D] with q's B, S and D")
+    return B, H, k.shape[1], S, D
+
+
+def _like(out, ref, name):
+    if out is None:
+        return torch.empty_like(ref)
+    _bf16_4d(out, name)
+    if out.shape != ref.shape:
+        raise ValueError(f"{name} must have shape {tuple(ref.shape)}")
+    return out
+
+
+def _softcap_fwd(entry, q, k, v, cap, causal, out, with_lse):
+    B, H, Hkv, S, D = _attn_shapes(q, k, v)
+    o = _like(out, q, "out")
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device) if with_lse else None
+    _check(entry(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                 None if lse is None else lse.data_ptr(), B, H, Hkv, S, D, float(cap),
+                 int(bool(causal)), _stream(q)))
+    return (o, lse) if with_lse else o
+
+
+def poly_softcap_attn_fwd(q, k, v, cap: float = 50.0, causal: bool = True, out=None,
+                          with_lse: bool = False):
+    """Softcapped attention forward with the D4 tanh program (BF16, D = 128).
+    q [B, H, S, D], k and v [B, Hkv, S, D].  Returns O, or (O, lse) with
+    with_lse (the natural log-sum-exp per row, FP32 [B, H, S])."""
+    return _softcap_fwd(lib().poly_softcap_attn_fwd, q, k, v, cap, causal, out, with_lse)
+
+
+def native_softcap_attn_fwd(q, k, v, cap: float = 50.0, causal: bool = True, out=None,
+                            with_lse: bool = False):
+    return _softcap_fwd(lib().native_softcap_attn_fwd, q, k, v, cap, causal, out, with_lse)
+
+
+def _grads(q, k, dq, dk, dv):
+    return _like(dq, q, "dq"), _like(dk, k, "dk"), _like(dv, k, "dv")
+
+
+def _softcap_bwd(entry, q, k, v, o, dout, lse, cap, causal, dq, dk, dv, workspace):
+    B, H, Hkv, S, D = _attn_shapes(q, k, v)
+    _bf16_4d(o, "o")
+    _bf16_4d(dout, "dout")
+    if o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("o and dout must have q's shape")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, S) or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [B, H, S]")
+    dq, dk, dv = _grads(q, k, dq, dk, dv)
+    if workspace is None:
+        workspace = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    elif workspace.dtype != torch.float32 or workspace.numel() < B * H * S:
+        raise ValueError("workspace must be float32 with at least B * H * S elements")
+    _check(entry(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                 lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                 workspace.data_ptr(), B, H, Hkv, S, D, float(cap), int(bool(causal)),
+                 _stream(q)))
+    return dq, dk, dv
+
+
+def poly_softcap_attn_bwd(q, k, v, o, dout, lse, cap: float = 50.0, causal: bool = True,
+                          dq=None, dk=None, dv=None, workspace=None):
+    """Backward of poly_softcap_attn_fwd: (dq, dk, dv), with the analytic
+    derivative of the D4 tanh program."""
+    return _softcap_bwd(lib().poly_softcap_attn_bwd, q, k, v, o, dout, lse, cap, causal, dq, dk,
+                        dv, workspace)
+
+
+def native_softcap_attn_bwd(q, k, v, o, dout, lse, cap: float = 50.0, causal: bool = True,
+                            dq=None, dk=None, dv=None, workspace=None):
+    return _softcap_bwd(lib().native_softcap_attn_bwd, q, k, v, o, dout, lse, cap, causal, dq,
+                        dk, dv, workspace)
+
+
+def _sigmoid_fwd(entry, q, k, v, causal, out):
+    B, H, Hkv, S, D = _attn_shapes(q, k, v)
+    o = _like(out, q, "out")
+    _check(entry(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), B, H, Hkv, S, D,
                  int(bool(causal)), _stream(q)))
     return o
 
 
-def poly_softcap_attn_fwd(q, k, v, cap: float = 50.0, causal: bool = True, out=None):
-    """Softcapped attention forward with the D4 tanh program (BF16, D = 128)."""
-    return _attn(lib().poly_softcap_attn_fwd, q, k, v, cap, causal, out)
+def poly_sigmoid_attn_fwd(q, k, v, causal: bool = True, out=None):
+    """Sigmoid attention O = sigma(s - ln S) V with the two-region cubic
+    (S must be the program's fitted length, 4096)."""
+    return _sigmoid_fwd(lib().poly_sigmoid_attn_fwd, q, k, v, causal, out)
 
 
-def native_softcap_attn_fwd(q, k, v, cap: float = 50.0, causal: bool = True, out=None):
-    return _attn(lib().native_softcap_attn_fwd, q, k, v, cap, causal, out)
+def native_sigmoid_attn_fwd(q, k, v, causal: bool = True, out=None):
+    return _sigmoid_fwd(lib().native_sigmoid_attn_fwd, q, k, v, causal, out)
+
+
+def _sigmoid_bwd(entry, q, k, v, dout, causal, dq, dk, dv):
+    B, H, Hkv, S, D = _attn_shapes(q, k, v)
+    _bf16_4d(dout, "dout")
+    if dout.shape != q.shape:
+        raise ValueError("dout must have q's shape")
+    dq, dk, dv = _grads(q, k, dq, dk, dv)
+    _check(entry(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(), dq.data_ptr(),
+                 dk.data_ptr(), dv.data_ptr(), B, H, Hkv, S, D, int(bool(causal)), _stream(q)))
+    return dq, dk, dv
+
+
+def poly_sigmoid_attn_bwd(q, k, v, dout, causal: bool = True, dq=None, dk=None, dv=None):
+    """Backward of poly_sigmoid_attn_fwd with the factored derivative surrogate."""
+    return _sigmoid_bwd(lib().poly_sigmoid_attn_bwd, q, k, v, dout, causal, dq, dk, dv)
+
+
+def native_sigmoid_attn_bwd(q, k, v, dout, causal: bool = True, dq=None, dk=None, dv=None):
+    return _sigmoid_bwd(lib().native_sigmoid_attn_bwd, q, k, v, dout, causal, dq, dk, dv)
+
+
+def sigmoid_attn_program() -> dict:
+    """The sigmoid-attention program the kernels execute (host query)."""
+    out = PaSigmoidAttnProgram()
+    _check(lib().poly_sigmoid_attn_program(C.byref(out)))
+    return {"n": out.n, "thr": out.thr, "clamp_lo": out.clamp_lo, "clamp_hi": out.clamp_hi,
+            "coeff_bits": [[int(out.coeff_bits[r][j]) for j in range(4)] for r in range(2)],
+            "a_bits": [int(x) for x in out.a_bits], "b_bits": [int(x) for x in out.b_bits],
+            "order": out.order}

@@ -21,7 +21,7 @@ HIPCC_FLAGS = [
 
 
 # the sources that define the elementwise streaming kernels and their launch
-STREAM_SOURCES = ("ops.hpp", "stream.hpp", "programs.hpp", "polyact.hip")
+STREAM_SOURCES = ("ops.hpp", "stream.hpp", "stream_launch.hpp", "programs.hpp")
 
 
 def source_digest(files=STREAM_SOURCES) -> str:

@@ -1,15 +1,25 @@
-// attn.hpp -- softcapped flash-attention forward on gfx950 MFMA.
+// attn.hpp -- flash-attention forward with a transformed score, gfx950 MFMA.
 //
-// Scores are transformed by the softcap alpha tanh(x / alpha) ("Fast
-// Polynomial Transcendentals for LLMs", Eq. 1) inside the attention tile;
-// the polynomial variant evaluates the D4 tanh program (section 5.2.2 puts a
-// packed D4 tanh inside the attention forward).  On gfx950 the packed 16-bit
-// FMA is FP16 (v_pk_fma_f16); there is no packed BF16 FMA.  The program
-// therefore runs in packed FP16 on x = RN_f16(RN_f32(S) * RN_f32(1/(cap sqrt D))),
-// two scores per instruction, with the FP16 coefficients of the same BF16 fit.
-// The comparator uses accurate FP32 tanhf on the unrounded FP32 x.
+// Two score transforms from "Fast Polynomial Transcendentals for LLMs":
+//   softcap  s = cap tanh(x / cap) on the logits, then softmax (Eq. 1); the
+//            polynomial variant evaluates the D4 tanh program (section 5.2.2
+//            puts a packed D4 tanh inside the attention forward);
+//   sigmoid  P = sigma(s - ln n), no normalisation (Eq. 14); the polynomial
+//            variant evaluates the two-region cubic of section 3.4 with ln n
+//            and 1 / n folded into its coefficients (one n only).
+// Each has an accurate FP32 comparator (tanhf; expf and an IEEE divide).
 //
-// Layout and tiling (D = 128):
+// Arithmetic of the programs.  gfx950's packed 16-bit FMA is FP16
+// (v_pk_fma_f16) and it has no packed BF16 FMA.  The tanh program therefore
+// runs in packed FP16 on x = RN_f16(RN_f32(S) * RN_f32(1 / (cap sqrt D))), two
+// scores per instruction, with the FP16 values of the BF16 coefficients.  The
+// sigmoid program keeps the pages' BF16 format: x = RN_bf16(RN_f32(S) *
+// RN_f32(1 / sqrt D)) and each Horner stage is an FP32 FMA rounded to BF16.
+//
+// Layout: Q, O [B, H, S, D]; K, V [B, Hkv, S, D], H a multiple of Hkv (query
+// head h reads key/value head h / (H / Hkv)); D = 128; BF16.
+//
+// Tiling (D = 128):
 //   workgroup = 4 waves = 128 queries of one (batch, head); wave w owns
 //   queries q0 .. q0 + 31.  Blocks are numbered heaviest query tile first
 //   across all heads (causal work grows with the query index).  Key/value
@@ -17,8 +27,8 @@
 //   (no register staging), double buffered with one barrier per tile: tile
 //   kt + 1 streams in while tile kt is consumed.  Rows are 256 B with the
 //   16-byte chunks XOR-swizzled by row: chunk c of row r sits at slot
-//   c ^ f(r), f(r) = 4 (r mod 4) + (r / 4 mod 4).  The K reads (16 lanes =
-//   16 consecutive rows, one chunk) and the transposed V reads (a half-wave =
+//   c ^ f(r), f(r) = 4 (r mod 4) + (r / 4 mod 4).  The row reads (16 lanes =
+//   16 consecutive rows, one chunk) and the transposed reads (a half-wave =
 //   4 consecutive rows x 4 consecutive chunks) then each touch 16 distinct
 //   slots, i.e. all 64 banks once.
 //   S^T = K Q^T on v_mfma_f32_32x32x16_bf16: A = K rows from LDS, B = Q held
@@ -32,11 +42,14 @@
 //   instruction returns to lane i element (i mod 4) of the 4-element vectors
 //   addressed by lanes i/4, i/4 + 4, i/4 + 8, i/4 + 12, so lanes addressing
 //   V[k0 + j/4][d0 + 4 (j mod 4)] deliver V[k0 .. k0 + 3][d0 + i] to lane i.
-//   Online softmax in the log2 domain (cap * log2 e folded in).  The running
-//   reference max is only moved when a row's max exceeds it by more than 8
-//   (so P <= 2^8): the O rescale (64 multiplies per lane) is skipped for
-//   almost every tile and the result is unchanged up to rounding.  P is
-//   rounded to BF16 for the MFMA, O^T accumulated in FP32, O = O^T / l.
+//   Softcap: online softmax in the log2 domain (cap * log2 e folded in).  The
+//   running reference max is only moved when a row's max exceeds it by more
+//   than 8 (so P <= 2^8): the O rescale (64 multiplies per lane) is skipped
+//   for almost every tile and the result is unchanged up to rounding.  P is
+//   rounded to BF16 for the MFMA, O^T accumulated in FP32, O = O^T / l, and
+//   the natural log-sum-exp of each row is written for the backward.
+//   Sigmoid: P (already BF16 for the program) goes straight into the MFMA;
+//   O = O^T.
 #pragma once
 #include <type_traits>
 
@@ -46,23 +59,40 @@ namespace pa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int AT_D = 128;
 constexpr int AT_BM = 128;          // queries per workgroup
 constexpr int AT_BN = 64;           // keys per tile
-constexpr int AT_TILE = AT_BN * AT_D;   // elements of one K or V tile in LDS
+constexpr int AT_TILE = AT_BN * AT_D;   // elements of one 64-row tile in LDS
 constexpr float AT_RESCALE = 8.0f;  // log2 headroom before the reference max moves
+constexpr float AT_LN2 = 0.693147180559945309f;
+constexpr float AT_LOG2E = 1.442695040888963407f;
+
+// score transforms
+enum { AM_SOFTCAP_POLY = 0, AM_SOFTCAP_NATIVE = 1, AM_SIGMOID_POLY = 2, AM_SIGMOID_NATIVE = 3 };
+__host__ __device__ constexpr bool am_softcap(int m) { return m == AM_SOFTCAP_POLY || m == AM_SOFTCAP_NATIVE; }
+
+// two-region sigmoid program as FP32 values of its BF16 constants
+struct SigCoef {
+    float c[2][4];
+    float a[2], b[2];
+    float thr, lo, hi;
+};
 
 struct AttnArgs {
     const uint16_t *q, *k, *v;
     uint16_t *o;
-    int32_t S;
+    float *lse;        // softcap: natural log-sum-exp per query row (nullable)
+    int32_t S, H, G;   // G = H / Hkv
     int32_t causal;
-    float scale;       // RN_f32(1 / (cap sqrt(D)))
-    float c2;          // RN_f32(cap * log2(e))
+    float scale;       // softcap: RN_f32(1 / (cap sqrt D)); sigmoid: RN_f32(1 / sqrt D)
+    float c2;          // softcap: RN_f32(cap * log2(e))
+    float logn;        // sigmoid comparator: RN_f32(ln S)
     CoefF16 tanh16;    // D4 tanh program, FP16 coefficients
+    SigCoef sig;
 };
 
 __device__ __forceinline__ bf16x8 ld_bf16x8(const uint16_t *p) { return *(const bf16x8 *)p; }
@@ -77,9 +107,108 @@ __device__ __forceinline__ u32x2 ds_read_tr16(const uint16_t *p)
     return bc<u32x2>(r);
 }
 
-template <bool POLY>
+// A 64-row tile of a [rows, 128] BF16 matrix into LDS, rows past S repeating
+// row S - 1 (finite data; those rows are masked).  16 wave instructions per
+// tile, 4 per wave: instruction r of wave w fills LDS bytes [(4 w + r) KiB,
+// +1 KiB): lane p writes slot p % 16 of row (4 w + r) * 4 + p / 16, so it
+// fetches the chunk that belongs in that slot.
+__device__ __forceinline__ void load_rows64(const uint16_t *src, uint16_t *lds, int row0, int S,
+                                            int wave, int lane)
+{
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int row = (wave * 4 + r) * 4 + (lane >> 4);
+        const int slot = lane & 15;
+        int g = row0 + row;
+        g = g < S ? g : S - 1;
+        const int64_t off = (int64_t)g * AT_D + swz(row, slot) * 8;
+        const int dst = __builtin_amdgcn_readfirstlane((wave * 4 + r) * 512);
+        __builtin_amdgcn_global_load_lds((const void *)(src + off),
+                                         (void __attribute__((address_space(3))) *)(lds + dst),
+                                         16, 0, 0);
+    }
+}
+
+// 8 BF16 of row `row`, chunk `chunk` of a swizzled LDS tile
+__device__ __forceinline__ bf16x8 lds_row8(const uint16_t *t, int row, int chunk)
+{
+    return ld_bf16x8(t + row * AT_D + swz(row, chunk) * 8);
+}
+
+// A operand (8 x 4 BF16 per lane as two tr16 reads) of X^T for the
+// contraction step ks over 64 rows of a swizzled row-major tile, d block d0:
+// lane (i16, g16) provides rows k0 .. k0 + 3 and k0 + 8 .. k0 + 11 of column
+// d, where the contraction order matches the permuted B operand built from a
+// 32x32 accumulator (see the header).
+__device__ __forceinline__ bf16x8 lds_tr_a(const uint16_t *t, int ks, int db, int g16, int i16)
+{
+    const int d = db * 32 + (g16 & 1) * 16 + 4 * (i16 & 3);
+    const int k0 = (ks >> 1) * 32 + (ks & 1) * 16 + (g16 >> 1) * 4 + (i16 >> 2);
+    const u32x2 lo = ds_read_tr16(t + k0 * AT_D + swz(k0, d >> 3) * 8 + (d & 7));
+    const u32x2 hi = ds_read_tr16(t + (k0 + 8) * AT_D + swz(k0 + 8, d >> 3) * 8 + (d & 7));
+    const u32x4 av = {lo.x, lo.y, hi.x, hi.y};
+    return bc<bf16x8>(av);
+}
+
+// ---- score transforms on a pair of raw FP32 scores --------------------------
+
+// softcap program: packed FP16 tanh~ of x = RN_f16(s * scale); returns the
+// packed FP16 t and (through xabs) the packed |x| for the derivative program.
+__device__ __forceinline__ uint32_t softcap_poly_pair(float s0, float s1, float scale,
+                                                      const CoefF16 &k, uint32_t &aw)
+{
+    // the FP32 product rounded once to FP16 equals RN_f16(RN_f32(s * scale))
+    // only through the explicit FP32 multiply (no contraction)
+    h2 xh;
+    xh[0] = (_Float16)fmaf(s0, scale, -0.0f);
+    xh[1] = (_Float16)fmaf(s1, scale, -0.0f);
+    const uint32_t xw = bc<uint32_t>(xh);
+    aw = xw & 0x7FFF7FFFu;
+    const h2 v = horner_f16<4, true>(bc<h2>(min_u16x2(aw, k.lc)), k);
+    return bc<uint32_t>(v) ^ (xw ^ aw);
+}
+
+// sigmoid program on a pair: packed BF16 P~ (and the packed BF16 surrogate
+// derivative when GRAD)
+template <bool GRAD>
+__device__ __forceinline__ uint32_t sigmoid_poly_pair(float s0, float s1, float scale,
+                                                      const SigCoef &k, uint32_t *grad)
+{
+    const uint32_t xw = pack_bf(s0 * scale, s1 * scale);
+    const float x0 = lo_f(xw), x1 = hi_f(xw);
+    const int r0 = x0 >= k.thr, r1 = x1 >= k.thr;
+    const float t0 = fminf(fmaxf(x0, k.lo), k.hi);
+    const float t1 = fminf(fmaxf(x1, k.lo), k.hi);
+    float v0 = r0 ? k.c[1][3] : k.c[0][3];
+    float v1 = r1 ? k.c[1][3] : k.c[0][3];
+    uint32_t w = 0;
+#pragma unroll
+    for (int j = 2; j >= 0; --j) {
+        w = pack_bf(fmaf(t0, v0, r0 ? k.c[1][j] : k.c[0][j]), fmaf(t1, v1, r1 ? k.c[1][j] : k.c[0][j]));
+        v0 = lo_f(w);
+        v1 = hi_f(w);
+    }
+    v0 = fmaxf(v0, 0.0f);
+    v1 = fmaxf(v1, 0.0f);
+    if constexpr (GRAD) {
+        const uint32_t fw = pack_bf(fmaf(t0, r0 ? k.b[1] : k.b[0], r0 ? k.a[1] : k.a[0]),
+                                    fmaf(t1, r1 ? k.b[1] : k.b[0], r1 ? k.a[1] : k.a[0]));
+        *grad = pack_bf(v0 * lo_f(fw), v1 * hi_f(fw));
+    }
+    return pack_bf(v0, v1);   // exact: v0, v1 are BF16 values
+}
+
+// accurate sigmoid of u (the comparator)
+__device__ __forceinline__ float sigmoid_acc(float u)
+{
+    const float e = expf(-fabsf(u));
+    return (u >= 0.0f ? 1.0f : e) / (1.0f + e);
+}
+
+template <int MODE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_fwd(AttnArgs a)
 {
+    constexpr bool SOFTCAP = am_softcap(MODE);
     __shared__ __attribute__((aligned(16))) uint16_t Ks[2][AT_TILE];
     __shared__ __attribute__((aligned(16))) uint16_t Vs[2][AT_TILE];
 
@@ -93,8 +222,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int qrank = (int)blockIdx.x / nbh;          // 0 = heaviest query tile
     const int bh = (int)blockIdx.x - qrank * nbh;
     const int qt = a.causal ? ntq - 1 - qrank : qrank;
-    const int64_t base = (int64_t)bh * S * AT_D;
-    const uint16_t *Q = a.q + base, *K = a.k + base, *V = a.v + base;
+    const int64_t qbase = (int64_t)bh * S * AT_D;
+    const int64_t kvbase = (int64_t)(bh / a.G) * S * AT_D;   // (b H + h) / G = b Hkv + h / G
+    const uint16_t *Q = a.q + qbase, *K = a.k + kvbase, *V = a.v + kvbase;
     const int q0 = qt * AT_BM + wave * 32;
     const int my_q = q0 + col;
 
@@ -109,43 +239,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     f32x16 o[4];
 #pragma unroll
     for (int db = 0; db < 4; ++db) o[db] = f32x16{};
-    float m = -INFINITY;   // reference max of the log2-domain score
-    float l = 0.0f;        // this lane's partial row sum
+    float m = -INFINITY;   // reference max of the log2-domain score (softcap)
+    float l = 0.0f;        // this lane's partial row sum (softcap)
 
     const int kend = a.causal ? (qt * AT_BM + AT_BM < S ? qt * AT_BM + AT_BM : S) : S;
     const int nkt = (kend + AT_BN - 1) / AT_BN;
 
-    // One tile = 64 rows x 16 chunks of 16 B for each of K and V: 16 wave
-    // instructions each, 4 per wave.  Instruction r of wave w fills LDS bytes
-    // [(4 w + r) KiB, +1 KiB): lane p writes slot p % 16 of row (4 w + r) * 4 +
-    // p / 16, so it fetches the chunk that belongs in that slot.  Rows past S
-    // repeat row S - 1 (finite data; those keys are masked).
-    auto load_tile = [&](int kt, int buf) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = (wave * 4 + r) * 4 + (lane >> 4);
-            const int slot = lane & 15;
-            int g = kt * AT_BN + row;
-            g = g < S ? g : S - 1;
-            const int64_t src = (int64_t)g * AT_D + swz(row, slot) * 8;
-            const int dst = __builtin_amdgcn_readfirstlane((wave * 4 + r) * 512);
-            __builtin_amdgcn_global_load_lds((const void *)(K + src),
-                                             (void __attribute__((address_space(3))) *)(&Ks[buf][dst]),
-                                             16, 0, 0);
-            __builtin_amdgcn_global_load_lds((const void *)(V + src),
-                                             (void __attribute__((address_space(3))) *)(&Vs[buf][dst]),
-                                             16, 0, 0);
-        }
-    };
-
-    load_tile(0, 0);
+    load_rows64(K, Ks[0], 0, S, wave, lane);
+    load_rows64(V, Vs[0], 0, S, wave, lane);
     // One tile; BUF is the LDS buffer holding it (a constant: the loop below
     // is unrolled by two so that buffer bases become immediate offsets).
     auto tile = [&](int kt, auto bufc) {
         constexpr int buf = decltype(bufc)::value;
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's share of tile kt landed
         __syncthreads();   // all of tile kt landed; nobody reads buffer buf ^ 1 any more
-        if (kt + 1 < nkt) load_tile(kt + 1, buf ^ 1);
+        if (kt + 1 < nkt) {
+            load_rows64(K, Ks[buf ^ 1], (kt + 1) * AT_BN, S, wave, lane);
+            load_rows64(V, Vs[buf ^ 1], (kt + 1) * AT_BN, S, wave, lane);
+        }
 
         const int key0 = kt * AT_BN;
         if (a.causal && key0 > q0 + 31) return;   // tile entirely above this wave's rows
@@ -159,38 +270,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int kb = 0; kb < 2; ++kb) {
             s[kb] = f32x16{};
 #pragma unroll
-            for (int ks = 0; ks < 8; ++ks) {
-                const int row = kb * 32 + col;
-                const bf16x8 af = ld_bf16x8(Kb + row * AT_D + swz(row, ks * 2 + h) * 8);
-                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[ks], s[kb], 0, 0, 0);
-            }
+            for (int ks = 0; ks < 8; ++ks)
+                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row8(Kb, kb * 32 + col, ks * 2 + h),
+                                                                qf[ks], s[kb], 0, 0, 0);
         }
 
-        // ---- score transform: t = tanh(x), z = t * cap * log2(e) ------------
+        // ---- score transform ---------------------------------------------
         // s[kb][j*4 + i] is the score of key key0 + kb*32 + j*8 + h*4 + i.
-        // Masked keys (beyond the query, or beyond S) get t = -inf.  Tiles
-        // that need no mask (all but the diagonal and the ragged end) take a
-        // branch-free pass without the key arithmetic.
+        // Masked keys (beyond the query, or beyond S) get t = -inf (softcap)
+        // or P = 0 (sigmoid).  Tiles that need no mask (all but the diagonal
+        // and the ragged end) take a branch-free pass without the key
+        // arithmetic.
         const bool need_mask = (a.causal && key0 + AT_BN - 1 > q0) || key0 + AT_BN > S;
         const int lim = a.causal ? (my_q < S - 1 ? my_q : S - 1) : S - 1;   // last visible key
-        float tmax;
+        float tmax = -INFINITY;
+        bf16x8 pf[4];
         auto transform = [&](auto masked) {
             constexpr bool MASKED = decltype(masked)::value;
-            if constexpr (POLY) {
+            if constexpr (MODE == AM_SOFTCAP_POLY) {
                 uint32_t mx = 0xFC00FC00u;   // packed FP16 -inf
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
                     for (int e = 0; e < 16; e += 2) {
-                        // x = RN_f16(s * scale): the FP32 product rounded once to
-                        // FP16 equals RN_f16(RN_f32(s * scale)) (24 >= 2 * 11 + 2)
-                        h2 xh;
-                        xh[0] = (_Float16)fmaf(s[kb][e], a.scale, -0.0f);
-                        xh[1] = (_Float16)fmaf(s[kb][e + 1], a.scale, -0.0f);
-                        const uint32_t xw = bc<uint32_t>(xh);
-                        const uint32_t aw = xw & 0x7FFF7FFFu;
-                        const h2 v = horner_f16<4, true>(bc<h2>(min_u16x2(aw, a.tanh16.lc)), a.tanh16);
-                        uint32_t w = bc<uint32_t>(v) ^ (xw ^ aw);
+                        uint32_t aw;
+                        uint32_t w = softcap_poly_pair(s[kb][e], s[kb][e + 1], a.scale, a.tanh16, aw);
                         if constexpr (MASKED) {
                             const int k0 = key0 + kb * 32 + (e >> 2) * 8 + h * 4 + (e & 3);
                             const uint32_t mlo = k0 > lim ? 0x0000FFFFu : 0u;
@@ -203,8 +307,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     }
                 }
                 tmax = fmaxf(f16_lo(mx), f16_hi(mx));
-            } else {
-                tmax = -INFINITY;
+            } else if constexpr (MODE == AM_SOFTCAP_NATIVE) {
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -218,38 +321,68 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                         tmax = fmaxf(tmax, t);
                     }
                 }
+            } else {
+                // sigmoid: P directly, as BF16 B-operand fragments
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+                    for (int jj = 0; jj < 2; ++jj) {
+                        u32x4 fw;
+#pragma unroll
+                        for (int e2 = 0; e2 < 4; ++e2) {
+                            const int e = jj * 8 + e2 * 2;
+                            uint32_t w;
+                            if constexpr (MODE == AM_SIGMOID_POLY) {
+                                w = sigmoid_poly_pair<false>(s[kb][e], s[kb][e + 1], a.scale, a.sig, nullptr);
+                            } else {
+                                w = pack_bf(sigmoid_acc(fmaf(s[kb][e], a.scale, -a.logn)),
+                                            sigmoid_acc(fmaf(s[kb][e + 1], a.scale, -a.logn)));
+                            }
+                            if constexpr (MASKED) {
+                                const int k0 = key0 + kb * 32 + (e >> 2) * 8 + h * 4 + (e & 3);
+                                const uint32_t mlo = k0 > lim ? 0x0000FFFFu : 0u;
+                                const uint32_t mhi = k0 + 1 > lim ? 0xFFFF0000u : 0u;
+                                w &= ~(mlo | mhi);
+                            }
+                            fw[e2] = w;
+                        }
+                        pf[kb * 2 + jj] = bc<bf16x8>(fw);
+                    }
+                }
             }
         };
         if (need_mask) transform(std::true_type{});
         else transform(std::false_type{});
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        const float zmax = tmax * a.c2;
 
-        // lazy rescale: move the reference only when the row max outgrows it
-        const bool grow = zmax > m + AT_RESCALE;
-        if (__builtin_amdgcn_ballot_w64(grow)) {
-            const float m_new = grow ? zmax : m;
-            const float corr = __builtin_amdgcn_exp2f(m - m_new);
-            l *= corr;
-#pragma unroll
-            for (int db = 0; db < 4; ++db) o[db] *= corr;
-            m = m_new;
-        }
+        if constexpr (SOFTCAP) {
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+            const float zmax = tmax * a.c2;
 
-        // ---- P = exp2(t c2 - m), row sums, BF16 B operands ------------------
-        bf16x8 pf[4];
+            // lazy rescale: move the reference only when the row max outgrows it
+            const bool grow = zmax > m + AT_RESCALE;
+            if (__builtin_amdgcn_ballot_w64(grow)) {
+                const float m_new = grow ? zmax : m;
+                const float corr = __builtin_amdgcn_exp2f(m - m_new);
+                l *= corr;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+                for (int db = 0; db < 4; ++db) o[db] *= corr;
+                m = m_new;
+            }
+
+            // ---- P = exp2(t c2 - m), row sums, BF16 B operands ----------------
 #pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-                bf16x8 frag;
+            for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][jj * 8 + e], a.c2, -m));
-                    l += p;
-                    frag[e] = (__bf16)p;
+                for (int jj = 0; jj < 2; ++jj) {
+                    bf16x8 frag;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][jj * 8 + e], a.c2, -m));
+                        l += p;
+                        frag[e] = (__bf16)p;
+                    }
+                    pf[kb * 2 + jj] = frag;
                 }
-                pf[kb * 2 + jj] = frag;
             }
         }
 
@@ -258,15 +391,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         // kb*32 + jj*16 + (e/4)*8 + h*4 + (e%4)   (ks = 2 kb + jj)
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
-            const int d = db * 32 + (g16 & 1) * 16 + 4 * (i16 & 3);
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const int k0 = (ks >> 1) * 32 + (ks & 1) * 16 + (g16 >> 1) * 4 + (i16 >> 2);
-                const u32x2 lo = ds_read_tr16(Vb + k0 * AT_D + swz(k0, d >> 3) * 8 + (d & 7));
-                const u32x2 hi = ds_read_tr16(Vb + (k0 + 8) * AT_D + swz(k0 + 8, d >> 3) * 8 + (d & 7));
-                const u32x4 av = {lo.x, lo.y, hi.x, hi.y};
-                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bc<bf16x8>(av), pf[ks], o[db], 0, 0, 0);
-            }
+            for (int ks = 0; ks < 4; ++ks)
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_tr_a(Vb, ks, db, g16, i16), pf[ks],
+                                                                o[db], 0, 0, 0);
         }
     };
     for (int kt = 0; kt < nkt; kt += 2) {
@@ -275,9 +403,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
 
     if (my_q >= S) return;
-    const float lt = l + __shfl_xor(l, 32);
-    const float inv = 1.0f / lt;
-    uint16_t *orow = a.o + base + (int64_t)my_q * AT_D;
+    float inv = 1.0f;
+    if constexpr (SOFTCAP) {
+        const float lt = l + __shfl_xor(l, 32);
+        inv = 1.0f / lt;
+        if (a.lse && h == 0) a.lse[(int64_t)bh * S + my_q] = (m + __log2f(lt)) * AT_LN2;
+    }
+    uint16_t *orow = a.o + qbase + (int64_t)my_q * AT_D;
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
 #pragma unroll
@@ -289,37 +421,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             *(u32x2 *)(orow + d) = w;
         }
     }
-}
-
-inline pa_status attn_fwd(const void *q, const void *k, const void *v, void *o, int32_t B,
-                          int32_t H, int32_t S, int32_t D, float cap, int32_t causal, bool poly,
-                          const CoefF16 &tanh16, hipStream_t stream)
-{
-    if (!q || !k || !v || !o) return PA_ERR_NULL;
-    for (const void *p : {q, k, v, (const void *)o})
-        if ((uintptr_t)p & 15u) return PA_ERR_ALIGN;
-    if (B < 0 || H < 0 || S < 0 || D != AT_D) return PA_ERR_SHAPE;
-    if (!(cap > 0.0f) || cap == INFINITY) return PA_ERR_SHAPE;
-    const int64_t bytes = (int64_t)B * H * S * D * 2;
-    for (const void *p : {q, k, v})
-        if ((uintptr_t)o < (uintptr_t)p + (uintptr_t)bytes && (uintptr_t)p < (uintptr_t)o + (uintptr_t)bytes)
-            return PA_ERR_OVERLAP;   // O is written while Q, K, V are still read
-    if ((int64_t)B * H == 0 || S == 0) return PA_OK;
-    if ((int64_t)B * H * ((S + AT_BM - 1) / AT_BM) > 0x7FFFFFFF) return PA_ERR_SHAPE;
-    AttnArgs a;
-    a.q = (const uint16_t *)q;
-    a.k = (const uint16_t *)k;
-    a.v = (const uint16_t *)v;
-    a.o = (uint16_t *)o;
-    a.S = S;
-    a.causal = causal ? 1 : 0;
-    a.scale = (float)(1.0 / ((double)cap * sqrt((double)D)));
-    a.c2 = (float)((double)cap * 1.4426950408889634074);
-    a.tanh16 = tanh16;
-    const dim3 grid((unsigned)(((S + AT_BM - 1) / AT_BM) * (B * H)));
-    if (poly) hipLaunchKernelGGL(k_attn_fwd<true>, grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL(k_attn_fwd<false>, grid, dim3(256), 0, stream, a);
-    return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
 }  // namespace pa

@@ -1,0 +1,423 @@
+// attn_bwd.hpp -- flash-attention backward with a transformed score, gfx950 MFMA.
+//
+// The chain rule through O = P V for the two transforms of attn.hpp
+// ("Fast Polynomial Transcendentals for LLMs"):
+//   dV = P^T dO,  dP = dO V^T,
+//   softcap  dS = P (dP - Delta) ds/dS,  Delta_i = dO_i . O_i, P recomputed
+//            from the saved natural log-sum-exp; the polynomial variant uses
+//            the analytic derivative of the D4 tanh program, a D3 with
+//            coefficients (j + 1) c_{j+1} (exact in FP16), in packed FP16 at
+//            the same clamped |x| (sections 3.3 and 5.2.2); the comparator
+//            uses 1 - tanh^2 recomputed with tanhf (Eq. 12);
+//   sigmoid  dS = dP dP~/ds; the polynomial variant uses the factored
+//            surrogate P~ (a + b x) of section 3.4 from the same region,
+//            clamp and Horner value as the forward; the comparator
+//            sigma (1 - sigma);
+//   dQ = dS K / sqrt(D),  dK = dS^T Q / sqrt(D) (summed over the query heads
+//   that share a key/value head).
+//
+// Two kernels, no atomics:
+//   k_attn_bwd_dq    one workgroup per 128 queries of one head (4 waves x 32
+//                    queries, lane = query as in the forward).  It computes
+//                    Delta for its rows first (softcap) and stores it in the
+//                    caller's workspace, then streams K / V tiles of 64 keys
+//                    through LDS: S^T = K Q^T and dP^T = V dO^T with Q and dO
+//                    held in registers, the transform, dQ^T += K^T dS^T with
+//                    K^T read transposed from the K tile.
+//   k_attn_bwd_dkdv  one workgroup per 128 keys of one key/value head (4
+//                    waves x 32 keys, lane = key); it loops over the query
+//                    heads of the group and the query tiles of 64 rows that
+//                    see its keys, with Q / dO tiles (and the rows' LSE and
+//                    Delta) streamed through LDS: S = Q K^T and dP = dO V^T
+//                    with K and V held in registers, the transform,
+//                    dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T read
+//                    transposed from the tiles.
+// Both run after the forward has written O and the LSE; dkdv after dq (it
+// reads Delta).  Every MFMA is v_mfma_f32_32x32x16_bf16 with the operand
+// layouts described in attn.hpp; P and dS are rounded to BF16 for the MFMA.
+#pragma once
+#include <type_traits>
+
+#include "attn.hpp"
+
+namespace pa {
+
+struct AttnBwdArgs {
+    const uint16_t *q, *k, *v, *o, *dout;
+    const float *lse;      // softcap: natural log-sum-exp per query row
+    float *delta;          // softcap: workspace, Delta per query row
+    uint16_t *dq, *dk, *dv;
+    int32_t S, H, G;       // G = H / Hkv
+    int32_t causal;
+    float scale;           // as AttnArgs
+    float c2;
+    float logn;
+    float rsd;             // RN_f32(1 / sqrt D)
+    CoefF16 tanh16;        // D4 tanh program
+    CoefF16 dtanh16;       // its derivative, D3 (FP16 coefficients)
+    SigCoef sig;
+};
+
+// dS (and P) of a pair of scores; s0, s1 raw scores, dp0, dp1 = dO . V,
+// nl0, nl1 = -lse * log2(e) (softcap), dl0, dl1 = Delta (softcap).
+template <int MODE>
+__device__ __forceinline__ void bwd_pair(const AttnBwdArgs &a, float s0, float s1, float dp0,
+                                         float dp1, float nl0, float nl1, float dl0, float dl1,
+                                         float &p0, float &p1, float &ds0, float &ds1)
+{
+    if constexpr (MODE == AM_SOFTCAP_POLY) {
+        uint32_t aw;
+        const uint32_t tw = softcap_poly_pair(s0, s1, a.scale, a.tanh16, aw);
+        const uint32_t dw = bc<uint32_t>(horner_f16<3, false>(bc<h2>(min_u16x2(aw, a.dtanh16.lc)), a.dtanh16));
+        p0 = __builtin_amdgcn_exp2f(fmaf(f16_lo(tw), a.c2, nl0));
+        p1 = __builtin_amdgcn_exp2f(fmaf(f16_hi(tw), a.c2, nl1));
+        ds0 = p0 * (dp0 - dl0) * f16_lo(dw);
+        ds1 = p1 * (dp1 - dl1) * f16_hi(dw);
+    } else if constexpr (MODE == AM_SOFTCAP_NATIVE) {
+        const float t0 = tanhf(s0 * a.scale), t1 = tanhf(s1 * a.scale);
+        p0 = __builtin_amdgcn_exp2f(fmaf(t0, a.c2, nl0));
+        p1 = __builtin_amdgcn_exp2f(fmaf(t1, a.c2, nl1));
+        ds0 = p0 * (dp0 - dl0) * fmaf(-t0, t0, 1.0f);
+        ds1 = p1 * (dp1 - dl1) * fmaf(-t1, t1, 1.0f);
+    } else if constexpr (MODE == AM_SIGMOID_POLY) {
+        uint32_t gw;
+        const uint32_t pw = sigmoid_poly_pair<true>(s0, s1, a.scale, a.sig, &gw);
+        p0 = lo_f(pw);
+        p1 = hi_f(pw);
+        ds0 = dp0 * lo_f(gw);
+        ds1 = dp1 * hi_f(gw);
+    } else {
+        p0 = sigmoid_acc(fmaf(s0, a.scale, -a.logn));
+        p1 = sigmoid_acc(fmaf(s1, a.scale, -a.logn));
+        ds0 = dp0 * (p0 * (1.0f - p0));
+        ds1 = dp1 * (p1 * (1.0f - p1));
+    }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void k_attn_bwd_dq(AttnBwdArgs a)
+{
+    constexpr bool SOFTCAP = am_softcap(MODE);
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[2][AT_TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t Vs[2][AT_TILE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int col = lane & 31, h = lane >> 5;
+    const int g16 = lane >> 4, i16 = lane & 15;
+    const int S = a.S;
+    const int ntq = (S + AT_BM - 1) / AT_BM;
+    const int nbh = (int)(gridDim.x / (unsigned)ntq);
+    const int qrank = (int)blockIdx.x / nbh;
+    const int bh = (int)blockIdx.x - qrank * nbh;
+    const int qt = a.causal ? ntq - 1 - qrank : qrank;
+    const int64_t qbase = (int64_t)bh * S * AT_D;
+    const int64_t kvbase = (int64_t)(bh / a.G) * S * AT_D;
+    const uint16_t *Q = a.q + qbase, *dO = a.dout + qbase;
+    const uint16_t *K = a.k + kvbase, *V = a.v + kvbase;
+    const int q0 = qt * AT_BM + wave * 32;
+    const int my_q = q0 + col;
+    const bool valid = my_q < S;
+
+    // Q and dO as B operands: lane holds row my_q, columns ks*16 + h*8 + 0..7
+    bf16x8 qf[8], df[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+        qf[ks] = valid ? ld_bf16x8(Q + (int64_t)my_q * AT_D + ks * 16 + h * 8) : bf16x8{};
+        df[ks] = valid ? ld_bf16x8(dO + (int64_t)my_q * AT_D + ks * 16 + h * 8) : bf16x8{};
+    }
+    float nl = 0.0f, dl = 0.0f;
+    if constexpr (SOFTCAP) {
+        float acc = 0.0f;
+        if (valid) {
+            const uint16_t *orow = a.o + qbase + (int64_t)my_q * AT_D;
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+                const bf16x8 ov = ld_bf16x8(orow + ks * 16 + h * 8);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc = fmaf((float)df[ks][e], (float)ov[e], acc);
+            }
+        }
+        dl = acc + __shfl_xor(acc, 32);
+        if (valid) {
+            nl = -a.lse[(int64_t)bh * S + my_q] * AT_LOG2E;
+            if (h == 0) a.delta[(int64_t)bh * S + my_q] = dl;
+        }
+    }
+
+    f32x16 dq[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db) dq[db] = f32x16{};
+
+    const int kend = a.causal ? (qt * AT_BM + AT_BM < S ? qt * AT_BM + AT_BM : S) : S;
+    const int nkt = (kend + AT_BN - 1) / AT_BN;
+
+    load_rows64(K, Ks[0], 0, S, wave, lane);
+    load_rows64(V, Vs[0], 0, S, wave, lane);
+    auto tile = [&](int kt, auto bufc) {
+        constexpr int buf = decltype(bufc)::value;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (kt + 1 < nkt) {
+            load_rows64(K, Ks[buf ^ 1], (kt + 1) * AT_BN, S, wave, lane);
+            load_rows64(V, Vs[buf ^ 1], (kt + 1) * AT_BN, S, wave, lane);
+        }
+        const int key0 = kt * AT_BN;
+        if (a.causal && key0 > q0 + 31) return;
+        if (q0 >= S) return;
+        const uint16_t *Kb = Ks[buf];
+        const uint16_t *Vb = Vs[buf];
+
+        f32x16 s[2], dp[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            s[kb] = f32x16{};
+            dp[kb] = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row8(Kb, kb * 32 + col, ks * 2 + h),
+                                                                qf[ks], s[kb], 0, 0, 0);
+                dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row8(Vb, kb * 32 + col, ks * 2 + h),
+                                                                 df[ks], dp[kb], 0, 0, 0);
+            }
+        }
+
+        // dS^T, as BF16 B operands in the permuted key order
+        const bool need_mask = (a.causal && key0 + AT_BN - 1 > q0) || key0 + AT_BN > S;
+        const int lim = a.causal ? (my_q < S - 1 ? my_q : S - 1) : S - 1;
+        bf16x8 dsf[4];
+        auto transform = [&](auto masked) {
+            constexpr bool MASKED = decltype(masked)::value;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj) {
+                    u32x4 fw;
+#pragma unroll
+                    for (int e2 = 0; e2 < 4; ++e2) {
+                        const int e = jj * 8 + e2 * 2;
+                        float p0, p1, d0, d1;
+                        bwd_pair<MODE>(a, s[kb][e], s[kb][e + 1], dp[kb][e], dp[kb][e + 1], nl, nl, dl,
+                                       dl, p0, p1, d0, d1);
+                        uint32_t w = pack_bf(d0, d1);
+                        if constexpr (MASKED) {
+                            const int k0 = key0 + kb * 32 + (e >> 2) * 8 + h * 4 + (e & 3);
+                            const uint32_t mlo = k0 > lim ? 0x0000FFFFu : 0u;
+                            const uint32_t mhi = k0 + 1 > lim ? 0xFFFF0000u : 0u;
+                            w &= ~(mlo | mhi);
+                        }
+                        fw[e2] = w;
+                    }
+                    dsf[kb * 2 + jj] = bc<bf16x8>(fw);
+                }
+            }
+        };
+        if (need_mask) transform(std::true_type{});
+        else transform(std::false_type{});
+
+        // dQ^T += K^T dS^T
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_tr_a(Kb, ks, db, g16, i16), dsf[ks],
+                                                                 dq[db], 0, 0, 0);
+        }
+    };
+    for (int kt = 0; kt < nkt; kt += 2) {
+        tile(kt, std::integral_constant<int, 0>{});
+        if (kt + 1 < nkt) tile(kt + 1, std::integral_constant<int, 1>{});
+    }
+
+    if (!valid) return;
+    uint16_t *row = a.dq + qbase + (int64_t)my_q * AT_D;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int d = db * 32 + j * 8 + h * 4;
+            u32x2 w;
+            w.x = pack_bf(dq[db][j * 4 + 0] * a.rsd, dq[db][j * 4 + 1] * a.rsd);
+            w.y = pack_bf(dq[db][j * 4 + 2] * a.rsd, dq[db][j * 4 + 3] * a.rsd);
+            *(u32x2 *)(row + d) = w;
+        }
+    }
+}
+
+constexpr int AT_BK = 128;   // keys per dK/dV workgroup
+constexpr int AT_BQ = 64;    // query rows per streamed tile
+
+template <int MODE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_attn_bwd_dkdv(AttnBwdArgs a)
+{
+    constexpr bool SOFTCAP = am_softcap(MODE);
+    __shared__ __attribute__((aligned(16))) uint16_t Qs[2][AT_TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t Ds[2][AT_TILE];
+    __shared__ __attribute__((aligned(16))) float Ls[2][AT_BQ];   // -lse * log2(e)
+    __shared__ __attribute__((aligned(16))) float Es[2][AT_BQ];   // Delta
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int col = lane & 31, h = lane >> 5;
+    const int g16 = lane >> 4, i16 = lane & 15;
+    const int S = a.S, G = a.G;
+    const int ntk = (S + AT_BK - 1) / AT_BK;
+    const int nbk = (int)(gridDim.x / (unsigned)ntk);       // B * Hkv
+    const int krank = (int)blockIdx.x / nbk;                 // 0 = heaviest key tile
+    const int bk = (int)blockIdx.x - krank * nbk;            // b Hkv + hk
+    const int kt = krank;                                    // causal: key tile 0 sees the most queries
+    const int64_t kvbase = (int64_t)bk * S * AT_D;
+    const int k0 = kt * AT_BK + wave * 32;
+    const int my_k = k0 + col;
+    const bool valid = my_k < S;
+
+    // K and V as B operands of S = Q K^T and dP = dO V^T: lane holds row my_k
+    bf16x8 kf[8], vf[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+        kf[ks] = valid ? ld_bf16x8(a.k + kvbase + (int64_t)my_k * AT_D + ks * 16 + h * 8) : bf16x8{};
+        vf[ks] = valid ? ld_bf16x8(a.v + kvbase + (int64_t)my_k * AT_D + ks * 16 + h * 8) : bf16x8{};
+    }
+    f32x16 dk[4], dv[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db) dk[db] = dv[db] = f32x16{};
+
+    // query tiles: every head of the group, rows from the first one that can
+    // see this workgroup's keys
+    const int qstart = a.causal ? kt * AT_BK : 0;
+    const int nqt = (S - qstart + AT_BQ - 1) / AT_BQ;
+    const int ntile = G * nqt;
+
+    auto head_of = [&](int t) { return (int64_t)bk * G + t / nqt; };
+    auto load = [&](int t, int buf) {
+        const int64_t bh = head_of(t);
+        const int r0 = qstart + (t % nqt) * AT_BQ;
+        load_rows64(a.q + bh * S * AT_D, Qs[buf], r0, S, wave, lane);
+        load_rows64(a.dout + bh * S * AT_D, Ds[buf], r0, S, wave, lane);
+        if constexpr (SOFTCAP) {
+            const int wv = __builtin_amdgcn_readfirstlane(wave);   // wave-uniform
+            if (wv < 2) {
+                int r = r0 + lane;
+                r = r < S ? r : S - 1;
+                const float *src = (wv == 0 ? a.lse : a.delta) + bh * S + r;
+                float *dst = wv == 0 ? Ls[buf] : Es[buf];
+                __builtin_amdgcn_global_load_lds((const void *)src,
+                                                 (void __attribute__((address_space(3))) *)dst, 4, 0, 0);
+            }
+        }
+    };
+
+    load(0, 0);
+    auto tile = [&](int t, auto bufc) {
+        constexpr int buf = decltype(bufc)::value;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (t + 1 < ntile) load(t + 1, buf ^ 1);
+        const int r0 = qstart + (t % nqt) * AT_BQ;
+        if (a.causal && r0 + AT_BQ - 1 < k0) return;   // every row of the tile precedes these keys
+        if (k0 >= S) return;
+        const uint16_t *Qb = Qs[buf];
+        const uint16_t *Db = Ds[buf];
+
+        f32x16 s[2], dp[2];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            s[qb] = f32x16{};
+            dp[qb] = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+                s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row8(Qb, qb * 32 + col, ks * 2 + h),
+                                                                kf[ks], s[qb], 0, 0, 0);
+                dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row8(Db, qb * 32 + col, ks * 2 + h),
+                                                                 vf[ks], dp[qb], 0, 0, 0);
+            }
+        }
+
+        // s[qb][j*4 + i] is query r0 + qb*32 + j*8 + h*4 + i of this lane's key
+        const bool need_mask = (a.causal && r0 < k0 + 31) || r0 + AT_BQ > S;
+        bf16x8 pf[4] = {}, dsf[4] = {};
+        auto transform = [&](auto masked) {
+            constexpr bool MASKED = decltype(masked)::value;
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    f32x4 nl4 = {}, dl4 = {};
+                    if constexpr (SOFTCAP) {
+                        nl4 = *(const f32x4 *)(&Ls[buf][qb * 32 + j * 8 + h * 4]);
+                        dl4 = *(const f32x4 *)(&Es[buf][qb * 32 + j * 8 + h * 4]);
+                        nl4 *= -AT_LOG2E;
+                    }
+                    uint32_t pw[2], dw[2];
+#pragma unroll
+                    for (int i = 0; i < 4; i += 2) {
+                        const int e = j * 4 + i;
+                        float p0, p1, d0, d1;
+                        bwd_pair<MODE>(a, s[qb][e], s[qb][e + 1], dp[qb][e], dp[qb][e + 1], nl4[i],
+                                       nl4[i + 1], dl4[i], dl4[i + 1], p0, p1, d0, d1);
+                        uint32_t pk = pack_bf(p0, p1), dk2 = pack_bf(d0, d1);
+                        if constexpr (MASKED) {
+                            const int q = r0 + qb * 32 + j * 8 + h * 4 + i;
+                            const bool vis0 = q < S && (!a.causal || q >= my_k);
+                            const bool vis1 = q + 1 < S && (!a.causal || q + 1 >= my_k);
+                            const uint32_t keep = (vis0 ? 0x0000FFFFu : 0u) | (vis1 ? 0xFFFF0000u : 0u);
+                            pk &= keep;
+                            dk2 &= keep;
+                        }
+                        pw[i >> 1] = pk;
+                        dw[i >> 1] = dk2;
+                    }
+                    // B-operand fragment ks = 2 qb + j / 2 holds accumulator
+                    // entries (j % 2) * 8 .. + 7
+                    const int f = qb * 2 + (j >> 1);
+                    const int half = (j & 1) * 2;
+                    u32x4 pv = bc<u32x4>(pf[f]), dv4 = bc<u32x4>(dsf[f]);
+                    pv[half] = pw[0];
+                    pv[half + 1] = pw[1];
+                    dv4[half] = dw[0];
+                    dv4[half + 1] = dw[1];
+                    pf[f] = bc<bf16x8>(pv);
+                    dsf[f] = bc<bf16x8>(dv4);
+                }
+            }
+        };
+        if (need_mask) transform(std::true_type{});
+        else transform(std::false_type{});
+
+        // dV^T += dO^T P,  dK^T += Q^T dS
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_tr_a(Db, ks, db, g16, i16), pf[ks],
+                                                                 dv[db], 0, 0, 0);
+                dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_tr_a(Qb, ks, db, g16, i16), dsf[ks],
+                                                                 dk[db], 0, 0, 0);
+            }
+        }
+    };
+    for (int t = 0; t < ntile; t += 2) {
+        tile(t, std::integral_constant<int, 0>{});
+        if (t + 1 < ntile) tile(t + 1, std::integral_constant<int, 1>{});
+    }
+
+    if (!valid) return;
+    uint16_t *krow = a.dk + kvbase + (int64_t)my_k * AT_D;
+    uint16_t *vrow = a.dv + kvbase + (int64_t)my_k * AT_D;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int d = db * 32 + j * 8 + h * 4;
+            u32x2 w;
+            w.x = pack_bf(dk[db][j * 4 + 0] * a.rsd, dk[db][j * 4 + 1] * a.rsd);
+            w.y = pack_bf(dk[db][j * 4 + 2] * a.rsd, dk[db][j * 4 + 3] * a.rsd);
+            *(u32x2 *)(krow + d) = w;
+            w.x = pack_bf(dv[db][j * 4 + 0], dv[db][j * 4 + 1]);
+            w.y = pack_bf(dv[db][j * 4 + 2], dv[db][j * 4 + 3]);
+            *(u32x2 *)(vrow + d) = w;
+        }
+    }
+}
+
+}  // namespace pa

@@ -1,0 +1,218 @@
+// attn_host.hpp -- argument validation and launches of the attention kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <initializer_list>
+
+#include "../../include/polyact.h"
+#include "attn.hpp"
+#include "attn_bwd.hpp"
+#include "attn_programs.hpp"
+#include "programs.hpp"
+
+namespace pa {
+
+struct Span {
+    const void *p;
+    int64_t bytes;
+};
+
+inline bool spans_overlap(const Span &a, const Span &b)
+{
+    if (a.bytes <= 0 || b.bytes <= 0) return false;
+    const uintptr_t x = (uintptr_t)a.p, y = (uintptr_t)b.p;
+    return x < y + (uintptr_t)b.bytes && y < x + (uintptr_t)a.bytes;
+}
+
+// Every output against every other buffer (outputs and inputs).
+inline bool any_overlap(std::initializer_list<Span> outs, std::initializer_list<Span> ins)
+{
+    for (const Span *o = outs.begin(); o != outs.end(); ++o) {
+        for (const Span *p = outs.begin(); p != outs.end(); ++p)
+            if (p != o && spans_overlap(*o, *p)) return true;
+        for (const Span &i : ins)
+            if (spans_overlap(*o, i)) return true;
+    }
+    return false;
+}
+
+inline bool aligned16(std::initializer_list<const void *> ps)
+{
+    for (const void *p : ps)
+        if ((uintptr_t)p & 15u) return false;
+    return true;
+}
+
+// Shape rules shared by every attention entry point.
+inline pa_status attn_shape(int32_t B, int32_t H, int32_t Hkv, int32_t S, int32_t D)
+{
+    if (B < 0 || H < 0 || Hkv < 0 || S < 0 || D != AT_D) return PA_ERR_SHAPE;
+    if ((int64_t)B * H > 0 && (Hkv == 0 || H % Hkv != 0)) return PA_ERR_SHAPE;
+    const int64_t tiles = (int64_t)(S + AT_BM - 1) / AT_BM;
+    if ((int64_t)B * H * tiles > 0x7FFFFFFF) return PA_ERR_SHAPE;
+    return PA_OK;
+}
+
+inline bool cap_ok(float cap) { return cap > 0.0f && cap != INFINITY; }
+
+inline uint32_t f16_dup(float v)
+{
+    const _Float16 h = (_Float16)v;
+    uint16_t b;
+    std::memcpy(&b, &h, 2);
+    return (uint32_t)b | ((uint32_t)b << 16);
+}
+
+inline float bf16_value(uint16_t bits)
+{
+    const uint32_t w = (uint32_t)bits << 16;
+    float v;
+    std::memcpy(&v, &w, 4);
+    return v;
+}
+
+// The D4 tanh program and its analytic derivative (coefficients (j + 1)
+// c_{j+1}, all exact in FP16) in FP16.
+inline void tanh_coefs(CoefF16 &fwd, CoefF16 &der)
+{
+    const ProgramDef *p = find_program(PA_TANH, 0);
+    fwd = CoefF16{};
+    der = CoefF16{};
+    for (int j = 0; j <= p->degree; ++j) fwd.c[j] = f16_dup(bf16_value(p->coeff[j]));
+    for (int j = 0; j < p->degree; ++j) der.c[j] = f16_dup((float)(j + 1) * bf16_value(p->coeff[j + 1]));
+    fwd.lc = der.lc = f16_dup(p->Lc);
+}
+
+inline SigCoef sigmoid_coefs()
+{
+    const SigmoidAttnDef &d = kSigmoidAttn;
+    SigCoef k{};
+    for (int r = 0; r < 2; ++r) {
+        for (int j = 0; j < 4; ++j) k.c[r][j] = bf16_value(d.c[r][j]);
+        k.a[r] = bf16_value(d.a[r]);
+        k.b[r] = bf16_value(d.b[r]);
+    }
+    k.thr = bf16_value(d.thr);
+    k.lo = bf16_value(d.lo);
+    k.hi = bf16_value(d.hi);
+    return k;
+}
+
+inline pa_status attn_launched() { return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH; }
+
+inline pa_status attn_fwd(int mode, const void *q, const void *k, const void *v, void *o, float *lse,
+                          int32_t B, int32_t H, int32_t Hkv, int32_t S, int32_t D, float cap,
+                          int32_t causal, hipStream_t stream)
+{
+    if (!q || !k || !v || !o) return PA_ERR_NULL;
+    if (!aligned16({q, k, v, o}) || ((uintptr_t)lse & 3u)) return PA_ERR_ALIGN;
+    pa_status st = attn_shape(B, H, Hkv, S, D);
+    if (st != PA_OK) return st;
+    const bool softcap = am_softcap(mode);
+    if (softcap && !cap_ok(cap)) return PA_ERR_SHAPE;
+    if (mode == AM_SIGMOID_POLY && S != kSigmoidAttn.n && (int64_t)B * H * S > 0) return PA_ERR_SHAPE;
+    const int64_t qb = (int64_t)B * H * S * D * 2, kb = (int64_t)B * Hkv * S * D * 2;
+    const int64_t lb = lse ? (int64_t)B * H * S * 4 : 0;
+    if (any_overlap({{o, qb}, {lse, lb}}, {{q, qb}, {k, kb}, {v, kb}})) return PA_ERR_OVERLAP;
+    if ((int64_t)B * H == 0 || S == 0) return PA_OK;
+    AttnArgs a{};
+    a.q = (const uint16_t *)q;
+    a.k = (const uint16_t *)k;
+    a.v = (const uint16_t *)v;
+    a.o = (uint16_t *)o;
+    a.lse = softcap ? lse : nullptr;
+    a.S = S;
+    a.H = H;
+    a.G = H / Hkv;
+    a.causal = causal ? 1 : 0;
+    if (softcap) {
+        a.scale = (float)(1.0 / ((double)cap * std::sqrt((double)D)));
+        a.c2 = (float)((double)cap * 1.4426950408889634074);
+        CoefF16 der;
+        tanh_coefs(a.tanh16, der);
+    } else {
+        a.scale = (float)(1.0 / std::sqrt((double)D));
+        a.logn = (float)std::log((double)S);
+        a.sig = sigmoid_coefs();
+    }
+    const dim3 grid((unsigned)(((S + AT_BM - 1) / AT_BM) * (B * H)));
+    switch (mode) {
+    case AM_SOFTCAP_POLY: hipLaunchKernelGGL(k_attn_fwd<AM_SOFTCAP_POLY>, grid, dim3(256), 0, stream, a); break;
+    case AM_SOFTCAP_NATIVE: hipLaunchKernelGGL(k_attn_fwd<AM_SOFTCAP_NATIVE>, grid, dim3(256), 0, stream, a); break;
+    case AM_SIGMOID_POLY: hipLaunchKernelGGL(k_attn_fwd<AM_SIGMOID_POLY>, grid, dim3(256), 0, stream, a); break;
+    default: hipLaunchKernelGGL(k_attn_fwd<AM_SIGMOID_NATIVE>, grid, dim3(256), 0, stream, a); break;
+    }
+    return attn_launched();
+}
+
+template <int MODE>
+inline void attn_bwd_launch(const AttnBwdArgs &a, int32_t B, int32_t H, int32_t Hkv, int32_t S,
+                            hipStream_t stream)
+{
+    const dim3 gq((unsigned)(((S + AT_BM - 1) / AT_BM) * (B * H)));
+    const dim3 gk((unsigned)(((S + AT_BK - 1) / AT_BK) * (B * Hkv)));
+    hipLaunchKernelGGL(k_attn_bwd_dq<MODE>, gq, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(k_attn_bwd_dkdv<MODE>, gk, dim3(256), 0, stream, a);
+}
+
+// o, lse and ws are used by the softcap modes only.
+inline pa_status attn_bwd(int mode, const void *q, const void *k, const void *v, const void *o,
+                          const void *dout, const float *lse, void *dq, void *dk, void *dv, float *ws,
+                          int32_t B, int32_t H, int32_t Hkv, int32_t S, int32_t D, float cap,
+                          int32_t causal, hipStream_t stream)
+{
+    const bool softcap = am_softcap(mode);
+    if (!q || !k || !v || !dout || !dq || !dk || !dv) return PA_ERR_NULL;
+    if (softcap && (!o || !lse || !ws)) return PA_ERR_NULL;
+    if (!aligned16({q, k, v, dout, dq, dk, dv}) || (softcap && !aligned16({o})) ||
+        ((uintptr_t)lse & 3u) || ((uintptr_t)ws & 3u))
+        return PA_ERR_ALIGN;
+    pa_status st = attn_shape(B, H, Hkv, S, D);
+    if (st != PA_OK) return st;
+    if (softcap && !cap_ok(cap)) return PA_ERR_SHAPE;
+    if (mode == AM_SIGMOID_POLY && S != kSigmoidAttn.n && (int64_t)B * H * S > 0) return PA_ERR_SHAPE;
+    if ((int64_t)B * Hkv * ((S + AT_BK - 1) / AT_BK) > 0x7FFFFFFF) return PA_ERR_SHAPE;
+    const int64_t qb = (int64_t)B * H * S * D * 2, kb = (int64_t)B * Hkv * S * D * 2;
+    const int64_t rb = softcap ? (int64_t)B * H * S * 4 : 0;
+    if (any_overlap({{dq, qb}, {dk, kb}, {dv, kb}, {ws, rb}},
+                    {{q, qb}, {k, kb}, {v, kb}, {o, softcap ? qb : 0}, {dout, qb}, {lse, rb}}))
+        return PA_ERR_OVERLAP;
+    if ((int64_t)B * H == 0 || S == 0) return PA_OK;
+    AttnBwdArgs a{};
+    a.q = (const uint16_t *)q;
+    a.k = (const uint16_t *)k;
+    a.v = (const uint16_t *)v;
+    a.o = (const uint16_t *)o;
+    a.dout = (const uint16_t *)dout;
+    a.lse = lse;
+    a.delta = ws;
+    a.dq = (uint16_t *)dq;
+    a.dk = (uint16_t *)dk;
+    a.dv = (uint16_t *)dv;
+    a.S = S;
+    a.H = H;
+    a.G = H / Hkv;
+    a.causal = causal ? 1 : 0;
+    a.rsd = (float)(1.0 / std::sqrt((double)D));
+    if (softcap) {
+        a.scale = (float)(1.0 / ((double)cap * std::sqrt((double)D)));
+        a.c2 = (float)((double)cap * 1.4426950408889634074);
+        tanh_coefs(a.tanh16, a.dtanh16);
+    } else {
+        a.scale = a.rsd;
+        a.logn = (float)std::log((double)S);
+        a.sig = sigmoid_coefs();
+    }
+    switch (mode) {
+    case AM_SOFTCAP_POLY: attn_bwd_launch<AM_SOFTCAP_POLY>(a, B, H, Hkv, S, stream); break;
+    case AM_SOFTCAP_NATIVE: attn_bwd_launch<AM_SOFTCAP_NATIVE>(a, B, H, Hkv, S, stream); break;
+    case AM_SIGMOID_POLY: attn_bwd_launch<AM_SIGMOID_POLY>(a, B, H, Hkv, S, stream); break;
+    default: attn_bwd_launch<AM_SIGMOID_NATIVE>(a, B, H, Hkv, S, stream); break;
+    }
+    return attn_launched();
+}
+
+}  // namespace pa

@@ -7,56 +7,15 @@
 #include <cstring>
 
 #include "../../include/polyact.h"
-#include "attn.hpp"
+#include "attn_host.hpp"
 #include "ops.hpp"
 #include "programs.hpp"
-#include "stream.hpp"
+#include "stream_launch.hpp"
 #include "swiglu.hpp"
 
 using namespace pa;
 
 namespace {
-
-constexpr int kThreads = 256;       // scalar kernels
-// Streaming tiles (threads per block, 16-byte chunks per thread).  A sweep of
-// block sizes 128-1024 and 1-4 chunks per thread on MI355X put one chunk per
-// thread and the most blocks first for every stream shape: 6.49 TB/s for one
-// input and one output, 6.52 TB/s for two inputs and one output, 6.20 TB/s
-// for three inputs and two outputs.
-constexpr int kMap1BS = 512, kMap1U = 1;   // x -> y
-constexpr int kMap2BS = 1024, kMap2U = 1;  // x, g -> y; SwiGLU fwd and bwd
-constexpr int64_t kMaxGrid = 0x7FFFFFFF;
-constexpr int kBlocksPerCU = 8;     // scalar kernels: blocks per compute unit
-
-int cu_count()
-{
-    static int cached[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            n <= 0)
-            n = 256;
-        cached[dev] = n;
-    }
-    return cached[dev];
-}
-
-// one block per tile of tile_items work items (capped by the launch limit)
-int64_t grid_tiles(int64_t work_items, int64_t tile_items)
-{
-    const int64_t need = (work_items + tile_items - 1) / tile_items;
-    return need < 1 ? 1 : (need < kMaxGrid ? need : kMaxGrid);
-}
-
-int64_t grid_for(int64_t work_items, int per_thread)
-{
-    const int64_t need = (work_items + (int64_t)kThreads * per_thread - 1) /
-                         ((int64_t)kThreads * per_thread);
-    const int64_t cap = (int64_t)cu_count() * kBlocksPerCU;
-    return need < 1 ? 1 : (need < cap ? need : cap);
-}
 
 pa_status launched()
 {
@@ -111,68 +70,6 @@ CoefBF16 coef_bf16(const ProgramDef &p)
     }
     std::memcpy(&k.lc, &p.Lc, 4);
     return k;
-}
-
-// Split [0, n) of 16-bit elements into a scalar head, a 16-byte vector body
-// and a scalar tail, given the byte addresses of all streams.
-struct Split {
-    int64_t head, nvec, tail0, n;
-};
-Split split_range(int64_t n, std::initializer_list<const void *> ptrs)
-{
-    Split s{n, 0, n, n};
-    uintptr_t mis = (uintptr_t)(*ptrs.begin()) & 15u;
-    for (const void *p : ptrs)
-        if (((uintptr_t)p & 15u) != mis) return s;   // different phases: all scalar
-    int64_t head = (int64_t)(((16u - mis) & 15u) / 2u);
-    if (head > n) head = n;
-    s.head = head;
-    s.nvec = (n - head) / 8;
-    s.tail0 = head + s.nvec * 8;
-    return s;
-}
-
-template <class Op>
-pa_status run_map1(const void *x, void *y, int64_t n, hipStream_t st, const Op &op)
-{
-    const Split sp = split_range(n, {x, y});
-    const uint16_t *xs = (const uint16_t *)x;
-    uint16_t *ys = (uint16_t *)y;
-    if (sp.nvec > 0) {
-        const int64_t grid = grid_tiles(sp.nvec, (int64_t)kMap1BS * kMap1U);
-        hipLaunchKernelGGL((k_map1<Op, kMap1BS, kMap1U>), dim3((unsigned)grid), dim3(kMap1BS), 0, st,
-                           (const u32x4 *)(xs + sp.head), (u32x4 *)(ys + sp.head), sp.nvec, op);
-        if (launched() != PA_OK) return PA_ERR_LAUNCH;
-    }
-    const int64_t rest = sp.head + (n - sp.tail0);
-    if (rest > 0) {
-        hipLaunchKernelGGL((k_scalar1<Op>), dim3((unsigned)grid_for(rest, 1)), dim3(kThreads), 0,
-                           st, xs, ys, (int64_t)0, sp.head, sp.tail0, n, op);
-        if (launched() != PA_OK) return PA_ERR_LAUNCH;
-    }
-    return PA_OK;
-}
-
-template <class Op>
-pa_status run_map2(const void *x, const void *g, void *y, int64_t n, hipStream_t st, const Op &op)
-{
-    const Split sp = split_range(n, {x, g, y});
-    const uint16_t *xs = (const uint16_t *)x, *gs = (const uint16_t *)g;
-    uint16_t *ys = (uint16_t *)y;
-    if (sp.nvec > 0) {
-        const int64_t grid = grid_tiles(sp.nvec, (int64_t)kMap2BS * kMap2U);
-        hipLaunchKernelGGL((k_map2<Op, kMap2BS, kMap2U>), dim3((unsigned)grid), dim3(kMap2BS), 0, st,
-                           (const u32x4 *)(xs + sp.head), (const u32x4 *)(gs + sp.head),
-                           (u32x4 *)(ys + sp.head), sp.nvec, op);
-        if (launched() != PA_OK) return PA_ERR_LAUNCH;
-    }
-    const int64_t rest = sp.head + (n - sp.tail0);
-    if (rest > 0) {
-        hipLaunchKernelGGL((k_scalar2<Op>), dim3((unsigned)grid_for(rest, 1)), dim3(kThreads), 0,
-                           st, xs, gs, ys, (int64_t)0, sp.head, sp.tail0, n, op);
-        if (launched() != PA_OK) return PA_ERR_LAUNCH;
-    }
-    return PA_OK;
 }
 
 pa_status check_unary(pa_dtype t, const void *x, const void *y, int64_t n)
@@ -384,8 +281,27 @@ pa_status poly_program_info(pa_func f, int32_t deriv, pa_dtype t, pa_program *ou
 {
     if (!out) return PA_ERR_NULL;
     if (t != PA_F16 && t != PA_BF16) return PA_ERR_DTYPE;
+    if (deriv == 2) {
+        // the analytic derivative of the D4 tanh program (softcap attention
+        // backward), FP16 coefficients
+        if (f != PA_TANH) return PA_ERR_FUNC;
+        if (t != PA_F16) return PA_ERR_DTYPE;
+        const ProgramDef *p = find_program(PA_TANH, 0);
+        std::memset(out, 0, sizeof *out);
+        CoefF16 fwd, der;
+        tanh_coefs(fwd, der);
+        out->func = PA_TANH;
+        out->deriv = 2;
+        out->degree = p->degree - 1;
+        out->dtype = t;
+        out->Li = p->Li;
+        out->Lc = p->Lc;
+        for (int j = 0; j < p->degree; ++j) out->coeff_bits[j] = (uint16_t)(der.c[j] & 0xFFFFu);
+        out->order = PA_ORDER_F16_FMA;
+        return PA_OK;
+    }
     const ProgramDef *p = find_program((int)f, deriv ? 1 : 0);
-    if (!p) return PA_ERR_FUNC;
+    if (!p || deriv < 0 || deriv > 1) return PA_ERR_FUNC;
     std::memset(out, 0, sizeof *out);
     out->func = p->func;
     out->deriv = p->deriv;
@@ -541,20 +457,84 @@ pa_status native_swiglu_bwd(pa_dtype t, const void *gate, const void *up, const 
     return swiglu_bwd_launch(a, stream, SwiNativeBwd{});
 }
 
-pa_status poly_softcap_attn_fwd(const void *q, const void *k, const void *v, void *o, int32_t B,
-                                int32_t H, int32_t S, int32_t D, float cap, int32_t causal,
-                                hipStream_t stream)
+pa_status poly_softcap_attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+                                int32_t B, int32_t H, int32_t Hkv, int32_t S, int32_t D, float cap,
+                                int32_t causal, hipStream_t stream)
 {
-    const ProgramDef *p = find_program(PA_TANH, 0);
-    return attn_fwd(q, k, v, o, B, H, S, D, cap, causal, true, coef_f16(*p), stream);
+    return attn_fwd(AM_SOFTCAP_POLY, q, k, v, o, lse, B, H, Hkv, S, D, cap, causal, stream);
 }
 
-pa_status native_softcap_attn_fwd(const void *q, const void *k, const void *v, void *o,
-                                  int32_t B, int32_t H, int32_t S, int32_t D, float cap,
-                                  int32_t causal, hipStream_t stream)
+pa_status native_softcap_attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+                                  int32_t B, int32_t H, int32_t Hkv, int32_t S, int32_t D,
+                                  float cap, int32_t causal, hipStream_t stream)
 {
-    const ProgramDef *p = find_program(PA_TANH, 0);
-    return attn_fwd(q, k, v, o, B, H, S, D, cap, causal, false, coef_f16(*p), stream);
+    return attn_fwd(AM_SOFTCAP_NATIVE, q, k, v, o, lse, B, H, Hkv, S, D, cap, causal, stream);
+}
+
+pa_status poly_softcap_attn_bwd(const void *q, const void *k, const void *v, const void *o,
+                                const void *dout, const float *lse, void *dq, void *dk, void *dv,
+                                float *workspace, int32_t B, int32_t H, int32_t Hkv, int32_t S,
+                                int32_t D, float cap, int32_t causal, hipStream_t stream)
+{
+    return attn_bwd(AM_SOFTCAP_POLY, q, k, v, o, dout, lse, dq, dk, dv, workspace, B, H, Hkv, S, D,
+                    cap, causal, stream);
+}
+
+pa_status native_softcap_attn_bwd(const void *q, const void *k, const void *v, const void *o,
+                                  const void *dout, const float *lse, void *dq, void *dk, void *dv,
+                                  float *workspace, int32_t B, int32_t H, int32_t Hkv, int32_t S,
+                                  int32_t D, float cap, int32_t causal, hipStream_t stream)
+{
+    return attn_bwd(AM_SOFTCAP_NATIVE, q, k, v, o, dout, lse, dq, dk, dv, workspace, B, H, Hkv, S,
+                    D, cap, causal, stream);
+}
+
+pa_status poly_sigmoid_attn_fwd(const void *q, const void *k, const void *v, void *o, int32_t B,
+                                int32_t H, int32_t Hkv, int32_t S, int32_t D, int32_t causal,
+                                hipStream_t stream)
+{
+    return attn_fwd(AM_SIGMOID_POLY, q, k, v, o, nullptr, B, H, Hkv, S, D, 0.0f, causal, stream);
+}
+
+pa_status native_sigmoid_attn_fwd(const void *q, const void *k, const void *v, void *o, int32_t B,
+                                  int32_t H, int32_t Hkv, int32_t S, int32_t D, int32_t causal,
+                                  hipStream_t stream)
+{
+    return attn_fwd(AM_SIGMOID_NATIVE, q, k, v, o, nullptr, B, H, Hkv, S, D, 0.0f, causal, stream);
+}
+
+pa_status poly_sigmoid_attn_bwd(const void *q, const void *k, const void *v, const void *dout,
+                                void *dq, void *dk, void *dv, int32_t B, int32_t H, int32_t Hkv,
+                                int32_t S, int32_t D, int32_t causal, hipStream_t stream)
+{
+    return attn_bwd(AM_SIGMOID_POLY, q, k, v, nullptr, dout, nullptr, dq, dk, dv, nullptr, B, H, Hkv,
+                    S, D, 0.0f, causal, stream);
+}
+
+pa_status native_sigmoid_attn_bwd(const void *q, const void *k, const void *v, const void *dout,
+                                  void *dq, void *dk, void *dv, int32_t B, int32_t H, int32_t Hkv,
+                                  int32_t S, int32_t D, int32_t causal, hipStream_t stream)
+{
+    return attn_bwd(AM_SIGMOID_NATIVE, q, k, v, nullptr, dout, nullptr, dq, dk, dv, nullptr, B, H,
+                    Hkv, S, D, 0.0f, causal, stream);
+}
+
+pa_status poly_sigmoid_attn_program(pa_sigmoid_attn_program *out)
+{
+    if (!out) return PA_ERR_NULL;
+    const SigmoidAttnDef &d = kSigmoidAttn;
+    std::memset(out, 0, sizeof *out);
+    out->n = d.n;
+    out->thr = d.thr;
+    out->clamp_lo = d.lo;
+    out->clamp_hi = d.hi;
+    for (int r = 0; r < 2; ++r) {
+        for (int j = 0; j < 4; ++j) out->coeff_bits[r][j] = d.c[r][j];
+        out->a_bits[r] = d.a[r];
+        out->b_bits[r] = d.b[r];
+    }
+    out->order = PA_ORDER_F32FMA_BF16;
+    return PA_OK;
 }
 
 }  // extern "C"

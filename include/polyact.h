@@ -13,7 +13,11 @@
  *   - the same D3 sigmoid inside a fused SwiGLU forward / backward
  *     (section 3.3, section 3.4, Eq. 15) over dense or expert-grouped rows
  *   - the D4 tanh as the softcap alpha tanh(x / alpha) on attention logits
- *     inside a flash-attention forward (Eq. 1, section 5.2.2).
+ *     inside a flash-attention forward, and its analytic derivative (a D3)
+ *     in the backward (Eq. 1, Eq. 12, sections 3.3 and 5.2.2)
+ *   - sigmoid attention P = sigma(s - ln n) (Eq. 14) with the two-region
+ *     cubic and its factored derivative surrogate of section 3.4, forward
+ *     and backward.
  *
  * Arithmetic.  FP16 programs run on packed FP16 FMA (one IEEE rounding per
  * stage).  gfx950 has no packed BF16 FMA, so BF16 programs run each stage as
@@ -55,7 +59,7 @@ extern "C" {
 /* HIP's stream handle (the same typedef as hip_runtime_api.h). */
 typedef struct ihipStream_t *hipStream_t;
 
-#define PA_ABI_VERSION 1
+#define PA_ABI_VERSION 2
 
 typedef enum {
     PA_OK = 0,
@@ -89,7 +93,12 @@ typedef enum { PA_ORDER_F16_FMA = 1, PA_ORDER_F32FMA_BF16 = 3 } pa_order;
  * same values, each exactly representable in FP16. */
 typedef struct {
     int32_t func;          /* pa_func                                        */
-    int32_t deriv;         /* 0 forward program, 1 direct derivative program */
+    int32_t deriv;         /* 0 forward program, 1 direct derivative program,
+                              2 analytic derivative of the forward program
+                              (PA_TANH with PA_F16 only: the softcap
+                              attention backward; coeff_bits are then FP16
+                              bit patterns (j + 1) c_{j+1}, not all of which
+                              are BF16 values)                              */
     int32_t degree;        /* D                                              */
     int32_t dtype;         /* pa_dtype the info was requested for            */
     float Li;              /* fit interval [0, Li] (section 3.2)             */
@@ -97,6 +106,16 @@ typedef struct {
     uint16_t coeff_bits[8];
     int32_t order;         /* pa_order used for dtype                        */
 } pa_program;
+
+/* The two-region sigmoid-attention program (see poly_sigmoid_attn_fwd). */
+typedef struct {
+    int32_t n;                 /* sequence length the coefficients hold for */
+    uint16_t thr;              /* region threshold (BF16)                   */
+    uint16_t clamp_lo, clamp_hi;
+    uint16_t coeff_bits[2][4]; /* [region][j], BF16                         */
+    uint16_t a_bits[2], b_bits[2];
+    int32_t order;             /* PA_ORDER_F32FMA_BF16                      */
+} pa_sigmoid_attn_program;
 
 /* y[i] = f~(x[i]), i < n.  f = PA_SIGMOID (D3), PA_TANH (D4), PA_SILU (D3,
  * reusing the sigmoid polynomial), PA_GELU (D5).  x, y: n elements of
@@ -138,18 +157,66 @@ pa_status poly_swiglu_bwd(pa_dtype t, const void *gate, const void *up, const vo
                           int64_t ld_dgate, int64_t ld_dup, const int64_t *row_offsets,
                           int32_t n_groups, hipStream_t stream);
 
-/* Softcapped attention forward, BF16 in/out, FP32 accumulation on MFMA:
+/* ---- attention (BF16 in/out, FP32 accumulation on MFMA, D = 128) -------
+ * Layout: q, o, dout, dq: [B, H, S, D]; k, v, dk, dv: [B, Hkv, S, D], all
+ * contiguous BF16 and 16-byte aligned; H must be a multiple of Hkv (query head
+ * h uses key/value head h / (H / Hkv): grouped-query attention; Hkv = H is
+ * plain multi-head attention).  D must be 128; any S >= 0; causal != 0 masks
+ * key j from query i when j > i.  lse and workspace: [B, H, S] FP32, 4-byte
+ * aligned.  No output may overlap another output or an input
+ * (PA_ERR_OVERLAP).  B * H * ceil(S / 128) must fit in int32. */
+
+/* Softcapped attention forward:
  *   S = Q K^T;  x = RN_f16(RN_f32(S) * RN_f32(1 / (cap sqrt(D))));
  *   s = cap * tanh~(x), the D4 tanh program in packed FP16 arithmetic (the
  *   packed 16-bit FMA of gfx950; its coefficients are the BF16 fit, exact in
- *   FP16);  causal mask key <= query;  P = softmax(s) (FP32, online, exp2);
+ *   FP16);  causal mask;  P = softmax(s) (FP32, online, exp2);
  *   O = P V / l with P rounded to BF16 for the MFMA.
- * q, k, v, o: [B, H, S, D] contiguous BF16, 16-byte aligned; D must be 128;
- * any S >= 0; B * H <= 65535; cap > 0 and finite.  O must not overlap Q, K, V.
+ * lse (nullable): the natural log-sum-exp of each row's softcapped logits,
+ *   the input the backward needs.  cap > 0 and finite.
  * Paper: Eq. 1 and section 5.2.2 (D4 tanh softcap inside attention). */
-pa_status poly_softcap_attn_fwd(const void *q, const void *k, const void *v, void *o,
-                                int32_t B, int32_t H, int32_t S, int32_t D, float cap,
+pa_status poly_softcap_attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+                                int32_t B, int32_t H, int32_t Hkv, int32_t S, int32_t D, float cap,
                                 int32_t causal, hipStream_t stream);
+
+/* Softcapped attention backward: given the forward's O and lse and the
+ * upstream gradient dout, writes dq, dk, dv:
+ *   P = exp(s - lse) recomputed with the forward's program;  dV = P^T dO;
+ *   dP = dO V^T;  Delta_i = dO_i . O_i;  dS = P (dP - Delta) ds/dS;
+ *   dQ = dS K,  dK = dS^T Q (summed over the query heads of a group),
+ * where ds/dS uses the analytic derivative of the D4 tanh program (a D3 with
+ * coefficients (j + 1) c_{j+1}, exact in FP16; poly_program_info(PA_TANH, 2,
+ * PA_F16)) in packed FP16 at the same clamped |x|.  P and dS are rounded to
+ * BF16 for the MFMA.  workspace: caller-owned scratch of B * H * S floats
+ * (receives Delta; contents on return unspecified).
+ * Paper: Eq. 12 and section 5.2.2 (the differentiated D3 at the recomputed
+ * scaled score), section 3.3 (differentiated-polynomial backward). */
+pa_status poly_softcap_attn_bwd(const void *q, const void *k, const void *v, const void *o,
+                                const void *dout, const float *lse, void *dq, void *dk, void *dv,
+                                float *workspace, int32_t B, int32_t H, int32_t Hkv, int32_t S,
+                                int32_t D, float cap, int32_t causal, hipStream_t stream);
+
+/* Sigmoid attention forward, O = P V with P = sigma(s - ln n) and
+ * s = q.k / sqrt(D) (Eq. 14), n = S.  The program: x = RN_bf16(RN_f32(S_ij) *
+ * RN_f32(1 / sqrt D)); region r = (x >= 1.25); x clamped to [-6, 6]; one
+ * cubic per region with ln n and 1/n folded into its BF16 coefficients,
+ * Horner with an FP32 FMA rounded to BF16 per stage; P = max(value, 0), used
+ * directly (no normalisation).  The coefficients hold for n = 4096 only: any
+ * other S > 0 returns PA_ERR_SHAPE (the runtime length guard).  The constants
+ * are those printed for the paper's B3 evaluator (poly_sigmoid_attn_program).
+ * Paper: section 3.4, section 5.2.3 (Eq. 14), Appendix C (Listing 1). */
+pa_status poly_sigmoid_attn_fwd(const void *q, const void *k, const void *v, void *o, int32_t B,
+                                int32_t H, int32_t Hkv, int32_t S, int32_t D, int32_t causal,
+                                hipStream_t stream);
+
+/* Sigmoid attention backward: dV = P^T dO, dP = dO V^T, dS = dP g,
+ * dQ = dS K / sqrt(D), dK = dS^T Q / sqrt(D), with g the factored derivative
+ * surrogate P~(x) (a + b x) of the same region and clamped x (BF16 per
+ * stage).  Same length guard.  Paper: section 3.4 (the coupled value /
+ * derivative evaluator), Appendix C (Listing 2). */
+pa_status poly_sigmoid_attn_bwd(const void *q, const void *k, const void *v, const void *dout,
+                                void *dq, void *dk, void *dv, int32_t B, int32_t H, int32_t Hkv,
+                                int32_t S, int32_t D, int32_t causal, hipStream_t stream);
 
 /* ---- matched comparators (same memory path, accurate FP32 math) -------- */
 
@@ -177,18 +244,36 @@ pa_status native_swiglu_bwd(pa_dtype t, const void *gate, const void *up, const 
                             int64_t ld_dgate, int64_t ld_dup, const int64_t *row_offsets,
                             int32_t n_groups, hipStream_t stream);
 
-/* Softcapped attention with accurate FP32 tanhf on the unrounded FP32 scaled
- * score x = RN_f32(S) * RN_f32(1 / (cap sqrt(D))) (arguments as
- * poly_softcap_attn_fwd). */
-pa_status native_softcap_attn_fwd(const void *q, const void *k, const void *v, void *o,
-                                  int32_t B, int32_t H, int32_t S, int32_t D, float cap,
-                                  int32_t causal, hipStream_t stream);
+/* Attention comparators (arguments as the poly_ entry points): softcap with
+ * accurate FP32 tanhf on the unrounded FP32 scaled score and, backward,
+ * 1 - tanh^2 (Eq. 12); sigmoid with sigma(RN_f32(S) * RN_f32(1 / sqrt D) -
+ * RN_f32(ln S)) from expf and an IEEE divide, sigma (1 - sigma) backward, for
+ * any S. */
+pa_status native_softcap_attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+                                  int32_t B, int32_t H, int32_t Hkv, int32_t S, int32_t D,
+                                  float cap, int32_t causal, hipStream_t stream);
+pa_status native_softcap_attn_bwd(const void *q, const void *k, const void *v, const void *o,
+                                  const void *dout, const float *lse, void *dq, void *dk, void *dv,
+                                  float *workspace, int32_t B, int32_t H, int32_t Hkv, int32_t S,
+                                  int32_t D, float cap, int32_t causal, hipStream_t stream);
+pa_status native_sigmoid_attn_fwd(const void *q, const void *k, const void *v, void *o, int32_t B,
+                                  int32_t H, int32_t Hkv, int32_t S, int32_t D, int32_t causal,
+                                  hipStream_t stream);
+pa_status native_sigmoid_attn_bwd(const void *q, const void *k, const void *v, const void *dout,
+                                  void *dq, void *dk, void *dv, int32_t B, int32_t H, int32_t Hkv,
+                                  int32_t S, int32_t D, int32_t causal, hipStream_t stream);
 
 /* ---- host-only queries (no device work) -------------------------------- */
 
 /* The program the kernels execute for (f, deriv, t).  Returns PA_ERR_FUNC if
  * there is none, PA_ERR_NULL if out is NULL. */
 pa_status poly_program_info(pa_func f, int32_t deriv, pa_dtype t, pa_program *out);
+
+/* The sigmoid-attention program (BF16 bit patterns): region threshold, clamp
+ * bounds, coeff_bits[r][j] = coefficient of x^j in region r (r = 1 when
+ * x >= thr), derivative factor a_bits[r] + b_bits[r] x, and the sequence
+ * length n it holds for.  Returns PA_ERR_NULL if out is NULL. */
+pa_status poly_sigmoid_attn_program(pa_sigmoid_attn_program *out);
 
 /* Static description of a status code. */
 const char *pa_status_str(pa_status s);

@@ -110,7 +110,7 @@ def lib():
                                             C.c_void_p, i64, C.c_void_p, C.c_void_p,
                                             C.c_void_p]),
             "orc_attn_bwd_rows": (C.c_int, [P(Attn)] + [C.c_void_p] * 7 + [i64, C.c_void_p, i64]
-                                  + [C.c_void_p] * 6),
+                                  + [C.c_void_p] * 10),
             "orc_dtanh_prog_f16": (u16, [P(Prog), u16]),
             "orc_sig_prog_eval": (u16, [P(SigProg), u16, C.c_int, P(u16)]),
             "orc_threads": (C.c_int, []),
@@ -260,14 +260,18 @@ def attn_bwd_rows(kind: int, q, k, v, o, dout, lse, qrows, krows, cap: float = 5
     """Gradients of sum(O * dout) for the flat query rows (dQ) and key rows
     (b Hkv + hk) S + j (dK, dV).  o: float64 [B, H, S, D] (the forward output
     the backward is given), lse: float64 [B, H, S] (softcap only).  Returns
-    (dq, dk, dv, nz_dq, nz_dk, nz_dv), float64 [rows, D] each."""
+    (dq, dk, dv, nz_dq, nz_dk, nz_dv, cs_dq, cs_dk, sd_dq, sd_dk), float64
+    [rows, D] each: the gradients, their noise scales, their cancellation
+    scales and their sensitivity to an absolute error in the transform's
+    derivative."""
     q, k, v, dout = _u16(q), _u16(k), _u16(v), _u16(dout)
     D = q.shape[3]
     o = np.ascontiguousarray(o, dtype=np.float64)
     lse = np.ascontiguousarray(np.zeros(1) if lse is None else lse, dtype=np.float64)
     qrows = np.ascontiguousarray(qrows, dtype=np.int64)
     krows = np.ascontiguousarray(krows, dtype=np.int64)
-    res = [np.zeros((n, D)) for n in (qrows.size, krows.size, krows.size) * 2]
+    res = [np.zeros((n, D)) for n in (qrows.size, krows.size, krows.size) * 2
+           + (qrows.size, krows.size) * 2]
     a = _attn(kind, q, k, cap, causal, tanh_prog, sig, order)
     rc = lib().orc_attn_bwd_rows(C.byref(a), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout),
                                  _ptr(lse), _ptr(qrows), qrows.size, _ptr(krows), krows.size,

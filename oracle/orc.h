@@ -136,7 +136,8 @@ int orc_attn_bwd_rows(const orc_attn *a, const uint16_t *q, const uint16_t *k,
                       const uint16_t *v, const double *o, const uint16_t *dout,
                       const double *lse, const int64_t *qrows, int64_t nq,
                       const int64_t *krows, int64_t nk, double *dq, double *dk,
-                      double *dv, double *nz_dq, double *nz_dk, double *nz_dv);
+                      double *dv, double *nz_dq, double *nz_dk, double *nz_dv,
+                      double *cs_dq, double *cs_dk, double *sd_dq, double *sd_dk);
 uint16_t orc_dtanh_prog_f16(const orc_prog *tanh_prog, uint16_t x);
 uint16_t orc_sig_prog_eval(const orc_sig_prog *sp, uint16_t x, int order, uint16_t *grad);
 int orc_threads(void);

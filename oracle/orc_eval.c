@@ -248,8 +248,13 @@ void orc_swiglu_bwd(const orc_prog *sig, const uint16_t *gate, const uint16_t *u
  *   dQ_i = sum_j dS_ij K_j;   dK_j = sum over query heads of the group and
  *   visible i of dS_ij Q_i.
  * Each output also gets a noise scale sqrt(sum of squared terms): the size of
- * the change caused by independent relative roundings of the terms (used to
- * state the tolerance of a faster implementation). */
+ * the change caused by independent relative roundings of the terms; dQ and dK
+ * also get sum_j |dS_ij / (dP_ij - Delta_i)| A_ij |K_j| (resp. over i with
+ * |Q_i|), A_ij the sum of the absolute products that form dP_ij - Delta_i:
+ * an FP32 evaluation of that difference errs by at most D 2^-24 A_ij, which
+ * matters where dP and Delta cancel; and sum_j |dS_ij / g_ij| |K_j| (resp.
+ * |Q_i|), the sensitivity to an absolute error in the transform's derivative
+ * g (used to state the tolerance of a faster implementation). */
 
 static double stable_sigmoid(double s)
 {
@@ -431,21 +436,38 @@ int orc_attn_fwd_rows(const orc_attn *a, const uint16_t *q, const uint16_t *k,
     return 0;
 }
 
-/* dS_ij and P_ij of one (query row, key row) pair. */
+/* dS_ij and P_ij of one (query row, key row) pair, and two error scales of
+ * an FP32 evaluation of dS:
+ *   cs  |dS / (dP - Delta)| (softcap) or |dS / dP| (sigmoid) times the sum of
+ *       the absolute products that form dP - Delta (or dP);
+ *   sd  |dS / g|, g the derivative of the transform before the 1/sqrt(D) or
+ *       cap / (cap sqrt D) chain factor: the sensitivity to an absolute error
+ *       in g (e.g. 1 - tanh^2 formed from a rounded tanh). */
 static void pair_grad(const actx *c, const uint16_t *qi, const uint16_t *kj,
-                      const uint16_t *vj, const uint16_t *doi, double lse_i,
-                      double delta_i, double *P, double *dS)
+                      const uint16_t *vj, const uint16_t *doi, const double *oi,
+                      double lse_i, double delta_i, double *P, double *dS, double *cs,
+                      double *sd)
 {
     const int D = c->a->D;
     double val, dval;
     score(c, dot_bf16(qi, kj, D), &val, &dval);
     const double dP = dot_bf16(doi, vj, D);
+    double a = 0.0;
+    for (int d = 0; d < D; d++) {
+        const double g = fabs(orc_bf16_to_f64(doi[d]));
+        a += g * fabs(orc_bf16_to_f64(vj[d]));
+        if (oi) a += g * fabs(oi[d]);
+    }
     if (is_softcap(c->a)) {
         *P = exp(val - lse_i);
         *dS = *P * (dP - delta_i) * dval;
+        *cs = fabs(*P * dval) * a;
+        *sd = fabs(*P * (dP - delta_i)) * c->rsd;
     } else {
         *P = val;
         *dS = dP * dval;
+        *cs = fabs(dval) * a;
+        *sd = fabs(dP) * c->rsd;
     }
 }
 
@@ -460,7 +482,8 @@ int orc_attn_bwd_rows(const orc_attn *a, const uint16_t *q, const uint16_t *k,
                       const uint16_t *v, const double *o, const uint16_t *dout,
                       const double *lse, const int64_t *qrows, int64_t nq,
                       const int64_t *krows, int64_t nk, double *dq, double *dk,
-                      double *dv, double *nz_dq, double *nz_dk, double *nz_dv)
+                      double *dv, double *nz_dq, double *nz_dk, double *nz_dv,
+                      double *cs_dq, double *cs_dk, double *sd_dq, double *sd_dk)
 {
     actx c;
     const int rc = actx_init(&c, a);
@@ -477,15 +500,23 @@ int orc_attn_bwd_rows(const orc_attn *a, const uint16_t *q, const uint16_t *k,
         const double delta = sc ? row_delta(dout + r * D, o + r * D, (int)D) : 0.0;
         const double li = sc ? lse[r] : 0.0;
         const int64_t n = a->causal ? i + 1 : S;
-        for (int64_t d = 0; d < D; d++) { dq[ri * D + d] = 0.0; if (nz_dq) nz_dq[ri * D + d] = 0.0; }
+        for (int64_t d = 0; d < D; d++) {
+            dq[ri * D + d] = 0.0;
+            if (nz_dq) nz_dq[ri * D + d] = 0.0;
+            if (cs_dq) cs_dq[ri * D + d] = 0.0;
+            if (sd_dq) sd_dq[ri * D + d] = 0.0;
+        }
         for (int64_t j = 0; j < n; j++) {
-            double P, dS;
-            pair_grad(&c, q + r * D, k + kvb + j * D, v + kvb + j * D, dout + r * D, li,
-                      delta, &P, &dS);
+            double P, dS, cs, sd;
+            pair_grad(&c, q + r * D, k + kvb + j * D, v + kvb + j * D, dout + r * D,
+                      sc ? o + r * D : NULL, li, delta, &P, &dS, &cs, &sd);
             for (int64_t d = 0; d < D; d++) {
-                const double t = dS * orc_bf16_to_f64(k[kvb + j * D + d]);
+                const double kd = orc_bf16_to_f64(k[kvb + j * D + d]);
+                const double t = dS * kd;
                 dq[ri * D + d] += t;
                 if (nz_dq) nz_dq[ri * D + d] += t * t;
+                if (cs_dq) cs_dq[ri * D + d] += cs * fabs(kd);
+                if (sd_dq) sd_dq[ri * D + d] += sd * fabs(kd);
             }
         }
         if (nz_dq)
@@ -501,17 +532,23 @@ int orc_attn_bwd_rows(const orc_attn *a, const uint16_t *q, const uint16_t *k,
             dk[ri * D + d] = dv[ri * D + d] = 0.0;
             if (nz_dk) nz_dk[ri * D + d] = 0.0;
             if (nz_dv) nz_dv[ri * D + d] = 0.0;
+            if (cs_dk) cs_dk[ri * D + d] = 0.0;
+            if (sd_dk) sd_dk[ri * D + d] = 0.0;
         }
         for (int64_t h = hk * G; h < (hk + 1) * G; h++) {
             const int64_t qb = (b * a->H + h) * S;
             for (int64_t i = a->causal ? j : 0; i < S; i++) {
                 const int64_t qr = qb + i;
                 const double delta = sc ? row_delta(dout + qr * D, o + qr * D, (int)D) : 0.0;
-                double P, dS;
+                double P, dS, cs, sd;
                 pair_grad(&c, q + qr * D, k + r * D, v + r * D, dout + qr * D,
-                          sc ? lse[qr] : 0.0, delta, &P, &dS);
+                          sc ? o + qr * D : NULL, sc ? lse[qr] : 0.0, delta, &P, &dS, &cs,
+                          &sd);
                 for (int64_t d = 0; d < D; d++) {
-                    const double tk = dS * orc_bf16_to_f64(q[qr * D + d]);
+                    const double qd = orc_bf16_to_f64(q[qr * D + d]);
+                    const double tk = dS * qd;
+                    if (cs_dk) cs_dk[ri * D + d] += cs * fabs(qd);
+                    if (sd_dk) sd_dk[ri * D + d] += sd * fabs(qd);
                     const double tv = P * orc_bf16_to_f64(dout[qr * D + d]);
                     dk[ri * D + d] += tk;
                     dv[ri * D + d] += tv;

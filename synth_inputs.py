@@ -34,7 +34,7 @@ GOLDEN = np.uint64(0x9E3779B97F4A7C15)
 M1 = np.uint64(0xBF58476D1CE4E5B9)
 M2 = np.uint64(0x94D049BB133111EB)
 
-SEED_X, SEED_U, SEED_G, SEED_ROUTE = 1, 2, 3, 4
+SEED_X, SEED_U, SEED_G, SEED_ROUTE, SEED_DO = 1, 2, 3, 4, 5
 
 
 def splitmix64(seed: int, n: int, offset: int = 0) -> np.ndarray:
@@ -135,10 +135,18 @@ def t_swiglu_inputs(rows: int, cols: int, device="cuda"):
     return g, u, d
 
 
-def t_attn_inputs(B=1, H=16, S=8192, D=128, device="cuda"):
-    n = B * H * S * D
-    return tuple(t_bf16(t_normal(s, n, 1.0, device)).view(B, H, S, D)
-                 for s in (SEED_X, SEED_U, SEED_G))
+def t_attn_inputs(B=1, H=16, S=8192, D=128, device="cuda", Hkv=None):
+    """Q [B, H, S, D], K and V [B, Hkv, S, D] (Hkv = H by default), BF16 ~ N(0, 1)."""
+    Hkv = H if Hkv is None else Hkv
+    q = t_bf16(t_normal(SEED_X, B * H * S * D, 1.0, device)).view(B, H, S, D)
+    k, v = (t_bf16(t_normal(s, B * Hkv * S * D, 1.0, device)).view(B, Hkv, S, D)
+            for s in (SEED_U, SEED_G))
+    return q, k, v
+
+
+def t_attn_grad(B=1, H=16, S=8192, D=128, device="cuda"):
+    """Upstream gradient dO [B, H, S, D], BF16 ~ N(0, 1)."""
+    return t_bf16(t_normal(SEED_DO, B * H * S * D, 1.0, device)).view(B, H, S, D)
 
 
 def to_f16_bits(v: np.ndarray) -> np.ndarray:
@@ -224,9 +232,13 @@ def zipf_routing(tokens: int = 16384, experts: int = 64, top_k: int = 8, s: floa
     return offsets, counts
 
 
-def attn_inputs(B: int = 1, H: int = 16, S: int = 8192, D: int = 128):
-    n = B * H * S * D
-    q = to_bf16_bits(normal(SEED_X, n)).reshape(B, H, S, D)
-    k = to_bf16_bits(normal(SEED_U, n)).reshape(B, H, S, D)
-    v = to_bf16_bits(normal(SEED_G, n)).reshape(B, H, S, D)
+def attn_inputs(B: int = 1, H: int = 16, S: int = 8192, D: int = 128, Hkv: int = None):
+    Hkv = H if Hkv is None else Hkv
+    q = to_bf16_bits(normal(SEED_X, B * H * S * D)).reshape(B, H, S, D)
+    k = to_bf16_bits(normal(SEED_U, B * Hkv * S * D)).reshape(B, Hkv, S, D)
+    v = to_bf16_bits(normal(SEED_G, B * Hkv * S * D)).reshape(B, Hkv, S, D)
     return q, k, v
+
+
+def attn_grad(B: int = 1, H: int = 16, S: int = 8192, D: int = 128):
+    return to_bf16_bits(normal(SEED_DO, B * H * S * D)).reshape(B, H, S, D)

@@ -29,11 +29,11 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(pa):
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 20, names
     L = pa.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert L.pa_abi_version() == 1
+    assert L.pa_abi_version() == 2
 
 
 def test_program_table_matches_oracle(pa, orc):
@@ -48,7 +48,18 @@ def test_program_table_matches_oracle(pa, orc):
         # and the oracle, fitting now, agrees
         p = orc.make_prog(g["func"], g["deriv"], g["degree"], g["Li"], g["Lc"])
         assert p.coeff_bits() == g["coeff_bits"]
+    # the softcap backward program: the analytic derivative of tanh D4,
+    # coefficients (j + 1) c_{j+1} of the golden BF16 values, in FP16
+    import numpy as np
+    t4 = [g for g in gold if g["name"] == "tanh_fwd_d4"][0]
+    c = [float(np.array([b << 16], np.uint32).view(np.float32)[0]) for b in t4["coeff_bits"]]
+    want = [int(np.float16((j + 1) * c[j + 1]).view(np.uint16)) for j in range(4)]
+    assert all(float(np.float16((j + 1) * c[j + 1])) == (j + 1) * c[j + 1] for j in range(4))
+    d = pa.program_info("tanh", 2, "f16")
+    assert d["coeff_bits"] == want and d["degree"] == 3 and d["order"] == 1
     out = pa.PaProgram()
+    assert pa.lib().poly_program_info(2, 2, 2, C.byref(out)) == 3   # derivative program: FP16 only
+    assert pa.lib().poly_program_info(1, 2, 1, C.byref(out)) == 4   # only for tanh
     assert pa.lib().poly_program_info(9, 0, 1, C.byref(out)) == 4   # no such function
     assert pa.lib().poly_program_info(1, 0, 5, C.byref(out)) == 3   # no such dtype
 
@@ -91,13 +102,53 @@ def test_error_paths_swiglu(pa):
              None, 0, None) == 0
 
 
+def test_sigmoid_attention_program_matches_golden(pa):
+    """The library's sigmoid-attention constants are the printed ones."""
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "sigmoid_attn_b3.json")))
+    info = pa.sigmoid_attn_program()
+    h = lambda x: int(x, 16)
+    assert info["n"] == g["n"]
+    assert (info["thr"], info["clamp_lo"], info["clamp_hi"]) == \
+        (h(g["threshold"]), h(g["clamp_lo"]), h(g["clamp_hi"]))
+    for r, name in enumerate(("region_lo", "region_hi")):
+        assert info["coeff_bits"][r] == [h(g[name][f"c{j}"]) for j in range(4)]
+        assert info["a_bits"][r] == h(g[name]["a"]) and info["b_bits"][r] == h(g[name]["b"])
+    assert info["order"] == 3
+    assert pa.lib().poly_sigmoid_attn_program(None) == 1
+
+
 def test_error_paths_attention(pa):
     L = pa.lib()
     a = L.poly_softcap_attn_fwd
     big = 1 << 30
-    assert a(FAKE, FAKE + big, FAKE + 2 * big, FAKE + 3 * big, 1, 2, 64, 64, 50.0, 1, None) == 2
-    assert a(FAKE, FAKE + big, FAKE + 2 * big, FAKE + 3 * big, 1, 2, 64, 128, -1.0, 1, None) == 2
-    assert a(FAKE + 2, FAKE + big, FAKE + 2 * big, FAKE + 3 * big, 1, 2, 64, 128, 50.0, 1, None) == 7
-    assert a(FAKE, FAKE + big, FAKE + 2 * big, FAKE, 1, 2, 64, 128, 50.0, 1, None) == 5
-    assert a(None, FAKE, FAKE, FAKE, 1, 2, 64, 128, 50.0, 1, None) == 1
-    assert a(FAKE, FAKE + big, FAKE + 2 * big, FAKE + 3 * big, 0, 2, 64, 128, 50.0, 1, None) == 0
+    Q, K, V, O, LSE = FAKE, FAKE + big, FAKE + 2 * big, FAKE + 3 * big, FAKE + 4 * big
+    assert a(Q, K, V, O, None, 1, 2, 2, 64, 64, 50.0, 1, None) == 2           # D != 128
+    assert a(Q, K, V, O, None, 1, 2, 2, 64, 128, -1.0, 1, None) == 2          # cap
+    assert a(Q, K, V, O, None, 1, 4, 3, 64, 128, 50.0, 1, None) == 2          # H % Hkv
+    assert a(Q, K, V, O, None, 1, 4, 0, 64, 128, 50.0, 1, None) == 2          # Hkv = 0
+    assert a(Q + 2, K, V, O, None, 1, 2, 2, 64, 128, 50.0, 1, None) == 7      # alignment
+    assert a(Q, K, V, O, LSE + 2, 1, 2, 2, 64, 128, 50.0, 1, None) == 7       # lse alignment
+    assert a(Q, K, V, Q, None, 1, 2, 2, 64, 128, 50.0, 1, None) == 5          # O over Q
+    assert a(Q, K, V, O, O + 64, 1, 2, 2, 64, 128, 50.0, 1, None) == 5        # lse over O
+    assert a(None, K, V, O, None, 1, 2, 2, 64, 128, 50.0, 1, None) == 1
+    assert a(Q, K, V, O, None, 0, 2, 2, 64, 128, 50.0, 1, None) == 0          # empty: no launch
+    assert a(Q, K, V, O, LSE, 1, 2, 1, 0, 128, 50.0, 1, None) == 0
+    b = L.poly_softcap_attn_bwd
+    DO, DQ, DK, DV, WS = (FAKE + i * big for i in range(5, 10))
+    assert b(Q, K, V, O, DO, LSE, DQ, DK, DV, None, 1, 2, 2, 64, 128, 50.0, 1, None) == 1
+    assert b(Q, K, V, None, DO, LSE, DQ, DK, DV, WS, 1, 2, 2, 64, 128, 50.0, 1, None) == 1
+    assert b(Q, K, V, O, DO, LSE, DQ, DQ + 64, DV, WS, 1, 2, 2, 64, 128, 50.0, 1, None) == 5
+    assert b(Q, K, V, O, DO, LSE, DQ, DK, DV, DO, 1, 2, 2, 64, 128, 50.0, 1, None) == 5
+    assert b(Q, K, V, O, DO, LSE, DQ, DK, DV, WS + 1, 1, 2, 2, 64, 128, 50.0, 1, None) == 7
+    assert b(Q, K, V, O, DO, LSE, DQ, DK, DV, WS, 1, 2, 2, 64, 128, 0.0, 1, None) == 2
+    assert b(Q, K, V, O, DO, LSE, DQ, DK, DV, WS, 1, 2, 2, 0, 128, 50.0, 1, None) == 0
+    s = L.poly_sigmoid_attn_fwd
+    assert s(Q, K, V, O, 1, 2, 2, 2048, 128, 1, None) == 2     # the fitted length is 4096
+    assert s(Q, K, V, O, 1, 2, 2, 4096, 96, 1, None) == 2
+    assert s(Q, K, V, O, 1, 2, 2, 0, 128, 1, None) == 0
+    assert L.native_sigmoid_attn_fwd(Q, K, V, K, 1, 2, 2, 2048, 128, 1, None) == 5
+    sb = L.poly_sigmoid_attn_bwd
+    assert sb(Q, K, V, DO, DQ, DK, DV, 1, 2, 2, 1000, 128, 1, None) == 2
+    assert sb(Q, K, V, DO, DQ, DK, DK, 1, 2, 2, 4096, 128, 1, None) == 5     # dk == dv
+    assert sb(Q, K, V, None, DQ, DK, DV, 1, 2, 2, 4096, 128, 1, None) == 1
+    assert L.native_sigmoid_attn_bwd(Q, K, V, DO, DQ, DK, DV, 1, 2, 2, 0, 128, 1, None) == 0

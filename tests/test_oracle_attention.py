@@ -105,12 +105,12 @@ def run_both(orc, kind, q, k, v, do, causal, transform, softmax, **kw):
     o, lse, noise = orc.attn_fwd_rows(kind, q, k, v, rows, causal=causal, **kw)
     o_exact = o_ref.detach().numpy()
     lse_exact = None if lse_ref is None else lse_ref.detach().numpy()
-    dq, dk, dv, nq, nk, nv = orc.attn_bwd_rows(kind, q, k, v, o_exact, do, lse_exact, rows,
+    dq, dk, dv, nq, nk, nv, cq, ck, sq, sk = orc.attn_bwd_rows(kind, q, k, v, o_exact, do, lse_exact, rows,
                                                np.arange(B * Hkv * S), causal=causal, **kw)
     ref = dict(o=o_exact.reshape(-1, D), lse=None if lse_exact is None else lse_exact.ravel(),
                dq=qt.grad.numpy().reshape(-1, D), dk=kt.grad.numpy().reshape(-1, D),
                dv=vt.grad.numpy().reshape(-1, D))
-    got = dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv, noise=(noise, nq, nk, nv))
+    got = dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv, noise=(noise, nq, nk, nv, cq, ck, sq, sk))
     return got, ref
 
 
