@@ -209,8 +209,11 @@ def components(torch, pa, si):
     tp, tn = alternating(torch, fp, fn, 5, 5)
     res["sigmoid_attn_fwd"] = attn_row(tp, tn, flops, {"causal_scores": scores})
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    fp = lambda: pa.poly_sigmoid_attn_bwd(q, k, v, dout, True, dq=dq, dk=dk, dv=dv)  # noqa: E731
-    fn = lambda: pa.native_sigmoid_attn_bwd(q, k, v, dout, True, dq=dq, dk=dk, dv=dv)  # noqa: E731
+    ws = pa.attn_bwd_workspace(False, 1, 32, 8, 4096, 128, device=q.device)
+    fp = lambda: pa.poly_sigmoid_attn_bwd(q, k, v, dout, True, dq=dq, dk=dk, dv=dv,  # noqa: E731
+                                          workspace=ws)
+    fn = lambda: pa.native_sigmoid_attn_bwd(q, k, v, dout, True, dq=dq, dk=dk, dv=dv,  # noqa: E731
+                                            workspace=ws)
     fp(), fn()
     tp, tn = alternating(torch, fp, fn, 5, 5)
     res["sigmoid_attn_bwd"] = attn_row(tp, tn, 2.5 * flops, {"causal_scores": scores})

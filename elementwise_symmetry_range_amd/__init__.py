@@ -27,7 +27,7 @@ __all__ = [
     "native_swiglu_bwd", "poly_softcap_attn_fwd", "native_softcap_attn_fwd",
     "poly_softcap_attn_bwd", "native_softcap_attn_bwd", "poly_sigmoid_attn_fwd",
     "native_sigmoid_attn_fwd", "poly_sigmoid_attn_bwd", "native_sigmoid_attn_bwd",
-    "sigmoid_attn_program", "FUNCS",
+    "sigmoid_attn_program", "attn_bwd_workspace", "FUNCS",
 ]
 
 FUNCS = {"sigmoid": 1, "tanh": 2, "silu": 3, "gelu": 4}
@@ -82,8 +82,8 @@ def lib() -> C.CDLL:
             "native_softcap_attn_bwd": [p] * 10 + [i32] * 5 + [f32, i32, p],
             "poly_sigmoid_attn_fwd": [p] * 4 + [i32] * 6 + [p],
             "native_sigmoid_attn_fwd": [p] * 4 + [i32] * 6 + [p],
-            "poly_sigmoid_attn_bwd": [p] * 7 + [i32] * 6 + [p],
-            "native_sigmoid_attn_bwd": [p] * 7 + [i32] * 6 + [p],
+            "poly_sigmoid_attn_bwd": [p] * 8 + [i32] * 6 + [p],
+            "native_sigmoid_attn_bwd": [p] * 8 + [i32] * 6 + [p],
             "poly_sigmoid_attn_program": [C.POINTER(PaSigmoidAttnProgram)],
             "poly_program_info": [i32, i32, i32, C.POINTER(PaProgram)],
         }
@@ -93,6 +93,8 @@ def lib() -> C.CDLL:
             fn.restype = C.c_int
         L.pa_status_str.argtypes = [C.c_int]
         L.pa_status_str.restype = C.c_char_p
+        L.pa_attn_bwd_workspace_bytes.argtypes = [i32] * 6
+        L.pa_attn_bwd_workspace_bytes.restype = C.c_int64
         L.pa_abi_version.argtypes = []
         L.pa_abi_version.restype = C.c_int32
         _lib = L
@@ -286,6 +288,26 @@ def _grads(q, k, dq, dk, dv):
     return _like(dq, q, "dq"), _like(dk, k, "dk"), _like(dv, k, "dv")
 
 
+def attn_bwd_workspace(softcap: bool, B, H, Hkv, S, D=128, device=None):
+    """A workspace tensor of the size the attention backward needs (None if
+    it needs none)."""
+    n = lib().pa_attn_bwd_workspace_bytes(int(bool(softcap)), B, H, Hkv, S, D)
+    if n < 0:
+        raise ValueError("invalid attention shape")
+    if n == 0:
+        return None
+    return torch.empty(n // 4, dtype=torch.float32, device=device)
+
+
+def _ws(workspace, softcap, B, H, Hkv, S, D, device):
+    need = lib().pa_attn_bwd_workspace_bytes(int(bool(softcap)), B, H, Hkv, S, D)
+    if workspace is None:
+        return attn_bwd_workspace(softcap, B, H, Hkv, S, D, device)
+    if workspace.dtype != torch.float32 or workspace.numel() * 4 < need or not workspace.is_cuda:
+        raise ValueError(f"workspace must be a float32 CUDA tensor of at least {need} bytes")
+    return workspace
+
+
 def _softcap_bwd(entry, q, k, v, o, dout, lse, cap, causal, dq, dk, dv, workspace):
     B, H, Hkv, S, D = _attn_shapes(q, k, v)
     _bf16_4d(o, "o")
@@ -295,10 +317,7 @@ def _softcap_bwd(entry, q, k, v, o, dout, lse, cap, causal, dq, dk, dv, workspac
     if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, S) or not lse.is_contiguous():
         raise ValueError("lse must be contiguous float32 [B, H, S]")
     dq, dk, dv = _grads(q, k, dq, dk, dv)
-    if workspace is None:
-        workspace = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
-    elif workspace.dtype != torch.float32 or workspace.numel() < B * H * S:
-        raise ValueError("workspace must be float32 with at least B * H * S elements")
+    workspace = _ws(workspace, True, B, H, Hkv, S, D, q.device)
     _check(entry(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
                  lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                  workspace.data_ptr(), B, H, Hkv, S, D, float(cap), int(bool(causal)),
@@ -338,24 +357,30 @@ def native_sigmoid_attn_fwd(q, k, v, causal: bool = True, out=None):
     return _sigmoid_fwd(lib().native_sigmoid_attn_fwd, q, k, v, causal, out)
 
 
-def _sigmoid_bwd(entry, q, k, v, dout, causal, dq, dk, dv):
+def _sigmoid_bwd(entry, q, k, v, dout, causal, dq, dk, dv, workspace):
     B, H, Hkv, S, D = _attn_shapes(q, k, v)
     _bf16_4d(dout, "dout")
     if dout.shape != q.shape:
         raise ValueError("dout must have q's shape")
     dq, dk, dv = _grads(q, k, dq, dk, dv)
+    workspace = _ws(workspace, False, B, H, Hkv, S, D, q.device)
     _check(entry(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(), dq.data_ptr(),
-                 dk.data_ptr(), dv.data_ptr(), B, H, Hkv, S, D, int(bool(causal)), _stream(q)))
+                 dk.data_ptr(), dv.data_ptr(), None if workspace is None else workspace.data_ptr(),
+                 B, H, Hkv, S, D, int(bool(causal)), _stream(q)))
     return dq, dk, dv
 
 
-def poly_sigmoid_attn_bwd(q, k, v, dout, causal: bool = True, dq=None, dk=None, dv=None):
+def poly_sigmoid_attn_bwd(q, k, v, dout, causal: bool = True, dq=None, dk=None, dv=None,
+                          workspace=None):
     """Backward of poly_sigmoid_attn_fwd with the factored derivative surrogate."""
-    return _sigmoid_bwd(lib().poly_sigmoid_attn_bwd, q, k, v, dout, causal, dq, dk, dv)
+    return _sigmoid_bwd(lib().poly_sigmoid_attn_bwd, q, k, v, dout, causal, dq, dk, dv,
+                        workspace)
 
 
-def native_sigmoid_attn_bwd(q, k, v, dout, causal: bool = True, dq=None, dk=None, dv=None):
-    return _sigmoid_bwd(lib().native_sigmoid_attn_bwd, q, k, v, dout, causal, dq, dk, dv)
+def native_sigmoid_attn_bwd(q, k, v, dout, causal: bool = True, dq=None, dk=None, dv=None,
+                            workspace=None):
+    return _sigmoid_bwd(lib().native_sigmoid_attn_bwd, q, k, v, dout, causal, dq, dk, dv,
+                        workspace)
 
 
 def sigmoid_attn_program() -> dict:

@@ -46,6 +46,7 @@ struct AttnBwdArgs {
     const uint16_t *q, *k, *v, *o, *dout;
     const float *lse;      // softcap: natural log-sum-exp per query row
     float *delta;          // softcap: workspace, Delta per query row
+    float *part;           // grouped query heads: FP32 dK, dV partials per query head
     uint16_t *dq, *dk, *dv;
     int32_t S, H, G;       // G = H / Hkv
     int32_t causal;
@@ -247,7 +248,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
 constexpr int AT_BK = 128;   // keys per dK/dV workgroup
 constexpr int AT_BQ = 64;    // query rows per streamed tile
 
-template <int MODE>
+// SPLIT (grouped query heads): one workgroup per (query head, key tile)
+// instead of per (key/value head, key tile), so a group's heads run in
+// parallel; each writes its FP32 dK, dV contribution to a.part and
+// k_attn_bwd_reduce sums the group.  Without the split the workgroups of a
+// causal launch differ G-fold more in work and there are G times fewer.
+template <int MODE, bool SPLIT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_attn_bwd_dkdv(AttnBwdArgs a)
 {
     constexpr bool SOFTCAP = am_softcap(MODE);
@@ -262,9 +268,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int g16 = lane >> 4, i16 = lane & 15;
     const int S = a.S, G = a.G;
     const int ntk = (S + AT_BK - 1) / AT_BK;
-    const int nbk = (int)(gridDim.x / (unsigned)ntk);       // B * Hkv
+    const int nbk = (int)(gridDim.x / (unsigned)ntk);       // B * Hkv, or B * H (SPLIT)
     const int krank = (int)blockIdx.x / nbk;                 // 0 = heaviest key tile
-    const int bk = (int)blockIdx.x - krank * nbk;            // b Hkv + hk
+    const int bx = (int)blockIdx.x - krank * nbk;            // b Hkv + hk, or b H + h (SPLIT)
+    const int bk = SPLIT ? bx / G : bx;                      // key/value head
     const int kt = krank;                                    // causal: key tile 0 sees the most queries
     const int64_t kvbase = (int64_t)bk * S * AT_D;
     const int k0 = kt * AT_BK + wave * 32;
@@ -286,9 +293,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // see this workgroup's keys
     const int qstart = a.causal ? kt * AT_BK : 0;
     const int nqt = (S - qstart + AT_BQ - 1) / AT_BQ;
-    const int ntile = G * nqt;
+    const int ntile = SPLIT ? nqt : G * nqt;
 
-    auto head_of = [&](int t) { return (int64_t)bk * G + t / nqt; };
+    auto head_of = [&](int t) { return SPLIT ? (int64_t)bx : (int64_t)bk * G + t / nqt; };
     auto load = [&](int t, int buf) {
         const int64_t bh = head_of(t);
         const int r0 = qstart + (t % nqt) * AT_BQ;
@@ -402,6 +409,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
 
     if (!valid) return;
+    if constexpr (SPLIT) {
+        // FP32 partials of this query head: part[0][bx][my_k][:] = dK (before
+        // the 1/sqrt(D) factor), part[1][bx][my_k][:] = dV
+        const int64_t plane = (int64_t)gridDim.x / ntk * S * AT_D;   // B H S D
+        float *pk = a.part + (int64_t)bx * S * AT_D + (int64_t)my_k * AT_D;
+        float *pv = pk + plane;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int d = db * 32 + j * 8 + h * 4;
+                *(f32x4 *)(pk + d) = f32x4{dk[db][j * 4], dk[db][j * 4 + 1], dk[db][j * 4 + 2], dk[db][j * 4 + 3]};
+                *(f32x4 *)(pv + d) = f32x4{dv[db][j * 4], dv[db][j * 4 + 1], dv[db][j * 4 + 2], dv[db][j * 4 + 3]};
+            }
+        }
+        return;
+    }
     uint16_t *krow = a.dk + kvbase + (int64_t)my_k * AT_D;
     uint16_t *vrow = a.dv + kvbase + (int64_t)my_k * AT_D;
 #pragma unroll
@@ -418,6 +442,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             *(u32x2 *)(vrow + d) = w;
         }
     }
+}
+
+// dK, dV of a key/value head = the sum of its G query heads' FP32 partials
+// (the group's heads in order, so the result does not depend on scheduling);
+// one thread per 8 consecutive elements of a [B Hkv S D] output.
+__global__ __launch_bounds__(256) void k_attn_bwd_reduce(AttnBwdArgs a, int64_t n8, int64_t SD)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n8) return;
+    const int64_t e = i * 8;                 // element of [B Hkv S D]
+    const int64_t bk = e / SD, r = e - bk * SD;
+    const int64_t plane = n8 * 8 * a.G;      // B H S D
+    const float *pk = a.part + (bk * a.G) * SD + r;
+    f32x4 k0 = {}, k1 = {}, v0 = {}, v1 = {};
+    for (int g = 0; g < a.G; ++g) {
+        const float *p = pk + (int64_t)g * SD;
+        k0 += *(const f32x4 *)p;
+        k1 += *(const f32x4 *)(p + 4);
+        v0 += *(const f32x4 *)(p + plane);
+        v1 += *(const f32x4 *)(p + plane + 4);
+    }
+    u32x4 wk, wv;
+    wk[0] = pack_bf(k0[0] * a.rsd, k0[1] * a.rsd);
+    wk[1] = pack_bf(k0[2] * a.rsd, k0[3] * a.rsd);
+    wk[2] = pack_bf(k1[0] * a.rsd, k1[1] * a.rsd);
+    wk[3] = pack_bf(k1[2] * a.rsd, k1[3] * a.rsd);
+    wv[0] = pack_bf(v0[0], v0[1]);
+    wv[1] = pack_bf(v0[2], v0[3]);
+    wv[2] = pack_bf(v1[0], v1[1]);
+    wv[3] = pack_bf(v1[2], v1[3]);
+    *(u32x4 *)(a.dk + e) = wk;
+    *(u32x4 *)(a.dv + e) = wv;
 }
 
 }  // namespace pa

@@ -148,14 +148,35 @@ inline pa_status attn_fwd(int mode, const void *q, const void *k, const void *v,
     return attn_launched();
 }
 
+// Workspace of a backward call, in floats: Delta per query row (softcap),
+// then, for grouped query heads, FP32 dK and dV partials per query head
+// (16-byte aligned).  0 when none is needed.
+inline int64_t attn_bwd_ws_floats(bool softcap, int32_t B, int32_t H, int32_t Hkv, int32_t S,
+                                  int32_t D)
+{
+    const int64_t rows = (int64_t)B * H * S;
+    int64_t n = softcap ? (rows + 3) / 4 * 4 : 0;
+    if (Hkv > 0 && H > Hkv) n += 2 * rows * D;
+    return n;
+}
+
 template <int MODE>
 inline void attn_bwd_launch(const AttnBwdArgs &a, int32_t B, int32_t H, int32_t Hkv, int32_t S,
                             hipStream_t stream)
 {
     const dim3 gq((unsigned)(((S + AT_BM - 1) / AT_BM) * (B * H)));
-    const dim3 gk((unsigned)(((S + AT_BK - 1) / AT_BK) * (B * Hkv)));
     hipLaunchKernelGGL(k_attn_bwd_dq<MODE>, gq, dim3(256), 0, stream, a);
-    hipLaunchKernelGGL(k_attn_bwd_dkdv<MODE>, gk, dim3(256), 0, stream, a);
+    const int ntk = (S + AT_BK - 1) / AT_BK;
+    if (H == Hkv) {
+        hipLaunchKernelGGL((k_attn_bwd_dkdv<MODE, false>), dim3((unsigned)(ntk * B * Hkv)), dim3(256), 0,
+                           stream, a);
+        return;
+    }
+    hipLaunchKernelGGL((k_attn_bwd_dkdv<MODE, true>), dim3((unsigned)(ntk * B * H)), dim3(256), 0, stream,
+                       a);
+    const int64_t n8 = (int64_t)B * Hkv * S * AT_D / 8;
+    hipLaunchKernelGGL(k_attn_bwd_reduce, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream, a, n8,
+                       (int64_t)S * AT_D);
 }
 
 // o, lse and ws are used by the softcap modes only.
@@ -166,18 +187,20 @@ inline pa_status attn_bwd(int mode, const void *q, const void *k, const void *v,
 {
     const bool softcap = am_softcap(mode);
     if (!q || !k || !v || !dout || !dq || !dk || !dv) return PA_ERR_NULL;
-    if (softcap && (!o || !lse || !ws)) return PA_ERR_NULL;
-    if (!aligned16({q, k, v, dout, dq, dk, dv}) || (softcap && !aligned16({o})) ||
-        ((uintptr_t)lse & 3u) || ((uintptr_t)ws & 3u))
-        return PA_ERR_ALIGN;
+    if (softcap && (!o || !lse)) return PA_ERR_NULL;
     pa_status st = attn_shape(B, H, Hkv, S, D);
     if (st != PA_OK) return st;
+    const int64_t wsn = attn_bwd_ws_floats(softcap, B, H, Hkv, S, D);
+    if (wsn > 0 && !ws) return PA_ERR_NULL;
+    if (!aligned16({q, k, v, dout, dq, dk, dv, ws}) || (softcap && !aligned16({o})) ||
+        ((uintptr_t)lse & 3u))
+        return PA_ERR_ALIGN;
     if (softcap && !cap_ok(cap)) return PA_ERR_SHAPE;
     if (mode == AM_SIGMOID_POLY && S != kSigmoidAttn.n && (int64_t)B * H * S > 0) return PA_ERR_SHAPE;
     if ((int64_t)B * Hkv * ((S + AT_BK - 1) / AT_BK) > 0x7FFFFFFF) return PA_ERR_SHAPE;
     const int64_t qb = (int64_t)B * H * S * D * 2, kb = (int64_t)B * Hkv * S * D * 2;
     const int64_t rb = softcap ? (int64_t)B * H * S * 4 : 0;
-    if (any_overlap({{dq, qb}, {dk, kb}, {dv, kb}, {ws, rb}},
+    if (any_overlap({{dq, qb}, {dk, kb}, {dv, kb}, {ws, wsn * 4}},
                     {{q, qb}, {k, kb}, {v, kb}, {o, softcap ? qb : 0}, {dout, qb}, {lse, rb}}))
         return PA_ERR_OVERLAP;
     if ((int64_t)B * H == 0 || S == 0) return PA_OK;
@@ -188,7 +211,8 @@ inline pa_status attn_bwd(int mode, const void *q, const void *k, const void *v,
     a.o = (const uint16_t *)o;
     a.dout = (const uint16_t *)dout;
     a.lse = lse;
-    a.delta = ws;
+    a.delta = softcap ? ws : nullptr;
+    a.part = H > Hkv ? ws + (softcap ? ((int64_t)B * H * S + 3) / 4 * 4 : 0) : nullptr;
     a.dq = (uint16_t *)dq;
     a.dk = (uint16_t *)dk;
     a.dv = (uint16_t *)dv;

@@ -504,19 +504,26 @@ pa_status native_sigmoid_attn_fwd(const void *q, const void *k, const void *v, v
 }
 
 pa_status poly_sigmoid_attn_bwd(const void *q, const void *k, const void *v, const void *dout,
-                                void *dq, void *dk, void *dv, int32_t B, int32_t H, int32_t Hkv,
-                                int32_t S, int32_t D, int32_t causal, hipStream_t stream)
+                                void *dq, void *dk, void *dv, float *workspace, int32_t B, int32_t H,
+                                int32_t Hkv, int32_t S, int32_t D, int32_t causal, hipStream_t stream)
 {
-    return attn_bwd(AM_SIGMOID_POLY, q, k, v, nullptr, dout, nullptr, dq, dk, dv, nullptr, B, H, Hkv,
-                    S, D, 0.0f, causal, stream);
+    return attn_bwd(AM_SIGMOID_POLY, q, k, v, nullptr, dout, nullptr, dq, dk, dv, workspace, B, H, Hkv, S,
+                    D, 0.0f, causal, stream);
 }
 
 pa_status native_sigmoid_attn_bwd(const void *q, const void *k, const void *v, const void *dout,
-                                  void *dq, void *dk, void *dv, int32_t B, int32_t H, int32_t Hkv,
-                                  int32_t S, int32_t D, int32_t causal, hipStream_t stream)
+                                  void *dq, void *dk, void *dv, float *workspace, int32_t B, int32_t H,
+                                  int32_t Hkv, int32_t S, int32_t D, int32_t causal, hipStream_t stream)
 {
-    return attn_bwd(AM_SIGMOID_NATIVE, q, k, v, nullptr, dout, nullptr, dq, dk, dv, nullptr, B, H,
-                    Hkv, S, D, 0.0f, causal, stream);
+    return attn_bwd(AM_SIGMOID_NATIVE, q, k, v, nullptr, dout, nullptr, dq, dk, dv, workspace, B, H, Hkv, S,
+                    D, 0.0f, causal, stream);
+}
+
+int64_t pa_attn_bwd_workspace_bytes(int32_t softcap, int32_t B, int32_t H, int32_t Hkv,
+                                    int32_t S, int32_t D)
+{
+    if (attn_shape(B, H, Hkv, S, D) != PA_OK) return -1;
+    return 4 * attn_bwd_ws_floats(softcap != 0, B, H, Hkv, S, D);
 }
 
 pa_status poly_sigmoid_attn_program(pa_sigmoid_attn_program *out)

@@ -187,8 +187,11 @@ pa_status poly_softcap_attn_fwd(const void *q, const void *k, const void *v, voi
  * where ds/dS uses the analytic derivative of the D4 tanh program (a D3 with
  * coefficients (j + 1) c_{j+1}, exact in FP16; poly_program_info(PA_TANH, 2,
  * PA_F16)) in packed FP16 at the same clamped |x|.  P and dS are rounded to
- * BF16 for the MFMA.  workspace: caller-owned scratch of B * H * S floats
- * (receives Delta; contents on return unspecified).
+ * BF16 for the MFMA.  workspace: caller-owned scratch, 16-byte aligned, of
+ * pa_attn_bwd_workspace_bytes(1, B, H, Hkv, S, D) bytes: B * H * S floats
+ * for Delta and, when H > Hkv, FP32 dK and dV partials of every query head
+ * (summed per group by a final pass in a fixed order); contents on return
+ * unspecified.
  * Paper: Eq. 12 and section 5.2.2 (the differentiated D3 at the recomputed
  * scaled score), section 3.3 (differentiated-polynomial backward). */
 pa_status poly_softcap_attn_bwd(const void *q, const void *k, const void *v, const void *o,
@@ -212,11 +215,14 @@ pa_status poly_sigmoid_attn_fwd(const void *q, const void *k, const void *v, voi
 /* Sigmoid attention backward: dV = P^T dO, dP = dO V^T, dS = dP g,
  * dQ = dS K / sqrt(D), dK = dS^T Q / sqrt(D), with g the factored derivative
  * surrogate P~(x) (a + b x) of the same region and clamped x (BF16 per
- * stage).  Same length guard.  Paper: section 3.4 (the coupled value /
- * derivative evaluator), Appendix C (Listing 2). */
+ * stage).  Same length guard.  workspace: as for the softcap backward,
+ * pa_attn_bwd_workspace_bytes(0, ...) bytes (none, and NULL allowed, when
+ * H == Hkv).  Paper: section 3.4 (the coupled value / derivative
+ * evaluator), Appendix C (Listing 2). */
 pa_status poly_sigmoid_attn_bwd(const void *q, const void *k, const void *v, const void *dout,
-                                void *dq, void *dk, void *dv, int32_t B, int32_t H, int32_t Hkv,
-                                int32_t S, int32_t D, int32_t causal, hipStream_t stream);
+                                void *dq, void *dk, void *dv, float *workspace, int32_t B,
+                                int32_t H, int32_t Hkv, int32_t S, int32_t D, int32_t causal,
+                                hipStream_t stream);
 
 /* ---- matched comparators (same memory path, accurate FP32 math) -------- */
 
@@ -260,8 +266,9 @@ pa_status native_sigmoid_attn_fwd(const void *q, const void *k, const void *v, v
                                   int32_t H, int32_t Hkv, int32_t S, int32_t D, int32_t causal,
                                   hipStream_t stream);
 pa_status native_sigmoid_attn_bwd(const void *q, const void *k, const void *v, const void *dout,
-                                  void *dq, void *dk, void *dv, int32_t B, int32_t H, int32_t Hkv,
-                                  int32_t S, int32_t D, int32_t causal, hipStream_t stream);
+                                  void *dq, void *dk, void *dv, float *workspace, int32_t B,
+                                  int32_t H, int32_t Hkv, int32_t S, int32_t D, int32_t causal,
+                                  hipStream_t stream);
 
 /* ---- host-only queries (no device work) -------------------------------- */
 
@@ -274,6 +281,11 @@ pa_status poly_program_info(pa_func f, int32_t deriv, pa_dtype t, pa_program *ou
  * x >= thr), derivative factor a_bits[r] + b_bits[r] x, and the sequence
  * length n it holds for.  Returns PA_ERR_NULL if out is NULL. */
 pa_status poly_sigmoid_attn_program(pa_sigmoid_attn_program *out);
+
+/* Bytes of caller-owned workspace an attention backward needs (softcap != 0
+ * for the softcap backward, 0 for sigmoid); -1 for an invalid shape. */
+int64_t pa_attn_bwd_workspace_bytes(int32_t softcap, int32_t B, int32_t H, int32_t Hkv,
+                                    int32_t S, int32_t D);
 
 /* Static description of a status code. */
 const char *pa_status_str(pa_status s);

@@ -23,13 +23,13 @@ def pa():
 def declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*|pa_status\s|int32_t\s)\s*(\w+)\s*\(",
+    return sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*|pa_status\s|int32_t\s|int64_t\s)\s*(\w+)\s*\(",
                                  src, flags=re.M)))
 
 
 def test_exports_every_declared_symbol(pa):
     names = declared_functions()
-    assert len(names) == 20, names
+    assert len(names) == 21, names
     L = pa.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -139,7 +139,7 @@ def test_error_paths_attention(pa):
     assert b(Q, K, V, None, DO, LSE, DQ, DK, DV, WS, 1, 2, 2, 64, 128, 50.0, 1, None) == 1
     assert b(Q, K, V, O, DO, LSE, DQ, DQ + 64, DV, WS, 1, 2, 2, 64, 128, 50.0, 1, None) == 5
     assert b(Q, K, V, O, DO, LSE, DQ, DK, DV, DO, 1, 2, 2, 64, 128, 50.0, 1, None) == 5
-    assert b(Q, K, V, O, DO, LSE, DQ, DK, DV, WS + 1, 1, 2, 2, 64, 128, 50.0, 1, None) == 7
+    assert b(Q, K, V, O, DO, LSE, DQ, DK, DV, WS + 4, 1, 2, 2, 64, 128, 50.0, 1, None) == 7
     assert b(Q, K, V, O, DO, LSE, DQ, DK, DV, WS, 1, 2, 2, 64, 128, 0.0, 1, None) == 2
     assert b(Q, K, V, O, DO, LSE, DQ, DK, DV, WS, 1, 2, 2, 0, 128, 50.0, 1, None) == 0
     s = L.poly_sigmoid_attn_fwd
@@ -148,7 +148,16 @@ def test_error_paths_attention(pa):
     assert s(Q, K, V, O, 1, 2, 2, 0, 128, 1, None) == 0
     assert L.native_sigmoid_attn_fwd(Q, K, V, K, 1, 2, 2, 2048, 128, 1, None) == 5
     sb = L.poly_sigmoid_attn_bwd
-    assert sb(Q, K, V, DO, DQ, DK, DV, 1, 2, 2, 1000, 128, 1, None) == 2
-    assert sb(Q, K, V, DO, DQ, DK, DK, 1, 2, 2, 4096, 128, 1, None) == 5     # dk == dv
-    assert sb(Q, K, V, None, DQ, DK, DV, 1, 2, 2, 4096, 128, 1, None) == 1
-    assert L.native_sigmoid_attn_bwd(Q, K, V, DO, DQ, DK, DV, 1, 2, 2, 0, 128, 1, None) == 0
+    assert sb(Q, K, V, DO, DQ, DK, DV, None, 1, 2, 2, 1000, 128, 1, None) == 2
+    assert sb(Q, K, V, DO, DQ, DK, DK, None, 1, 2, 2, 4096, 128, 1, None) == 5     # dk == dv
+    assert sb(Q, K, V, None, DQ, DK, DV, None, 1, 2, 2, 4096, 128, 1, None) == 1
+    assert sb(Q, K, V, DO, DQ, DK, DV, None, 1, 4, 2, 4096, 128, 1, None) == 1      # GQA needs ws
+    assert sb(Q, K, V, DO, DQ, DK, DV, WS + 4, 1, 4, 2, 4096, 128, 1, None) == 7    # 16-B aligned
+    assert sb(Q, K, V, DO, DQ, DK, DV, DQ, 1, 4, 2, 4096, 128, 1, None) == 5        # ws over dq
+    assert L.native_sigmoid_attn_bwd(Q, K, V, DO, DQ, DK, DV, None, 1, 2, 2, 0, 128, 1, None) == 0
+    wb = L.pa_attn_bwd_workspace_bytes
+    assert wb(0, 1, 8, 8, 4096, 128) == 0
+    assert wb(1, 1, 8, 8, 4095, 128) == 4 * 8 * 4095
+    assert wb(0, 1, 8, 2, 100, 128) == 4 * 2 * 8 * 100 * 128
+    assert wb(1, 1, 3, 1, 5, 128) == 4 * (16 + 2 * 3 * 5 * 128)   # Delta region padded to 16 B
+    assert wb(1, 1, 3, 2, 5, 128) == -1
