@@ -183,6 +183,15 @@ def components(torch, pa, si):
     fp(), fn()
     tp, tn = alternating(torch, fp, fn, 5, 5)
     res["softcap_attn_fwd"] = attn_row(tp, tn, flops, {"causal_scores": scores})
+    # the softmax's exponentials by software exp2 cores (same kernel, same
+    # tanh program) against v_exp_f32
+    cores = {}
+    for core in ("d1", "pwl2", "d2", "d3"):
+        fc = lambda core=core: pa.poly_softcap_attn_fwd_exp2(q, k, v, 50.0, True, core=core, out=o)  # noqa: E731
+        fc()
+        tc, th = alternating(torch, fc, fp, 5, 5)
+        cores[core] = {"ms": round(tc, 4), "hw_exp2_ms": round(th, 4), "speedup_vs_hw": round(th / tc, 3)}
+    res["softcap_attn_fwd_exp2_cores"] = cores
     op, lp = pa.poly_softcap_attn_fwd(q, k, v, 50.0, True, with_lse=True)
     on, ln = pa.native_softcap_attn_fwd(q, k, v, 50.0, True, with_lse=True)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)

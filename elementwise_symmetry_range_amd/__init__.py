@@ -25,7 +25,8 @@ __all__ = [
     "PolyActError", "lib", "program_info", "poly_act_fwd", "poly_act_bwd", "native_act_fwd",
     "native_act_bwd", "poly_swiglu_fwd", "poly_swiglu_bwd", "native_swiglu_fwd",
     "native_swiglu_bwd", "poly_softcap_attn_fwd", "native_softcap_attn_fwd",
-    "poly_softcap_attn_bwd", "native_softcap_attn_bwd", "poly_sigmoid_attn_fwd",
+    "poly_softcap_attn_fwd_exp2", "poly_softcap_attn_bwd", "native_softcap_attn_bwd",
+    "poly_sigmoid_attn_fwd",
     "native_sigmoid_attn_fwd", "poly_sigmoid_attn_bwd", "native_sigmoid_attn_bwd",
     "sigmoid_attn_program", "attn_bwd_workspace", "FUNCS",
 ]
@@ -78,6 +79,7 @@ def lib() -> C.CDLL:
                                   p],
             "poly_softcap_attn_fwd": [p, p, p, p, p, i32, i32, i32, i32, i32, f32, i32, p],
             "native_softcap_attn_fwd": [p, p, p, p, p, i32, i32, i32, i32, i32, f32, i32, p],
+            "poly_softcap_attn_fwd_exp2": [p, p, p, p, p, i32, i32, i32, i32, i32, f32, i32, i32, p],
             "poly_softcap_attn_bwd": [p] * 10 + [i32] * 5 + [f32, i32, p],
             "native_softcap_attn_bwd": [p] * 10 + [i32] * 5 + [f32, i32, p],
             "poly_sigmoid_attn_fwd": [p] * 4 + [i32] * 6 + [p],
@@ -277,6 +279,23 @@ def poly_softcap_attn_fwd(q, k, v, cap: float = 50.0, causal: bool = True, out=N
     q [B, H, S, D], k and v [B, Hkv, S, D].  Returns O, or (O, lse) with
     with_lse (the natural log-sum-exp per row, FP32 [B, H, S])."""
     return _softcap_fwd(lib().poly_softcap_attn_fwd, q, k, v, cap, causal, out, with_lse)
+
+
+EXP2_CORES = {"hw": 0, "d1": 1, "pwl2": 2, "d2": 3, "d3": 4}
+
+
+def poly_softcap_attn_fwd_exp2(q, k, v, cap: float = 50.0, causal: bool = True,
+                               core: str = "pwl2", out=None, with_lse: bool = False):
+    """poly_softcap_attn_fwd with the softmax's exponentials by a software exp2
+    core: "hw" (v_exp_f32), "d1", "pwl2" (packed FP16), "d2", "d3"."""
+    B, H, Hkv, S, D = _attn_shapes(q, k, v)
+    o = _like(out, q, "out")
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device) if with_lse else None
+    _check(lib().poly_softcap_attn_fwd_exp2(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+        None if lse is None else lse.data_ptr(), B, H, Hkv, S, D, float(cap), int(bool(causal)),
+        EXP2_CORES[core], _stream(q)))
+    return (o, lse) if with_lse else o
 
 
 def native_softcap_attn_fwd(q, k, v, cap: float = 50.0, causal: bool = True, out=None,

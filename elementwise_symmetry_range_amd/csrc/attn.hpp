@@ -198,6 +198,54 @@ __device__ __forceinline__ uint32_t sigmoid_poly_pair(float s0, float s1, float 
     return pack_bf(v0, v1);   // exact: v0, v1 are BF16 values
 }
 
+// Software exp2 of the softmax (Appendix B.1, Eqs. 16-19): 2^z = 2^n p(f),
+// n = floor(z), f = z - n, with the reference max m an integer so that
+// 2^(z - m) = ldexp(p(f), n - m) exactly scales by a power of two and the
+// normalised weights do not depend on m.  z is clamped below at -16384
+// (masked keys, z = -inf, give 0).  Cores (p(0) = 1, p(1) = 2 after rounding
+// except D3):
+//   1 D1    p = f + 1                                         (FP32)
+//   2 PWL2  p = 1 + a f + 2 (1 - a) max(f - 1/2, 0), a = 0.7978515625,
+//           in packed FP16 (f rounded to FP16, one rounding per op)
+//   3 D2    p = 1 + a f + (1 - a) f^2, a = RN32(0.6602339719)   (FP32 FMA)
+//   4 D3    the pages' printed cubic                           (FP32 FMA)
+constexpr float EXP2_D2_A = 0.6602339719f;
+constexpr float EXP2_D3_C1 = 0.6951461434f, EXP2_D3_C2 = 0.2275643945f, EXP2_D3_C3 = 0.0771190897f;
+
+template <int EXP>
+__device__ __forceinline__ void exp2_core_pair(float z0, float z1, float m, float &p0, float &p1)
+{
+    z0 = fmaxf(z0, -16384.0f);
+    z1 = fmaxf(z1, -16384.0f);
+    const float n0 = floorf(z0), n1 = floorf(z1);
+    const float f0 = z0 - n0, f1 = z1 - n1;
+    float c0, c1;
+    if constexpr (EXP == 1) {
+        c0 = f0 + 1.0f;
+        c1 = f1 + 1.0f;
+    } else if constexpr (EXP == 2) {
+        h2 fh;
+        fh[0] = (_Float16)f0;
+        fh[1] = (_Float16)f1;
+        const h2 hinge = __builtin_elementwise_max(fh - h2{(_Float16)0.5f, (_Float16)0.5f},
+                                                   h2{(_Float16)0.0f, (_Float16)0.0f});
+        h2 p = __builtin_elementwise_fma(h2{(_Float16)0.7978515625f, (_Float16)0.7978515625f}, fh,
+                                         h2{(_Float16)1.0f, (_Float16)1.0f});
+        p = __builtin_elementwise_fma(h2{(_Float16)0.40380859375f, (_Float16)0.40380859375f}, hinge, p);
+        c0 = (float)p[0];
+        c1 = (float)p[1];
+    } else if constexpr (EXP == 3) {
+        constexpr float b = 1.0f - EXP2_D2_A;   // exact
+        c0 = fmaf(fmaf(b, f0, EXP2_D2_A), f0, 1.0f);
+        c1 = fmaf(fmaf(b, f1, EXP2_D2_A), f1, 1.0f);
+    } else {
+        c0 = fmaf(fmaf(fmaf(EXP2_D3_C3, f0, EXP2_D3_C2), f0, EXP2_D3_C1), f0, 1.0f);
+        c1 = fmaf(fmaf(fmaf(EXP2_D3_C3, f1, EXP2_D3_C2), f1, EXP2_D3_C1), f1, 1.0f);
+    }
+    p0 = __builtin_amdgcn_ldexpf(c0, (int)(n0 - m));
+    p1 = __builtin_amdgcn_ldexpf(c1, (int)(n1 - m));
+}
+
 // accurate sigmoid of u (the comparator)
 __device__ __forceinline__ float sigmoid_acc(float u)
 {
@@ -205,7 +253,9 @@ __device__ __forceinline__ float sigmoid_acc(float u)
     return (u >= 0.0f ? 1.0f : e) / (1.0f + e);
 }
 
-template <int MODE>
+// EXP: 0 = hardware exp2 (v_exp_f32), 1-4 = the software cores above
+// (softcap only).
+template <int MODE, int EXP = 0>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_fwd(AttnArgs a)
 {
     constexpr bool SOFTCAP = am_softcap(MODE);
@@ -361,8 +411,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             // lazy rescale: move the reference only when the row max outgrows it
             const bool grow = zmax > m + AT_RESCALE;
             if (__builtin_amdgcn_ballot_w64(grow)) {
-                const float m_new = grow ? zmax : m;
-                const float corr = __builtin_amdgcn_exp2f(m - m_new);
+                float m_new, corr;
+                if constexpr (EXP == 0) {
+                    m_new = grow ? zmax : m;
+                    corr = __builtin_amdgcn_exp2f(m - m_new);
+                } else {   // integer reference; the rescale is an exact power of two
+                    m_new = grow ? ceilf(zmax) : m;
+                    corr = m == -INFINITY ? 0.0f : __builtin_amdgcn_ldexpf(1.0f, (int)(m - m_new));
+                }
                 l *= corr;
 #pragma unroll
                 for (int db = 0; db < 4; ++db) o[db] *= corr;
@@ -375,11 +431,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
                 for (int jj = 0; jj < 2; ++jj) {
                     bf16x8 frag;
+                    if constexpr (EXP == 0) {
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][jj * 8 + e], a.c2, -m));
-                        l += p;
-                        frag[e] = (__bf16)p;
+                        for (int e = 0; e < 8; ++e) {
+                            const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][jj * 8 + e], a.c2, -m));
+                            l += p;
+                            frag[e] = (__bf16)p;
+                        }
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 8; e += 2) {
+                            float p0, p1;
+                            exp2_core_pair<EXP>(s[kb][jj * 8 + e] * a.c2, s[kb][jj * 8 + e + 1] * a.c2, m,
+                                                p0, p1);
+                            l += p0;
+                            l += p1;
+                            frag[e] = (__bf16)p0;
+                            frag[e + 1] = (__bf16)p1;
+                        }
                     }
                     pf[kb * 2 + jj] = frag;
                 }

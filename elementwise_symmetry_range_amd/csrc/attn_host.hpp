@@ -105,8 +105,9 @@ inline pa_status attn_launched() { return hipGetLastError() == hipSuccess ? PA_O
 
 inline pa_status attn_fwd(int mode, const void *q, const void *k, const void *v, void *o, float *lse,
                           int32_t B, int32_t H, int32_t Hkv, int32_t S, int32_t D, float cap,
-                          int32_t causal, hipStream_t stream)
+                          int32_t causal, hipStream_t stream, int exp2_core = 0)
 {
+    if (exp2_core < 0 || exp2_core > 4 || (exp2_core && mode != AM_SOFTCAP_POLY)) return PA_ERR_FUNC;
     if (!q || !k || !v || !o) return PA_ERR_NULL;
     if (!aligned16({q, k, v, o}) || ((uintptr_t)lse & 3u)) return PA_ERR_ALIGN;
     pa_status st = attn_shape(B, H, Hkv, S, D);
@@ -139,6 +140,13 @@ inline pa_status attn_fwd(int mode, const void *q, const void *k, const void *v,
         a.sig = sigmoid_coefs();
     }
     const dim3 grid((unsigned)(((S + AT_BM - 1) / AT_BM) * (B * H)));
+    switch (exp2_core) {
+    case 1: hipLaunchKernelGGL((k_attn_fwd<AM_SOFTCAP_POLY, 1>), grid, dim3(256), 0, stream, a); return attn_launched();
+    case 2: hipLaunchKernelGGL((k_attn_fwd<AM_SOFTCAP_POLY, 2>), grid, dim3(256), 0, stream, a); return attn_launched();
+    case 3: hipLaunchKernelGGL((k_attn_fwd<AM_SOFTCAP_POLY, 3>), grid, dim3(256), 0, stream, a); return attn_launched();
+    case 4: hipLaunchKernelGGL((k_attn_fwd<AM_SOFTCAP_POLY, 4>), grid, dim3(256), 0, stream, a); return attn_launched();
+    default: break;
+    }
     switch (mode) {
     case AM_SOFTCAP_POLY: hipLaunchKernelGGL(k_attn_fwd<AM_SOFTCAP_POLY>, grid, dim3(256), 0, stream, a); break;
     case AM_SOFTCAP_NATIVE: hipLaunchKernelGGL(k_attn_fwd<AM_SOFTCAP_NATIVE>, grid, dim3(256), 0, stream, a); break;

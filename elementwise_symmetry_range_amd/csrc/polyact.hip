@@ -464,6 +464,15 @@ pa_status poly_softcap_attn_fwd(const void *q, const void *k, const void *v, voi
     return attn_fwd(AM_SOFTCAP_POLY, q, k, v, o, lse, B, H, Hkv, S, D, cap, causal, stream);
 }
 
+pa_status poly_softcap_attn_fwd_exp2(const void *q, const void *k, const void *v, void *o,
+                                     float *lse, int32_t B, int32_t H, int32_t Hkv, int32_t S,
+                                     int32_t D, float cap, int32_t causal, pa_exp2_core core,
+                                     hipStream_t stream)
+{
+    return attn_fwd(AM_SOFTCAP_POLY, q, k, v, o, lse, B, H, Hkv, S, D, cap, causal, stream,
+                    (int)core);
+}
+
 pa_status native_softcap_attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
                                   int32_t B, int32_t H, int32_t Hkv, int32_t S, int32_t D,
                                   float cap, int32_t causal, hipStream_t stream)

@@ -179,6 +179,28 @@ pa_status poly_softcap_attn_fwd(const void *q, const void *k, const void *v, voi
                                 int32_t B, int32_t H, int32_t Hkv, int32_t S, int32_t D, float cap,
                                 int32_t causal, hipStream_t stream);
 
+/* The softmax's exponentials of poly_softcap_attn_fwd by a software exp2
+ * (Appendix B.1, Eqs. 16-19): 2^z = 2^n p(f) with n = floor(z), f = z - n
+ * in [0, 1), z = RN_f32(t * RN_f32(cap log2 e)) clamped below at -16384, and
+ * the running reference kept an integer so that every rescale is an exact
+ * power of two and the normalised weights do not depend on it.  Cores:
+ *   PA_EXP2_HW     v_exp_f32 (the same kernel as poly_softcap_attn_fwd)
+ *   PA_EXP2_D1     p = 1 + f (FP32)
+ *   PA_EXP2_PWL2   p = 1 + a f + 2 (1 - a) max(f - 1/2, 0), a = 0.7978515625,
+ *                  2 (1 - a) = 0.40380859375, packed FP16 (f rounded to FP16)
+ *   PA_EXP2_D2     p = 1 + a f + (1 - a) f^2, a = RN_f32(0.6602339719), FP32 FMA
+ *   PA_EXP2_D3     1 + 0.6951461434 f + 0.2275643945 f^2 + 0.0771190897 f^3
+ *                  (the pages' reference cubic; p(1) != 2), FP32 FMA
+ * D1, PWL2 and D2 keep p(0) = 1 and p(1) = 2 exactly after rounding (the
+ * invariants online softmax needs).  lse as for poly_softcap_attn_fwd, with
+ * the approximate exponentials. */
+typedef enum { PA_EXP2_HW = 0, PA_EXP2_D1 = 1, PA_EXP2_PWL2 = 2, PA_EXP2_D2 = 3,
+               PA_EXP2_D3 = 4 } pa_exp2_core;
+pa_status poly_softcap_attn_fwd_exp2(const void *q, const void *k, const void *v, void *o,
+                                     float *lse, int32_t B, int32_t H, int32_t Hkv, int32_t S,
+                                     int32_t D, float cap, int32_t causal, pa_exp2_core core,
+                                     hipStream_t stream);
+
 /* Softcapped attention backward: given the forward's O and lse and the
  * upstream gradient dout, writes dq, dk, dv:
  *   P = exp(s - lse) recomputed with the forward's program;  dV = P^T dO;

@@ -19,7 +19,7 @@ import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liborc.so")
-SOURCES = ["orc_fp.c", "orc_fit.c", "orc_eval.c"]
+SOURCES = ["orc_fp.c", "orc_fit.c", "orc_eval.c", "orc_exp2.c"]
 
 SIGMOID, TANH, SILU, GELU = 1, 2, 3, 4
 FUNC_NAMES = {SIGMOID: "sigmoid", TANH: "tanh", SILU: "silu", GELU: "gelu"}
@@ -62,11 +62,13 @@ class SigProg(C.Structure):
 class Attn(C.Structure):
     _fields_ = [("kind", C.c_int32), ("B", C.c_int32), ("H", C.c_int32), ("Hkv", C.c_int32),
                 ("S", C.c_int32), ("D", C.c_int32), ("causal", C.c_int32),
-                ("order", C.c_int32), ("cap", C.c_float), ("tanh_prog", C.POINTER(Prog)),
+                ("order", C.c_int32), ("exp2_core", C.c_int32), ("cap", C.c_float),
+                ("tanh_prog", C.POINTER(Prog)),
                 ("sig", C.POINTER(SigProg))]
 
 
 ATTN_SOFTCAP_POLY, ATTN_SOFTCAP_EXACT, ATTN_SIGMOID_POLY, ATTN_SIGMOID_EXACT = 1, 2, 3, 4
+EXP2_EXACT, EXP2_D1, EXP2_PWL2, EXP2_D2, EXP2_D3 = 0, 1, 2, 3, 4
 
 _lib = None
 
@@ -112,6 +114,10 @@ def lib():
             "orc_attn_bwd_rows": (C.c_int, [P(Attn)] + [C.c_void_p] * 7 + [i64, C.c_void_p, i64]
                                   + [C.c_void_p] * 10),
             "orc_dtanh_prog_f16": (u16, [P(Prog), u16]),
+            "orc_exp2_core": (f64, [C.c_int, f64, f64]),
+            "orc_exp2_errors": (None, [C.c_int, f64, P(f64), P(f64)]),
+            "orc_exp2_fit": (f64, [C.c_int, C.c_int]),
+            "orc_exp2_core_target": (C.c_float, [C.c_int, C.c_float]),
             "orc_sig_prog_eval": (u16, [P(SigProg), u16, C.c_int, P(u16)]),
             "orc_threads": (C.c_int, []),
         }
@@ -222,11 +228,11 @@ def sig_prog_from_golden(d: dict) -> SigProg:
     return sp
 
 
-def _attn(kind, q, k, cap, causal, tanh_prog, sig, order):
+def _attn(kind, q, k, cap, causal, tanh_prog, sig, order, exp2_core=0):
     B, H, S, D = q.shape
     a = Attn()
     a.kind, a.B, a.H, a.Hkv, a.S, a.D = kind, B, H, k.shape[1], S, D
-    a.causal, a.order, a.cap = int(causal), order, cap
+    a.causal, a.order, a.cap, a.exp2_core = int(causal), order, cap, exp2_core
     a._keep = (tanh_prog, sig)
     if tanh_prog is not None:
         a.tanh_prog = C.pointer(tanh_prog)
@@ -236,17 +242,19 @@ def _attn(kind, q, k, cap, causal, tanh_prog, sig, order):
 
 
 def attn_fwd_rows(kind: int, q, k, v, rows, cap: float = 50.0, causal: bool = True,
-                  tanh_prog: Prog = None, sig: SigProg = None, order: int = 0):
+                  tanh_prog: Prog = None, sig: SigProg = None, order: int = 0,
+                  exp2_core: int = 0):
     """q: uint16 BF16 bits [B, H, S, D]; k, v: [B, Hkv, S, D].  Returns (O, lse,
     noise) in float64 for the flat query rows (b H + h) S + i: O and noise
-    [len(rows), D], lse [len(rows)] (NaN for sigmoid attention)."""
+    [len(rows), D], lse [len(rows)] (NaN for sigmoid attention).  exp2_core
+    (softcap poly only): the softmax's exponentials by that fractional core."""
     q, k, v = _u16(q), _u16(k), _u16(v)
     D = q.shape[3]
     rows = np.ascontiguousarray(rows, dtype=np.int64)
     out = np.zeros((rows.size, D))
     lse = np.zeros(rows.size)
     noise = np.zeros((rows.size, D))
-    a = _attn(kind, q, k, cap, causal, tanh_prog, sig, order)
+    a = _attn(kind, q, k, cap, causal, tanh_prog, sig, order, exp2_core)
     rc = lib().orc_attn_fwd_rows(C.byref(a), _ptr(q), _ptr(k), _ptr(v), _ptr(rows), rows.size,
                                  _ptr(out), _ptr(lse), _ptr(noise))
     if rc:
@@ -279,6 +287,21 @@ def attn_bwd_rows(kind: int, q, k, v, o, dout, lse, qrows, krows, cap: float = 5
     if rc:
         raise ValueError(f"orc_attn_bwd_rows: {rc}")
     return tuple(res)
+
+
+def exp2_errors(core: int, a: float = 0.0):
+    mx, rms = C.c_double(), C.c_double()
+    lib().orc_exp2_errors(core, a, C.byref(mx), C.byref(rms))
+    return mx.value, rms.value
+
+
+def exp2_fit(core: int, minimax: bool) -> float:
+    return lib().orc_exp2_fit(core, int(minimax))
+
+
+def exp2_core_target(core: int, f) -> np.ndarray:
+    return np.array([lib().orc_exp2_core_target(core, float(x)) for x in np.atleast_1d(f)],
+                    dtype=np.float32)
 
 
 def dtanh_prog_f16(tanh_prog: Prog, x_bits) -> np.ndarray:

@@ -117,11 +117,20 @@ typedef struct {
     uint16_t a[2], b[2];
 } orc_sig_prog;
 
+/* Fractional cores of a software exp2 (orc_exp2.c; Appendix B.1). */
+enum { ORC_EXP2_EXACT = 0, ORC_EXP2_D1 = 1, ORC_EXP2_PWL2 = 2, ORC_EXP2_D2 = 3,
+       ORC_EXP2_D3 = 4 };
+double orc_exp2_core(int core, double a, double f);
+void   orc_exp2_errors(int core, double a, double *max_rel, double *rms_rel);
+double orc_exp2_fit(int core, int minimax);
+float  orc_exp2_core_target(int core, float f);
+
 typedef struct {
     int32_t kind;              /* ORC_ATTN_*                                   */
     int32_t B, H, Hkv, S, D;   /* Q [B, H, S, D]; K, V [B, Hkv, S, D]          */
     int32_t causal;
     int32_t order;             /* replay order of the sigmoid program (0: F32FMA_BF16) */
+    int32_t exp2_core;         /* softcap: ORC_EXP2_* for the softmax's 2^z (0: exact) */
     float cap;                 /* softcap alpha                                 */
     const orc_prog *tanh_prog; /* D4 tanh program (SOFTCAP_POLY)                */
     const orc_sig_prog *sig;   /* SIGMOID_POLY                                  */

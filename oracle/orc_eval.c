@@ -389,6 +389,32 @@ static double dot_bf16(const uint16_t *x, const uint16_t *y, int D)
     return s;
 }
 
+/* Softmax weights of one row with a software exp2: z = RN32(t RN32(cap
+ * log2 e)) from the program's FP16 t, 2^z = 2^floor(z) p(z - floor(z)) with p
+ * the core in target precision; the weights are taken relative to the row's
+ * largest floor(z) (an exact power of two, which the normalisation cancels).
+ * Returns the natural log-sum-exp. */
+static double exp2_core_weights(const actx *c, const double *t, double *w, int64_t nk)
+{
+    const float c2 = (float)((double)c->a->cap * 1.4426950408889634074);
+    double M = -INFINITY;
+    for (int64_t j = 0; j < nk; j++) {
+        const float z = orc_mul_f32((float)t[j], c2);
+        const double n = floor((double)z);
+        if (n > M) M = n;
+    }
+    double l = 0.0;
+    for (int64_t j = 0; j < nk; j++) {
+        const float z = orc_mul_f32((float)t[j], c2);
+        const double n = floor((double)z);
+        const float f = (float)((double)z - n);      /* exact */
+        w[j] = ldexp((double)orc_exp2_core_target(c->a->exp2_core, f), (int)(n - M));
+        l += w[j];
+    }
+    for (int64_t j = 0; j < nk; j++) w[j] /= l;
+    return (M + log2(l)) * 0.69314718055994530942;
+}
+
 int orc_attn_fwd_rows(const orc_attn *a, const uint16_t *q, const uint16_t *k,
                       const uint16_t *v, const int64_t *rows, int64_t n_rows,
                       double *out, double *lse, double *noise)
@@ -396,6 +422,7 @@ int orc_attn_fwd_rows(const orc_attn *a, const uint16_t *q, const uint16_t *k,
     actx c;
     const int rc = actx_init(&c, a);
     if (rc) return rc;
+    if (a->exp2_core && a->kind != ORC_ATTN_SOFTCAP_POLY) return -3;
     const int64_t S = a->S, D = a->D, G = a->H / a->Hkv;
 #pragma omp parallel
     {
@@ -412,7 +439,11 @@ int orc_attn_fwd_rows(const orc_attn *a, const uint16_t *q, const uint16_t *k,
                 score(&c, dot_bf16(q + r * D, k + kvb + j * D, (int)D), &w[j], &dummy);
                 if (w[j] > m) m = w[j];
             }
-            if (is_softcap(a)) {
+            if (a->exp2_core) {
+                for (int64_t j = 0; j < nk; j++) w[j] /= (double)a->cap;   /* t, exactly */
+                const double ls = exp2_core_weights(&c, w, w, nk);
+                if (lse) lse[ri] = ls;
+            } else if (is_softcap(a)) {
                 double l = 0.0;
                 for (int64_t j = 0; j < nk; j++) { w[j] = exp(w[j] - m); l += w[j]; }
                 for (int64_t j = 0; j < nk; j++) w[j] /= l;

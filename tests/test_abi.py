@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(pa):
     names = declared_functions()
-    assert len(names) == 21, names
+    assert len(names) == 22, names
     L = pa.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -133,6 +133,11 @@ def test_error_paths_attention(pa):
     assert a(None, K, V, O, None, 1, 2, 2, 64, 128, 50.0, 1, None) == 1
     assert a(Q, K, V, O, None, 0, 2, 2, 64, 128, 50.0, 1, None) == 0          # empty: no launch
     assert a(Q, K, V, O, LSE, 1, 2, 1, 0, 128, 50.0, 1, None) == 0
+    e = L.poly_softcap_attn_fwd_exp2
+    assert e(Q, K, V, O, None, 1, 2, 2, 64, 128, 50.0, 1, 5, None) == 4       # no such core
+    assert e(Q, K, V, O, None, 1, 2, 2, 64, 128, 50.0, 1, -1, None) == 4
+    assert e(Q, K, V, O, None, 1, 2, 2, 64, 96, 50.0, 1, 2, None) == 2
+    assert e(Q, K, V, O, None, 1, 2, 2, 0, 128, 50.0, 1, 3, None) == 0
     b = L.poly_softcap_attn_bwd
     DO, DQ, DK, DV, WS = (FAKE + i * big for i in range(5, 10))
     assert b(Q, K, V, O, DO, LSE, DQ, DK, DV, None, 1, 2, 2, 64, 128, 50.0, 1, None) == 1

@@ -180,3 +180,36 @@ def test_sigmoid_full_size_sampled(pa, orc, sp):
         kind = orc.ATTN_SIGMOID_POLY if poly else orc.ATTN_SIGMOID_EXACT
         ref, _, noise = orc.attn_fwd_rows(kind, q, k, v, rows, sig=sp)
         check(o[rows], ref, noise, f"sigmoid full poly={poly}")
+
+
+@pytest.mark.parametrize("core", ["d1", "pwl2", "d2", "d3"])
+@pytest.mark.parametrize("S,causal", [(200, True), (384, False)])
+def test_softcap_exp2_cores(pa, orc, tp, core, S, causal):
+    """The softmax's exponentials by a software exp2 core: the oracle forms
+    the same weights 2^floor(z) p(z - floor(z)) with the core in target
+    precision, so the comparison keeps the forward's tolerance."""
+    cid = pa.EXP2_CORES[core]
+    q, k, v = draw(1, 4, 2, S, 81 + cid)
+    note(f"softcap exp2 core={core} S={S} causal={causal}")
+    o, lse = pa.poly_softcap_attn_fwd_exp2(to_dev(q, BF), to_dev(k, BF), to_dev(v, BF), 50.0,
+                                           causal, core=core, with_lse=True)
+    o, lse = to_bits(o).reshape(-1, 128), lse.cpu().numpy().ravel()
+    rows = np.arange(4 * S)
+    ref, ref_lse, noise = orc.attn_fwd_rows(orc.ATTN_SOFTCAP_POLY, q, k, v, rows, cap=50.0,
+                                            causal=causal, tanh_prog=tp, exp2_core=cid)
+    check(o, ref, noise, f"exp2 {core} S={S} causal={causal}")
+    check_lse(lse, ref_lse, f"exp2 {core} S={S} causal={causal}")
+
+
+def test_softcap_exp2_cores_full_size_sampled(pa, orc, tp):
+    B, H, S = 1, 16, 8192
+    note("softcap exp2 full size draw")
+    qt, kt, vt = si.t_attn_inputs(B, H, S)
+    q, k, v = to_bits(qt), to_bits(kt), to_bits(vt)
+    rows = sample_rows(1, 1, B * H * S, 40, 82)
+    for core in ("d1", "pwl2", "d2", "d3"):
+        note(f"softcap exp2 full size core={core}")
+        o = to_bits(pa.poly_softcap_attn_fwd_exp2(qt, kt, vt, 50.0, True, core=core)).reshape(-1, 128)
+        ref, _, noise = orc.attn_fwd_rows(orc.ATTN_SOFTCAP_POLY, q, k, v, rows, tanh_prog=tp,
+                                          exp2_core=pa.EXP2_CORES[core])
+        check(o[rows], ref, noise, f"exp2 full {core}")
