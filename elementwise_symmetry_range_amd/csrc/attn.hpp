@@ -246,6 +246,21 @@ __device__ __forceinline__ void exp2_core_pair(float z0, float z1, float m, floa
     p1 = __builtin_amdgcn_ldexpf(c1, (int)(n1 - m));
 }
 
+// fma(t, b, c) with t the low / high FP16 half of a packed word, converted
+// exactly (v_fma_mix_f32: one rounding, as fmaf((float)t, b, c))
+__device__ __forceinline__ float fma_mix_lo(uint32_t w, float b, float c)
+{
+    float r;
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(w), "v"(b), "v"(c));
+    return r;
+}
+__device__ __forceinline__ float fma_mix_hi(uint32_t w, float b, float c)
+{
+    float r;
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(w), "v"(b), "v"(c));
+    return r;
+}
+
 // accurate sigmoid of u (the comparator)
 __device__ __forceinline__ float sigmoid_acc(float u)
 {
@@ -335,6 +350,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int lim = a.causal ? (my_q < S - 1 ? my_q : S - 1) : S - 1;   // last visible key
         float tmax = -INFINITY;
         bf16x8 pf[4];
+        uint32_t tw[2][8];   // softcap program: packed FP16 t of the 32 scores
         auto transform = [&](auto masked) {
             constexpr bool MASKED = decltype(masked)::value;
             if constexpr (MODE == AM_SOFTCAP_POLY) {
@@ -352,8 +368,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                             w = sel(mlo | mhi, 0xFC00FC00u, w);
                         }
                         mx = bc<uint32_t>(__builtin_elementwise_max(bc<h2>(mx), bc<h2>(w)));
-                        s[kb][e] = f16_lo(w);
-                        s[kb][e + 1] = f16_hi(w);
+                        tw[kb][e >> 1] = w;
                     }
                 }
                 tmax = fmaxf(f16_lo(mx), f16_hi(mx));
@@ -431,7 +446,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
                 for (int jj = 0; jj < 2; ++jj) {
                     bf16x8 frag;
-                    if constexpr (EXP == 0) {
+                    if constexpr (MODE == AM_SOFTCAP_NATIVE) {
 #pragma unroll
                         for (int e = 0; e < 8; ++e) {
                             const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][jj * 8 + e], a.c2, -m));
@@ -439,11 +454,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                             frag[e] = (__bf16)p;
                         }
                     } else {
+                        // the FP16 t feed the FMA directly (no conversions)
+                        const float nm = -m;
 #pragma unroll
                         for (int e = 0; e < 8; e += 2) {
+                            const uint32_t w = tw[kb][(jj * 8 + e) >> 1];
                             float p0, p1;
-                            exp2_core_pair<EXP>(s[kb][jj * 8 + e] * a.c2, s[kb][jj * 8 + e + 1] * a.c2, m,
-                                                p0, p1);
+                            if constexpr (EXP == 0) {
+                                p0 = __builtin_amdgcn_exp2f(fma_mix_lo(w, a.c2, nm));
+                                p1 = __builtin_amdgcn_exp2f(fma_mix_hi(w, a.c2, nm));
+                            } else {
+                                exp2_core_pair<EXP>(fma_mix_lo(w, a.c2, -0.0f), fma_mix_hi(w, a.c2, -0.0f), m,
+                                                    p0, p1);
+                            }
                             l += p0;
                             l += p1;
                             frag[e] = (__bf16)p0;

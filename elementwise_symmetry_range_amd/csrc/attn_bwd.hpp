@@ -70,10 +70,10 @@ __device__ __forceinline__ void bwd_pair(const AttnBwdArgs &a, float s0, float s
         uint32_t aw;
         const uint32_t tw = softcap_poly_pair(s0, s1, a.scale, a.tanh16, aw);
         const uint32_t dw = bc<uint32_t>(horner_f16<3, false>(bc<h2>(min_u16x2(aw, a.dtanh16.lc)), a.dtanh16));
-        p0 = __builtin_amdgcn_exp2f(fmaf(f16_lo(tw), a.c2, nl0));
-        p1 = __builtin_amdgcn_exp2f(fmaf(f16_hi(tw), a.c2, nl1));
-        ds0 = p0 * (dp0 - dl0) * f16_lo(dw);
-        ds1 = p1 * (dp1 - dl1) * f16_hi(dw);
+        p0 = __builtin_amdgcn_exp2f(fma_mix_lo(tw, a.c2, nl0));
+        p1 = __builtin_amdgcn_exp2f(fma_mix_hi(tw, a.c2, nl1));
+        ds0 = fma_mix_lo(dw, p0 * (dp0 - dl0), -0.0f);
+        ds1 = fma_mix_hi(dw, p1 * (dp1 - dl1), -0.0f);
     } else if constexpr (MODE == AM_SOFTCAP_NATIVE) {
         const float t0 = tanhf(s0 * a.scale), t1 = tanhf(s1 * a.scale);
         p0 = __builtin_amdgcn_exp2f(fmaf(t0, a.c2, nl0));

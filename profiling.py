@@ -5,6 +5,10 @@ under profiles/ and the traffic table bench.py reports.
         --fetch DIR/pmc_counter_collection.csv --write DIR/pmc_counter_collection.csv \
         --command "<the exact rocprofv3 command>"
 
+and the kernel table of `bench.py --components-only` (SwiGLU and attention):
+
+    python profiling.py --components DIR/comp_kernel_stats.csv --command "<command>"
+
 Traffic calibration: the FETCH_SIZE / WRITE_SIZE derived counters are scaled
 by what they read for the device-to-device hipMemcpy of x (536,870,912 bytes
 read and written) issued at the end of the profiled run: factor = true bytes /
@@ -53,16 +57,68 @@ def per_dispatch(path):
     return {k: sum(v) / len(v) for k, v in agg.items()}, last_copy
 
 
+# attention kernels: template arguments -> (what, causal scores per launch,
+# MFMA products per score of 2 D flop)
+ATTN_MODES = {"0": "softcap poly", "1": "softcap comparator", "2": "sigmoid poly",
+              "3": "sigmoid comparator"}
+EXP_CORES = {"1": "D1", "2": "PWL2 FP16", "3": "D2", "4": "D3"}
+SCORES = {"softcap": 16 * 8192 * 8193 // 2, "sigmoid": 32 * 4096 * 4097 // 2}
+
+
+def components(path, command, out):
+    lines = ["# SwiGLU and attention components", "",
+             "Kernel trace of `bench.py --components-only` (alternating poly / comparator "
+             "rounds; softcap attention 1 x 16 x 8192 x 128 causal, sigmoid attention 1 x 32 "
+             "(8 key/value heads) x 4096 x 128 causal, SwiGLU dense 8192 x 14336 and routed "
+             "131,072 x 1408 rows averaged together):", "", "```", command, "```", "",
+             "| kernel | what | calls | mean us | MFMA TFLOP/s | % of 2.5 PF |",
+             "|---|---|---|---|---|---|"]
+    import re
+    for r in sorted(csv.DictReader(open(path)), key=lambda r: r["Name"]):
+        name = r["Name"]
+        avg = float(r["AverageNs"])
+        what, tfl = "", ""
+        m = re.search(r"k_attn_(fwd|bwd_dq|bwd_dkdv|bwd_reduce)<?(\d)?(?:, ?(\w+))?>?", name)
+        if m:
+            kind, mode, extra = m.group(1), m.group(2), m.group(3)
+            what = ATTN_MODES.get(mode, "") if mode else "sum of dK/dV partials"
+            if kind == "fwd" and extra in EXP_CORES:
+                what += f", exp2 core {EXP_CORES[extra]}"
+            if kind != "bwd_reduce" and mode:
+                sc = SCORES["softcap" if mode in "01" else "sigmoid"]
+                prods = {"fwd": 2, "bwd_dq": 3, "bwd_dkdv": 4}[kind]
+                t = prods * 2 * 128 * sc / (avg * 1e-9) / 1e12
+                tfl = f"{t:.0f} | {100 * t / 2500:.1f}"
+            what = f"{kind} {what}"
+        elif "swiglu" in name:
+            what = "SwiGLU " + ("poly" if "Poly" in name else "comparator")
+        else:
+            continue
+        short_name = name.split("(")[0].replace("void ", "")
+        lines.append(f"| `{short_name}` | {what} | {r['Calls']} | {avg / 1e3:.1f} | "
+                     f"{tfl if tfl else '- | -'} |")
+    lines += ["", "MFMA FLOP per launch counts the products each kernel performs (forward: "
+              "S and PV; dq kernel: S, dP, dQ; dK/dV kernel: S, dP, dV, dK), 2 x 128 flop "
+              "per causal score each."]
+    with open(os.path.join(out, "attention_components.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("--stats", required=True)
-    ap.add_argument("--fetch", required=True)
-    ap.add_argument("--write", required=True)
+    ap.add_argument("--components", default="")
+    ap.add_argument("--stats")
+    ap.add_argument("--fetch")
+    ap.add_argument("--write")
     ap.add_argument("--command", required=True)
     ap.add_argument("--fetch-command", default="")
     ap.add_argument("--write-command", default="")
     ap.add_argument("--out", default=os.path.join(ROOT, "profiles"))
     a = ap.parse_args()
+    if a.components:
+        components(a.components, a.command, a.out)
+        return
     import sys
     sys.path.insert(0, ROOT)
     from elementwise_symmetry_range_amd._build import source_digest
