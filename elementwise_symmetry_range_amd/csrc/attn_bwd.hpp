@@ -96,7 +96,7 @@ __device__ __forceinline__ void bwd_pair(const AttnBwdArgs &a, float s0, float s
 }
 
 template <int MODE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void k_attn_bwd_dq(AttnBwdArgs a)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_bwd_dq(AttnBwdArgs a)
 {
     constexpr bool SOFTCAP = am_softcap(MODE);
     __shared__ __attribute__((aligned(16))) uint16_t Ks[2][AT_TILE];
@@ -169,28 +169,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
         const uint16_t *Kb = Ks[buf];
         const uint16_t *Vb = Vs[buf];
 
-        f32x16 s[2], dp[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            s[kb] = f32x16{};
-            dp[kb] = f32x16{};
-#pragma unroll
-            for (int ks = 0; ks < 8; ++ks) {
-                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row8(Kb, kb * 32 + col, ks * 2 + h),
-                                                                qf[ks], s[kb], 0, 0, 0);
-                dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row8(Vb, kb * 32 + col, ks * 2 + h),
-                                                                 df[ks], dp[kb], 0, 0, 0);
-            }
-        }
-
-        // dS^T, as BF16 B operands in the permuted key order
+        // one 32-key block at a time (keeps two accumulators live, not four)
         const bool need_mask = (a.causal && key0 + AT_BN - 1 > q0) || key0 + AT_BN > S;
         const int lim = a.causal ? (my_q < S - 1 ? my_q : S - 1) : S - 1;
-        bf16x8 dsf[4];
-        auto transform = [&](auto masked) {
-            constexpr bool MASKED = decltype(masked)::value;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < 2; ++kb) {
+            f32x16 s = {}, dp = {};
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row8(Kb, kb * 32 + col, ks * 2 + h), qf[ks],
+                                                            s, 0, 0, 0);
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row8(Vb, kb * 32 + col, ks * 2 + h), df[ks],
+                                                             dp, 0, 0, 0);
+            }
+            // dS^T of the block, as BF16 B operands in the permuted key order
+            bf16x8 dsf[2];
+            auto transform = [&](auto masked) {
+                constexpr bool MASKED = decltype(masked)::value;
 #pragma unroll
                 for (int jj = 0; jj < 2; ++jj) {
                     u32x4 fw;
@@ -198,8 +193,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
                     for (int e2 = 0; e2 < 4; ++e2) {
                         const int e = jj * 8 + e2 * 2;
                         float p0, p1, d0, d1;
-                        bwd_pair<MODE>(a, s[kb][e], s[kb][e + 1], dp[kb][e], dp[kb][e + 1], nl, nl, dl,
-                                       dl, p0, p1, d0, d1);
+                        bwd_pair<MODE>(a, s[e], s[e + 1], dp[e], dp[e + 1], nl, nl, dl, dl, p0, p1, d0, d1);
                         uint32_t w = pack_bf(d0, d1);
                         if constexpr (MASKED) {
                             const int k0 = key0 + kb * 32 + (e >> 2) * 8 + h * 4 + (e & 3);
@@ -209,20 +203,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
                         }
                         fw[e2] = w;
                     }
-                    dsf[kb * 2 + jj] = bc<bf16x8>(fw);
+                    dsf[jj] = bc<bf16x8>(fw);
                 }
-            }
-        };
-        if (need_mask) transform(std::true_type{});
-        else transform(std::false_type{});
+            };
+            if (need_mask) transform(std::true_type{});
+            else transform(std::false_type{});
 
-        // dQ^T += K^T dS^T
+            // dQ^T += K^T dS^T over this block's two contraction steps
 #pragma unroll
-        for (int db = 0; db < 4; ++db) {
+            for (int db = 0; db < 4; ++db) {
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-                dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_tr_a(Kb, ks, db, g16, i16), dsf[ks],
-                                                                 dq[db], 0, 0, 0);
+                for (int jj = 0; jj < 2; ++jj)
+                    dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_tr_a(Kb, kb * 2 + jj, db, g16, i16),
+                                                                     dsf[jj], dq[db], 0, 0, 0);
+            }
         }
     };
     for (int kt = 0; kt < nkt; kt += 2) {
