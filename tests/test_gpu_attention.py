@@ -213,3 +213,13 @@ def test_softcap_exp2_cores_full_size_sampled(pa, orc, tp):
         ref, _, noise = orc.attn_fwd_rows(orc.ATTN_SOFTCAP_POLY, q, k, v, rows, tanh_prog=tp,
                                           exp2_core=pa.EXP2_CORES[core])
         check(o[rows], ref, noise, f"exp2 full {core}")
+
+
+@pytest.mark.parametrize("S", [1, 65, 129])
+def test_edge_lengths_and_wide_groups(pa, orc, tp, sp, S):
+    """Sequences shorter than, or one past, a tile; eight query heads on one
+    key/value head; causal and not."""
+    q, k, v = draw(1, 8, 1, S, 90 + S)
+    for causal in (True, False):
+        softcap_case(pa, orc, tp, q, k, v, causal, True, label="edge")
+        sigmoid_case(pa, orc, sp, q, k, v, causal, False, label="edge")

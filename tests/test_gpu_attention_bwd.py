@@ -170,3 +170,12 @@ def test_sigmoid_full_size_sampled(pa, orc, sp):
         dq, dk, dv = to_bits(dq), to_bits(dk), to_bits(dv)
         compare(orc, kind, q, k, v, None, do, None, dq, dk, dv, qrows, krows, True,
                 f"sigmoid bwd full poly={poly}", sig=sp)
+
+
+@pytest.mark.parametrize("S", [1, 65, 129])
+def test_edge_lengths_and_wide_groups(pa, orc, tp, sp, S):
+    """Sequences shorter than, or one past, a tile; eight query heads on one
+    key/value head (the summing pass over a group of eight)."""
+    for causal in (True, False):
+        softcap_case(pa, orc, tp, 1, 8, 1, S, causal, True, 95 + S)
+        sigmoid_case(pa, orc, sp, 1, 8, 1, S, causal, False, 96 + S)
