@@ -91,6 +91,7 @@ struct AttnArgs {
     float scale;       // softcap: RN_f32(1 / (cap sqrt D)); sigmoid: RN_f32(1 / sqrt D)
     float c2;          // softcap: RN_f32(cap * log2(e))
     float logn;        // sigmoid comparator: RN_f32(ln S)
+    float mref;        // softcap, fixed reference (see SREF)
     CoefF16 tanh16;    // D4 tanh program, FP16 coefficients
     SigCoef sig;
 };
@@ -270,7 +271,11 @@ __device__ __forceinline__ float sigmoid_acc(float u)
 
 // EXP: 0 = hardware exp2 (v_exp_f32), 1-4 = the software cores above
 // (softcap only).
-template <int MODE, int EXP = 0>
+// SREF (softcap with cap log2 e <= 80): the logits are bounded, |z| <= cap
+// log2 e, so a fixed reference m = ceil(cap log2 e - 40) keeps every P in
+// [2^-120, 2^40] -- normal FP32 and BF16, row sums far from overflow -- and
+// the running max, its reductions and the rescales are not needed at all.
+template <int MODE, int EXP = 0, bool SREF = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_fwd(AttnArgs a)
 {
     constexpr bool SOFTCAP = am_softcap(MODE);
@@ -304,7 +309,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     f32x16 o[4];
 #pragma unroll
     for (int db = 0; db < 4; ++db) o[db] = f32x16{};
-    float m = -INFINITY;   // reference max of the log2-domain score (softcap)
+    float m = SREF ? a.mref : -INFINITY;   // reference of the log2-domain score (softcap)
     float l = 0.0f;        // this lane's partial row sum (softcap)
 
     const int kend = a.causal ? (qt * AT_BM + AT_BM < S ? qt * AT_BM + AT_BM : S) : S;
@@ -419,7 +424,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         if (need_mask) transform(std::true_type{});
         else transform(std::false_type{});
 
-        if constexpr (SOFTCAP) {
+        if constexpr (SOFTCAP && !SREF) {
             tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
             const float zmax = tmax * a.c2;
 
@@ -439,7 +444,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 for (int db = 0; db < 4; ++db) o[db] *= corr;
                 m = m_new;
             }
-
+        }
+        if constexpr (SOFTCAP) {
             // ---- P = exp2(t c2 - m), row sums, BF16 B operands ----------------
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {

@@ -140,6 +140,22 @@ inline pa_status attn_fwd(int mode, const void *q, const void *k, const void *v,
         a.sig = sigmoid_coefs();
     }
     const dim3 grid((unsigned)(((S + AT_BM - 1) / AT_BM) * (B * H)));
+    const bool sref = softcap && a.c2 <= 80.0f;
+    if (sref) a.mref = std::ceil(a.c2 - 40.0f);
+    if (sref) {
+        switch (exp2_core) {
+        case 1: hipLaunchKernelGGL((k_attn_fwd<AM_SOFTCAP_POLY, 1, true>), grid, dim3(256), 0, stream, a); break;
+        case 2: hipLaunchKernelGGL((k_attn_fwd<AM_SOFTCAP_POLY, 2, true>), grid, dim3(256), 0, stream, a); break;
+        case 3: hipLaunchKernelGGL((k_attn_fwd<AM_SOFTCAP_POLY, 3, true>), grid, dim3(256), 0, stream, a); break;
+        case 4: hipLaunchKernelGGL((k_attn_fwd<AM_SOFTCAP_POLY, 4, true>), grid, dim3(256), 0, stream, a); break;
+        default:
+            if (mode == AM_SOFTCAP_POLY)
+                hipLaunchKernelGGL((k_attn_fwd<AM_SOFTCAP_POLY, 0, true>), grid, dim3(256), 0, stream, a);
+            else
+                hipLaunchKernelGGL((k_attn_fwd<AM_SOFTCAP_NATIVE, 0, true>), grid, dim3(256), 0, stream, a);
+        }
+        return attn_launched();
+    }
     switch (exp2_core) {
     case 1: hipLaunchKernelGGL((k_attn_fwd<AM_SOFTCAP_POLY, 1>), grid, dim3(256), 0, stream, a); return attn_launched();
     case 2: hipLaunchKernelGGL((k_attn_fwd<AM_SOFTCAP_POLY, 2>), grid, dim3(256), 0, stream, a); return attn_launched();

@@ -223,3 +223,20 @@ def test_edge_lengths_and_wide_groups(pa, orc, tp, sp, S):
     for causal in (True, False):
         softcap_case(pa, orc, tp, q, k, v, causal, True, label="edge")
         sigmoid_case(pa, orc, sp, q, k, v, causal, False, label="edge")
+
+
+@pytest.mark.parametrize("poly", [True, False])
+def test_softcap_large_cap_running_max(pa, orc, tp, poly):
+    """cap = 100 (cap log2 e > 80): the logits' range no longer fits a fixed
+    reference, so the kernel tracks the running row max (lazy rescale)."""
+    q, k, v = draw(1, 2, 1, 300, 97, sd=3.0)
+    B, H, S, D = q.shape
+    note(f"softcap fwd cap=100 poly={poly}")
+    entry = pa.poly_softcap_attn_fwd if poly else pa.native_softcap_attn_fwd
+    o, lse = entry(to_dev(q, BF), to_dev(k, BF), to_dev(v, BF), 100.0, True, with_lse=True)
+    o, lse = to_bits(o).reshape(-1, D), lse.cpu().numpy().ravel()
+    rows = np.arange(B * H * S)
+    kind = orc.ATTN_SOFTCAP_POLY if poly else orc.ATTN_SOFTCAP_EXACT
+    ref, ref_lse, noise = orc.attn_fwd_rows(kind, q, k, v, rows, cap=100.0, tanh_prog=tp)
+    check(o, ref, noise, f"cap=100 poly={poly}")
+    check_lse(lse, ref_lse, f"cap=100 poly={poly}")
