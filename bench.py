@@ -346,6 +346,24 @@ def main():
                     "poly_us": round(1e3 * tp, 2), "native_us": round(1e3 * tn, 2)}
     del xs, gs, ys
 
+    # reference rates measured on this GPU: the runtime's device-to-device
+    # copy of the same 268,435,456-element array (one read and one write
+    # stream, 1,073,741,824 bytes moved) and a large BF16 library GEMM
+    # (hipBLASLt through torch.mm), the MFMA rate a tuned library reaches
+    tcopy = time_calls(torch, lambda: y.copy_(x), 10)
+    copy_gbs = 4 * N_HBM / (tcopy * 1e-3) / 1e9
+    ga = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
+    gb = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
+    gc = torch.empty_like(ga)
+    torch.mm(ga, gb, out=gc)
+    tmm = time_calls(torch, lambda: torch.mm(ga, gb, out=gc), 10)
+    del ga, gb, gc
+    gemm_tf = 2 * 8192 ** 3 / (tmm * 1e-3) / 1e12
+    ceilings = {"runtime_d2d_copy_gbs": round(copy_gbs, 1),
+                "runtime_d2d_copy_pct_hbm": round(100 * copy_gbs / HBM_PEAK_GBS, 1),
+                "bf16_gemm_8192_tflops": round(gemm_tf, 1),
+                "bf16_gemm_8192_pct_peak": round(100 * gemm_tf / BF16_DENSE_TFLOPS, 1)}
+
     comp = None if args.no_components else components(torch, pa, si)
     cpu = None if args.no_cpu else cpu_baseline(x, g)
 
@@ -368,6 +386,7 @@ def main():
         "per_kernel_ms": {k: round(v, 5) for k, v in per.items()},
         "detail_hbm": detail,
         "detail_l2_resident_4M": l2,
+        "measured_ceilings": ceilings,
         "components": comp,
     }
     print(json.dumps(line), flush=True)
