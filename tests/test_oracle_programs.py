@@ -110,6 +110,31 @@ def test_replay_within_rounding_bound_of_real_program(orc, progs, fmt, name):
 
 
 @pytest.mark.parametrize("fmt", ["f16", "bf16"])
+def test_clamp_holds_the_chain_at_lc(orc, progs, fmt):
+    """t^ = min(|x|, Lc) (Eq. 2): every input with |x| >= Lc gives exactly the
+    output at sign(x) Lc for the clamped programs, and for SiLU / GELU the
+    chain value v = (y - x/2) / t is that of Lc (checked through the
+    derivative-free identity y(x) = x/2 + |x| v(Lc) in real arithmetic within
+    one rounding of y)."""
+    F = FMT[fmt]
+    xs = ALL[_finite(ALL, fmt)]
+    x = F["val"](xs)
+    for name in ("sigmoid_fwd_d3", "tanh_fwd_d4", "sigmoid_bwd_d4", "tanh_bwd_d4",
+                 "silu_bwd_d3", "gelu_bwd_d5"):
+        p = progs[name]
+        big = np.abs(x) >= p.Lc
+        y = orc.act_fwd(p, xs[big], F["order"])
+        enc = (lambda v: np.array([v], np.float16).view(np.uint16)[0]) if fmt == "f16" else \
+            (lambda v: torch.tensor([v]).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)[0])
+        at = orc.act_fwd(p, np.array([enc(p.Lc), enc(-p.Lc)], np.uint16), F["order"])
+        want = np.where(np.signbit(x[big]), at[1], at[0])
+        assert np.array_equal(y, want), name
+        # and just below the clamp the chain is not held
+        below = (np.abs(x) < p.Lc) & (np.abs(x) > p.Lc * 0.75)
+        assert not np.all(orc.act_fwd(p, xs[below & (x > 0)], F["order"]) == at[0]), name
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
 def test_special_values(orc, progs, fmt):
     F = FMT[fmt]
     inf, ninf = F["nan"], F["nan"] | 0x8000
