@@ -227,6 +227,63 @@ def components(torch, pa, si):
     fp(), fn()
     tp, tn = alternating(torch, fp, fn, 5, 5)
     res["sigmoid_attn_bwd"] = attn_row(tp, tn, 2.5 * flops, {"causal_scores": scores})
+    del q, k, v, dout, o, dq, dk, dv, ws
+
+    # the pages' own component geometries (their GB200 ratios are context):
+    # B2 softcap attention at B = 1, 32 query / 8 key-value heads, S = 4096
+    q, k, v = si.t_attn_inputs(1, 32, 4096, 128, Hkv=8)
+    dout = si.t_attn_grad(1, 32, 4096, 128)
+    o = torch.empty_like(q)
+    scores = 32 * 4096 * 4097 // 2
+    flops = 4 * 128 * scores
+    fp = lambda: pa.poly_softcap_attn_fwd(q, k, v, 50.0, True, out=o)  # noqa: E731
+    fn = lambda: pa.native_softcap_attn_fwd(q, k, v, 50.0, True, out=o)  # noqa: E731
+    fp(), fn()
+    tp, tn = alternating(torch, fp, fn, 5, 5)
+    res["b2_softcap_attn_fwd_32x8x4096"] = attn_row(tp, tn, flops, {"causal_scores": scores})
+    op, lp = pa.poly_softcap_attn_fwd(q, k, v, 50.0, True, with_lse=True)
+    on, ln = pa.native_softcap_attn_fwd(q, k, v, 50.0, True, with_lse=True)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = pa.attn_bwd_workspace(True, 1, 32, 8, 4096, 128, device=q.device)
+    fp = lambda: pa.poly_softcap_attn_bwd(q, k, v, op, dout, lp, 50.0, True, dq=dq, dk=dk, dv=dv,  # noqa: E731
+                                          workspace=ws)
+    fn = lambda: pa.native_softcap_attn_bwd(q, k, v, on, dout, ln, 50.0, True, dq=dq, dk=dk,  # noqa: E731
+                                            dv=dv, workspace=ws)
+    fp(), fn()
+    tp, tn = alternating(torch, fp, fn, 5, 5)
+    res["b2_softcap_attn_bwd_32x8x4096"] = attn_row(tp, tn, 2.5 * flops, {"causal_scores": scores})
+    del q, k, v, dout, o, op, on, lp, ln, dq, dk, dv, ws
+
+    # B1 one-kernel SiLU probe: 58,720,256 BF16 values, D3 forward and the
+    # direct D3 derivative from x, against the accurate comparators
+    n = 58_720_256
+    x = si.t_bf16(si.t_normal(si.SEED_X, n, 2.0))
+    gr = si.t_bf16(si.t_normal(si.SEED_G, n, 1.0))
+    y = torch.empty_like(x)
+    for name, fp, fn, by in (
+            ("b1_silu_bf16_fwd", lambda: pa.poly_act_fwd(x, "silu", out=y),
+             lambda: pa.native_act_fwd(x, "silu", out=y), 4),
+            ("b1_silu_bf16_bwd", lambda: pa.poly_act_bwd(x, gr, "silu", out=y),
+             lambda: pa.native_act_bwd(x, gr, "silu", "native", out=y), 6)):
+        fp(), fn()
+        tp, tn = alternating(torch, fp, fn, 20, 5)
+        res[name] = {"elements": n, "poly_ms": round(tp, 4), "native_ms": round(tn, 4),
+                     "speedup": round(tn / tp, 3), "pct_hbm": round(100 * n * by / tp / 1e6 / HBM_PEAK_GBS, 1)}
+    del x, gr, y
+
+    # B4 one-kernel routed-expert SwiGLU: 24,576 rows x 1,280
+    g, u, d = si.t_swiglu_inputs(24576, 1280)
+    h, dg, du = torch.empty_like(g), torch.empty_like(g), torch.empty_like(g)
+    n = g.numel()
+    for name, fp, fn, by in (
+            ("b4_swiglu_24576x1280_fwd", lambda: pa.poly_swiglu_fwd(g, u, out=h),
+             lambda: pa.native_swiglu_fwd(g, u, out=h), 6),
+            ("b4_swiglu_24576x1280_bwd", lambda: pa.poly_swiglu_bwd(g, u, d, out=(dg, du)),
+             lambda: pa.native_swiglu_bwd(g, u, d, out=(dg, du)), 10)):
+        fp(), fn()
+        tp, tn = alternating(torch, fp, fn, 20, 5)
+        res[name] = {"elements": n, "poly_ms": round(tp, 4), "native_ms": round(tn, 4),
+                     "speedup": round(tn / tp, 3), "pct_hbm": round(100 * n * by / tp / 1e6 / HBM_PEAK_GBS, 1)}
     return res
 
 
