@@ -11,6 +11,9 @@ value   = elements processed per second over the timed steps (Gelem/s);
 roofline = the dominant kernel of the step, algorithmic bytes per launch
           (4 B/elem forward, 6 B/elem backward) over its mean launch time,
           measured with HIP events on the launch stream, against 8 TB/s;
+          measured_ceilings also gives the rate of the same streaming kernels
+          with no arithmetic (pa_stream_copy) and the dominant kernel's time
+          relative to that copy;
 cpu_baseline = the CPU oracle replaying the same programs on a bounded
           sample of the same arrays, on this host's cores.
 Also reported: each program's Gelem/s and share of HBM peak, the matched
@@ -416,7 +419,22 @@ def main():
     tmm = time_calls(torch, lambda: torch.mm(ga, gb, out=gc), 10)
     del ga, gb, gc
     gemm_tf = 2 * 8192 ** 3 / (tmm * 1e-3) / 1e12
-    ceilings = {"runtime_d2d_copy_gbs": round(copy_gbs, 1),
+    # the library's own streaming kernels with no arithmetic (same launch
+    # shape): one read + one write stream, two reads + one write; and the
+    # dominant kernel against the copy of its own stream shape, alternating
+    ts1 = time_calls(torch, lambda: pa.stream_copy(x, out=y), 10)
+    ts2 = time_calls(torch, lambda: pa.stream_copy(x, g, out=y), 10)
+    sc1_gbs = 4 * N_HBM / (ts1 * 1e-3) / 1e9
+    sc2_gbs = 6 * N_HBM / (ts2 * 1e-3) / 1e9
+    dom_copy = ((lambda: pa.stream_copy(x, g, out=y)) if dom[1] == 6
+                else (lambda: pa.stream_copy(x, out=y)))
+    tdom, tref = alternating(torch, dom[2], dom_copy, 10, args.rounds)
+    ceilings = {"stream_copy_1r1w_gbs": round(sc1_gbs, 1),
+                "stream_copy_1r1w_pct_hbm": round(100 * sc1_gbs / HBM_PEAK_GBS, 1),
+                "stream_copy_2r1w_gbs": round(sc2_gbs, 1),
+                "stream_copy_2r1w_pct_hbm": round(100 * sc2_gbs / HBM_PEAK_GBS, 1),
+                "dominant_kernel_vs_stream_copy": round(tref / tdom, 4),
+                "runtime_d2d_copy_gbs": round(copy_gbs, 1),
                 "runtime_d2d_copy_pct_hbm": round(100 * copy_gbs / HBM_PEAK_GBS, 1),
                 "bf16_gemm_8192_tflops": round(gemm_tf, 1),
                 "bf16_gemm_8192_pct_peak": round(100 * gemm_tf / BF16_DENSE_TFLOPS, 1)}

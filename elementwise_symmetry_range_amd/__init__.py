@@ -28,7 +28,7 @@ __all__ = [
     "poly_softcap_attn_fwd_exp2", "poly_softcap_attn_bwd", "native_softcap_attn_bwd",
     "poly_sigmoid_attn_fwd",
     "native_sigmoid_attn_fwd", "poly_sigmoid_attn_bwd", "native_sigmoid_attn_bwd",
-    "sigmoid_attn_program", "attn_bwd_workspace", "FUNCS",
+    "sigmoid_attn_program", "attn_bwd_workspace", "stream_copy", "FUNCS",
 ]
 
 FUNCS = {"sigmoid": 1, "tanh": 2, "silu": 3, "gelu": 4}
@@ -88,6 +88,7 @@ def lib() -> C.CDLL:
             "native_sigmoid_attn_bwd": [p] * 8 + [i32] * 6 + [p],
             "poly_sigmoid_attn_program": [C.POINTER(PaSigmoidAttnProgram)],
             "poly_program_info": [i32, i32, i32, C.POINTER(PaProgram)],
+            "pa_stream_copy": [p, p, p, i64, p],
         }
         for name, args in sigs.items():
             fn = getattr(L, name)
@@ -163,6 +164,20 @@ def native_act_fwd(x: torch.Tensor, func: str, out=None) -> torch.Tensor:
     y = _out(out, x)
     _check(lib().native_act_fwd(FUNCS[func], _DTYPES[x.dtype], x.data_ptr(), y.data_ptr(),
                                 x.numel(), _stream(x)))
+    return y
+
+
+def stream_copy(a: torch.Tensor, b: torch.Tensor | None = None, out=None) -> torch.Tensor:
+    """The streaming kernels with no arithmetic: out = a, or out = a XOR b
+    bitwise when b is given (the elementwise kernels' HBM reference rate)."""
+    _dev(a, "a")
+    if b is not None:
+        _dev(b, "b")
+        if b.dtype != a.dtype or b.numel() != a.numel():
+            raise ValueError("b must match a")
+    y = _out(out, a)
+    _check(lib().pa_stream_copy(a.data_ptr(), None if b is None else b.data_ptr(), y.data_ptr(),
+                                a.numel(), _stream(a)))
     return y
 
 

@@ -275,6 +275,16 @@ __device__ __forceinline__ float sigmoid_acc(float u)
 // log2 e, so a fixed reference m = ceil(cap log2 e - 40) keeps every P in
 // [2^-120, 2^40] -- normal FP32 and BF16, row sums far from overflow -- and
 // the running max, its reductions and the rescales are not needed at all.
+//
+// Software pipeline.  Each wave walks its keys in units of 32 (one 32x32
+// score block).  Stage j issues the QK^T MFMAs of unit j + 1 and the PV MFMAs
+// of unit j - 1 and, independent of both, the VALU score transform of unit j,
+// so the matrix cores and the vector ALU work on different units at the same
+// time instead of taking turns.  K tiles therefore run one LDS tile ahead of
+// V tiles: period p (stages 2p - 1 and 2p) reads K tile p and V tile p - 1
+// from the two halves of each buffer while K tile p + 1 and V tile p stream
+// in.  The order of every accumulation (over keys for S, O and the row sum)
+// is the unpipelined one.
 template <int MODE, int EXP = 0, bool SREF = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_fwd(AttnArgs a)
 {
@@ -312,192 +322,208 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     float m = SREF ? a.mref : -INFINITY;   // reference of the log2-domain score (softcap)
     float l = 0.0f;        // this lane's partial row sum (softcap)
 
+    // keys of the workgroup and of this wave (units of 32 keys); the last
+    // unit of a wave is the only one that can need a mask (the causal
+    // diagonal, or the ragged end of S)
     const int kend = a.causal ? (qt * AT_BM + AT_BM < S ? qt * AT_BM + AT_BM : S) : S;
     const int nkt = (kend + AT_BN - 1) / AT_BN;
+    const int wend = q0 >= S ? 0 : (a.causal ? (q0 + 32 < S ? q0 + 32 : S) : S);
+    const int nu = (wend + 31) / 32;
+    const bool last_masked = nu > 0 && (a.causal || wend < nu * 32);
+    const int lim = a.causal ? (my_q < S - 1 ? my_q : S - 1) : S - 1;   // last visible key
 
-    load_rows64(K, Ks[0], 0, S, wave, lane);
-    load_rows64(V, Vs[0], 0, S, wave, lane);
-    // One tile; BUF is the LDS buffer holding it (a constant: the loop below
-    // is unrolled by two so that buffer bases become immediate offsets).
-    auto tile = [&](int kt, auto bufc) {
-        constexpr int buf = decltype(bufc)::value;
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's share of tile kt landed
-        __syncthreads();   // all of tile kt landed; nobody reads buffer buf ^ 1 any more
-        if (kt + 1 < nkt) {
-            load_rows64(K, Ks[buf ^ 1], (kt + 1) * AT_BN, S, wave, lane);
-            load_rows64(V, Vs[buf ^ 1], (kt + 1) * AT_BN, S, wave, lane);
-        }
+    f32x16 sc[2];          // raw scores of an even / odd unit
+    bf16x8 pf[2][2];       // P of an even / odd unit as two B-operand fragments
 
-        const int key0 = kt * AT_BN;
-        if (a.causal && key0 > q0 + 31) return;   // tile entirely above this wave's rows
-        if (q0 >= S) return;
-        const uint16_t *Kb = Ks[buf];
-        const uint16_t *Vb = Vs[buf];
-
-        // ---- S^T for two 32-key blocks ----
-        f32x16 s[2];
+    // ---- the three parts of a stage ------------------------------------------
+    // S^T of unit u from rows 32 * (u & 1) of a K tile
+    auto qk = [&](f32x16 &s, const uint16_t *Kb, int half) __attribute__((always_inline)) {
+        s = f32x16{};
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            s[kb] = f32x16{};
-#pragma unroll
-            for (int ks = 0; ks < 8; ++ks)
-                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row8(Kb, kb * 32 + col, ks * 2 + h),
-                                                                qf[ks], s[kb], 0, 0, 0);
-        }
-
-        // ---- score transform ---------------------------------------------
-        // s[kb][j*4 + i] is the score of key key0 + kb*32 + j*8 + h*4 + i.
-        // Masked keys (beyond the query, or beyond S) get t = -inf (softcap)
-        // or P = 0 (sigmoid).  Tiles that need no mask (all but the diagonal
-        // and the ragged end) take a branch-free pass without the key
-        // arithmetic.
-        const bool need_mask = (a.causal && key0 + AT_BN - 1 > q0) || key0 + AT_BN > S;
-        const int lim = a.causal ? (my_q < S - 1 ? my_q : S - 1) : S - 1;   // last visible key
-        float tmax = -INFINITY;
-        bf16x8 pf[4];
-        uint32_t tw[2][8];   // softcap program: packed FP16 t of the 32 scores
-        auto transform = [&](auto masked) {
-            constexpr bool MASKED = decltype(masked)::value;
-            if constexpr (MODE == AM_SOFTCAP_POLY) {
-                uint32_t mx = 0xFC00FC00u;   // packed FP16 -inf
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-                    for (int e = 0; e < 16; e += 2) {
-                        uint32_t aw;
-                        uint32_t w = softcap_poly_pair(s[kb][e], s[kb][e + 1], a.scale, a.tanh16, aw);
-                        if constexpr (MASKED) {
-                            const int k0 = key0 + kb * 32 + (e >> 2) * 8 + h * 4 + (e & 3);
-                            const uint32_t mlo = k0 > lim ? 0x0000FFFFu : 0u;
-                            const uint32_t mhi = k0 + 1 > lim ? 0xFFFF0000u : 0u;
-                            w = sel(mlo | mhi, 0xFC00FC00u, w);
-                        }
-                        mx = bc<uint32_t>(__builtin_elementwise_max(bc<h2>(mx), bc<h2>(w)));
-                        tw[kb][e >> 1] = w;
-                    }
-                }
-                tmax = fmaxf(f16_lo(mx), f16_hi(mx));
-            } else if constexpr (MODE == AM_SOFTCAP_NATIVE) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        float t = tanhf(s[kb][e] * a.scale);
-                        if constexpr (MASKED) {
-                            const int k0 = key0 + kb * 32 + (e >> 2) * 8 + h * 4 + (e & 3);
-                            t = k0 > lim ? -INFINITY : t;
-                        }
-                        s[kb][e] = t;
-                        tmax = fmaxf(tmax, t);
-                    }
-                }
-            } else {
-                // sigmoid: P directly, as BF16 B-operand fragments
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-                    for (int jj = 0; jj < 2; ++jj) {
-                        u32x4 fw;
-#pragma unroll
-                        for (int e2 = 0; e2 < 4; ++e2) {
-                            const int e = jj * 8 + e2 * 2;
-                            uint32_t w;
-                            if constexpr (MODE == AM_SIGMOID_POLY) {
-                                w = sigmoid_poly_pair<false>(s[kb][e], s[kb][e + 1], a.scale, a.sig, nullptr);
-                            } else {
-                                w = pack_bf(sigmoid_acc(fmaf(s[kb][e], a.scale, -a.logn)),
-                                            sigmoid_acc(fmaf(s[kb][e + 1], a.scale, -a.logn)));
-                            }
-                            if constexpr (MASKED) {
-                                const int k0 = key0 + kb * 32 + (e >> 2) * 8 + h * 4 + (e & 3);
-                                const uint32_t mlo = k0 > lim ? 0x0000FFFFu : 0u;
-                                const uint32_t mhi = k0 + 1 > lim ? 0xFFFF0000u : 0u;
-                                w &= ~(mlo | mhi);
-                            }
-                            fw[e2] = w;
-                        }
-                        pf[kb * 2 + jj] = bc<bf16x8>(fw);
-                    }
-                }
-            }
-        };
-        if (need_mask) transform(std::true_type{});
-        else transform(std::false_type{});
-
-        if constexpr (SOFTCAP && !SREF) {
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-            const float zmax = tmax * a.c2;
-
-            // lazy rescale: move the reference only when the row max outgrows it
-            const bool grow = zmax > m + AT_RESCALE;
-            if (__builtin_amdgcn_ballot_w64(grow)) {
-                float m_new, corr;
-                if constexpr (EXP == 0) {
-                    m_new = grow ? zmax : m;
-                    corr = __builtin_amdgcn_exp2f(m - m_new);
-                } else {   // integer reference; the rescale is an exact power of two
-                    m_new = grow ? ceilf(zmax) : m;
-                    corr = m == -INFINITY ? 0.0f : __builtin_amdgcn_ldexpf(1.0f, (int)(m - m_new));
-                }
-                l *= corr;
-#pragma unroll
-                for (int db = 0; db < 4; ++db) o[db] *= corr;
-                m = m_new;
-            }
-        }
-        if constexpr (SOFTCAP) {
-            // ---- P = exp2(t c2 - m), row sums, BF16 B operands ----------------
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-                for (int jj = 0; jj < 2; ++jj) {
-                    bf16x8 frag;
-                    if constexpr (MODE == AM_SOFTCAP_NATIVE) {
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][jj * 8 + e], a.c2, -m));
-                            l += p;
-                            frag[e] = (__bf16)p;
-                        }
-                    } else {
-                        // the FP16 t feed the FMA directly (no conversions)
-                        const float nm = -m;
-#pragma unroll
-                        for (int e = 0; e < 8; e += 2) {
-                            const uint32_t w = tw[kb][(jj * 8 + e) >> 1];
-                            float p0, p1;
-                            if constexpr (EXP == 0) {
-                                p0 = __builtin_amdgcn_exp2f(fma_mix_lo(w, a.c2, nm));
-                                p1 = __builtin_amdgcn_exp2f(fma_mix_hi(w, a.c2, nm));
-                            } else {
-                                exp2_core_pair<EXP>(fma_mix_lo(w, a.c2, -0.0f), fma_mix_hi(w, a.c2, -0.0f), m,
-                                                    p0, p1);
-                            }
-                            l += p0;
-                            l += p1;
-                            frag[e] = (__bf16)p0;
-                            frag[e + 1] = (__bf16)p1;
-                        }
-                    }
-                    pf[kb * 2 + jj] = frag;
-                }
-            }
-        }
-
-        // ---- O^T += V^T P^T ------------------------------------------------
-        // contraction index h*8 + e of step ks maps to key
-        // kb*32 + jj*16 + (e/4)*8 + h*4 + (e%4)   (ks = 2 kb + jj)
+        for (int ks = 0; ks < 8; ++ks)
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row8(Kb, half * 32 + col, ks * 2 + h),
+                                                        qf[ks], s, 0, 0, 0);
+    };
+    // O^T += V^T P^T for a unit from rows 32 * half of a V tile; contraction
+    // index h*8 + e of step kk maps to key kk*16 + (e/4)*8 + h*4 + (e%4)
+    auto pv = [&](const bf16x8 (&p)[2], const uint16_t *Vb, int half) __attribute__((always_inline)) {
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_tr_a(Vb, ks, db, g16, i16), pf[ks],
-                                                                o[db], 0, 0, 0);
+            for (int kk = 0; kk < 2; ++kk)
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_tr_a(Vb, half * 2 + kk, db, g16, i16),
+                                                                p[kk], o[db], 0, 0, 0);
         }
     };
-    for (int kt = 0; kt < nkt; kt += 2) {
-        tile(kt, std::integral_constant<int, 0>{});
-        if (kt + 1 < nkt) tile(kt + 1, std::integral_constant<int, 1>{});
+    // score transform of one unit: s[j*4 + i] is the score of key
+    // ukey0 + j*8 + h*4 + i.  Masked keys get t = -inf (softcap) or P = 0
+    // (sigmoid).  For the online max (softcap without SREF) the returned
+    // factor rescales O once this stage's PV product has landed.
+    auto transform = [&](f32x16 &s, bf16x8 (&p)[2], int ukey0, auto masked) __attribute__((always_inline)) -> float {
+        constexpr bool MASKED = decltype(masked)::value;
+        float corr = 1.0f;
+        if constexpr (SOFTCAP) {
+            uint32_t tw[8];      // packed FP16 t (poly)
+            float tmax = -INFINITY;
+            if constexpr (MODE == AM_SOFTCAP_POLY) {
+                uint32_t mx = 0xFC00FC00u;   // packed FP16 -inf
+#pragma unroll
+                for (int e = 0; e < 16; e += 2) {
+                    uint32_t aw;
+                    uint32_t w = softcap_poly_pair(s[e], s[e + 1], a.scale, a.tanh16, aw);
+                    if constexpr (MASKED) {
+                        const int k0 = ukey0 + (e >> 2) * 8 + h * 4 + (e & 3);
+                        const uint32_t mlo = k0 > lim ? 0x0000FFFFu : 0u;
+                        const uint32_t mhi = k0 + 1 > lim ? 0xFFFF0000u : 0u;
+                        w = sel(mlo | mhi, 0xFC00FC00u, w);
+                    }
+                    if constexpr (!SREF) mx = bc<uint32_t>(__builtin_elementwise_max(bc<h2>(mx), bc<h2>(w)));
+                    tw[e >> 1] = w;
+                }
+                if constexpr (!SREF) tmax = fmaxf(f16_lo(mx), f16_hi(mx));
+            } else {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    float t = tanhf(s[e] * a.scale);
+                    if constexpr (MASKED) {
+                        const int k0 = ukey0 + (e >> 2) * 8 + h * 4 + (e & 3);
+                        t = k0 > lim ? -INFINITY : t;
+                    }
+                    s[e] = t;
+                    if constexpr (!SREF) tmax = fmaxf(tmax, t);
+                }
+            }
+            if constexpr (!SREF) {
+                // lazy rescale: move the reference only when the row max
+                // outgrows it by more than AT_RESCALE
+                tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+                const float zmax = tmax * a.c2;
+                const bool grow = zmax > m + AT_RESCALE;
+                float m_new;
+                if constexpr (EXP == 0) {
+                    m_new = grow ? zmax : m;
+                    corr = grow ? __builtin_amdgcn_exp2f(m - m_new) : 1.0f;
+                } else {   // integer reference; the rescale is an exact power of two
+                    m_new = grow ? ceilf(zmax) : m;
+                    corr = !grow ? 1.0f
+                                 : (m == -INFINITY ? 0.0f : __builtin_amdgcn_ldexpf(1.0f, (int)(m - m_new)));
+                }
+                l *= corr;
+                m = m_new;
+            }
+            // P = exp2(t c2 - m), row sums, BF16 B operands
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                bf16x8 frag;
+                if constexpr (MODE == AM_SOFTCAP_NATIVE) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float pe = __builtin_amdgcn_exp2f(fmaf(s[jj * 8 + e], a.c2, -m));
+                        l += pe;
+                        frag[e] = (__bf16)pe;
+                    }
+                } else {
+                    // the FP16 t feed the FMA directly (no conversions)
+                    const float nm = -m;
+#pragma unroll
+                    for (int e = 0; e < 8; e += 2) {
+                        const uint32_t w = tw[(jj * 8 + e) >> 1];
+                        float p0, p1;
+                        if constexpr (EXP == 0) {
+                            p0 = __builtin_amdgcn_exp2f(fma_mix_lo(w, a.c2, nm));
+                            p1 = __builtin_amdgcn_exp2f(fma_mix_hi(w, a.c2, nm));
+                        } else {
+                            exp2_core_pair<EXP>(fma_mix_lo(w, a.c2, -0.0f), fma_mix_hi(w, a.c2, -0.0f), m,
+                                                p0, p1);
+                        }
+                        l += p0;
+                        l += p1;
+                        frag[e] = (__bf16)p0;
+                        frag[e + 1] = (__bf16)p1;
+                    }
+                }
+                p[jj] = frag;
+            }
+        } else {
+            // sigmoid: P directly, as BF16 B-operand fragments
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                u32x4 fw;
+#pragma unroll
+                for (int e2 = 0; e2 < 4; ++e2) {
+                    const int e = jj * 8 + e2 * 2;
+                    uint32_t w;
+                    if constexpr (MODE == AM_SIGMOID_POLY) {
+                        w = sigmoid_poly_pair<false>(s[e], s[e + 1], a.scale, a.sig, nullptr);
+                    } else {
+                        w = pack_bf(sigmoid_acc(fmaf(s[e], a.scale, -a.logn)),
+                                    sigmoid_acc(fmaf(s[e + 1], a.scale, -a.logn)));
+                    }
+                    if constexpr (MASKED) {
+                        const int k0 = ukey0 + (e >> 2) * 8 + h * 4 + (e & 3);
+                        const uint32_t mlo = k0 > lim ? 0x0000FFFFu : 0u;
+                        const uint32_t mhi = k0 + 1 > lim ? 0xFFFF0000u : 0u;
+                        w &= ~(mlo | mhi);
+                    }
+                    fw[e2] = w;
+                }
+                p[jj] = bc<bf16x8>(fw);
+            }
+        }
+        return corr;
+    };
+    auto rescale = [&](float corr) __attribute__((always_inline)) {
+        if constexpr (SOFTCAP && !SREF) {
+            if (__builtin_amdgcn_ballot_w64(corr != 1.0f)) {
+#pragma unroll
+                for (int db = 0; db < 4; ++db) o[db] *= corr;
+            }
+        }
+    };
+
+    // ---- stage j of period p: HALF = j & 1 ... written out for the two
+    // halves so that every register and LDS offset is a constant.
+    // Stage j (HALF = (j + 1) & 1 is the K half of unit j + 1 and the V half
+    // of unit j - 1): QK^T(j + 1) from Kb, transform(j), PV(j - 1) from Vb.
+    auto stage = [&](int j, const uint16_t *Kb, const uint16_t *Vb, auto halfc) __attribute__((always_inline)) {
+        constexpr int HALF = decltype(halfc)::value;   // = (j + 1) & 1
+        constexpr int SN = HALF;                      // S(j + 1) lives in sc[(j + 1) & 1]
+        constexpr int SC = HALF ^ 1;                  // S(j) in sc[j & 1]
+        constexpr int PC = HALF ^ 1;                  // P(j) into pf[j & 1]
+        constexpr int PP = HALF;                      // P(j - 1) from pf[(j - 1) & 1]
+        if (j >= 1 && j + 1 < nu) {
+            // steady state: all three parts, no mask, one basic block
+            qk(sc[SN], Kb, HALF);
+            const float corr = transform(sc[SC], pf[PC], j * 32, std::false_type{});
+            pv(pf[PP], Vb, HALF);
+            rescale(corr);
+            return;
+        }
+        if (j + 1 < nu) qk(sc[SN], Kb, HALF);
+        float corr = 1.0f;
+        if (j >= 0 && j < nu) {
+            if (j == nu - 1 && last_masked) corr = transform(sc[SC], pf[PC], j * 32, std::true_type{});
+            else corr = transform(sc[SC], pf[PC], j * 32, std::false_type{});
+        }
+        if (j >= 1 && j <= nu) pv(pf[PP], Vb, HALF);
+        rescale(corr);
+    };
+
+    // ---- periods: p = 0 .. nkt; period p runs stages 2p - 1 and 2p --------
+    load_rows64(K, Ks[0], 0, S, wave, lane);
+    auto period = [&](int p, auto bufc) __attribute__((always_inline)) {
+        constexpr int kb = decltype(bufc)::value;    // K tile p in Ks[kb], V tile p - 1 in Vs[kb ^ 1]
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's loads of K p / V p - 1 landed
+        __syncthreads();   // everybody's landed; nobody reads Ks[kb ^ 1] / Vs[kb] any more
+        if (p + 1 < nkt) load_rows64(K, Ks[kb ^ 1], (p + 1) * AT_BN, S, wave, lane);
+        if (p < nkt) load_rows64(V, Vs[kb], p * AT_BN, S, wave, lane);
+        if (2 * p - 1 > nu) return;   // this wave is done (still takes part in the barriers)
+        stage(2 * p - 1, Ks[kb], Vs[kb ^ 1], std::integral_constant<int, 0>{});
+        stage(2 * p, Ks[kb], Vs[kb ^ 1], std::integral_constant<int, 1>{});
+    };
+    for (int p = 0; p <= nkt; p += 2) {
+        period(p, std::integral_constant<int, 0>{});
+        if (p + 1 <= nkt) period(p + 1, std::integral_constant<int, 1>{});
     }
 
     if (my_q >= S) return;

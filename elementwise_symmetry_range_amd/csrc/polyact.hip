@@ -257,6 +257,16 @@ const ProgramDef &sigmoid_d3() { return *find_program(PA_SIGMOID, 0); }
 
 }  // namespace
 
+namespace {
+// No arithmetic: the streaming kernels' own HBM rate (pa_stream_copy).
+struct CopyOp {
+    __device__ __forceinline__ uint32_t operator()(uint32_t aw) const { return aw; }
+};
+struct XorOp {
+    __device__ __forceinline__ uint32_t operator()(uint32_t aw, uint32_t bw) const { return aw ^ bw; }
+};
+}  // namespace
+
 // =============================================================================
 extern "C" {
 
@@ -378,6 +388,14 @@ pa_status native_act_fwd(pa_func f, pa_dtype t, const void *x, void *y, int64_t 
                   : run_map1(x, y, n, stream, NativeFwd<F_GELU, false>{});
     }
     return PA_ERR_FUNC;
+}
+
+pa_status pa_stream_copy(const void *a, const void *b, void *y, int64_t n, hipStream_t stream)
+{
+    pa_status s = b ? check_binary(PA_F16, a, b, y, n) : check_unary(PA_F16, a, y, n);
+    if (s != PA_OK) return s;
+    if (n == 0) return PA_OK;
+    return b ? run_map2(a, b, y, n, stream, XorOp{}) : run_map1(a, y, n, stream, CopyOp{});
 }
 
 pa_status native_act_bwd(pa_impl impl, pa_func f, pa_dtype t, const void *x_or_y, const void *dy,

@@ -292,6 +292,18 @@ pa_status native_sigmoid_attn_bwd(const void *q, const void *k, const void *v, c
                                   int32_t H, int32_t Hkv, int32_t S, int32_t D, int32_t causal,
                                   hipStream_t stream);
 
+/* ---- measurement reference ---------------------------------------------- */
+
+/* The elementwise streaming kernels with no arithmetic: y[i] = a[i] when b is
+ * NULL (one read stream and one write stream, 4 bytes per 16-bit element),
+ * y[i] = a[i] XOR b[i] bitwise otherwise (two read streams and one write
+ * stream, 6 bytes per element).  Same launch configuration, 16-byte vector
+ * body and scalar head / tail as poly_act_fwd / poly_act_bwd, so its rate is
+ * the HBM rate that launch shape reaches with nothing to compute: the
+ * ceiling the programs' rates are read against.  Arguments and errors as
+ * poly_act_fwd (16-bit elements of any type; no dtype argument). */
+pa_status pa_stream_copy(const void *a, const void *b, void *y, int64_t n, hipStream_t stream);
+
 /* ---- host-only queries (no device work) -------------------------------- */
 
 /* The program the kernels execute for (f, deriv, t).  Returns PA_ERR_FUNC if

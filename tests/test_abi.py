@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(pa):
     names = declared_functions()
-    assert len(names) == 22, names
+    assert len(names) == 23, names
     L = pa.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -82,6 +82,11 @@ def test_error_paths_unary(pa):
     assert L.poly_act_bwd(1, 1, FAKE, FAKE + 64, FAKE + 66, 8, None) == 5    # dx over dy
     assert L.native_act_bwd(5, 1, 1, FAKE, FAKE + 64, FAKE + 128, 8, None) == 4
     assert L.native_act_fwd(0, 1, FAKE, FAKE + 64, 8, None) == 4
+    assert L.pa_stream_copy(None, None, FAKE, 8, None) == 1          # NULL input
+    assert L.pa_stream_copy(FAKE, None, FAKE + 2, 8, None) == 5      # partial overlap
+    assert L.pa_stream_copy(FAKE, FAKE + 64, FAKE + 66, 8, None) == 5
+    assert L.pa_stream_copy(FAKE, None, FAKE + 64, -1, None) == 2
+    assert L.pa_stream_copy(FAKE, FAKE + 64, FAKE + 128, 0, None) == 0
     assert L.pa_status_str(5) == b"output partially overlaps another buffer"
 
 

@@ -206,3 +206,16 @@ def test_native_bwd(pa, orc, fmt, func):
     ref = np.array([enc(float(v)) for v in val], dtype=np.uint16)
     fine = np.isfinite(val)
     assert np.all(_ulp_diff(dxy[fine], ref[fine], fmt) <= 1), (func, fmt)
+
+
+def test_stream_copy_reference(pa):
+    """The no-arithmetic measurement reference moves bits unchanged: y = a, and
+    y = a XOR b, over aligned, misaligned and ragged ranges."""
+    rng = np.random.default_rng(31)
+    a = rng.integers(0, 65536, 70001).astype(np.uint16)
+    b = rng.integers(0, 65536, 70001).astype(np.uint16)
+    for n, off in ((70000, 0), (69993, 1), (9, 3), (1, 0)):
+        note(f"stream copy n={n} off={off}")
+        at, bt = to_dev(a, torch.float16)[off:off + n], to_dev(b, torch.float16)[off:off + n]
+        assert np.array_equal(to_bits(pa.stream_copy(at)), a[off:off + n])
+        assert np.array_equal(to_bits(pa.stream_copy(at, bt)), a[off:off + n] ^ b[off:off + n])
