@@ -17,9 +17,12 @@ roofline = the dominant kernel of the step, algorithmic bytes per launch
 cpu_baseline = the CPU oracle replaying the same programs on a bounded
           sample of the same arrays, on this host's cores.
 Also reported: each program's Gelem/s and share of HBM peak, the matched
-accurate-expf comparator and the speedup (alternating rounds, median of
-per-round times), the cache-resident 4,194,304-element endpoint (launches
-replayed from a HIP graph), the fused
+accurate-expf comparator and the speedup, timed as the pages time it
+(section 4.2: 1,000 warm-up calls per path, then nine rounds of 1,000 calls
+alternating which path goes first, ratio of the median per-round times;
+section 4.3 for the components: 25 warm-ups, five rounds of 100), the
+cache-resident 4,194,304-element endpoint (launches replayed from a HIP
+graph), the fused
 SwiGLU components, and softcap / sigmoid attention forward and backward.
 """
 from __future__ import annotations
@@ -47,12 +50,20 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--rounds", type=int, default=5, help="alternating poly/native rounds")
+    ap.add_argument("--protocol", choices=("pages", "quick"), default="pages",
+                    help="timing of the poly / comparator ratios: the pages' protocols "
+                         "(isolated: 1,000 warm-up calls, 9 alternating rounds of 1,000 calls; "
+                         "components: 25 warm-ups, 5 rounds of 100) or a short one for "
+                         "profiling runs")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-components", action="store_true", help="skip SwiGLU / attention")
     ap.add_argument("--only", default="", help="profile helper: run one kernel name only")
     ap.add_argument("--components-only", action="store_true",
                     help="profiling run: only the SwiGLU and attention components")
+    ap.add_argument("--component-set", choices=("all", "main", "pages"), default="all",
+                    help="main: SwiGLU dense / routed, softcap attention 1 x 16 x 8192, sigmoid "
+                         "attention 1 x 32 (8) x 4096; pages: the B1, B2 and B4 geometries "
+                         "(a kernel trace of one set maps every launch of a kernel to one shape)")
     ap.add_argument("--step-only", action="store_true",
                     help="profiling run: warm-up and timed steps, then one plain device copy "
                          "of x (1,073,741,824 bytes moved) as the counter reference")
@@ -84,8 +95,18 @@ def time_calls(torch, fn, reps):
     return s.elapsed_time(e) / reps
 
 
-def alternating(torch, poly, native, reps, rounds):
-    """Median per-round mean times, alternating which path goes first."""
+# (warm-up calls, rounds, calls per round) of the two protocols
+ISOLATED = {"pages": (1000, 9, 1000), "quick": (10, 5, 10)}
+COMPONENT = {"pages": (25, 5, 100), "quick": (2, 3, 5)}
+
+
+def alternating(torch, poly, native, reps, rounds, warmup=0):
+    """Median per-round mean times (ms per call) after `warmup` calls of each
+    path, alternating which path goes first."""
+    for _ in range(warmup):
+        poly()
+        native()
+    torch.cuda.synchronize()
     tp, tn = [], []
     for r in range(rounds):
         if r % 2 == 0:
@@ -128,12 +149,35 @@ def cpu_baseline(x_t, g_t, budget_s=12.0):
                       f"of the same x / grad arrays ({elems} element evaluations, {el:.1f} s)"}
 
 
-def components(torch, pa, si):
+def components(torch, pa, si, protocol="pages", which="all"):
     """Fused SwiGLU (dense 8192 x 14336; routed 131,072 x 1408), softcap
     attention forward and backward (1 x 16 x 8192 x 128, causal) and sigmoid
     attention forward and backward (1 x 32 (8 kv) x 4096 x 128, causal),
     poly vs accurate comparator."""
+    cw, cr, cn = COMPONENT[protocol]
+
+    def alt(fp, fn):
+        return alternating(torch, fp, fn, cn, cr, cw)
+
     res = {}
+    if which in ("all", "main"):
+        components_main(torch, pa, si, alt, res)
+    if which in ("all", "pages"):
+        components_pages(torch, pa, si, alt, res)
+    return res
+
+
+def attn_row(tp, tn, flops, extra):
+    row = dict(extra)
+    row.update({"poly_ms": round(tp, 4), "native_ms": round(tn, 4), "speedup": round(tn / tp, 3),
+                "tflops": round(flops / tp / 1e9, 1),
+                "pct_mfma_bf16": round(100 * flops / tp / 1e9 / BF16_DENSE_TFLOPS, 1)})
+    return row
+
+
+def components_main(torch, pa, si, alt, res):
+    """The configured workloads: SwiGLU dense and routed, softcap and sigmoid
+    attention forward and backward."""
     g, u, d = si.t_swiglu_inputs(8192, 14336)
     h, dg, du = torch.empty_like(g), torch.empty_like(g), torch.empty_like(g)
     n = g.numel()
@@ -143,7 +187,7 @@ def components(torch, pa, si):
             ("swiglu_dense_bwd", lambda: pa.poly_swiglu_bwd(g, u, d, out=(dg, du)),
              lambda: pa.native_swiglu_bwd(g, u, d, out=(dg, du)), 10)):
         fp(), fn()
-        tp, tn = alternating(torch, fp, fn, 20, 5)
+        tp, tn = alt(fp, fn)
         res[name] = {"elements": n, "poly_ms": round(tp, 4), "native_ms": round(tn, 4),
                      "speedup": round(tn / tp, 3), "gelem_s": round(n / tp / 1e6, 2),
                      "pct_hbm": round(100 * n * by / tp / 1e6 / HBM_PEAK_GBS, 1)}
@@ -160,18 +204,11 @@ def components(torch, pa, si):
             ("swiglu_routed_bwd", lambda: pa.poly_swiglu_bwd(g, u, d, out=(dg, du), row_offsets=off),
              lambda: pa.native_swiglu_bwd(g, u, d, out=(dg, du), row_offsets=off), 10)):
         fp(), fn()
-        tp, tn = alternating(torch, fp, fn, 20, 5)
+        tp, tn = alt(fp, fn)
         res[name] = {"elements": n, "poly_ms": round(tp, 4), "native_ms": round(tn, 4),
                      "speedup": round(tn / tp, 3), "gelem_s": round(n / tp / 1e6, 2),
                      "pct_hbm": round(100 * n * by / tp / 1e6 / HBM_PEAK_GBS, 1)}
     del g, u, d, h, dg, du
-
-    def attn_row(tp, tn, flops, extra):
-        row = dict(extra)
-        row.update({"poly_ms": round(tp, 4), "native_ms": round(tn, 4), "speedup": round(tn / tp, 3),
-                    "tflops": round(flops / tp / 1e9, 1),
-                    "pct_mfma_bf16": round(100 * flops / tp / 1e9 / BF16_DENSE_TFLOPS, 1)})
-        return row
 
     # softcap attention, 1 x 16 x 8192 x 128 causal: forward, and backward
     # from the forward's O and lse.  MFMA FLOP: forward 2 products of 2 D
@@ -185,7 +222,7 @@ def components(torch, pa, si):
     fp = lambda: pa.poly_softcap_attn_fwd(q, k, v, 50.0, True, out=o)  # noqa: E731
     fn = lambda: pa.native_softcap_attn_fwd(q, k, v, 50.0, True, out=o)  # noqa: E731
     fp(), fn()
-    tp, tn = alternating(torch, fp, fn, 5, 5)
+    tp, tn = alt(fp, fn)
     res["softcap_attn_fwd"] = attn_row(tp, tn, flops, {"causal_scores": scores})
     # the softmax's exponentials by software exp2 cores (same kernel, same
     # tanh program) against v_exp_f32
@@ -193,7 +230,7 @@ def components(torch, pa, si):
     for core in ("d1", "pwl2", "d2", "d3"):
         fc = lambda core=core: pa.poly_softcap_attn_fwd_exp2(q, k, v, 50.0, True, core=core, out=o)  # noqa: E731
         fc()
-        tc, th = alternating(torch, fc, fp, 5, 5)
+        tc, th = alt(fc, fp)
         cores[core] = {"ms": round(tc, 4), "hw_exp2_ms": round(th, 4), "speedup_vs_hw": round(th / tc, 3)}
     res["softcap_attn_fwd_exp2_cores"] = cores
     op, lp = pa.poly_softcap_attn_fwd(q, k, v, 50.0, True, with_lse=True)
@@ -205,7 +242,7 @@ def components(torch, pa, si):
     fn = lambda: pa.native_softcap_attn_bwd(q, k, v, on, dout, ln, 50.0, True, dq=dq, dk=dk,  # noqa: E731
                                             dv=dv, workspace=ws)
     fp(), fn()
-    tp, tn = alternating(torch, fp, fn, 5, 5)
+    tp, tn = alt(fp, fn)
     res["softcap_attn_bwd"] = attn_row(tp, tn, 2.5 * flops, {"causal_scores": scores})
     del q, k, v, dout, o, op, on, lp, ln, dq, dk, dv, ws
 
@@ -219,7 +256,7 @@ def components(torch, pa, si):
     fp = lambda: pa.poly_sigmoid_attn_fwd(q, k, v, True, out=o)  # noqa: E731
     fn = lambda: pa.native_sigmoid_attn_fwd(q, k, v, True, out=o)  # noqa: E731
     fp(), fn()
-    tp, tn = alternating(torch, fp, fn, 5, 5)
+    tp, tn = alt(fp, fn)
     res["sigmoid_attn_fwd"] = attn_row(tp, tn, flops, {"causal_scores": scores})
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws = pa.attn_bwd_workspace(False, 1, 32, 8, 4096, 128, device=q.device)
@@ -228,12 +265,15 @@ def components(torch, pa, si):
     fn = lambda: pa.native_sigmoid_attn_bwd(q, k, v, dout, True, dq=dq, dk=dk, dv=dv,  # noqa: E731
                                             workspace=ws)
     fp(), fn()
-    tp, tn = alternating(torch, fp, fn, 5, 5)
+    tp, tn = alt(fp, fn)
     res["sigmoid_attn_bwd"] = attn_row(tp, tn, 2.5 * flops, {"causal_scores": scores})
     del q, k, v, dout, o, dq, dk, dv, ws
 
-    # the pages' own component geometries (their GB200 ratios are context):
-    # B2 softcap attention at B = 1, 32 query / 8 key-value heads, S = 4096
+
+def components_pages(torch, pa, si, alt, res):
+    """The pages' own component geometries (their GB200 ratios are context):
+    B2 softcap attention at B = 1, 32 query / 8 key-value heads, S = 4096;
+    B1 SiLU over 58,720,256 BF16 values; B4 SwiGLU 24,576 x 1,280."""
     q, k, v = si.t_attn_inputs(1, 32, 4096, 128, Hkv=8)
     dout = si.t_attn_grad(1, 32, 4096, 128)
     o = torch.empty_like(q)
@@ -242,7 +282,7 @@ def components(torch, pa, si):
     fp = lambda: pa.poly_softcap_attn_fwd(q, k, v, 50.0, True, out=o)  # noqa: E731
     fn = lambda: pa.native_softcap_attn_fwd(q, k, v, 50.0, True, out=o)  # noqa: E731
     fp(), fn()
-    tp, tn = alternating(torch, fp, fn, 5, 5)
+    tp, tn = alt(fp, fn)
     res["b2_softcap_attn_fwd_32x8x4096"] = attn_row(tp, tn, flops, {"causal_scores": scores})
     op, lp = pa.poly_softcap_attn_fwd(q, k, v, 50.0, True, with_lse=True)
     on, ln = pa.native_softcap_attn_fwd(q, k, v, 50.0, True, with_lse=True)
@@ -253,7 +293,7 @@ def components(torch, pa, si):
     fn = lambda: pa.native_softcap_attn_bwd(q, k, v, on, dout, ln, 50.0, True, dq=dq, dk=dk,  # noqa: E731
                                             dv=dv, workspace=ws)
     fp(), fn()
-    tp, tn = alternating(torch, fp, fn, 5, 5)
+    tp, tn = alt(fp, fn)
     res["b2_softcap_attn_bwd_32x8x4096"] = attn_row(tp, tn, 2.5 * flops, {"causal_scores": scores})
     del q, k, v, dout, o, op, on, lp, ln, dq, dk, dv, ws
 
@@ -269,7 +309,7 @@ def components(torch, pa, si):
             ("b1_silu_bf16_bwd", lambda: pa.poly_act_bwd(x, gr, "silu", out=y),
              lambda: pa.native_act_bwd(x, gr, "silu", "native", out=y), 6)):
         fp(), fn()
-        tp, tn = alternating(torch, fp, fn, 20, 5)
+        tp, tn = alt(fp, fn)
         res[name] = {"elements": n, "poly_ms": round(tp, 4), "native_ms": round(tn, 4),
                      "speedup": round(tn / tp, 3), "pct_hbm": round(100 * n * by / tp / 1e6 / HBM_PEAK_GBS, 1)}
     del x, gr, y
@@ -284,10 +324,9 @@ def components(torch, pa, si):
             ("b4_swiglu_24576x1280_bwd", lambda: pa.poly_swiglu_bwd(g, u, d, out=(dg, du)),
              lambda: pa.native_swiglu_bwd(g, u, d, out=(dg, du)), 10)):
         fp(), fn()
-        tp, tn = alternating(torch, fp, fn, 20, 5)
+        tp, tn = alt(fp, fn)
         res[name] = {"elements": n, "poly_ms": round(tp, 4), "native_ms": round(tn, 4),
                      "speedup": round(tn / tp, 3), "pct_hbm": round(100 * n * by / tp / 1e6 / HBM_PEAK_GBS, 1)}
-    return res
 
 
 def main():
@@ -303,7 +342,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     pa.lib()
     if args.components_only:
-        print(json.dumps({"components_only": True, "components": components(torch, pa, si)}),
+        print(json.dumps({"components_only": True,
+                          "components": components(torch, pa, si, args.protocol,
+                                                   args.component_set)}),
               flush=True)
         return
 
@@ -355,25 +396,27 @@ def main():
             traffic = tr["kernels"][dom[0]]
 
     # ---- matched comparators and the L2-resident endpoint (not in the step) --
+    iw, ir, ic = ISOLATED[args.protocol]
     detail = {}
     for name, by, fp, fn in ks:
-        tp, tn = alternating(torch, fp, fn, 10, args.rounds)
+        tp, tn = alternating(torch, fp, fn, ic, ir, iw)
         detail[name] = {"poly_gelem_s": round(N_HBM / tp / 1e6, 1),
                         "pct_hbm": round(100 * by * N_HBM / tp / 1e6 / HBM_PEAK_GBS, 1),
                         "native_gelem_s": round(N_HBM / tn / 1e6, 1),
                         "speedup_vs_accurate": round(tn / tp, 3)}
     for f in ("silu", "gelu"):   # centered-odd derivative programs (not in the step)
         tp, tn = alternating(torch, lambda f=f: pa.poly_act_bwd(x, g, f, out=y),
-                             lambda f=f: pa.native_act_bwd(x, g, f, "native", out=y), 10,
-                             args.rounds)
+                             lambda f=f: pa.native_act_bwd(x, g, f, "native", out=y), ic,
+                             ir, iw)
         detail[f"{f}_bwd"] = {"poly_gelem_s": round(N_HBM / tp / 1e6, 1),
                               "pct_hbm": round(100 * 6 * N_HBM / tp / 1e6 / HBM_PEAK_GBS, 1),
                               "native_gelem_s": round(N_HBM / tn / 1e6, 1),
                               "speedup_vs_accurate": round(tn / tp, 3), "in_step": False}
     for f in BWD:   # the paper's native backward consumes the saved y
         yy = pa.native_act_fwd(x, f)
-        tp = time_calls(torch, lambda f=f: pa.poly_act_bwd(x, g, f, out=y), 10)
-        tn = time_calls(torch, lambda f=f: pa.native_act_bwd(yy, g, f, "native_from_y", out=y), 10)
+        tp, tn = alternating(torch, lambda f=f: pa.poly_act_bwd(x, g, f, out=y),
+                             lambda f=f: pa.native_act_bwd(yy, g, f, "native_from_y", out=y), ic,
+                             ir, iw)
         detail[f"{f}_bwd"]["speedup_vs_from_y"] = round(tn / tp, 3)
         del yy
     # L2 / cache-resident endpoint: 4,194,304 elements (16 MiB read and
@@ -400,7 +443,8 @@ def main():
                lambda f=f: pa.native_act_bwd(xs, gs, f, "native", out=ys)) for f in BWD]
     for name, fp, fn in cases:
         (gp, n), (gn, _) = graphed(fp), graphed(fn)
-        tp, tn = alternating(torch, gp, gn, 5, args.rounds)
+        # replays of n launches: the same number of calls per round as above
+        tp, tn = alternating(torch, gp, gn, max(1, ic // n), ir, max(1, iw // n))
         tp, tn = tp / n, tn / n
         l2[name] = {"poly_gelem_s": round(N_L2 / tp / 1e6, 1), "speedup": round(tn / tp, 3),
                     "poly_us": round(1e3 * tp, 2), "native_us": round(1e3 * tn, 2)}
@@ -428,7 +472,7 @@ def main():
     sc2_gbs = 6 * N_HBM / (ts2 * 1e-3) / 1e9
     dom_copy = ((lambda: pa.stream_copy(x, g, out=y)) if dom[1] == 6
                 else (lambda: pa.stream_copy(x, out=y)))
-    tdom, tref = alternating(torch, dom[2], dom_copy, 10, args.rounds)
+    tdom, tref = alternating(torch, dom[2], dom_copy, ic, ir, iw)
     ceilings = {"stream_copy_1r1w_gbs": round(sc1_gbs, 1),
                 "stream_copy_1r1w_pct_hbm": round(100 * sc1_gbs / HBM_PEAK_GBS, 1),
                 "stream_copy_2r1w_gbs": round(sc2_gbs, 1),
@@ -439,7 +483,7 @@ def main():
                 "bf16_gemm_8192_tflops": round(gemm_tf, 1),
                 "bf16_gemm_8192_pct_peak": round(100 * gemm_tf / BF16_DENSE_TFLOPS, 1)}
 
-    comp = None if args.no_components else components(torch, pa, si)
+    comp = None if args.no_components else components(torch, pa, si, args.protocol)
     cpu = None if args.no_cpu else cpu_baseline(x, g)
 
     line = {

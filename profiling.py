@@ -5,7 +5,8 @@ under profiles/ and the traffic table bench.py reports.
         --fetch DIR/pmc_counter_collection.csv --write DIR/pmc_counter_collection.csv \
         --command "<the exact rocprofv3 command>"
 
-and the kernel table of `bench.py --components-only` (SwiGLU and attention):
+and the kernel table of `bench.py --components-only --component-set main`
+(SwiGLU and attention at the configured shapes, one shape per kernel):
 
     python profiling.py --components DIR/comp_kernel_stats.csv --command "<command>"
 
@@ -67,10 +68,11 @@ SCORES = {"softcap": 16 * 8192 * 8193 // 2, "sigmoid": 32 * 4096 * 4097 // 2}
 
 def components(path, command, out):
     lines = ["# SwiGLU and attention components", "",
-             "Kernel trace of `bench.py --components-only` (alternating poly / comparator "
-             "rounds; softcap attention 1 x 16 x 8192 x 128 causal, sigmoid attention 1 x 32 "
-             "(8 key/value heads) x 4096 x 128 causal, SwiGLU dense 8192 x 14336 and routed "
-             "131,072 x 1408 rows averaged together):", "", "```", command, "```", "",
+             "Kernel trace of `bench.py --components-only --component-set main` "
+             "(alternating poly / comparator rounds; softcap attention 1 x 16 x 8192 x 128 "
+             "causal, sigmoid attention 1 x 32 (8 key/value heads) x 4096 x 128 causal, "
+             "SwiGLU dense 8192 x 14336 and routed 131,072 x 1408 rows averaged together):",
+             "", "```", command, "```", "",
              "| kernel | what | calls | mean us | MFMA TFLOP/s | % of 2.5 PF |",
              "|---|---|---|---|---|---|"]
     import re
