@@ -66,7 +66,10 @@ def parse():
                          "(a kernel trace of one set maps every launch of a kernel to one shape)")
     ap.add_argument("--step-only", action="store_true",
                     help="profiling run: warm-up and timed steps, then one plain device copy "
-                         "of x (1,073,741,824 bytes moved) as the counter reference")
+                         "of x (4 bytes per element moved) as the counter reference")
+    ap.add_argument("--elements", type=int, default=N_HBM,
+                    help="with --step-only: elements per kernel (e.g. 4194304 for the "
+                         "cache-resident endpoint); the default run always uses 268,435,456")
     return ap.parse_args()
 
 
@@ -348,7 +351,10 @@ def main():
               flush=True)
         return
 
-    x, g = si.t_cfg2(N_HBM, device="cuda")
+    if args.elements != N_HBM and not args.step_only:
+        print("--elements applies to --step-only profiling runs only", flush=True)
+        sys.exit(2)
+    x, g = si.t_cfg2(args.elements, device="cuda")
     ks, y = kernels(pa, x, g)
     if args.only:
         ks = [k for k in ks if k[0] == args.only]
@@ -448,6 +454,16 @@ def main():
         tp, tn = tp / n, tn / n
         l2[name] = {"poly_gelem_s": round(N_L2 / tp / 1e6, 1), "speedup": round(tn / tp, 3),
                     "poly_us": round(1e3 * tp, 2), "native_us": round(1e3 * tn, 2)}
+    # the cache-resident copy ceiling: the same streaming kernels with no
+    # arithmetic at 4M, graphed the same way
+    (g1, n), (g2, _) = (graphed(lambda: pa.stream_copy(xs, out=ys)),
+                        graphed(lambda: pa.stream_copy(xs, gs, out=ys)))
+    t1c, t2c = alternating(torch, g1, g2, max(1, ic // n), ir, max(1, iw // n))
+    t1c, t2c = t1c / n, t2c / n
+    l2["stream_copy_1r1w"] = {"gelem_s": round(N_L2 / t1c / 1e6, 1), "us": round(1e3 * t1c, 2),
+                              "gbs": round(4 * N_L2 / t1c / 1e6, 1)}
+    l2["stream_copy_2r1w"] = {"gelem_s": round(N_L2 / t2c / 1e6, 1), "us": round(1e3 * t2c, 2),
+                              "gbs": round(6 * N_L2 / t2c / 1e6, 1)}
     del xs, gs, ys
 
     # reference rates measured on this GPU: the runtime's device-to-device
@@ -473,11 +489,15 @@ def main():
     dom_copy = ((lambda: pa.stream_copy(x, g, out=y)) if dom[1] == 6
                 else (lambda: pa.stream_copy(x, out=y)))
     tdom, tref = alternating(torch, dom[2], dom_copy, ic, ir, iw)
+    # the measurement's own false-alarm floor (the pages report one for their
+    # rebuilt binaries): the dominant kernel alternated against itself
+    ta, tb = alternating(torch, dom[2], dom[2], ic, ir, iw)
     ceilings = {"stream_copy_1r1w_gbs": round(sc1_gbs, 1),
                 "stream_copy_1r1w_pct_hbm": round(100 * sc1_gbs / HBM_PEAK_GBS, 1),
                 "stream_copy_2r1w_gbs": round(sc2_gbs, 1),
                 "stream_copy_2r1w_pct_hbm": round(100 * sc2_gbs / HBM_PEAK_GBS, 1),
                 "dominant_kernel_vs_stream_copy": round(tref / tdom, 4),
+                "dominant_kernel_a_a_ratio": round(tb / ta, 4),
                 "runtime_d2d_copy_gbs": round(copy_gbs, 1),
                 "runtime_d2d_copy_pct_hbm": round(100 * copy_gbs / HBM_PEAK_GBS, 1),
                 "bf16_gemm_8192_tflops": round(gemm_tf, 1),

@@ -107,17 +107,69 @@ def components(path, command, out):
     print("\n".join(lines))
 
 
+def per_dispatch_counters(path):
+    """{kernel short name: {counter: mean over dispatches of the per-dispatch sum}}"""
+    rows = list(csv.DictReader(open(path)))
+    agg = collections.defaultdict(lambda: collections.defaultdict(float))
+    names = {}
+    for r in rows:
+        k = short(r["Kernel_Name"])
+        if not k:
+            continue
+        agg[r["Dispatch_Id"]][r["Counter_Name"]] += float(r["Counter_Value"])
+        names[r["Dispatch_Id"]] = k
+    out = collections.defaultdict(lambda: collections.defaultdict(list))
+    for d, cs in agg.items():
+        for c, v in cs.items():
+            out[names[d]][c].append(v)
+    return {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in out.items()}
+
+
+def counters(specs, out):
+    """specs: (elements, VALU-pass csv, L2-pass csv, VALU command, L2 command)"""
+    lines = ["# Elementwise FP16 kernels: VALU busy and L2 hit rate", "",
+             "PMC passes (one counter group per run, no tracing) over the timed steps of "
+             "`bench.py --step-only` at the two endpoints of the isolated sweep. VALUBusy is "
+             "rocprofv3's derived metric (100 x SQ_ACTIVE_INST_VALU / CUs / GRBM_GUI_ACTIVE); "
+             "VALU instructions are per wave, i.e. per 512 elements (one 16-byte chunk per "
+             "lane); the L2 hit rate is TCC_HIT / (TCC_HIT + TCC_MISS).", ""]
+    for n, vpath, lpath, vcmd, lcmd in specs:
+        v, l2 = per_dispatch_counters(vpath), per_dispatch_counters(lpath)
+        lines += [f"## {n:,} elements", "", "```", vcmd, lcmd, "```", "",
+                  "| kernel | bench name | VALUBusy % | VALU instructions per wave | L2 hit % |",
+                  "|---|---|---|---|---|"]
+        for k, (names, _) in KERNELS.items():
+            if k not in v or k not in l2:
+                continue
+            waves = n / 512
+            hit = l2[k].get("TCC_HIT_sum", 0.0)
+            miss = l2[k].get("TCC_MISS_sum", 0.0)
+            lines.append(f"| `{k}` | {', '.join(names)} | {v[k].get('VALUBusy', float('nan')):.1f} | "
+                         f"{v[k].get('SQ_INSTS_VALU', float('nan')) / waves:.1f} | "
+                         f"{100 * hit / max(hit + miss, 1):.1f} |")
+        lines.append("")
+    with open(os.path.join(out, "elementwise_counters.md"), "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--components", default="")
+    ap.add_argument("--counters", nargs=5, action="append", default=[],
+                    metavar=("ELEMENTS", "VALU_CSV", "L2_CSV", "VALU_COMMAND", "L2_COMMAND"),
+                    help="VALU busy / L2 hit rate summary for one step size (repeatable)")
     ap.add_argument("--stats")
     ap.add_argument("--fetch")
     ap.add_argument("--write")
-    ap.add_argument("--command", required=True)
+    ap.add_argument("--command", default="")
     ap.add_argument("--fetch-command", default="")
     ap.add_argument("--write-command", default="")
     ap.add_argument("--out", default=os.path.join(ROOT, "profiles"))
     a = ap.parse_args()
+    if a.counters:
+        counters([(int(c[0]),) + tuple(c[1:]) for c in a.counters], a.out)
+        return
     if a.components:
         components(a.components, a.command, a.out)
         return
