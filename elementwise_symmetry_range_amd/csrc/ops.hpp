@@ -153,19 +153,36 @@ struct PolyBwdOddF16 {   // centered-odd direct-derivative program, dx = g (1/2 
 };
 
 // ---- BF16 programs ----------------------------------------------------------
+// v rounded to nearest even BF16, as an FP32 value: v_cvt_pk_bf16_f32 with a
+// zero low lane puts RN_bf16(v) in the high half, which is that FP32 value,
+// so one instruction per lane replaces a packed convert and an unpack.
+__device__ __forceinline__ float rn_bf16(float v)
+{
+    float r;   // the compiler would build {0, v} with a convert and a permute
+    asm("v_cvt_pk_bf16_f32 %0, 0, %1" : "=v"(r) : "v"(v));
+    return r;
+}
+
+// Horner stages D-1 .. 1 for the two lanes' clamped |x|: v0, v1 end as the
+// BF16-rounded chain values (each stage one FP32 FMA and one rounding).
+template <int D>
+__device__ __forceinline__ void horner_bf16_mid(float t0, float t1, const CoefBF16 &k, float &v0, float &v1)
+{
+    v0 = k.c[D];
+    v1 = k.c[D];
+#pragma unroll
+    for (int j = D - 1; j >= 1; --j) {
+        v0 = rn_bf16(fmaf(v0, t0, k.c[j]));
+        v1 = rn_bf16(fmaf(v1, t1, k.c[j]));
+    }
+}
+
 // Returns the packed BF16 Horner value for the two lanes' clamped |x|.
 template <int D, bool C0_ZERO>
 __device__ __forceinline__ uint32_t horner_bf16(float t0, float t1, const CoefBF16 &k)
 {
-    float v0 = k.c[D], v1 = k.c[D];
-#pragma unroll
-    for (int j = D - 1; j >= 1; --j) {
-        v0 = fmaf(v0, t0, k.c[j]);
-        v1 = fmaf(v1, t1, k.c[j]);
-        const uint32_t w = pack_bf(v0, v1);
-        v0 = lo_f(w);
-        v1 = hi_f(w);
-    }
+    float v0, v1;
+    horner_bf16_mid<D>(t0, t1, k, v0, v1);
     if constexpr (C0_ZERO) return pack_bf(v0 * t0, v1 * t1);
     else return pack_bf(fmaf(v0, t0, k.c[0]), fmaf(v1, t1, k.c[0]));
 }
@@ -180,16 +197,19 @@ __device__ __forceinline__ uint32_t poly_fwd_bf16_core(uint32_t xw, const CoefBF
     const uint32_t a0 = aw << 16, a1 = aw & 0xFFFF0000u;
     const float t0 = bc<float>(a0 < k.lc ? a0 : k.lc);
     const float t1 = bc<float>(a1 < k.lc ? a1 : k.lc);
-    const uint32_t v = horner_bf16<D, true>(t0, t1, k);
     if constexpr (FUNC == F_SIGMOID) {
-        const uint32_t r = v ^ sw;
+        const uint32_t r = horner_bf16<D, true>(t0, t1, k) ^ sw;
         return pack_bf(0.5f + lo_f(r), 0.5f + hi_f(r));
     } else if constexpr (FUNC == F_TANH) {
-        return v ^ sw;
+        return horner_bf16<D, true>(t0, t1, k) ^ sw;
     } else {
-        const uint32_t xh = pack_bf(lo_f(xw) * 0.5f, hi_f(xw) * 0.5f);
-        const uint32_t y = pack_bf(fmaf(bc<float>(a0), lo_f(v), lo_f(xh)),
-                                   fmaf(bc<float>(a1), hi_f(v), hi_f(xh)));
+        // x/2 + t v with v = RN(v t^) and x/2 rounded, each per lane
+        float v0, v1;
+        horner_bf16_mid<D>(t0, t1, k, v0, v1);
+        v0 = rn_bf16(v0 * t0);
+        v1 = rn_bf16(v1 * t1);
+        const uint32_t y = pack_bf(fmaf(bc<float>(a0), v0, rn_bf16(lo_f(xw) * 0.5f)),
+                                   fmaf(bc<float>(a1), v1, rn_bf16(hi_f(xw) * 0.5f)));
         return sel(not_ninf_bf16(xw), y, 0x80008000u);
     }
 }
@@ -213,8 +233,11 @@ struct PolyBwdBF16 {
         const uint32_t a0 = aw << 16, a1 = aw & 0xFFFF0000u;
         const float t0 = bc<float>(a0 < k.lc ? a0 : k.lc);
         const float t1 = bc<float>(a1 < k.lc ? a1 : k.lc);
-        const uint32_t v = horner_bf16<D, false>(t0, t1, k);
-        uint32_t y = pack_bf(lo_f(gw) * lo_f(v), hi_f(gw) * hi_f(v));
+        float v0, v1;
+        horner_bf16_mid<D>(t0, t1, k, v0, v1);
+        v0 = rn_bf16(fmaf(v0, t0, k.c[0]));
+        v1 = rn_bf16(fmaf(v1, t1, k.c[0]));
+        uint32_t y = pack_bf(lo_f(gw) * v0, hi_f(gw) * v1);
         y = sel(nan_mask_bf16(gw & 0x7FFF7FFFu), gw | 0x00400040u, y);
         return sel(nan_mask_bf16(aw), xw | 0x00400040u, y);
     }
