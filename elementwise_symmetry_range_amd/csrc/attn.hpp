@@ -175,26 +175,24 @@ template <bool GRAD>
 __device__ __forceinline__ uint32_t sigmoid_poly_pair(float s0, float s1, float scale,
                                                       const SigCoef &k, uint32_t *grad)
 {
-    const uint32_t xw = pack_bf(s0 * scale, s1 * scale);
-    const float x0 = lo_f(xw), x1 = hi_f(xw);
+    // every value BF16-rounded per lane (rn_bf16: one instruction, no unpack)
+    const float x0 = rn_bf16(s0 * scale), x1 = rn_bf16(s1 * scale);
     const int r0 = x0 >= k.thr, r1 = x1 >= k.thr;
     const float t0 = fminf(fmaxf(x0, k.lo), k.hi);
     const float t1 = fminf(fmaxf(x1, k.lo), k.hi);
     float v0 = r0 ? k.c[1][3] : k.c[0][3];
     float v1 = r1 ? k.c[1][3] : k.c[0][3];
-    uint32_t w = 0;
 #pragma unroll
     for (int j = 2; j >= 0; --j) {
-        w = pack_bf(fmaf(t0, v0, r0 ? k.c[1][j] : k.c[0][j]), fmaf(t1, v1, r1 ? k.c[1][j] : k.c[0][j]));
-        v0 = lo_f(w);
-        v1 = hi_f(w);
+        v0 = rn_bf16(fmaf(t0, v0, r0 ? k.c[1][j] : k.c[0][j]));
+        v1 = rn_bf16(fmaf(t1, v1, r1 ? k.c[1][j] : k.c[0][j]));
     }
     v0 = fmaxf(v0, 0.0f);
     v1 = fmaxf(v1, 0.0f);
     if constexpr (GRAD) {
-        const uint32_t fw = pack_bf(fmaf(t0, r0 ? k.b[1] : k.b[0], r0 ? k.a[1] : k.a[0]),
-                                    fmaf(t1, r1 ? k.b[1] : k.b[0], r1 ? k.a[1] : k.a[0]));
-        *grad = pack_bf(v0 * lo_f(fw), v1 * hi_f(fw));
+        const float f0 = rn_bf16(fmaf(t0, r0 ? k.b[1] : k.b[0], r0 ? k.a[1] : k.a[0]));
+        const float f1 = rn_bf16(fmaf(t1, r1 ? k.b[1] : k.b[0], r1 ? k.a[1] : k.a[0]));
+        *grad = pack_bf(v0 * f0, v1 * f1);
     }
     return pack_bf(v0, v1);   // exact: v0, v1 are BF16 values
 }
