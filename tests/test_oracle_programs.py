@@ -218,3 +218,20 @@ def test_swiglu_row_range(orc, progs):
     full = orc.swiglu_fwd(progs["sigmoid_fwd_d3"], g, u)
     assert np.array_equal(h[3:7], full[3:7])
     assert not h[:3].any() and not h[7:].any()
+
+
+def test_bf16_rounding_orders_agree_on_every_input(orc, progs):
+    """The deployed BF16 order (FP32 FMA rounded to FP32, then to BF16) and the
+    pages' single-rounding BF16 FMA (section 3.4, fma.rn.bf16x2) give the same
+    output for every BF16 input of every program: a Horner step's exact
+    result fits FP32 unless the product is far below the addend, where both
+    orders round to the addend.  A split multiply / add does differ."""
+    g = np.random.default_rng(5).integers(0, 65536, 65536).astype(np.uint16)
+    for name, p in progs.items():
+        if p.deriv:
+            run = lambda order: orc.act_bwd(p, ALL, g, order)  # noqa: E731
+        else:
+            run = lambda order: orc.act_fwd(p, ALL, order)  # noqa: E731
+        deployed = run(orc.ORDER_F32FMA_BF16)
+        assert np.array_equal(deployed, run(orc.ORDER_BF16_FMA)), name
+        assert (deployed != run(orc.ORDER_BF16_SPLIT)).any(), name
