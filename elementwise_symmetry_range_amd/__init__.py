@@ -127,8 +127,15 @@ def _dev(t: torch.Tensor, name: str):
         raise ValueError(f"{name} must be contiguous")
 
 
-def _stream(t: torch.Tensor) -> int:
-    return torch.cuda.current_stream(t.device).cuda_stream
+def _call(entry, *args, on: torch.Tensor, tensors=()):
+    """One library call on the device of `on`, made current for the call (the
+    library launches on the current device), with that device's current
+    stream as the last argument.  Every tensor of the call must live there."""
+    for t in tensors:
+        if t is not None and t.device != on.device:
+            raise ValueError(f"all tensors of a call must be on {on.device}; one is on {t.device}")
+    with torch.cuda.device(on.device):
+        _check(entry(*args, torch.cuda.current_stream(on.device).cuda_stream))
 
 
 def _out(out, like):
@@ -143,8 +150,8 @@ def _out(out, like):
 def poly_act_fwd(x: torch.Tensor, func: str, out=None) -> torch.Tensor:
     _dev(x, "x")
     y = _out(out, x)
-    _check(lib().poly_act_fwd(FUNCS[func], _DTYPES[x.dtype], x.data_ptr(), y.data_ptr(),
-                              x.numel(), _stream(x)))
+    _call(lib().poly_act_fwd, FUNCS[func], _DTYPES[x.dtype], x.data_ptr(), y.data_ptr(), x.numel(),
+          on=x, tensors=(y,))
     return y
 
 
@@ -154,16 +161,16 @@ def poly_act_bwd(x: torch.Tensor, dy: torch.Tensor, func: str, out=None) -> torc
     if dy.dtype != x.dtype or dy.numel() != x.numel():
         raise ValueError("dy must match x")
     dx = _out(out, x)
-    _check(lib().poly_act_bwd(FUNCS[func], _DTYPES[x.dtype], x.data_ptr(), dy.data_ptr(),
-                              dx.data_ptr(), x.numel(), _stream(x)))
+    _call(lib().poly_act_bwd, FUNCS[func], _DTYPES[x.dtype], x.data_ptr(), dy.data_ptr(),
+          dx.data_ptr(), x.numel(), on=x, tensors=(dy, dx))
     return dx
 
 
 def native_act_fwd(x: torch.Tensor, func: str, out=None) -> torch.Tensor:
     _dev(x, "x")
     y = _out(out, x)
-    _check(lib().native_act_fwd(FUNCS[func], _DTYPES[x.dtype], x.data_ptr(), y.data_ptr(),
-                                x.numel(), _stream(x)))
+    _call(lib().native_act_fwd, FUNCS[func], _DTYPES[x.dtype], x.data_ptr(), y.data_ptr(),
+          x.numel(), on=x, tensors=(y,))
     return y
 
 
@@ -176,8 +183,8 @@ def stream_copy(a: torch.Tensor, b: torch.Tensor | None = None, out=None) -> tor
         if b.dtype != a.dtype or b.numel() != a.numel():
             raise ValueError("b must match a")
     y = _out(out, a)
-    _check(lib().pa_stream_copy(a.data_ptr(), None if b is None else b.data_ptr(), y.data_ptr(),
-                                a.numel(), _stream(a)))
+    _call(lib().pa_stream_copy, a.data_ptr(), None if b is None else b.data_ptr(), y.data_ptr(),
+          a.numel(), on=a, tensors=(b, y))
     return y
 
 
@@ -188,9 +195,8 @@ def native_act_bwd(x_or_y: torch.Tensor, dy: torch.Tensor, func: str, impl: str 
     if dy.dtype != x_or_y.dtype or dy.numel() != x_or_y.numel():
         raise ValueError("dy must match x_or_y")
     dx = _out(out, x_or_y)
-    _check(lib().native_act_bwd(IMPLS[impl], FUNCS[func], _DTYPES[x_or_y.dtype],
-                                x_or_y.data_ptr(), dy.data_ptr(), dx.data_ptr(), x_or_y.numel(),
-                                _stream(x_or_y)))
+    _call(lib().native_act_bwd, IMPLS[impl], FUNCS[func], _DTYPES[x_or_y.dtype], x_or_y.data_ptr(),
+          dy.data_ptr(), dx.data_ptr(), x_or_y.numel(), on=x_or_y, tensors=(dy, dx))
     return dx
 
 
@@ -218,8 +224,8 @@ def _swiglu_fwd(entry, gate, up, out, row_offsets):
     ldh = _mat(h, "out")
     off, ng = _offsets(row_offsets)
     rows, cols = gate.shape
-    _check(entry(2, gate.data_ptr(), up.data_ptr(), h.data_ptr(), rows, cols, ldg, ldu, ldh, off,
-                 ng, _stream(gate)))
+    _call(entry, 2, gate.data_ptr(), up.data_ptr(), h.data_ptr(), rows, cols, ldg, ldu, ldh, off,
+          ng, on=gate, tensors=(up, h, row_offsets))
     return h
 
 
@@ -231,8 +237,9 @@ def _swiglu_bwd(entry, gate, up, dh, out, row_offsets):
     lddg, lddu = _mat(dg, "dgate"), _mat(du, "dup")
     off, ng = _offsets(row_offsets)
     rows, cols = gate.shape
-    _check(entry(2, gate.data_ptr(), up.data_ptr(), dh.data_ptr(), dg.data_ptr(), du.data_ptr(),
-                 rows, cols, ldg, ldu, ldd, lddg, lddu, off, ng, _stream(gate)))
+    _call(entry, 2, gate.data_ptr(), up.data_ptr(), dh.data_ptr(), dg.data_ptr(), du.data_ptr(),
+          rows, cols, ldg, ldu, ldd, lddg, lddu, off, ng, on=gate,
+          tensors=(up, dh, dg, du, row_offsets))
     return dg, du
 
 
@@ -282,9 +289,9 @@ def _softcap_fwd(entry, q, k, v, cap, causal, out, with_lse):
     B, H, Hkv, S, D = _attn_shapes(q, k, v)
     o = _like(out, q, "out")
     lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device) if with_lse else None
-    _check(entry(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                 None if lse is None else lse.data_ptr(), B, H, Hkv, S, D, float(cap),
-                 int(bool(causal)), _stream(q)))
+    _call(entry, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+          None if lse is None else lse.data_ptr(), B, H, Hkv, S, D, float(cap), int(bool(causal)),
+          on=q, tensors=(k, v, o))
     return (o, lse) if with_lse else o
 
 
@@ -306,10 +313,9 @@ def poly_softcap_attn_fwd_exp2(q, k, v, cap: float = 50.0, causal: bool = True,
     B, H, Hkv, S, D = _attn_shapes(q, k, v)
     o = _like(out, q, "out")
     lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device) if with_lse else None
-    _check(lib().poly_softcap_attn_fwd_exp2(
-        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-        None if lse is None else lse.data_ptr(), B, H, Hkv, S, D, float(cap), int(bool(causal)),
-        EXP2_CORES[core], _stream(q)))
+    _call(lib().poly_softcap_attn_fwd_exp2, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+          None if lse is None else lse.data_ptr(), B, H, Hkv, S, D, float(cap), int(bool(causal)),
+          EXP2_CORES[core], on=q, tensors=(k, v, o))
     return (o, lse) if with_lse else o
 
 
@@ -352,10 +358,10 @@ def _softcap_bwd(entry, q, k, v, o, dout, lse, cap, causal, dq, dk, dv, workspac
         raise ValueError("lse must be contiguous float32 [B, H, S]")
     dq, dk, dv = _grads(q, k, dq, dk, dv)
     workspace = _ws(workspace, True, B, H, Hkv, S, D, q.device)
-    _check(entry(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
-                 lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                 workspace.data_ptr(), B, H, Hkv, S, D, float(cap), int(bool(causal)),
-                 _stream(q)))
+    _call(entry, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+          lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), B, H,
+          Hkv, S, D, float(cap), int(bool(causal)), on=q,
+          tensors=(k, v, o, dout, lse, dq, dk, dv, workspace))
     return dq, dk, dv
 
 
@@ -376,8 +382,8 @@ def native_softcap_attn_bwd(q, k, v, o, dout, lse, cap: float = 50.0, causal: bo
 def _sigmoid_fwd(entry, q, k, v, causal, out):
     B, H, Hkv, S, D = _attn_shapes(q, k, v)
     o = _like(out, q, "out")
-    _check(entry(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), B, H, Hkv, S, D,
-                 int(bool(causal)), _stream(q)))
+    _call(entry, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), B, H, Hkv, S, D,
+          int(bool(causal)), on=q, tensors=(k, v, o))
     return o
 
 
@@ -398,9 +404,9 @@ def _sigmoid_bwd(entry, q, k, v, dout, causal, dq, dk, dv, workspace):
         raise ValueError("dout must have q's shape")
     dq, dk, dv = _grads(q, k, dq, dk, dv)
     workspace = _ws(workspace, False, B, H, Hkv, S, D, q.device)
-    _check(entry(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(), dq.data_ptr(),
-                 dk.data_ptr(), dv.data_ptr(), None if workspace is None else workspace.data_ptr(),
-                 B, H, Hkv, S, D, int(bool(causal)), _stream(q)))
+    _call(entry, q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(), dq.data_ptr(),
+          dk.data_ptr(), dv.data_ptr(), None if workspace is None else workspace.data_ptr(), B, H,
+          Hkv, S, D, int(bool(causal)), on=q, tensors=(k, v, dout, dq, dk, dv, workspace))
     return dq, dk, dv
 
 
