@@ -148,13 +148,18 @@ template <class Op>
 pa_status swiglu_fwd_launch(const SwiArgs &a, hipStream_t st, const Op &op)
 {
     if (vec_ok(a, false)) {
-        const int64_t grid = grid_tiles(a.rows * (a.cols / 8), (int64_t)kMap2BS * kMap2U);
-        if (flat(a, false))
-            hipLaunchKernelGGL((k_swiglu_fwd_vec<Op, kMap2BS, kMap2U, true>), dim3((unsigned)grid),
-                               dim3(kMap2BS), 0, st, a, op);
+        const int64_t chunks = a.rows * (a.cols / 8);
+        const bool small = chunks <= kSmallChunks;
+        const int bs = small ? kSmallBS : kMap2BS;
+        const dim3 grid((unsigned)grid_tiles(chunks, (int64_t)bs * kMap2U));
+        if (small && flat(a, false))
+            hipLaunchKernelGGL((k_swiglu_fwd_vec<Op, kSmallBS, kMap2U, true>), grid, dim3(bs), 0, st, a, op);
+        else if (small)
+            hipLaunchKernelGGL((k_swiglu_fwd_vec<Op, kSmallBS, kMap2U, false>), grid, dim3(bs), 0, st, a, op);
+        else if (flat(a, false))
+            hipLaunchKernelGGL((k_swiglu_fwd_vec<Op, kMap2BS, kMap2U, true>), grid, dim3(bs), 0, st, a, op);
         else
-            hipLaunchKernelGGL((k_swiglu_fwd_vec<Op, kMap2BS, kMap2U, false>), dim3((unsigned)grid),
-                               dim3(kMap2BS), 0, st, a, op);
+            hipLaunchKernelGGL((k_swiglu_fwd_vec<Op, kMap2BS, kMap2U, false>), grid, dim3(bs), 0, st, a, op);
     } else {
         hipLaunchKernelGGL((k_swiglu_fwd_scalar<Op>), dim3((unsigned)grid_for(a.rows * a.cols, 1)),
                            dim3(kThreads), 0, st, a, op);
@@ -166,13 +171,18 @@ template <class Op>
 pa_status swiglu_bwd_launch(const SwiArgs &a, hipStream_t st, const Op &op)
 {
     if (vec_ok(a, true)) {
-        const int64_t grid = grid_tiles(a.rows * (a.cols / 8), (int64_t)kMap2BS * kMap2U);
-        if (flat(a, true))
-            hipLaunchKernelGGL((k_swiglu_bwd_vec<Op, kMap2BS, kMap2U, true>), dim3((unsigned)grid),
-                               dim3(kMap2BS), 0, st, a, op);
+        const int64_t chunks = a.rows * (a.cols / 8);
+        const bool small = chunks <= kSmallChunks;
+        const int bs = small ? kSmallBS : kMap2BS;
+        const dim3 grid((unsigned)grid_tiles(chunks, (int64_t)bs * kMap2U));
+        if (small && flat(a, true))
+            hipLaunchKernelGGL((k_swiglu_bwd_vec<Op, kSmallBS, kMap2U, true>), grid, dim3(bs), 0, st, a, op);
+        else if (small)
+            hipLaunchKernelGGL((k_swiglu_bwd_vec<Op, kSmallBS, kMap2U, false>), grid, dim3(bs), 0, st, a, op);
+        else if (flat(a, true))
+            hipLaunchKernelGGL((k_swiglu_bwd_vec<Op, kMap2BS, kMap2U, true>), grid, dim3(bs), 0, st, a, op);
         else
-            hipLaunchKernelGGL((k_swiglu_bwd_vec<Op, kMap2BS, kMap2U, false>), dim3((unsigned)grid),
-                               dim3(kMap2BS), 0, st, a, op);
+            hipLaunchKernelGGL((k_swiglu_bwd_vec<Op, kMap2BS, kMap2U, false>), grid, dim3(bs), 0, st, a, op);
     } else {
         hipLaunchKernelGGL((k_swiglu_bwd_scalar<Op>), dim3((unsigned)grid_for(a.rows * a.cols, 1)),
                            dim3(kThreads), 0, st, a, op);

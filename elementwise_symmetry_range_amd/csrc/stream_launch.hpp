@@ -14,13 +14,18 @@ namespace pa {
 namespace {
 
 constexpr int kThreads = 256;       // scalar kernels
-// Streaming tiles (threads per block, 16-byte chunks per thread).  A sweep of
-// block sizes 128-1024 and 1-4 chunks per thread on MI355X put one chunk per
-// thread and the most blocks first for every stream shape: 6.49 TB/s for one
-// input and one output, 6.52 TB/s for two inputs and one output, 6.20 TB/s
-// for three inputs and two outputs.
-constexpr int kMap1BS = 512, kMap1U = 1;   // x -> y
-constexpr int kMap2BS = 1024, kMap2U = 1;  // x, g -> y; SwiGLU fwd and bwd
+// Streaming tiles (threads per block, 16-byte chunks per thread).  Sweeps of
+// block sizes 128-1024 and 1-8 chunks per thread on MI355X put one chunk per
+// thread first for every stream shape (6.5 TB/s for one input and one
+// output, 6.5 TB/s for two inputs and one output, 6.2 TB/s for three inputs
+// and two outputs at 268,435,456 elements, with 512 threads for one input
+// and 1024 for two or three).  Below 2^23 chunks per stream (128 MiB) a
+// 256-thread block is faster -- the grid is small there: 25 % for two inputs
+// at 4M elements, 10 % for the BF16 SiLU at 58.7M -- while above it 256
+// threads lose 2-6 %, so the block size follows the size.
+constexpr int kMap1BS = 512, kMap2BS = 1024, kSmallBS = 256;
+constexpr int kMap1U = 1, kMap2U = 1;
+constexpr int64_t kSmallChunks = int64_t(1) << 23;   // 16-byte chunks per stream
 constexpr int64_t kMaxGrid = 0x7FFFFFFF;
 constexpr int kBlocksPerCU = 8;     // scalar kernels: blocks per compute unit
 
@@ -85,9 +90,15 @@ pa_status run_map1(const void *x, void *y, int64_t n, hipStream_t st, const Op &
     const uint16_t *xs = (const uint16_t *)x;
     uint16_t *ys = (uint16_t *)y;
     if (sp.nvec > 0) {
-        const int64_t grid = grid_tiles(sp.nvec, (int64_t)kMap1BS * kMap1U);
-        hipLaunchKernelGGL((k_map1<Op, kMap1BS, kMap1U>), dim3((unsigned)grid), dim3(kMap1BS), 0, st,
-                           (const u32x4 *)(xs + sp.head), (u32x4 *)(ys + sp.head), sp.nvec, op);
+        const u32x4 *xv = (const u32x4 *)(xs + sp.head);
+        u32x4 *yv = (u32x4 *)(ys + sp.head);
+        if (sp.nvec <= kSmallChunks)
+            hipLaunchKernelGGL((k_map1<Op, kSmallBS, 1>), dim3((unsigned)grid_tiles(sp.nvec, kSmallBS)),
+                               dim3(kSmallBS), 0, st, xv, yv, sp.nvec, op);
+        else
+            hipLaunchKernelGGL((k_map1<Op, kMap1BS, kMap1U>),
+                               dim3((unsigned)grid_tiles(sp.nvec, (int64_t)kMap1BS * kMap1U)), dim3(kMap1BS),
+                               0, st, xv, yv, sp.nvec, op);
         if (stream_launched() != PA_OK) return PA_ERR_LAUNCH;
     }
     const int64_t rest = sp.head + (n - sp.tail0);
@@ -106,10 +117,15 @@ pa_status run_map2(const void *x, const void *g, void *y, int64_t n, hipStream_t
     const uint16_t *xs = (const uint16_t *)x, *gs = (const uint16_t *)g;
     uint16_t *ys = (uint16_t *)y;
     if (sp.nvec > 0) {
-        const int64_t grid = grid_tiles(sp.nvec, (int64_t)kMap2BS * kMap2U);
-        hipLaunchKernelGGL((k_map2<Op, kMap2BS, kMap2U>), dim3((unsigned)grid), dim3(kMap2BS), 0, st,
-                           (const u32x4 *)(xs + sp.head), (const u32x4 *)(gs + sp.head),
-                           (u32x4 *)(ys + sp.head), sp.nvec, op);
+        const u32x4 *xv = (const u32x4 *)(xs + sp.head), *gv = (const u32x4 *)(gs + sp.head);
+        u32x4 *yv = (u32x4 *)(ys + sp.head);
+        if (sp.nvec <= kSmallChunks)
+            hipLaunchKernelGGL((k_map2<Op, kSmallBS, 1>), dim3((unsigned)grid_tiles(sp.nvec, kSmallBS)),
+                               dim3(kSmallBS), 0, st, xv, gv, yv, sp.nvec, op);
+        else
+            hipLaunchKernelGGL((k_map2<Op, kMap2BS, kMap2U>),
+                               dim3((unsigned)grid_tiles(sp.nvec, (int64_t)kMap2BS * kMap2U)), dim3(kMap2BS),
+                               0, st, xv, gv, yv, sp.nvec, op);
         if (stream_launched() != PA_OK) return PA_ERR_LAUNCH;
     }
     const int64_t rest = sp.head + (n - sp.tail0);
