@@ -52,6 +52,7 @@
 //   O = O^T.
 #pragma once
 #include <type_traits>
+#include <utility>
 
 #include "ops.hpp"
 
@@ -95,6 +96,18 @@ struct AttnArgs {
     CoefF16 tanh16;    // D4 tanh program, FP16 coefficients
     SigCoef sig;
 };
+
+// f(integral_constant<int, i>) for i = 0 .. N - 1, unrolled at compile time
+template <class F, int... I>
+__device__ __forceinline__ void static_for_seq(F &&f, std::integer_sequence<int, I...>)
+{
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    if constexpr (N > 0) static_for_seq(f, std::make_integer_sequence<int, N>{});
+}
 
 __device__ __forceinline__ bf16x8 ld_bf16x8(const uint16_t *p) { return *(const bf16x8 *)p; }
 
@@ -282,7 +295,8 @@ __device__ __forceinline__ float sigmoid_acc(float u)
 // V tiles: period p (stages 2p - 1 and 2p) reads K tile p and V tile p - 1
 // from the two halves of each buffer while K tile p + 1 and V tile p stream
 // in.  The order of every accumulation (over keys for S, O and the row sum)
-// is the unpipelined one.
+// is the unpipelined one.  Steady-state stages are laid out as explicit
+// scheduling slots (see `slotted`).
 template <int MODE, int EXP = 0, bool SREF = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_fwd(AttnArgs a)
 {
@@ -353,20 +367,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                                                                 p[kk], o[db], 0, 0, 0);
         }
     };
-    // score transform of one unit: s[j*4 + i] is the score of key
+    // score transform of one unit, as NPC pieces run in order (the steady
+    // state spreads them between its MFMAs): s[j*4 + i] is the score of key
     // ukey0 + j*8 + h*4 + i.  Masked keys get t = -inf (softcap) or P = 0
-    // (sigmoid).  For the online max (softcap without SREF) the returned
-    // factor rescales O once this stage's PV product has landed.
-    auto transform = [&](f32x16 &s, bf16x8 (&p)[2], int ukey0, auto masked) __attribute__((always_inline)) -> float {
+    // (sigmoid).  Softcap pieces 0-7 map the score pairs through the tanh
+    // (packed FP16 words kept in st.w), then (online max only) one piece
+    // moves the reference, then pieces for the pairs' exp2, row sums and BF16
+    // words of P.  Sigmoid: one piece per pair.  For the online max the
+    // factor st.corr rescales O once this stage's PV product has landed.
+    constexpr int NPC = SOFTCAP ? (SREF ? 16 : 17) : 8;
+    struct TState {
+        uint32_t w[8];     // packed FP16 t (softcap poly), then the BF16 P words
+        uint32_t mx;       // packed FP16 running max of t (softcap poly, online max)
+        float tmax;        // running max of t (softcap comparator, online max)
+        float corr;
+    };
+    auto piece = [&](auto pc, f32x16 &s, TState &st, int ukey0, auto masked) __attribute__((always_inline)) {
+        constexpr int P = decltype(pc)::value;
         constexpr bool MASKED = decltype(masked)::value;
-        float corr = 1.0f;
         if constexpr (SOFTCAP) {
-            uint32_t tw[8];      // packed FP16 t (poly)
-            float tmax = -INFINITY;
-            if constexpr (MODE == AM_SOFTCAP_POLY) {
-                uint32_t mx = 0xFC00FC00u;   // packed FP16 -inf
-#pragma unroll
-                for (int e = 0; e < 16; e += 2) {
+            if constexpr (P < 8) {
+                constexpr int e = 2 * P;
+                if constexpr (MODE == AM_SOFTCAP_POLY) {
                     uint32_t aw;
                     uint32_t w = softcap_poly_pair(s[e], s[e + 1], a.scale, a.tanh16, aw);
                     if constexpr (MASKED) {
@@ -375,100 +397,98 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                         const uint32_t mhi = k0 + 1 > lim ? 0xFFFF0000u : 0u;
                         w = sel(mlo | mhi, 0xFC00FC00u, w);
                     }
-                    if constexpr (!SREF) mx = bc<uint32_t>(__builtin_elementwise_max(bc<h2>(mx), bc<h2>(w)));
-                    tw[e >> 1] = w;
-                }
-                if constexpr (!SREF) tmax = fmaxf(f16_lo(mx), f16_hi(mx));
-            } else {
+                    if constexpr (!SREF) st.mx = bc<uint32_t>(__builtin_elementwise_max(bc<h2>(st.mx), bc<h2>(w)));
+                    st.w[P] = w;
+                } else {
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    float t = tanhf(s[e] * a.scale);
-                    if constexpr (MASKED) {
-                        const int k0 = ukey0 + (e >> 2) * 8 + h * 4 + (e & 3);
-                        t = k0 > lim ? -INFINITY : t;
+                    for (int i = 0; i < 2; ++i) {
+                        float t = tanhf(s[e + i] * a.scale);
+                        if constexpr (MASKED) {
+                            const int k0 = ukey0 + (e >> 2) * 8 + h * 4 + (e & 3) + i;
+                            t = k0 > lim ? -INFINITY : t;
+                        }
+                        s[e + i] = t;
+                        if constexpr (!SREF) st.tmax = fmaxf(st.tmax, t);
                     }
-                    s[e] = t;
-                    if constexpr (!SREF) tmax = fmaxf(tmax, t);
                 }
-            }
-            if constexpr (!SREF) {
+            } else if constexpr (!SREF && P == 8) {
                 // lazy rescale: move the reference only when the row max
                 // outgrows it by more than AT_RESCALE
+                float tmax = MODE == AM_SOFTCAP_POLY ? fmaxf(f16_lo(st.mx), f16_hi(st.mx)) : st.tmax;
                 tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
                 const float zmax = tmax * a.c2;
                 const bool grow = zmax > m + AT_RESCALE;
                 float m_new;
                 if constexpr (EXP == 0) {
                     m_new = grow ? zmax : m;
-                    corr = grow ? __builtin_amdgcn_exp2f(m - m_new) : 1.0f;
+                    st.corr = grow ? __builtin_amdgcn_exp2f(m - m_new) : 1.0f;
                 } else {   // integer reference; the rescale is an exact power of two
                     m_new = grow ? ceilf(zmax) : m;
-                    corr = !grow ? 1.0f
-                                 : (m == -INFINITY ? 0.0f : __builtin_amdgcn_ldexpf(1.0f, (int)(m - m_new)));
+                    st.corr = !grow ? 1.0f
+                                    : (m == -INFINITY ? 0.0f : __builtin_amdgcn_ldexpf(1.0f, (int)(m - m_new)));
                 }
-                l *= corr;
+                l *= st.corr;
                 m = m_new;
-            }
-            // P = exp2(t c2 - m), row sums, BF16 B operands
-#pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-                bf16x8 frag;
+            } else {
+                // P = exp2(t c2 - m) of pair e2, the row sum, the BF16 word
+                constexpr int e2 = P - (SREF ? 8 : 9);
+                constexpr int e = 2 * e2;
+                float p0, p1;
                 if constexpr (MODE == AM_SOFTCAP_NATIVE) {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const float pe = __builtin_amdgcn_exp2f(fmaf(s[jj * 8 + e], a.c2, -m));
-                        l += pe;
-                        frag[e] = (__bf16)pe;
-                    }
+                    p0 = __builtin_amdgcn_exp2f(fmaf(s[e], a.c2, -m));
+                    l += p0;
+                    p1 = __builtin_amdgcn_exp2f(fmaf(s[e + 1], a.c2, -m));
+                    l += p1;
                 } else {
                     // the FP16 t feed the FMA directly (no conversions)
-                    const float nm = -m;
-#pragma unroll
-                    for (int e = 0; e < 8; e += 2) {
-                        const uint32_t w = tw[(jj * 8 + e) >> 1];
-                        float p0, p1;
-                        if constexpr (EXP == 0) {
-                            p0 = __builtin_amdgcn_exp2f(fma_mix_lo(w, a.c2, nm));
-                            p1 = __builtin_amdgcn_exp2f(fma_mix_hi(w, a.c2, nm));
-                        } else {
-                            exp2_core_pair<EXP>(fma_mix_lo(w, a.c2, -0.0f), fma_mix_hi(w, a.c2, -0.0f), m,
-                                                p0, p1);
-                        }
-                        l += p0;
-                        l += p1;
-                        frag[e] = (__bf16)p0;
-                        frag[e + 1] = (__bf16)p1;
+                    const uint32_t w = st.w[e2];
+                    if constexpr (EXP == 0) {
+                        p0 = __builtin_amdgcn_exp2f(fma_mix_lo(w, a.c2, -m));
+                        p1 = __builtin_amdgcn_exp2f(fma_mix_hi(w, a.c2, -m));
+                    } else {
+                        exp2_core_pair<EXP>(fma_mix_lo(w, a.c2, -0.0f), fma_mix_hi(w, a.c2, -0.0f), m, p0, p1);
                     }
+                    l += p0;
+                    l += p1;
                 }
-                p[jj] = frag;
+                st.w[e2] = pack_bf(p0, p1);
             }
         } else {
-            // sigmoid: P directly, as BF16 B-operand fragments
-#pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-                u32x4 fw;
-#pragma unroll
-                for (int e2 = 0; e2 < 4; ++e2) {
-                    const int e = jj * 8 + e2 * 2;
-                    uint32_t w;
-                    if constexpr (MODE == AM_SIGMOID_POLY) {
-                        w = sigmoid_poly_pair<false>(s[e], s[e + 1], a.scale, a.sig, nullptr);
-                    } else {
-                        w = pack_bf(sigmoid_acc(fmaf(s[e], a.scale, -a.logn)),
-                                    sigmoid_acc(fmaf(s[e + 1], a.scale, -a.logn)));
-                    }
-                    if constexpr (MASKED) {
-                        const int k0 = ukey0 + (e >> 2) * 8 + h * 4 + (e & 3);
-                        const uint32_t mlo = k0 > lim ? 0x0000FFFFu : 0u;
-                        const uint32_t mhi = k0 + 1 > lim ? 0xFFFF0000u : 0u;
-                        w &= ~(mlo | mhi);
-                    }
-                    fw[e2] = w;
-                }
-                p[jj] = bc<bf16x8>(fw);
+            // sigmoid: P of pair P directly, as a BF16 word
+            constexpr int e = 2 * P;
+            uint32_t w;
+            if constexpr (MODE == AM_SIGMOID_POLY) {
+                w = sigmoid_poly_pair<false>(s[e], s[e + 1], a.scale, a.sig, nullptr);
+            } else {
+                w = pack_bf(sigmoid_acc(fmaf(s[e], a.scale, -a.logn)),
+                            sigmoid_acc(fmaf(s[e + 1], a.scale, -a.logn)));
             }
+            if constexpr (MASKED) {
+                const int k0 = ukey0 + (e >> 2) * 8 + h * 4 + (e & 3);
+                const uint32_t mlo = k0 > lim ? 0x0000FFFFu : 0u;
+                const uint32_t mhi = k0 + 1 > lim ? 0xFFFF0000u : 0u;
+                w &= ~(mlo | mhi);
+            }
+            st.w[P] = w;
         }
-        return corr;
+    };
+    auto tstate = [&]() __attribute__((always_inline)) {
+        TState st;
+        st.mx = 0xFC00FC00u;   // packed FP16 -inf
+        st.tmax = -INFINITY;
+        st.corr = 1.0f;
+        return st;
+    };
+    // P as the two B-operand fragments of the PV product
+    auto finish = [&](const TState &st, bf16x8 (&p)[2]) __attribute__((always_inline)) {
+        p[0] = bc<bf16x8>(u32x4{st.w[0], st.w[1], st.w[2], st.w[3]});
+        p[1] = bc<bf16x8>(u32x4{st.w[4], st.w[5], st.w[6], st.w[7]});
+    };
+    auto transform = [&](f32x16 &s, bf16x8 (&p)[2], int ukey0, auto masked) __attribute__((always_inline)) -> float {
+        TState st = tstate();
+        static_for<NPC>([&](auto pc) __attribute__((always_inline)) { piece(pc, s, st, ukey0, masked); });
+        finish(st, p);
+        return st.corr;
     };
     auto rescale = [&](float corr) __attribute__((always_inline)) {
         if constexpr (SOFTCAP && !SREF) {
@@ -477,6 +497,56 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 for (int db = 0; db < 4; ++db) o[db] *= corr;
             }
         }
+    };
+
+    // ---- the steady-state stage as explicit slots --------------------------
+    // The 16 MFMAs of a stage alternate QK^T (even m, contraction step m / 2)
+    // and PV (odd m, d block m / 4, key step (m / 2) & 1); every accumulator
+    // sees its terms in the order above.  Slot t issues the LDS reads of the
+    // operands of slot t + 1, its own MFMAs and its share of the transform
+    // pieces; a scheduling fence closes each slot, so every LDS read runs one
+    // slot ahead of its MFMA (the compiler otherwise waits for each operand
+    // right before its MFMA) and the VALU work is spread evenly between the
+    // matrix instructions.  Softcap: 16 slots (one MFMA and one piece each);
+    // sigmoid: 8 slots (two MFMAs and one pair each).  Measured on MI355X:
+    // softcap 1.03-1.045x, sigmoid 1.01x, outputs bit-identical.
+    constexpr int AT_SLOTS = SOFTCAP ? 16 : 8, AT_AHEAD = 1;
+    auto slotted = [&](f32x16 &sn, f32x16 &scur, bf16x8 (&pc)[2], const bf16x8 (&pp)[2],
+                       const uint16_t *Kb, const uint16_t *Vb, int ukey0, auto halfc) __attribute__((always_inline)) {
+        constexpr int HALF = decltype(halfc)::value;
+        constexpr int MPS = 16 / AT_SLOTS;    // MFMAs per slot
+        bf16x8 op[16];
+        auto load_op = [&](auto mc) __attribute__((always_inline)) {
+            constexpr int mm = decltype(mc)::value;
+            if constexpr ((mm & 1) == 0) op[mm] = lds_row8(Kb, HALF * 32 + col, mm + h);
+            else op[mm] = lds_tr_a(Vb, HALF * 2 + ((mm >> 1) & 1), mm >> 2, g16, i16);
+        };
+        auto mfma_op = [&](auto mc) __attribute__((always_inline)) {
+            constexpr int mm = decltype(mc)::value;
+            if constexpr ((mm & 1) == 0)
+                sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[mm], qf[mm >> 1], mm == 0 ? f32x16{} : sn, 0, 0, 0);
+            else
+                o[mm >> 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[mm], pp[(mm >> 1) & 1], o[mm >> 2], 0, 0, 0);
+        };
+        TState st = tstate();
+        static_for<AT_AHEAD * MPS>([&](auto mc) __attribute__((always_inline)) { load_op(mc); });
+        static_for<AT_SLOTS>([&](auto tc) __attribute__((always_inline)) {
+            constexpr int t = decltype(tc)::value;
+            static_for<MPS>([&](auto ic) __attribute__((always_inline)) {
+                constexpr int mm = (t + AT_AHEAD) * MPS + decltype(ic)::value;
+                if constexpr (mm < 16) load_op(std::integral_constant<int, mm>{});
+            });
+            static_for<MPS>([&](auto ic) __attribute__((always_inline)) {
+                mfma_op(std::integral_constant<int, t * MPS + decltype(ic)::value>{});
+            });
+            constexpr int p0 = t * NPC / AT_SLOTS, p1 = (t + 1) * NPC / AT_SLOTS;
+            static_for<p1 - p0>([&](auto ic) __attribute__((always_inline)) {
+                piece(std::integral_constant<int, p0 + decltype(ic)::value>{}, scur, st, ukey0, std::false_type{});
+            });
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        finish(st, pc);
+        rescale(st.corr);
     };
 
     // ---- stage j of period p: HALF = j & 1 ... written out for the two
@@ -491,10 +561,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         constexpr int PP = HALF;                      // P(j - 1) from pf[(j - 1) & 1]
         if (j >= 1 && j + 1 < nu) {
             // steady state: all three parts, no mask, one basic block
-            qk(sc[SN], Kb, HALF);
-            const float corr = transform(sc[SC], pf[PC], j * 32, std::false_type{});
-            pv(pf[PP], Vb, HALF);
-            rescale(corr);
+            slotted(sc[SN], sc[SC], pf[PC], pf[PP], Kb, Vb, j * 32, halfc);
             return;
         }
         if (j + 1 < nu) qk(sc[SN], Kb, HALF);
