@@ -10,6 +10,11 @@ and the kernel table of `bench.py --components-only --component-set main`
 
     python profiling.py --components DIR/comp_kernel_stats.csv --command "<command>"
 
+and, from three PMC passes over the same components run, the attention
+kernels' MFMA busy, VALU issue and wait fractions:
+
+    python profiling.py --attn-counters P1.csv P2.csv P3.csv "<cmd 1>" "<cmd 2>" "<cmd 3>"
+
 Traffic calibration: the FETCH_SIZE / WRITE_SIZE derived counters are scaled
 by what they read for the device-to-device hipMemcpy of x (536,870,912 bytes
 read and written) issued at the end of the profiled run: factor = true bytes /
@@ -153,9 +158,85 @@ def counters(specs, out):
     print("\n".join(lines))
 
 
+CLOCK_HZ = 2.4e9      # MI355X peak engine clock (MFMA-busy fractions assume it)
+SIMDS = 256 * 4
+
+
+def attn_label(name):
+    import re
+    m = re.search(r"k_attn_(fwd|bwd_dq|bwd_dkdv)<(\d)(?:, ?(\w+))?", name)
+    if not m:
+        return None
+    kind, mode, extra = m.group(1), m.group(2), m.group(3)
+    what = ATTN_MODES.get(mode, "")
+    if kind == "fwd" and extra in EXP_CORES:
+        what += f", exp2 core {EXP_CORES[extra]}"
+    return f"{kind} {what}"
+
+
+def attn_pass(path):
+    """{label: (summed counters over the label's dispatches, summed ns)} of one PMC pass"""
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    span = {}
+    for r in csv.DictReader(open(path)):
+        lab = attn_label(r["Kernel_Name"])
+        if not lab:
+            continue
+        per[lab][r["Counter_Name"]] += float(r["Counter_Value"])
+        span[(lab, r["Dispatch_Id"])] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    ns = collections.defaultdict(float)
+    for (lab, _), d in span.items():
+        ns[lab] += d
+    return {lab: (cs, ns[lab]) for lab, cs in per.items()}
+
+
+def attn_counters(paths, commands, out):
+    """paths / commands: the three PMC passes (wave states; MFMA and
+    instruction counts; L2 and LDS conflicts)."""
+    p1, p2, p3 = (attn_pass(p) for p in paths)
+    lines = ["# Attention kernels: MFMA busy, VALU issue and waits", "",
+             "PMC passes (one counter group per run, no tracing) over "
+             "`bench.py --components-only --component-set main --protocol quick` (softcap "
+             "attention 1 x 16 x 8192 x 128 causal, sigmoid attention 1 x 32 (8) x 4096 x 128 "
+             "causal, forward and backward):", "", "```"] + list(commands) + ["```", "",
+             "MFMA busy and MFMA/VALU co-execution: SQ_VALU_MFMA_BUSY_CYCLES and "
+             "SQ_VALU_MFMA_COEXEC_CYCLES over the dispatches' duration x 1,024 SIMDs x 2.4 GHz "
+             "(the peak clock, so a lower clock under the profiler would read lower). Per wave "
+             "(fractions of SQ_WAVE_CYCLES): VALU issue SQ_ACTIVE_INST_VALU, LDS issue "
+             "SQ_ACTIVE_INST_LDS, waiting on s_waitcnt SQ_WAIT_ANY, instruction-issue stalls "
+             "SQ_WAIT_INST_ANY. VALU / MFMA is SQ_INSTS_VALU / SQ_INSTS_MFMA. L2 hit rate "
+             "TCC_HIT / (TCC_HIT + TCC_MISS); LDS bank conflicts as cycles per LDS-active cycle.", "",
+             "| kernel | MFMA busy % | co-exec % | VALU issue % | LDS issue % | s_waitcnt % | "
+             "issue stall % | VALU / MFMA | L2 hit % | LDS conflict % |",
+             "|---|---|---|---|---|---|---|---|---|---|"]
+    for lab in sorted(set(p1) & set(p2) & set(p3)):
+        c1, _ = p1[lab]
+        c2, ns2 = p2[lab]
+        c3, _ = p3[lab]
+        simd_cycles = ns2 * 1e-9 * CLOCK_HZ * SIMDS
+        wc = max(c1.get("SQ_WAVE_CYCLES", 0.0), 1.0)
+        hit, miss = c3.get("TCC_HIT_sum", 0.0), c3.get("TCC_MISS_sum", 0.0)
+        lines.append(
+            f"| {lab} | {100 * c2.get('SQ_VALU_MFMA_BUSY_CYCLES', 0) / simd_cycles:.1f} | "
+            f"{100 * c2.get('SQ_VALU_MFMA_COEXEC_CYCLES', 0) / simd_cycles:.1f} | "
+            f"{100 * c1.get('SQ_ACTIVE_INST_VALU', 0) / wc:.1f} | "
+            f"{100 * c1.get('SQ_ACTIVE_INST_LDS', 0) / wc:.1f} | "
+            f"{100 * c1.get('SQ_WAIT_ANY', 0) / wc:.1f} | "
+            f"{100 * c1.get('SQ_WAIT_INST_ANY', 0) / wc:.1f} | "
+            f"{c2.get('SQ_INSTS_VALU', 0) / max(c2.get('SQ_INSTS_MFMA', 0), 1):.1f} | "
+            f"{100 * hit / max(hit + miss, 1):.1f} | "
+            f"{100 * c3.get('SQ_LDS_BANK_CONFLICT', 0) / max(c3.get('SQ_LDS_IDX_ACTIVE', 0), 1):.2f} |")
+    with open(os.path.join(out, "attention_counters.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--components", default="")
+    ap.add_argument("--attn-counters", nargs=6, default=None,
+                    metavar=("CSV1", "CSV2", "CSV3", "COMMAND1", "COMMAND2", "COMMAND3"),
+                    help="attention counter summary from three PMC passes")
     ap.add_argument("--counters", nargs=5, action="append", default=[],
                     metavar=("ELEMENTS", "VALU_CSV", "L2_CSV", "VALU_COMMAND", "L2_COMMAND"),
                     help="VALU busy / L2 hit rate summary for one step size (repeatable)")
@@ -167,6 +248,9 @@ def main():
     ap.add_argument("--write-command", default="")
     ap.add_argument("--out", default=os.path.join(ROOT, "profiles"))
     a = ap.parse_args()
+    if a.attn_counters:
+        attn_counters(a.attn_counters[:3], a.attn_counters[3:], a.out)
+        return
     if a.counters:
         counters([(int(c[0]),) + tuple(c[1:]) for c in a.counters], a.out)
         return
