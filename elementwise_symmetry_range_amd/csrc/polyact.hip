@@ -72,7 +72,7 @@ CoefBF16 coef_bf16(const ProgramDef &p)
     return k;
 }
 
-pa_status check_unary(pa_dtype t, const void *x, const void *y, int64_t n)
+pa_status check_unary(int32_t t, const void *x, const void *y, int64_t n)
 {
     if (t != PA_F16 && t != PA_BF16) return PA_ERR_DTYPE;
     if (n < 0) return PA_ERR_SHAPE;
@@ -83,7 +83,7 @@ pa_status check_unary(pa_dtype t, const void *x, const void *y, int64_t n)
     return PA_OK;
 }
 
-pa_status check_binary(pa_dtype t, const void *x, const void *g, const void *y, int64_t n)
+pa_status check_binary(int32_t t, const void *x, const void *g, const void *y, int64_t n)
 {
     pa_status s = check_unary(t, x, y, n);
     if (s != PA_OK) return s;
@@ -93,7 +93,7 @@ pa_status check_binary(pa_dtype t, const void *x, const void *g, const void *y, 
 }
 
 template <int F, int D>
-pa_status poly_fwd_dispatch(const ProgramDef &p, pa_dtype t, const void *x, void *y, int64_t n,
+pa_status poly_fwd_dispatch(const ProgramDef &p, int32_t t, const void *x, void *y, int64_t n,
                             hipStream_t st)
 {
     if (t == PA_F16) return run_map1(x, y, n, st, PolyFwdF16<F, D>{coef_f16(p)});
@@ -101,7 +101,7 @@ pa_status poly_fwd_dispatch(const ProgramDef &p, pa_dtype t, const void *x, void
 }
 
 template <int F, bool FROM_Y>
-pa_status native_bwd_dispatch(pa_dtype t, const void *x, const void *g, void *y, int64_t n,
+pa_status native_bwd_dispatch(int32_t t, const void *x, const void *g, void *y, int64_t n,
                               hipStream_t st)
 {
     if (t == PA_F16) return run_map2(x, g, y, n, st, NativeBwd<F, false, FROM_Y>{});
@@ -190,7 +190,7 @@ pa_status swiglu_bwd_launch(const SwiArgs &a, hipStream_t st, const Op &op)
     return launched();
 }
 
-pa_status swiglu_fwd_check(pa_dtype t, const void *gate, const void *up, void *h, int64_t rows,
+pa_status swiglu_fwd_check(int32_t t, const void *gate, const void *up, void *h, int64_t rows,
                            int64_t cols, int64_t ldg, int64_t ldu, int64_t ldh,
                            const int64_t *off, int32_t ng)
 {
@@ -209,7 +209,7 @@ pa_status swiglu_fwd_check(pa_dtype t, const void *gate, const void *up, void *h
     return PA_OK;
 }
 
-pa_status swiglu_bwd_check(pa_dtype t, const void *gate, const void *up, const void *dh,
+pa_status swiglu_bwd_check(int32_t t, const void *gate, const void *up, const void *dh,
                            void *dgate, void *dup, int64_t rows, int64_t cols, int64_t ldg,
                            int64_t ldu, int64_t lddh, int64_t lddg, int64_t lddu,
                            const int64_t *off, int32_t ng)
@@ -297,7 +297,7 @@ const char *pa_status_str(pa_status s)
     return "unknown status";
 }
 
-pa_status poly_program_info(pa_func f, int32_t deriv, pa_dtype t, pa_program *out)
+pa_status poly_program_info(int32_t f, int32_t deriv, int32_t t, pa_program *out)
 {
     if (!out) return PA_ERR_NULL;
     if (t != PA_F16 && t != PA_BF16) return PA_ERR_DTYPE;
@@ -334,7 +334,7 @@ pa_status poly_program_info(pa_func f, int32_t deriv, pa_dtype t, pa_program *ou
     return PA_OK;
 }
 
-pa_status poly_act_fwd(pa_func f, pa_dtype t, const void *x, void *y, int64_t n,
+pa_status poly_act_fwd(int32_t f, int32_t t, const void *x, void *y, int64_t n,
                        hipStream_t stream)
 {
     pa_status s = check_unary(t, x, y, n);
@@ -351,7 +351,7 @@ pa_status poly_act_fwd(pa_func f, pa_dtype t, const void *x, void *y, int64_t n,
     return PA_ERR_FUNC;
 }
 
-pa_status poly_act_bwd(pa_func f, pa_dtype t, const void *x, const void *dy, void *dx, int64_t n,
+pa_status poly_act_bwd(int32_t f, int32_t t, const void *x, const void *dy, void *dx, int64_t n,
                        hipStream_t stream)
 {
     pa_status s = check_binary(t, x, dy, dx, n);
@@ -375,7 +375,7 @@ pa_status poly_act_bwd(pa_func f, pa_dtype t, const void *x, const void *dy, voi
     return PA_ERR_FUNC;
 }
 
-pa_status native_act_fwd(pa_func f, pa_dtype t, const void *x, void *y, int64_t n,
+pa_status native_act_fwd(int32_t f, int32_t t, const void *x, void *y, int64_t n,
                          hipStream_t stream)
 {
     pa_status s = check_unary(t, x, y, n);
@@ -408,7 +408,7 @@ pa_status pa_stream_copy(const void *a, const void *b, void *y, int64_t n, hipSt
     return b ? run_map2(a, b, y, n, stream, XorOp{}) : run_map1(a, y, n, stream, CopyOp{});
 }
 
-pa_status native_act_bwd(pa_impl impl, pa_func f, pa_dtype t, const void *x_or_y, const void *dy,
+pa_status native_act_bwd(int32_t impl, int32_t f, int32_t t, const void *x_or_y, const void *dy,
                          void *dx, int64_t n, hipStream_t stream)
 {
     pa_status s = check_binary(t, x_or_y, dy, dx, n);
@@ -431,7 +431,7 @@ pa_status native_act_bwd(pa_impl impl, pa_func f, pa_dtype t, const void *x_or_y
     return PA_ERR_FUNC;
 }
 
-pa_status poly_swiglu_fwd(pa_dtype t, const void *gate, const void *up, void *h, int64_t rows,
+pa_status poly_swiglu_fwd(int32_t t, const void *gate, const void *up, void *h, int64_t rows,
                           int64_t cols, int64_t ld_gate, int64_t ld_up, int64_t ld_h,
                           const int64_t *row_offsets, int32_t n_groups, hipStream_t stream)
 {
@@ -444,7 +444,7 @@ pa_status poly_swiglu_fwd(pa_dtype t, const void *gate, const void *up, void *h,
     return swiglu_fwd_launch(a, stream, SwiPolyFwd{coef_bf16(sigmoid_d3())});
 }
 
-pa_status poly_swiglu_bwd(pa_dtype t, const void *gate, const void *up, const void *dh,
+pa_status poly_swiglu_bwd(int32_t t, const void *gate, const void *up, const void *dh,
                           void *dgate, void *dup, int64_t rows, int64_t cols, int64_t ld_gate,
                           int64_t ld_up, int64_t ld_dh, int64_t ld_dgate, int64_t ld_dup,
                           const int64_t *row_offsets, int32_t n_groups, hipStream_t stream)
@@ -458,7 +458,7 @@ pa_status poly_swiglu_bwd(pa_dtype t, const void *gate, const void *up, const vo
     return swiglu_bwd_launch(a, stream, SwiPolyBwd{coef_bf16(sigmoid_d3())});
 }
 
-pa_status native_swiglu_fwd(pa_dtype t, const void *gate, const void *up, void *h, int64_t rows,
+pa_status native_swiglu_fwd(int32_t t, const void *gate, const void *up, void *h, int64_t rows,
                             int64_t cols, int64_t ld_gate, int64_t ld_up, int64_t ld_h,
                             const int64_t *row_offsets, int32_t n_groups, hipStream_t stream)
 {
@@ -471,7 +471,7 @@ pa_status native_swiglu_fwd(pa_dtype t, const void *gate, const void *up, void *
     return swiglu_fwd_launch(a, stream, SwiNativeFwd{});
 }
 
-pa_status native_swiglu_bwd(pa_dtype t, const void *gate, const void *up, const void *dh,
+pa_status native_swiglu_bwd(int32_t t, const void *gate, const void *up, const void *dh,
                             void *dgate, void *dup, int64_t rows, int64_t cols, int64_t ld_gate,
                             int64_t ld_up, int64_t ld_dh, int64_t ld_dgate, int64_t ld_dup,
                             const int64_t *row_offsets, int32_t n_groups, hipStream_t stream)
@@ -494,7 +494,7 @@ pa_status poly_softcap_attn_fwd(const void *q, const void *k, const void *v, voi
 
 pa_status poly_softcap_attn_fwd_exp2(const void *q, const void *k, const void *v, void *o,
                                      float *lse, int32_t B, int32_t H, int32_t Hkv, int32_t S,
-                                     int32_t D, float cap, int32_t causal, pa_exp2_core core,
+                                     int32_t D, float cap, int32_t causal, int32_t core,
                                      hipStream_t stream)
 {
     return attn_fwd(AM_SOFTCAP_POLY, q, k, v, o, lse, B, H, Hkv, S, D, cap, causal, stream,

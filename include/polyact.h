@@ -72,6 +72,9 @@ typedef enum {
     PA_ERR_ALIGN = 7     /* a pointer is not 2-byte aligned                 */
 } pa_status;
 
+/* The functions take the codes below as int32_t, so a caller may pass any
+ * value: an unknown one is reported (PA_ERR_DTYPE / PA_ERR_FUNC), never
+ * acted on.  The enums name the valid codes. */
 typedef enum { PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
 typedef enum { PA_SIGMOID = 1, PA_TANH = 2, PA_SILU = 3, PA_GELU = 4 } pa_func;
 
@@ -120,7 +123,7 @@ typedef struct {
 /* y[i] = f~(x[i]), i < n.  f = PA_SIGMOID (D3), PA_TANH (D4), PA_SILU (D3,
  * reusing the sigmoid polynomial), PA_GELU (D5).  x, y: n elements of
  * dtype t.  Paper: section 3.1, Eqs. 2-6; Table 2 programs. */
-pa_status poly_act_fwd(pa_func f, pa_dtype t, const void *x, void *y, int64_t n,
+pa_status poly_act_fwd(int32_t f, int32_t t, const void *x, void *y, int64_t n,
                        hipStream_t stream);
 
 /* dx[i] = dy[i] * f~'(x[i]) with the direct derivative fit of f, evaluated
@@ -128,7 +131,7 @@ pa_status poly_act_fwd(pa_func f, pa_dtype t, const void *x, void *y, int64_t n,
  * 3.3; section 4.2 backward from x; Table 3).  f = PA_SILU (D3) or PA_GELU
  * (D5): the centered-odd form 1/2 + sign(x) q(t^), which keeps
  * f~'(x) + f~'(-x) = 1 (Eq. 9); dx = RN(dy * RN(1/2 + (q xor sign))). */
-pa_status poly_act_bwd(pa_func f, pa_dtype t, const void *x, const void *dy,
+pa_status poly_act_bwd(int32_t f, int32_t t, const void *x, const void *dy,
                        void *dx, int64_t n, hipStream_t stream);
 
 /* Fused SwiGLU forward, BF16 only: h = SiLU~(g) * u with SiLU~(g) = g p(g)
@@ -141,7 +144,7 @@ pa_status poly_act_bwd(pa_func f, pa_dtype t, const void *x, const void *dy,
  * device and processes rows [row_offsets[0], row_offsets[n_groups]),
  * clipped to [0, rows): `rows` is the buffer's capacity, so the caller never
  * synchronises to learn the routed row count.  Rows outside are untouched. */
-pa_status poly_swiglu_fwd(pa_dtype t, const void *gate, const void *up, void *h,
+pa_status poly_swiglu_fwd(int32_t t, const void *gate, const void *up, void *h,
                           int64_t rows, int64_t cols, int64_t ld_gate, int64_t ld_up,
                           int64_t ld_h, const int64_t *row_offsets, int32_t n_groups,
                           hipStream_t stream);
@@ -151,7 +154,7 @@ pa_status poly_swiglu_fwd(pa_dtype t, const void *gate, const void *up, void *h,
  *   ds = RN_f32(g p (1 - p) + p),  dup = RN_bf16(dh * RN_f32(g p)),
  *   dgate = RN_bf16(RN_f32(RN_f32(dh u) * ds)).
  * Row selection as in poly_swiglu_fwd. */
-pa_status poly_swiglu_bwd(pa_dtype t, const void *gate, const void *up, const void *dh,
+pa_status poly_swiglu_bwd(int32_t t, const void *gate, const void *up, const void *dh,
                           void *dgate, void *dup, int64_t rows, int64_t cols,
                           int64_t ld_gate, int64_t ld_up, int64_t ld_dh,
                           int64_t ld_dgate, int64_t ld_dup, const int64_t *row_offsets,
@@ -198,7 +201,7 @@ typedef enum { PA_EXP2_HW = 0, PA_EXP2_D1 = 1, PA_EXP2_PWL2 = 2, PA_EXP2_D2 = 3,
                PA_EXP2_D3 = 4 } pa_exp2_core;
 pa_status poly_softcap_attn_fwd_exp2(const void *q, const void *k, const void *v, void *o,
                                      float *lse, int32_t B, int32_t H, int32_t Hkv, int32_t S,
-                                     int32_t D, float cap, int32_t causal, pa_exp2_core core,
+                                     int32_t D, float cap, int32_t causal, int32_t core,
                                      hipStream_t stream);
 
 /* Softcapped attention backward: given the forward's O and lse and the
@@ -251,22 +254,22 @@ pa_status poly_sigmoid_attn_bwd(const void *q, const void *k, const void *v, con
 /* y = f(x) with accurate FP32 math (sigmoid 1/(1+e^-|x|) in the overflow-safe
  * form, tanhf, SiLU (x >= 0 ? x : x e) / (1 + e) with e = expf(-|x|), GELU
  * x erfc(-x / sqrt 2) / 2), rounded once to dtype t. */
-pa_status native_act_fwd(pa_func f, pa_dtype t, const void *x, void *y, int64_t n,
+pa_status native_act_fwd(int32_t f, int32_t t, const void *x, void *y, int64_t n,
                          hipStream_t stream);
 
 /* Backward comparators.  impl = PA_IMPL_NATIVE: x_or_y is x and the derivative
  * is recomputed accurately from x (all four functions; SiLU' = sigma (1 +
  * x sigma(-x)), GELU' = Phi + x phi); impl = PA_IMPL_NATIVE_FROM_Y: x_or_y is
  * the saved forward output y (Eqs. 10-11), PA_SIGMOID and PA_TANH only. */
-pa_status native_act_bwd(pa_impl impl, pa_func f, pa_dtype t, const void *x_or_y,
+pa_status native_act_bwd(int32_t impl, int32_t f, int32_t t, const void *x_or_y,
                          const void *dy, void *dx, int64_t n, hipStream_t stream);
 
 /* SwiGLU with accurate FP32 SiLU (arguments as poly_swiglu_fwd / _bwd). */
-pa_status native_swiglu_fwd(pa_dtype t, const void *gate, const void *up, void *h,
+pa_status native_swiglu_fwd(int32_t t, const void *gate, const void *up, void *h,
                             int64_t rows, int64_t cols, int64_t ld_gate, int64_t ld_up,
                             int64_t ld_h, const int64_t *row_offsets, int32_t n_groups,
                             hipStream_t stream);
-pa_status native_swiglu_bwd(pa_dtype t, const void *gate, const void *up, const void *dh,
+pa_status native_swiglu_bwd(int32_t t, const void *gate, const void *up, const void *dh,
                             void *dgate, void *dup, int64_t rows, int64_t cols,
                             int64_t ld_gate, int64_t ld_up, int64_t ld_dh,
                             int64_t ld_dgate, int64_t ld_dup, const int64_t *row_offsets,
@@ -308,7 +311,7 @@ pa_status pa_stream_copy(const void *a, const void *b, void *y, int64_t n, hipSt
 
 /* The program the kernels execute for (f, deriv, t).  Returns PA_ERR_FUNC if
  * there is none, PA_ERR_NULL if out is NULL. */
-pa_status poly_program_info(pa_func f, int32_t deriv, pa_dtype t, pa_program *out);
+pa_status poly_program_info(int32_t f, int32_t deriv, int32_t t, pa_program *out);
 
 /* The sigmoid-attention program (BF16 bit patterns): region threshold, clamp
  * bounds, coeff_bits[r][j] = coefficient of x^j in region r (r = 1 when
