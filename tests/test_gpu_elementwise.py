@@ -219,3 +219,26 @@ def test_stream_copy_reference(pa):
         at, bt = to_dev(a, torch.float16)[off:off + n], to_dev(b, torch.float16)[off:off + n]
         assert np.array_equal(to_bits(pa.stream_copy(at)), a[off:off + n])
         assert np.array_equal(to_bits(pa.stream_copy(at, bt)), a[off:off + n] ^ b[off:off + n])
+
+
+@pytest.mark.parametrize("extra", [-3, 13])
+def test_launch_shape_boundary(pa, orc, progs, extra):
+    """The streaming launches change block size at 2^23 16-byte chunks per
+    stream (67,108,864 FP16 elements): just below it (2^23 - 1 chunks) and
+    just above it (2^23 + 1 chunks), each with a 5-element tail, the forward
+    and backward programs equal the oracle on every 31st element and on the
+    last 4,096."""
+    n = (1 << 26) + extra
+    rng = np.random.default_rng(40 + extra)
+    x = rng.integers(0, 65536, n, dtype=np.uint16)
+    g = rng.integers(0, 65536, n, dtype=np.uint16)
+    note(f"launch boundary n={n}")
+    xt, gt = to_dev(x, torch.float16), to_dev(g, torch.float16)
+    idx = np.concatenate([np.arange(0, n, 31), np.arange(n - 4096, n)])
+    it = torch.from_numpy(idx).cuda()
+    got = to_bits(pa.poly_act_fwd(xt, "sigmoid")[it])
+    ref = orc.act_fwd(progs[fwd_prog_name("sigmoid")], x[idx], 1)
+    assert np.array_equal(got, ref), diff_report(got, ref, x[idx])
+    got = to_bits(pa.poly_act_bwd(xt, gt, "tanh")[it])
+    ref = orc.act_bwd(progs[bwd_prog_name("tanh")], x[idx], g[idx], 1)
+    assert np.array_equal(got, ref), diff_report(got, ref, x[idx])

@@ -149,3 +149,27 @@ def test_native_swiglu_close(pa, orc, sig):
     ref = si.to_bf16_bits(gv * expit(gv) * uv)
     key = lambda b: np.where(b & 0x8000, -(b.astype(np.int64) & 0x7FFF), b.astype(np.int64))  # noqa: E731
     assert np.abs(key(h) - key(ref)).max() <= 1
+
+
+@pytest.mark.parametrize("cols", [8192, 8200])
+def test_launch_shape_boundary(pa, orc, sig, cols):
+    """Dense SwiGLU on both sides of the 2^23-chunk launch switch: 8192 rows
+    of 8192 columns (exactly 2^23 16-byte chunks per stream) and of 8200
+    (2^23 + 8192); forward and backward equal the oracle on sampled rows."""
+    R = 8192
+    rng = np.random.default_rng(cols)
+    g = rng.integers(0, 65536, (R, cols), dtype=np.uint16)
+    u = rng.integers(0, 65536, (R, cols), dtype=np.uint16)
+    d = rng.integers(0, 65536, (R, cols), dtype=np.uint16)
+    note(f"swiglu launch boundary {R}x{cols}")
+    gt, ut, dt = to_dev(g, BF), to_dev(u, BF), to_dev(d, BF)
+    h = pa.poly_swiglu_fwd(gt, ut)
+    dg, du = pa.poly_swiglu_bwd(gt, ut, dt)
+    rows = np.array([0, 1, 2047, 4096, 8190, 8191])
+    rt = torch.from_numpy(rows).cuda()
+    got = (to_bits(h[rt]), to_bits(dg[rt]), to_bits(du[rt]))
+    rh = orc.swiglu_fwd(sig, g[rows], u[rows])
+    rdg, rdu = orc.swiglu_bwd(sig, g[rows], u[rows], d[rows])
+    for a, b in zip(got, (rh, rdg, rdu)):
+        ok, msg = same(a, b)
+        assert ok, msg
