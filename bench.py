@@ -452,8 +452,12 @@ def main():
         # replays of n launches: the same number of calls per round as above
         tp, tn = alternating(torch, gp, gn, max(1, ic // n), ir, max(1, iw // n))
         tp, tn = tp / n, tn / n
+        by = 4 if name.endswith("_fwd") else 6
+        # share of the HBM peak the working set would need from HBM; the
+        # 16-24 MiB per call sit in the caches, so this may exceed 100 %
         l2[name] = {"poly_gelem_s": round(N_L2 / tp / 1e6, 1), "speedup": round(tn / tp, 3),
-                    "poly_us": round(1e3 * tp, 2), "native_us": round(1e3 * tn, 2)}
+                    "poly_us": round(1e3 * tp, 2), "native_us": round(1e3 * tn, 2),
+                    "pct_hbm": round(100 * by * N_L2 / tp / 1e6 / HBM_PEAK_GBS, 1)}
     # the cache-resident copy ceiling: the same streaming kernels with no
     # arithmetic at 4M, graphed the same way
     (g1, n), (g2, _) = (graphed(lambda: pa.stream_copy(xs, out=ys)),
