@@ -222,6 +222,8 @@ def _swiglu_fwd(entry, gate, up, out, row_offsets):
         raise ValueError("up must match gate")
     h = torch.empty_like(gate) if out is None else out
     ldh = _mat(h, "out")
+    if h.shape != gate.shape:   # the kernel writes rows x cols through out
+        raise ValueError("out must match gate")
     off, ng = _offsets(row_offsets)
     rows, cols = gate.shape
     _call(entry, 2, gate.data_ptr(), up.data_ptr(), h.data_ptr(), rows, cols, ldg, ldu, ldh, off,
@@ -235,6 +237,8 @@ def _swiglu_bwd(entry, gate, up, dh, out, row_offsets):
         raise ValueError("up and dh must match gate")
     dg, du = (torch.empty_like(gate), torch.empty_like(gate)) if out is None else out
     lddg, lddu = _mat(dg, "dgate"), _mat(du, "dup")
+    if dg.shape != gate.shape or du.shape != gate.shape:   # written rows x cols
+        raise ValueError("dgate and dup must match gate")
     off, ng = _offsets(row_offsets)
     rows, cols = gate.shape
     _call(entry, 2, gate.data_ptr(), up.data_ptr(), dh.data_ptr(), dg.data_ptr(), du.data_ptr(),
@@ -343,8 +347,9 @@ def _ws(workspace, softcap, B, H, Hkv, S, D, device):
     need = lib().pa_attn_bwd_workspace_bytes(int(bool(softcap)), B, H, Hkv, S, D)
     if workspace is None:
         return attn_bwd_workspace(softcap, B, H, Hkv, S, D, device)
-    if workspace.dtype != torch.float32 or workspace.numel() * 4 < need or not workspace.is_cuda:
-        raise ValueError(f"workspace must be a float32 CUDA tensor of at least {need} bytes")
+    if (workspace.dtype != torch.float32 or workspace.numel() * 4 < need or not workspace.is_cuda
+            or not workspace.is_contiguous()):
+        raise ValueError(f"workspace must be a contiguous float32 CUDA tensor of at least {need} bytes")
     return workspace
 
 

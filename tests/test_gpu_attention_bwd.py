@@ -179,3 +179,14 @@ def test_edge_lengths_and_wide_groups(pa, orc, tp, sp, S):
     for causal in (True, False):
         softcap_case(pa, orc, tp, 1, 8, 1, S, causal, True, 95 + S)
         sigmoid_case(pa, orc, sp, 1, 8, 1, S, causal, False, 96 + S)
+
+
+def test_workspace_must_be_contiguous(pa):
+    import synth_inputs as si
+    q, k, v = si.t_attn_inputs(1, 2, 64, 128)
+    dout = si.t_attn_grad(1, 2, 64, 128)
+    o, lse = pa.poly_softcap_attn_fwd(q, k, v, 50.0, True, with_lse=True)
+    need = pa.attn_bwd_workspace(True, 1, 2, 2, 64, 128, device=q.device).numel()
+    strided = torch.empty(2 * need, dtype=torch.float32, device=q.device)[::2]
+    with pytest.raises(ValueError):
+        pa.poly_softcap_attn_bwd(q, k, v, o, dout, lse, 50.0, True, workspace=strided)

@@ -173,3 +173,16 @@ def test_launch_shape_boundary(pa, orc, sig, cols):
     for a, b in zip(got, (rh, rdg, rdu)):
         ok, msg = same(a, b)
         assert ok, msg
+
+
+def test_output_shape_checked(pa):
+    """The kernels write rows x cols through the output pointers, so outputs
+    of another shape are refused before any launch."""
+    g = torch.zeros(64, 128, dtype=BF, device="cuda")
+    small = torch.zeros(32, 128, dtype=BF, device="cuda")
+    with pytest.raises(ValueError):
+        pa.poly_swiglu_fwd(g, g, out=small)
+    with pytest.raises(ValueError):
+        pa.poly_swiglu_bwd(g, g, g, out=(small, torch.zeros_like(g)))
+    with pytest.raises(ValueError):
+        pa.native_swiglu_bwd(g, g, g, out=(torch.zeros_like(g), small))
