@@ -434,10 +434,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             }
         }
 
-        // s[qb][j*4 + i] is query r0 + qb*32 + j*8 + h*4 + i of this lane's key
+        // a masked tile (the causal diagonal or the ragged end; every other
+        // tile takes slotted_tile): s[qb][j*4 + i] is query r0 + qb*32 + j*8 +
+        // h*4 + i of this lane's key
         bf16x8 pf[4] = {}, dsf[4] = {};
-        auto transform = [&](auto masked) {
-            constexpr bool MASKED = decltype(masked)::value;
+        {
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
@@ -456,14 +457,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                         bwd_pair<MODE>(a, s[qb][e], s[qb][e + 1], dp[qb][e], dp[qb][e + 1], nl4[i],
                                        nl4[i + 1], dl4[i], dl4[i + 1], p0, p1, d0, d1);
                         uint32_t pk = pack_bf(p0, p1), dk2 = pack_bf(d0, d1);
-                        if constexpr (MASKED) {
-                            const int q = r0 + qb * 32 + j * 8 + h * 4 + i;
-                            const bool vis0 = q < S && (!a.causal || q >= my_k);
-                            const bool vis1 = q + 1 < S && (!a.causal || q + 1 >= my_k);
-                            const uint32_t keep = (vis0 ? 0x0000FFFFu : 0u) | (vis1 ? 0xFFFF0000u : 0u);
-                            pk &= keep;
-                            dk2 &= keep;
-                        }
+                        const int q = r0 + qb * 32 + j * 8 + h * 4 + i;
+                        const bool vis0 = q < S && (!a.causal || q >= my_k);
+                        const bool vis1 = q + 1 < S && (!a.causal || q + 1 >= my_k);
+                        const uint32_t keep = (vis0 ? 0x0000FFFFu : 0u) | (vis1 ? 0xFFFF0000u : 0u);
+                        pk &= keep;
+                        dk2 &= keep;
                         pw[i >> 1] = pk;
                         dw[i >> 1] = dk2;
                     }
@@ -480,8 +479,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                     dsf[f] = bc<bf16x8>(dv4);
                 }
             }
-        };
-        transform(std::true_type{});
+        }
 
         // dV^T += dO^T P,  dK^T += Q^T dS
 #pragma unroll
