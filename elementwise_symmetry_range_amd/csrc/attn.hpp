@@ -191,8 +191,10 @@ __device__ __forceinline__ uint32_t sigmoid_poly_pair(float s0, float s1, float 
     // every value BF16-rounded per lane (rn_bf16: one instruction, no unpack)
     const float x0 = rn_bf16(s0 * scale), x1 = rn_bf16(s1 * scale);
     const int r0 = x0 >= k.thr, r1 = x1 >= k.thr;
-    const float t0 = fminf(fmaxf(x0, k.lo), k.hi);
-    const float t1 = fminf(fmaxf(x1, k.lo), k.hi);
+    // clamp to [lo, hi] as one median of three (lo < hi; the same value as
+    // min(max(x, lo), hi) for every finite score)
+    const float t0 = __builtin_amdgcn_fmed3f(x0, k.lo, k.hi);
+    const float t1 = __builtin_amdgcn_fmed3f(x1, k.lo, k.hi);
     float v0 = r0 ? k.c[1][3] : k.c[0][3];
     float v1 = r1 ? k.c[1][3] : k.c[0][3];
 #pragma unroll
