@@ -198,12 +198,15 @@ __device__ __forceinline__ uint32_t sigmoid_poly_pair(float s0, float s1, float 
     float v0 = r0 ? k.c[1][3] : k.c[0][3];
     float v1 = r1 ? k.c[1][3] : k.c[0][3];
 #pragma unroll
-    for (int j = 2; j >= 0; --j) {
+    for (int j = 2; j >= 1; --j) {
         v0 = rn_bf16(fmaf(t0, v0, r0 ? k.c[1][j] : k.c[0][j]));
         v1 = rn_bf16(fmaf(t1, v1, r1 ? k.c[1][j] : k.c[0][j]));
     }
-    v0 = fmaxf(v0, 0.0f);
-    v1 = fmaxf(v1, 0.0f);
+    // The program's value lies below 0.06 for every input, so clamping the
+    // last FMA to [0, 1] before its rounding gives max(value, 0) after it;
+    // the clamp is the FMA's output modifier (no instruction of its own).
+    v0 = rn_bf16(__builtin_amdgcn_fmed3f(fmaf(t0, v0, r0 ? k.c[1][0] : k.c[0][0]), 0.0f, 1.0f));
+    v1 = rn_bf16(__builtin_amdgcn_fmed3f(fmaf(t1, v1, r1 ? k.c[1][0] : k.c[0][0]), 0.0f, 1.0f));
     if constexpr (GRAD) {
         const float f0 = rn_bf16(fmaf(t0, r0 ? k.b[1] : k.b[0], r0 ? k.a[1] : k.a[0]));
         const float f1 = rn_bf16(fmaf(t1, r1 ? k.b[1] : k.b[0], r1 ? k.a[1] : k.a[0]));

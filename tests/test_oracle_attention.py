@@ -251,6 +251,19 @@ def test_b3_program_against_closed_form(orc, sig_prog, order):
     assert abs(r[1] - r[0]) / r[1] < 0.02
 
 
+@pytest.mark.parametrize("order", [2, 3])
+def test_b3_program_range(orc, sig_prog, order):
+    """Over every finite BF16 input the program's value lies in [0, 0.06):
+    the attention kernels clamp its last FMA to [0, 1] before rounding in
+    place of the floor at zero after it, which is the same value only when
+    the program never reaches 1."""
+    allx = np.arange(65536, dtype=np.uint16)
+    allx = allx[np.isfinite(bf16v(allx))]
+    p, _ = orc.sig_prog_eval(sig_prog, allx, order)
+    pv = bf16v(p)
+    assert np.all(pv >= 0) and np.max(pv) < 0.06
+
+
 def test_dtanh_program_is_derivative_of_tanh_program(orc, tanh_prog):
     """q(x) = p'(min(|x|, Lc)) in FP16: against a central difference of the
     real polynomial (orc_prog_real), to FP16 Horner accuracy."""
