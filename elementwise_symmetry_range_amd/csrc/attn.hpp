@@ -76,10 +76,14 @@ constexpr float AT_LOG2E = 1.442695040888963407f;
 enum { AM_SOFTCAP_POLY = 0, AM_SOFTCAP_NATIVE = 1, AM_SIGMOID_POLY = 2, AM_SIGMOID_NATIVE = 3 };
 __host__ __device__ constexpr bool am_softcap(int m) { return m == AM_SOFTCAP_POLY || m == AM_SOFTCAP_NATIVE; }
 
-// two-region sigmoid program as FP32 values of its BF16 constants
+// two-region sigmoid program: threshold and clamp bounds as FP32 values of
+// their BF16 constants; the coefficients as FP16 pairs (each BF16 coefficient
+// is an FP16 value, checked at compile time), one pair of region r per word,
+// so that one per-lane select fetches two of them
 struct SigCoef {
-    float c[2][4];
-    float a[2], b[2];
+    uint32_t c23[2];   // c2 (low half), c3 (high half)
+    uint32_t c01[2];   // c0 (low), c1 (high)
+    uint32_t ab[2];    // a (low), b (high) of the derivative surrogate
     float thr, lo, hi;
 };
 
@@ -182,6 +186,30 @@ __device__ __forceinline__ uint32_t softcap_poly_pair(float s0, float s1, float 
     return bc<uint32_t>(v) ^ (xw ^ aw);
 }
 
+// FP32 FMAs with FP16 operands taken from the halves of a packed word
+// (v_fma_mix_f32: the halves convert to FP32 exactly, one rounding)
+// t * high(w) + low(w)
+__device__ __forceinline__ float fma_mix_pair(float t, uint32_t w)
+{
+    float r;
+    asm("v_fma_mix_f32 %0, %1, %2, %2 op_sel:[0,1,0] op_sel_hi:[0,1,1]" : "=v"(r) : "v"(t), "v"(w));
+    return r;
+}
+// t * v + high(w)
+__device__ __forceinline__ float fma_mix_add_hi(float t, float v, uint32_t w)
+{
+    float r;
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[0,0,1] op_sel_hi:[0,0,1]" : "=v"(r) : "v"(t), "v"(v), "v"(w));
+    return r;
+}
+// t * v + low(w), clamped to [0, 1]
+__device__ __forceinline__ float fma_mix_add_lo_clamp(float t, float v, uint32_t w)
+{
+    float r;
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel_hi:[0,0,1] clamp" : "=v"(r) : "v"(t), "v"(v), "v"(w));
+    return r;
+}
+
 // sigmoid program on a pair: packed BF16 P~ (and the packed BF16 surrogate
 // derivative when GRAD)
 template <bool GRAD>
@@ -195,21 +223,22 @@ __device__ __forceinline__ uint32_t sigmoid_poly_pair(float s0, float s1, float 
     // min(max(x, lo), hi) for every finite score)
     const float t0 = __builtin_amdgcn_fmed3f(x0, k.lo, k.hi);
     const float t1 = __builtin_amdgcn_fmed3f(x1, k.lo, k.hi);
-    float v0 = r0 ? k.c[1][3] : k.c[0][3];
-    float v1 = r1 ? k.c[1][3] : k.c[0][3];
-#pragma unroll
-    for (int j = 2; j >= 1; --j) {
-        v0 = rn_bf16(fmaf(t0, v0, r0 ? k.c[1][j] : k.c[0][j]));
-        v1 = rn_bf16(fmaf(t1, v1, r1 ? k.c[1][j] : k.c[0][j]));
-    }
-    // The program's value lies below 0.06 for every input, so clamping the
-    // last FMA to [0, 1] before its rounding gives max(value, 0) after it;
-    // the clamp is the FMA's output modifier (no instruction of its own).
-    v0 = rn_bf16(__builtin_amdgcn_fmed3f(fmaf(t0, v0, r0 ? k.c[1][0] : k.c[0][0]), 0.0f, 1.0f));
-    v1 = rn_bf16(__builtin_amdgcn_fmed3f(fmaf(t1, v1, r1 ? k.c[1][0] : k.c[0][0]), 0.0f, 1.0f));
+    // Horner in FP32 FMAs with FP16 coefficient operands (exact conversions,
+    // so each stage is the FP32 FMA of the BF16 constants), each rounded to
+    // BF16: c3 t + c2, then + c1, then + c0.  The program's value lies below
+    // 0.06 for every input, so the last FMA's [0, 1] clamp before its
+    // rounding is max(value, 0) after it.
+    const uint32_t w0 = r0 ? k.c23[1] : k.c23[0], w1 = r1 ? k.c23[1] : k.c23[0];
+    const uint32_t u0 = r0 ? k.c01[1] : k.c01[0], u1 = r1 ? k.c01[1] : k.c01[0];
+    float v0 = rn_bf16(fma_mix_pair(t0, w0)), v1 = rn_bf16(fma_mix_pair(t1, w1));
+    v0 = rn_bf16(fma_mix_add_hi(t0, v0, u0));
+    v1 = rn_bf16(fma_mix_add_hi(t1, v1, u1));
+    v0 = rn_bf16(fma_mix_add_lo_clamp(t0, v0, u0));
+    v1 = rn_bf16(fma_mix_add_lo_clamp(t1, v1, u1));
     if constexpr (GRAD) {
-        const float f0 = rn_bf16(fmaf(t0, r0 ? k.b[1] : k.b[0], r0 ? k.a[1] : k.a[0]));
-        const float f1 = rn_bf16(fmaf(t1, r1 ? k.b[1] : k.b[0], r1 ? k.a[1] : k.a[0]));
+        const uint32_t z0 = r0 ? k.ab[1] : k.ab[0], z1 = r1 ? k.ab[1] : k.ab[0];
+        const float f0 = rn_bf16(fma_mix_pair(t0, z0));   // b t + a
+        const float f1 = rn_bf16(fma_mix_pair(t1, z1));
         *grad = pack_bf(v0 * f0, v1 * f1);
     }
     return pack_bf(v0, v1);   // exact: v0, v1 are BF16 values

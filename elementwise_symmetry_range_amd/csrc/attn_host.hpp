@@ -86,14 +86,54 @@ inline void tanh_coefs(CoefF16 &fwd, CoefF16 &der)
     fwd.lc = der.lc = f16_dup(p->Lc);
 }
 
+// The FP16 encoding of a BF16 value, or -1 when FP16 cannot hold it exactly.
+// A finite nonzero BF16 value is (128 + m) 2^(e - 7) with a 7-bit m; FP16
+// holds it as a normal number for -14 <= e <= 15 and, below, as a multiple
+// of 2^-24 when the low bits that would fall off are zero.
+constexpr int32_t bf16_as_f16(uint16_t b)
+{
+    const uint32_t s = uint32_t(b >> 15), E = (b >> 7) & 0xFFu, m = b & 0x7Fu;
+    if (E == 0 && m == 0) return int32_t(s << 15);
+    if (E == 0 || E == 0xFF) return -1;
+    const int e = int(E) - 127;
+    if (e > 15) return -1;
+    if (e >= -14) return int32_t((s << 15) | (uint32_t(e + 15) << 10) | (m << 3));
+    uint32_t n = 128 + m;              // units of 2^(e - 7); FP16 subnormals count 2^-24
+    const int sh = e - 7 + 24;
+    if (sh >= 0) {
+        n <<= sh;
+    } else {
+        if (n & ((1u << -sh) - 1)) return -1;
+        n >>= -sh;
+    }
+    return int32_t((s << 15) | n);     // n < 1024 here
+}
+
+constexpr bool sigmoid_coefs_are_f16()
+{
+    for (int r = 0; r < 2; ++r) {
+        for (int j = 0; j < 4; ++j)
+            if (bf16_as_f16(kSigmoidAttn.c[r][j]) < 0) return false;
+        if (bf16_as_f16(kSigmoidAttn.a[r]) < 0 || bf16_as_f16(kSigmoidAttn.b[r]) < 0) return false;
+    }
+    return true;
+}
+static_assert(sigmoid_coefs_are_f16(), "the sigmoid kernels read the coefficients as FP16");
+static_assert(bf16_as_f16(0x3F80) == 0x3C00 && bf16_as_f16(0x37E8) == 0x01D0 &&
+              bf16_as_f16(0xB380) == 0x8001 && bf16_as_f16(0x3381) == -1,
+              "BF16 to FP16: normal, subnormal and inexact cases");
+
 inline SigCoef sigmoid_coefs()
 {
     const SigmoidAttnDef &d = kSigmoidAttn;
+    auto pair = [](uint16_t lo, uint16_t hi) {
+        return uint32_t(uint16_t(bf16_as_f16(lo))) | (uint32_t(uint16_t(bf16_as_f16(hi))) << 16);
+    };
     SigCoef k{};
     for (int r = 0; r < 2; ++r) {
-        for (int j = 0; j < 4; ++j) k.c[r][j] = bf16_value(d.c[r][j]);
-        k.a[r] = bf16_value(d.a[r]);
-        k.b[r] = bf16_value(d.b[r]);
+        k.c23[r] = pair(d.c[r][2], d.c[r][3]);
+        k.c01[r] = pair(d.c[r][0], d.c[r][1]);
+        k.ab[r] = pair(d.a[r], d.b[r]);
     }
     k.thr = bf16_value(d.thr);
     k.lo = bf16_value(d.lo);
