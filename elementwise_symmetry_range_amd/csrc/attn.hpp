@@ -113,6 +113,25 @@ __device__ __forceinline__ void static_for(F &&f)
     if constexpr (N > 0) static_for_seq(f, std::make_integer_sequence<int, N>{});
 }
 
+// Buffer B (compile time, 0 or 1) of an LDS double buffer, held either as
+// two LDS arrays (SPLIT) or as one [2][N] array.  The compiler gives every
+// LDS variable its own alias scope: with two arrays it can tell that a
+// global-to-LDS load into one buffer does not write what a read of the other
+// buffer reads, and does not wait for the load before the read.  That frees
+// the schedule (a gain where the kernel has registers to spare) but raises
+// the register count (a loss, or spills, where it has none); the kernels
+// choose per mode.  The unused declaration is dropped by the compiler.
+template <int B, bool SPLIT, class T, int N>
+__device__ __forceinline__ T *dbuf(T *b0, T *b1, T (&pair)[2][N])
+{
+    if constexpr (SPLIT) {
+        if constexpr (B == 0) return b0;
+        else return b1;
+    } else {
+        return pair[B];
+    }
+}
+
 __device__ __forceinline__ bf16x8 ld_bf16x8(const uint16_t *p) { return *(const bf16x8 *)p; }
 
 // slot of 16-byte chunk c of LDS row r (rows are 256 B, 16 chunks)
@@ -335,8 +354,11 @@ template <int MODE, int EXP = 0, bool SREF = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_fwd(AttnArgs a)
 {
     constexpr bool SOFTCAP = am_softcap(MODE);
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[2][AT_TILE];
-    __shared__ __attribute__((aligned(16))) uint16_t Vs[2][AT_TILE];
+    // K and V double buffers (see dbuf): separate arrays except for the
+    // softcap with the hardware exponential, which runs 1-2 % slower with them
+    constexpr bool SPLIT_LDS = !(SOFTCAP && EXP == 0);
+    __shared__ __attribute__((aligned(16))) uint16_t Ks0[AT_TILE], Ks1[AT_TILE], Kp[2][AT_TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t Vs0[AT_TILE], Vs1[AT_TILE], Vp[2][AT_TILE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -609,16 +631,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     };
 
     // ---- periods: p = 0 .. nkt; period p runs stages 2p - 1 and 2p --------
-    load_rows64(K, Ks[0], 0, S, wave, lane);
+    load_rows64(K, dbuf<0, SPLIT_LDS>(Ks0, Ks1, Kp), 0, S, wave, lane);
     auto period = [&](int p, auto bufc) __attribute__((always_inline)) {
-        constexpr int kb = decltype(bufc)::value;    // K tile p in Ks[kb], V tile p - 1 in Vs[kb ^ 1]
+        constexpr int kb = decltype(bufc)::value;    // K tile p in buffer kb, V tile p - 1 in buffer kb ^ 1
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's loads of K p / V p - 1 landed
-        __syncthreads();   // everybody's landed; nobody reads Ks[kb ^ 1] / Vs[kb] any more
-        if (p + 1 < nkt) load_rows64(K, Ks[kb ^ 1], (p + 1) * AT_BN, S, wave, lane);
-        if (p < nkt) load_rows64(V, Vs[kb], p * AT_BN, S, wave, lane);
+        __syncthreads();   // everybody's landed; nobody reads K buffer kb ^ 1 / V buffer kb any more
+        uint16_t *const Kc = dbuf<kb, SPLIT_LDS>(Ks0, Ks1, Kp), *const Kn = dbuf<kb ^ 1, SPLIT_LDS>(Ks0, Ks1, Kp);
+        uint16_t *const Vc = dbuf<kb ^ 1, SPLIT_LDS>(Vs0, Vs1, Vp), *const Vn = dbuf<kb, SPLIT_LDS>(Vs0, Vs1, Vp);
+        if (p + 1 < nkt) load_rows64(K, Kn, (p + 1) * AT_BN, S, wave, lane);
+        if (p < nkt) load_rows64(V, Vn, p * AT_BN, S, wave, lane);
         if (2 * p - 1 > nu) return;   // this wave is done (still takes part in the barriers)
-        stage(2 * p - 1, Ks[kb], Vs[kb ^ 1], std::integral_constant<int, 0>{});
-        stage(2 * p, Ks[kb], Vs[kb ^ 1], std::integral_constant<int, 1>{});
+        stage(2 * p - 1, Kc, Vc, std::integral_constant<int, 0>{});
+        stage(2 * p, Kc, Vc, std::integral_constant<int, 1>{});
     };
     for (int p = 0; p <= nkt; p += 2) {
         period(p, std::integral_constant<int, 0>{});

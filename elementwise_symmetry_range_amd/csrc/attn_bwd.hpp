@@ -99,6 +99,7 @@ template <int MODE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_bwd_dq(AttnBwdArgs a)
 {
     constexpr bool SOFTCAP = am_softcap(MODE);
+    // one [2][tile] array each (see dbuf: separate arrays make this kernel spill)
     __shared__ __attribute__((aligned(16))) uint16_t Ks[2][AT_TILE];
     __shared__ __attribute__((aligned(16))) uint16_t Vs[2][AT_TILE];
 
@@ -251,10 +252,13 @@ template <int MODE, bool SPLIT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_attn_bwd_dkdv(AttnBwdArgs a)
 {
     constexpr bool SOFTCAP = am_softcap(MODE);
-    __shared__ __attribute__((aligned(16))) uint16_t Qs[2][AT_TILE];
-    __shared__ __attribute__((aligned(16))) uint16_t Ds[2][AT_TILE];
-    __shared__ __attribute__((aligned(16))) float Ls[2][AT_BQ];   // -lse * log2(e)
-    __shared__ __attribute__((aligned(16))) float Es[2][AT_BQ];   // Delta
+    // double buffers (see dbuf): separate arrays except for the softcap
+    // comparator, whose tanh needs the registers (it spills with them)
+    constexpr bool SPLIT_LDS = MODE != AM_SOFTCAP_NATIVE;
+    __shared__ __attribute__((aligned(16))) uint16_t Qs0[AT_TILE], Qs1[AT_TILE], Qp[2][AT_TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t Ds0[AT_TILE], Ds1[AT_TILE], Dp[2][AT_TILE];
+    __shared__ __attribute__((aligned(16))) float Ls0[AT_BQ], Ls1[AT_BQ], Lp[2][AT_BQ];   // -lse * log2(e)
+    __shared__ __attribute__((aligned(16))) float Es0[AT_BQ], Es1[AT_BQ], Ep[2][AT_BQ];   // Delta
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -290,21 +294,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int ntile = SPLIT ? nqt : G * nqt;
 
     auto head_of = [&](int t) { return SPLIT ? (int64_t)bx : (int64_t)bk * G + t / nqt; };
-    auto load = [&](int t, int buf) {
+    auto load = [&](int t, auto bufc) __attribute__((always_inline)) {
+        constexpr int buf = decltype(bufc)::value;
         const int64_t bh = head_of(t);
         const int r0 = qstart + (t % nqt) * AT_BQ;
-        load_rows64(a.q + bh * S * AT_D, Qs[buf], r0, S, wave, lane);
-        load_rows64(a.dout + bh * S * AT_D, Ds[buf], r0, S, wave, lane);
+        load_rows64(a.q + bh * S * AT_D, dbuf<buf, SPLIT_LDS>(Qs0, Qs1, Qp), r0, S, wave, lane);
+        load_rows64(a.dout + bh * S * AT_D, dbuf<buf, SPLIT_LDS>(Ds0, Ds1, Dp), r0, S, wave, lane);
         if constexpr (SOFTCAP) {
             const int wv = __builtin_amdgcn_readfirstlane(wave);   // wave-uniform
-            if (wv < 2) {
-                int r = r0 + lane;
-                r = r < S ? r : S - 1;
-                const float *src = (wv == 0 ? a.lse : a.delta) + bh * S + r;
-                float *dst = wv == 0 ? Ls[buf] : Es[buf];
-                __builtin_amdgcn_global_load_lds((const void *)src,
-                                                 (void __attribute__((address_space(3))) *)dst, 4, 0, 0);
-            }
+            int r = r0 + lane;
+            r = r < S ? r : S - 1;
+            // one fixed destination array per load (keeps its alias scope)
+            if (wv == 0)
+                __builtin_amdgcn_global_load_lds((const void *)(a.lse + bh * S + r),
+                                                 (void __attribute__((address_space(3))) *)dbuf<buf, SPLIT_LDS>(Ls0, Ls1, Lp), 4, 0, 0);
+            else if (wv == 1)
+                __builtin_amdgcn_global_load_lds((const void *)(a.delta + bh * S + r),
+                                                 (void __attribute__((address_space(3))) *)dbuf<buf, SPLIT_LDS>(Es0, Es1, Ep), 4, 0, 0);
         }
     };
 
@@ -358,8 +364,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         auto group_load = [&](auto gc) __attribute__((always_inline)) {
             constexpr int g = decltype(gc)::value, qb = g >> 2, j = g & 3;
             if constexpr (SOFTCAP) {
-                nlb[g & 1] = *(const f32x4 *)(&Ls[buf][qb * 32 + j * 8 + h * 4]);
-                dlb[g & 1] = *(const f32x4 *)(&Es[buf][qb * 32 + j * 8 + h * 4]);
+                nlb[g & 1] = *(const f32x4 *)(&dbuf<buf, SPLIT_LDS>(Ls0, Ls1, Lp)[qb * 32 + j * 8 + h * 4]);
+                dlb[g & 1] = *(const f32x4 *)(&dbuf<buf, SPLIT_LDS>(Es0, Es1, Ep)[qb * 32 + j * 8 + h * 4]);
             }
         };
         // score pair P: query block P / 8, rows j*8 + h*4 + i, i + 1 with
@@ -403,17 +409,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         });
     };
 
-    load(0, 0);
+    load(0, std::integral_constant<int, 0>{});
     auto tile = [&](int t, auto bufc) {
         constexpr int buf = decltype(bufc)::value;
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        if (t + 1 < ntile) load(t + 1, buf ^ 1);
+        if (t + 1 < ntile) load(t + 1, std::integral_constant<int, buf ^ 1>{});
         const int r0 = qstart + (t % nqt) * AT_BQ;
         if (a.causal && r0 + AT_BQ - 1 < k0) return;   // every row of the tile precedes these keys
         if (k0 >= S) return;
-        const uint16_t *Qb = Qs[buf];
-        const uint16_t *Db = Ds[buf];
+        const uint16_t *Qb = dbuf<buf, SPLIT_LDS>(Qs0, Qs1, Qp);
+        const uint16_t *Db = dbuf<buf, SPLIT_LDS>(Ds0, Ds1, Dp);
         const bool need_mask = (a.causal && r0 < k0 + 31) || r0 + AT_BQ > S;
         if (!need_mask) {
             slotted_tile(Qb, Db, bufc);
@@ -445,8 +451,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 for (int j = 0; j < 4; ++j) {
                     f32x4 nl4 = {}, dl4 = {};
                     if constexpr (SOFTCAP) {
-                        nl4 = *(const f32x4 *)(&Ls[buf][qb * 32 + j * 8 + h * 4]);
-                        dl4 = *(const f32x4 *)(&Es[buf][qb * 32 + j * 8 + h * 4]);
+                        nl4 = *(const f32x4 *)(&dbuf<buf, SPLIT_LDS>(Ls0, Ls1, Lp)[qb * 32 + j * 8 + h * 4]);
+                        dl4 = *(const f32x4 *)(&dbuf<buf, SPLIT_LDS>(Es0, Es1, Ep)[qb * 32 + j * 8 + h * 4]);
                         nl4 *= -AT_LOG2E;
                     }
                     uint32_t pw[2], dw[2];
