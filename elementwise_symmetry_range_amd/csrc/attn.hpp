@@ -229,11 +229,11 @@ __device__ __forceinline__ float fma_mix_add_lo_clamp(float t, float v, uint32_t
     return r;
 }
 
-// sigmoid program on a pair: packed BF16 P~ (and the packed BF16 surrogate
-// derivative when GRAD)
+// sigmoid program on a pair: packed BF16 P~ (and, when GRAD, the BF16
+// surrogate derivatives as FP32 values in g0, g1)
 template <bool GRAD>
 __device__ __forceinline__ uint32_t sigmoid_poly_pair(float s0, float s1, float scale,
-                                                      const SigCoef &k, uint32_t *grad)
+                                                      const SigCoef &k, float *g0, float *g1)
 {
     // every value BF16-rounded per lane (rn_bf16: one instruction, no unpack)
     const float x0 = rn_bf16(s0 * scale), x1 = rn_bf16(s1 * scale);
@@ -258,7 +258,8 @@ __device__ __forceinline__ uint32_t sigmoid_poly_pair(float s0, float s1, float 
         const uint32_t z0 = r0 ? k.ab[1] : k.ab[0], z1 = r1 ? k.ab[1] : k.ab[0];
         const float f0 = rn_bf16(fma_mix_pair(t0, z0));   // b t + a
         const float f1 = rn_bf16(fma_mix_pair(t1, z1));
-        *grad = pack_bf(v0 * f0, v1 * f1);
+        *g0 = rn_bf16(v0 * f0);
+        *g1 = rn_bf16(v1 * f1);
     }
     return pack_bf(v0, v1);   // exact: v0, v1 are BF16 values
 }
@@ -514,7 +515,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             constexpr int e = 2 * P;
             uint32_t w;
             if constexpr (MODE == AM_SIGMOID_POLY) {
-                w = sigmoid_poly_pair<false>(s[e], s[e + 1], a.scale, a.sig, nullptr);
+                w = sigmoid_poly_pair<false>(s[e], s[e + 1], a.scale, a.sig, nullptr, nullptr);
             } else {
                 w = pack_bf(sigmoid_acc(fmaf(s[e], a.scale, -a.logn)),
                             sigmoid_acc(fmaf(s[e + 1], a.scale, -a.logn)));

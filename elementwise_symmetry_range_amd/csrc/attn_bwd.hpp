@@ -59,39 +59,42 @@ struct AttnBwdArgs {
     SigCoef sig;
 };
 
-// dS (and P) of a pair of scores; s0, s1 raw scores, dp0, dp1 = dO . V,
-// nl0, nl1 = -lse * log2(e) (softcap), dl0, dl1 = Delta (softcap).
+// dS and P of a pair of scores; s0, s1 raw scores, dp0, dp1 = dO . V,
+// nl0, nl1 = -lse * log2(e) (softcap), dl0, dl1 = Delta (softcap).  P comes
+// back as the packed BF16 pair the dV product takes (the sigmoid program
+// produces it in that form), dS as FP32.
 template <int MODE>
 __device__ __forceinline__ void bwd_pair(const AttnBwdArgs &a, float s0, float s1, float dp0,
                                          float dp1, float nl0, float nl1, float dl0, float dl1,
-                                         float &p0, float &p1, float &ds0, float &ds1)
+                                         uint32_t &pw, float &ds0, float &ds1)
 {
     if constexpr (MODE == AM_SOFTCAP_POLY) {
         uint32_t aw;
         const uint32_t tw = softcap_poly_pair(s0, s1, a.scale, a.tanh16, aw);
         const uint32_t dw = bc<uint32_t>(horner_f16<3, false>(bc<h2>(min_u16x2(aw, a.dtanh16.lc)), a.dtanh16));
-        p0 = __builtin_amdgcn_exp2f(fma_mix_lo(tw, a.c2, nl0));
-        p1 = __builtin_amdgcn_exp2f(fma_mix_hi(tw, a.c2, nl1));
+        const float p0 = __builtin_amdgcn_exp2f(fma_mix_lo(tw, a.c2, nl0));
+        const float p1 = __builtin_amdgcn_exp2f(fma_mix_hi(tw, a.c2, nl1));
         ds0 = fma_mix_lo(dw, p0 * (dp0 - dl0), -0.0f);
         ds1 = fma_mix_hi(dw, p1 * (dp1 - dl1), -0.0f);
+        pw = pack_bf(p0, p1);
     } else if constexpr (MODE == AM_SOFTCAP_NATIVE) {
         const float t0 = tanhf(s0 * a.scale), t1 = tanhf(s1 * a.scale);
-        p0 = __builtin_amdgcn_exp2f(fmaf(t0, a.c2, nl0));
-        p1 = __builtin_amdgcn_exp2f(fmaf(t1, a.c2, nl1));
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(t0, a.c2, nl0));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(t1, a.c2, nl1));
         ds0 = p0 * (dp0 - dl0) * fmaf(-t0, t0, 1.0f);
         ds1 = p1 * (dp1 - dl1) * fmaf(-t1, t1, 1.0f);
+        pw = pack_bf(p0, p1);
     } else if constexpr (MODE == AM_SIGMOID_POLY) {
-        uint32_t gw;
-        const uint32_t pw = sigmoid_poly_pair<true>(s0, s1, a.scale, a.sig, &gw);
-        p0 = lo_f(pw);
-        p1 = hi_f(pw);
-        ds0 = dp0 * lo_f(gw);
-        ds1 = dp1 * hi_f(gw);
+        float g0, g1;
+        pw = sigmoid_poly_pair<true>(s0, s1, a.scale, a.sig, &g0, &g1);
+        ds0 = dp0 * g0;
+        ds1 = dp1 * g1;
     } else {
-        p0 = sigmoid_acc(fmaf(s0, a.scale, -a.logn));
-        p1 = sigmoid_acc(fmaf(s1, a.scale, -a.logn));
+        const float p0 = sigmoid_acc(fmaf(s0, a.scale, -a.logn));
+        const float p1 = sigmoid_acc(fmaf(s1, a.scale, -a.logn));
         ds0 = dp0 * (p0 * (1.0f - p0));
         ds1 = dp1 * (p1 * (1.0f - p1));
+        pw = pack_bf(p0, p1);
     }
 }
 
@@ -193,8 +196,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
                     for (int e2 = 0; e2 < 4; ++e2) {
                         const int e = jj * 8 + e2 * 2;
-                        float p0, p1, d0, d1;
-                        bwd_pair<MODE>(a, s[e], s[e + 1], dp[e], dp[e + 1], nl, nl, dl, dl, p0, p1, d0, d1);
+                        uint32_t pw;   // P is not needed here
+                        float d0, d1;
+                        bwd_pair<MODE>(a, s[e], s[e + 1], dp[e], dp[e + 1], nl, nl, dl, dl, pw, d0, d1);
                         uint32_t w = pack_bf(d0, d1);
                         if constexpr (MASKED) {
                             const int k0 = key0 + kb * 32 + (e >> 2) * 8 + h * 4 + (e & 3);
@@ -380,11 +384,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 dl0 = dlb[j & 1][i];
                 dl1 = dlb[j & 1][i + 1];
             }
-            float p0, p1, d0, d1;
-            bwd_pair<MODE>(a, s[qb][e], s[qb][e + 1], dp[qb][e], dp[qb][e + 1], nl0, nl1, dl0, dl1,
-                           p0, p1, d0, d1);
+            float d0, d1;
             constexpr int f = qb * 2 + (j >> 1), w = (j & 1) * 2 + (i >> 1);
-            pw[f][w] = pack_bf(p0, p1);
+            bwd_pair<MODE>(a, s[qb][e], s[qb][e + 1], dp[qb][e], dp[qb][e + 1], nl0, nl1, dl0, dl1,
+                           pw[f][w], d0, d1);
             dw[f][w] = pack_bf(d0, d1);
             if constexpr (w == 3) {
                 pf[f] = bc<bf16x8>(u32x4{pw[f][0], pw[f][1], pw[f][2], pw[f][3]});
@@ -459,10 +462,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
                     for (int i = 0; i < 4; i += 2) {
                         const int e = j * 4 + i;
-                        float p0, p1, d0, d1;
+                        uint32_t pk;
+                        float d0, d1;
                         bwd_pair<MODE>(a, s[qb][e], s[qb][e + 1], dp[qb][e], dp[qb][e + 1], nl4[i],
-                                       nl4[i + 1], dl4[i], dl4[i + 1], p0, p1, d0, d1);
-                        uint32_t pk = pack_bf(p0, p1), dk2 = pack_bf(d0, d1);
+                                       nl4[i + 1], dl4[i], dl4[i + 1], pk, d0, d1);
+                        uint32_t dk2 = pack_bf(d0, d1);
                         const int q = r0 + qb * 32 + j * 8 + h * 4 + i;
                         const bool vis0 = q < S && (!a.causal || q >= my_k);
                         const bool vis1 = q + 1 < S && (!a.causal || q + 1 >= my_k);
