@@ -19,16 +19,17 @@
 // Two kernels, no atomics:
 //   k_attn_bwd_dq    one workgroup per 128 queries of one head (4 waves x 32
 //                    queries, lane = query as in the forward).  It computes
-//                    Delta for its rows first (softcap) and stores it in the
-//                    caller's workspace, then streams K / V tiles of 64 keys
+//                    Delta for its rows first (softcap) and stores it, with
+//                    -lse log2(e), in the caller's workspace, then streams
+//                    K / V tiles of 64 keys
 //                    through LDS: S^T = K Q^T and dP^T = V dO^T with Q and dO
 //                    held in registers, the transform, dQ^T += K^T dS^T with
 //                    K^T read transposed from the K tile.
 //   k_attn_bwd_dkdv  one workgroup per 128 keys of one key/value head (4
 //                    waves x 32 keys, lane = key); it loops over the query
 //                    heads of the group and the query tiles of 64 rows that
-//                    see its keys, with Q / dO tiles (and the rows' LSE and
-//                    Delta) streamed through LDS: S = Q K^T and dP = dO V^T
+//                    see its keys, with Q / dO tiles (and the rows'
+//                    -lse log2(e) and Delta) streamed through LDS: S = Q K^T and dP = dO V^T
 //                    with K and V held in registers, the transform,
 //                    dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T read
 //                    transposed from the tiles.
@@ -46,6 +47,7 @@ struct AttnBwdArgs {
     const uint16_t *q, *k, *v, *o, *dout;
     const float *lse;      // softcap: natural log-sum-exp per query row
     float *delta;          // softcap: workspace, Delta per query row
+    float *nlse;           // softcap: workspace, -lse * log2(e) per query row
     float *part;           // grouped query heads: FP32 dK, dV partials per query head
     uint16_t *dq, *dk, *dv;
     int32_t S, H, G;       // G = H / Hkv
@@ -146,7 +148,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         dl = acc + __shfl_xor(acc, 32);
         if (valid) {
             nl = -a.lse[(int64_t)bh * S + my_q] * AT_LOG2E;
-            if (h == 0) a.delta[(int64_t)bh * S + my_q] = dl;
+            if (h == 0) {
+                a.delta[(int64_t)bh * S + my_q] = dl;
+                a.nlse[(int64_t)bh * S + my_q] = nl;   // the dK/dV kernel streams it
+            }
         }
     }
 
@@ -310,7 +315,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             r = r < S ? r : S - 1;
             // one fixed destination array per load (keeps its alias scope)
             if (wv == 0)
-                __builtin_amdgcn_global_load_lds((const void *)(a.lse + bh * S + r),
+                __builtin_amdgcn_global_load_lds((const void *)(a.nlse + bh * S + r),
                                                  (void __attribute__((address_space(3))) *)dbuf<buf, SPLIT_LDS>(Ls0, Ls1, Lp), 4, 0, 0);
             else if (wv == 1)
                 __builtin_amdgcn_global_load_lds((const void *)(a.delta + bh * S + r),
@@ -337,7 +342,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         bf16x8 pf[4], dsf[4];
         uint32_t pw[4][4], dw[4][4];   // P and dS words of fragment f
         bf16x8 op[64];
-        f32x4 nlb[2], dlb[2];          // LSE and Delta of a group of 4 query rows
+        f32x4 nlb[2], dlb[2];          // -lse log2(e) and Delta of a group of 4 query rows
         auto load_op = [&](auto mc) __attribute__((always_inline)) {
             constexpr int M = decltype(mc)::value;
             if constexpr (M < 32) {
@@ -379,8 +384,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             constexpr int e = j * 4 + i;
             float nl0 = 0.0f, nl1 = 0.0f, dl0 = 0.0f, dl1 = 0.0f;
             if constexpr (SOFTCAP) {
-                nl0 = nlb[j & 1][i] * -AT_LOG2E;
-                nl1 = nlb[j & 1][i + 1] * -AT_LOG2E;
+                nl0 = nlb[j & 1][i];
+                nl1 = nlb[j & 1][i + 1];
                 dl0 = dlb[j & 1][i];
                 dl1 = dlb[j & 1][i + 1];
             }
@@ -456,7 +461,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                     if constexpr (SOFTCAP) {
                         nl4 = *(const f32x4 *)(&dbuf<buf, SPLIT_LDS>(Ls0, Ls1, Lp)[qb * 32 + j * 8 + h * 4]);
                         dl4 = *(const f32x4 *)(&dbuf<buf, SPLIT_LDS>(Es0, Es1, Ep)[qb * 32 + j * 8 + h * 4]);
-                        nl4 *= -AT_LOG2E;
                     }
                     uint32_t pw[2], dw[2];
 #pragma unroll

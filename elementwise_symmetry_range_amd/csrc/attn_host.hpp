@@ -212,14 +212,14 @@ inline pa_status attn_fwd(int mode, const void *q, const void *k, const void *v,
     return attn_launched();
 }
 
-// Workspace of a backward call, in floats: Delta per query row (softcap),
-// then, for grouped query heads, FP32 dK and dV partials per query head
-// (16-byte aligned).  0 when none is needed.
+// Workspace of a backward call, in floats: Delta and -lse log2(e) per query
+// row (softcap; each region padded to 16 bytes), then, for grouped query
+// heads, FP32 dK and dV partials per query head.  0 when none is needed.
 inline int64_t attn_bwd_ws_floats(bool softcap, int32_t B, int32_t H, int32_t Hkv, int32_t S,
                                   int32_t D)
 {
     const int64_t rows = (int64_t)B * H * S;
-    int64_t n = softcap ? (rows + 3) / 4 * 4 : 0;
+    int64_t n = softcap ? 2 * ((rows + 3) / 4 * 4) : 0;
     if (Hkv > 0 && H > Hkv) n += 2 * rows * D;
     return n;
 }
@@ -275,8 +275,10 @@ inline pa_status attn_bwd(int mode, const void *q, const void *k, const void *v,
     a.o = (const uint16_t *)o;
     a.dout = (const uint16_t *)dout;
     a.lse = lse;
+    const int64_t rows4 = ((int64_t)B * H * S + 3) / 4 * 4;
     a.delta = softcap ? ws : nullptr;
-    a.part = H > Hkv ? ws + (softcap ? ((int64_t)B * H * S + 3) / 4 * 4 : 0) : nullptr;
+    a.nlse = softcap ? ws + rows4 : nullptr;
+    a.part = H > Hkv ? ws + (softcap ? 2 * rows4 : 0) : nullptr;
     a.dq = (uint16_t *)dq;
     a.dk = (uint16_t *)dk;
     a.dv = (uint16_t *)dv;

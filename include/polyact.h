@@ -214,7 +214,8 @@ pa_status poly_softcap_attn_fwd_exp2(const void *q, const void *k, const void *v
  * PA_F16)) in packed FP16 at the same clamped |x|.  P and dS are rounded to
  * BF16 for the MFMA.  workspace: caller-owned scratch, 16-byte aligned, of
  * pa_attn_bwd_workspace_bytes(1, B, H, Hkv, S, D) bytes: B * H * S floats
- * for Delta and, when H > Hkv, FP32 dK and dV partials of every query head
+ * each for Delta and for -lse log2(e) (each region rounded up to 16 bytes)
+ * and, when H > Hkv, FP32 dK and dV partials of every query head
  * (summed per group by a final pass in a fixed order); contents on return
  * unspecified.
  * Paper: Eq. 12 and section 5.2.2 (the differentiated D3 at the recomputed

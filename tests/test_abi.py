@@ -167,7 +167,7 @@ def test_error_paths_attention(pa):
     assert L.native_sigmoid_attn_bwd(Q, K, V, DO, DQ, DK, DV, None, 1, 2, 2, 0, 128, 1, None) == 0
     wb = L.pa_attn_bwd_workspace_bytes
     assert wb(0, 1, 8, 8, 4096, 128) == 0
-    assert wb(1, 1, 8, 8, 4095, 128) == 4 * 8 * 4095
+    assert wb(1, 1, 8, 8, 4095, 128) == 4 * 2 * 8 * 4095            # Delta, -lse log2(e)
     assert wb(0, 1, 8, 2, 100, 128) == 4 * 2 * 8 * 100 * 128
-    assert wb(1, 1, 3, 1, 5, 128) == 4 * (16 + 2 * 3 * 5 * 128)   # Delta region padded to 16 B
+    assert wb(1, 1, 3, 1, 5, 128) == 4 * (2 * 16 + 2 * 3 * 5 * 128)   # regions padded to 16 B
     assert wb(1, 1, 3, 2, 5, 128) == -1
