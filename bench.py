@@ -239,7 +239,7 @@ def components_main(torch, pa, si, alt, res):
     op, lp = pa.poly_softcap_attn_fwd(q, k, v, 50.0, True, with_lse=True)
     on, ln = pa.native_softcap_attn_fwd(q, k, v, 50.0, True, with_lse=True)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = torch.empty((1, 16, 8192), dtype=torch.float32, device=q.device)
+    ws = pa.attn_bwd_workspace(True, 1, 16, 16, 8192, 128, device=q.device)
     fp = lambda: pa.poly_softcap_attn_bwd(q, k, v, op, dout, lp, 50.0, True, dq=dq, dk=dk, dv=dv,  # noqa: E731
                                           workspace=ws)
     fn = lambda: pa.native_softcap_attn_bwd(q, k, v, on, dout, ln, 50.0, True, dq=dq, dk=dk,  # noqa: E731
