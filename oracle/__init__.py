@@ -64,7 +64,7 @@ class Attn(C.Structure):
                 ("S", C.c_int32), ("D", C.c_int32), ("causal", C.c_int32),
                 ("order", C.c_int32), ("exp2_core", C.c_int32), ("cap", C.c_float),
                 ("tanh_prog", C.POINTER(Prog)),
-                ("sig", C.POINTER(SigProg))]
+                ("sig", C.POINTER(SigProg)), ("tanh_order", C.c_int32), ("replay", C.c_int32)]
 
 
 ATTN_SOFTCAP_POLY, ATTN_SOFTCAP_EXACT, ATTN_SIGMOID_POLY, ATTN_SIGMOID_EXACT = 1, 2, 3, 4
@@ -114,6 +114,7 @@ def lib():
             "orc_attn_bwd_rows": (C.c_int, [P(Attn)] + [C.c_void_p] * 7 + [i64, C.c_void_p, i64]
                                   + [C.c_void_p] * 10),
             "orc_dtanh_prog_f16": (u16, [P(Prog), u16]),
+            "orc_dtanh_prog": (u16, [P(Prog), u16, C.c_int]),
             "orc_exp2_core": (f64, [C.c_int, f64, f64]),
             "orc_exp2_errors": (None, [C.c_int, f64, P(f64), P(f64)]),
             "orc_exp2_fit": (f64, [C.c_int, C.c_int]),
@@ -228,11 +229,17 @@ def sig_prog_from_golden(d: dict) -> SigProg:
     return sp
 
 
-def _attn(kind, q, k, cap, causal, tanh_prog, sig, order, exp2_core=0):
+TANH_ORDERS = {"bf16": ORDER_F32FMA_BF16, "f16": ORDER_F16_FMA}
+
+
+def _attn(kind, q, k, cap, causal, tanh_prog, sig, order, exp2_core=0, tanh_fmt="bf16",
+          replay=True):
     B, H, S, D = q.shape
     a = Attn()
     a.kind, a.B, a.H, a.Hkv, a.S, a.D = kind, B, H, k.shape[1], S, D
     a.causal, a.order, a.cap, a.exp2_core = int(causal), order, cap, exp2_core
+    a.tanh_order = TANH_ORDERS[tanh_fmt]
+    a.replay = int(bool(replay))
     a._keep = (tanh_prog, sig)
     if tanh_prog is not None:
         a.tanh_prog = C.pointer(tanh_prog)
@@ -243,18 +250,21 @@ def _attn(kind, q, k, cap, causal, tanh_prog, sig, order, exp2_core=0):
 
 def attn_fwd_rows(kind: int, q, k, v, rows, cap: float = 50.0, causal: bool = True,
                   tanh_prog: Prog = None, sig: SigProg = None, order: int = 0,
-                  exp2_core: int = 0):
+                  exp2_core: int = 0, tanh_fmt: str = "bf16", replay: bool = True):
     """q: uint16 BF16 bits [B, H, S, D]; k, v: [B, Hkv, S, D].  Returns (O, lse,
     noise) in float64 for the flat query rows (b H + h) S + i: O and noise
     [len(rows), D], lse [len(rows)] (NaN for sigmoid attention).  exp2_core
-    (softcap poly only): the softmax's exponentials by that fractional core."""
+    (softcap poly only): the softmax's exponentials by that fractional core.
+    tanh_fmt: format of the softcap program ("bf16", the pages' path, or
+    "f16").  replay: the method's FP32 steps and BF16 rounding of P (True) or
+    real arithmetic around the programs (False)."""
     q, k, v = _u16(q), _u16(k), _u16(v)
     D = q.shape[3]
     rows = np.ascontiguousarray(rows, dtype=np.int64)
     out = np.zeros((rows.size, D))
     lse = np.zeros(rows.size)
     noise = np.zeros((rows.size, D))
-    a = _attn(kind, q, k, cap, causal, tanh_prog, sig, order, exp2_core)
+    a = _attn(kind, q, k, cap, causal, tanh_prog, sig, order, exp2_core, tanh_fmt, replay)
     rc = lib().orc_attn_fwd_rows(C.byref(a), _ptr(q), _ptr(k), _ptr(v), _ptr(rows), rows.size,
                                  _ptr(out), _ptr(lse), _ptr(noise))
     if rc:
@@ -264,14 +274,15 @@ def attn_fwd_rows(kind: int, q, k, v, rows, cap: float = 50.0, causal: bool = Tr
 
 def attn_bwd_rows(kind: int, q, k, v, o, dout, lse, qrows, krows, cap: float = 50.0,
                   causal: bool = True, tanh_prog: Prog = None, sig: SigProg = None,
-                  order: int = 0):
+                  order: int = 0, exp2_core: int = 0, tanh_fmt: str = "bf16",
+                  replay: bool = True):
     """Gradients of sum(O * dout) for the flat query rows (dQ) and key rows
     (b Hkv + hk) S + j (dK, dV).  o: float64 [B, H, S, D] (the forward output
     the backward is given), lse: float64 [B, H, S] (softcap only).  Returns
     (dq, dk, dv, nz_dq, nz_dk, nz_dv, cs_dq, cs_dk, sd_dq, sd_dk), float64
     [rows, D] each: the gradients, their noise scales, their cancellation
     scales and their sensitivity to an absolute error in the transform's
-    derivative."""
+    derivative.  tanh_fmt, replay, exp2_core: as attn_fwd_rows."""
     q, k, v, dout = _u16(q), _u16(k), _u16(v), _u16(dout)
     D = q.shape[3]
     o = np.ascontiguousarray(o, dtype=np.float64)
@@ -280,7 +291,7 @@ def attn_bwd_rows(kind: int, q, k, v, o, dout, lse, qrows, krows, cap: float = 5
     krows = np.ascontiguousarray(krows, dtype=np.int64)
     res = [np.zeros((n, D)) for n in (qrows.size, krows.size, krows.size) * 2
            + (qrows.size, krows.size) * 2]
-    a = _attn(kind, q, k, cap, causal, tanh_prog, sig, order)
+    a = _attn(kind, q, k, cap, causal, tanh_prog, sig, order, exp2_core, tanh_fmt, replay)
     rc = lib().orc_attn_bwd_rows(C.byref(a), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout),
                                  _ptr(lse), _ptr(qrows), qrows.size, _ptr(krows), krows.size,
                                  *[_ptr(r) for r in res])
@@ -304,10 +315,16 @@ def exp2_core_target(core: int, f) -> np.ndarray:
                     dtype=np.float32)
 
 
-def dtanh_prog_f16(tanh_prog: Prog, x_bits) -> np.ndarray:
+def dtanh_prog(tanh_prog: Prog, x_bits, tanh_fmt: str = "bf16") -> np.ndarray:
+    """The analytic derivative of the tanh program at x (bits of tanh_fmt)."""
     x = np.atleast_1d(np.asarray(x_bits, dtype=np.uint16))
-    return np.array([lib().orc_dtanh_prog_f16(C.byref(tanh_prog), int(b)) for b in x],
+    order = TANH_ORDERS[tanh_fmt]
+    return np.array([lib().orc_dtanh_prog(C.byref(tanh_prog), int(b), order) for b in x],
                     dtype=np.uint16)
+
+
+def dtanh_prog_f16(tanh_prog: Prog, x_bits) -> np.ndarray:
+    return dtanh_prog(tanh_prog, x_bits, "f16")
 
 
 def sig_prog_eval(sp: SigProg, x_bits, order: int = ORDER_F32FMA_BF16):

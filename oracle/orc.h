@@ -134,6 +134,16 @@ typedef struct {
     float cap;                 /* softcap alpha                                 */
     const orc_prog *tanh_prog; /* D4 tanh program (SOFTCAP_POLY)                */
     const orc_sig_prog *sig;   /* SIGMOID_POLY                                  */
+    int32_t tanh_order;        /* format of the softcap program and its
+                                  derivative: ORC_ORDER_F32FMA_BF16 (the pages'
+                                  BF16 path; also 0) or ORC_ORDER_F16_FMA      */
+    int32_t replay;            /* 0: real arithmetic around the programs (FP64
+                                  scores, weights and sums);
+                                  1: the method's FP32 steps (scores, scaled
+                                  scores, exponent arguments, dP - Delta, dS)
+                                  rounded to FP32 and P / dS rounded to BF16
+                                  before the products with V / K / Q / dO;
+                                  sums exact                                    */
 } orc_attn;
 
 /* Returns 0, or -1 (sequence length differs from the sigmoid program's n),
@@ -147,6 +157,10 @@ int orc_attn_bwd_rows(const orc_attn *a, const uint16_t *q, const uint16_t *k,
                       const int64_t *krows, int64_t nk, double *dq, double *dk,
                       double *dv, double *nz_dq, double *nz_dk, double *nz_dv,
                       double *cs_dq, double *cs_dk, double *sd_dq, double *sd_dk);
+/* The analytic derivative of the softcap tanh program at x (bits in the
+ * format of `order`): the D3 with coefficients (j + 1) c_{j+1} (exact in
+ * FP16; rounded to BF16 for the BF16 program) at |x|, 0 beyond the clamp. */
+uint16_t orc_dtanh_prog(const orc_prog *tanh_prog, uint16_t x, int order);
 uint16_t orc_dtanh_prog_f16(const orc_prog *tanh_prog, uint16_t x);
 uint16_t orc_sig_prog_eval(const orc_sig_prog *sp, uint16_t x, int order, uint16_t *grad);
 int orc_threads(void);

@@ -221,25 +221,54 @@ void orc_swiglu_bwd(const orc_prog *sig, const uint16_t *gate, const uint16_t *u
  * Layout: Q, O, dO [B, H, S, D]; K, V [B, Hkv, S, D] (grouped-query attention:
  * query head h reads key/value head h / (H / Hkv)); BF16 bit patterns, except
  * O and the log-sum-exp, which are passed as FP64 values.  Raw score
- * S_ij = q_i . k_j, computed in FP64.  Causal: key j visible from query i when
- * j <= i.
+ * S_ij = q_i . k_j (exact in FP64: BF16 products have 16 significant bits).
+ * Causal: key j visible from query i when j <= i.
  *
  * Score transforms:
  *   SOFTCAP (Eq. 1): logit s = cap tanh(S / (cap sqrt D)), P = softmax_j(s).
- *     POLY  x = RN_f16(RN32(RN32(S) * RN32(1 / (cap sqrt D)))), tanh by the D4
- *           program in FP16 arithmetic.  Backward (sections 3.3 and 5.2.2):
- *           the analytic derivative of that program, i.e. the D3 polynomial
- *           with coefficients (j + 1) c_{j+1} (exact in FP16), evaluated in
- *           FP16 arithmetic at the same clamped |x|, so ds/dS = cap RN32(..)
- *           q(x).
- *     EXACT tanh in FP64; ds/dS = (1 - tanh^2) / sqrt D (Eq. 12).
+ *     POLY  x = RN_fmt(RN32(RN32(S) * RN32(1 / (cap sqrt D)))), tanh by the D4
+ *           program in the program's format: BF16 (each stage an FP32 FMA
+ *           rounded to BF16; the pages run the integrations on the BF16 path,
+ *           section 3.4) or FP16 (one FP16 rounding per stage).  Backward
+ *           (section 3.3, section 5.2.2): the analytic derivative of that
+ *           program, the D3 with coefficients (j + 1) c_{j+1} (exact in FP16,
+ *           rounded to BF16 for the BF16 program) evaluated in the same format
+ *           at |x|; beyond the clamp Lc the forward program is constant, so
+ *           its derivative is 0 there.
+ *     EXACT tanh of the scaled score; derivative 1 - tanh^2 (Eq. 12).
  *   SIGMOID (Eq. 14): P = sigma(s - ln n) with s = S / sqrt D and n = S, the
  *     sequence length; no normalisation.
  *     POLY  x = RN_bf16(RN32(RN32(S) * RN32(1 / sqrt D))); the two-region
  *           cubic of section 3.4 / Appendix C on the clamped x, floored at 0,
  *           with ln n and 1 / n folded into its coefficients (so it holds for
  *           one n only); backward surrogate P~ (a + b x) per region.
- *     EXACT FP64 sigma; dP/dS = P (1 - P) / sqrt D.
+ *     EXACT sigma; dP/dS = P (1 - P) / sqrt D.
+ *
+ * Two arithmetic models around the programs (orc_attn.replay):
+ *   0  real arithmetic: scores, weights and sums in FP64 (the program values
+ *      exact as computed); the softcap chain factor is cap RN32(1 / (cap
+ *      sqrt D)).  Pinned against automatic differentiation.
+ *   1  the method's rounding steps: the FP32 score path of the pages'
+ *      attention kernels (QK^T accumulated in FP32, the softmax in FP32 with
+ *      its exponential as exp2) and the BF16 operands of the P V, dS K and
+ *      dS^T Q products (section 3.4: P cast to the value dtype before the
+ *      product).  Every scalar step below is rounded to FP32 once (a fused
+ *      multiply-add where one operation forms a product and a sum); P and dS
+ *      are rounded to BF16 before they multiply V, dO, K or Q; the row sum l
+ *      adds the FP32 P; the sums themselves are exact.
+ *      Softcap forward: z = RN32(t c2 - m), c2 = RN32(cap log2 e), with the
+ *      fixed reference m = ceil(RN32(c2 - 40)) when c2 <= 80 (every logit is
+ *      bounded by cap, so one reference keeps each P in FP32's normal range);
+ *      otherwise, and with a software exp2 core, z = RN32(t c2) split as
+ *      2^floor(z) 2^(z - floor z), which makes each P independent of the
+ *      reference up to an exact power of two.  P = RN32(2^z) (or the core's
+ *      value).  lse = (m + log2 l) ln 2.
+ *      Backward: P = 2^z with z = RN32(t c2 + RN32(-lse log2 e)) from the
+ *      forward's FP32 log-sum-exp (through the same exp2 core, if any);
+ *      Delta_i = RN32(dO_i . O_i), dP = RN32(dO_i . V_j);
+ *      softcap dS = RN32(q' RN32(P RN32(dP - Delta))), q' the derivative
+ *      value; sigmoid dS = RN32(dP g); dQ and dK scaled by RN32(1 / sqrt D)
+ *      at the end.
  *
  * Backward (chain rule through O = P V):
  *   dV_j = sum_i P_ij dO_i;   dP_ij = dO_i . V_j;
@@ -247,14 +276,12 @@ void orc_swiglu_bwd(const orc_prog *sig, const uint16_t *gate, const uint16_t *u
  *   sigmoid: dS_ij = dP_ij dP/dS;
  *   dQ_i = sum_j dS_ij K_j;   dK_j = sum over query heads of the group and
  *   visible i of dS_ij Q_i.
- * Each output also gets a noise scale sqrt(sum of squared terms): the size of
- * the change caused by independent relative roundings of the terms; dQ and dK
- * also get sum_j |dS_ij / (dP_ij - Delta_i)| A_ij |K_j| (resp. over i with
- * |Q_i|), A_ij the sum of the absolute products that form dP_ij - Delta_i:
- * an FP32 evaluation of that difference errs by at most D 2^-24 A_ij, which
- * matters where dP and Delta cancel; and sum_j |dS_ij / g_ij| |K_j| (resp.
- * |Q_i|), the sensitivity to an absolute error in the transform's derivative
- * g (used to state the tolerance of a faster implementation). */
+ * Each output also gets a noise scale sqrt(sum of squared terms), and dQ / dK
+ * two further scales (see pair_grad); these are diagnostics that do not
+ * enter the values. */
+
+static const double LOG2E = 1.4426950408889634074;
+static const double LN2 = 0.69314718055994530942;
 
 static double stable_sigmoid(double s)
 {
@@ -262,26 +289,33 @@ static double stable_sigmoid(double s)
     return s >= 0.0 ? 1.0 / (1.0 + e) : e / (1.0 + e);
 }
 
-/* Differentiated tanh program at FP16 x (see above). */
-static uint16_t dtanh_prog_f16(const orc_prog *tp, uint16_t x)
+/* Analytic derivative of the tanh program at x (bits of format f): the D3
+ * with coefficients (j + 1) c_{j+1} in format f at |x|, 0 beyond the clamp. */
+static uint16_t dtanh_prog(const fmt_ops *f, const orc_prog *tp, uint16_t x)
 {
-    const fmt_ops f = ops_for(ORC_ORDER_F16_FMA);
     uint16_t d[8];
     for (int j = 0; j < tp->degree; j++) {
         const double v = (double)(j + 1) * orc_bf16_to_f64(tp->c[j + 1]);
-        d[j] = orc_f64_to_f16(v);
-        if (orc_f16_to_f64(d[j]) != v) abort();
+        d[j] = enc(f, v);
+        if (f->order == ORC_ORDER_F16_FMA && orc_f16_to_f64(d[j]) != v) abort();
     }
+    if (is_nan(f, x)) return x | f->quiet;
     const uint16_t t = x & 0x7FFF;
-    const uint16_t th = orc_f16_to_f64(t) > tp->Lc ? orc_f64_to_f16(tp->Lc) : t;
+    if (val(f, t) > tp->Lc) return 0;
     uint16_t v = d[tp->degree - 1];
-    for (int j = tp->degree - 2; j >= 0; j--) v = t_fma(&f, v, th, d[j]);
+    for (int j = tp->degree - 2; j >= 0; j--) v = t_fma(f, v, t, d[j]);
     return v;
+}
+
+uint16_t orc_dtanh_prog(const orc_prog *tp, uint16_t x, int order)
+{
+    const fmt_ops f = ops_for(order);
+    return dtanh_prog(&f, tp, x);
 }
 
 uint16_t orc_dtanh_prog_f16(const orc_prog *tp, uint16_t x)
 {
-    return dtanh_prog_f16(tp, x);
+    return orc_dtanh_prog(tp, x, ORC_ORDER_F16_FMA);
 }
 
 /* Two-region sigmoid-attention program at BF16 x: region 1 when x >= thr;
@@ -310,8 +344,14 @@ uint16_t orc_sig_prog_eval(const orc_sig_prog *sp, uint16_t x, int order, uint16
 
 typedef struct {
     const orc_attn *a;
-    fmt_ops f16, fs;
+    fmt_ops ft;       /* format of the softcap program */
+    fmt_ops fs;       /* replay order of the sigmoid program */
     float scale;      /* RN32 of the factor applied to S before rounding x */
+    float c2;         /* RN32(cap log2 e) */
+    float mref;       /* fixed reference of the softcap forward (c2 <= 80) */
+    int sref;
+    float rsd32;      /* RN32(1 / sqrt D) */
+    float logn32;     /* RN32(ln S) */
     double rsd;       /* 1 / sqrt(D) */
     double logn;      /* ln S (sigmoid) */
 } actx;
@@ -319,11 +359,18 @@ typedef struct {
 static int actx_init(actx *c, const orc_attn *a)
 {
     if (a->H <= 0 || a->Hkv <= 0 || a->H % a->Hkv || a->S < 0 || a->D <= 0) return -2;
+    if (a->replay < 0 || a->replay > 1) return -2;
     c->a = a;
-    c->f16 = ops_for(ORC_ORDER_F16_FMA);
+    c->ft = ops_for(a->tanh_order ? a->tanh_order : ORC_ORDER_F32FMA_BF16);
+    if (c->ft.order != ORC_ORDER_F16_FMA && c->ft.order != ORC_ORDER_F32FMA_BF16) return -3;
     c->fs = ops_for(a->order ? a->order : ORC_ORDER_F32FMA_BF16);
     c->rsd = 1.0 / sqrt((double)a->D);
+    c->rsd32 = (float)c->rsd;
     c->logn = log((double)a->S);
+    c->logn32 = (float)c->logn;
+    c->c2 = (float)((double)a->cap * LOG2E);
+    c->sref = c->c2 <= 80.0f;
+    c->mref = ceilf(orc_add_f32(c->c2, -40.0f));
     switch (a->kind) {
     case ORC_ATTN_SOFTCAP_POLY:
     case ORC_ATTN_SOFTCAP_EXACT:
@@ -332,54 +379,104 @@ static int actx_init(actx *c, const orc_attn *a)
         return 0;
     case ORC_ATTN_SIGMOID_POLY:
         if (!a->sig || a->sig->n != a->S) return -1;   /* the length guard */
-        c->scale = (float)c->rsd;
+        c->scale = c->rsd32;
         return 0;
     case ORC_ATTN_SIGMOID_EXACT:
-        c->scale = (float)c->rsd;
+        c->scale = c->rsd32;
         return 0;
     default:
         return -3;
     }
 }
 
-/* Transformed score of raw score Sr: the logit (softcap) or the probability
- * (sigmoid), and its derivative with respect to Sr. */
-static void score(const actx *c, double Sr, double *val, double *dval)
-{
-    const orc_attn *a = c->a;
-    switch (a->kind) {
-    case ORC_ATTN_SOFTCAP_POLY: {
-        const uint16_t x = orc_f64_to_f16((double)orc_mul_f32((float)Sr, c->scale));
-        *val = (double)a->cap * orc_f16_to_f64(eval_one(&c->f16, a->tanh_prog, x));
-        *dval = (double)a->cap * (double)c->scale *
-                orc_f16_to_f64(dtanh_prog_f16(a->tanh_prog, x));
-        return;
-    }
-    case ORC_ATTN_SOFTCAP_EXACT: {
-        const double t = tanh(Sr / ((double)a->cap * sqrt((double)a->D)));
-        *val = (double)a->cap * t;
-        *dval = (1.0 - t * t) * c->rsd;
-        return;
-    }
-    case ORC_ATTN_SIGMOID_POLY: {
-        const uint16_t x = orc_f64_to_bf16((double)orc_mul_f32((float)Sr, c->scale));
-        uint16_t g;
-        *val = orc_bf16_to_f64(sig_eval(&c->fs, a->sig, x, &g));
-        *dval = orc_bf16_to_f64(g) * (double)c->scale;
-        return;
-    }
-    default: {
-        const double p = stable_sigmoid(Sr * c->rsd - c->logn);
-        *val = p;
-        *dval = p * (1.0 - p) * c->rsd;
-        return;
-    }
-    }
-}
-
 static int is_softcap(const orc_attn *a)
 {
     return a->kind == ORC_ATTN_SOFTCAP_POLY || a->kind == ORC_ATTN_SOFTCAP_EXACT;
+}
+
+static double bf16r(double v)
+{
+    return orc_bf16_to_f64(orc_f64_to_bf16(v));
+}
+
+/* Softcap: tanh value t and derivative value q' (of t with respect to the
+ * scaled score x) at raw score Sr. */
+static void softcap_t(const actx *c, double Sr, double *t, double *dq)
+{
+    const orc_attn *a = c->a;
+    if (a->kind == ORC_ATTN_SOFTCAP_POLY) {
+        const uint16_t x = enc(&c->ft, (double)orc_mul_f32((float)Sr, c->scale));
+        *t = val(&c->ft, eval_one(&c->ft, a->tanh_prog, x));
+        *dq = val(&c->ft, dtanh_prog(&c->ft, a->tanh_prog, x));
+    } else if (a->replay) {
+        const float tt = (float)tanh((double)orc_mul_f32((float)Sr, c->scale));
+        *t = tt;
+        *dq = orc_fma_f32(-tt, tt, 1.0f);
+    } else {
+        *t = tanh(Sr / ((double)a->cap * sqrt((double)a->D)));
+        *dq = 1.0 - *t * *t;
+    }
+}
+
+/* 2^z in FP32 by the softmax's exponential: core 0 the exponential itself
+ * (correctly rounded), else 2^floor(z) p(z - floor z) with the core p in
+ * target precision (z clamped below at -16384).  The power of two is applied
+ * relative to 2^ref (an integer). */
+static double exp2_fp32(int core, float z, double ref)
+{
+    if (core == 0) return (double)(float)exp2((double)z - ref);
+    if (z < -16384.0f) z = -16384.0f;
+    const double n = floor((double)z);
+    const float f = (float)((double)z - n);      /* exact */
+    return (double)(float)ldexp((double)orc_exp2_core_target(core, f), (int)(n - ref));
+}
+
+/* Softmax weights of one softcap row (real-arithmetic model) with a
+ * software exp2: 2^z = 2^floor(z) p(z - floor(z)), z = RN32(t RN32(cap
+ * log2 e)), relative to the row's largest floor(z).  Returns the natural
+ * log-sum-exp; w holds the normalised weights. */
+static double exp2_core_weights(const actx *c, const double *t, double *w, int64_t nk)
+{
+    double M = -INFINITY;
+    for (int64_t j = 0; j < nk; j++) {
+        const double n = floor((double)orc_mul_f32((float)t[j], c->c2));
+        if (n > M) M = n;
+    }
+    double l = 0.0;
+    for (int64_t j = 0; j < nk; j++) {
+        w[j] = exp2_fp32(c->a->exp2_core, orc_mul_f32((float)t[j], c->c2), M);
+        l += w[j];
+    }
+    for (int64_t j = 0; j < nk; j++) w[j] /= l;
+    return (M + log2(l)) * LN2;
+}
+
+/* Softmax of one softcap row in the replay model: P_j in FP32 (see the
+ * header), l the sum of the FP32 P_j, w_j = RN_bf16(P_j) / l.  Returns the
+ * natural log-sum-exp. */
+static double softcap_row_replay(const actx *c, const double *t, double *w, int64_t nk)
+{
+    const int core = c->a->exp2_core;
+    double ref = 0.0;
+    if (core == 0 && c->sref) {
+        for (int64_t j = 0; j < nk; j++)
+            w[j] = (double)(float)exp2((double)orc_fma_f32((float)t[j], c->c2, -c->mref));
+        ref = c->mref;
+    } else {
+        ref = -INFINITY;
+        for (int64_t j = 0; j < nk; j++) {
+            float z = orc_mul_f32((float)t[j], c->c2);
+            if (z < -16384.0f) z = -16384.0f;
+            const double n = floor((double)z);
+            if (n > ref) ref = n;
+        }
+        for (int64_t j = 0; j < nk; j++)
+            w[j] = exp2_fp32(core, orc_mul_f32((float)t[j], c->c2), ref);
+    }
+    double l = 0.0;
+    for (int64_t j = 0; j < nk; j++) l += w[j];
+    for (int64_t j = 0; j < nk; j++) w[j] = bf16r(w[j]) / l;
+    return (ref + log2(l)) * LN2;
 }
 
 static double dot_bf16(const uint16_t *x, const uint16_t *y, int D)
@@ -389,30 +486,17 @@ static double dot_bf16(const uint16_t *x, const uint16_t *y, int D)
     return s;
 }
 
-/* Softmax weights of one row with a software exp2: z = RN32(t RN32(cap
- * log2 e)) from the program's FP16 t, 2^z = 2^floor(z) p(z - floor(z)) with p
- * the core in target precision; the weights are taken relative to the row's
- * largest floor(z) (an exact power of two, which the normalisation cancels).
- * Returns the natural log-sum-exp. */
-static double exp2_core_weights(const actx *c, const double *t, double *w, int64_t nk)
+/* P of one sigmoid-attention score: the program value (BF16) or sigma. */
+static double sigmoid_p(const actx *c, double Sr, uint16_t *g)
 {
-    const float c2 = (float)((double)c->a->cap * 1.4426950408889634074);
-    double M = -INFINITY;
-    for (int64_t j = 0; j < nk; j++) {
-        const float z = orc_mul_f32((float)t[j], c2);
-        const double n = floor((double)z);
-        if (n > M) M = n;
+    const orc_attn *a = c->a;
+    if (a->kind == ORC_ATTN_SIGMOID_POLY) {
+        const uint16_t x = orc_f64_to_bf16((double)orc_mul_f32((float)Sr, c->scale));
+        return orc_bf16_to_f64(sig_eval(&c->fs, a->sig, x, g));
     }
-    double l = 0.0;
-    for (int64_t j = 0; j < nk; j++) {
-        const float z = orc_mul_f32((float)t[j], c2);
-        const double n = floor((double)z);
-        const float f = (float)((double)z - n);      /* exact */
-        w[j] = ldexp((double)orc_exp2_core_target(c->a->exp2_core, f), (int)(n - M));
-        l += w[j];
-    }
-    for (int64_t j = 0; j < nk; j++) w[j] /= l;
-    return (M + log2(l)) * 0.69314718055994530942;
+    if (a->replay)
+        return (double)(float)stable_sigmoid((double)orc_fma_f32((float)Sr, c->scale, -c->logn32));
+    return stable_sigmoid(Sr * c->rsd - c->logn);
 }
 
 int orc_attn_fwd_rows(const orc_attn *a, const uint16_t *q, const uint16_t *k,
@@ -434,22 +518,31 @@ int orc_attn_fwd_rows(const orc_attn *a, const uint16_t *q, const uint16_t *k,
             const int64_t b = bh / a->H, h = bh % a->H;
             const int64_t kvb = (b * a->Hkv + h / G) * S * D;
             const int64_t nk = a->causal ? i + 1 : S;
-            double m = -INFINITY, dummy;
-            for (int64_t j = 0; j < nk; j++) {
-                score(&c, dot_bf16(q + r * D, k + kvb + j * D, (int)D), &w[j], &dummy);
-                if (w[j] > m) m = w[j];
-            }
-            if (a->exp2_core) {
-                for (int64_t j = 0; j < nk; j++) w[j] /= (double)a->cap;   /* t, exactly */
-                const double ls = exp2_core_weights(&c, w, w, nk);
+            if (is_softcap(a)) {
+                double dummy, ls;
+                for (int64_t j = 0; j < nk; j++)
+                    softcap_t(&c, dot_bf16(q + r * D, k + kvb + j * D, (int)D), &w[j], &dummy);
+                if (a->replay) {
+                    ls = softcap_row_replay(&c, w, w, nk);
+                } else if (a->exp2_core) {
+                    ls = exp2_core_weights(&c, w, w, nk);
+                } else {
+                    double m = -INFINITY, l = 0.0;
+                    for (int64_t j = 0; j < nk; j++) {
+                        w[j] *= (double)a->cap;
+                        if (w[j] > m) m = w[j];
+                    }
+                    for (int64_t j = 0; j < nk; j++) { w[j] = exp(w[j] - m); l += w[j]; }
+                    for (int64_t j = 0; j < nk; j++) w[j] /= l;
+                    ls = m + log(l);
+                }
                 if (lse) lse[ri] = ls;
-            } else if (is_softcap(a)) {
-                double l = 0.0;
-                for (int64_t j = 0; j < nk; j++) { w[j] = exp(w[j] - m); l += w[j]; }
-                for (int64_t j = 0; j < nk; j++) w[j] /= l;
-                if (lse) lse[ri] = m + log(l);
-            } else if (lse) {
-                lse[ri] = NAN;
+            } else {
+                for (int64_t j = 0; j < nk; j++) {
+                    const double p = sigmoid_p(&c, dot_bf16(q + r * D, k + kvb + j * D, (int)D), NULL);
+                    w[j] = a->replay ? bf16r(p) : p;
+                }
+                if (lse) lse[ri] = NAN;
             }
             for (int64_t d = 0; d < D; d++) {
                 double o = 0.0, n2 = 0.0;
@@ -467,46 +560,80 @@ int orc_attn_fwd_rows(const orc_attn *a, const uint16_t *q, const uint16_t *k,
     return 0;
 }
 
-/* dS_ij and P_ij of one (query row, key row) pair, and two error scales of
- * an FP32 evaluation of dS:
+/* P_ij and dS_ij of one (query row, key row) pair as the products use them
+ * (BF16-rounded in the replay model), and two scales of an FP32 evaluation
+ * of dS:
  *   cs  |dS / (dP - Delta)| (softcap) or |dS / dP| (sigmoid) times the sum of
  *       the absolute products that form dP - Delta (or dP);
- *   sd  |dS / g|, g the derivative of the transform before the 1/sqrt(D) or
- *       cap / (cap sqrt D) chain factor: the sensitivity to an absolute error
- *       in g (e.g. 1 - tanh^2 formed from a rounded tanh). */
+ *   sd  |dS / g|, g the transform's derivative before the chain factor: the
+ *       sensitivity to an absolute error in g.
+ * delta_i is Delta_i (RN32 of it in the replay model), lse_i the row's
+ * log-sum-exp (softcap). */
 static void pair_grad(const actx *c, const uint16_t *qi, const uint16_t *kj,
                       const uint16_t *vj, const uint16_t *doi, const double *oi,
                       double lse_i, double delta_i, double *P, double *dS, double *cs,
                       double *sd)
 {
-    const int D = c->a->D;
-    double val, dval;
-    score(c, dot_bf16(qi, kj, D), &val, &dval);
+    const orc_attn *a = c->a;
+    const int D = a->D;
+    const double Sr = dot_bf16(qi, kj, D);
     const double dP = dot_bf16(doi, vj, D);
-    double a = 0.0;
+    double ab = 0.0;
     for (int d = 0; d < D; d++) {
         const double g = fabs(orc_bf16_to_f64(doi[d]));
-        a += g * fabs(orc_bf16_to_f64(vj[d]));
-        if (oi) a += g * fabs(oi[d]);
+        ab += g * fabs(orc_bf16_to_f64(vj[d]));
+        if (oi) ab += g * fabs(oi[d]);
     }
-    if (is_softcap(c->a)) {
-        *P = exp(val - lse_i);
-        *dS = *P * (dP - delta_i) * dval;
-        *cs = fabs(*P * dval) * a;
-        *sd = fabs(*P * (dP - delta_i)) * c->rsd;
+    if (is_softcap(a)) {
+        double t, dq;
+        softcap_t(c, Sr, &t, &dq);
+        if (a->replay) {
+            const float nl = -orc_mul_f32((float)lse_i, (float)LOG2E);
+            const float p = (float)exp2_fp32(a->exp2_core, orc_fma_f32((float)t, c->c2, nl), 0.0);
+            const float u = orc_add_f32((float)dP, -(float)delta_i);
+            const float ds = orc_mul_f32((float)dq, orc_mul_f32(p, u));
+            *P = bf16r(p);
+            *dS = bf16r(ds);
+            *cs = fabs((double)p * dq) * ab;
+            *sd = fabs((double)p * u);
+        } else {
+            /* the program sees RN32(S scale); the exact transform S itself */
+            const double dval = a->kind == ORC_ATTN_SOFTCAP_POLY
+                                    ? (double)a->cap * (double)c->scale * dq : dq * c->rsd;
+            *P = exp((double)a->cap * t - lse_i);
+            *dS = *P * (dP - delta_i) * dval;
+            *cs = fabs(*P * dval) * ab;
+            *sd = fabs(*P * (dP - delta_i)) * c->rsd;
+        }
+        return;
+    }
+    uint16_t g = 0;
+    const double p = sigmoid_p(c, Sr, &g);
+    double dval;
+    if (a->kind == ORC_ATTN_SIGMOID_POLY) {
+        dval = orc_bf16_to_f64(g);
+        if (!a->replay) dval *= (double)c->scale;
+    } else if (a->replay) {
+        dval = orc_mul_f32((float)p, orc_add_f32(1.0f, -(float)p));
     } else {
-        *P = val;
-        *dS = dP * dval;
-        *cs = fabs(dval) * a;
-        *sd = fabs(dP) * c->rsd;
+        dval = p * (1.0 - p) * c->rsd;
     }
+    if (a->replay) {
+        *P = bf16r(p);
+        *dS = bf16r(orc_mul_f32((float)dP, (float)dval));
+    } else {
+        *P = p;
+        *dS = dP * dval;
+    }
+    *cs = fabs(dval) * ab;
+    *sd = fabs(dP) * (a->replay ? 1.0 : c->rsd);
 }
 
-static double row_delta(const uint16_t *doi, const double *oi, int D)
+static double row_delta(const actx *c, const uint16_t *doi, const double *oi, int D)
 {
     double s = 0.0;
     for (int d = 0; d < D; d++) s += orc_bf16_to_f64(doi[d]) * oi[d];
-    return s;
+    return c->a->replay ? (double)(float)s : s;
 }
 
 int orc_attn_bwd_rows(const orc_attn *a, const uint16_t *q, const uint16_t *k,
@@ -519,8 +646,12 @@ int orc_attn_bwd_rows(const orc_attn *a, const uint16_t *q, const uint16_t *k,
     actx c;
     const int rc = actx_init(&c, a);
     if (rc) return rc;
+    if (a->exp2_core && a->kind != ORC_ATTN_SOFTCAP_POLY) return -3;
     const int64_t S = a->S, D = a->D, G = a->H / a->Hkv;
     const int sc = is_softcap(a);
+    /* replay: dQ, dK scaled by RN32(1 / sqrt D) at the end; the real model
+     * carries the chain factor inside dS */
+    const double fin = a->replay ? (double)c.rsd32 : 1.0;
     /* dQ rows */
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t ri = 0; ri < nq; ri++) {
@@ -528,7 +659,7 @@ int orc_attn_bwd_rows(const orc_attn *a, const uint16_t *q, const uint16_t *k,
         const int64_t bh = r / S, i = r % S;
         const int64_t b = bh / a->H, h = bh % a->H;
         const int64_t kvb = (b * a->Hkv + h / G) * S * D;
-        const double delta = sc ? row_delta(dout + r * D, o + r * D, (int)D) : 0.0;
+        const double delta = sc ? row_delta(&c, dout + r * D, o + r * D, (int)D) : 0.0;
         const double li = sc ? lse[r] : 0.0;
         const int64_t n = a->causal ? i + 1 : S;
         for (int64_t d = 0; d < D; d++) {
@@ -550,8 +681,12 @@ int orc_attn_bwd_rows(const orc_attn *a, const uint16_t *q, const uint16_t *k,
                 if (sd_dq) sd_dq[ri * D + d] += sd * fabs(kd);
             }
         }
-        if (nz_dq)
-            for (int64_t d = 0; d < D; d++) nz_dq[ri * D + d] = sqrt(nz_dq[ri * D + d]);
+        for (int64_t d = 0; d < D; d++) {
+            dq[ri * D + d] *= fin;
+            if (nz_dq) nz_dq[ri * D + d] = sqrt(nz_dq[ri * D + d]) * fin;
+            if (cs_dq) cs_dq[ri * D + d] *= fin;
+            if (sd_dq) sd_dq[ri * D + d] *= fin;
+        }
     }
     /* dK, dV rows: key row r = (b Hkv + hk) S + j */
 #pragma omp parallel for schedule(dynamic, 1)
@@ -570,7 +705,7 @@ int orc_attn_bwd_rows(const orc_attn *a, const uint16_t *q, const uint16_t *k,
             const int64_t qb = (b * a->H + h) * S;
             for (int64_t i = a->causal ? j : 0; i < S; i++) {
                 const int64_t qr = qb + i;
-                const double delta = sc ? row_delta(dout + qr * D, o + qr * D, (int)D) : 0.0;
+                const double delta = sc ? row_delta(&c, dout + qr * D, o + qr * D, (int)D) : 0.0;
                 double P, dS, cs, sd;
                 pair_grad(&c, q + qr * D, k + r * D, v + r * D, dout + qr * D,
                           sc ? o + qr * D : NULL, sc ? lse[qr] : 0.0, delta, &P, &dS, &cs,
@@ -589,8 +724,11 @@ int orc_attn_bwd_rows(const orc_attn *a, const uint16_t *q, const uint16_t *k,
             }
         }
         for (int64_t d = 0; d < D; d++) {
-            if (nz_dk) nz_dk[ri * D + d] = sqrt(nz_dk[ri * D + d]);
+            dk[ri * D + d] *= fin;
+            if (nz_dk) nz_dk[ri * D + d] = sqrt(nz_dk[ri * D + d]) * fin;
             if (nz_dv) nz_dv[ri * D + d] = sqrt(nz_dv[ri * D + d]);
+            if (cs_dk) cs_dk[ri * D + d] *= fin;
+            if (sd_dk) sd_dk[ri * D + d] *= fin;
         }
     }
     return 0;

@@ -102,6 +102,7 @@ def run_both(orc, kind, q, k, v, do, causal, transform, softmax, **kw):
     o_ref, lse_ref = textbook(qt, kt, vt, causal, transform, softmax)
     (o_ref * torch.from_numpy(bf16v(do))).sum().backward()
     rows = np.arange(B * H * S)
+    kw.setdefault("replay", False)
     o, lse, noise = orc.attn_fwd_rows(kind, q, k, v, rows, causal=causal, **kw)
     o_exact = o_ref.detach().numpy()
     lse_exact = None if lse_ref is None else lse_ref.detach().numpy()
@@ -144,37 +145,55 @@ def test_sigmoid_exact_fwd_bwd_vs_autograd(orc, B, H, Hkv, S, D, causal):
     assert np.all(np.isnan(got["lse"]))
 
 
-def softcap_tables(orc, tanh_prog, cap, D):
-    """The oracle's elementwise FP16 programs as functions of the raw score."""
-    scale = np.float32(1.0 / (cap * np.sqrt(D)))
+def program_tables(orc, tanh_prog, fmt):
+    """The tanh program and its derivative program over every 16-bit input of
+    the format (values), and the map from an FP32 scaled score to the input's
+    bits."""
     allx = np.arange(65536, dtype=np.uint16)
-    t_tab = f16v(orc.act_fwd(tanh_prog, allx, 1))
-    d_tab = f16v(orc.dtanh_prog_f16(tanh_prog, allx))
+    vals = f16v if fmt == "f16" else bf16v
+    t_tab = vals(orc.act_fwd(tanh_prog, allx, orc.TANH_ORDERS[fmt]))
+    d_tab = vals(orc.dtanh_prog(tanh_prog, allx, fmt))
 
-    def xbits(s):
-        return (s.astype(np.float32) * scale).astype(np.float32).astype(np.float16).view(np.uint16)
-    return (lambda s: cap * t_tab[xbits(s)],
-            lambda s: cap * np.float64(scale) * d_tab[xbits(s)])
+    def xbits(xs):
+        xs = np.asarray(xs, dtype=np.float64).astype(np.float32)
+        if fmt == "f16":
+            return xs.astype(np.float16).view(np.uint16)
+        return bf16_bits(xs.astype(np.float64))
+    return t_tab, d_tab, xbits
 
 
+def softcap_tables(orc, tanh_prog, cap, D, fmt="f16"):
+    """The oracle's elementwise programs as functions of the raw score."""
+    scale = np.float32(1.0 / (cap * np.sqrt(D)))
+    t_tab, d_tab, xbits = program_tables(orc, tanh_prog, fmt)
+
+    def xb(s):
+        return xbits((s.astype(np.float32) * scale).astype(np.float32))
+    return (lambda s: cap * t_tab[xb(s)],
+            lambda s: cap * np.float64(scale) * d_tab[xb(s)])
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "f16"])
 @pytest.mark.parametrize("B,H,Hkv,S,D,causal", CASES)
-def test_softcap_poly_chain_rule_exact(orc, tanh_prog, B, H, Hkv, S, D, causal):
+def test_softcap_poly_chain_rule_exact(orc, tanh_prog, B, H, Hkv, S, D, causal, fmt):
     """With the program values as the transform, the oracle's poly attention
-    equals autograd of textbook attention to rounding."""
+    (real-arithmetic model) equals autograd of textbook attention to
+    rounding, for either program format."""
     cap = 1.0
     q, k, v, do = inputs(B, H, Hkv, S, D, sd_q=0.7, seed=S + 2)
-    val, der = softcap_tables(orc, tanh_prog, cap, D)
+    val, der = softcap_tables(orc, tanh_prog, cap, D, fmt)
     got, ref = run_both(orc, orc.ATTN_SOFTCAP_POLY, q, k, v, do, causal, table_fn(val, der),
-                        True, cap=cap, tanh_prog=tanh_prog)
+                        True, cap=cap, tanh_prog=tanh_prog, tanh_fmt=fmt)
     for name in ("o", "lse", "dq", "dk", "dv"):
         close(got[name], ref[name], 1e-12)
 
 
 def test_softcap_poly_backward_is_derivative_of_forward(orc, tanh_prog):
     """Autograd of the real-arithmetic D4 polynomial (BF16 coefficients, no
-    rounding anywhere) against the oracle's FP16 forward and differentiated
-    backward: they differ only by FP16 rounding (~1e-3), while a wrong
-    derivative coefficient moves the gradients by ~1e-1."""
+    rounding anywhere) against the oracle's forward and differentiated
+    backward in either format: they differ only by the program's rounding
+    (~1e-3 in FP16, a few 1e-3 in BF16), while a wrong derivative coefficient
+    moves the gradients by ~1e-1."""
     B, H, Hkv, S, D, cap = 1, 2, 1, 48, 16, 1.0
     q, k, v, do = inputs(B, H, Hkv, S, D, sd_q=0.45, seed=5)
     c = [bf16v(np.array([b], np.uint16))[0] for b in tanh_prog.coeff_bits()]
@@ -186,10 +205,11 @@ def test_softcap_poly_backward_is_derivative_of_forward(orc, tanh_prog):
         a = u.abs()
         p = sum(cj * a ** j for j, cj in enumerate(c))
         return cap * torch.sign(u) * p
-    got, ref = run_both(orc, orc.ATTN_SOFTCAP_POLY, q, k, v, do, True, real_tanh, True,
-                        cap=cap, tanh_prog=tanh_prog)
-    for name in ("o", "dq", "dk", "dv"):
-        close(got[name], ref[name], 1e-2)
+    for fmt in ("bf16", "f16"):
+        got, ref = run_both(orc, orc.ATTN_SOFTCAP_POLY, q, k, v, do, True, real_tanh, True,
+                            cap=cap, tanh_prog=tanh_prog, tanh_fmt=fmt)
+        for name in ("o", "dq", "dk", "dv"):
+            close(got[name], ref[name], 1e-2)
 
 
 def sigmoid_tables(orc, sp, D):
@@ -264,21 +284,30 @@ def test_b3_program_range(orc, sig_prog, order):
     assert np.all(pv >= 0) and np.max(pv) < 0.06
 
 
-def test_dtanh_program_is_derivative_of_tanh_program(orc, tanh_prog):
-    """q(x) = p'(min(|x|, Lc)) in FP16: against a central difference of the
-    real polynomial (orc_prog_real), to FP16 Horner accuracy."""
-    allx = np.arange(0, 0x7C00, dtype=np.uint16)
-    xv = f16v(allx)
-    keep = xv < tanh_prog.Lc
+@pytest.mark.parametrize("fmt,tol", [("f16", 3e-3), ("bf16", 1.2e-2)])
+def test_dtanh_program_is_derivative_of_tanh_program(orc, tanh_prog, fmt, tol):
+    """q(x) = p'(|x|) for |x| <= Lc: against a central difference of the real
+    polynomial (orc_prog_real), to the format's Horner accuracy; beyond the
+    clamp the forward program is constant and its derivative is exactly 0."""
+    allx = np.arange(0, 0x7C00 if fmt == "f16" else 0x7F80, dtype=np.uint16)
+    xv = f16v(allx) if fmt == "f16" else bf16v(allx)
+    keep = xv <= tanh_prog.Lc
     xb, xv = allx[keep], xv[keep]
-    q = f16v(orc.dtanh_prog_f16(tanh_prog, xb))
+    qv = orc.dtanh_prog(tanh_prog, xb, fmt)
+    q = f16v(qv) if fmt == "f16" else bf16v(qv)
     L = orc.lib()
     h = 1e-6
-    fd = np.array([(L.orc_prog_real(tanh_prog, x + h) - L.orc_prog_real(tanh_prog, x - h)) / (2 * h)
-                   if x > h else (L.orc_prog_real(tanh_prog, x + h) - L.orc_prog_real(tanh_prog, x)) / h
-                   for x in xv])
-    assert np.max(np.abs(q - fd)) < 3e-3
-    # beyond the clamp the program holds its value at Lc
-    lc = np.float16(tanh_prog.Lc).view(np.uint16)
-    big = np.array([lc, 0x4500, 0x7BFF], np.uint16)
-    assert len(set(orc.dtanh_prog_f16(tanh_prog, big).tolist())) == 1
+    Lc = tanh_prog.Lc
+
+    def fdiff(x):   # one-sided at 0 and at the clamp (the real program is flat beyond)
+        lo, hi = (x, x + h) if x <= h else ((x - h, x) if x >= Lc - h else (x - h, x + h))
+        return (L.orc_prog_real(tanh_prog, hi) - L.orc_prog_real(tanh_prog, lo)) / (hi - lo)
+    fd = np.array([fdiff(x) for x in xv])
+    assert np.max(np.abs(q - fd)) < tol
+    # beyond the clamp, either sign: 0
+    big = allx[~keep]
+    for sign in (0, 0x8000):
+        assert not np.any(orc.dtanh_prog(tanh_prog, big | sign, fmt))
+    # the derivative's coefficients are the forward's (j + 1) c_{j+1} in the
+    # format: q(0) = c_1 exactly
+    assert q[0] == bf16v(np.array([tanh_prog.c[1]], np.uint16))[0]
