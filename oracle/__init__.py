@@ -112,7 +112,7 @@ def lib():
                                             C.c_void_p, i64, C.c_void_p, C.c_void_p,
                                             C.c_void_p]),
             "orc_attn_bwd_rows": (C.c_int, [P(Attn)] + [C.c_void_p] * 7 + [i64, C.c_void_p, i64]
-                                  + [C.c_void_p] * 10),
+                                  + [C.c_void_p] * 6),
             "orc_dtanh_prog_f16": (u16, [P(Prog), u16]),
             "orc_dtanh_prog": (u16, [P(Prog), u16, C.c_int]),
             "orc_exp2_core": (f64, [C.c_int, f64, f64]),
@@ -252,24 +252,26 @@ def attn_fwd_rows(kind: int, q, k, v, rows, cap: float = 50.0, causal: bool = Tr
                   tanh_prog: Prog = None, sig: SigProg = None, order: int = 0,
                   exp2_core: int = 0, tanh_fmt: str = "bf16", replay: bool = True):
     """q: uint16 BF16 bits [B, H, S, D]; k, v: [B, Hkv, S, D].  Returns (O, lse,
-    noise) in float64 for the flat query rows (b H + h) S + i: O and noise
+    spread) in float64 for the flat query rows (b H + h) S + i: O and spread
     [len(rows), D], lse [len(rows)] (NaN for sigmoid attention).  exp2_core
     (softcap poly only): the softmax's exponentials by that fractional core.
     tanh_fmt: format of the softcap program ("bf16", the pages' path, or
     "f16").  replay: the method's FP32 steps and BF16 rounding of P (True) or
-    real arithmetic around the programs (False)."""
+    real arithmetic around the programs (False).  spread: per output, the
+    largest change that admissible alternatives of the replay's rounding
+    decisions can cause (0 without replay)."""
     q, k, v = _u16(q), _u16(k), _u16(v)
     D = q.shape[3]
     rows = np.ascontiguousarray(rows, dtype=np.int64)
     out = np.zeros((rows.size, D))
     lse = np.zeros(rows.size)
-    noise = np.zeros((rows.size, D))
+    spread = np.zeros((rows.size, D))
     a = _attn(kind, q, k, cap, causal, tanh_prog, sig, order, exp2_core, tanh_fmt, replay)
     rc = lib().orc_attn_fwd_rows(C.byref(a), _ptr(q), _ptr(k), _ptr(v), _ptr(rows), rows.size,
-                                 _ptr(out), _ptr(lse), _ptr(noise))
+                                 _ptr(out), _ptr(lse), _ptr(spread))
     if rc:
         raise ValueError(f"orc_attn_fwd_rows: {rc}")
-    return out, lse, noise
+    return out, lse, spread
 
 
 def attn_bwd_rows(kind: int, q, k, v, o, dout, lse, qrows, krows, cap: float = 50.0,
@@ -279,18 +281,16 @@ def attn_bwd_rows(kind: int, q, k, v, o, dout, lse, qrows, krows, cap: float = 5
     """Gradients of sum(O * dout) for the flat query rows (dQ) and key rows
     (b Hkv + hk) S + j (dK, dV).  o: float64 [B, H, S, D] (the forward output
     the backward is given), lse: float64 [B, H, S] (softcap only).  Returns
-    (dq, dk, dv, nz_dq, nz_dk, nz_dv, cs_dq, cs_dk, sd_dq, sd_dk), float64
-    [rows, D] each: the gradients, their noise scales, their cancellation
-    scales and their sensitivity to an absolute error in the transform's
-    derivative.  tanh_fmt, replay, exp2_core: as attn_fwd_rows."""
+    (dq, dk, dv, sp_dq, sp_dk, sp_dv), float64 [rows, D] each: the gradients
+    and their spreads (as attn_fwd_rows).  tanh_fmt, replay, exp2_core: as
+    attn_fwd_rows."""
     q, k, v, dout = _u16(q), _u16(k), _u16(v), _u16(dout)
     D = q.shape[3]
     o = np.ascontiguousarray(o, dtype=np.float64)
     lse = np.ascontiguousarray(np.zeros(1) if lse is None else lse, dtype=np.float64)
     qrows = np.ascontiguousarray(qrows, dtype=np.int64)
     krows = np.ascontiguousarray(krows, dtype=np.int64)
-    res = [np.zeros((n, D)) for n in (qrows.size, krows.size, krows.size) * 2
-           + (qrows.size, krows.size) * 2]
+    res = [np.zeros((n, D)) for n in (qrows.size, krows.size, krows.size) * 2]
     a = _attn(kind, q, k, cap, causal, tanh_prog, sig, order, exp2_core, tanh_fmt, replay)
     rc = lib().orc_attn_bwd_rows(C.byref(a), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout),
                                  _ptr(lse), _ptr(qrows), qrows.size, _ptr(krows), krows.size,

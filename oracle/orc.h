@@ -147,16 +147,17 @@ typedef struct {
 } orc_attn;
 
 /* Returns 0, or -1 (sequence length differs from the sigmoid program's n),
- * -2 (bad shape), -3 (unknown kind). */
+ * -2 (bad shape), -3 (unknown kind).  spread (nullable): per output, the
+ * largest change admissible alternatives of the replay model's rounding
+ * decisions can cause (orc_eval.c); 0 in the real-arithmetic model. */
 int orc_attn_fwd_rows(const orc_attn *a, const uint16_t *q, const uint16_t *k,
                       const uint16_t *v, const int64_t *rows, int64_t n_rows,
-                      double *out, double *lse, double *noise);
+                      double *out, double *lse, double *spread);
 int orc_attn_bwd_rows(const orc_attn *a, const uint16_t *q, const uint16_t *k,
                       const uint16_t *v, const double *o, const uint16_t *dout,
                       const double *lse, const int64_t *qrows, int64_t nq,
                       const int64_t *krows, int64_t nk, double *dq, double *dk,
-                      double *dv, double *nz_dq, double *nz_dk, double *nz_dv,
-                      double *cs_dq, double *cs_dk, double *sd_dq, double *sd_dk);
+                      double *dv, double *sp_dq, double *sp_dk, double *sp_dv);
 /* The analytic derivative of the softcap tanh program at x (bits in the
  * format of `order`): the D3 with coefficients (j + 1) c_{j+1} (exact in
  * FP16; rounded to BF16 for the BF16 program) at |x|, 0 beyond the clamp. */

@@ -276,9 +276,27 @@ void orc_swiglu_bwd(const orc_prog *sig, const uint16_t *gate, const uint16_t *u
  *   sigmoid: dS_ij = dP_ij dP/dS;
  *   dQ_i = sum_j dS_ij K_j;   dK_j = sum over query heads of the group and
  *   visible i of dS_ij Q_i.
- * Each output also gets a noise scale sqrt(sum of squared terms), and dQ / dK
- * two further scales (see pair_grad); these are diagnostics that do not
- * enter the values. */
+ *
+ * Several results are correct.  The pages fix the precision of each step but
+ * not the order in which an FP32 dot product accumulates, nor the last bit of
+ * an FP32 exponential, so the replay model's rounding decisions (the program
+ * input x, the BF16 P, the BF16 dS) can go either way where the value that
+ * is rounded lies close to a rounding boundary.  The oracle therefore also
+ * returns, per output, the spread: the largest change of that output that
+ * admissible alternatives of those decisions can cause, each score taken on
+ * its own (first order in l for the forward):
+ *   raw score and dP: any FP32 value within 8 u sum |a_d b_d| of the exact
+ *     dot product (u = 2^-24; an FP32 accumulation that rounds once per 16
+ *     products, the depth of one BF16 matrix instruction);
+ *   Delta: any FP32 value within 128 u sum |dO_d O_d| (any order);
+ *   the hardware exponential 2^z: the correctly rounded FP32 value or a
+ *     neighbour (1 ulp); the software exp2 cores are exact FP32 arithmetic;
+ *   the comparators' tanh and sigma: within 4 ulps of the correctly rounded
+ *     FP32 value.
+ * The spread is 0 in the real-arithmetic model. */
+
+#define U32 5.9604644775390625e-08   /* 2^-24 */
+#define XC_MAX 64
 
 static const double LOG2E = 1.4426950408889634074;
 static const double LN2 = 0.69314718055994530942;
@@ -342,6 +360,98 @@ uint16_t orc_sig_prog_eval(const orc_sig_prog *sp, uint16_t x, int order, uint16
     return sig_eval(&f, sp, x, grad);
 }
 
+static int is_softcap(const orc_attn *a)
+{
+    return a->kind == ORC_ATTN_SOFTCAP_POLY || a->kind == ORC_ATTN_SOFTCAP_EXACT;
+}
+
+static double bf16r(double v)
+{
+    return orc_bf16_to_f64(orc_f64_to_bf16(v));
+}
+
+/* Smallest FP32 value >= v and largest FP32 value <= v. */
+static float ru32(double v)
+{
+    float f = (float)v;
+    if ((double)f < v) f = nextafterf(f, INFINITY);
+    return f;
+}
+
+static float rd32(double v)
+{
+    float f = (float)v;
+    if ((double)f > v) f = nextafterf(f, -INFINITY);
+    return f;
+}
+
+/* x +- k ulps of FP32 */
+static float ulps32(float x, int k)
+{
+    for (int i = 0; i < (k < 0 ? -k : k); i++) x = nextafterf(x, k < 0 ? -INFINITY : INFINITY);
+    return x;
+}
+
+/* Exact dot product of two BF16 rows and the sum of the absolute products. */
+static double dot_bf16(const uint16_t *x, const uint16_t *y, int D, double *abs_sum)
+{
+    double s = 0.0, a = 0.0;
+    for (int d = 0; d < D; d++) {
+        const double p = orc_bf16_to_f64(x[d]) * orc_bf16_to_f64(y[d]);
+        s += p;
+        a += fabs(p);
+    }
+    if (abs_sum) *abs_sum = a;
+    return s;
+}
+
+/* The admissible FP32 values of a dot product: RN32 of the exact value and
+ * every FP32 value within eps of it. */
+typedef struct { float v, lo, hi; } f32r;
+
+static f32r fp32_range(double exact, double eps)
+{
+    f32r r;
+    r.v = (float)exact;
+    r.lo = ru32(exact - eps);
+    r.hi = rd32(exact + eps);
+    if (r.lo > r.v) r.lo = r.v;
+    if (r.hi < r.v) r.hi = r.v;
+    return r;
+}
+
+/* Order key of a 16-bit float pattern (monotone in value; +-0 -> 0). */
+static int fkey(uint16_t b)
+{
+    return (b & 0x8000) ? -(int)(b & 0x7FFF) : (int)(b & 0x7FFF);
+}
+
+static uint16_t fbits(int k)
+{
+    return k >= 0 ? (uint16_t)k : (uint16_t)(0x8000 | (uint16_t)(-k));
+}
+
+/* The program inputs x in format f reachable from scaled scores in
+ * [xs_lo, xs_hi] (RN to the format is monotone): every format value between
+ * the two roundings, x0 first.  More than XC_MAX values occur only where the
+ * range straddles zero, where every program in use is RN(c_1 t) to first
+ * order and monotone, so the two ends stand for the rest.  Returns the count. */
+static int x_cands(const fmt_ops *f, float xs0, float xs_lo, float xs_hi, uint16_t *out)
+{
+    const uint16_t x0 = enc(f, (double)xs0);
+    const int k0 = fkey(enc(f, (double)xs_lo)), k1 = fkey(enc(f, (double)xs_hi));
+    int n = 0;
+    out[n++] = x0;
+    if (k1 - k0 + 1 > XC_MAX) {
+        if (fbits(k0) != x0) out[n++] = fbits(k0);
+        if (fbits(k1) != x0) out[n++] = fbits(k1);
+        return n;
+    }
+    for (int k = k0; k <= k1; k++)
+        if (k != fkey(x0)) out[n++] = fbits(k);
+    return n;
+}
+
 typedef struct {
     const orc_attn *a;
     fmt_ops ft;       /* format of the softcap program */
@@ -389,38 +499,45 @@ static int actx_init(actx *c, const orc_attn *a)
     }
 }
 
-static int is_softcap(const orc_attn *a)
-{
-    return a->kind == ORC_ATTN_SOFTCAP_POLY || a->kind == ORC_ATTN_SOFTCAP_EXACT;
-}
+/* ---- real-arithmetic model ----------------------------------------------- */
 
-static double bf16r(double v)
-{
-    return orc_bf16_to_f64(orc_f64_to_bf16(v));
-}
-
-/* Softcap: tanh value t and derivative value q' (of t with respect to the
- * scaled score x) at raw score Sr. */
-static void softcap_t(const actx *c, double Sr, double *t, double *dq)
+/* Transformed score of raw score Sr: the logit (softcap) or the probability
+ * (sigmoid), and its derivative with respect to Sr. */
+static void score_real(const actx *c, double Sr, double *value, double *dval)
 {
     const orc_attn *a = c->a;
-    if (a->kind == ORC_ATTN_SOFTCAP_POLY) {
+    switch (a->kind) {
+    case ORC_ATTN_SOFTCAP_POLY: {
         const uint16_t x = enc(&c->ft, (double)orc_mul_f32((float)Sr, c->scale));
-        *t = val(&c->ft, eval_one(&c->ft, a->tanh_prog, x));
-        *dq = val(&c->ft, dtanh_prog(&c->ft, a->tanh_prog, x));
-    } else if (a->replay) {
-        const float tt = (float)tanh((double)orc_mul_f32((float)Sr, c->scale));
-        *t = tt;
-        *dq = orc_fma_f32(-tt, tt, 1.0f);
-    } else {
-        *t = tanh(Sr / ((double)a->cap * sqrt((double)a->D)));
-        *dq = 1.0 - *t * *t;
+        *value = (double)a->cap * val(&c->ft, eval_one(&c->ft, a->tanh_prog, x));
+        *dval = (double)a->cap * (double)c->scale * val(&c->ft, dtanh_prog(&c->ft, a->tanh_prog, x));
+        return;
+    }
+    case ORC_ATTN_SOFTCAP_EXACT: {
+        const double t = tanh(Sr / ((double)a->cap * sqrt((double)a->D)));
+        *value = (double)a->cap * t;
+        *dval = (1.0 - t * t) * c->rsd;
+        return;
+    }
+    case ORC_ATTN_SIGMOID_POLY: {
+        const uint16_t x = orc_f64_to_bf16((double)orc_mul_f32((float)Sr, c->scale));
+        uint16_t g;
+        *value = orc_bf16_to_f64(sig_eval(&c->fs, a->sig, x, &g));
+        *dval = orc_bf16_to_f64(g) * (double)c->scale;
+        return;
+    }
+    default: {
+        const double p = stable_sigmoid(Sr * c->rsd - c->logn);
+        *value = p;
+        *dval = p * (1.0 - p) * c->rsd;
+        return;
+    }
     }
 }
 
 /* 2^z in FP32 by the softmax's exponential: core 0 the exponential itself
  * (correctly rounded), else 2^floor(z) p(z - floor z) with the core p in
- * target precision (z clamped below at -16384).  The power of two is applied
+ * target precision (z clamped below at -16384).  The power of two is taken
  * relative to 2^ref (an integer). */
 static double exp2_fp32(int core, float z, double ref)
 {
@@ -431,86 +548,125 @@ static double exp2_fp32(int core, float z, double ref)
     return (double)(float)ldexp((double)orc_exp2_core_target(core, f), (int)(n - ref));
 }
 
-/* Softmax weights of one softcap row (real-arithmetic model) with a
- * software exp2: 2^z = 2^floor(z) p(z - floor(z)), z = RN32(t RN32(cap
- * log2 e)), relative to the row's largest floor(z).  Returns the natural
- * log-sum-exp; w holds the normalised weights. */
-static double exp2_core_weights(const actx *c, const double *t, double *w, int64_t nk)
-{
-    double M = -INFINITY;
-    for (int64_t j = 0; j < nk; j++) {
-        const double n = floor((double)orc_mul_f32((float)t[j], c->c2));
-        if (n > M) M = n;
-    }
-    double l = 0.0;
-    for (int64_t j = 0; j < nk; j++) {
-        w[j] = exp2_fp32(c->a->exp2_core, orc_mul_f32((float)t[j], c->c2), M);
-        l += w[j];
-    }
-    for (int64_t j = 0; j < nk; j++) w[j] /= l;
-    return (M + log2(l)) * LN2;
-}
+/* ---- replay model: one score's rounding decisions --------------------------
+ * cand_t: the softcap's tanh value t and derivative value q' for every
+ * admissible program input (or comparator tanh); entry 0 is the primary. */
+typedef struct { int n; double t[XC_MAX + 2], d[XC_MAX + 2]; } tcands;
 
-/* Softmax of one softcap row in the replay model: P_j in FP32 (see the
- * header), l the sum of the FP32 P_j, w_j = RN_bf16(P_j) / l.  Returns the
- * natural log-sum-exp. */
-static double softcap_row_replay(const actx *c, const double *t, double *w, int64_t nk)
-{
-    const int core = c->a->exp2_core;
-    double ref = 0.0;
-    if (core == 0 && c->sref) {
-        for (int64_t j = 0; j < nk; j++)
-            w[j] = (double)(float)exp2((double)orc_fma_f32((float)t[j], c->c2, -c->mref));
-        ref = c->mref;
-    } else {
-        ref = -INFINITY;
-        for (int64_t j = 0; j < nk; j++) {
-            float z = orc_mul_f32((float)t[j], c->c2);
-            if (z < -16384.0f) z = -16384.0f;
-            const double n = floor((double)z);
-            if (n > ref) ref = n;
-        }
-        for (int64_t j = 0; j < nk; j++)
-            w[j] = exp2_fp32(core, orc_mul_f32((float)t[j], c->c2), ref);
-    }
-    double l = 0.0;
-    for (int64_t j = 0; j < nk; j++) l += w[j];
-    for (int64_t j = 0; j < nk; j++) w[j] = bf16r(w[j]) / l;
-    return (ref + log2(l)) * LN2;
-}
-
-static double dot_bf16(const uint16_t *x, const uint16_t *y, int D)
-{
-    double s = 0.0;
-    for (int d = 0; d < D; d++) s += orc_bf16_to_f64(x[d]) * orc_bf16_to_f64(y[d]);
-    return s;
-}
-
-/* P of one sigmoid-attention score: the program value (BF16) or sigma. */
-static double sigmoid_p(const actx *c, double Sr, uint16_t *g)
+static void softcap_cands(const actx *c, double S, double A, tcands *tc)
 {
     const orc_attn *a = c->a;
-    if (a->kind == ORC_ATTN_SIGMOID_POLY) {
-        const uint16_t x = orc_f64_to_bf16((double)orc_mul_f32((float)Sr, c->scale));
-        return orc_bf16_to_f64(sig_eval(&c->fs, a->sig, x, g));
+    const f32r s = fp32_range(S, 8.0 * U32 * A);
+    const float xs0 = orc_mul_f32(s.v, c->scale);
+    const float xlo = orc_mul_f32(s.lo, c->scale), xhi = orc_mul_f32(s.hi, c->scale);
+    if (a->kind == ORC_ATTN_SOFTCAP_POLY) {
+        uint16_t xb[XC_MAX + 2];
+        tc->n = x_cands(&c->ft, xs0, xlo, xhi, xb);
+        for (int i = 0; i < tc->n; i++) {
+            tc->t[i] = val(&c->ft, eval_one(&c->ft, a->tanh_prog, xb[i]));
+            tc->d[i] = val(&c->ft, dtanh_prog(&c->ft, a->tanh_prog, xb[i]));
+        }
+        return;
     }
-    if (a->replay)
-        return (double)(float)stable_sigmoid((double)orc_fma_f32((float)Sr, c->scale, -c->logn32));
-    return stable_sigmoid(Sr * c->rsd - c->logn);
+    /* comparator: FP32 tanh within 4 ulps; q' = RN32(1 - t^2) as one FMA */
+    const float t0 = (float)tanh((double)xs0);
+    const float tl = ulps32((float)tanh((double)xlo), -4), th = ulps32((float)tanh((double)xhi), 4);
+    const float ts[4] = {t0, tl, th, 0.0f};
+    tc->n = (tl < 0.0f && th > 0.0f) ? 4 : 3;
+    for (int i = 0; i < tc->n; i++) {
+        tc->t[i] = ts[i];
+        tc->d[i] = orc_fma_f32(-ts[i], ts[i], 1.0f);
+    }
 }
+
+/* FP32 P of the candidates: primary and [lo, hi], the hardware exponential
+ * taken within 1 ulp.  z = RN32(t c2 + zoff) when fused, else RN32(t c2)
+ * with the result relative to 2^ref. */
+static void p_range(const actx *c, const tcands *tc, int fused, float zoff, double ref,
+                    double *P0, double *Plo, double *Phi)
+{
+    const int core = c->a->exp2_core;
+    *Plo = INFINITY;
+    *Phi = -INFINITY;
+    for (int i = 0; i < tc->n; i++) {
+        const float z = fused ? orc_fma_f32((float)tc->t[i], c->c2, zoff)
+                              : orc_mul_f32((float)tc->t[i], c->c2);
+        const double p = exp2_fp32(core, z, ref);
+        if (i == 0) *P0 = p;
+        const double lo = core ? p : (double)ulps32((float)p, -1);
+        const double hi = core ? p : (double)ulps32((float)p, 1);
+        if (lo < *Plo) *Plo = lo;
+        if (hi > *Phi) *Phi = hi;
+    }
+}
+
+static double half_spread(double v0, double lo, double hi)
+{
+    return fmax(v0 - lo, hi - v0);
+}
+
+/* Sigmoid attention: P (primary, range) and derivative value g (primary,
+ * range) of one score. */
+static void sigmoid_cands(const actx *c, double S, double A, double *P0, double *Plo,
+                          double *Phi, double *g0, double *glo, double *ghi)
+{
+    const orc_attn *a = c->a;
+    const f32r s = fp32_range(S, 8.0 * U32 * A);
+    if (a->kind == ORC_ATTN_SIGMOID_POLY) {
+        uint16_t xb[XC_MAX + 2];
+        const int n = x_cands(&c->fs, orc_mul_f32(s.v, c->scale), orc_mul_f32(s.lo, c->scale),
+                              orc_mul_f32(s.hi, c->scale), xb);
+        *Plo = *glo = INFINITY;
+        *Phi = *ghi = -INFINITY;
+        for (int i = 0; i < n; i++) {
+            uint16_t gb;
+            const double p = orc_bf16_to_f64(sig_eval(&c->fs, a->sig, xb[i], &gb));
+            const double g = orc_bf16_to_f64(gb);
+            if (i == 0) { *P0 = p; *g0 = g; }
+            *Plo = fmin(*Plo, p); *Phi = fmax(*Phi, p);
+            *glo = fmin(*glo, g); *ghi = fmax(*ghi, g);
+        }
+        return;
+    }
+    /* comparator: u = RN32(S scale - ln n) as one FMA, FP32 sigma within 4
+     * ulps, g = RN32(P RN32(1 - P)) */
+    const float u0 = orc_fma_f32(s.v, c->scale, -c->logn32);
+    const float ul = orc_fma_f32(s.lo, c->scale, -c->logn32), uh = orc_fma_f32(s.hi, c->scale, -c->logn32);
+    const float p0 = (float)stable_sigmoid((double)u0);
+    const float pl = ulps32((float)stable_sigmoid((double)ul), -4);
+    const float ph = ulps32((float)stable_sigmoid((double)uh), 4);
+    *P0 = p0; *Plo = pl; *Phi = ph;
+    const float ps[4] = {p0, pl, ph, 0.5f};
+    const int n = (pl < 0.5f && ph > 0.5f) ? 4 : 3;
+    *glo = INFINITY;
+    *ghi = -INFINITY;
+    for (int i = 0; i < n; i++) {
+        const double g = orc_mul_f32(ps[i], orc_add_f32(1.0f, -ps[i]));
+        if (i == 0) *g0 = g;
+        *glo = fmin(*glo, g);
+        *ghi = fmax(*ghi, g);
+    }
+}
+
+/* ---- forward ------------------------------------------------------------- */
 
 int orc_attn_fwd_rows(const orc_attn *a, const uint16_t *q, const uint16_t *k,
                       const uint16_t *v, const int64_t *rows, int64_t n_rows,
-                      double *out, double *lse, double *noise)
+                      double *out, double *lse, double *spread)
 {
     actx c;
     const int rc = actx_init(&c, a);
     if (rc) return rc;
     if (a->exp2_core && a->kind != ORC_ATTN_SOFTCAP_POLY) return -3;
     const int64_t S = a->S, D = a->D, G = a->H / a->Hkv;
+    const int sc = is_softcap(a);
 #pragma omp parallel
     {
-        double *w = malloc(sizeof(double) * (size_t)(S > 0 ? S : 1));
+        const size_t nb = (size_t)(S > 0 ? S : 1);
+        double *w = malloc(sizeof(double) * nb);    /* weight entering P V (over l) */
+        double *dw = malloc(sizeof(double) * nb);   /* its admissible half-spread */
+        double *dl = malloc(sizeof(double) * nb);   /* of the term's share of l */
+        tcands *tc = malloc(sizeof(tcands));
 #pragma omp for schedule(dynamic, 1)
         for (int64_t ri = 0; ri < n_rows; ri++) {
             const int64_t r = rows[ri];
@@ -518,130 +674,197 @@ int orc_attn_fwd_rows(const orc_attn *a, const uint16_t *q, const uint16_t *k,
             const int64_t b = bh / a->H, h = bh % a->H;
             const int64_t kvb = (b * a->Hkv + h / G) * S * D;
             const int64_t nk = a->causal ? i + 1 : S;
-            if (is_softcap(a)) {
-                double dummy, ls;
-                for (int64_t j = 0; j < nk; j++)
-                    softcap_t(&c, dot_bf16(q + r * D, k + kvb + j * D, (int)D), &w[j], &dummy);
-                if (a->replay) {
-                    ls = softcap_row_replay(&c, w, w, nk);
-                } else if (a->exp2_core) {
-                    ls = exp2_core_weights(&c, w, w, nk);
-                } else {
-                    double m = -INFINITY, l = 0.0;
-                    for (int64_t j = 0; j < nk; j++) {
-                        w[j] *= (double)a->cap;
-                        if (w[j] > m) m = w[j];
-                    }
-                    for (int64_t j = 0; j < nk; j++) { w[j] = exp(w[j] - m); l += w[j]; }
-                    for (int64_t j = 0; j < nk; j++) w[j] /= l;
-                    ls = m + log(l);
-                }
-                if (lse) lse[ri] = ls;
-            } else {
+            double l = 1.0;
+            for (int64_t j = 0; j < nk; j++) dw[j] = dl[j] = 0.0;
+            if (sc && !a->replay) {
+                double m = -INFINITY, dummy;
                 for (int64_t j = 0; j < nk; j++) {
-                    const double p = sigmoid_p(&c, dot_bf16(q + r * D, k + kvb + j * D, (int)D), NULL);
-                    w[j] = a->replay ? bf16r(p) : p;
+                    score_real(&c, dot_bf16(q + r * D, k + kvb + j * D, (int)D, NULL), &w[j], &dummy);
+                    if (w[j] > m) m = w[j];
+                }
+                if (a->exp2_core) {
+                    /* 2^floor(z) p(frac z), z = RN32(t c2), relative to the
+                     * row's largest floor(z) */
+                    double M = -INFINITY;
+                    for (int64_t j = 0; j < nk; j++) {
+                        w[j] /= (double)a->cap;
+                        M = fmax(M, floor((double)orc_mul_f32((float)w[j], c.c2)));
+                    }
+                    l = 0.0;
+                    for (int64_t j = 0; j < nk; j++) {
+                        w[j] = exp2_fp32(a->exp2_core, orc_mul_f32((float)w[j], c.c2), M);
+                        l += w[j];
+                    }
+                    if (lse) lse[ri] = (M + log2(l)) * LN2;
+                } else {
+                    l = 0.0;
+                    for (int64_t j = 0; j < nk; j++) { w[j] = exp(w[j] - m); l += w[j]; }
+                    if (lse) lse[ri] = m + log(l);
+                }
+            } else if (sc) {
+                /* replay: FP32 P_j (fixed reference, or 2^z split relative to
+                 * the row's largest floor(z)), l = sum of the FP32 P_j */
+                const int fused = a->exp2_core == 0 && c.sref;
+                double ref = fused ? (double)c.mref : -INFINITY;
+                double *P0 = w;
+                if (!fused) {
+                    for (int64_t j = 0; j < nk; j++) {
+                        double A;
+                        const double Sr = dot_bf16(q + r * D, k + kvb + j * D, (int)D, &A);
+                        softcap_cands(&c, Sr, A, tc);
+                        float z = orc_mul_f32((float)tc->t[0], c.c2);
+                        if (z < -16384.0f) z = -16384.0f;
+                        ref = fmax(ref, floor((double)z));
+                    }
+                }
+                l = 0.0;
+                for (int64_t j = 0; j < nk; j++) {
+                    double A, Plo, Phi;
+                    const double Sr = dot_bf16(q + r * D, k + kvb + j * D, (int)D, &A);
+                    softcap_cands(&c, Sr, A, tc);
+                    p_range(&c, tc, fused, fused ? -c.mref : 0.0f, fused ? 0.0 : ref, &P0[j], &Plo, &Phi);
+                    l += P0[j];
+                    dl[j] = half_spread(P0[j], Plo, Phi);
+                    const double pb = bf16r(P0[j]);
+                    dw[j] = half_spread(pb, bf16r(Plo), bf16r(Phi));
+                    w[j] = pb;
+                }
+                if (lse) lse[ri] = (ref + log2(l)) * LN2;
+            } else {
+                l = 1.0;
+                for (int64_t j = 0; j < nk; j++) {
+                    double A, p0, plo, phi, g0, glo, ghi;
+                    const double Sr = dot_bf16(q + r * D, k + kvb + j * D, (int)D, &A);
+                    if (a->replay) {
+                        sigmoid_cands(&c, Sr, A, &p0, &plo, &phi, &g0, &glo, &ghi);
+                        w[j] = bf16r(p0);
+                        dw[j] = half_spread(w[j], bf16r(plo), bf16r(phi));
+                    } else {
+                        double dummy;
+                        score_real(&c, Sr, &w[j], &dummy);
+                    }
                 }
                 if (lse) lse[ri] = NAN;
             }
             for (int64_t d = 0; d < D; d++) {
-                double o = 0.0, n2 = 0.0;
+                double o = 0.0, sp = 0.0;
                 for (int64_t j = 0; j < nk; j++) {
                     const double vj = orc_bf16_to_f64(v[kvb + j * D + d]);
                     o += w[j] * vj;
-                    n2 += w[j] * w[j] * vj * vj;
+                    sp += dw[j] * fabs(vj);
                 }
+                o /= l;
+                sp /= l;
+                if (sc && a->replay)
+                    for (int64_t j = 0; j < nk; j++) sp += dl[j] * fabs(o) / l;
                 out[ri * D + d] = o;
-                if (noise) noise[ri * D + d] = sqrt(n2);
+                if (spread) spread[ri * D + d] = sp;
             }
         }
         free(w);
+        free(dw);
+        free(dl);
+        free(tc);
     }
     return 0;
 }
 
-/* P_ij and dS_ij of one (query row, key row) pair as the products use them
- * (BF16-rounded in the replay model), and two scales of an FP32 evaluation
- * of dS:
- *   cs  |dS / (dP - Delta)| (softcap) or |dS / dP| (sigmoid) times the sum of
- *       the absolute products that form dP - Delta (or dP);
- *   sd  |dS / g|, g the transform's derivative before the chain factor: the
- *       sensitivity to an absolute error in g.
- * delta_i is Delta_i (RN32 of it in the replay model), lse_i the row's
- * log-sum-exp (softcap). */
-static void pair_grad(const actx *c, const uint16_t *qi, const uint16_t *kj,
-                      const uint16_t *vj, const uint16_t *doi, const double *oi,
-                      double lse_i, double delta_i, double *P, double *dS, double *cs,
-                      double *sd)
+/* ---- backward ------------------------------------------------------------ */
+
+/* Delta_i (RN32 of it in the replay model) and its admissible half-range. */
+static double row_delta(const actx *c, const uint16_t *doi, const double *oi, int D,
+                        double *lo, double *hi)
+{
+    double s = 0.0, A = 0.0;
+    for (int d = 0; d < D; d++) {
+        const double p = orc_bf16_to_f64(doi[d]) * oi[d];
+        s += p;
+        A += fabs(p);
+    }
+    if (!c->a->replay) {
+        *lo = *hi = s;
+        return s;
+    }
+    const f32r r = fp32_range(s, 128.0 * U32 * A);
+    *lo = r.lo;
+    *hi = r.hi;
+    return r.v;
+}
+
+/* P_ij and dS_ij of one pair as the products use them (BF16 in the replay
+ * model) and their admissible half-spreads (0 in the real model). */
+static void pair_grad(const actx *c, tcands *tc, const uint16_t *qi, const uint16_t *kj,
+                      const uint16_t *vj, const uint16_t *doi, double lse_i, double delta,
+                      double dlo, double dhi, double *P, double *dS, double *sP, double *sS)
 {
     const orc_attn *a = c->a;
     const int D = a->D;
-    const double Sr = dot_bf16(qi, kj, D);
-    const double dP = dot_bf16(doi, vj, D);
-    double ab = 0.0;
-    for (int d = 0; d < D; d++) {
-        const double g = fabs(orc_bf16_to_f64(doi[d]));
-        ab += g * fabs(orc_bf16_to_f64(vj[d]));
-        if (oi) ab += g * fabs(oi[d]);
-    }
-    if (is_softcap(a)) {
-        double t, dq;
-        softcap_t(c, Sr, &t, &dq);
-        if (a->replay) {
-            const float nl = -orc_mul_f32((float)lse_i, (float)LOG2E);
-            const float p = (float)exp2_fp32(a->exp2_core, orc_fma_f32((float)t, c->c2, nl), 0.0);
-            const float u = orc_add_f32((float)dP, -(float)delta_i);
-            const float ds = orc_mul_f32((float)dq, orc_mul_f32(p, u));
-            *P = bf16r(p);
-            *dS = bf16r(ds);
-            *cs = fabs((double)p * dq) * ab;
-            *sd = fabs((double)p * u);
+    double A, AdP;
+    const double Sr = dot_bf16(qi, kj, D, &A);
+    const double dP = dot_bf16(doi, vj, D, &AdP);
+    *sP = *sS = 0.0;
+    if (!a->replay) {
+        double val, dval;
+        score_real(c, Sr, &val, &dval);
+        if (is_softcap(a)) {
+            *P = exp(val - lse_i);
+            *dS = *P * (dP - delta) * dval;
         } else {
-            /* the program sees RN32(S scale); the exact transform S itself */
-            const double dval = a->kind == ORC_ATTN_SOFTCAP_POLY
-                                    ? (double)a->cap * (double)c->scale * dq : dq * c->rsd;
-            *P = exp((double)a->cap * t - lse_i);
-            *dS = *P * (dP - delta_i) * dval;
-            *cs = fabs(*P * dval) * ab;
-            *sd = fabs(*P * (dP - delta_i)) * c->rsd;
+            *P = val;
+            *dS = dP * dval;
         }
         return;
     }
-    uint16_t g = 0;
-    const double p = sigmoid_p(c, Sr, &g);
-    double dval;
-    if (a->kind == ORC_ATTN_SIGMOID_POLY) {
-        dval = orc_bf16_to_f64(g);
-        if (!a->replay) dval *= (double)c->scale;
-    } else if (a->replay) {
-        dval = orc_mul_f32((float)p, orc_add_f32(1.0f, -(float)p));
-    } else {
-        dval = p * (1.0 - p) * c->rsd;
+    const f32r dp = fp32_range(dP, 8.0 * U32 * AdP);
+    double P0, Plo, Phi, d0, dlo_, dhi_;
+    if (is_softcap(a)) {
+        softcap_cands(c, Sr, A, tc);
+        const float nl = -orc_mul_f32((float)lse_i, (float)LOG2E);
+        p_range(c, tc, 1, nl, 0.0, &P0, &Plo, &Phi);
+        d0 = tc->d[0];
+        dlo_ = dhi_ = d0;
+        for (int i = 1; i < tc->n; i++) { dlo_ = fmin(dlo_, tc->d[i]); dhi_ = fmax(dhi_, tc->d[i]); }
+        /* dS = RN32(q' RN32(P RN32(dP - Delta))) */
+        const float u0 = orc_add_f32(dp.v, -(float)delta);
+        const float ul = orc_add_f32(dp.lo, -(float)dhi), uh = orc_add_f32(dp.hi, -(float)dlo);
+        const float ds0 = orc_mul_f32((float)d0, orc_mul_f32((float)P0, u0));
+        double sl = INFINITY, sh = -INFINITY;
+        const double pc[2] = {Plo, Phi}, uc[2] = {ul, uh}, dc[2] = {dlo_, dhi_};
+        for (int x = 0; x < 2; x++)
+            for (int y = 0; y < 2; y++)
+                for (int z = 0; z < 2; z++) {
+                    const double ds = orc_mul_f32((float)dc[z], orc_mul_f32((float)pc[x], (float)uc[y]));
+                    sl = fmin(sl, ds);
+                    sh = fmax(sh, ds);
+                }
+        *dS = bf16r(ds0);
+        *sS = half_spread(*dS, bf16r(sl), bf16r(sh));
+        *P = bf16r(P0);
+        *sP = half_spread(*P, bf16r(Plo), bf16r(Phi));
+        return;
     }
-    if (a->replay) {
-        *P = bf16r(p);
-        *dS = bf16r(orc_mul_f32((float)dP, (float)dval));
-    } else {
-        *P = p;
-        *dS = dP * dval;
-    }
-    *cs = fabs(dval) * ab;
-    *sd = fabs(dP) * (a->replay ? 1.0 : c->rsd);
-}
-
-static double row_delta(const actx *c, const uint16_t *doi, const double *oi, int D)
-{
-    double s = 0.0;
-    for (int d = 0; d < D; d++) s += orc_bf16_to_f64(doi[d]) * oi[d];
-    return c->a->replay ? (double)(float)s : s;
+    /* sigmoid: dS = RN32(dP g) */
+    sigmoid_cands(c, Sr, A, &P0, &Plo, &Phi, &d0, &dlo_, &dhi_);
+    const float ds0 = orc_mul_f32(dp.v, (float)d0);
+    double sl = INFINITY, sh = -INFINITY;
+    const double uc[2] = {dp.lo, dp.hi}, gc[2] = {dlo_, dhi_};
+    for (int x = 0; x < 2; x++)
+        for (int y = 0; y < 2; y++) {
+            const double ds = orc_mul_f32((float)uc[x], (float)gc[y]);
+            sl = fmin(sl, ds);
+            sh = fmax(sh, ds);
+        }
+    *dS = bf16r(ds0);
+    *sS = half_spread(*dS, bf16r(sl), bf16r(sh));
+    *P = bf16r(P0);
+    *sP = half_spread(*P, bf16r(Plo), bf16r(Phi));
 }
 
 int orc_attn_bwd_rows(const orc_attn *a, const uint16_t *q, const uint16_t *k,
                       const uint16_t *v, const double *o, const uint16_t *dout,
                       const double *lse, const int64_t *qrows, int64_t nq,
                       const int64_t *krows, int64_t nk, double *dq, double *dk,
-                      double *dv, double *nz_dq, double *nz_dk, double *nz_dv,
-                      double *cs_dq, double *cs_dk, double *sd_dq, double *sd_dk)
+                      double *dv, double *sp_dq, double *sp_dk, double *sp_dv)
 {
     actx c;
     const int rc = actx_init(&c, a);
@@ -653,83 +876,80 @@ int orc_attn_bwd_rows(const orc_attn *a, const uint16_t *q, const uint16_t *k,
      * carries the chain factor inside dS */
     const double fin = a->replay ? (double)c.rsd32 : 1.0;
     /* dQ rows */
-#pragma omp parallel for schedule(dynamic, 1)
-    for (int64_t ri = 0; ri < nq; ri++) {
-        const int64_t r = qrows[ri];
-        const int64_t bh = r / S, i = r % S;
-        const int64_t b = bh / a->H, h = bh % a->H;
-        const int64_t kvb = (b * a->Hkv + h / G) * S * D;
-        const double delta = sc ? row_delta(&c, dout + r * D, o + r * D, (int)D) : 0.0;
-        const double li = sc ? lse[r] : 0.0;
-        const int64_t n = a->causal ? i + 1 : S;
-        for (int64_t d = 0; d < D; d++) {
-            dq[ri * D + d] = 0.0;
-            if (nz_dq) nz_dq[ri * D + d] = 0.0;
-            if (cs_dq) cs_dq[ri * D + d] = 0.0;
-            if (sd_dq) sd_dq[ri * D + d] = 0.0;
-        }
-        for (int64_t j = 0; j < n; j++) {
-            double P, dS, cs, sd;
-            pair_grad(&c, q + r * D, k + kvb + j * D, v + kvb + j * D, dout + r * D,
-                      sc ? o + r * D : NULL, li, delta, &P, &dS, &cs, &sd);
+#pragma omp parallel
+    {
+        tcands *tc = malloc(sizeof(tcands));
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t ri = 0; ri < nq; ri++) {
+            const int64_t r = qrows[ri];
+            const int64_t bh = r / S, i = r % S;
+            const int64_t b = bh / a->H, h = bh % a->H;
+            const int64_t kvb = (b * a->Hkv + h / G) * S * D;
+            double dlo = 0.0, dhi = 0.0;
+            const double delta = sc ? row_delta(&c, dout + r * D, o + r * D, (int)D, &dlo, &dhi) : 0.0;
+            const double li = sc ? lse[r] : 0.0;
+            const int64_t n = a->causal ? i + 1 : S;
             for (int64_t d = 0; d < D; d++) {
-                const double kd = orc_bf16_to_f64(k[kvb + j * D + d]);
-                const double t = dS * kd;
-                dq[ri * D + d] += t;
-                if (nz_dq) nz_dq[ri * D + d] += t * t;
-                if (cs_dq) cs_dq[ri * D + d] += cs * fabs(kd);
-                if (sd_dq) sd_dq[ri * D + d] += sd * fabs(kd);
+                dq[ri * D + d] = 0.0;
+                if (sp_dq) sp_dq[ri * D + d] = 0.0;
             }
-        }
-        for (int64_t d = 0; d < D; d++) {
-            dq[ri * D + d] *= fin;
-            if (nz_dq) nz_dq[ri * D + d] = sqrt(nz_dq[ri * D + d]) * fin;
-            if (cs_dq) cs_dq[ri * D + d] *= fin;
-            if (sd_dq) sd_dq[ri * D + d] *= fin;
-        }
-    }
-    /* dK, dV rows: key row r = (b Hkv + hk) S + j */
-#pragma omp parallel for schedule(dynamic, 1)
-    for (int64_t ri = 0; ri < nk; ri++) {
-        const int64_t r = krows[ri];
-        const int64_t bk = r / S, j = r % S;
-        const int64_t b = bk / a->Hkv, hk = bk % a->Hkv;
-        for (int64_t d = 0; d < D; d++) {
-            dk[ri * D + d] = dv[ri * D + d] = 0.0;
-            if (nz_dk) nz_dk[ri * D + d] = 0.0;
-            if (nz_dv) nz_dv[ri * D + d] = 0.0;
-            if (cs_dk) cs_dk[ri * D + d] = 0.0;
-            if (sd_dk) sd_dk[ri * D + d] = 0.0;
-        }
-        for (int64_t h = hk * G; h < (hk + 1) * G; h++) {
-            const int64_t qb = (b * a->H + h) * S;
-            for (int64_t i = a->causal ? j : 0; i < S; i++) {
-                const int64_t qr = qb + i;
-                const double delta = sc ? row_delta(&c, dout + qr * D, o + qr * D, (int)D) : 0.0;
-                double P, dS, cs, sd;
-                pair_grad(&c, q + qr * D, k + r * D, v + r * D, dout + qr * D,
-                          sc ? o + qr * D : NULL, sc ? lse[qr] : 0.0, delta, &P, &dS, &cs,
-                          &sd);
+            for (int64_t j = 0; j < n; j++) {
+                double P, dS, sP, sS;
+                pair_grad(&c, tc, q + r * D, k + kvb + j * D, v + kvb + j * D, dout + r * D, li,
+                          delta, dlo, dhi, &P, &dS, &sP, &sS);
                 for (int64_t d = 0; d < D; d++) {
-                    const double qd = orc_bf16_to_f64(q[qr * D + d]);
-                    const double tk = dS * qd;
-                    if (cs_dk) cs_dk[ri * D + d] += cs * fabs(qd);
-                    if (sd_dk) sd_dk[ri * D + d] += sd * fabs(qd);
-                    const double tv = P * orc_bf16_to_f64(dout[qr * D + d]);
-                    dk[ri * D + d] += tk;
-                    dv[ri * D + d] += tv;
-                    if (nz_dk) nz_dk[ri * D + d] += tk * tk;
-                    if (nz_dv) nz_dv[ri * D + d] += tv * tv;
+                    const double kd = orc_bf16_to_f64(k[kvb + j * D + d]);
+                    dq[ri * D + d] += dS * kd;
+                    if (sp_dq) sp_dq[ri * D + d] += sS * fabs(kd);
                 }
             }
+            for (int64_t d = 0; d < D; d++) {
+                dq[ri * D + d] *= fin;
+                if (sp_dq) sp_dq[ri * D + d] *= fin;
+            }
         }
-        for (int64_t d = 0; d < D; d++) {
-            dk[ri * D + d] *= fin;
-            if (nz_dk) nz_dk[ri * D + d] = sqrt(nz_dk[ri * D + d]) * fin;
-            if (nz_dv) nz_dv[ri * D + d] = sqrt(nz_dv[ri * D + d]);
-            if (cs_dk) cs_dk[ri * D + d] *= fin;
-            if (sd_dk) sd_dk[ri * D + d] *= fin;
+        free(tc);
+    }
+    /* dK, dV rows: key row r = (b Hkv + hk) S + j */
+#pragma omp parallel
+    {
+        tcands *tc = malloc(sizeof(tcands));
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t ri = 0; ri < nk; ri++) {
+            const int64_t r = krows[ri];
+            const int64_t bk = r / S, j = r % S;
+            const int64_t b = bk / a->Hkv, hk = bk % a->Hkv;
+            for (int64_t d = 0; d < D; d++) {
+                dk[ri * D + d] = dv[ri * D + d] = 0.0;
+                if (sp_dk) sp_dk[ri * D + d] = 0.0;
+                if (sp_dv) sp_dv[ri * D + d] = 0.0;
+            }
+            for (int64_t h = hk * G; h < (hk + 1) * G; h++) {
+                const int64_t qb = (b * a->H + h) * S;
+                for (int64_t i = a->causal ? j : 0; i < S; i++) {
+                    const int64_t qr = qb + i;
+                    double dlo = 0.0, dhi = 0.0;
+                    const double delta =
+                        sc ? row_delta(&c, dout + qr * D, o + qr * D, (int)D, &dlo, &dhi) : 0.0;
+                    double P, dS, sP, sS;
+                    pair_grad(&c, tc, q + qr * D, k + r * D, v + r * D, dout + qr * D,
+                              sc ? lse[qr] : 0.0, delta, dlo, dhi, &P, &dS, &sP, &sS);
+                    for (int64_t d = 0; d < D; d++) {
+                        const double qd = orc_bf16_to_f64(q[qr * D + d]);
+                        const double gd = orc_bf16_to_f64(dout[qr * D + d]);
+                        dk[ri * D + d] += dS * qd;
+                        dv[ri * D + d] += P * gd;
+                        if (sp_dk) sp_dk[ri * D + d] += sS * fabs(qd);
+                        if (sp_dv) sp_dv[ri * D + d] += sP * fabs(gd);
+                    }
+                }
+            }
+            for (int64_t d = 0; d < D; d++) {
+                dk[ri * D + d] *= fin;
+                if (sp_dk) sp_dk[ri * D + d] *= fin;
+            }
         }
+        free(tc);
     }
     return 0;
 }
