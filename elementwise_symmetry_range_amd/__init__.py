@@ -79,8 +79,11 @@ def lib() -> C.CDLL:
                                   p],
             "poly_softcap_attn_fwd": [p, p, p, p, p, i32, i32, i32, i32, i32, f32, i32, p],
             "native_softcap_attn_fwd": [p, p, p, p, p, i32, i32, i32, i32, i32, f32, i32, p],
+            "poly_softcap_attn_fwd_f16": [p, p, p, p, p, i32, i32, i32, i32, i32, f32, i32, p],
             "poly_softcap_attn_fwd_exp2": [p, p, p, p, p, i32, i32, i32, i32, i32, f32, i32, i32, p],
             "poly_softcap_attn_bwd": [p] * 10 + [i32] * 5 + [f32, i32, p],
+            "poly_softcap_attn_bwd_f16": [p] * 10 + [i32] * 5 + [f32, i32, p],
+            "poly_softcap_attn_bwd_exp2": [p] * 10 + [i32] * 5 + [f32, i32, i32, p],
             "native_softcap_attn_bwd": [p] * 10 + [i32] * 5 + [f32, i32, p],
             "poly_sigmoid_attn_fwd": [p] * 4 + [i32] * 6 + [p],
             "native_sigmoid_attn_fwd": [p] * 4 + [i32] * 6 + [p],
@@ -299,27 +302,41 @@ def _softcap_fwd(entry, q, k, v, cap, causal, out, with_lse):
     return (o, lse) if with_lse else o
 
 
+SOFTCAP_FORMATS = ("bf16", "f16")
+
+
 def poly_softcap_attn_fwd(q, k, v, cap: float = 50.0, causal: bool = True, out=None,
-                          with_lse: bool = False):
-    """Softcapped attention forward with the D4 tanh program (BF16, D = 128).
-    q [B, H, S, D], k and v [B, Hkv, S, D].  Returns O, or (O, lse) with
-    with_lse (the natural log-sum-exp per row, FP32 [B, H, S])."""
-    return _softcap_fwd(lib().poly_softcap_attn_fwd, q, k, v, cap, causal, out, with_lse)
+                          with_lse: bool = False, fmt: str = "bf16"):
+    """Softcapped attention forward with the D4 tanh program (BF16 in / out,
+    D = 128).  q [B, H, S, D], k and v [B, Hkv, S, D].  fmt: the program's
+    format, "bf16" (the pages' path) or "f16" (packed FP16).  Returns O, or
+    (O, lse) with with_lse (the natural log-sum-exp per row, FP32 [B, H, S])."""
+    if fmt not in SOFTCAP_FORMATS:
+        raise ValueError(f"fmt must be one of {SOFTCAP_FORMATS}")
+    entry = lib().poly_softcap_attn_fwd if fmt == "bf16" else lib().poly_softcap_attn_fwd_f16
+    return _softcap_fwd(entry, q, k, v, cap, causal, out, with_lse)
 
 
 EXP2_CORES = {"hw": 0, "d1": 1, "pwl2": 2, "d2": 3, "d3": 4}
 
 
+def _core(core):
+    if core not in EXP2_CORES:
+        raise ValueError(f"core must be one of {sorted(EXP2_CORES)}")
+    return EXP2_CORES[core]
+
+
 def poly_softcap_attn_fwd_exp2(q, k, v, cap: float = 50.0, causal: bool = True,
                                core: str = "pwl2", out=None, with_lse: bool = False):
-    """poly_softcap_attn_fwd with the softmax's exponentials by a software exp2
-    core: "hw" (v_exp_f32), "d1", "pwl2" (packed FP16), "d2", "d3"."""
+    """poly_softcap_attn_fwd (BF16 program) with the softmax's exponentials by
+    a software exp2 core: "hw" (v_exp_f32), "d1", "pwl2" (packed FP16), "d2",
+    "d3"."""
     B, H, Hkv, S, D = _attn_shapes(q, k, v)
     o = _like(out, q, "out")
     lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device) if with_lse else None
     _call(lib().poly_softcap_attn_fwd_exp2, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
           None if lse is None else lse.data_ptr(), B, H, Hkv, S, D, float(cap), int(bool(causal)),
-          EXP2_CORES[core], on=q, tensors=(k, v, o))
+          _core(core), on=q, tensors=(k, v, o))
     return (o, lse) if with_lse else o
 
 
@@ -353,7 +370,7 @@ def _ws(workspace, softcap, B, H, Hkv, S, D, device):
     return workspace
 
 
-def _softcap_bwd(entry, q, k, v, o, dout, lse, cap, causal, dq, dk, dv, workspace):
+def _softcap_bwd(entry, q, k, v, o, dout, lse, cap, causal, dq, dk, dv, workspace, extra=()):
     B, H, Hkv, S, D = _attn_shapes(q, k, v)
     _bf16_4d(o, "o")
     _bf16_4d(dout, "dout")
@@ -365,17 +382,26 @@ def _softcap_bwd(entry, q, k, v, o, dout, lse, cap, causal, dq, dk, dv, workspac
     workspace = _ws(workspace, True, B, H, Hkv, S, D, q.device)
     _call(entry, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
           lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), B, H,
-          Hkv, S, D, float(cap), int(bool(causal)), on=q,
+          Hkv, S, D, float(cap), int(bool(causal)), *extra, on=q,
           tensors=(k, v, o, dout, lse, dq, dk, dv, workspace))
     return dq, dk, dv
 
 
 def poly_softcap_attn_bwd(q, k, v, o, dout, lse, cap: float = 50.0, causal: bool = True,
-                          dq=None, dk=None, dv=None, workspace=None):
+                          dq=None, dk=None, dv=None, workspace=None, fmt: str = "bf16",
+                          core: str | None = None):
     """Backward of poly_softcap_attn_fwd: (dq, dk, dv), with the analytic
-    derivative of the D4 tanh program."""
-    return _softcap_bwd(lib().poly_softcap_attn_bwd, q, k, v, o, dout, lse, cap, causal, dq, dk,
-                        dv, workspace)
+    derivative of the D4 tanh program in the forward's format.  core: the
+    exp2 core of poly_softcap_attn_fwd_exp2 (BF16 program only)."""
+    if fmt not in SOFTCAP_FORMATS:
+        raise ValueError(f"fmt must be one of {SOFTCAP_FORMATS}")
+    if core is not None:
+        if fmt != "bf16":
+            raise ValueError("the exp2 cores run with the BF16 program")
+        return _softcap_bwd(lib().poly_softcap_attn_bwd_exp2, q, k, v, o, dout, lse, cap, causal,
+                            dq, dk, dv, workspace, extra=(_core(core),))
+    entry = lib().poly_softcap_attn_bwd if fmt == "bf16" else lib().poly_softcap_attn_bwd_f16
+    return _softcap_bwd(entry, q, k, v, o, dout, lse, cap, causal, dq, dk, dv, workspace)
 
 
 def native_softcap_attn_bwd(q, k, v, o, dout, lse, cap: float = 50.0, causal: bool = True,

@@ -9,12 +9,15 @@
 //            and 1 / n folded into its coefficients (one n only).
 // Each has an accurate FP32 comparator (tanhf; expf and an IEEE divide).
 //
-// Arithmetic of the programs.  gfx950's packed 16-bit FMA is FP16
-// (v_pk_fma_f16) and it has no packed BF16 FMA.  The tanh program therefore
-// runs in packed FP16 on x = RN_f16(RN_f32(S) * RN_f32(1 / (cap sqrt D))), two
-// scores per instruction, with the FP16 values of the BF16 coefficients.  The
-// sigmoid program keeps the pages' BF16 format: x = RN_bf16(RN_f32(S) *
-// RN_f32(1 / sqrt D)) and each Horner stage is an FP32 FMA rounded to BF16.
+// Arithmetic of the programs.  The pages run the attention integrations on
+// the BF16 path (section 3.4).  gfx950 has no packed BF16 FMA, so a BF16
+// program runs each Horner stage as an FP32 FMA rounded to BF16 (one
+// v_cvt_pk_bf16_f32 per lane): the tanh program on x = RN_bf16(RN_f32(S) *
+// RN_f32(1 / (cap sqrt D))) and the sigmoid program on x = RN_bf16(RN_f32(S) *
+// RN_f32(1 / sqrt D)).  The tanh program is also offered in packed FP16
+// (v_pk_fma_f16, two scores per instruction) on x = RN_f16(...), with the FP16
+// values of the same BF16 coefficients: fewer VALU instructions, a different
+// rounding of every stage.
 //
 // Layout: Q, O [B, H, S, D]; K, V [B, Hkv, S, D], H a multiple of Hkv (query
 // head h reads key/value head h / (H / Hkv)); D = 128; BF16.
@@ -72,9 +75,24 @@ constexpr float AT_RESCALE = 8.0f;  // log2 headroom before the reference max mo
 constexpr float AT_LN2 = 0.693147180559945309f;
 constexpr float AT_LOG2E = 1.442695040888963407f;
 
-// score transforms
-enum { AM_SOFTCAP_POLY = 0, AM_SOFTCAP_NATIVE = 1, AM_SIGMOID_POLY = 2, AM_SIGMOID_NATIVE = 3 };
-__host__ __device__ constexpr bool am_softcap(int m) { return m == AM_SOFTCAP_POLY || m == AM_SOFTCAP_NATIVE; }
+// score transforms: the softcap with the D4 tanh program in FP16 or BF16 or
+// with accurate tanhf, the sigmoid with the two-region program or accurate
+// sigma
+enum { AM_SOFTCAP_POLY = 0, AM_SOFTCAP_NATIVE = 1, AM_SIGMOID_POLY = 2, AM_SIGMOID_NATIVE = 3,
+       AM_SOFTCAP_POLY_BF16 = 4 };
+__host__ __device__ constexpr bool am_softcap(int m)
+{
+    return m == AM_SOFTCAP_POLY || m == AM_SOFTCAP_NATIVE || m == AM_SOFTCAP_POLY_BF16;
+}
+__host__ __device__ constexpr bool am_softcap_poly(int m) { return m == AM_SOFTCAP_POLY || m == AM_SOFTCAP_POLY_BF16; }
+
+// The D4 tanh program in BF16 (coefficient values as FP32) and, for the
+// backward, its analytic derivative (a D3, coefficients (j + 1) c_{j+1}
+// rounded to BF16); lc = Lc.
+struct TanhBF16 {
+    float c[5];
+    float lc;
+};
 
 // two-region sigmoid program: threshold and clamp bounds as FP32 values of
 // their BF16 constants; the coefficients as FP16 pairs (each BF16 coefficient
@@ -98,6 +116,7 @@ struct AttnArgs {
     float logn;        // sigmoid comparator: RN_f32(ln S)
     float mref;        // softcap, fixed reference (see SREF)
     CoefF16 tanh16;    // D4 tanh program, FP16 coefficients
+    TanhBF16 tanhbf;   // the same program in BF16
     SigCoef sig;
 };
 
@@ -205,6 +224,45 @@ __device__ __forceinline__ uint32_t softcap_poly_pair(float s0, float s1, float 
     return bc<uint32_t>(v) ^ (xw ^ aw);
 }
 
+// softcap program in BF16 on a pair: x = RN_bf16(s * scale), t^ = min(|x|,
+// Lc), v = c4; v = RN_bf16(fma(v, t^, c_j)) for j = 3, 2, 1; t = RN_bf16(v t^)
+// with x's sign.  Returns t0, t1 (BF16 values as FP32) and, through th0 / th1
+// and x0 / x1, the clamped |x| and x for the derivative program.
+__device__ __forceinline__ void softcap_bf16_pair(float s0, float s1, float scale, const TanhBF16 &k,
+                                                  float &t0, float &t1, float &x0, float &x1,
+                                                  float &th0, float &th1)
+{
+    x0 = rn_bf16(s0 * scale);
+    x1 = rn_bf16(s1 * scale);
+    th0 = fminf(fabsf(x0), k.lc);
+    th1 = fminf(fabsf(x1), k.lc);
+    float v0 = rn_bf16(fmaf(k.c[4], th0, k.c[3])), v1 = rn_bf16(fmaf(k.c[4], th1, k.c[3]));
+    v0 = rn_bf16(fmaf(v0, th0, k.c[2]));
+    v1 = rn_bf16(fmaf(v1, th1, k.c[2]));
+    v0 = rn_bf16(fmaf(v0, th0, k.c[1]));
+    v1 = rn_bf16(fmaf(v1, th1, k.c[1]));
+    // the sign before the last rounding (nearest even is symmetric)
+    t0 = rn_bf16(__builtin_copysignf(v0 * th0, x0));
+    t1 = rn_bf16(__builtin_copysignf(v1 * th1, x1));
+}
+
+// the same, returning the packed BF16 pair (t0 low, t1 high): the last
+// stage's two roundings become one packed convert
+__device__ __forceinline__ uint32_t softcap_bf16_word(float s0, float s1, float scale, const TanhBF16 &k,
+                                                      float &tmax)
+{
+    const float x0 = rn_bf16(s0 * scale), x1 = rn_bf16(s1 * scale);
+    const float th0 = fminf(fabsf(x0), k.lc), th1 = fminf(fabsf(x1), k.lc);
+    float v0 = rn_bf16(fmaf(k.c[4], th0, k.c[3])), v1 = rn_bf16(fmaf(k.c[4], th1, k.c[3]));
+    v0 = rn_bf16(fmaf(v0, th0, k.c[2]));
+    v1 = rn_bf16(fmaf(v1, th1, k.c[2]));
+    v0 = rn_bf16(fmaf(v0, th0, k.c[1]));
+    v1 = rn_bf16(fmaf(v1, th1, k.c[1]));
+    const float p0 = __builtin_copysignf(v0 * th0, x0), p1 = __builtin_copysignf(v1 * th1, x1);
+    tmax = fmaxf(tmax, fmaxf(p0, p1));   // within one rounding of the rounded max (enough for a reference)
+    return pack_bf(p0, p1);
+}
+
 // FP32 FMAs with FP16 operands taken from the halves of a packed word
 // (v_fma_mix_f32: the halves convert to FP32 exactly, one rounding)
 // t * high(w) + low(w)
@@ -264,12 +322,15 @@ __device__ __forceinline__ uint32_t sigmoid_poly_pair(float s0, float s1, float 
     return pack_bf(v0, v1);   // exact: v0, v1 are BF16 values
 }
 
-// Software exp2 of the softmax (Appendix B.1, Eqs. 16-19): 2^z = 2^n p(f),
+// Split exp2 of the softmax (Appendix B.1, Eqs. 16-19): 2^z = 2^n p(f),
 // n = floor(z), f = z - n, with the reference max m an integer so that
 // 2^(z - m) = ldexp(p(f), n - m) exactly scales by a power of two and the
 // normalised weights do not depend on m.  z is clamped below at -16384
 // (masked keys, z = -inf, give 0).  Cores (p(0) = 1, p(1) = 2 after rounding
 // except D3):
+//   0 HW    p = 2^f by v_exp_f32 (the large-cap path of the hardware
+//           exponential: each P is the same FP32 value up to an exact power of
+//           two whatever the reference)
 //   1 D1    p = f + 1                                         (FP32)
 //   2 PWL2  p = 1 + a f + 2 (1 - a) max(f - 1/2, 0), a = 0.7978515625,
 //           in packed FP16 (f rounded to FP16, one rounding per op)
@@ -286,7 +347,10 @@ __device__ __forceinline__ void exp2_core_pair(float z0, float z1, float m, floa
     const float n0 = floorf(z0), n1 = floorf(z1);
     const float f0 = z0 - n0, f1 = z1 - n1;
     float c0, c1;
-    if constexpr (EXP == 1) {
+    if constexpr (EXP == 0) {
+        c0 = __builtin_amdgcn_exp2f(f0);
+        c1 = __builtin_amdgcn_exp2f(f1);
+    } else if constexpr (EXP == 1) {
         c0 = f0 + 1.0f;
         c1 = f1 + 1.0f;
     } else if constexpr (EXP == 2) {
@@ -355,9 +419,10 @@ template <int MODE, int EXP = 0, bool SREF = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_fwd(AttnArgs a)
 {
     constexpr bool SOFTCAP = am_softcap(MODE);
-    // K and V double buffers (see dbuf): separate arrays except for the
-    // softcap with the hardware exponential, which runs 1-2 % slower with them
-    constexpr bool SPLIT_LDS = !(SOFTCAP && EXP == 0);
+    // K and V double buffers (see dbuf): separate arrays for sigmoid only;
+    // the softcap with the hardware exponential runs 1-2 % slower with them,
+    // and the BF16 softcap with a software exp2 core spills with them
+    constexpr bool SPLIT_LDS = !SOFTCAP;
     __shared__ __attribute__((aligned(16))) uint16_t Ks0[AT_TILE], Ks1[AT_TILE], Kp[2][AT_TILE];
     __shared__ __attribute__((aligned(16))) uint16_t Vs0[AT_TILE], Vs1[AT_TILE], Vp[2][AT_TILE];
 
@@ -434,9 +499,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // factor st.corr rescales O once this stage's PV product has landed.
     constexpr int NPC = SOFTCAP ? (SREF ? 16 : 17) : 8;
     struct TState {
-        uint32_t w[8];     // packed FP16 t (softcap poly), then the BF16 P words
-        uint32_t mx;       // packed FP16 running max of t (softcap poly, online max)
-        float tmax;        // running max of t (softcap comparator, online max)
+        uint32_t w[8];     // packed FP16 / BF16 t (softcap poly), then the BF16 P words
+        uint32_t mx;       // packed FP16 running max of t (FP16 softcap poly, online max)
+        float tmax;        // running max of t (BF16 softcap poly, comparator; online max)
         float corr;
     };
     auto piece = [&](auto pc, f32x16 &s, TState &st, int ukey0, auto masked) __attribute__((always_inline)) {
@@ -456,6 +521,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     }
                     if constexpr (!SREF) st.mx = bc<uint32_t>(__builtin_elementwise_max(bc<h2>(st.mx), bc<h2>(w)));
                     st.w[P] = w;
+                } else if constexpr (MODE == AM_SOFTCAP_POLY_BF16) {
+                    // packed BF16 t (masked keys: BF16 -inf); the row max for
+                    // the online reference from the unmasked values
+                    float tm = -INFINITY;
+                    uint32_t w = softcap_bf16_word(s[e], s[e + 1], a.scale, a.tanhbf, tm);
+                    if constexpr (MASKED) {
+                        const int k0 = ukey0 + (e >> 2) * 8 + h * 4 + (e & 3);
+                        const uint32_t mlo = k0 > lim ? 0x0000FFFFu : 0u;
+                        const uint32_t mhi = k0 + 1 > lim ? 0xFFFF0000u : 0u;
+                        w = sel(mlo | mhi, 0xFF80FF80u, w);
+                        if constexpr (!SREF) tm = fmaxf(lo_f(w), hi_f(w));
+                    }
+                    if constexpr (!SREF) st.tmax = fmaxf(st.tmax, tm);
+                    st.w[P] = w;
                 } else {
 #pragma unroll
                     for (int i = 0; i < 2; ++i) {
@@ -472,42 +551,49 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 // lazy rescale: move the reference only when the row max
                 // outgrows it by more than AT_RESCALE
                 float tmax = MODE == AM_SOFTCAP_POLY ? fmaxf(f16_lo(st.mx), f16_hi(st.mx)) : st.tmax;
+                if (tmax == -INFINITY) tmax = -1.0f;   // every key masked: any reference
                 tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
                 const float zmax = tmax * a.c2;
                 const bool grow = zmax > m + AT_RESCALE;
-                float m_new;
-                if constexpr (EXP == 0) {
-                    m_new = grow ? zmax : m;
-                    st.corr = grow ? __builtin_amdgcn_exp2f(m - m_new) : 1.0f;
-                } else {   // integer reference; the rescale is an exact power of two
-                    m_new = grow ? ceilf(zmax) : m;
-                    st.corr = !grow ? 1.0f
-                                    : (m == -INFINITY ? 0.0f : __builtin_amdgcn_ldexpf(1.0f, (int)(m - m_new)));
-                }
+                // integer reference; the rescale is an exact power of two
+                const float m_new = grow ? ceilf(zmax) : m;
+                st.corr = !grow ? 1.0f
+                                : (m == -INFINITY ? 0.0f : __builtin_amdgcn_ldexpf(1.0f, (int)(m - m_new)));
                 l *= st.corr;
                 m = m_new;
             } else {
-                // P = exp2(t c2 - m) of pair e2, the row sum, the BF16 word
+                // P of pair e2, the row sum, the BF16 word: with the fixed
+                // reference P = exp2(RN32(t c2 - m)) in one FMA; otherwise
+                // z = RN32(t c2) through the split exp2 (its core, or 2^frac
+                // by v_exp_f32), relative to the integer reference
                 constexpr int e2 = P - (SREF ? 8 : 9);
                 constexpr int e = 2 * e2;
-                float p0, p1;
+                float t0, t1;
                 if constexpr (MODE == AM_SOFTCAP_NATIVE) {
-                    p0 = __builtin_amdgcn_exp2f(fmaf(s[e], a.c2, -m));
-                    l += p0;
-                    p1 = __builtin_amdgcn_exp2f(fmaf(s[e + 1], a.c2, -m));
-                    l += p1;
-                } else {
+                    t0 = s[e];
+                    t1 = s[e + 1];
+                } else if constexpr (MODE == AM_SOFTCAP_POLY_BF16) {
+                    t0 = lo_f(st.w[e2]);
+                    t1 = hi_f(st.w[e2]);
+                }
+                float p0, p1;
+                if constexpr (MODE == AM_SOFTCAP_POLY) {
                     // the FP16 t feed the FMA directly (no conversions)
                     const uint32_t w = st.w[e2];
-                    if constexpr (EXP == 0) {
+                    if constexpr (EXP == 0 && SREF) {
                         p0 = __builtin_amdgcn_exp2f(fma_mix_lo(w, a.c2, -m));
                         p1 = __builtin_amdgcn_exp2f(fma_mix_hi(w, a.c2, -m));
                     } else {
                         exp2_core_pair<EXP>(fma_mix_lo(w, a.c2, -0.0f), fma_mix_hi(w, a.c2, -0.0f), m, p0, p1);
                     }
-                    l += p0;
-                    l += p1;
+                } else if constexpr (EXP == 0 && SREF) {
+                    p0 = __builtin_amdgcn_exp2f(fmaf(t0, a.c2, -m));
+                    p1 = __builtin_amdgcn_exp2f(fmaf(t1, a.c2, -m));
+                } else {
+                    exp2_core_pair<EXP>(t0 * a.c2, t1 * a.c2, m, p0, p1);
                 }
+                l += p0;
+                l += p1;
                 st.w[e2] = pack_bf(p0, p1);
             }
         } else {

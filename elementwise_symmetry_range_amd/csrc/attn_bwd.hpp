@@ -4,11 +4,14 @@
 // ("Fast Polynomial Transcendentals for LLMs"):
 //   dV = P^T dO,  dP = dO V^T,
 //   softcap  dS = P (dP - Delta) ds/dS,  Delta_i = dO_i . O_i, P recomputed
-//            from the saved natural log-sum-exp; the polynomial variant uses
-//            the analytic derivative of the D4 tanh program, a D3 with
-//            coefficients (j + 1) c_{j+1} (exact in FP16), in packed FP16 at
-//            the same clamped |x| (sections 3.3 and 5.2.2); the comparator
-//            uses 1 - tanh^2 recomputed with tanhf (Eq. 12);
+//            from the saved natural log-sum-exp (with the forward's exp2: the
+//            hardware exponential or a software core); the polynomial variant
+//            uses the analytic derivative of the D4 tanh program, a D3 with
+//            coefficients (j + 1) c_{j+1} (BF16-rounded for the BF16 program,
+//            exact in FP16 for the FP16 one), in the program's format at |x|,
+//            and 0 beyond the clamp, where the clamped forward program is
+//            constant (sections 3.3 and 5.2.2); the comparator uses
+//            1 - tanh^2 recomputed with tanhf (Eq. 12);
 //   sigmoid  dS = dP dP~/ds; the polynomial variant uses the factored
 //            surrogate P~ (a + b x) of section 3.4 from the same region,
 //            clamp and Horner value as the forward; the comparator
@@ -58,14 +61,40 @@ struct AttnBwdArgs {
     float rsd;             // RN_f32(1 / sqrt D)
     CoefF16 tanh16;        // D4 tanh program
     CoefF16 dtanh16;       // its derivative, D3 (FP16 coefficients)
+    TanhBF16 tanhbf;       // the D4 tanh program in BF16
+    TanhBF16 dtanhbf;      // its derivative, D3 (BF16 coefficients)
     SigCoef sig;
 };
+
+// The D3 derivative program in BF16 at the clamped |x| (th), 0 where
+// |x| > Lc.
+__device__ __forceinline__ float dtanh_bf16(float x, float th, const TanhBF16 &d)
+{
+    float v = rn_bf16(fmaf(d.c[3], th, d.c[2]));
+    v = rn_bf16(fmaf(v, th, d.c[1]));
+    v = rn_bf16(fmaf(v, th, d.c[0]));
+    return fabsf(x) > d.lc ? 0.0f : v;
+}
+
+// P = 2^z of the backward for a pair, z the exponent arguments, with the
+// forward's exponential: v_exp_f32 (EXP = 0) or 2^floor(z) p(z - floor z)
+// by a software core.
+template <int EXP>
+__device__ __forceinline__ void bwd_exp2(float z0, float z1, float &p0, float &p1)
+{
+    if constexpr (EXP == 0) {
+        p0 = __builtin_amdgcn_exp2f(z0);
+        p1 = __builtin_amdgcn_exp2f(z1);
+    } else {
+        exp2_core_pair<EXP>(z0, z1, 0.0f, p0, p1);
+    }
+}
 
 // dS and P of a pair of scores; s0, s1 raw scores, dp0, dp1 = dO . V,
 // nl0, nl1 = -lse * log2(e) (softcap), dl0, dl1 = Delta (softcap).  P comes
 // back as the packed BF16 pair the dV product takes (the sigmoid program
 // produces it in that form), dS as FP32.
-template <int MODE>
+template <int MODE, int EXP = 0>
 __device__ __forceinline__ void bwd_pair(const AttnBwdArgs &a, float s0, float s1, float dp0,
                                          float dp1, float nl0, float nl1, float dl0, float dl1,
                                          uint32_t &pw, float &ds0, float &ds1)
@@ -73,11 +102,23 @@ __device__ __forceinline__ void bwd_pair(const AttnBwdArgs &a, float s0, float s
     if constexpr (MODE == AM_SOFTCAP_POLY) {
         uint32_t aw;
         const uint32_t tw = softcap_poly_pair(s0, s1, a.scale, a.tanh16, aw);
-        const uint32_t dw = bc<uint32_t>(horner_f16<3, false>(bc<h2>(min_u16x2(aw, a.dtanh16.lc)), a.dtanh16));
-        const float p0 = __builtin_amdgcn_exp2f(fma_mix_lo(tw, a.c2, nl0));
-        const float p1 = __builtin_amdgcn_exp2f(fma_mix_hi(tw, a.c2, nl1));
+        uint32_t dw = bc<uint32_t>(horner_f16<3, false>(bc<h2>(min_u16x2(aw, a.dtanh16.lc)), a.dtanh16));
+        // 0 where |x| > Lc: the sign of the 16-bit Lc - |x| (no overflow:
+        // both are at most 0x7FFF)
+        dw &= ~fill_sign16(bc<uint32_t>(bc<i16x2>(a.dtanh16.lc) - bc<i16x2>(aw)));
+        float p0, p1;
+        bwd_exp2<EXP>(fma_mix_lo(tw, a.c2, nl0), fma_mix_hi(tw, a.c2, nl1), p0, p1);
         ds0 = fma_mix_lo(dw, p0 * (dp0 - dl0), -0.0f);
         ds1 = fma_mix_hi(dw, p1 * (dp1 - dl1), -0.0f);
+        pw = pack_bf(p0, p1);
+    } else if constexpr (MODE == AM_SOFTCAP_POLY_BF16) {
+        float t0, t1, x0, x1, th0, th1;
+        softcap_bf16_pair(s0, s1, a.scale, a.tanhbf, t0, t1, x0, x1, th0, th1);
+        const float d0 = dtanh_bf16(x0, th0, a.dtanhbf), d1 = dtanh_bf16(x1, th1, a.dtanhbf);
+        float p0, p1;
+        bwd_exp2<EXP>(fmaf(t0, a.c2, nl0), fmaf(t1, a.c2, nl1), p0, p1);
+        ds0 = d0 * (p0 * (dp0 - dl0));
+        ds1 = d1 * (p1 * (dp1 - dl1));
         pw = pack_bf(p0, p1);
     } else if constexpr (MODE == AM_SOFTCAP_NATIVE) {
         const float t0 = tanhf(s0 * a.scale), t1 = tanhf(s1 * a.scale);
@@ -100,7 +141,7 @@ __device__ __forceinline__ void bwd_pair(const AttnBwdArgs &a, float s0, float s
     }
 }
 
-template <int MODE>
+template <int MODE, int EXP = 0>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_bwd_dq(AttnBwdArgs a)
 {
     constexpr bool SOFTCAP = am_softcap(MODE);
@@ -203,7 +244,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                         const int e = jj * 8 + e2 * 2;
                         uint32_t pw;   // P is not needed here
                         float d0, d1;
-                        bwd_pair<MODE>(a, s[e], s[e + 1], dp[e], dp[e + 1], nl, nl, dl, dl, pw, d0, d1);
+                        bwd_pair<MODE, EXP>(a, s[e], s[e + 1], dp[e], dp[e + 1], nl, nl, dl, dl, pw, d0, d1);
                         uint32_t w = pack_bf(d0, d1);
                         if constexpr (MASKED) {
                             const int k0 = key0 + kb * 32 + (e >> 2) * 8 + h * 4 + (e & 3);
@@ -257,7 +298,7 @@ constexpr int AT_BQ = 64;    // query rows per streamed tile
 // parallel; each writes its FP32 dK, dV contribution to a.part and
 // k_attn_bwd_reduce sums the group.  Without the split the workgroups of a
 // causal launch differ G-fold more in work and there are G times fewer.
-template <int MODE, bool SPLIT>
+template <int MODE, bool SPLIT, int EXP = 0>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_attn_bwd_dkdv(AttnBwdArgs a)
 {
     constexpr bool SOFTCAP = am_softcap(MODE);
@@ -391,8 +432,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             }
             float d0, d1;
             constexpr int f = qb * 2 + (j >> 1), w = (j & 1) * 2 + (i >> 1);
-            bwd_pair<MODE>(a, s[qb][e], s[qb][e + 1], dp[qb][e], dp[qb][e + 1], nl0, nl1, dl0, dl1,
-                           pw[f][w], d0, d1);
+            bwd_pair<MODE, EXP>(a, s[qb][e], s[qb][e + 1], dp[qb][e], dp[qb][e + 1], nl0, nl1, dl0, dl1,
+                                pw[f][w], d0, d1);
             dw[f][w] = pack_bf(d0, d1);
             if constexpr (w == 3) {
                 pf[f] = bc<bf16x8>(u32x4{pw[f][0], pw[f][1], pw[f][2], pw[f][3]});
@@ -468,8 +509,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                         const int e = j * 4 + i;
                         uint32_t pk;
                         float d0, d1;
-                        bwd_pair<MODE>(a, s[qb][e], s[qb][e + 1], dp[qb][e], dp[qb][e + 1], nl4[i],
-                                       nl4[i + 1], dl4[i], dl4[i + 1], pk, d0, d1);
+                        bwd_pair<MODE, EXP>(a, s[qb][e], s[qb][e + 1], dp[qb][e], dp[qb][e + 1], nl4[i],
+                                            nl4[i + 1], dl4[i], dl4[i + 1], pk, d0, d1);
                         uint32_t dk2 = pack_bf(d0, d1);
                         const int q = r0 + qb * 32 + j * 8 + h * 4 + i;
                         const bool vis0 = q < S && (!a.causal || q >= my_k);

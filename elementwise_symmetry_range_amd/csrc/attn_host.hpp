@@ -74,6 +74,17 @@ inline float bf16_value(uint16_t bits)
     return v;
 }
 
+// Round an FP32 value to the nearest BF16 value, ties to even (finite input).
+inline float bf16_round(float v)
+{
+    uint32_t w;
+    std::memcpy(&w, &v, 4);
+    w = (w + 0x7FFFu + ((w >> 16) & 1u)) & 0xFFFF0000u;
+    float r;
+    std::memcpy(&r, &w, 4);
+    return r;
+}
+
 // The D4 tanh program and its analytic derivative (coefficients (j + 1)
 // c_{j+1}, all exact in FP16) in FP16.
 inline void tanh_coefs(CoefF16 &fwd, CoefF16 &der)
@@ -84,6 +95,18 @@ inline void tanh_coefs(CoefF16 &fwd, CoefF16 &der)
     for (int j = 0; j <= p->degree; ++j) fwd.c[j] = f16_dup(bf16_value(p->coeff[j]));
     for (int j = 0; j < p->degree; ++j) der.c[j] = f16_dup((float)(j + 1) * bf16_value(p->coeff[j + 1]));
     fwd.lc = der.lc = f16_dup(p->Lc);
+}
+
+// The same program in BF16, and its derivative with the coefficients
+// (j + 1) c_{j+1} rounded to BF16 (3 c_3 needs more than 8 bits).
+inline void tanh_coefs_bf16(TanhBF16 &fwd, TanhBF16 &der)
+{
+    const ProgramDef *p = find_program(PA_TANH, 0);
+    fwd = TanhBF16{};
+    der = TanhBF16{};
+    for (int j = 0; j <= p->degree && j < 5; ++j) fwd.c[j] = bf16_value(p->coeff[j]);
+    for (int j = 0; j < p->degree && j < 4; ++j) der.c[j] = bf16_round((float)(j + 1) * bf16_value(p->coeff[j + 1]));
+    fwd.lc = der.lc = p->Lc;
 }
 
 // The FP16 encoding of a BF16 value, or -1 when FP16 cannot hold it exactly.
@@ -143,11 +166,19 @@ inline SigCoef sigmoid_coefs()
 
 inline pa_status attn_launched() { return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH; }
 
+template <int MODE, int EXP, bool SREF>
+inline void attn_fwd_launch(const AttnArgs &a, dim3 grid, hipStream_t stream)
+{
+    hipLaunchKernelGGL((k_attn_fwd<MODE, EXP, SREF>), grid, dim3(256), 0, stream, a);
+}
+
+// exp2_core: 0 the hardware exponential, 1-4 a software core (the BF16
+// softcap program only).
 inline pa_status attn_fwd(int mode, const void *q, const void *k, const void *v, void *o, float *lse,
                           int32_t B, int32_t H, int32_t Hkv, int32_t S, int32_t D, float cap,
                           int32_t causal, hipStream_t stream, int exp2_core = 0)
 {
-    if (exp2_core < 0 || exp2_core > 4 || (exp2_core && mode != AM_SOFTCAP_POLY)) return PA_ERR_FUNC;
+    if (exp2_core < 0 || exp2_core > 4 || (exp2_core && mode != AM_SOFTCAP_POLY_BF16)) return PA_ERR_FUNC;
     if (!q || !k || !v || !o) return PA_ERR_NULL;
     if (!aligned16({q, k, v, o}) || ((uintptr_t)lse & 3u)) return PA_ERR_ALIGN;
     pa_status st = attn_shape(B, H, Hkv, S, D);
@@ -174,40 +205,42 @@ inline pa_status attn_fwd(int mode, const void *q, const void *k, const void *v,
         a.c2 = (float)((double)cap * 1.4426950408889634074);
         CoefF16 der;
         tanh_coefs(a.tanh16, der);
+        TanhBF16 derb;
+        tanh_coefs_bf16(a.tanhbf, derb);
     } else {
         a.scale = (float)(1.0 / std::sqrt((double)D));
         a.logn = (float)std::log((double)S);
         a.sig = sigmoid_coefs();
     }
     const dim3 grid((unsigned)(((S + AT_BM - 1) / AT_BM) * (B * H)));
+    // the fixed reference while every logit's exponent fits (cap log2 e <= 80)
     const bool sref = softcap && a.c2 <= 80.0f;
     if (sref) a.mref = std::ceil(a.c2 - 40.0f);
-    if (sref) {
-        switch (exp2_core) {
-        case 1: hipLaunchKernelGGL((k_attn_fwd<AM_SOFTCAP_POLY, 1, true>), grid, dim3(256), 0, stream, a); break;
-        case 2: hipLaunchKernelGGL((k_attn_fwd<AM_SOFTCAP_POLY, 2, true>), grid, dim3(256), 0, stream, a); break;
-        case 3: hipLaunchKernelGGL((k_attn_fwd<AM_SOFTCAP_POLY, 3, true>), grid, dim3(256), 0, stream, a); break;
-        case 4: hipLaunchKernelGGL((k_attn_fwd<AM_SOFTCAP_POLY, 4, true>), grid, dim3(256), 0, stream, a); break;
-        default:
-            if (mode == AM_SOFTCAP_POLY)
-                hipLaunchKernelGGL((k_attn_fwd<AM_SOFTCAP_POLY, 0, true>), grid, dim3(256), 0, stream, a);
-            else
-                hipLaunchKernelGGL((k_attn_fwd<AM_SOFTCAP_NATIVE, 0, true>), grid, dim3(256), 0, stream, a);
-        }
-        return attn_launched();
-    }
-    switch (exp2_core) {
-    case 1: hipLaunchKernelGGL((k_attn_fwd<AM_SOFTCAP_POLY, 1>), grid, dim3(256), 0, stream, a); return attn_launched();
-    case 2: hipLaunchKernelGGL((k_attn_fwd<AM_SOFTCAP_POLY, 2>), grid, dim3(256), 0, stream, a); return attn_launched();
-    case 3: hipLaunchKernelGGL((k_attn_fwd<AM_SOFTCAP_POLY, 3>), grid, dim3(256), 0, stream, a); return attn_launched();
-    case 4: hipLaunchKernelGGL((k_attn_fwd<AM_SOFTCAP_POLY, 4>), grid, dim3(256), 0, stream, a); return attn_launched();
-    default: break;
-    }
     switch (mode) {
-    case AM_SOFTCAP_POLY: hipLaunchKernelGGL(k_attn_fwd<AM_SOFTCAP_POLY>, grid, dim3(256), 0, stream, a); break;
-    case AM_SOFTCAP_NATIVE: hipLaunchKernelGGL(k_attn_fwd<AM_SOFTCAP_NATIVE>, grid, dim3(256), 0, stream, a); break;
-    case AM_SIGMOID_POLY: hipLaunchKernelGGL(k_attn_fwd<AM_SIGMOID_POLY>, grid, dim3(256), 0, stream, a); break;
-    default: hipLaunchKernelGGL(k_attn_fwd<AM_SIGMOID_NATIVE>, grid, dim3(256), 0, stream, a); break;
+    case AM_SOFTCAP_POLY_BF16:
+        switch (exp2_core * 2 + (sref ? 1 : 0)) {
+        case 0: attn_fwd_launch<AM_SOFTCAP_POLY_BF16, 0, false>(a, grid, stream); break;
+        case 1: attn_fwd_launch<AM_SOFTCAP_POLY_BF16, 0, true>(a, grid, stream); break;
+        case 2: attn_fwd_launch<AM_SOFTCAP_POLY_BF16, 1, false>(a, grid, stream); break;
+        case 3: attn_fwd_launch<AM_SOFTCAP_POLY_BF16, 1, true>(a, grid, stream); break;
+        case 4: attn_fwd_launch<AM_SOFTCAP_POLY_BF16, 2, false>(a, grid, stream); break;
+        case 5: attn_fwd_launch<AM_SOFTCAP_POLY_BF16, 2, true>(a, grid, stream); break;
+        case 6: attn_fwd_launch<AM_SOFTCAP_POLY_BF16, 3, false>(a, grid, stream); break;
+        case 7: attn_fwd_launch<AM_SOFTCAP_POLY_BF16, 3, true>(a, grid, stream); break;
+        case 8: attn_fwd_launch<AM_SOFTCAP_POLY_BF16, 4, false>(a, grid, stream); break;
+        default: attn_fwd_launch<AM_SOFTCAP_POLY_BF16, 4, true>(a, grid, stream); break;
+        }
+        break;
+    case AM_SOFTCAP_POLY:
+        if (sref) attn_fwd_launch<AM_SOFTCAP_POLY, 0, true>(a, grid, stream);
+        else attn_fwd_launch<AM_SOFTCAP_POLY, 0, false>(a, grid, stream);
+        break;
+    case AM_SOFTCAP_NATIVE:
+        if (sref) attn_fwd_launch<AM_SOFTCAP_NATIVE, 0, true>(a, grid, stream);
+        else attn_fwd_launch<AM_SOFTCAP_NATIVE, 0, false>(a, grid, stream);
+        break;
+    case AM_SIGMOID_POLY: attn_fwd_launch<AM_SIGMOID_POLY, 0, false>(a, grid, stream); break;
+    default: attn_fwd_launch<AM_SIGMOID_NATIVE, 0, false>(a, grid, stream); break;
     }
     return attn_launched();
 }
@@ -224,19 +257,19 @@ inline int64_t attn_bwd_ws_floats(bool softcap, int32_t B, int32_t H, int32_t Hk
     return n;
 }
 
-template <int MODE>
+template <int MODE, int EXP = 0>
 inline void attn_bwd_launch(const AttnBwdArgs &a, int32_t B, int32_t H, int32_t Hkv, int32_t S,
                             hipStream_t stream)
 {
     const dim3 gq((unsigned)(((S + AT_BM - 1) / AT_BM) * (B * H)));
-    hipLaunchKernelGGL(k_attn_bwd_dq<MODE>, gq, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((k_attn_bwd_dq<MODE, EXP>), gq, dim3(256), 0, stream, a);
     const int ntk = (S + AT_BK - 1) / AT_BK;
     if (H == Hkv) {
-        hipLaunchKernelGGL((k_attn_bwd_dkdv<MODE, false>), dim3((unsigned)(ntk * B * Hkv)), dim3(256), 0,
+        hipLaunchKernelGGL((k_attn_bwd_dkdv<MODE, false, EXP>), dim3((unsigned)(ntk * B * Hkv)), dim3(256), 0,
                            stream, a);
         return;
     }
-    hipLaunchKernelGGL((k_attn_bwd_dkdv<MODE, true>), dim3((unsigned)(ntk * B * H)), dim3(256), 0, stream,
+    hipLaunchKernelGGL((k_attn_bwd_dkdv<MODE, true, EXP>), dim3((unsigned)(ntk * B * H)), dim3(256), 0, stream,
                        a);
     const int64_t n8 = (int64_t)B * Hkv * S * AT_D / 8;
     hipLaunchKernelGGL(k_attn_bwd_reduce, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream, a, n8,
@@ -247,8 +280,9 @@ inline void attn_bwd_launch(const AttnBwdArgs &a, int32_t B, int32_t H, int32_t 
 inline pa_status attn_bwd(int mode, const void *q, const void *k, const void *v, const void *o,
                           const void *dout, const float *lse, void *dq, void *dk, void *dv, float *ws,
                           int32_t B, int32_t H, int32_t Hkv, int32_t S, int32_t D, float cap,
-                          int32_t causal, hipStream_t stream)
+                          int32_t causal, hipStream_t stream, int exp2_core = 0)
 {
+    if (exp2_core < 0 || exp2_core > 4 || (exp2_core && mode != AM_SOFTCAP_POLY_BF16)) return PA_ERR_FUNC;
     const bool softcap = am_softcap(mode);
     if (!q || !k || !v || !dout || !dq || !dk || !dv) return PA_ERR_NULL;
     if (softcap && (!o || !lse)) return PA_ERR_NULL;
@@ -291,12 +325,22 @@ inline pa_status attn_bwd(int mode, const void *q, const void *k, const void *v,
         a.scale = (float)(1.0 / ((double)cap * std::sqrt((double)D)));
         a.c2 = (float)((double)cap * 1.4426950408889634074);
         tanh_coefs(a.tanh16, a.dtanh16);
+        tanh_coefs_bf16(a.tanhbf, a.dtanhbf);
     } else {
         a.scale = a.rsd;
         a.logn = (float)std::log((double)S);
         a.sig = sigmoid_coefs();
     }
     switch (mode) {
+    case AM_SOFTCAP_POLY_BF16:
+        switch (exp2_core) {
+        case 1: attn_bwd_launch<AM_SOFTCAP_POLY_BF16, 1>(a, B, H, Hkv, S, stream); break;
+        case 2: attn_bwd_launch<AM_SOFTCAP_POLY_BF16, 2>(a, B, H, Hkv, S, stream); break;
+        case 3: attn_bwd_launch<AM_SOFTCAP_POLY_BF16, 3>(a, B, H, Hkv, S, stream); break;
+        case 4: attn_bwd_launch<AM_SOFTCAP_POLY_BF16, 4>(a, B, H, Hkv, S, stream); break;
+        default: attn_bwd_launch<AM_SOFTCAP_POLY_BF16, 0>(a, B, H, Hkv, S, stream); break;
+        }
+        break;
     case AM_SOFTCAP_POLY: attn_bwd_launch<AM_SOFTCAP_POLY>(a, B, H, Hkv, S, stream); break;
     case AM_SOFTCAP_NATIVE: attn_bwd_launch<AM_SOFTCAP_NATIVE>(a, B, H, Hkv, S, stream); break;
     case AM_SIGMOID_POLY: attn_bwd_launch<AM_SIGMOID_POLY>(a, B, H, Hkv, S, stream); break;

@@ -303,21 +303,31 @@ pa_status poly_program_info(int32_t f, int32_t deriv, int32_t t, pa_program *out
     if (t != PA_F16 && t != PA_BF16) return PA_ERR_DTYPE;
     if (deriv == 2) {
         // the analytic derivative of the D4 tanh program (softcap attention
-        // backward), FP16 coefficients
+        // backward): FP16 coefficients (exact), or BF16 ones (rounded)
         if (f != PA_TANH) return PA_ERR_FUNC;
-        if (t != PA_F16) return PA_ERR_DTYPE;
         const ProgramDef *p = find_program(PA_TANH, 0);
         std::memset(out, 0, sizeof *out);
-        CoefF16 fwd, der;
-        tanh_coefs(fwd, der);
         out->func = PA_TANH;
         out->deriv = 2;
         out->degree = p->degree - 1;
         out->dtype = t;
         out->Li = p->Li;
         out->Lc = p->Lc;
-        for (int j = 0; j < p->degree; ++j) out->coeff_bits[j] = (uint16_t)(der.c[j] & 0xFFFFu);
-        out->order = PA_ORDER_F16_FMA;
+        if (t == PA_F16) {
+            CoefF16 fwd, der;
+            tanh_coefs(fwd, der);
+            for (int j = 0; j < p->degree; ++j) out->coeff_bits[j] = (uint16_t)(der.c[j] & 0xFFFFu);
+            out->order = PA_ORDER_F16_FMA;
+        } else {
+            TanhBF16 fwd, der;
+            tanh_coefs_bf16(fwd, der);
+            for (int j = 0; j < p->degree; ++j) {
+                uint32_t w;
+                std::memcpy(&w, &der.c[j], 4);
+                out->coeff_bits[j] = (uint16_t)(w >> 16);
+            }
+            out->order = PA_ORDER_F32FMA_BF16;
+        }
         return PA_OK;
     }
     const ProgramDef *p = find_program((int)f, deriv ? 1 : 0);
@@ -489,6 +499,13 @@ pa_status poly_softcap_attn_fwd(const void *q, const void *k, const void *v, voi
                                 int32_t B, int32_t H, int32_t Hkv, int32_t S, int32_t D, float cap,
                                 int32_t causal, hipStream_t stream)
 {
+    return attn_fwd(AM_SOFTCAP_POLY_BF16, q, k, v, o, lse, B, H, Hkv, S, D, cap, causal, stream);
+}
+
+pa_status poly_softcap_attn_fwd_f16(const void *q, const void *k, const void *v, void *o, float *lse,
+                                    int32_t B, int32_t H, int32_t Hkv, int32_t S, int32_t D, float cap,
+                                    int32_t causal, hipStream_t stream)
+{
     return attn_fwd(AM_SOFTCAP_POLY, q, k, v, o, lse, B, H, Hkv, S, D, cap, causal, stream);
 }
 
@@ -497,7 +514,7 @@ pa_status poly_softcap_attn_fwd_exp2(const void *q, const void *k, const void *v
                                      int32_t D, float cap, int32_t causal, int32_t core,
                                      hipStream_t stream)
 {
-    return attn_fwd(AM_SOFTCAP_POLY, q, k, v, o, lse, B, H, Hkv, S, D, cap, causal, stream,
+    return attn_fwd(AM_SOFTCAP_POLY_BF16, q, k, v, o, lse, B, H, Hkv, S, D, cap, causal, stream,
                     (int)core);
 }
 
@@ -513,8 +530,27 @@ pa_status poly_softcap_attn_bwd(const void *q, const void *k, const void *v, con
                                 float *workspace, int32_t B, int32_t H, int32_t Hkv, int32_t S,
                                 int32_t D, float cap, int32_t causal, hipStream_t stream)
 {
+    return attn_bwd(AM_SOFTCAP_POLY_BF16, q, k, v, o, dout, lse, dq, dk, dv, workspace, B, H, Hkv, S,
+                    D, cap, causal, stream);
+}
+
+pa_status poly_softcap_attn_bwd_f16(const void *q, const void *k, const void *v, const void *o,
+                                    const void *dout, const float *lse, void *dq, void *dk, void *dv,
+                                    float *workspace, int32_t B, int32_t H, int32_t Hkv, int32_t S,
+                                    int32_t D, float cap, int32_t causal, hipStream_t stream)
+{
     return attn_bwd(AM_SOFTCAP_POLY, q, k, v, o, dout, lse, dq, dk, dv, workspace, B, H, Hkv, S, D,
                     cap, causal, stream);
+}
+
+pa_status poly_softcap_attn_bwd_exp2(const void *q, const void *k, const void *v, const void *o,
+                                     const void *dout, const float *lse, void *dq, void *dk,
+                                     void *dv, float *workspace, int32_t B, int32_t H, int32_t Hkv,
+                                     int32_t S, int32_t D, float cap, int32_t causal, int32_t core,
+                                     hipStream_t stream)
+{
+    return attn_bwd(AM_SOFTCAP_POLY_BF16, q, k, v, o, dout, lse, dq, dk, dv, workspace, B, H, Hkv, S,
+                    D, cap, causal, stream, (int)core);
 }
 
 pa_status native_softcap_attn_bwd(const void *q, const void *k, const void *v, const void *o,

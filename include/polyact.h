@@ -14,7 +14,9 @@
  *     (section 3.3, section 3.4, Eq. 15) over dense or expert-grouped rows
  *   - the D4 tanh as the softcap alpha tanh(x / alpha) on attention logits
  *     inside a flash-attention forward, and its analytic derivative (a D3)
- *     in the backward (Eq. 1, Eq. 12, sections 3.3 and 5.2.2)
+ *     in the backward (Eq. 1, Eq. 12, sections 3.3 and 5.2.2), in BF16 as
+ *     the pages run it (section 3.4) or in packed FP16; the softmax's
+ *     exponentials optionally by a software exp2 core (Appendix B.1)
  *   - sigmoid attention P = sigma(s - ln n) (Eq. 14) with the two-region
  *     cubic and its factored derivative surrogate of section 3.4, forward
  *     and backward.
@@ -59,7 +61,7 @@ extern "C" {
 /* HIP's stream handle (the same typedef as hip_runtime_api.h). */
 typedef struct ihipStream_t *hipStream_t;
 
-#define PA_ABI_VERSION 2
+#define PA_ABI_VERSION 3
 
 typedef enum {
     PA_OK = 0,
@@ -98,10 +100,10 @@ typedef struct {
     int32_t func;          /* pa_func                                        */
     int32_t deriv;         /* 0 forward program, 1 direct derivative program,
                               2 analytic derivative of the forward program
-                              (PA_TANH with PA_F16 only: the softcap
-                              attention backward; coeff_bits are then FP16
-                              bit patterns (j + 1) c_{j+1}, not all of which
-                              are BF16 values)                              */
+                              (PA_TANH only: the softcap attention backward;
+                              coeff_bits are (j + 1) c_{j+1} as FP16 bit
+                              patterns for PA_F16, exact, or rounded to BF16
+                              for PA_BF16)                                  */
     int32_t degree;        /* D                                              */
     int32_t dtype;         /* pa_dtype the info was requested for            */
     float Li;              /* fit interval [0, Li] (section 3.2)             */
@@ -169,20 +171,32 @@ pa_status poly_swiglu_bwd(int32_t t, const void *gate, const void *up, const voi
  * aligned.  No output may overlap another output or an input
  * (PA_ERR_OVERLAP).  B * H * ceil(S / 128) must fit in int32. */
 
-/* Softcapped attention forward:
- *   S = Q K^T;  x = RN_f16(RN_f32(S) * RN_f32(1 / (cap sqrt(D))));
- *   s = cap * tanh~(x), the D4 tanh program in packed FP16 arithmetic (the
- *   packed 16-bit FMA of gfx950; its coefficients are the BF16 fit, exact in
- *   FP16);  causal mask;  P = softmax(s) (FP32, online, exp2);
- *   O = P V / l with P rounded to BF16 for the MFMA.
+/* Softcapped attention forward, the pages' B2 program in BF16:
+ *   S = Q K^T (FP32);  x = RN_bf16(RN_f32(S) * RN_f32(1 / (cap sqrt(D))));
+ *   t = the D4 tanh program on x, each Horner stage an FP32 FMA rounded to
+ *   BF16, t^ = min(|x|, Lc), sign restored;  s = cap t;  causal mask;
+ *   P = softmax(s) in FP32 with exp2 (log2 e folded into RN_f32(cap log2 e));
+ *   O = P V / l with P rounded to BF16 for the product, l the FP32 row sum.
+ * The softmax runs against a fixed reference ceil(RN_f32(cap log2 e) - 40)
+ * when cap log2 e <= 80 (every logit is bounded by cap, so all P stay normal
+ * FP32), else against an integer running reference with 2^z evaluated as
+ * 2^floor(z) 2^(z - floor z).
  * lse (nullable): the natural log-sum-exp of each row's softcapped logits,
  *   the input the backward needs.  cap > 0 and finite.
- * Paper: Eq. 1 and section 5.2.2 (D4 tanh softcap inside attention). */
+ * Paper: Eq. 1, section 3.4 (BF16 integrations), section 5.2.2 (the D4 tanh
+ * softcap inside attention). */
 pa_status poly_softcap_attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
                                 int32_t B, int32_t H, int32_t Hkv, int32_t S, int32_t D, float cap,
                                 int32_t causal, hipStream_t stream);
 
-/* The softmax's exponentials of poly_softcap_attn_fwd by a software exp2
+/* The same with the tanh program in packed FP16 (the isolated sweep's
+ * format, section 3.4): x = RN_f16(RN_f32(S) * RN_f32(1 / (cap sqrt(D)))), the
+ * BF16-fitted coefficients as FP16 values, one FP16 rounding per stage. */
+pa_status poly_softcap_attn_fwd_f16(const void *q, const void *k, const void *v, void *o,
+                                    float *lse, int32_t B, int32_t H, int32_t Hkv, int32_t S,
+                                    int32_t D, float cap, int32_t causal, hipStream_t stream);
+
+/* poly_softcap_attn_fwd with the softmax's exponentials by a software exp2
  * (Appendix B.1, Eqs. 16-19): 2^z = 2^n p(f) with n = floor(z), f = z - n
  * in [0, 1), z = RN_f32(t * RN_f32(cap log2 e)) clamped below at -16384, and
  * the running reference kept an integer so that every rescale is an exact
@@ -196,7 +210,7 @@ pa_status poly_softcap_attn_fwd(const void *q, const void *k, const void *v, voi
  *                  (the pages' reference cubic; p(1) != 2), FP32 FMA
  * D1, PWL2 and D2 keep p(0) = 1 and p(1) = 2 exactly after rounding (the
  * invariants online softmax needs).  lse as for poly_softcap_attn_fwd, with
- * the approximate exponentials. */
+ * the approximate exponentials.  Unknown core: PA_ERR_FUNC. */
 typedef enum { PA_EXP2_HW = 0, PA_EXP2_D1 = 1, PA_EXP2_PWL2 = 2, PA_EXP2_D2 = 3,
                PA_EXP2_D3 = 4 } pa_exp2_core;
 pa_status poly_softcap_attn_fwd_exp2(const void *q, const void *k, const void *v, void *o,
@@ -204,18 +218,21 @@ pa_status poly_softcap_attn_fwd_exp2(const void *q, const void *k, const void *v
                                      int32_t D, float cap, int32_t causal, int32_t core,
                                      hipStream_t stream);
 
-/* Softcapped attention backward: given the forward's O and lse and the
- * upstream gradient dout, writes dq, dk, dv:
- *   P = exp(s - lse) recomputed with the forward's program;  dV = P^T dO;
- *   dP = dO V^T;  Delta_i = dO_i . O_i;  dS = P (dP - Delta) ds/dS;
- *   dQ = dS K,  dK = dS^T Q (summed over the query heads of a group),
- * where ds/dS uses the analytic derivative of the D4 tanh program (a D3 with
- * coefficients (j + 1) c_{j+1}, exact in FP16; poly_program_info(PA_TANH, 2,
- * PA_F16)) in packed FP16 at the same clamped |x|.  P and dS are rounded to
- * BF16 for the MFMA.  workspace: caller-owned scratch, 16-byte aligned, of
- * pa_attn_bwd_workspace_bytes(1, B, H, Hkv, S, D) bytes: B * H * S floats
- * each for Delta and for -lse log2(e) (each region rounded up to 16 bytes)
- * and, when H > Hkv, FP32 dK and dV partials of every query head
+/* Softcapped attention backward of poly_softcap_attn_fwd: given the
+ * forward's O and lse and the upstream gradient dout, writes dq, dk, dv:
+ *   P = exp2(RN_f32(t RN_f32(cap log2 e) - RN_f32(lse log2 e))) recomputed
+ *   with the forward's program;  dV = P^T dO;  dP = dO V^T;
+ *   Delta_i = dO_i . O_i;  dS = RN_f32(q'(x) RN_f32(P RN_f32(dP - Delta)));
+ *   dQ = dS K / sqrt(D),  dK = dS^T Q / sqrt(D) (summed over the query heads
+ *   of a group),
+ * where q'(x) is the analytic derivative of the D4 tanh program, the D3 with
+ * coefficients (j + 1) c_{j+1} rounded to BF16 (poly_program_info(PA_TANH, 2,
+ * PA_BF16)) evaluated like the forward program at |x|, and 0 where
+ * |x| > Lc (the clamped forward program is constant there).  P and dS are
+ * rounded to BF16 for the MFMA.  workspace: caller-owned scratch, 16-byte
+ * aligned, of pa_attn_bwd_workspace_bytes(1, B, H, Hkv, S, D) bytes: B * H * S
+ * floats each for Delta and for -lse log2(e) (each region rounded up to 16
+ * bytes) and, when H > Hkv, FP32 dK and dV partials of every query head
  * (summed per group by a final pass in a fixed order); contents on return
  * unspecified.
  * Paper: Eq. 12 and section 5.2.2 (the differentiated D3 at the recomputed
@@ -224,6 +241,26 @@ pa_status poly_softcap_attn_bwd(const void *q, const void *k, const void *v, con
                                 const void *dout, const float *lse, void *dq, void *dk, void *dv,
                                 float *workspace, int32_t B, int32_t H, int32_t Hkv, int32_t S,
                                 int32_t D, float cap, int32_t causal, hipStream_t stream);
+
+/* Backward of poly_softcap_attn_fwd_f16: the FP16 program and its FP16
+ * derivative (coefficients exact in FP16; poly_program_info(PA_TANH, 2,
+ * PA_F16)), 0 beyond the clamp; otherwise as poly_softcap_attn_bwd. */
+pa_status poly_softcap_attn_bwd_f16(const void *q, const void *k, const void *v, const void *o,
+                                    const void *dout, const float *lse, void *dq, void *dk,
+                                    void *dv, float *workspace, int32_t B, int32_t H, int32_t Hkv,
+                                    int32_t S, int32_t D, float cap, int32_t causal,
+                                    hipStream_t stream);
+
+/* Backward of poly_softcap_attn_fwd_exp2: P recomputed as 2^z with
+ * z = RN_f32(t RN_f32(cap log2 e) - RN_f32(lse log2 e)) through the same exp2
+ * core (2^floor(z) p(z - floor z)); otherwise as poly_softcap_attn_bwd.
+ * Paper: Appendix B.1 (the cores inside the attention's forward and
+ * backward). */
+pa_status poly_softcap_attn_bwd_exp2(const void *q, const void *k, const void *v, const void *o,
+                                     const void *dout, const float *lse, void *dq, void *dk,
+                                     void *dv, float *workspace, int32_t B, int32_t H, int32_t Hkv,
+                                     int32_t S, int32_t D, float cap, int32_t causal, int32_t core,
+                                     hipStream_t stream);
 
 /* Sigmoid attention forward, O = P V with P = sigma(s - ln n) and
  * s = q.k / sqrt(D) (Eq. 14), n = S.  The program: x = RN_bf16(RN_f32(S_ij) *

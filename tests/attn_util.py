@@ -1,27 +1,22 @@
-"""Helpers of the attention parity tests: tolerance checks and oracle inputs.
+"""Helpers of the attention parity tests: the gate and oracle inputs.
 
-Tolerance of one BF16 output g against the oracle's FP64 value r, derived from
-the arithmetic the kernels perform: the MFMA operands P (and, backward, dS)
-are rounded to BF16 (unit roundoff u = 2^-8) while everything else runs in
-FP32 (relative 2^-24); the oracle returns, per output, the noise scale
-n = sqrt(sum of squared terms of the sum that forms r).  Independent uniform
-relative roundings of the terms give a standard deviation (u / sqrt 3) n, so
+The oracle's replay model performs the method's own rounding steps (FP32
+scores, exponent arguments and backward scalars; P and dS rounded to BF16
+before the products; Fast Polynomial Transcendentals for LLMs, section 3.4
+and section 5.2.2) and returns each output in FP64 with its spread: the
+largest change admissible alternatives of the replay's rounding decisions can
+cause (the pages leave the accumulation order of an FP32 dot product and the
+last bit of an FP32 exponential open).  The gate for one BF16 output g
+against the oracle's r:
 
-    |g - r| <= ulp_bf16(r) + 7 (u / sqrt 3) n + 2^-20,
+    |g - r| <= u(r) + spread,    u(r) = max(ulp_bf16(r), 2^-16),
 
-the first term for the final BF16 rounding of g, the last for FP32 rounding
-of results near zero.  Backward, dS = P (dP - Delta) ds/dS (softcap) or
-dP dP/ds (sigmoid) is formed from FP32 sums of D products; their rounding
-errs by at most D 2^-24 times the sum of the absolute products, which the
-oracle propagates into a cancellation scale c per dQ / dK output (it matters
-where dP and Delta cancel, e.g. a causal row that sees one key, where the
-exact gradient is 0); the bound then gains D 2^-24 c.  The comparators form
-the transform's derivative g from a rounded FP32 value (1 - t^2 from tanhf,
-sigma (1 - sigma)), off by at most 2^-21 in absolute terms (two ulps of t
-doubled, plus the roundings of t^2 and of the difference), which matters
-where 1 - t^2 is tiny; with the oracle's sensitivity s = sum |dS / g| |K|
-the comparator bound gains 2^-21 s.  The programs' derivative values are
-exact (the oracle replays them).
+one BF16 ulp of the oracle's value, floored at 2^-16 for |r| < 2^-8 (the
+final rounding of g and the FP32 accumulation of the sums), plus the spread,
+which is zero unless a rounding decision is close.  Every comparison prints
+how many outputs are within 1 ulp and how many needed the spread, and the
+latter are capped (ALT_CAP of the outputs): the spread explains individual
+decisions, it is not a tolerance for a whole tensor.
 """
 import json
 import os
@@ -30,34 +25,35 @@ import numpy as np
 
 import synth_inputs as si
 
-U = 2.0 ** -8
 HERE = os.path.dirname(os.path.abspath(__file__))
+ALT_CAP = 5e-3   # largest share of outputs that may need the spread (at least 16)
 
 
 def bf16v(b):
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
-def ulp_bf16(a):
-    a = np.abs(a)
-    e = np.floor(np.log2(np.maximum(a, 2.0 ** -126)))
-    return 2.0 ** (e - 7)
+def ulp_floor(a):
+    """One BF16 ulp of |a|, floored at 2^-16."""
+    e = np.floor(np.log2(np.maximum(np.abs(a), 2.0 ** -126)))
+    return np.maximum(2.0 ** (e - 7), 2.0 ** -16)
 
 
-def check(got_bits, ref, noise, label, cancel=None, dsens=None, D=128):
+def check(got_bits, ref, spread, label):
     got = bf16v(got_bits)
     err = np.abs(got - ref)
-    tol = ulp_bf16(ref) + 7 * (U / np.sqrt(3)) * noise + 2.0 ** -20
-    if cancel is not None:
-        tol = tol + D * 2.0 ** -24 * cancel
-    if dsens is not None:
-        tol = tol + 2.0 ** -21 * dsens
-    within1 = np.mean(err <= ulp_bf16(ref))
-    ratio = float(np.max(err / tol))
-    print(f"[attn] {label}: max err/tol {ratio:.3f}, within 1 ulp {within1:.4%}", flush=True)
+    u = ulp_floor(ref)
+    within1 = err <= u
+    needed = int(np.sum(~within1))
+    worst = float(np.max(err / u)) if err.size else 0.0
+    over = err - u - spread
+    print(f"[attn] {label}: {err.size} outputs, within 1 ulp {np.mean(within1):.6%}, "
+          f"needed the spread {needed}, max err {worst:.2f} ulp, "
+          f"not covered {int(np.sum(over > 0))}", flush=True)
     assert np.all(np.isfinite(got)), label
-    assert ratio <= 1.0, label
-    return ratio
+    assert np.all(over <= 0), f"{label}: {int(np.sum(over > 0))} outputs beyond 1 ulp + spread"
+    assert needed <= max(16, ALT_CAP * err.size), f"{label}: {needed} outputs needed the spread"
+    return needed
 
 
 def tanh_prog(orc):

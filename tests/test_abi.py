@@ -29,11 +29,11 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(pa):
     names = declared_functions()
-    assert len(names) == 23, names
+    assert len(names) == 26, names
     L = pa.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert L.pa_abi_version() == 2
+    assert L.pa_abi_version() == 3
 
 
 def test_program_table_matches_oracle(pa, orc):
@@ -57,8 +57,16 @@ def test_program_table_matches_oracle(pa, orc):
     assert all(float(np.float16((j + 1) * c[j + 1])) == (j + 1) * c[j + 1] for j in range(4))
     d = pa.program_info("tanh", 2, "f16")
     assert d["coeff_bits"] == want and d["degree"] == 3 and d["order"] == 1
+    # in BF16 the same values rounded to nearest even BF16 (3 c_3 is not a
+    # BF16 value), as the oracle's BF16 derivative program uses them
+    import synth_inputs as si
+    want_bf = [int(b) for b in si.to_bf16_bits(np.array([(j + 1) * c[j + 1] for j in range(4)]))]
+    d = pa.program_info("tanh", 2, "bf16")
+    assert d["coeff_bits"] == want_bf and d["degree"] == 3 and d["order"] == 3
+    assert want_bf[2] != int(np.float32(3 * c[3]).view(np.uint32) >> 16)   # rounded, not truncated
+    tp = orc.make_prog(t4["func"], t4["deriv"], t4["degree"], t4["Li"], t4["Lc"])
+    assert orc.dtanh_prog(tp, [0], "bf16")[0] == want_bf[0]                # q(0) = c_1
     out = pa.PaProgram()
-    assert pa.lib().poly_program_info(2, 2, 2, C.byref(out)) == 3   # derivative program: FP16 only
     assert pa.lib().poly_program_info(1, 2, 1, C.byref(out)) == 4   # only for tanh
     assert pa.lib().poly_program_info(9, 0, 1, C.byref(out)) == 4   # no such function
     assert pa.lib().poly_program_info(1, 0, 5, C.byref(out)) == 3   # no such dtype
@@ -152,6 +160,18 @@ def test_error_paths_attention(pa):
     assert b(Q, K, V, O, DO, LSE, DQ, DK, DV, WS + 4, 1, 2, 2, 64, 128, 50.0, 1, None) == 7
     assert b(Q, K, V, O, DO, LSE, DQ, DK, DV, WS, 1, 2, 2, 64, 128, 0.0, 1, None) == 2
     assert b(Q, K, V, O, DO, LSE, DQ, DK, DV, WS, 1, 2, 2, 0, 128, 50.0, 1, None) == 0
+    f16 = L.poly_softcap_attn_fwd_f16
+    assert f16(Q, K, V, O, None, 1, 2, 2, 64, 64, 50.0, 1, None) == 2
+    assert f16(Q, K, V, Q, None, 1, 2, 2, 64, 128, 50.0, 1, None) == 5
+    assert f16(Q, K, V, O, None, 1, 2, 2, 0, 128, 50.0, 1, None) == 0
+    b16 = L.poly_softcap_attn_bwd_f16
+    assert b16(Q, K, V, O, DO, LSE, DQ, DK, DV, None, 1, 2, 2, 64, 128, 50.0, 1, None) == 1
+    assert b16(Q, K, V, O, DO, LSE, DQ, DK, DV, WS, 1, 2, 2, 0, 128, 50.0, 1, None) == 0
+    be = L.poly_softcap_attn_bwd_exp2
+    assert be(Q, K, V, O, DO, LSE, DQ, DK, DV, WS, 1, 2, 2, 64, 128, 50.0, 1, 5, None) == 4    # core
+    assert be(Q, K, V, O, DO, LSE, DQ, DK, DV, WS, 1, 2, 2, 64, 128, 50.0, 1, -1, None) == 4
+    assert be(Q, K, V, O, DO, LSE, DQ, DK, DV, None, 1, 2, 2, 64, 128, 50.0, 1, 1, None) == 1
+    assert be(Q, K, V, O, DO, LSE, DQ, DK, DV, WS, 1, 2, 2, 0, 128, 50.0, 1, 2, None) == 0
     s = L.poly_sigmoid_attn_fwd
     assert s(Q, K, V, O, 1, 2, 2, 2048, 128, 1, None) == 2     # the fitted length is 4096
     assert s(Q, K, V, O, 1, 2, 2, 4096, 96, 1, None) == 2

@@ -1,16 +1,18 @@
 """GPU parity of the attention forwards against the CPU oracle.
 
-Softcap attention (Eq. 1; the D4 tanh program in packed FP16, or accurate
-tanhf) and sigmoid attention (Eq. 14; the two-region BF16 cubic at the
-fitted length 4096, or accurate sigma), multi-head and grouped-query layouts,
-causal or not, ragged sequence lengths.  The oracle computes each output row
-in FP64 from the same BF16 inputs with the program replayed exactly; the
-tolerance is derived in attn_util.  The log-sum-exp the softcap forward
-writes for the backward is compared too: the kernel forms it in FP32 from the
-running max and the row sum of up to S terms, so
+Softcap attention (Eq. 1; the D4 tanh program in BF16 as the pages run it,
+or in packed FP16, or accurate tanhf; the softmax's exp2 by the hardware or
+a software core) and sigmoid attention (Eq. 14; the two-region BF16 cubic at
+the fitted length 4096, or accurate sigma), multi-head and grouped-query
+layouts, causal or not, ragged sequence lengths, the fixed and the running
+softmax reference.  The oracle replays the method's rounding steps from the
+same BF16 inputs; the gate is one BF16 ulp plus the oracle's spread
+(attn_util).  The log-sum-exp the softcap forward writes for the backward is
+compared too: the kernel forms it in FP32 from the reference and the row sum
+of up to S terms, so
     |lse - lse_ref| <= 2^-14 (1 + |lse_ref|)
 (S 2^-24 relative for the sum at S = 8192, plus the FP32 rounding of the log
-and of the max).
+and of the reference).
 """
 import numpy as np
 import pytest
@@ -56,41 +58,60 @@ def draw(B, H, Hkv, S, seed, sd=1.0):
     return q, k, v
 
 
-def softcap_case(pa, orc, tp, q, k, v, causal, poly, rows=None, label=""):
+FMTS = ("bf16", "f16", "native")
+
+
+def softcap_entry(pa, fmt, core=None):
+    """(kernel call, oracle kind, oracle keywords) of a softcap variant."""
+    if core is not None:
+        cid = pa.EXP2_CORES[core]
+        return ((lambda q, k, v, cap, causal: pa.poly_softcap_attn_fwd_exp2(
+            q, k, v, cap, causal, core=core, with_lse=True)), 1, dict(tanh_fmt="bf16", exp2_core=cid))
+    if fmt == "native":
+        return ((lambda q, k, v, cap, causal: pa.native_softcap_attn_fwd(q, k, v, cap, causal,
+                                                                         with_lse=True)), 2, {})
+    return ((lambda q, k, v, cap, causal: pa.poly_softcap_attn_fwd(q, k, v, cap, causal,
+                                                                   with_lse=True, fmt=fmt)),
+            1, dict(tanh_fmt=fmt))
+
+
+def softcap_case(pa, orc, tp, q, k, v, causal, fmt, rows=None, label="", cap=50.0, core=None):
     B, H, S, D = q.shape
-    note(f"softcap fwd {label} B={B} H={H} Hkv={k.shape[1]} S={S} causal={causal} poly={poly}")
-    entry = pa.poly_softcap_attn_fwd if poly else pa.native_softcap_attn_fwd
-    o, lse = entry(to_dev(q, BF), to_dev(k, BF), to_dev(v, BF), 50.0, causal, with_lse=True)
+    note(f"softcap fwd {label} B={B} H={H} Hkv={k.shape[1]} S={S} causal={causal} fmt={fmt} "
+         f"core={core} cap={cap}")
+    call, kind, kw = softcap_entry(pa, fmt, core)
+    o, lse = call(to_dev(q, BF), to_dev(k, BF), to_dev(v, BF), cap, causal)
     o, lse = to_bits(o).reshape(-1, D), lse.cpu().numpy().ravel()
     if rows is None:
         rows = np.arange(B * H * S)
-    kind = orc.ATTN_SOFTCAP_POLY if poly else orc.ATTN_SOFTCAP_EXACT
-    ref, ref_lse, noise = orc.attn_fwd_rows(kind, q, k, v, rows, cap=50.0, causal=causal,
-                                            tanh_prog=tp)
-    lab = f"{label} S={S} causal={causal} poly={poly}"
-    check(o[rows], ref, noise, lab)
+    ref, ref_lse, spread = orc.attn_fwd_rows(kind, q, k, v, rows, cap=cap, causal=causal,
+                                             tanh_prog=tp, **kw)
+    lab = f"{label} S={S} causal={causal} fmt={fmt} core={core} cap={cap}"
+    check(o[rows], ref, spread, lab)
     check_lse(lse[rows], ref_lse, lab)
 
 
-@pytest.mark.parametrize("poly", [True, False])
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("S", [64, 128, 200, 384])
-def test_softcap_small(pa, orc, tp, S, causal, poly):
+def test_softcap_small(pa, orc, tp, S, causal, fmt):
     q, k, v = draw(1, 2, 2, S, S * 7 + 2)
-    softcap_case(pa, orc, tp, q, k, v, causal, poly)
+    softcap_case(pa, orc, tp, q, k, v, causal, fmt)
 
 
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("causal", [True, False])
-def test_softcap_grouped_query(pa, orc, tp, causal):
+def test_softcap_grouped_query(pa, orc, tp, causal, fmt):
     """Four query heads on two key/value heads, two batches, ragged S."""
     q, k, v = draw(2, 4, 2, 300, 41)
-    softcap_case(pa, orc, tp, q, k, v, causal, True, label="gqa")
+    softcap_case(pa, orc, tp, q, k, v, causal, fmt, label="gqa")
 
 
-def test_softcap_large_logits(pa, orc, tp):
+@pytest.mark.parametrize("fmt", FMTS)
+def test_softcap_large_logits(pa, orc, tp, fmt):
     """Scores beyond the softcap's clamp (|x| > Lc) and saturated tails."""
     q, k, v = draw(2, 1, 1, 256, 43, sd=40.0)
-    softcap_case(pa, orc, tp, q, k, v, True, True, label="large")
+    softcap_case(pa, orc, tp, q, k, v, True, fmt, label="large")
 
 
 def test_softcap_one_hot_v_readback(pa, orc, tp):
@@ -100,8 +121,8 @@ def test_softcap_one_hot_v_readback(pa, orc, tp):
     rng = np.random.default_rng(31)
     q, k = (si.to_bf16_bits(rng.standard_normal((1, 1, S, 128)) * 2) for _ in range(2))
     v = si.to_bf16_bits(np.eye(S, 128)[None, None])
-    for poly in (True, False):
-        softcap_case(pa, orc, tp, q, k, v, True, poly, label="one-hot")
+    for fmt in FMTS:
+        softcap_case(pa, orc, tp, q, k, v, True, fmt, label="one-hot")
 
 
 def test_softcap_full_size_sampled(pa, orc, tp):
@@ -111,18 +132,17 @@ def test_softcap_full_size_sampled(pa, orc, tp):
     note("softcap full size draw")
     qt, kt, vt = si.t_attn_inputs(B, H, S)
     rng = np.random.default_rng(32)
-    rows = np.unique(np.concatenate([[0, S - 1, 5 * S + 4095, H * S - 1],
-                                     rng.integers(0, B * H * S, 44)]))
+    rows = np.unique(np.concatenate([[0, 1, 2, S - 1, 5 * S + 4095, H * S - 1],
+                                     rng.integers(0, B * H * S, 42)]))
     q, k, v = to_bits(qt), to_bits(kt), to_bits(vt)
-    for poly in (True, False):
-        note(f"softcap full size poly={poly}")
-        entry = pa.poly_softcap_attn_fwd if poly else pa.native_softcap_attn_fwd
-        o, lse = entry(qt, kt, vt, 50.0, True, with_lse=True)
+    for fmt in FMTS:
+        note(f"softcap full size fmt={fmt}")
+        call, kind, kw = softcap_entry(pa, fmt)
+        o, lse = call(qt, kt, vt, 50.0, True)
         o, lse = to_bits(o).reshape(-1, 128), lse.cpu().numpy().ravel()
-        kind = orc.ATTN_SOFTCAP_POLY if poly else orc.ATTN_SOFTCAP_EXACT
-        ref, ref_lse, noise = orc.attn_fwd_rows(kind, q, k, v, rows, tanh_prog=tp)
-        check(o[rows], ref, noise, f"full poly={poly}")
-        check_lse(lse[rows], ref_lse, f"full poly={poly}")
+        ref, ref_lse, spread = orc.attn_fwd_rows(kind, q, k, v, rows, tanh_prog=tp, **kw)
+        check(o[rows], ref, spread, f"full fmt={fmt}")
+        check_lse(lse[rows], ref_lse, f"full fmt={fmt}")
 
 
 def sigmoid_case(pa, orc, sp, q, k, v, causal, poly, rows=None, label=""):
@@ -133,8 +153,8 @@ def sigmoid_case(pa, orc, sp, q, k, v, causal, poly, rows=None, label=""):
     if rows is None:
         rows = np.arange(B * H * S)
     kind = orc.ATTN_SIGMOID_POLY if poly else orc.ATTN_SIGMOID_EXACT
-    ref, _, noise = orc.attn_fwd_rows(kind, q, k, v, rows, causal=causal, sig=sp)
-    check(o[rows], ref, noise, f"sigmoid {label} S={S} causal={causal} poly={poly}")
+    ref, _, spread = orc.attn_fwd_rows(kind, q, k, v, rows, causal=causal, sig=sp)
+    check(o[rows], ref, spread, f"sigmoid {label} S={S} causal={causal} poly={poly}")
 
 
 def sample_rows(B, H, S, n, seed):
@@ -178,27 +198,20 @@ def test_sigmoid_full_size_sampled(pa, orc, sp):
         entry = pa.poly_sigmoid_attn_fwd if poly else pa.native_sigmoid_attn_fwd
         o = to_bits(entry(qt, kt, vt, True)).reshape(-1, 128)
         kind = orc.ATTN_SIGMOID_POLY if poly else orc.ATTN_SIGMOID_EXACT
-        ref, _, noise = orc.attn_fwd_rows(kind, q, k, v, rows, sig=sp)
-        check(o[rows], ref, noise, f"sigmoid full poly={poly}")
+        ref, _, spread = orc.attn_fwd_rows(kind, q, k, v, rows, sig=sp)
+        check(o[rows], ref, spread, f"sigmoid full poly={poly}")
 
 
-@pytest.mark.parametrize("core", ["d1", "pwl2", "d2", "d3"])
-@pytest.mark.parametrize("S,causal", [(200, True), (384, False)])
-def test_softcap_exp2_cores(pa, orc, tp, core, S, causal):
-    """The softmax's exponentials by a software exp2 core: the oracle forms
-    the same weights 2^floor(z) p(z - floor(z)) with the core in target
-    precision, so the comparison keeps the forward's tolerance."""
+@pytest.mark.parametrize("core", ["hw", "d1", "pwl2", "d2", "d3"])
+@pytest.mark.parametrize("S,causal,cap", [(200, True, 50.0), (384, False, 50.0), (300, True, 100.0)])
+def test_softcap_exp2_cores(pa, orc, tp, core, S, causal, cap):
+    """The softmax's exponentials by a software exp2 core, with the fixed
+    reference (cap 50) and the running integer reference (cap 100, where
+    cap log2 e > 80): the oracle forms the same weights 2^floor(z) p(z -
+    floor(z)) with the core in target precision."""
     cid = pa.EXP2_CORES[core]
-    q, k, v = draw(1, 4, 2, S, 81 + cid)
-    note(f"softcap exp2 core={core} S={S} causal={causal}")
-    o, lse = pa.poly_softcap_attn_fwd_exp2(to_dev(q, BF), to_dev(k, BF), to_dev(v, BF), 50.0,
-                                           causal, core=core, with_lse=True)
-    o, lse = to_bits(o).reshape(-1, 128), lse.cpu().numpy().ravel()
-    rows = np.arange(4 * S)
-    ref, ref_lse, noise = orc.attn_fwd_rows(orc.ATTN_SOFTCAP_POLY, q, k, v, rows, cap=50.0,
-                                            causal=causal, tanh_prog=tp, exp2_core=cid)
-    check(o, ref, noise, f"exp2 {core} S={S} causal={causal}")
-    check_lse(lse, ref_lse, f"exp2 {core} S={S} causal={causal}")
+    q, k, v = draw(1, 4, 2, S, 81 + cid, sd=3.0 if cap > 50 else 1.0)
+    softcap_case(pa, orc, tp, q, k, v, causal, "bf16", label="exp2", cap=cap, core=core)
 
 
 def test_softcap_exp2_cores_full_size_sampled(pa, orc, tp):
@@ -210,9 +223,9 @@ def test_softcap_exp2_cores_full_size_sampled(pa, orc, tp):
     for core in ("d1", "pwl2", "d2", "d3"):
         note(f"softcap exp2 full size core={core}")
         o = to_bits(pa.poly_softcap_attn_fwd_exp2(qt, kt, vt, 50.0, True, core=core)).reshape(-1, 128)
-        ref, _, noise = orc.attn_fwd_rows(orc.ATTN_SOFTCAP_POLY, q, k, v, rows, tanh_prog=tp,
-                                          exp2_core=pa.EXP2_CORES[core])
-        check(o[rows], ref, noise, f"exp2 full {core}")
+        ref, _, spread = orc.attn_fwd_rows(orc.ATTN_SOFTCAP_POLY, q, k, v, rows, tanh_prog=tp,
+                                           exp2_core=pa.EXP2_CORES[core])
+        check(o[rows], ref, spread, f"exp2 full {core}")
 
 
 @pytest.mark.parametrize("S", [1, 65, 129])
@@ -221,22 +234,16 @@ def test_edge_lengths_and_wide_groups(pa, orc, tp, sp, S):
     key/value head; causal and not."""
     q, k, v = draw(1, 8, 1, S, 90 + S)
     for causal in (True, False):
-        softcap_case(pa, orc, tp, q, k, v, causal, True, label="edge")
+        for fmt in FMTS:
+            softcap_case(pa, orc, tp, q, k, v, causal, fmt, label="edge")
         sigmoid_case(pa, orc, sp, q, k, v, causal, False, label="edge")
 
 
-@pytest.mark.parametrize("poly", [True, False])
-def test_softcap_large_cap_running_max(pa, orc, tp, poly):
+@pytest.mark.parametrize("fmt", FMTS)
+def test_softcap_large_cap_running_max(pa, orc, tp, fmt):
     """cap = 100 (cap log2 e > 80): the logits' range no longer fits a fixed
-    reference, so the kernel tracks the running row max (lazy rescale)."""
+    reference, so the kernel tracks an integer running reference (lazy
+    rescale by exact powers of two) and evaluates 2^z as 2^floor(z)
+    2^(z - floor(z))."""
     q, k, v = draw(1, 2, 1, 300, 97, sd=3.0)
-    B, H, S, D = q.shape
-    note(f"softcap fwd cap=100 poly={poly}")
-    entry = pa.poly_softcap_attn_fwd if poly else pa.native_softcap_attn_fwd
-    o, lse = entry(to_dev(q, BF), to_dev(k, BF), to_dev(v, BF), 100.0, True, with_lse=True)
-    o, lse = to_bits(o).reshape(-1, D), lse.cpu().numpy().ravel()
-    rows = np.arange(B * H * S)
-    kind = orc.ATTN_SOFTCAP_POLY if poly else orc.ATTN_SOFTCAP_EXACT
-    ref, ref_lse, noise = orc.attn_fwd_rows(kind, q, k, v, rows, cap=100.0, tanh_prog=tp)
-    check(o, ref, noise, f"cap=100 poly={poly}")
-    check_lse(lse, ref_lse, f"cap=100 poly={poly}")
+    softcap_case(pa, orc, tp, q, k, v, True, fmt, label="cap=100", cap=100.0)

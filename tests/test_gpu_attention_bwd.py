@@ -3,11 +3,13 @@
 The backward entry points take the forward's O and log-sum-exp; here those
 inputs come from the oracle's forward (O rounded to BF16, lse to FP32), and
 the oracle's backward receives exactly the same values, so the comparison
-isolates the backward.  dQ, dK and dV are checked against the oracle's FP64
-gradients with the tolerance derived in attn_util (P and dS are the BF16
-MFMA operands).  Softcap: the analytic derivative of the D4 tanh program
-(poly) or 1 - tanh^2 (comparator); sigmoid: the factored surrogate (poly, at
-the fitted length 4096) or sigma (1 - sigma).
+isolates the backward.  dQ, dK and dV are checked against the oracle's replay
+of the method's rounding steps (P and dS are the BF16 MFMA operands) with
+the gate of attn_util: one BF16 ulp plus the oracle's spread.  Softcap: the
+analytic derivative of the D4 tanh program in BF16 or FP16 (0 beyond the
+clamp), with the hardware exponential or a software exp2 core, or 1 - tanh^2
+(comparator); sigmoid: the factored surrogate (poly, at the fitted length
+4096) or sigma (1 - sigma).
 """
 import numpy as np
 import pytest
@@ -49,46 +51,69 @@ def draw(B, H, Hkv, S, seed, sd=1.0):
 
 def compare(orc, kind, q, k, v, o, do, lse, dq, dk, dv, qrows, krows, causal, label, **kw):
     D = q.shape[3]
-    rq, rk, rv, nq, nk, nv, cq, ck, sq, sk = orc.attn_bwd_rows(
+    rq, rk, rv, sq, sk, sv = orc.attn_bwd_rows(
         kind, q, k, v, None if o is None else bf16v(o), do,
         None if lse is None else lse.astype(np.float64), qrows, krows, causal=causal, **kw)
-    native = kind in (orc.ATTN_SOFTCAP_EXACT, orc.ATTN_SIGMOID_EXACT)
-    check(dq.reshape(-1, D)[qrows], rq, nq, f"{label} dQ", cancel=cq, dsens=sq if native else None)
-    check(dk.reshape(-1, D)[krows], rk, nk, f"{label} dK", cancel=ck, dsens=sk if native else None)
-    check(dv.reshape(-1, D)[krows], rv, nv, f"{label} dV")
+    check(dq.reshape(-1, D)[qrows], rq, sq, f"{label} dQ")
+    check(dk.reshape(-1, D)[krows], rk, sk, f"{label} dK")
+    check(dv.reshape(-1, D)[krows], rv, sv, f"{label} dV")
 
 
-def softcap_case(pa, orc, tp, B, H, Hkv, S, causal, poly, seed, qrows=None, krows=None, sd=1.0):
+FMTS = ("bf16", "f16", "native")
+
+
+def softcap_variant(pa, orc, fmt, core=None):
+    """(backward call, oracle kind, oracle keywords) of a softcap variant."""
+    if fmt == "native":
+        return (lambda *a: pa.native_softcap_attn_bwd(*a)), orc.ATTN_SOFTCAP_EXACT, {}
+    kw = dict(tanh_fmt=fmt)
+    if core is not None:
+        kw["exp2_core"] = pa.EXP2_CORES[core]
+    return ((lambda *a: pa.poly_softcap_attn_bwd(*a, fmt=fmt, core=core)), orc.ATTN_SOFTCAP_POLY, kw)
+
+
+def softcap_case(pa, orc, tp, B, H, Hkv, S, causal, fmt, seed, qrows=None, krows=None, sd=1.0,
+                 core=None, cap=50.0):
     q, k, v, do = draw(B, H, Hkv, S, seed, sd)
-    kind = orc.ATTN_SOFTCAP_POLY if poly else orc.ATTN_SOFTCAP_EXACT
-    o, lse = fwd_for_bwd(orc, kind, q, k, v, causal, tanh_prog=tp)
-    label = f"softcap bwd B={B} H={H} Hkv={Hkv} S={S} causal={causal} poly={poly}"
+    call, kind, kw = softcap_variant(pa, orc, fmt, core)
+    o, lse = fwd_for_bwd(orc, kind, q, k, v, causal, cap=cap, tanh_prog=tp, **kw)
+    label = f"softcap bwd B={B} H={H} Hkv={Hkv} S={S} causal={causal} fmt={fmt} core={core} cap={cap}"
     note(label)
-    entry = pa.poly_softcap_attn_bwd if poly else pa.native_softcap_attn_bwd
-    dq, dk, dv = entry(to_dev(q, BF), to_dev(k, BF), to_dev(v, BF), to_dev(o, BF), to_dev(do, BF),
-                       torch.from_numpy(lse).cuda(), 50.0, causal)
+    dq, dk, dv = call(to_dev(q, BF), to_dev(k, BF), to_dev(v, BF), to_dev(o, BF), to_dev(do, BF),
+                      torch.from_numpy(lse).cuda(), cap, causal)
     dq, dk, dv = to_bits(dq), to_bits(dk), to_bits(dv)
     qrows = np.arange(B * H * S) if qrows is None else qrows
     krows = np.arange(B * Hkv * S) if krows is None else krows
-    compare(orc, kind, q, k, v, o, do, lse, dq, dk, dv, qrows, krows, causal, label, cap=50.0,
-            tanh_prog=tp)
+    compare(orc, kind, q, k, v, o, do, lse, dq, dk, dv, qrows, krows, causal, label, cap=cap,
+            tanh_prog=tp, **kw)
 
 
-@pytest.mark.parametrize("poly", [True, False])
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("S", [64, 200, 384])
-def test_softcap_small(pa, orc, tp, S, causal, poly):
-    softcap_case(pa, orc, tp, 1, 2, 2, S, causal, poly, S * 3 + 1)
+def test_softcap_small(pa, orc, tp, S, causal, fmt):
+    softcap_case(pa, orc, tp, 1, 2, 2, S, causal, fmt, S * 3 + 1)
 
 
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("causal", [True, False])
-def test_softcap_grouped_query(pa, orc, tp, causal):
-    softcap_case(pa, orc, tp, 2, 4, 2, 300, causal, True, 61)
+def test_softcap_grouped_query(pa, orc, tp, causal, fmt):
+    softcap_case(pa, orc, tp, 2, 4, 2, 300, causal, fmt, 61)
 
 
-def test_softcap_large_logits(pa, orc, tp):
-    """Scores past the clamp: the differentiated program holds its value at Lc."""
-    softcap_case(pa, orc, tp, 1, 1, 1, 256, True, True, 62, sd=40.0)
+@pytest.mark.parametrize("fmt", FMTS)
+def test_softcap_large_logits(pa, orc, tp, fmt):
+    """Scores past the clamp: the differentiated program is 0 there (the
+    clamped forward program is constant)."""
+    softcap_case(pa, orc, tp, 1, 1, 1, 256, True, fmt, 62, sd=40.0)
+
+
+@pytest.mark.parametrize("core", ["d1", "pwl2", "d2", "d3"])
+@pytest.mark.parametrize("S,causal,cap", [(200, True, 50.0), (300, False, 100.0)])
+def test_softcap_exp2_cores(pa, orc, tp, core, S, causal, cap):
+    """P recomputed through the forward's software exp2 core (Appendix B.1)."""
+    softcap_case(pa, orc, tp, 1, 4, 2, S, causal, "bf16", 64 + S, core=core, cap=cap,
+                 sd=3.0 if cap > 50 else 1.0)
 
 
 def test_softcap_full_size_sampled(pa, orc, tp):
@@ -103,25 +128,24 @@ def test_softcap_full_size_sampled(pa, orc, tp):
     dot = si.t_attn_grad(B, H, S)
     q, k, v, do = to_bits(qt), to_bits(kt), to_bits(vt), to_bits(dot)
     rng = np.random.default_rng(63)
-    qrows = np.unique(np.concatenate([[h * S, h * S + S - 1, h * S + 5000] for h in heads]
-                                     + [heads[1] * S + rng.integers(0, S, 34)]))
-    krows = np.unique(np.concatenate([[h * S, h * S + S - 1, h * S + 77] for h in heads]
-                                     + [heads[0] * S + rng.integers(0, S, 34)]))
-    for poly in (True, False):
-        kind = orc.ATTN_SOFTCAP_POLY if poly else orc.ATTN_SOFTCAP_EXACT
+    qrows = np.unique(np.concatenate([[h * S, h * S + 1, h * S + S - 1, h * S + 5000] for h in heads]
+                                     + [heads[1] * S + rng.integers(0, S, 32)]))
+    krows = np.unique(np.concatenate([[h * S, h * S + S - 1, h * S + S - 2, h * S + 77] for h in heads]
+                                     + [heads[0] * S + rng.integers(0, S, 32)]))
+    for fmt in FMTS:
+        call, kind, kw = softcap_variant(pa, orc, fmt)
         o = np.zeros((B, H, S, 128), np.uint16)
         lse = np.full((B, H, S), 1e4, np.float32)
         for h in heads:
-            note(f"softcap bwd full size poly={poly}: oracle forward of head {h}")
+            note(f"softcap bwd full size fmt={fmt}: oracle forward of head {h}")
             sl = slice(h, h + 1)
             o[:, sl], lse[:, sl] = fwd_for_bwd(orc, kind, q[:, sl], k[:, sl], v[:, sl], True,
-                                               tanh_prog=tp)
-        note(f"softcap bwd full size poly={poly}: kernel")
-        entry = pa.poly_softcap_attn_bwd if poly else pa.native_softcap_attn_bwd
-        dq, dk, dv = entry(qt, kt, vt, to_dev(o, BF), dot, torch.from_numpy(lse).cuda(), 50.0, True)
+                                               tanh_prog=tp, **kw)
+        note(f"softcap bwd full size fmt={fmt}: kernel")
+        dq, dk, dv = call(qt, kt, vt, to_dev(o, BF), dot, torch.from_numpy(lse).cuda(), 50.0, True)
         dq, dk, dv = to_bits(dq), to_bits(dk), to_bits(dv)
         compare(orc, kind, q, k, v, o, do, lse, dq, dk, dv, qrows, krows, True,
-                f"softcap bwd full poly={poly}", cap=50.0, tanh_prog=tp)
+                f"softcap bwd full fmt={fmt}", cap=50.0, tanh_prog=tp, **kw)
 
 
 def sigmoid_case(pa, orc, sp, B, H, Hkv, S, causal, poly, seed, qrows=None, krows=None):
@@ -177,7 +201,8 @@ def test_edge_lengths_and_wide_groups(pa, orc, tp, sp, S):
     """Sequences shorter than, or one past, a tile; eight query heads on one
     key/value head (the summing pass over a group of eight)."""
     for causal in (True, False):
-        softcap_case(pa, orc, tp, 1, 8, 1, S, causal, True, 95 + S)
+        for fmt in FMTS:
+            softcap_case(pa, orc, tp, 1, 8, 1, S, causal, fmt, 95 + S)
         sigmoid_case(pa, orc, sp, 1, 8, 1, S, causal, False, 96 + S)
 
 
