@@ -224,43 +224,26 @@ __device__ __forceinline__ uint32_t softcap_poly_pair(float s0, float s1, float 
     return bc<uint32_t>(v) ^ (xw ^ aw);
 }
 
-// softcap program in BF16 on a pair: x = RN_bf16(s * scale), t^ = min(|x|,
-// Lc), v = c4; v = RN_bf16(fma(v, t^, c_j)) for j = 3, 2, 1; t = RN_bf16(v t^)
-// with x's sign.  Returns t0, t1 (BF16 values as FP32) and, through th0 / th1
-// and x0 / x1, the clamped |x| and x for the derivative program.
+// softcap program in BF16 on a pair: x = RN_bf16(s * scale), x^ = x clamped
+// to [-Lc, Lc] (one median of three; |x^| = min(|x|, Lc)), v = c4;
+// v = RN_bf16(fma(v, |x^|, c_j)) for j = 3, 2, 1 (the absolute value is a free
+// operand modifier); t = RN_bf16(v x^), which is RN_bf16(v |x^|) with x's sign
+// (nearest even is symmetric; v > 0).  Returns t0, t1 (BF16 values as FP32)
+// and x0, x1 (the rounded scaled scores, for the derivative program).
 __device__ __forceinline__ void softcap_bf16_pair(float s0, float s1, float scale, const TanhBF16 &k,
-                                                  float &t0, float &t1, float &x0, float &x1,
-                                                  float &th0, float &th1)
+                                                  float &t0, float &t1, float &x0, float &x1)
 {
     x0 = rn_bf16(s0 * scale);
     x1 = rn_bf16(s1 * scale);
-    th0 = fminf(fabsf(x0), k.lc);
-    th1 = fminf(fabsf(x1), k.lc);
-    float v0 = rn_bf16(fmaf(k.c[4], th0, k.c[3])), v1 = rn_bf16(fmaf(k.c[4], th1, k.c[3]));
-    v0 = rn_bf16(fmaf(v0, th0, k.c[2]));
-    v1 = rn_bf16(fmaf(v1, th1, k.c[2]));
-    v0 = rn_bf16(fmaf(v0, th0, k.c[1]));
-    v1 = rn_bf16(fmaf(v1, th1, k.c[1]));
-    // the sign before the last rounding (nearest even is symmetric)
-    t0 = rn_bf16(__builtin_copysignf(v0 * th0, x0));
-    t1 = rn_bf16(__builtin_copysignf(v1 * th1, x1));
-}
-
-// the same, returning the packed BF16 pair (t0 low, t1 high): the last
-// stage's two roundings become one packed convert
-__device__ __forceinline__ uint32_t softcap_bf16_word(float s0, float s1, float scale, const TanhBF16 &k,
-                                                      float &tmax)
-{
-    const float x0 = rn_bf16(s0 * scale), x1 = rn_bf16(s1 * scale);
-    const float th0 = fminf(fabsf(x0), k.lc), th1 = fminf(fabsf(x1), k.lc);
-    float v0 = rn_bf16(fmaf(k.c[4], th0, k.c[3])), v1 = rn_bf16(fmaf(k.c[4], th1, k.c[3]));
-    v0 = rn_bf16(fmaf(v0, th0, k.c[2]));
-    v1 = rn_bf16(fmaf(v1, th1, k.c[2]));
-    v0 = rn_bf16(fmaf(v0, th0, k.c[1]));
-    v1 = rn_bf16(fmaf(v1, th1, k.c[1]));
-    const float p0 = __builtin_copysignf(v0 * th0, x0), p1 = __builtin_copysignf(v1 * th1, x1);
-    tmax = fmaxf(tmax, fmaxf(p0, p1));   // within one rounding of the rounded max (enough for a reference)
-    return pack_bf(p0, p1);
+    const float c0 = __builtin_amdgcn_fmed3f(x0, -k.lc, k.lc);
+    const float c1 = __builtin_amdgcn_fmed3f(x1, -k.lc, k.lc);
+    float v0 = rn_bf16(fmaf(k.c[4], fabsf(c0), k.c[3])), v1 = rn_bf16(fmaf(k.c[4], fabsf(c1), k.c[3]));
+    v0 = rn_bf16(fmaf(v0, fabsf(c0), k.c[2]));
+    v1 = rn_bf16(fmaf(v1, fabsf(c1), k.c[2]));
+    v0 = rn_bf16(fmaf(v0, fabsf(c0), k.c[1]));
+    v1 = rn_bf16(fmaf(v1, fabsf(c1), k.c[1]));
+    t0 = rn_bf16(v0 * c0);
+    t1 = rn_bf16(v1 * c1);
 }
 
 // FP32 FMAs with FP16 operands taken from the halves of a packed word
@@ -499,7 +482,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // factor st.corr rescales O once this stage's PV product has landed.
     constexpr int NPC = SOFTCAP ? (SREF ? 16 : 17) : 8;
     struct TState {
-        uint32_t w[8];     // packed FP16 / BF16 t (softcap poly), then the BF16 P words
+        float tf[16];      // t of the BF16 softcap program
+        uint32_t w[8];     // packed FP16 t (FP16 softcap program), then the BF16 P words
         uint32_t mx;       // packed FP16 running max of t (FP16 softcap poly, online max)
         float tmax;        // running max of t (BF16 softcap poly, comparator; online max)
         float corr;
@@ -522,19 +506,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     if constexpr (!SREF) st.mx = bc<uint32_t>(__builtin_elementwise_max(bc<h2>(st.mx), bc<h2>(w)));
                     st.w[P] = w;
                 } else if constexpr (MODE == AM_SOFTCAP_POLY_BF16) {
-                    // packed BF16 t (masked keys: BF16 -inf); the row max for
-                    // the online reference from the unmasked values
-                    float tm = -INFINITY;
-                    uint32_t w = softcap_bf16_word(s[e], s[e + 1], a.scale, a.tanhbf, tm);
+                    // t as FP32 values (masked keys: -inf)
+                    float t0, t1, x0, x1;
+                    softcap_bf16_pair(s[e], s[e + 1], a.scale, a.tanhbf, t0, t1, x0, x1);
                     if constexpr (MASKED) {
                         const int k0 = ukey0 + (e >> 2) * 8 + h * 4 + (e & 3);
-                        const uint32_t mlo = k0 > lim ? 0x0000FFFFu : 0u;
-                        const uint32_t mhi = k0 + 1 > lim ? 0xFFFF0000u : 0u;
-                        w = sel(mlo | mhi, 0xFF80FF80u, w);
-                        if constexpr (!SREF) tm = fmaxf(lo_f(w), hi_f(w));
+                        t0 = k0 > lim ? -INFINITY : t0;
+                        t1 = k0 + 1 > lim ? -INFINITY : t1;
                     }
-                    if constexpr (!SREF) st.tmax = fmaxf(st.tmax, tm);
-                    st.w[P] = w;
+                    if constexpr (!SREF) st.tmax = fmaxf(st.tmax, fmaxf(t0, t1));
+                    st.tf[e] = t0;
+                    st.tf[e + 1] = t1;
                 } else {
 #pragma unroll
                     for (int i = 0; i < 2; ++i) {
@@ -573,8 +555,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     t0 = s[e];
                     t1 = s[e + 1];
                 } else if constexpr (MODE == AM_SOFTCAP_POLY_BF16) {
-                    t0 = lo_f(st.w[e2]);
-                    t1 = hi_f(st.w[e2]);
+                    t0 = st.tf[e];
+                    t1 = st.tf[e + 1];
                 }
                 float p0, p1;
                 if constexpr (MODE == AM_SOFTCAP_POLY) {

@@ -66,10 +66,10 @@ struct AttnBwdArgs {
     SigCoef sig;
 };
 
-// The D3 derivative program in BF16 at the clamped |x| (th), 0 where
-// |x| > Lc.
-__device__ __forceinline__ float dtanh_bf16(float x, float th, const TanhBF16 &d)
+// The D3 derivative program in BF16 at |x|, 0 where |x| > Lc.
+__device__ __forceinline__ float dtanh_bf16(float x, const TanhBF16 &d)
 {
+    const float th = fabsf(__builtin_amdgcn_fmed3f(x, -d.lc, d.lc));
     float v = rn_bf16(fmaf(d.c[3], th, d.c[2]));
     v = rn_bf16(fmaf(v, th, d.c[1]));
     v = rn_bf16(fmaf(v, th, d.c[0]));
@@ -112,9 +112,9 @@ __device__ __forceinline__ void bwd_pair(const AttnBwdArgs &a, float s0, float s
         ds1 = fma_mix_hi(dw, p1 * (dp1 - dl1), -0.0f);
         pw = pack_bf(p0, p1);
     } else if constexpr (MODE == AM_SOFTCAP_POLY_BF16) {
-        float t0, t1, x0, x1, th0, th1;
-        softcap_bf16_pair(s0, s1, a.scale, a.tanhbf, t0, t1, x0, x1, th0, th1);
-        const float d0 = dtanh_bf16(x0, th0, a.dtanhbf), d1 = dtanh_bf16(x1, th1, a.dtanhbf);
+        float t0, t1, x0, x1;
+        softcap_bf16_pair(s0, s1, a.scale, a.tanhbf, t0, t1, x0, x1);
+        const float d0 = dtanh_bf16(x0, a.dtanhbf), d1 = dtanh_bf16(x1, a.dtanhbf);
         float p0, p1;
         bwd_exp2<EXP>(fmaf(t0, a.c2, nl0), fmaf(t1, a.c2, nl1), p0, p1);
         ds0 = d0 * (p0 * (dp0 - dl0));
