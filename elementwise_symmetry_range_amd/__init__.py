@@ -84,6 +84,7 @@ def lib() -> C.CDLL:
             "poly_softcap_attn_bwd": [p] * 10 + [i32] * 5 + [f32, i32, p],
             "poly_softcap_attn_bwd_f16": [p] * 10 + [i32] * 5 + [f32, i32, p],
             "poly_softcap_attn_bwd_exp2": [p] * 10 + [i32] * 5 + [f32, i32, i32, p],
+            "poly_softcap_attn_bwd_static": [p] * 9 + [i32] * 5 + [f32, i32, p],
             "native_softcap_attn_bwd": [p] * 10 + [i32] * 5 + [f32, i32, p],
             "poly_sigmoid_attn_fwd": [p] * 4 + [i32] * 6 + [p],
             "native_sigmoid_attn_fwd": [p] * 4 + [i32] * 6 + [p],
@@ -101,6 +102,8 @@ def lib() -> C.CDLL:
         L.pa_status_str.restype = C.c_char_p
         L.pa_attn_bwd_workspace_bytes.argtypes = [i32] * 6
         L.pa_attn_bwd_workspace_bytes.restype = C.c_int64
+        L.pa_attn_bwd_static_scratch_bytes.argtypes = []
+        L.pa_attn_bwd_static_scratch_bytes.restype = C.c_int64
         L.pa_abi_version.argtypes = []
         L.pa_abi_version.restype = C.c_int32
         _lib = L
@@ -402,6 +405,26 @@ def poly_softcap_attn_bwd(q, k, v, o, dout, lse, cap: float = 50.0, causal: bool
                             dq, dk, dv, workspace, extra=(_core(core),))
     entry = lib().poly_softcap_attn_bwd if fmt == "bf16" else lib().poly_softcap_attn_bwd_f16
     return _softcap_bwd(entry, q, k, v, o, dout, lse, cap, causal, dq, dk, dv, workspace)
+
+
+def poly_softcap_attn_bwd_static(q, k, v, o, dout, lse, cap: float = 50.0, causal: bool = True,
+                                 dq=None, dk=None, dv=None):
+    """poly_softcap_attn_bwd with the library's own device scratch instead of
+    a workspace: the call allocates nothing (outputs the caller does not pass
+    are created here, before the call).  Calls on one GPU must not overlap."""
+    B, H, Hkv, S, D = _attn_shapes(q, k, v)
+    _bf16_4d(o, "o")
+    _bf16_4d(dout, "dout")
+    if o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("o and dout must have q's shape")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, S) or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [B, H, S]")
+    dq, dk, dv = _grads(q, k, dq, dk, dv)
+    _call(lib().poly_softcap_attn_bwd_static, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+          o.data_ptr(), dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+          dv.data_ptr(), B, H, Hkv, S, D, float(cap), int(bool(causal)), on=q,
+          tensors=(k, v, o, dout, lse, dq, dk, dv))
+    return dq, dk, dv
 
 
 def native_softcap_attn_bwd(q, k, v, o, dout, lse, cap: float = 50.0, causal: bool = True,

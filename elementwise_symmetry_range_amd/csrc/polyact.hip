@@ -5,6 +5,7 @@
 
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/polyact.h"
 #include "attn_host.hpp"
@@ -618,3 +619,62 @@ pa_status poly_sigmoid_attn_program(pa_sigmoid_attn_program *out)
 }
 
 }  // extern "C"
+
+// ---- allocation-free softcap backward -----------------------------------
+// The backward's scratch (Delta and -lse log2(e) per query row, and the FP32
+// dK / dV partials of grouped query heads) lives in one file-scope device
+// array instead of a caller workspace.  Each GPU the library runs on holds its
+// own copy until the process ends; its device address comes from
+// hipGetSymbolAddress once per device (the array's name is only a host-side
+// stand-in in host code) and is kept here.  Every call writes all the scratch
+// it reads before reading it, so nothing needs clearing between calls.
+namespace {
+constexpr int64_t kStaticScratchFloats = int64_t(2) << 20;   // 8 MiB
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float *g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+static __device__ __align__(256) float scratch[kStaticScratchFloats];
+
+// The device address of this device's scratch array, or nullptr.
+static float *static_scratch(pa_status &st)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        st = PA_ERR_LAUNCH;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+            st = PA_ERR_LAUNCH;
+            return nullptr;
+        }
+        g_scratch_ptr[dev] = (float *)p;
+    }
+    st = PA_OK;
+    return g_scratch_ptr[dev];
+}
+
+int64_t pa_attn_bwd_static_scratch_bytes(void) { return kStaticScratchFloats * 4; }
+
+pa_status poly_softcap_attn_bwd_static(const void *q, const void *k, const void *v, const void *o,
+                                       const void *dout, const float *lse, void *dq, void *dk,
+                                       void *dv, int32_t B, int32_t H, int32_t Hkv, int32_t S,
+                                       int32_t D, float cap, int32_t causal, hipStream_t stream)
+{
+    pa_status st = attn_shape(B, H, Hkv, S, D);
+    if (st != PA_OK) return st;
+    const int64_t need = attn_bwd_ws_floats(true, B, H, Hkv, S, D);
+    if (need > kStaticScratchFloats) return PA_ERR_SHAPE;
+    if ((int64_t)B * H == 0 || S == 0) {
+        return attn_bwd(AM_SOFTCAP_POLY_BF16, q, k, v, o, dout, lse, dq, dk, dv, nullptr, B, H, Hkv,
+                        S, D, cap, causal, stream);
+    }
+    float *ws = static_scratch(st);
+    if (!ws) return st;
+    return attn_bwd(AM_SOFTCAP_POLY_BF16, q, k, v, o, dout, lse, dq, dk, dv, ws, B, H, Hkv, S, D,
+                    cap, causal, stream);
+}

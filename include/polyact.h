@@ -262,6 +262,26 @@ pa_status poly_softcap_attn_bwd_exp2(const void *q, const void *k, const void *v
                                      int32_t S, int32_t D, float cap, int32_t causal, int32_t core,
                                      hipStream_t stream);
 
+/* poly_softcap_attn_bwd without a workspace argument, for callers that
+ * cannot allocate device memory (code under graph capture, serving loops,
+ * harnesses that forbid allocation).  The scratch lives in one device array
+ * of pa_attn_bwd_static_scratch_bytes() bytes (8 MiB) inside the library,
+ * held by each GPU the library runs on until the process ends; shapes whose
+ * workspace (pa_attn_bwd_workspace_bytes(1, ...)) exceeds it return
+ * PA_ERR_SHAPE (for example B H S <= 1,048,576 query rows when H == Hkv, and
+ * B H S <= 8,128 rows with grouped heads).  The call allocates nothing.  Every
+ * call on a GPU shares that GPU's array: calls that overlap in time on one
+ * GPU (other streams, other threads) race and must be serialised by the
+ * caller.  Results equal poly_softcap_attn_bwd's. */
+pa_status poly_softcap_attn_bwd_static(const void *q, const void *k, const void *v,
+                                       const void *o, const void *dout, const float *lse,
+                                       void *dq, void *dk, void *dv, int32_t B, int32_t H,
+                                       int32_t Hkv, int32_t S, int32_t D, float cap,
+                                       int32_t causal, hipStream_t stream);
+
+/* Size in bytes of poly_softcap_attn_bwd_static's device scratch array. */
+int64_t pa_attn_bwd_static_scratch_bytes(void);
+
 /* Sigmoid attention forward, O = P V with P = sigma(s - ln n) and
  * s = q.k / sqrt(D) (Eq. 14), n = S.  The program: x = RN_bf16(RN_f32(S_ij) *
  * RN_f32(1 / sqrt D)); region r = (x >= 1.25); x clamped to [-6, 6]; one

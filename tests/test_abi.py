@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(pa):
     names = declared_functions()
-    assert len(names) == 26, names
+    assert len(names) == 28, names
     L = pa.lib()
     for n in names:
         assert hasattr(L, n), n
