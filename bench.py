@@ -15,15 +15,20 @@ roofline = the dominant kernel of the step, algorithmic bytes per launch
           with no arithmetic (pa_stream_copy) and the dominant kernel's time
           relative to that copy;
 cpu_baseline = the CPU oracle replaying the same programs on a bounded
-          sample of the same arrays, on this host's cores.
+          sample of the same arrays, on this host's cores (and on one core),
+          median of 5 runs after one warm-up; also the oracle's SwiGLU and
+          softcap-attention rates on samples of those workloads.
 Also reported: each program's Gelem/s and share of HBM peak, the matched
 accurate-expf comparator and the speedup, timed as the pages time it
 (section 4.2: 1,000 warm-up calls per path, then nine rounds of 1,000 calls
 alternating which path goes first, ratio of the median per-round times;
 section 4.3 for the components: 25 warm-ups, five rounds of 100), the
 cache-resident 4,194,304-element endpoint (launches replayed from a HIP
-graph), the fused
-SwiGLU components, and softcap / sigmoid attention forward and backward.
+graph), the D3 sigmoid over config 1's inputs (U(-8, 8) plus every FP16 bit
+pattern), the fused SwiGLU components, softcap attention forward and backward
+(BF16 program, FP16 variant, software exp2 cores) and sigmoid attention
+forward and backward, and each program's Table-2 metric beside the printed
+bound.
 """
 from __future__ import annotations
 
@@ -121,8 +126,32 @@ def alternating(torch, poly, native, reps, rounds, warmup=0):
     return statistics.median(tp), statistics.median(tn)
 
 
-def cpu_baseline(x_t, g_t, budget_s=12.0):
-    """The oracle (OpenMP over this host's cores) on a bounded sample."""
+def _median_rate(fn, units, runs=5):
+    """One warm-up call, then `runs` timed calls: (median seconds, units per
+    second at the median)."""
+    fn()
+    ts = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        fn()
+        ts.append(time.perf_counter() - t0)
+    med = statistics.median(ts)
+    return med, units / med
+
+
+def _host_bits(t, np):
+    return t.contiguous().view(__import__("torch").int16).cpu().numpy().view(np.uint16)
+
+
+def cpu_baseline(x_t, g_t, swi=None, attn=None, n=1 << 22, n1=1 << 18, swi_rows=64,
+                 attn_rows=48, runs=5, swi_label="dense SwiGLU"):
+    """The oracle (OpenMP over this host's cores, and on one core) on bounded
+    samples of the same workloads, each the median of `runs` timed runs
+    after one warm-up: the six programs of the step over the first n (one
+    core: n1) elements of x / grad; the SwiGLU forward and backward over the
+    first swi_rows rows of the dense gate / up / dh (if given); the softcap
+    attention forward (BF16 program) over attn_rows query rows of q, k, v (if
+    given), in causal scores per second."""
     import numpy as np
 
     import oracle as orc
@@ -132,24 +161,69 @@ def cpu_baseline(x_t, g_t, budget_s=12.0):
     progs = {"sigmoid_fwd": byname["sigmoid_fwd_d3"], "tanh_fwd": byname["tanh_fwd_d4"],
              "silu_fwd": byname["silu_fwd_d3"], "gelu_fwd": byname["gelu_fwd_d5"],
              "sigmoid_bwd": byname["sigmoid_bwd_d4"], "tanh_bwd": byname["tanh_bwd_d4"]}
-    n = 1 << 21
-    xs = x_t[:n].contiguous().view(__import__("torch").int16).cpu().numpy().view(np.uint16)
-    gs = g_t[:n].contiguous().view(__import__("torch").int16).cpu().numpy().view(np.uint16)
-    done, t0 = 0, time.perf_counter()
-    while True:
+    n = min(n, x_t.numel())
+    n1 = min(n1, n)
+    xs, gs = _host_bits(x_t[:n], np), _host_bits(g_t[:n], np)
+
+    def elementwise(m):
         for f in FWD:
-            orc.act_fwd(progs[f"{f}_fwd"], xs, orc.ORDER_F16_FMA)
+            orc.act_fwd(progs[f"{f}_fwd"], xs[:m], orc.ORDER_F16_FMA)
         for f in BWD:
-            orc.act_bwd(progs[f"{f}_bwd"], xs, gs, orc.ORDER_F16_FMA)
-        done += 1
-        el = time.perf_counter() - t0
-        if el > budget_s or done >= 64:
-            break
-    elems = done * 6 * n
-    return {"value": round(elems / el / 1e9, 5), "unit": "Gelem/s", "cores": orc.threads(),
-            "kind": "oracle",
-            "sample": f"{done} passes of the six programs over the first {n} elements "
-                      f"of the same x / grad arrays ({elems} element evaluations, {el:.1f} s)"}
+            orc.act_bwd(progs[f"{f}_bwd"], xs[:m], gs[:m], orc.ORDER_F16_FMA)
+
+    cores = orc.threads()
+    t_all, rate = _median_rate(lambda: elementwise(n), 6 * n, runs)
+    prev = orc.set_threads(1)
+    try:
+        t_one, rate1 = _median_rate(lambda: elementwise(n1), 6 * n1, runs)
+    finally:
+        orc.set_threads(prev)
+    out = {"value": round(rate / 1e9, 5), "unit": "Gelem/s", "cores": cores, "kind": "oracle",
+           "sample": f"the six programs over the first {n} elements of the same x / grad arrays "
+                     f"({6 * n} element evaluations per run, median {t_all:.2f} s)",
+           "value_1core": round(rate1 / 1e9, 6),
+           "sample_1core": f"the same over the first {n1} elements on one thread "
+                           f"(median {t_one:.2f} s)",
+           "timing": f"median of {runs} runs after 1 warm-up (time.perf_counter)"}
+    if swi is not None:
+        g, u, d = swi
+        rows = min(swi_rows, g.shape[0])
+        gb, ub, db = (_host_bits(t[:rows], np) for t in (g, u, d))
+        sig = byname["sigmoid_fwd_d3"]
+        el = gb.size
+        tf, rf = _median_rate(lambda: orc.swiglu_fwd(sig, gb, ub), el, runs)
+        tb, rb = _median_rate(lambda: orc.swiglu_bwd(sig, gb, ub, db), el, runs)
+        out["swiglu"] = {"fwd_gelem_s": round(rf / 1e9, 5), "bwd_gelem_s": round(rb / 1e9, 5),
+                         "sample": f"the first {rows} rows of the {swi_label} gate / up / dh "
+                                   f"({el} elements; median {tf:.3f} s fwd, {tb:.3f} s bwd)"}
+    if attn is not None:
+        q, k, v = attn
+        B, H, S, D = q.shape
+        qb, kb, vb = (_host_bits(t, np).reshape(t.shape) for t in (q, k, v))
+        rows = np.unique(np.linspace(0, B * H * S - 1, attn_rows).astype(np.int64))
+        scores = int(np.sum(rows % S + 1))
+        tp = byname["tanh_fwd_d4"]
+        ta, ra = _median_rate(lambda: orc.attn_fwd_rows(orc.ATTN_SOFTCAP_POLY, qb, kb, vb, rows,
+                                                        tanh_prog=tp), scores, runs)
+        out["softcap_attention"] = {
+            "fwd_scores_s": round(ra, 1), "unit": "causal scores/s",
+            "sample": f"{rows.size} query rows evenly spaced over the {B} x {H} x {S} x {D} "
+                      f"causal softcap attention ({scores} scores; the oracle's BF16 replay "
+                      f"with its spread; median {ta:.3f} s)"}
+    return out
+
+
+def program_table():
+    """Each deployed program's Table-2 metric (the oracle's, written by
+    tests/golden/make_programs.py) beside the bound the pages print."""
+    gold = json.load(open(os.path.join(ROOT, "tests", "golden", "programs.json")))["programs"]
+    out = {}
+    for g in gold:
+        b = g.get("table2_bound")
+        out[g["name"]] = {"Li": g["Li"], "Lc": g["Lc"], "table2_metric": round(g["table2_metric"], 6),
+                          "printed_bound": b, "meets_printed_bound": None if b is None else
+                          bool(g["table2_metric"] <= b)}
+    return out
 
 
 def components(torch, pa, si, protocol="pages", which="all"):
@@ -226,28 +300,49 @@ def components_main(torch, pa, si, alt, res):
     fn = lambda: pa.native_softcap_attn_fwd(q, k, v, 50.0, True, out=o)  # noqa: E731
     fp(), fn()
     tp, tn = alt(fp, fn)
-    res["softcap_attn_fwd"] = attn_row(tp, tn, flops, {"causal_scores": scores})
-    # the softmax's exponentials by software exp2 cores (same kernel, same
-    # tanh program) against v_exp_f32
+    res["softcap_attn_fwd"] = attn_row(tp, tn, flops, {"causal_scores": scores, "program": "BF16"})
+    f16 = lambda: pa.poly_softcap_attn_fwd(q, k, v, 50.0, True, out=o, fmt="f16")  # noqa: E731
+    f16()
+    tp16, tn16 = alt(f16, fn)
+    res["softcap_attn_fwd_f16"] = attn_row(tp16, tn16, flops, {"causal_scores": scores,
+                                                               "program": "FP16 (packed)"})
+    op, lp = pa.poly_softcap_attn_fwd(q, k, v, 50.0, True, with_lse=True)
+    o16, l16 = pa.poly_softcap_attn_fwd(q, k, v, 50.0, True, with_lse=True, fmt="f16")
+    on, ln = pa.native_softcap_attn_fwd(q, k, v, 50.0, True, with_lse=True)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = pa.attn_bwd_workspace(True, 1, 16, 16, 8192, 128, device=q.device)
+    bp = lambda: pa.poly_softcap_attn_bwd(q, k, v, op, dout, lp, 50.0, True, dq=dq, dk=dk, dv=dv,  # noqa: E731
+                                          workspace=ws)
+    bn = lambda: pa.native_softcap_attn_bwd(q, k, v, on, dout, ln, 50.0, True, dq=dq, dk=dk,  # noqa: E731
+                                            dv=dv, workspace=ws)
+    bp(), bn()
+    tp, tn = alt(bp, bn)
+    res["softcap_attn_bwd"] = attn_row(tp, tn, 2.5 * flops, {"causal_scores": scores, "program": "BF16"})
+    b16 = lambda: pa.poly_softcap_attn_bwd(q, k, v, o16, dout, l16, 50.0, True, dq=dq, dk=dk,  # noqa: E731
+                                           dv=dv, workspace=ws, fmt="f16")
+    b16()
+    tp16, tn16 = alt(b16, bn)
+    res["softcap_attn_bwd_f16"] = attn_row(tp16, tn16, 2.5 * flops, {"causal_scores": scores,
+                                                                     "program": "FP16 (packed)"})
+    # the softmax's exponentials by software exp2 cores (BF16 program),
+    # forward and backward, each against the same kernel with v_exp_f32
     cores = {}
     for core in ("d1", "pwl2", "d2", "d3"):
         fc = lambda core=core: pa.poly_softcap_attn_fwd_exp2(q, k, v, 50.0, True, core=core, out=o)  # noqa: E731
         fc()
         tc, th = alt(fc, fp)
-        cores[core] = {"ms": round(tc, 4), "hw_exp2_ms": round(th, 4), "speedup_vs_hw": round(th / tc, 3)}
-    res["softcap_attn_fwd_exp2_cores"] = cores
-    op, lp = pa.poly_softcap_attn_fwd(q, k, v, 50.0, True, with_lse=True)
-    on, ln = pa.native_softcap_attn_fwd(q, k, v, 50.0, True, with_lse=True)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = pa.attn_bwd_workspace(True, 1, 16, 16, 8192, 128, device=q.device)
-    fp = lambda: pa.poly_softcap_attn_bwd(q, k, v, op, dout, lp, 50.0, True, dq=dq, dk=dk, dv=dv,  # noqa: E731
-                                          workspace=ws)
-    fn = lambda: pa.native_softcap_attn_bwd(q, k, v, on, dout, ln, 50.0, True, dq=dq, dk=dk,  # noqa: E731
-                                            dv=dv, workspace=ws)
-    fp(), fn()
-    tp, tn = alt(fp, fn)
-    res["softcap_attn_bwd"] = attn_row(tp, tn, 2.5 * flops, {"causal_scores": scores})
-    del q, k, v, dout, o, op, on, lp, ln, dq, dk, dv, ws
+        oc, lc = pa.poly_softcap_attn_fwd_exp2(q, k, v, 50.0, True, core=core, with_lse=True)
+        bc = lambda core=core, oc=oc, lc=lc: pa.poly_softcap_attn_bwd(  # noqa: E731
+            q, k, v, oc, dout, lc, 50.0, True, dq=dq, dk=dk, dv=dv, workspace=ws, core=core)
+        bc()
+        tcb, thb = alt(bc, bp)
+        cores[core] = {"fwd_ms": round(tc, 4), "hw_exp2_fwd_ms": round(th, 4),
+                       "fwd_speedup_vs_hw": round(th / tc, 3), "bwd_ms": round(tcb, 4),
+                       "hw_exp2_bwd_ms": round(thb, 4), "bwd_speedup_vs_hw": round(thb / tcb, 3),
+                       "fwd_bwd_speedup_vs_hw": round((th + thb) / (tc + tcb), 3)}
+        del oc, lc
+    res["softcap_attn_exp2_cores"] = cores
+    del q, k, v, dout, o, op, on, lp, ln, o16, l16, dq, dk, dv, ws
 
     # sigmoid attention at the program's fitted length: B = 1, 32 query heads
     # on 8 key/value heads, S = 4096, D = 128, causal
@@ -507,8 +602,33 @@ def main():
                 "bf16_gemm_8192_tflops": round(gemm_tf, 1),
                 "bf16_gemm_8192_pct_peak": round(100 * gemm_tf / BF16_DENSE_TFLOPS, 1)}
 
+    # config 1: the D3 sigmoid over 4,194,304 x U(-8, 8) FP16 followed by all
+    # 65,536 FP16 bit patterns (every special value), graph-replayed like the
+    # cache-resident endpoint
+    import numpy as np
+    x1 = torch.from_numpy(si.cfg1_x().view(np.int16)).to("cuda").view(torch.float16)
+    y1 = torch.empty_like(x1)
+    n1 = x1.numel()
+    (gp, n), (gn, _) = graphed(lambda: pa.poly_act_fwd(x1, "sigmoid", out=y1)), \
+        graphed(lambda: pa.native_act_fwd(x1, "sigmoid", out=y1))
+    tp, tn = alternating(torch, gp, gn, max(1, ic // n), ir, max(1, iw // n))
+    tp, tn = tp / n, tn / n
+    cfg1 = {"workload": "sigmoid D3 (Lc = 5.28125) over 4,194,304 x U(-8, 8) FP16 + all 65,536 "
+                        "FP16 bit patterns", "elements": n1,
+            "poly_gelem_s": round(n1 / tp / 1e6, 1), "native_gelem_s": round(n1 / tn / 1e6, 1),
+            "speedup_vs_accurate": round(tn / tp, 3), "poly_us": round(1e3 * tp, 2),
+            "native_us": round(1e3 * tn, 2),
+            "pct_hbm": round(100 * 4 * n1 / tp / 1e6 / HBM_PEAK_GBS, 1)}
+    del x1, y1, gp, gn
+
     comp = None if args.no_components else components(torch, pa, si, args.protocol)
-    cpu = None if args.no_cpu else cpu_baseline(x, g)
+    cpu = None
+    if not args.no_cpu:
+        swi = si.t_swiglu_inputs(64, 14336)
+        att = si.t_attn_inputs(1, 16, 8192, 128)
+        cpu = cpu_baseline(x, g, swi=swi, attn=att,
+                           swi_label="dense 8192 x 14336 workload (the same seeded streams)")
+        del swi, att
 
     line = {
         "metric": "Gelem/s and % of HBM roofline per poly activation vs accurate-expf kernel",
@@ -529,6 +649,8 @@ def main():
         "per_kernel_ms": {k: round(v, 5) for k, v in per.items()},
         "detail_hbm": detail,
         "detail_l2_resident_4M": l2,
+        "detail_cfg1": cfg1,
+        "programs": program_table(),
         "measured_ceilings": ceilings,
         "components": comp,
     }

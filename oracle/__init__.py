@@ -121,6 +121,7 @@ def lib():
             "orc_exp2_core_target": (C.c_float, [C.c_int, C.c_float]),
             "orc_sig_prog_eval": (u16, [P(SigProg), u16, C.c_int, P(u16)]),
             "orc_threads": (C.c_int, []),
+            "orc_set_threads": (C.c_int, [C.c_int]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -341,3 +342,8 @@ def sig_prog_eval(sp: SigProg, x_bits, order: int = ORDER_F32FMA_BF16):
 
 def threads() -> int:
     return lib().orc_threads()
+
+
+def set_threads(n: int) -> int:
+    """Threads of the oracle's later parallel loops; returns the previous count."""
+    return lib().orc_set_threads(int(n))

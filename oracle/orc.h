@@ -165,6 +165,7 @@ uint16_t orc_dtanh_prog(const orc_prog *tanh_prog, uint16_t x, int order);
 uint16_t orc_dtanh_prog_f16(const orc_prog *tanh_prog, uint16_t x);
 uint16_t orc_sig_prog_eval(const orc_sig_prog *sp, uint16_t x, int order, uint16_t *grad);
 int orc_threads(void);
+int orc_set_threads(int n);   /* threads of later parallel loops; returns the old count */
 
 #ifdef __cplusplus
 }

@@ -36,6 +36,18 @@ int orc_threads(void)
 #endif
 }
 
+/* Threads of the following parallel loops (n >= 1); the previous count. */
+int orc_set_threads(int n)
+{
+    const int old = orc_threads();
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+    return old;
+}
+
 /* ---- target-format arithmetic for one rounding order ------------------- */
 typedef struct {
     int order;

@@ -41,11 +41,33 @@ def test_traffic_profile_matches_kernels():
 
 
 def test_cpu_baseline_fields():
+    """The CPU leg's fields: all-core and one-core rates of the six programs
+    (median of 5 after 1 warm-up), the oracle's SwiGLU and softcap-attention
+    rates, each with its sample; small sizes here."""
     import bench
+    import synth_inputs as si
     rng = np.random.default_rng(5)
     x = torch.from_numpy(rng.integers(0, 65536, 1 << 16).astype(np.uint16).view(np.int16)).view(torch.float16)
     g = torch.from_numpy(rng.integers(0, 65536, 1 << 16).astype(np.uint16).view(np.int16)).view(torch.float16)
-    cb = bench.cpu_baseline(x, g, budget_s=0.05)
-    assert set(cb) == {"value", "unit", "cores", "kind", "sample"}
+    bits = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)  # noqa: E731
+    swi = tuple(bits(a) for a in si.swiglu_inputs(8, 256))
+    q, k, v = (bits(a) for a in si.attn_inputs(1, 2, 64, 128))
+    cb = bench.cpu_baseline(x, g, swi=swi, attn=(q, k, v), n=1 << 14, n1=1 << 12, attn_rows=8,
+                            runs=5)
+    assert {"value", "unit", "cores", "kind", "sample", "value_1core", "sample_1core",
+            "timing", "swiglu", "softcap_attention"} <= set(cb)
     assert cb["value"] > 0 and cb["unit"] == "Gelem/s" and cb["kind"] == "oracle"
-    assert cb["cores"] >= 1
+    assert cb["cores"] >= 1 and cb["value_1core"] > 0
+    assert "median of 5" in cb["timing"]
+    assert cb["swiglu"]["fwd_gelem_s"] > 0 and cb["swiglu"]["bwd_gelem_s"] > 0
+    assert cb["softcap_attention"]["fwd_scores_s"] > 0
+    import oracle
+    assert oracle.threads() == cb["cores"]          # the one-core leg restores the thread count
+
+
+def test_program_table_carries_printed_bounds():
+    import bench
+    t = bench.program_table()
+    assert t["sigmoid_bwd_d4"]["meets_printed_bound"] is True       # reproduced exactly
+    assert t["gelu_fwd_d5"]["meets_printed_bound"] is False         # unreachable (tested)
+    assert t["tanh_bwd_d4"]["printed_bound"] is None

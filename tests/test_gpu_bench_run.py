@@ -24,6 +24,9 @@ def test_bench_quick_run_prints_its_line():
     assert line["roofline"]["frac"] > 0
     comp = line["components"]
     for key in ("swiglu_dense_fwd", "swiglu_dense_bwd", "swiglu_routed_fwd", "swiglu_routed_bwd",
-                "softcap_attn_fwd", "softcap_attn_fwd_exp2_cores", "softcap_attn_bwd",
-                "sigmoid_attn_fwd", "sigmoid_attn_bwd"):
+                "softcap_attn_fwd", "softcap_attn_fwd_f16", "softcap_attn_exp2_cores",
+                "softcap_attn_bwd", "softcap_attn_bwd_f16", "sigmoid_attn_fwd", "sigmoid_attn_bwd"):
         assert key in comp, key
+    assert set(comp["softcap_attn_exp2_cores"]) == {"d1", "pwl2", "d2", "d3"}
+    assert line["detail_cfg1"]["elements"] == 4_194_304 + 65_536
+    assert line["programs"]["sigmoid_fwd_d3"]["Lc"] == 5.28125
