@@ -65,10 +65,26 @@ def per_dispatch(path):
 
 # attention kernels: template arguments -> (what, causal scores per launch,
 # MFMA products per score of 2 D flop)
-ATTN_MODES = {"0": "softcap poly", "1": "softcap comparator", "2": "sigmoid poly",
-              "3": "sigmoid comparator"}
+ATTN_MODES = {"0": "softcap poly FP16", "1": "softcap comparator", "2": "sigmoid poly",
+              "3": "sigmoid comparator", "4": "softcap poly BF16"}
 EXP_CORES = {"1": "D1", "2": "PWL2 FP16", "3": "D2", "4": "D3"}
 SCORES = {"softcap": 16 * 8192 * 8193 // 2, "sigmoid": 32 * 4096 * 4097 // 2}
+
+
+def attn_parts(name):
+    """(kind, mode, exp2 core or None) of an attention kernel's template
+    instance: k_attn_fwd<MODE, EXP, SREF>, k_attn_bwd_dq<MODE, EXP>,
+    k_attn_bwd_dkdv<MODE, SPLIT, EXP>, k_attn_bwd_reduce."""
+    import re
+    m = re.search(r"k_attn_(fwd|bwd_dq|bwd_dkdv|bwd_reduce)(?:<([^>]*)>)?", name)
+    if not m:
+        return None
+    kind = m.group(1)
+    args = [a.strip() for a in (m.group(2) or "").split(",") if a.strip()]
+    mode = args[0] if args else None
+    core = {"fwd": 1, "bwd_dq": 1, "bwd_dkdv": 2}.get(kind)
+    exp = args[core] if core is not None and len(args) > core else None
+    return kind, mode, exp if exp in EXP_CORES else None
 
 
 def components(path, command, out):
@@ -85,14 +101,14 @@ def components(path, command, out):
         name = r["Name"]
         avg = float(r["AverageNs"])
         what, tfl = "", ""
-        m = re.search(r"k_attn_(fwd|bwd_dq|bwd_dkdv|bwd_reduce)<?(\d)?(?:, ?(\w+))?>?", name)
-        if m:
-            kind, mode, extra = m.group(1), m.group(2), m.group(3)
+        parts = attn_parts(name)
+        if parts:
+            kind, mode, exp = parts
             what = ATTN_MODES.get(mode, "") if mode else "sum of dK/dV partials"
-            if kind == "fwd" and extra in EXP_CORES:
-                what += f", exp2 core {EXP_CORES[extra]}"
+            if exp:
+                what += f", exp2 core {EXP_CORES[exp]}"
             if kind != "bwd_reduce" and mode:
-                sc = SCORES["softcap" if mode in "01" else "sigmoid"]
+                sc = SCORES["softcap" if mode in "014" else "sigmoid"]
                 prods = {"fwd": 2, "bwd_dq": 3, "bwd_dkdv": 4}[kind]
                 t = prods * 2 * 128 * sc / (avg * 1e-9) / 1e12
                 tfl = f"{t:.0f} | {100 * t / 2500:.1f}"
@@ -163,14 +179,13 @@ SIMDS = 256 * 4
 
 
 def attn_label(name):
-    import re
-    m = re.search(r"k_attn_(fwd|bwd_dq|bwd_dkdv)<(\d)(?:, ?(\w+))?", name)
-    if not m:
+    parts = attn_parts(name)
+    if not parts or parts[0] == "bwd_reduce":
         return None
-    kind, mode, extra = m.group(1), m.group(2), m.group(3)
+    kind, mode, exp = parts
     what = ATTN_MODES.get(mode, "")
-    if kind == "fwd" and extra in EXP_CORES:
-        what += f", exp2 core {EXP_CORES[extra]}"
+    if exp:
+        what += f", exp2 core {EXP_CORES[exp]}"
     return f"{kind} {what}"
 
 
