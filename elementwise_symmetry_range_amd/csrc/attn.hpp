@@ -632,13 +632,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // pieces; a scheduling fence closes each slot, so every LDS read runs one
     // slot ahead of its MFMA (the compiler otherwise waits for each operand
     // right before its MFMA) and the VALU work is spread evenly between the
-    // matrix instructions.  Softcap with the hardware exponential: 16 slots
-    // (one MFMA and one piece each); sigmoid and the software exp2 cores: 8
-    // slots of two MFMAs, whose two pieces (or pair) the scheduler can
-    // interleave, filling the hazard stalls between dependent packed steps
-    // (the exp2 cores 1.035-1.05x faster than with 16 slots; the hardware-exp
-    // softcap 1-2 % slower).  Outputs are bit-identical either way.
-    constexpr int AT_SLOTS = (SOFTCAP && EXP == 0) ? 16 : 8, AT_AHEAD = 1;
+    // matrix instructions.  FP16 softcap and comparator with the hardware
+    // exponential: 16 slots (one MFMA and one piece each); sigmoid, the BF16
+    // softcap and the software exp2 cores: 8 slots of two MFMAs, whose two
+    // pieces (or pair) the scheduler can interleave, filling the stalls
+    // between dependent steps of one chain (the exp2 cores 1.035-1.05x and
+    // the BF16 softcap 1.03-1.04x faster than with 16 slots, 4 slots no
+    // better; the FP16 softcap 1-2 % slower).  Outputs are bit-identical
+    // either way.
+    constexpr int AT_SLOTS = (SOFTCAP && EXP == 0 && MODE != AM_SOFTCAP_POLY_BF16) ? 16 : 8, AT_AHEAD = 1;
     auto slotted = [&](f32x16 &sn, f32x16 &scur, bf16x8 (&pc)[2], const bf16x8 (&pp)[2],
                        const uint16_t *Kb, const uint16_t *Vb, int ukey0, auto halfc) __attribute__((always_inline)) {
         constexpr int HALF = decltype(halfc)::value;
