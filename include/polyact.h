@@ -309,20 +309,33 @@ pa_status poly_sigmoid_attn_bwd(const void *q, const void *k, const void *v, con
 
 /* ---- matched comparators (same memory path, accurate FP32 math) -------- */
 
-/* y = f(x) with accurate FP32 math (sigmoid 1/(1+e^-|x|) in the overflow-safe
- * form, tanhf, SiLU (x >= 0 ? x : x e) / (1 + e) with e = expf(-|x|), GELU
- * x erfc(-x / sqrt 2) / 2), rounded once to dtype t. */
+/* The "native" paths every timing in the paper divides by (Table 1's caption
+ * calls native the unchanged implementation of the same function in the same
+ * task; section 4.2 and
+ * Eq. 13 time the isolated functions against it, Table 3).  They share the
+ * launch shape and memory path of the poly_ entry points, so a speedup
+ * measures the arithmetic alone.  Arguments, layout, ownership and errors as
+ * the poly_ counterpart named beside each.
+ *
+ * Counterpart of poly_act_fwd: y = f(x) with accurate FP32 math (sigmoid
+ * 1/(1+e^-|x|) in the overflow-safe form, tanhf, SiLU (x >= 0 ? x : x e) /
+ * (1 + e) with e = expf(-|x|), GELU x erfc(-x / sqrt 2) / 2), rounded once to
+ * dtype t. */
 pa_status native_act_fwd(int32_t f, int32_t t, const void *x, void *y, int64_t n,
                          hipStream_t stream);
 
-/* Backward comparators.  impl = PA_IMPL_NATIVE: x_or_y is x and the derivative
- * is recomputed accurately from x (all four functions; SiLU' = sigma (1 +
- * x sigma(-x)), GELU' = Phi + x phi); impl = PA_IMPL_NATIVE_FROM_Y: x_or_y is
- * the saved forward output y (Eqs. 10-11), PA_SIGMOID and PA_TANH only. */
+/* Counterpart of poly_act_bwd (section 4.2's backward timing, section 3.3).
+ * impl = PA_IMPL_NATIVE: x_or_y is x and the derivative is recomputed
+ * accurately from x (all four functions; SiLU' = sigma (1 + x sigma(-x)),
+ * GELU' = Phi + x phi); impl = PA_IMPL_NATIVE_FROM_Y: x_or_y is the saved
+ * forward output y (the derivatives in terms of y, Eqs. 10-11: section 4.2's
+ * native sigmoid and tanh backward), PA_SIGMOID and PA_TANH only.  PA_ERR_FUNC for another impl or function. */
 pa_status native_act_bwd(int32_t impl, int32_t f, int32_t t, const void *x_or_y,
                          const void *dy, void *dx, int64_t n, hipStream_t stream);
 
-/* SwiGLU with accurate FP32 SiLU (arguments as poly_swiglu_fwd / _bwd). */
+/* SwiGLU with accurate FP32 SiLU, the native side of the B1 dense-MLP and B4
+ * routed-expert components (section 4.3, Table 4, sections 5.2.1 and 5.2.4);
+ * arguments as poly_swiglu_fwd / _bwd. */
 pa_status native_swiglu_fwd(int32_t t, const void *gate, const void *up, void *h,
                             int64_t rows, int64_t cols, int64_t ld_gate, int64_t ld_up,
                             int64_t ld_h, const int64_t *row_offsets, int32_t n_groups,
@@ -333,11 +346,12 @@ pa_status native_swiglu_bwd(int32_t t, const void *gate, const void *up, const v
                             int64_t ld_dgate, int64_t ld_dup, const int64_t *row_offsets,
                             int32_t n_groups, hipStream_t stream);
 
-/* Attention comparators (arguments as the poly_ entry points): softcap with
- * accurate FP32 tanhf on the unrounded FP32 scaled score and, backward,
- * 1 - tanh^2 (Eq. 12); sigmoid with sigma(RN_f32(S) * RN_f32(1 / sqrt D) -
- * RN_f32(ln S)) from expf and an IEEE divide, sigma (1 - sigma) backward, for
- * any S. */
+/* Attention comparators, the native side of the B2 softcap and B3 sigmoid
+ * attention components (section 4.3, Table 4, sections 5.2.2 and 5.2.3);
+ * arguments as the poly_ entry points: softcap with accurate FP32 tanhf on
+ * the unrounded FP32 scaled score (Eq. 1) and, backward, 1 - tanh^2 (Eq. 12);
+ * sigmoid with sigma(RN_f32(S) * RN_f32(1 / sqrt D) - RN_f32(ln S)) from expf
+ * and an IEEE divide (Eq. 14), sigma (1 - sigma) backward, for any S. */
 pa_status native_softcap_attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
                                   int32_t B, int32_t H, int32_t Hkv, int32_t S, int32_t D,
                                   float cap, int32_t causal, hipStream_t stream);
@@ -361,24 +375,35 @@ pa_status native_sigmoid_attn_bwd(const void *q, const void *k, const void *v, c
  * stream, 6 bytes per element).  Same launch configuration, 16-byte vector
  * body and scalar head / tail as poly_act_fwd / poly_act_bwd, so its rate is
  * the HBM rate that launch shape reaches with nothing to compute: the
- * ceiling the programs' rates are read against.  Arguments and errors as
+ * ceiling the programs' rates are read against (no passage of the paper
+ * defines it; section 4.2 reads its two endpoints as the L2-resident and the
+ * HBM-streaming regime, and this is that regime's rate).  Arguments and errors as
  * poly_act_fwd (16-bit elements of any type; no dtype argument). */
 pa_status pa_stream_copy(const void *a, const void *b, void *y, int64_t n, hipStream_t stream);
 
 /* ---- host-only queries (no device work) -------------------------------- */
 
-/* The program the kernels execute for (f, deriv, t).  Returns PA_ERR_FUNC if
- * there is none, PA_ERR_NULL if out is NULL. */
+/* The program the kernels execute for (f, deriv, t): the fitted and
+ * BF16-rounded coefficients, Li and Lc of section 3.2 (Table 2 prints their
+ * maximum errors), deriv = 0 forward, 1 the direct derivative fit (section
+ * 3.3, Eq. 9), 2 the differentiated D4 tanh the softcap backward uses (Eq. 12)
+ * in the format t.  Returns PA_ERR_FUNC if there is none, PA_ERR_NULL if out
+ * is NULL. */
 pa_status poly_program_info(int32_t f, int32_t deriv, int32_t t, pa_program *out);
 
-/* The sigmoid-attention program (BF16 bit patterns): region threshold, clamp
- * bounds, coeff_bits[r][j] = coefficient of x^j in region r (r = 1 when
- * x >= thr), derivative factor a_bits[r] + b_bits[r] x, and the sequence
- * length n it holds for.  Returns PA_ERR_NULL if out is NULL. */
+/* The sigmoid-attention program printed in the paper's Appendix C (packed
+ * PTX listings) and described in section 3.4 (BF16 bit patterns): region
+ * threshold, clamp bounds, coeff_bits[r][j] = coefficient of x^j in region r
+ * (r = 1 when x >= thr), derivative factor a_bits[r] + b_bits[r] x, and the
+ * sequence length n it holds for.  Returns PA_ERR_NULL if out is NULL. */
 pa_status poly_sigmoid_attn_program(pa_sigmoid_attn_program *out);
 
 /* Bytes of caller-owned workspace an attention backward needs (softcap != 0
- * for the softcap backward, 0 for sigmoid); -1 for an invalid shape. */
+ * for the softcap backward, 0 for sigmoid); -1 for an invalid shape.  The
+ * paper defines the gradients (Eq. 12, section 3.3), not their storage: the
+ * workspace is this library's split of the backward into a dQ kernel and a
+ * dK/dV kernel (the row terms Delta and -lse log2 e, and FP32 dK / dV partials
+ * per query head when Hkv < H). */
 int64_t pa_attn_bwd_workspace_bytes(int32_t softcap, int32_t B, int32_t H, int32_t Hkv,
                                     int32_t S, int32_t D);
 
