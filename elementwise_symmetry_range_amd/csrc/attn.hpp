@@ -231,12 +231,13 @@ __device__ __forceinline__ uint32_t softcap_poly_pair(float s0, float s1, float 
 // (nearest even is symmetric; v > 0).  Returns t0, t1 (BF16 values as FP32)
 // and x0, x1 (the rounded scaled scores, for the derivative program).
 __device__ __forceinline__ void softcap_bf16_pair(float s0, float s1, float scale, const TanhBF16 &k,
-                                                  float &t0, float &t1, float &x0, float &x1)
+                                                  float &t0, float &t1, float &x0, float &x1,
+                                                  float &c0, float &c1)
 {
     x0 = rn_bf16(s0 * scale);
     x1 = rn_bf16(s1 * scale);
-    const float c0 = __builtin_amdgcn_fmed3f(x0, -k.lc, k.lc);
-    const float c1 = __builtin_amdgcn_fmed3f(x1, -k.lc, k.lc);
+    c0 = __builtin_amdgcn_fmed3f(x0, -k.lc, k.lc);
+    c1 = __builtin_amdgcn_fmed3f(x1, -k.lc, k.lc);
     float v0 = rn_bf16(fmaf(k.c[4], fabsf(c0), k.c[3])), v1 = rn_bf16(fmaf(k.c[4], fabsf(c1), k.c[3]));
     v0 = rn_bf16(fmaf(v0, fabsf(c0), k.c[2]));
     v1 = rn_bf16(fmaf(v1, fabsf(c1), k.c[2]));
@@ -244,6 +245,12 @@ __device__ __forceinline__ void softcap_bf16_pair(float s0, float s1, float scal
     v1 = rn_bf16(fmaf(v1, fabsf(c1), k.c[1]));
     t0 = rn_bf16(v0 * c0);
     t1 = rn_bf16(v1 * c1);
+}
+__device__ __forceinline__ void softcap_bf16_pair(float s0, float s1, float scale, const TanhBF16 &k,
+                                                  float &t0, float &t1, float &x0, float &x1)
+{
+    float c0, c1;
+    softcap_bf16_pair(s0, s1, scale, k, t0, t1, x0, x1, c0, c1);
 }
 
 // FP32 FMAs with FP16 operands taken from the halves of a packed word

@@ -28,14 +28,15 @@
 //                    through LDS: S^T = K Q^T and dP^T = V dO^T with Q and dO
 //                    held in registers, the transform, dQ^T += K^T dS^T with
 //                    K^T read transposed from the K tile.
-//   k_attn_bwd_dkdv  one workgroup per 128 keys of one key/value head (4
-//                    waves x 32 keys, lane = key); it loops over the query
-//                    heads of the group and the query tiles of 64 rows that
-//                    see its keys, with Q / dO tiles (and the rows'
-//                    -lse log2(e) and Delta) streamed through LDS: S = Q K^T and dP = dO V^T
-//                    with K and V held in registers, the transform,
-//                    dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T read
-//                    transposed from the tiles.
+//   k_attn_bwd_dkdv  one workgroup per 128 keys of one key/value head (8
+//                    waves: 4 groups of 32 keys, lane = key, times the two
+//                    32-row halves of each query tile); it loops over the
+//                    query heads of the group and the query tiles of 64 rows
+//                    that see its keys, with Q / dO tiles (and the rows'
+//                    -lse log2(e) and Delta) streamed through LDS: S = Q K^T
+//                    and dP = dO V^T with K and V held in LDS, the
+//                    transform, dV^T += dO^T P and dK^T += Q^T dS with dO^T
+//                    and Q^T read transposed from the tiles.
 // Both run after the forward has written O and the LSE; dkdv after dq (it
 // reads Delta).  Every MFMA is v_mfma_f32_32x32x16_bf16 with the operand
 // layouts described in attn.hpp; P and dS are rounded to BF16 for the MFMA.
@@ -66,13 +67,13 @@ struct AttnBwdArgs {
     SigCoef sig;
 };
 
-// The D3 derivative program in BF16 at |x|, 0 where |x| > Lc.
-__device__ __forceinline__ float dtanh_bf16(float x, const TanhBF16 &d)
+// The D3 derivative program in BF16 at |c|, c = x clamped to [-Lc, Lc] by
+// the forward program (the derivative shares its clamp), 0 where |x| > Lc.
+__device__ __forceinline__ float dtanh_bf16(float x, float c, const TanhBF16 &d)
 {
-    const float th = fabsf(__builtin_amdgcn_fmed3f(x, -d.lc, d.lc));
-    float v = rn_bf16(fmaf(d.c[3], th, d.c[2]));
-    v = rn_bf16(fmaf(v, th, d.c[1]));
-    v = rn_bf16(fmaf(v, th, d.c[0]));
+    float v = rn_bf16(fmaf(d.c[3], fabsf(c), d.c[2]));
+    v = rn_bf16(fmaf(v, fabsf(c), d.c[1]));
+    v = rn_bf16(fmaf(v, fabsf(c), d.c[0]));
     return fabsf(x) > d.lc ? 0.0f : v;
 }
 
@@ -112,9 +113,9 @@ __device__ __forceinline__ void bwd_pair(const AttnBwdArgs &a, float s0, float s
         ds1 = fma_mix_hi(dw, p1 * (dp1 - dl1), -0.0f);
         pw = pack_bf(p0, p1);
     } else if constexpr (MODE == AM_SOFTCAP_POLY_BF16) {
-        float t0, t1, x0, x1;
-        softcap_bf16_pair(s0, s1, a.scale, a.tanhbf, t0, t1, x0, x1);
-        const float d0 = dtanh_bf16(x0, a.dtanhbf), d1 = dtanh_bf16(x1, a.dtanhbf);
+        float t0, t1, x0, x1, c0, c1;
+        softcap_bf16_pair(s0, s1, a.scale, a.tanhbf, t0, t1, x0, x1, c0, c1);
+        const float d0 = dtanh_bf16(x0, c0, a.dtanhbf), d1 = dtanh_bf16(x1, c1, a.dtanhbf);
         float p0, p1;
         bwd_exp2<EXP>(fmaf(t0, a.c2, nl0), fmaf(t1, a.c2, nl1), p0, p1);
         ds0 = d0 * (p0 * (dp0 - dl0));
@@ -293,25 +294,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 constexpr int AT_BK = 128;   // keys per dK/dV workgroup
 constexpr int AT_BQ = 64;    // query rows per streamed tile
 
+// dK / dV kernel with two waves per SIMD: eight waves per workgroup of 128
+// keys; wave w owns keys 32 (w % 4) .. + 31 of the workgroup and the query
+// half w / 4 (rows 32 (w / 4) .. + 31) of every streamed 64-row Q / dO tile,
+// so a wave keeps only its dK, dV accumulators (128 registers) and one
+// 32 x 32 score block, and the two waves of a key group sum their partials
+// through LDS at the end (half 0 + half 1, a fixed order).  K and V of the
+// workgroup's keys sit in LDS for the whole kernel (B operands of S and dP).
+// Measured on MI355X against the earlier form (four waves, one per SIMD,
+// K and V in registers, all 64 rows per wave): softcap backward 1.046x
+// (BF16 program), 1.01x (FP16), 1.15x (comparator); sigmoid 1.03x, 1.05x.
+//
 // SPLIT (grouped query heads): one workgroup per (query head, key tile)
 // instead of per (key/value head, key tile), so a group's heads run in
 // parallel; each writes its FP32 dK, dV contribution to a.part and
 // k_attn_bwd_reduce sums the group.  Without the split the workgroups of a
 // causal launch differ G-fold more in work and there are G times fewer.
 template <int MODE, bool SPLIT, int EXP = 0>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_attn_bwd_dkdv(AttnBwdArgs a)
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_bwd_dkdv(AttnBwdArgs a)
 {
     constexpr bool SOFTCAP = am_softcap(MODE);
-    // double buffers (see dbuf): separate arrays except for the softcap
-    // comparator, whose tanh needs the registers (it spills with them)
-    constexpr bool SPLIT_LDS = MODE != AM_SOFTCAP_NATIVE;
-    __shared__ __attribute__((aligned(16))) uint16_t Qs0[AT_TILE], Qs1[AT_TILE], Qp[2][AT_TILE];
-    __shared__ __attribute__((aligned(16))) uint16_t Ds0[AT_TILE], Ds1[AT_TILE], Dp[2][AT_TILE];
-    __shared__ __attribute__((aligned(16))) float Ls0[AT_BQ], Ls1[AT_BQ], Lp[2][AT_BQ];   // -lse * log2(e)
-    __shared__ __attribute__((aligned(16))) float Es0[AT_BQ], Es1[AT_BQ], Ep[2][AT_BQ];   // Delta
+    constexpr int AH = 1;   // operand reads ahead, in slots (2 measured no faster)
+    __shared__ __attribute__((aligned(16))) uint16_t Kt[2 * AT_TILE], Vt[2 * AT_TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t Qs0[AT_TILE], Qs1[AT_TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t Ds0[AT_TILE], Ds1[AT_TILE];
+    __shared__ __attribute__((aligned(16))) float Ls0[AT_BQ], Ls1[AT_BQ];   // -lse * log2(e)
+    __shared__ __attribute__((aligned(16))) float Es0[AT_BQ], Es1[AT_BQ];   // Delta
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
+    const int kg = wave & 3, qh = wave >> 2;
     const int col = lane & 31, h = lane >> 5;
     const int g16 = lane >> 4, i16 = lane & 15;
     const int S = a.S, G = a.G;
@@ -322,238 +334,221 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int bk = SPLIT ? bx / G : bx;                      // key/value head
     const int kt = krank;                                    // causal: key tile 0 sees the most queries
     const int64_t kvbase = (int64_t)bk * S * AT_D;
-    const int k0 = kt * AT_BK + wave * 32;
+    const int k0 = kt * AT_BK + kg * 32;
     const int my_k = k0 + col;
     const bool valid = my_k < S;
 
-    // K and V as B operands of S = Q K^T and dP = dO V^T: lane holds row my_k
-    bf16x8 kf[8], vf[8];
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-        kf[ks] = valid ? ld_bf16x8(a.k + kvbase + (int64_t)my_k * AT_D + ks * 16 + h * 8) : bf16x8{};
-        vf[ks] = valid ? ld_bf16x8(a.v + kvbase + (int64_t)my_k * AT_D + ks * 16 + h * 8) : bf16x8{};
-    }
+    // the workgroup's 128 K and V rows (rows past S repeat row S - 1)
+    load_rows64(a.k + kvbase, Kt, kt * AT_BK, S, wave, lane);
+    load_rows64(a.v + kvbase, Vt, kt * AT_BK, S, wave, lane);
+
     f32x16 dk[4], dv[4];
 #pragma unroll
     for (int db = 0; db < 4; ++db) dk[db] = dv[db] = f32x16{};
 
-    // query tiles: every head of the group, rows from the first one that can
-    // see this workgroup's keys
     const int qstart = a.causal ? kt * AT_BK : 0;
     const int nqt = (S - qstart + AT_BQ - 1) / AT_BQ;
     const int ntile = SPLIT ? nqt : G * nqt;
 
+    // byte offsets of the lane's reads in the swizzled tiles: row chunk
+    // h of row 32 qh + col (Q, dO) and 32 kg + col (K, V), and the
+    // transposed read of rows 32 qh + 4 (g16 / 2) + i16 / 4, chunk
+    // 2 (g16 % 2) + (i16 / 2) % 2, half 8 (i16 % 2) bytes
+    const uint32_t fr = (uint32_t)swz(col, 0);
+    const uint32_t bq0 = (uint32_t)(qh * 32 + col) * 256u + (((uint32_t)h ^ fr) << 4);
+    const uint32_t bkv0 = (uint32_t)(kg * 32 + col) * 256u + (((uint32_t)h ^ fr) << 4);
+    const int tr_r = (g16 >> 1) * 4 + (i16 >> 2), tr_c = (g16 & 1) * 2 + ((i16 >> 1) & 1);
+    const uint32_t btr0 = (uint32_t)(qh * 32 + tr_r) * 256u + ((uint32_t)swz(tr_r, tr_c) << 4) +
+                          (uint32_t)(i16 & 1) * 8u;
     auto head_of = [&](int t) { return SPLIT ? (int64_t)bx : (int64_t)bk * G + t / nqt; };
+    // waves 0-3 load the Q tile, waves 4-7 the dO tile; waves 0 and 4 the
+    // rows' -lse log2(e) and Delta
     auto load = [&](int t, auto bufc) __attribute__((always_inline)) {
         constexpr int buf = decltype(bufc)::value;
         const int64_t bh = head_of(t);
         const int r0 = qstart + (t % nqt) * AT_BQ;
-        load_rows64(a.q + bh * S * AT_D, dbuf<buf, SPLIT_LDS>(Qs0, Qs1, Qp), r0, S, wave, lane);
-        load_rows64(a.dout + bh * S * AT_D, dbuf<buf, SPLIT_LDS>(Ds0, Ds1, Dp), r0, S, wave, lane);
+        const int wv = __builtin_amdgcn_readfirstlane(wave);   // wave-uniform
+        if (wv < 4) load_rows64(a.q + bh * S * AT_D, buf ? Qs1 : Qs0, r0, S, wv, lane);
+        else load_rows64(a.dout + bh * S * AT_D, buf ? Ds1 : Ds0, r0, S, wv - 4, lane);
         if constexpr (SOFTCAP) {
-            const int wv = __builtin_amdgcn_readfirstlane(wave);   // wave-uniform
             int r = r0 + lane;
             r = r < S ? r : S - 1;
-            // one fixed destination array per load (keeps its alias scope)
             if (wv == 0)
                 __builtin_amdgcn_global_load_lds((const void *)(a.nlse + bh * S + r),
-                                                 (void __attribute__((address_space(3))) *)dbuf<buf, SPLIT_LDS>(Ls0, Ls1, Lp), 4, 0, 0);
-            else if (wv == 1)
+                                                 (void __attribute__((address_space(3))) *)(buf ? Ls1 : Ls0), 4, 0, 0);
+            else if (wv == 4)
                 __builtin_amdgcn_global_load_lds((const void *)(a.delta + bh * S + r),
-                                                 (void __attribute__((address_space(3))) *)dbuf<buf, SPLIT_LDS>(Es0, Es1, Ep), 4, 0, 0);
+                                                 (void __attribute__((address_space(3))) *)(buf ? Es1 : Es0), 4, 0, 0);
         }
     };
 
-    // ---- an unmasked tile as explicit scheduling slots -----------------------
-    // With one wave per SIMD nothing else hides a wave's latencies, so the 64
-    // MFMAs of a tile (m < 32: S and dP, query block m / 16, contraction step
-    // (m % 16) / 2, S for even m; m >= 32: n = m - 32, fragment n / 8, d block
-    // (n % 8) / 2, dV for even n) run two per slot with every LDS operand read
-    // AT_BW_AHEAD slots ahead, and the transform of query block 0 runs beside
-    // the S / dP MFMAs of block 1 (slots 8-15), that of block 1 beside the
-    // dV / dK MFMAs of fragments 0 and 1 (slots 16-23), one score pair per
-    // slot.  A scheduling fence closes each slot.  Every accumulator sees its
-    // terms in the order of the masked path below, so the outputs are those
-    // of the unslotted tile bit for bit (measured on MI355X: softcap backward
-    // 1.085x, sigmoid 1.07x, the comparators 1.09-1.13x).
-    constexpr int AT_BW_AHEAD = 2;   // 1 and 3 measured within 1 %
-    auto slotted_tile = [&](const uint16_t *Qb, const uint16_t *Db, auto bufc) __attribute__((always_inline)) {
-        constexpr int buf = decltype(bufc)::value;
-        f32x16 s[2], dp[2];
-        bf16x8 pf[4], dsf[4];
-        uint32_t pw[4][4], dw[4][4];   // P and dS words of fragment f
-        bf16x8 op[64];
-        f32x4 nlb[2], dlb[2];          // -lse log2(e) and Delta of a group of 4 query rows
-        auto load_op = [&](auto mc) __attribute__((always_inline)) {
-            constexpr int M = decltype(mc)::value;
-            if constexpr (M < 32) {
-                constexpr int qb = M >> 4, ks = (M & 15) >> 1;
-                op[M] = lds_row8((M & 1) ? Db : Qb, qb * 32 + col, ks * 2 + h);
-            } else {
-                constexpr int n = M - 32;
-                op[M] = lds_tr_a((n & 1) ? Qb : Db, n >> 3, (n & 7) >> 1, g16, i16);
-            }
-        };
-        auto mfma_op = [&](auto mc) __attribute__((always_inline)) {
-            constexpr int M = decltype(mc)::value;
-            if constexpr (M < 32) {
-                constexpr int qb = M >> 4, ks = (M & 15) >> 1;
-                if constexpr ((M & 1) == 0)
-                    s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[M], kf[ks], ks == 0 ? f32x16{} : s[qb], 0, 0, 0);
-                else
-                    dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[M], vf[ks], ks == 0 ? f32x16{} : dp[qb], 0, 0, 0);
-            } else {
-                constexpr int n = M - 32, f = n >> 3, db = (n & 7) >> 1;
-                if constexpr ((n & 1) == 0)
-                    dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[M], pf[f], dv[db], 0, 0, 0);
-                else
-                    dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[M], dsf[f], dk[db], 0, 0, 0);
-            }
-        };
-        // LSE / Delta of group g = 4 qb + j (query rows qb*32 + j*8 + h*4 .. + 3)
-        auto group_load = [&](auto gc) __attribute__((always_inline)) {
-            constexpr int g = decltype(gc)::value, qb = g >> 2, j = g & 3;
-            if constexpr (SOFTCAP) {
-                nlb[g & 1] = *(const f32x4 *)(&dbuf<buf, SPLIT_LDS>(Ls0, Ls1, Lp)[qb * 32 + j * 8 + h * 4]);
-                dlb[g & 1] = *(const f32x4 *)(&dbuf<buf, SPLIT_LDS>(Es0, Es1, Ep)[qb * 32 + j * 8 + h * 4]);
-            }
-        };
-        // score pair P: query block P / 8, rows j*8 + h*4 + i, i + 1 with
-        // j = (P % 8) / 2, i = 2 (P % 2)
-        auto pair = [&](auto pc) __attribute__((always_inline)) {
-            constexpr int P = decltype(pc)::value, qb = P >> 3, j = (P & 7) >> 1, i = (P & 1) * 2;
-            constexpr int e = j * 4 + i;
-            float nl0 = 0.0f, nl1 = 0.0f, dl0 = 0.0f, dl1 = 0.0f;
-            if constexpr (SOFTCAP) {
-                nl0 = nlb[j & 1][i];
-                nl1 = nlb[j & 1][i + 1];
-                dl0 = dlb[j & 1][i];
-                dl1 = dlb[j & 1][i + 1];
-            }
-            float d0, d1;
-            constexpr int f = qb * 2 + (j >> 1), w = (j & 1) * 2 + (i >> 1);
-            bwd_pair<MODE, EXP>(a, s[qb][e], s[qb][e + 1], dp[qb][e], dp[qb][e + 1], nl0, nl1, dl0, dl1,
-                                pw[f][w], d0, d1);
-            dw[f][w] = pack_bf(d0, d1);
-            if constexpr (w == 3) {
-                pf[f] = bc<bf16x8>(u32x4{pw[f][0], pw[f][1], pw[f][2], pw[f][3]});
-                dsf[f] = bc<bf16x8>(u32x4{dw[f][0], dw[f][1], dw[f][2], dw[f][3]});
-            }
-        };
-        static_for<2 * AT_BW_AHEAD>([&](auto mc) __attribute__((always_inline)) { load_op(mc); });
-        __builtin_amdgcn_sched_barrier(0);
-        static_for<32>([&](auto tc) __attribute__((always_inline)) {
-            constexpr int t = decltype(tc)::value;
-            static_for<2>([&](auto ic) __attribute__((always_inline)) {
-                constexpr int M = 2 * (t + AT_BW_AHEAD) + decltype(ic)::value;
-                if constexpr (M < 64) load_op(std::integral_constant<int, M>{});
-            });
-            // the group's LSE / Delta one slot before its first pair
-            if constexpr (t >= 7 && t < 23 && ((t - 7) & 1) == 0)
-                group_load(std::integral_constant<int, (t - 7) / 2>{});
-            mfma_op(std::integral_constant<int, 2 * t>{});
-            mfma_op(std::integral_constant<int, 2 * t + 1>{});
-            if constexpr (t >= 8 && t < 24) pair(std::integral_constant<int, t - 8>{});
-            __builtin_amdgcn_sched_barrier(0);
-        });
-    };
-
     load(0, std::integral_constant<int, 0>{});
-    auto tile = [&](int t, auto bufc) {
+    auto tile = [&](int t, auto bufc) __attribute__((always_inline)) {
         constexpr int buf = decltype(bufc)::value;
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         if (t + 1 < ntile) load(t + 1, std::integral_constant<int, buf ^ 1>{});
-        const int r0 = qstart + (t % nqt) * AT_BQ;
-        if (a.causal && r0 + AT_BQ - 1 < k0) return;   // every row of the tile precedes these keys
-        if (k0 >= S) return;
-        const uint16_t *Qb = dbuf<buf, SPLIT_LDS>(Qs0, Qs1, Qp);
-        const uint16_t *Db = dbuf<buf, SPLIT_LDS>(Ds0, Ds1, Dp);
-        const bool need_mask = (a.causal && r0 < k0 + 31) || r0 + AT_BQ > S;
-        if (!need_mask) {
-            slotted_tile(Qb, Db, bufc);
-            return;
-        }
+        const int r0 = qstart + (t % nqt) * AT_BQ + qh * 32;   // this wave's first row
+        if (a.causal && r0 + 31 < k0) return;   // every row of the half precedes these keys
+        if (k0 >= S || r0 >= S) return;
+        const uint16_t *Qb = buf ? Qs1 : Qs0;
+        const uint16_t *Db = buf ? Ds1 : Ds0;
+        const float *Lb = buf ? Ls1 : Ls0;
+        const float *Eb = buf ? Es1 : Es0;
+        const bool need_mask = (a.causal && r0 < k0 + 31) || r0 + 32 > S;
+        // the lane's byte offsets (per tile, so the compiler does not hold
+        // every derived address for the whole loop)
+        uint32_t bq = bq0, bkv = bkv0, btr = btr0;
+        asm volatile("" : "+v"(bq), "+v"(bkv), "+v"(btr));
 
-        f32x16 s[2], dp[2];
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            s[qb] = f32x16{};
-            dp[qb] = f32x16{};
-#pragma unroll
-            for (int ks = 0; ks < 8; ++ks) {
-                s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row8(Qb, qb * 32 + col, ks * 2 + h),
-                                                                kf[ks], s[qb], 0, 0, 0);
-                dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row8(Db, qb * 32 + col, ks * 2 + h),
-                                                                 vf[ks], dp[qb], 0, 0, 0);
-            }
-        }
-
-        // a masked tile (the causal diagonal or the ragged end; every other
-        // tile takes slotted_tile): s[qb][j*4 + i] is query r0 + qb*32 + j*8 +
-        // h*4 + i of this lane's key
-        bf16x8 pf[4] = {}, dsf[4] = {};
+        // S = Q K^T, dP = dO V^T of the half (lane holds key my_k, rows
+        // r0 + j*8 + h*4 + i in entry j*4 + i) as 8 fenced slots (S and dP
+        // of one contraction step) with the operands read one slot ahead.  Row chunk c of a swizzled tile row r
+        // sits at byte r * 256 + ((c ^ f(r)) << 4), so step ks of a lane's
+        // row is its step-0 offset XOR (ks << 5): one XOR per read from a
+        // per-lane base instead of one held address per step
+        f32x16 s = {}, dp = {};
         {
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    f32x4 nl4 = {}, dl4 = {};
-                    if constexpr (SOFTCAP) {
-                        nl4 = *(const f32x4 *)(&dbuf<buf, SPLIT_LDS>(Ls0, Ls1, Lp)[qb * 32 + j * 8 + h * 4]);
-                        dl4 = *(const f32x4 *)(&dbuf<buf, SPLIT_LDS>(Es0, Es1, Ep)[qb * 32 + j * 8 + h * 4]);
-                    }
-                    uint32_t pw[2], dw[2];
-#pragma unroll
-                    for (int i = 0; i < 4; i += 2) {
-                        const int e = j * 4 + i;
-                        uint32_t pk;
-                        float d0, d1;
-                        bwd_pair<MODE, EXP>(a, s[qb][e], s[qb][e + 1], dp[qb][e], dp[qb][e + 1], nl4[i],
-                                            nl4[i + 1], dl4[i], dl4[i + 1], pk, d0, d1);
-                        uint32_t dk2 = pack_bf(d0, d1);
-                        const int q = r0 + qb * 32 + j * 8 + h * 4 + i;
-                        const bool vis0 = q < S && (!a.causal || q >= my_k);
-                        const bool vis1 = q + 1 < S && (!a.causal || q + 1 >= my_k);
-                        const uint32_t keep = (vis0 ? 0x0000FFFFu : 0u) | (vis1 ? 0xFFFF0000u : 0u);
-                        pk &= keep;
-                        dk2 &= keep;
-                        pw[i >> 1] = pk;
-                        dw[i >> 1] = dk2;
-                    }
-                    // B-operand fragment ks = 2 qb + j / 2 holds accumulator
-                    // entries (j % 2) * 8 .. + 7
-                    const int f = qb * 2 + (j >> 1);
-                    const int half = (j & 1) * 2;
-                    u32x4 pv = bc<u32x4>(pf[f]), dv4 = bc<u32x4>(dsf[f]);
-                    pv[half] = pw[0];
-                    pv[half + 1] = pw[1];
-                    dv4[half] = dw[0];
-                    dv4[half + 1] = dw[1];
-                    pf[f] = bc<bf16x8>(pv);
-                    dsf[f] = bc<bf16x8>(dv4);
-                }
-            }
+            bf16x8 qa[AH + 1], ka[AH + 1], da[AH + 1], va[AH + 1];
+            auto ld = [&](auto kc) __attribute__((always_inline)) {
+                constexpr int ks = decltype(kc)::value, b = ks % (AH + 1);
+                const uint32_t oq = bq ^ (uint32_t)(ks << 5), ok = bkv ^ (uint32_t)(ks << 5);
+                qa[b] = ld_bf16x8((const uint16_t *)((const char *)Qb + oq));
+                da[b] = ld_bf16x8((const uint16_t *)((const char *)Db + oq));
+                ka[b] = ld_bf16x8((const uint16_t *)((const char *)Kt + ok));
+                va[b] = ld_bf16x8((const uint16_t *)((const char *)Vt + ok));
+            };
+            static_for<AH>([&](auto kc) __attribute__((always_inline)) { ld(kc); });
+            __builtin_amdgcn_sched_barrier(0);
+            static_for<8>([&](auto kc) __attribute__((always_inline)) {
+                constexpr int ks = decltype(kc)::value, b = ks % (AH + 1);
+                if constexpr (ks + AH < 8) ld(std::integral_constant<int, ks + AH>{});
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[b], ka[b], s, 0, 0, 0);
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[b], va[b], dp, 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            });
         }
+        // P and dS as the B operands of the two contraction steps: fragment
+        // f holds entries j = f (words 0-1) and j = f + 2 (words 2-3), i.e.
+        // rows 8 f + .. of the half and the rows 16 further on
+        u32x4 pw4[2], dw4[2];
+        f32x4 nl4[4], dl4[4];
+        auto pair = [&](auto jc, auto ic, auto masked) __attribute__((always_inline)) {
+            constexpr int j = decltype(jc)::value, i = decltype(ic)::value;
+            constexpr bool MASKED = decltype(masked)::value;
+            constexpr int e = j * 4 + i, f = j & 1, w = (j >> 1) * 2 + (i >> 1);
+            if constexpr (SOFTCAP && i == 0) {
+                nl4[j] = *(const f32x4 *)(&Lb[qh * 32 + j * 8 + h * 4]);
+                dl4[j] = *(const f32x4 *)(&Eb[qh * 32 + j * 8 + h * 4]);
+            }
+            float nl0 = 0.0f, nl1 = 0.0f, dl0 = 0.0f, dl1 = 0.0f;
+            if constexpr (SOFTCAP) {
+                nl0 = nl4[j][i];
+                nl1 = nl4[j][i + 1];
+                dl0 = dl4[j][i];
+                dl1 = dl4[j][i + 1];
+            }
+            uint32_t pk;
+            float d0, d1;
+            bwd_pair<MODE, EXP>(a, s[e], s[e + 1], dp[e], dp[e + 1], nl0, nl1, dl0, dl1, pk, d0, d1);
+            uint32_t dk2 = pack_bf(d0, d1);
+            if constexpr (MASKED) {
+                const int q = r0 + j * 8 + h * 4 + i;
+                const bool vis0 = q < S && (!a.causal || q >= my_k);
+                const bool vis1 = q + 1 < S && (!a.causal || q + 1 >= my_k);
+                const uint32_t keep = (vis0 ? 0x0000FFFFu : 0u) | (vis1 ? 0xFFFF0000u : 0u);
+                pk &= keep;
+                dk2 &= keep;
+            }
+            pw4[f][w] = pk;
+            dw4[f][w] = dk2;
+        };
 
-        // dV^T += dO^T P,  dK^T += Q^T dS
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_tr_a(Db, ks, db, g16, i16), pf[ks],
-                                                                 dv[db], 0, 0, 0);
-                dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_tr_a(Qb, ks, db, g16, i16), dsf[ks],
-                                                                 dk[db], 0, 0, 0);
-            }
-        }
+        // dV^T += dO^T P,  dK^T += Q^T dS over the half's two contraction
+        // steps f, in slots (d block db) with the operands read one slot
+        // ahead.  A transposed read covers rows 8 f + .. of the half and the
+        // rows 16 further on (the same swizzle, so a fixed offset); d block
+        // db is the chunk offset XOR (db << 6) and step f adds 8 rows, i.e.
+        // XOR (1 << 5) and + 2048 bytes.  The transform of fragment 1 runs
+        // one pair per slot beside the MFMAs of fragment 0.
+        bf16x8 oa[AH + 1], qa[AH + 1];
+        auto ld = [&](auto nc) __attribute__((always_inline)) {
+            constexpr int n = decltype(nc)::value, f = n >> 2, db = n & 3, b = n % (AH + 1);
+            const uint32_t o = (btr ^ (uint32_t)((db << 6) | (f << 5))) + (uint32_t)(f * 2048);
+            const u32x2 ol = ds_read_tr16((const uint16_t *)((const char *)Db + o));
+            const u32x2 oh = ds_read_tr16((const uint16_t *)((const char *)Db + o + 4096));
+            const u32x2 ql = ds_read_tr16((const uint16_t *)((const char *)Qb + o));
+            const u32x2 qh2 = ds_read_tr16((const uint16_t *)((const char *)Qb + o + 4096));
+            oa[b] = bc<bf16x8>(u32x4{ol.x, ol.y, oh.x, oh.y});
+            qa[b] = bc<bf16x8>(u32x4{ql.x, ql.y, qh2.x, qh2.y});
+        };
+        auto run = [&](auto masked) __attribute__((always_inline)) {
+            using I0 = std::integral_constant<int, 0>;
+            using I2 = std::integral_constant<int, 2>;
+            // fragment 0 (entries 0 and 2)
+            pair(I0{}, I0{}, masked);
+            pair(I0{}, I2{}, masked);
+            pair(I2{}, I0{}, masked);
+            pair(I2{}, I2{}, masked);
+            const bf16x8 pf0 = bc<bf16x8>(pw4[0]), ds0 = bc<bf16x8>(dw4[0]);
+            static_for<AH>([&](auto nc) __attribute__((always_inline)) { ld(nc); });
+            __builtin_amdgcn_sched_barrier(0);
+            static_for<8>([&](auto nc) __attribute__((always_inline)) {
+                constexpr int n = decltype(nc)::value, f = n >> 2, db = n & 3, b = n % (AH + 1);
+                if constexpr (n + AH < 8) ld(std::integral_constant<int, n + AH>{});
+                if constexpr (f == 0) {
+                    dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[b], pf0, dv[db], 0, 0, 0);
+                    dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[b], ds0, dk[db], 0, 0, 0);
+                    // fragment 1 (entries 1 and 3), one pair per slot
+                    pair(std::integral_constant<int, 1 + 2 * (db >> 1)>{}, std::integral_constant<int, 2 * (db & 1)>{},
+                         masked);
+                } else {
+                    dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[b], bc<bf16x8>(pw4[1]), dv[db], 0, 0, 0);
+                    dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[b], bc<bf16x8>(dw4[1]), dk[db], 0, 0, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        };
+        if (need_mask) run(std::true_type{});
+        else run(std::false_type{});
     };
     for (int t = 0; t < ntile; t += 2) {
         tile(t, std::integral_constant<int, 0>{});
         if (t + 1 < ntile) tile(t + 1, std::integral_constant<int, 1>{});
     }
 
-    if (!valid) return;
+    // half 1 hands its partials to half 0 through LDS (16 KB per array per
+    // key group: the Q / dO buffers take dK, K / V take dV)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    float *xk = (float *)(kg == 0 ? Qs0 : kg == 1 ? Qs1 : kg == 2 ? Ds0 : Ds1);
+    float *xv = (float *)(kg < 2 ? Kt : Vt) + (kg & 1) * 4096;
+    if (qh == 1) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int c = (db * 4 + j) * 64 + lane;
+                *(f32x4 *)(xk + c * 4) = f32x4{dk[db][j * 4], dk[db][j * 4 + 1], dk[db][j * 4 + 2], dk[db][j * 4 + 3]};
+                *(f32x4 *)(xv + c * 4) = f32x4{dv[db][j * 4], dv[db][j * 4 + 1], dv[db][j * 4 + 2], dv[db][j * 4 + 3]};
+            }
+        }
+    }
+    __syncthreads();
+    if (qh == 1 || !valid) return;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int c = (db * 4 + j) * 64 + lane;
+            const f32x4 ok = *(const f32x4 *)(xk + c * 4), ov = *(const f32x4 *)(xv + c * 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                dk[db][j * 4 + e] += ok[e];
+                dv[db][j * 4 + e] += ov[e];
+            }
+        }
+    }
     if constexpr (SPLIT) {
         // FP32 partials of this query head: part[0][bx][my_k][:] = dK (before
         // the 1/sqrt(D) factor), part[1][bx][my_k][:] = dV

@@ -265,11 +265,11 @@ inline void attn_bwd_launch(const AttnBwdArgs &a, int32_t B, int32_t H, int32_t 
     hipLaunchKernelGGL((k_attn_bwd_dq<MODE, EXP>), gq, dim3(256), 0, stream, a);
     const int ntk = (S + AT_BK - 1) / AT_BK;
     if (H == Hkv) {
-        hipLaunchKernelGGL((k_attn_bwd_dkdv<MODE, false, EXP>), dim3((unsigned)(ntk * B * Hkv)), dim3(256), 0,
+        hipLaunchKernelGGL((k_attn_bwd_dkdv<MODE, false, EXP>), dim3((unsigned)(ntk * B * Hkv)), dim3(512), 0,
                            stream, a);
         return;
     }
-    hipLaunchKernelGGL((k_attn_bwd_dkdv<MODE, true, EXP>), dim3((unsigned)(ntk * B * H)), dim3(256), 0, stream,
+    hipLaunchKernelGGL((k_attn_bwd_dkdv<MODE, true, EXP>), dim3((unsigned)(ntk * B * H)), dim3(512), 0, stream,
                        a);
     const int64_t n8 = (int64_t)B * Hkv * S * AT_D / 8;
     hipLaunchKernelGGL(k_attn_bwd_reduce, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream, a, n8,
