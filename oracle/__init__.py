@@ -19,7 +19,7 @@ import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liborc.so")
-SOURCES = ["orc_fp.c", "orc_fit.c", "orc_eval.c", "orc_exp2.c"]
+SOURCES = ["orc_fp.c", "orc_fit.c", "orc_eval.c", "orc_exp2.c", "orc_rope.c"]
 
 SIGMOID, TANH, SILU, GELU = 1, 2, 3, 4
 FUNC_NAMES = {SIGMOID: "sigmoid", TANH: "tanh", SILU: "silu", GELU: "gelu"}
@@ -65,6 +65,12 @@ class Attn(C.Structure):
                 ("order", C.c_int32), ("exp2_core", C.c_int32), ("cap", C.c_float),
                 ("tanh_prog", C.POINTER(Prog)),
                 ("sig", C.POINTER(SigProg)), ("tanh_order", C.c_int32), ("replay", C.c_int32)]
+
+
+class RopeProg(C.Structure):
+    """Paired sine / cosine program of the rotary embedding (BF16 bit patterns):
+    sin(pi u) ~ u (a1 + a3 u^2 + a5 u^4), cos(pi u) ~ b0 + b2 u^2 + b4 u^4 + b6 u^6."""
+    _fields_ = [("sin_c", C.c_uint16 * 3), ("cos_c", C.c_uint16 * 4)]
 
 
 ATTN_SOFTCAP_POLY, ATTN_SOFTCAP_EXACT, ATTN_SIGMOID_POLY, ATTN_SIGMOID_EXACT = 1, 2, 3, 4
@@ -120,6 +126,15 @@ def lib():
             "orc_exp2_fit": (f64, [C.c_int, C.c_int]),
             "orc_exp2_core_target": (C.c_float, [C.c_int, C.c_float]),
             "orc_sig_prog_eval": (u16, [P(SigProg), u16, C.c_int, P(u16)]),
+            "orc_lsq": (C.c_int, [C.c_int, C.c_int, P(f64), P(f64), P(f64)]),
+            "orc_rope_fit": (C.c_int, [P(f64), P(f64)]),
+            "orc_rope_prog": (C.c_int, [P(RopeProg)]),
+            "orc_rope_inc": (None, [C.c_int, f64, P(C.c_uint32)]),
+            "orc_rope_coord": (u16, [C.c_uint32]),
+            "orc_rope_sincos": (None, [P(RopeProg), C.c_uint32, P(u16), P(u16)]),
+            "orc_rope_rotate": (None, [u16, u16, u16, u16, P(u16), P(u16)]),
+            "orc_rope_rows": (None, [P(RopeProg), P(C.c_uint32), C.c_int, C.c_void_p, C.c_void_p,
+                                     i64, C.c_void_p]),
             "orc_threads": (C.c_int, []),
             "orc_set_threads": (C.c_int, [C.c_int]),
         }
@@ -347,3 +362,71 @@ def threads() -> int:
 def set_threads(n: int) -> int:
     """Threads of the oracle's later parallel loops; returns the previous count."""
     return lib().orc_set_threads(int(n))
+
+
+# ---- rotary embedding (Appendix B.2) ---------------------------------------
+
+def lsq(A, r) -> np.ndarray:
+    """Least squares by the oracle's Householder QR (A: N x m, column-major copy)."""
+    A = np.asarray(A, dtype=np.float64)
+    N, m = A.shape
+    a = np.ascontiguousarray(A.T).ravel().copy()
+    rr = np.asarray(r, dtype=np.float64).copy()
+    x = np.zeros(m)
+    rc = lib().orc_lsq(N, m, a.ctypes.data_as(C.POINTER(C.c_double)),
+                       rr.ctypes.data_as(C.POINTER(C.c_double)), x.ctypes.data_as(C.POINTER(C.c_double)))
+    assert rc == 0
+    return x
+
+
+def rope_fit():
+    """FP64 (a1, a3, a5), (b0, b2, b4, b6) before rounding."""
+    s, c = (C.c_double * 3)(), (C.c_double * 4)()
+    assert lib().orc_rope_fit(s, c) == 0
+    return np.array(list(s)), np.array(list(c))
+
+
+def rope_prog() -> RopeProg:
+    rp = RopeProg()
+    assert lib().orc_rope_prog(C.byref(rp)) == 0
+    return rp
+
+
+def rope_inc(D: int, base: float = 10000.0) -> np.ndarray:
+    out = (C.c_uint32 * (D // 2))()
+    lib().orc_rope_inc(D, base, out)
+    return np.array(list(out), dtype=np.uint32)
+
+
+def rope_coord(phase) -> np.ndarray:
+    return np.array([lib().orc_rope_coord(int(p)) for p in np.atleast_1d(phase)], dtype=np.uint16)
+
+
+def rope_sincos(rp: RopeProg, phase):
+    """(sin bits, cos bits) of the programs at each Q0.32 phase."""
+    ph = np.atleast_1d(np.asarray(phase, dtype=np.uint64))
+    s, c = np.empty(ph.size, np.uint16), np.empty(ph.size, np.uint16)
+    a, b = C.c_uint16(), C.c_uint16()
+    for j, p in enumerate(ph):
+        lib().orc_rope_sincos(C.byref(rp), int(p), C.byref(a), C.byref(b))
+        s[j], c[j] = a.value, b.value
+    return s, c
+
+
+def rope_rotate(x0, x1, s, c):
+    a, b = C.c_uint16(), C.c_uint16()
+    lib().orc_rope_rotate(int(x0), int(x1), int(s), int(c), C.byref(a), C.byref(b))
+    return a.value, b.value
+
+
+def rope_rows(rp: RopeProg, inc, x_bits, pos) -> np.ndarray:
+    """Rotary embedding of rows x [n, D] (FP16 bits) at positions pos [n]."""
+    x = _u16(x_bits)
+    n, D = x.shape
+    inc = np.ascontiguousarray(inc, dtype=np.uint32)
+    pos = np.ascontiguousarray(pos, dtype=np.int64)
+    assert pos.size == n and inc.size == D // 2
+    y = np.empty_like(x)
+    lib().orc_rope_rows(C.byref(rp), inc.ctypes.data_as(C.POINTER(C.c_uint32)), D, _ptr(x),
+                        _ptr(pos), n, _ptr(y))
+    return y

@@ -167,6 +167,24 @@ uint16_t orc_sig_prog_eval(const orc_sig_prog *sp, uint16_t x, int order, uint16
 int orc_threads(void);
 int orc_set_threads(int n);   /* threads of later parallel loops; returns the old count */
 
+/* ---- paired sine / cosine and rotary embedding (orc_rope.c) ----------------
+ * Appendix B.2: Q0.32 turn increments, signed Q15 half-turn coordinate,
+ * packed FP16 D5 sine and D6 cosine on the shared square, rotation of the
+ * interleaved pairs (the readings are listed in orc_rope.c). */
+typedef struct {
+    uint16_t sin_c[3];   /* BF16 a1, a3, a5: sin(pi u) ~ u (a1 + a3 u^2 + a5 u^4) */
+    uint16_t cos_c[4];   /* BF16 b0, b2, b4, b6: cos(pi u) ~ b0 + b2 u^2 + ...   */
+} orc_rope;
+int  orc_lsq(int N, int m, double *A, double *r, double *x);   /* Householder QR */
+int  orc_rope_fit(double *sin_coef, double *cos_coef);          /* FP64 a1,a3,a5; b0..b6 */
+int  orc_rope_prog(orc_rope *out);                              /* the BF16-rounded fit */
+void orc_rope_inc(int D, double base, uint32_t *inc);           /* D/2 turn increments */
+uint16_t orc_rope_coord(uint32_t phase);                        /* u = RN16(v / 2^15) */
+void orc_rope_sincos(const orc_rope *rp, uint32_t phase, uint16_t *s, uint16_t *c);
+void orc_rope_rotate(uint16_t x0, uint16_t x1, uint16_t s, uint16_t c, uint16_t *y0, uint16_t *y1);
+void orc_rope_rows(const orc_rope *rp, const uint32_t *inc, int D, const uint16_t *x,
+                   const int64_t *pos, int64_t nrows, uint16_t *y);
+
 #ifdef __cplusplus
 }
 #endif

@@ -83,7 +83,7 @@ double orc_residual(int func, int deriv, double t)
 
 /* Solve min ||A x - r||_2 for an N x m column-major A by Householder QR in
  * FP64.  A and r are overwritten.  Returns 0 on success. */
-static int lsq_householder(int N, int m, double *A, double *r, double *x)
+int orc_lsq(int N, int m, double *A, double *r, double *x)
 {
     for (int k = 0; k < m; k++) {
         double *ak = A + (size_t)k * N;
@@ -144,7 +144,7 @@ int orc_fit(int func, int deriv, int degree, double Li, double *coef)
             }
             r[k - 1] = orc_residual(func, deriv, t) - f0 - (fL - f0) * u;
         }
-        const int rc = lsq_householder(N_NODES, m, A, r, b);
+        const int rc = orc_lsq(N_NODES, m, A, r, b);
         free(A);
         free(r);
         if (rc) return -3;
