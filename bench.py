@@ -412,6 +412,27 @@ def components_pages(torch, pa, si, alt, res):
                      "speedup": round(tn / tp, 3), "pct_hbm": round(100 * n * by / tp / 1e6 / HBM_PEAK_GBS, 1)}
     del x, gr, y
 
+    # Appendix B.2 fused rotary embedding, Llama-3-8B-like geometry:
+    # Q [1, 4096, 32, 128] and K [1, 4096, 8, 128] FP16 in, transposed out;
+    # the paired D5 sine / D6 cosine programs against accurate sinf / cosf on
+    # the fly and against a cached (cos, sin) table (built once, not timed)
+    q, k = si.t_rope_inputs(1, 4096, 32, 8, 128)
+    qo = torch.empty((1, 32, 4096, 128), dtype=q.dtype, device=q.device)
+    ko = torch.empty((1, 8, 4096, 128), dtype=q.dtype, device=q.device)
+    tab = pa.rope_table(4096, 128, 10000.0)
+    fp = lambda: pa.poly_rope(q, k, 10000.0, q_out=qo, k_out=ko)  # noqa: E731
+    fn = lambda: pa.native_rope(q, k, 10000.0, q_out=qo, k_out=ko)  # noqa: E731
+    ft = lambda: pa.native_rope_table(q, k, tab, q_out=qo, k_out=ko)  # noqa: E731
+    fp(), fn(), ft()
+    tp, tn = alt(fp, fn)
+    tp2, tt = alt(fp, ft)
+    by = 2 * (q.numel() + k.numel()) * 2          # read and write, FP16
+    res["rope_fused_4096x32x8x128"] = {
+        "elements": q.numel() + k.numel(), "poly_ms": round(tp, 4), "native_ms": round(tn, 4),
+        "table_ms": round(tt, 4), "speedup": round(tn / tp, 3), "speedup_vs_table": round(tt / tp2, 3),
+        "pct_hbm": round(100 * by / tp / 1e6 / HBM_PEAK_GBS, 1)}
+    del q, k, qo, ko, tab
+
     # B4 one-kernel routed-expert SwiGLU: 24,576 rows x 1,280
     g, u, d = si.t_swiglu_inputs(24576, 1280)
     h, dg, du = torch.empty_like(g), torch.empty_like(g), torch.empty_like(g)

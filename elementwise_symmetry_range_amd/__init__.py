@@ -28,7 +28,8 @@ __all__ = [
     "poly_softcap_attn_fwd_exp2", "poly_softcap_attn_bwd", "native_softcap_attn_bwd",
     "poly_sigmoid_attn_fwd",
     "native_sigmoid_attn_fwd", "poly_sigmoid_attn_bwd", "native_sigmoid_attn_bwd",
-    "sigmoid_attn_program", "attn_bwd_workspace", "stream_copy", "FUNCS",
+    "sigmoid_attn_program", "attn_bwd_workspace", "stream_copy", "FUNCS", "poly_rope",
+    "native_rope", "native_rope_table", "rope_table", "rope_program",
 ]
 
 FUNCS = {"sigmoid": 1, "tanh": 2, "silu": 3, "gelu": 4}
@@ -47,6 +48,10 @@ class PaSigmoidAttnProgram(C.Structure):
     _fields_ = [("n", C.c_int32), ("thr", C.c_uint16), ("clamp_lo", C.c_uint16),
                 ("clamp_hi", C.c_uint16), ("coeff_bits", (C.c_uint16 * 4) * 2),
                 ("a_bits", C.c_uint16 * 2), ("b_bits", C.c_uint16 * 2), ("order", C.c_int32)]
+
+
+class PaRopeProgram(C.Structure):
+    _fields_ = [("sin_bits", C.c_uint16 * 3), ("cos_bits", C.c_uint16 * 4)]
 
 
 class PolyActError(RuntimeError):
@@ -93,6 +98,11 @@ def lib() -> C.CDLL:
             "poly_sigmoid_attn_program": [C.POINTER(PaSigmoidAttnProgram)],
             "poly_program_info": [i32, i32, i32, C.POINTER(PaProgram)],
             "pa_stream_copy": [p, p, p, i64, p],
+            "poly_rope": [p] * 4 + [i32] * 5 + [C.c_double, p],
+            "native_rope": [p] * 4 + [i32] * 5 + [C.c_double, p],
+            "native_rope_table": [p] * 5 + [i32] * 5 + [p],
+            "pa_rope_table": [p, i32, i32, C.c_double, p],
+            "poly_rope_program": [C.POINTER(PaRopeProgram)],
         }
         for name, args in sigs.items():
             fn = getattr(L, name)
@@ -485,3 +495,70 @@ def sigmoid_attn_program() -> dict:
             "coeff_bits": [[int(out.coeff_bits[r][j]) for j in range(4)] for r in range(2)],
             "a_bits": [int(x) for x in out.a_bits], "b_bits": [int(x) for x in out.b_bits],
             "order": out.order}
+
+
+# ---- rotary position embedding ---------------------------------------------
+
+def _rope_io(q, k, q_out, k_out):
+    _dev(q, "q")
+    _dev(k, "k")
+    if q.dtype != torch.float16 or k.dtype != torch.float16:
+        raise TypeError("q and k must be float16")
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B, S, Hq, D] and k [B, S, Hkv, D]")
+    B, S, Hq, D = q.shape
+    if k.shape[0] != B or k.shape[1] != S or k.shape[3] != D:
+        raise ValueError("k must be [B, S, Hkv, D] with q's B, S and D")
+    Hkv = k.shape[2]
+    if q_out is None:
+        q_out = torch.empty((B, Hq, S, D), dtype=q.dtype, device=q.device)
+    if k_out is None:
+        k_out = torch.empty((B, Hkv, S, D), dtype=k.dtype, device=k.device)
+    for t, name, shape in ((q_out, "q_out", (B, Hq, S, D)), (k_out, "k_out", (B, Hkv, S, D))):
+        _dev(t, name)
+        if tuple(t.shape) != shape or t.dtype != torch.float16:
+            raise ValueError(f"{name} must be float16 {list(shape)}")
+    return q_out, k_out, (B, S, Hq, Hkv, D)
+
+
+def poly_rope(q, k, base: float = 10000.0, q_out=None, k_out=None):
+    """Rotary embedding with the paired D5 sine / D6 cosine programs
+    (Appendix B.2): q [B, S, Hq, D], k [B, S, Hkv, D] FP16 -> q_out
+    [B, Hq, S, D], k_out [B, Hkv, S, D]."""
+    q_out, k_out, (B, S, Hq, Hkv, D) = _rope_io(q, k, q_out, k_out)
+    _call(lib().poly_rope, q.data_ptr(), k.data_ptr(), q_out.data_ptr(), k_out.data_ptr(), B, S, Hq,
+          Hkv, D, float(base), on=q, tensors=(k, q_out, k_out))
+    return q_out, k_out
+
+
+def native_rope(q, k, base: float = 10000.0, q_out=None, k_out=None):
+    """The same rotation with accurate sinf / cosf computed on the fly."""
+    q_out, k_out, (B, S, Hq, Hkv, D) = _rope_io(q, k, q_out, k_out)
+    _call(lib().native_rope, q.data_ptr(), k.data_ptr(), q_out.data_ptr(), k_out.data_ptr(), B, S,
+          Hq, Hkv, D, float(base), on=q, tensors=(k, q_out, k_out))
+    return q_out, k_out
+
+
+def rope_table(S: int, D: int, base: float = 10000.0, device=None) -> torch.Tensor:
+    """The comparator's (cos, sin) table: int32 [S, D / 2] words (two FP16 values)."""
+    t = torch.empty((S, D // 2), dtype=torch.int32, device=device or "cuda")
+    _call(lib().pa_rope_table, t.data_ptr(), S, D, float(base), on=t)
+    return t
+
+
+def native_rope_table(q, k, table: torch.Tensor, q_out=None, k_out=None):
+    """The same rotation with (cos, sin) read from a rope_table."""
+    q_out, k_out, (B, S, Hq, Hkv, D) = _rope_io(q, k, q_out, k_out)
+    if not table.is_cuda or table.numel() != S * (D // 2) or not table.is_contiguous():
+        raise ValueError("table must be a contiguous device tensor of S * D / 2 words")
+    _call(lib().native_rope_table, q.data_ptr(), k.data_ptr(), q_out.data_ptr(), k_out.data_ptr(),
+          table.data_ptr(), B, S, Hq, Hkv, D, on=q, tensors=(k, q_out, k_out, table))
+    return q_out, k_out
+
+
+def rope_program() -> dict:
+    """BF16 bits of the sine (a1, a3, a5) and cosine (b0, b2, b4, b6) programs."""
+    out = PaRopeProgram()
+    _check(lib().poly_rope_program(C.byref(out)))
+    return {"sin_bits": [int(x) for x in out.sin_bits], "cos_bits": [int(x) for x in out.cos_bits]}
+

@@ -11,6 +11,7 @@
 #include "attn_host.hpp"
 #include "ops.hpp"
 #include "programs.hpp"
+#include "rope.hpp"
 #include "stream_launch.hpp"
 #include "swiglu.hpp"
 
@@ -279,6 +280,79 @@ struct XorOp {
 }  // namespace
 
 // =============================================================================
+namespace {
+
+// FP16 value of a BF16 coefficient, duplicated into both halves (exact: the
+// rotary coefficients have at most 8 significant bits and FP16 exponents)
+uint32_t bf16_coef_f16x2(uint16_t b)
+{
+    uint32_t fbits = (uint32_t)b << 16;
+    float v;
+    std::memcpy(&v, &fbits, 4);
+    const _Float16 h = (_Float16)v;
+    uint16_t hb;
+    std::memcpy(&hb, &h, 2);
+    return (uint32_t)hb | ((uint32_t)hb << 16);
+}
+
+// shape checks shared by the rotary entry points; fills the sizes and the
+// turn increments inc_i = round(w_i 2^32 / (2 pi)), w_i = base^(-2 i / D)
+pa_status rope_args(int32_t B, int32_t S, int32_t Hq, int32_t Hkv, int32_t D, double base, bool need_base,
+                    RopeArgs &a)
+{
+    if (B < 0 || S < 0 || Hq < 0 || Hkv < 0) return PA_ERR_SHAPE;
+    if (D < 8 || D > RP_MAX_D || D % 8) return PA_ERR_SHAPE;
+    if (need_base && !(std::isfinite(base) && base >= 1.0)) return PA_ERR_SHAPE;
+    const int64_t rows = (int64_t)B * S;
+    if (rows > ((int64_t)1 << 40) || (int64_t)(Hq > Hkv ? Hq : Hkv) * D > ((int64_t)1 << 24)) return PA_ERR_SHAPE;
+    if ((rows * ((Hq + Hkv + RP_HPG - 1) / RP_HPG) * (D / 8) + 255) / 256 > 0x7FFFFFFF) return PA_ERR_SHAPE;
+    a = RopeArgs{};
+    a.rows = rows;
+    a.S = S;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.D = D;
+    for (int j = 0; j < 3; ++j) a.sc[j] = bf16_coef_f16x2(kRopeSin[j]);
+    for (int j = 0; j < 4; ++j) a.cc[j] = bf16_coef_f16x2(kRopeCos[j]);
+    if (need_base) {
+        const double turn = 4294967296.0 / (2.0 * 3.14159265358979323846);
+        for (int i = 0; i < D / 2; ++i)
+            a.inc[i] = (uint32_t)std::llround(std::pow(base, -2.0 * i / (double)D) * turn);
+    }
+    return PA_OK;
+}
+
+pa_status rope_run(int var, const void *q, const void *k, void *q_out, void *k_out, const void *table,
+                   int32_t B, int32_t S, int32_t Hq, int32_t Hkv, int32_t D, double base, hipStream_t stream)
+{
+    RopeArgs a;
+    pa_status st = rope_args(B, S, Hq, Hkv, D, base, var != RP_TABLE, a);
+    if (st != PA_OK) return st;
+    if (!q || !k || !q_out || !k_out || (var == RP_TABLE && !table)) return PA_ERR_NULL;
+    if (!aligned16({q, k, q_out, k_out}) || (var == RP_TABLE && !aligned16({table}))) return PA_ERR_ALIGN;
+    const int64_t qb = a.rows * Hq * D * 2, kb = a.rows * Hkv * D * 2;
+    const int64_t tb = var == RP_TABLE ? (int64_t)S * (D / 2) * 4 : 0;
+    if (pa::any_overlap({{q_out, qb}, {k_out, kb}}, {{q, qb}, {k, kb}, {table, tb}}) ||
+        (qb > 0 && kb > 0 && pa::any_overlap({{q_out, qb}}, {{k_out, kb}})))
+        return PA_ERR_OVERLAP;
+    if (a.rows == 0 || (Hq == 0 && Hkv == 0)) return PA_OK;
+    a.q = (const uint16_t *)q;
+    a.k = (const uint16_t *)k;
+    a.qo = (uint16_t *)q_out;
+    a.ko = (uint16_t *)k_out;
+    a.table = (const uint32_t *)table;
+    const int64_t ng = (Hq + Hkv + RP_HPG - 1) / RP_HPG;
+    const dim3 grid((unsigned)((a.rows * ng * (D / 8) + 255) / 256));
+    switch (var) {
+    case RP_POLY: hipLaunchKernelGGL(k_rope<RP_POLY>, grid, dim3(256), 0, stream, a); break;
+    case RP_NATIVE: hipLaunchKernelGGL(k_rope<RP_NATIVE>, grid, dim3(256), 0, stream, a); break;
+    default: hipLaunchKernelGGL(k_rope<RP_TABLE>, grid, dim3(256), 0, stream, a); break;
+    }
+    return launched();
+}
+
+}  // namespace
+
 extern "C" {
 
 int32_t pa_abi_version(void) { return PA_ABI_VERSION; }
@@ -615,6 +689,46 @@ pa_status poly_sigmoid_attn_program(pa_sigmoid_attn_program *out)
         out->b_bits[r] = d.b[r];
     }
     out->order = PA_ORDER_F32FMA_BF16;
+    return PA_OK;
+}
+
+pa_status poly_rope(const void *q, const void *k, void *q_out, void *k_out, int32_t B, int32_t S,
+                    int32_t Hq, int32_t Hkv, int32_t D, double base, hipStream_t stream)
+{
+    return rope_run(RP_POLY, q, k, q_out, k_out, nullptr, B, S, Hq, Hkv, D, base, stream);
+}
+
+pa_status native_rope(const void *q, const void *k, void *q_out, void *k_out, int32_t B, int32_t S,
+                      int32_t Hq, int32_t Hkv, int32_t D, double base, hipStream_t stream)
+{
+    return rope_run(RP_NATIVE, q, k, q_out, k_out, nullptr, B, S, Hq, Hkv, D, base, stream);
+}
+
+pa_status native_rope_table(const void *q, const void *k, void *q_out, void *k_out,
+                            const void *table, int32_t B, int32_t S, int32_t Hq, int32_t Hkv,
+                            int32_t D, hipStream_t stream)
+{
+    return rope_run(RP_TABLE, q, k, q_out, k_out, table, B, S, Hq, Hkv, D, 1.0, stream);
+}
+
+pa_status pa_rope_table(void *table, int32_t S, int32_t D, double base, hipStream_t stream)
+{
+    RopeArgs a;
+    const pa_status st = rope_args(1, S, 0, 0, D, base, true, a);
+    if (st != PA_OK) return st;
+    if (!table) return PA_ERR_NULL;
+    if (!aligned16({table})) return PA_ERR_ALIGN;
+    const int64_t n = (int64_t)S * (D / 2);
+    if (n == 0) return PA_OK;
+    hipLaunchKernelGGL(k_rope_table, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, (uint32_t *)table, a);
+    return launched();
+}
+
+pa_status poly_rope_program(pa_rope_program *out)
+{
+    if (!out) return PA_ERR_NULL;
+    for (int j = 0; j < 3; ++j) out->sin_bits[j] = kRopeSin[j];
+    for (int j = 0; j < 4; ++j) out->cos_bits[j] = kRopeCos[j];
     return PA_OK;
 }
 

@@ -61,7 +61,7 @@ extern "C" {
 /* HIP's stream handle (the same typedef as hip_runtime_api.h). */
 typedef struct ihipStream_t *hipStream_t;
 
-#define PA_ABI_VERSION 3
+#define PA_ABI_VERSION 4
 
 typedef enum {
     PA_OK = 0,
@@ -121,6 +121,14 @@ typedef struct {
     uint16_t a_bits[2], b_bits[2];
     int32_t order;             /* PA_ORDER_F32FMA_BF16                      */
 } pa_sigmoid_attn_program;
+
+/* The paired sine / cosine program of the rotary embedding (BF16 bit
+ * patterns, see poly_rope): sin(pi u) ~ u (a1 + a3 u^2 + a5 u^4),
+ * cos(pi u) ~ b0 + b2 u^2 + b4 u^4 + b6 u^6. */
+typedef struct {
+    uint16_t sin_bits[3];      /* a1, a3, a5     */
+    uint16_t cos_bits[4];      /* b0, b2, b4, b6 */
+} pa_rope_program;
 
 /* y[i] = f~(x[i]), i < n.  f = PA_SIGMOID (D3), PA_TANH (D4), PA_SILU (D3,
  * reusing the sigmoid polynomial), PA_GELU (D5).  x, y: n elements of
@@ -307,6 +315,49 @@ pa_status poly_sigmoid_attn_bwd(const void *q, const void *k, const void *v, con
                                 int32_t H, int32_t Hkv, int32_t S, int32_t D, int32_t causal,
                                 hipStream_t stream);
 
+/* ---- rotary position embedding (FP16 in/out) ---------------------------- */
+
+/* Rotary embedding of Q and K with the paired sine / cosine programs of the
+ * paper's Appendix B.2 (the fused RoPE experiment).  For frequency
+ * i < D / 2, w_i = base^(-2 i / D) and the host-side turn increment
+ * inc_i = round(w_i 2^32 / (2 pi)) (a Q0.32 fraction of a turn); at position
+ * s (0 .. S - 1) the phase is (s inc_i) mod 2^32, its top 16 bits read as a
+ * signed integer v give the Q15 half-turn coordinate (angle pi v / 2^15), and
+ * u = RN16(v) 2^-15, w = RN16(u u),
+ *   sin = RN16(u RN16(fma(RN16(fma(a5, w, a3)), w, a1)))          (D5)
+ *   cos = RN16(fma(RN16(fma(RN16(fma(b6, w, b4)), w, b2)), w, b0)) (D6)
+ * with the coefficients of poly_rope_program, every step one packed FP16
+ * operation.  Each interleaved pair (x_{2i}, x_{2i+1}) of a head row turns by
+ * that angle: y0 = RN16(x0 cos - RN16(x1 sin)), y1 = RN16(x1 cos +
+ * RN16(x0 sin)).  q: [B, S, Hq, D], k: [B, S, Hkv, D] FP16 in; q_out:
+ * [B, Hq, S, D], k_out: [B, Hkv, S, D] FP16 out (transposed, as the
+ * appendix's fused kernel writes them).  D a multiple of 8, 8 <= D <= 512;
+ * base finite and >= 1.  All pointers device memory, 16-byte aligned, the
+ * outputs overlapping no input.  Errors: PA_ERR_NULL, PA_ERR_ALIGN,
+ * PA_ERR_SHAPE, PA_ERR_OVERLAP, PA_ERR_LAUNCH. */
+pa_status poly_rope(const void *q, const void *k, void *q_out, void *k_out, int32_t B, int32_t S,
+                    int32_t Hq, int32_t Hkv, int32_t D, double base, hipStream_t stream);
+
+/* The same with accurate FP32 sinf / cosf of the same angle (RN32(pi / 2^15)
+ * times v), rounded to FP16, computed on the fly (the appendix's native
+ * on-the-fly variant; arguments and errors as poly_rope). */
+pa_status native_rope(const void *q, const void *k, void *q_out, void *k_out, int32_t B, int32_t S,
+                      int32_t Hq, int32_t Hkv, int32_t D, double base, hipStream_t stream);
+
+/* The appendix's cached-table variant: table holds S * D / 2 words, word
+ * s * D / 2 + i = (cos, sin) of frequency i at position s as two FP16 values
+ * (cos in the low half), as pa_rope_table writes them; arguments and errors
+ * otherwise as poly_rope (table 16-byte aligned, not overlapping the
+ * outputs). */
+pa_status native_rope_table(const void *q, const void *k, void *q_out, void *k_out,
+                            const void *table, int32_t B, int32_t S, int32_t Hq, int32_t Hkv,
+                            int32_t D, hipStream_t stream);
+
+/* Writes the (cos, sin) table of native_rope_table: S * D / 2 words of
+ * caller-owned device memory (16-byte aligned), the values native_rope
+ * computes.  Errors: PA_ERR_NULL, PA_ERR_ALIGN, PA_ERR_SHAPE, PA_ERR_LAUNCH. */
+pa_status pa_rope_table(void *table, int32_t S, int32_t D, double base, hipStream_t stream);
+
 /* ---- matched comparators (same memory path, accurate FP32 math) -------- */
 
 /* The "native" paths every timing in the paper divides by (Table 1's caption
@@ -397,6 +448,11 @@ pa_status poly_program_info(int32_t f, int32_t deriv, int32_t t, pa_program *out
  * (r = 1 when x >= thr), derivative factor a_bits[r] + b_bits[r] x, and the
  * sequence length n it holds for.  Returns PA_ERR_NULL if out is NULL. */
 pa_status poly_sigmoid_attn_program(pa_sigmoid_attn_program *out);
+
+/* The paired sine / cosine program poly_rope evaluates (Appendix B.2; fitted
+ * like the other programs, section 3.2 and Eq. 8, with sin(pi) = 0,
+ * cos(0) = 1 and cos(pi) = -1 imposed).  Returns PA_ERR_NULL if out is NULL. */
+pa_status poly_rope_program(pa_rope_program *out);
 
 /* Bytes of caller-owned workspace an attention backward needs (softcap != 0
  * for the softcap backward, 0 for sigmoid); -1 for an invalid shape.  The

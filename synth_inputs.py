@@ -19,7 +19,10 @@ sections 4.2 and 4.3):
   cfg4  16,384 tokens routed top-8 over 64 experts (Zipf s = 1.1 popularity
         over a seeded permutation), expert-sorted rows [sum counts x 1408]
   cfg5  Q, K, V ~ N(0, 1) BF16 [1, 16, 8192, 128]
-Seeds: 1 = x / gate / Q, 2 = up / K, 3 = grad / dh / V, 4 = routing.
+  rope  Q [1, 4096, 32, 128], K [1, 4096, 8, 128] ~ N(0, 1) FP16 (Appendix
+        B.2's fused rotary embedding, Llama-3-8B-like heads)
+Seeds: 1 = x / gate / Q, 2 = up / K, 3 = grad / dh / V, 4 = routing,
+5 = attention dO, 9 / 10 = rotary Q / K.
 """
 from __future__ import annotations
 
@@ -116,6 +119,13 @@ def t_cfg2(n: int, device="cuda"):
     x = torch.clamp(t_normal(SEED_X, n, 3.0, device), -12.0, 12.0).to(torch.float16)
     g = t_normal(SEED_G, n, 1.0, device).to(torch.float16)
     return x, g
+
+
+def t_rope_inputs(B: int = 1, S: int = 4096, Hq: int = 32, Hkv: int = 8, D: int = 128, device="cuda"):
+    """Q [B, S, Hq, D] and K [B, S, Hkv, D] ~ N(0, 1) as float16 (seeds 9, 10)."""
+    q = t_normal(9, B * S * Hq * D, 1.0, device).to(torch.float16).view(B, S, Hq, D)
+    k = t_normal(10, B * S * Hkv * D, 1.0, device).to(torch.float16).view(B, S, Hkv, D)
+    return q, k
 
 
 def t_bf16(v):

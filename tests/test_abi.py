@@ -29,11 +29,11 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(pa):
     names = declared_functions()
-    assert len(names) == 28, names
+    assert len(names) == 33, names
     L = pa.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert L.pa_abi_version() == 3
+    assert L.pa_abi_version() == 4
 
 
 def test_program_table_matches_oracle(pa, orc):
@@ -191,3 +191,44 @@ def test_error_paths_attention(pa):
     assert wb(0, 1, 8, 2, 100, 128) == 4 * 2 * 8 * 100 * 128
     assert wb(1, 1, 3, 1, 5, 128) == 4 * (2 * 16 + 2 * 3 * 5 * 128)   # regions padded to 16 B
     assert wb(1, 1, 3, 2, 5, 128) == -1
+
+
+def test_rope_program_matches_oracle(pa, orc):
+    """The library's sine / cosine coefficients are the oracle's BF16-rounded
+    fit (Appendix B.2 forms, section 3.2 workflow) and the golden file's."""
+    rp = orc.rope_prog()
+    got = pa.rope_program()
+    assert got["sin_bits"] == [int(b) for b in rp.sin_c]
+    assert got["cos_bits"] == [int(b) for b in rp.cos_c]
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "rope_program.json")))
+    assert got["sin_bits"] == g["sin_bits"] and got["cos_bits"] == g["cos_bits"]
+    assert pa.lib().poly_rope_program(None) == 1
+
+
+def test_error_paths_rope(pa):
+    L = pa.lib()
+    big = 1 << 30
+    Q, K, QO, KO, T = (FAKE + i * big for i in range(5))
+    for f in (L.poly_rope, L.native_rope):
+        assert f(Q, K, QO, KO, 1, 4, 2, 1, 12, 10000.0, None) == 2        # D % 8
+        assert f(Q, K, QO, KO, 1, 4, 2, 1, 1024, 10000.0, None) == 2      # D > 512
+        assert f(Q, K, QO, KO, 1, 4, 2, 1, 128, 0.5, None) == 2           # base < 1
+        assert f(Q, K, QO, KO, 1, 4, 2, 1, 128, float("nan"), None) == 2
+        assert f(Q, K, QO, KO, -1, 4, 2, 1, 128, 10000.0, None) == 2
+        assert f(None, K, QO, KO, 1, 4, 2, 1, 128, 10000.0, None) == 1
+        assert f(Q, K, QO + 2, KO, 1, 4, 2, 1, 128, 10000.0, None) == 7   # 16-byte alignment
+        assert f(Q, K, Q, KO, 1, 4, 2, 1, 128, 10000.0, None) == 5        # in place
+        assert f(Q, K, QO, QO + 256, 1, 4, 2, 1, 128, 10000.0, None) == 5  # outputs overlap
+        assert f(Q, K, QO, KO, 1, 0, 2, 1, 128, 10000.0, None) == 0       # empty: no launch
+        assert f(Q, K, QO, KO, 1, 4, 0, 0, 128, 10000.0, None) == 0
+    t = L.native_rope_table
+    assert t(Q, K, QO, KO, None, 1, 4, 2, 1, 128, None) == 1
+    assert t(Q, K, QO, KO, T + 4, 1, 4, 2, 1, 128, None) == 7
+    assert t(Q, K, QO, KO, QO, 1, 4, 2, 1, 128, None) == 5
+    assert t(Q, K, QO, KO, T, 1, 0, 2, 1, 128, None) == 0
+    b = L.pa_rope_table
+    assert b(None, 4, 128, 10000.0, None) == 1
+    assert b(T + 4, 4, 128, 10000.0, None) == 7
+    assert b(T, 4, 100, 10000.0, None) == 2
+    assert b(T, 0, 128, 10000.0, None) == 0
+

@@ -25,8 +25,10 @@ def test_bench_quick_run_prints_its_line():
     comp = line["components"]
     for key in ("swiglu_dense_fwd", "swiglu_dense_bwd", "swiglu_routed_fwd", "swiglu_routed_bwd",
                 "softcap_attn_fwd", "softcap_attn_fwd_f16", "softcap_attn_exp2_cores",
-                "softcap_attn_bwd", "softcap_attn_bwd_f16", "sigmoid_attn_fwd", "sigmoid_attn_bwd"):
+                "softcap_attn_bwd", "softcap_attn_bwd_f16", "sigmoid_attn_fwd", "sigmoid_attn_bwd",
+                "rope_fused_4096x32x8x128"):
         assert key in comp, key
     assert set(comp["softcap_attn_exp2_cores"]) == {"d1", "pwl2", "d2", "d3"}
+    assert comp["rope_fused_4096x32x8x128"]["table_ms"] > 0
     assert line["detail_cfg1"]["elements"] == 4_194_304 + 65_536
     assert line["programs"]["sigmoid_fwd_d3"]["Lc"] == 5.28125
