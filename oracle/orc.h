@@ -22,7 +22,9 @@
  * against rounding-error bounds and the symmetry identities; attention rows
  * against a textbook FP64 attention, attention gradients against automatic
  * differentiation of textbook FP64 attention, the sigmoid-attention program
- * against sigma(s - ln n).  Parity unpinned: the selection of the
+ * against sigma(s - ln n); the rotary embedding against an independent
+ * least-squares solve, big-integer phases and an exact rational FP16 replay.
+ * Parity unpinned: the selection of the
  * GELU D5 program (Table 2's 1.06e-3 is not reached under any reading) and of
  * the tanh-derivative D4 program (no printed value).
  */

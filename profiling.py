@@ -9,6 +9,7 @@ and the kernel table of `bench.py --components-only --component-set main`
 (SwiGLU and attention at the configured shapes, one shape per kernel):
 
     python profiling.py --components DIR/comp_kernel_stats.csv --command "<command>"
+    python profiling.py --rope-components DIR/pages_kernel_stats.csv --command "<command>"
 
 and, from three PMC passes over the same components run, the attention
 kernels' MFMA busy, VALU issue and wait fractions:
@@ -124,6 +125,55 @@ def components(path, command, out):
               "S and PV; dq kernel: S, dP, dQ; dK/dV kernel: S, dP, dV, dK), 2 x 128 flop "
               "per causal score each."]
     with open(os.path.join(out, "attention_components.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+ROPE_VARIANTS = {"0": "packed-FP16 D5 sine / D6 cosine", "1": "accurate sinf / cosf on the fly",
+                 "2": "cached (cos, sin) table"}
+ROPE_BYTES = 2 * (32 + 8) * 4096 * 128 * 2      # Q and K of 1 x 4096 x 32 (8) x 128, in and out
+
+
+def rope_components(path, command, out, fetch=None, write=None, fetch_command="", write_command=""):
+    """Kernel trace summary of the rotary-embedding kernels (bench.py's pages
+    component set: 1 x 4096 x 32 query / 8 key heads x 128, FP16), with their
+    HBM traffic when FETCH_SIZE / WRITE_SIZE passes are given (scaled by the
+    factors profiles/traffic.json holds for the copy calibration)."""
+    import re
+    lines = ["# Rotary embedding kernels", "",
+             "Kernel trace of `bench.py --components-only --component-set pages` (the fused "
+             "rotary embedding of Q [1, 4096, 32, 128] and K [1, 4096, 8, 128] FP16 into the "
+             "transposed layouts; 83,886,080 bytes moved per launch):", "", "```", command, "```", "",
+             "| kernel | what | calls | mean us | GB/s | % of 8 TB/s |", "|---|---|---|---|---|---|"]
+    for r in sorted(csv.DictReader(open(path)), key=lambda r: r["Name"]):
+        m = re.search(r"k_rope<(\d)>", r["Name"])
+        if not m:
+            continue
+        avg = float(r["AverageNs"])
+        gbs = ROPE_BYTES / avg
+        lines.append(f"| `pa::k_rope<{m.group(1)}>` | {ROPE_VARIANTS[m.group(1)]} | {r['Calls']} | "
+                     f"{avg / 1e3:.2f} | {gbs:.0f} | {100 * gbs / 8000:.1f} |")
+    if fetch and write:
+        cal = json.load(open(os.path.join(out, "traffic.json")))["calibration"]
+        per = {}
+        for pth, key in ((fetch, "f"), (write, "w")):
+            acc = collections.defaultdict(list)
+            for r in csv.DictReader(open(pth)):
+                m = re.search(r"k_rope<(\d)>", r["Kernel_Name"])
+                if m:
+                    acc[m.group(1)].append(float(r["Counter_Value"]))
+            for k, v in acc.items():
+                per.setdefault(k, {})[key] = sum(v) / len(v)
+        lines += ["", "HBM traffic per launch (PMC FETCH_SIZE and WRITE_SIZE in separate runs, KiB "
+                  f"per dispatch scaled by the copy calibration: x{cal['fetch_factor']:.4f} and "
+                  f"x{cal['write_factor']:.4f}):", "", "```", fetch_command, write_command, "```", "",
+                  "| kernel | read B | written B | algorithmic B | ratio |", "|---|---|---|---|---|"]
+        for k in sorted(per):
+            rd = per[k].get("f", 0.0) * 1024 * cal["fetch_factor"]
+            wr = per[k].get("w", 0.0) * 1024 * cal["write_factor"]
+            lines.append(f"| `pa::k_rope<{k}>` | {rd:,.0f} | {wr:,.0f} | {ROPE_BYTES:,} | "
+                         f"{(rd + wr) / ROPE_BYTES:.4f} |")
+    with open(os.path.join(out, "rope_components.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
@@ -249,6 +299,7 @@ def attn_counters(paths, commands, out):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--components", default="")
+    ap.add_argument("--rope-components", default="")
     ap.add_argument("--attn-counters", nargs=6, default=None,
                     metavar=("CSV1", "CSV2", "CSV3", "COMMAND1", "COMMAND2", "COMMAND3"),
                     help="attention counter summary from three PMC passes")
@@ -271,6 +322,10 @@ def main():
         return
     if a.components:
         components(a.components, a.command, a.out)
+        return
+    if a.rope_components:
+        rope_components(a.rope_components, a.command, a.out, a.fetch, a.write, a.fetch_command,
+                        a.write_command)
         return
     import sys
     sys.path.insert(0, ROOT)
