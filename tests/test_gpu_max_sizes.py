@@ -1,5 +1,5 @@
-"""GPU parity beyond 2^32 elements: 64-bit indexing of the streaming and the
-SwiGLU kernels.
+"""GPU parity beyond 2^32 elements: 64-bit indexing of the streaming, the
+SwiGLU and the rotary-embedding kernels.
 
 Each input element is a hash of its own 64-bit index, so a kernel that
 computed an address from a wrapped 32-bit index would read a different
@@ -103,3 +103,32 @@ def test_swiglu_beyond_2_32(pa, orc):
     nan_r = (ref & 0x7FFF) > 0x7F80
     ok = (got == ref) | (nan_g & nan_r)
     assert bool(ok.all()), diff_report(got.ravel(), ref.ravel())
+
+
+def test_rope_beyond_2_32(pa, orc):
+    """Rotary embedding of Q [1, 2^21 + 3, 16, 128] (2^32 + 6,144 elements)
+    and K [1, 2^21 + 3, 4, 128]: positions around the 2^31 and 2^32 input
+    elements and the last one, every head (the outputs of heads >= 8 lie
+    beyond 2^31 in the transposed layout), compared with the oracle."""
+    S, Hq, Hkv, D = (1 << 21) + 3, 16, 4, 128
+    note(f"max size rope draw S={S}")
+    qt = hashed(S * Hq * D, MULT_X, torch.float16).view(1, S, Hq, D)
+    kt = hashed(S * Hkv * D, MULT_G, torch.float16).view(1, S, Hkv, D)
+    note("max size rope")
+    qo, ko = pa.poly_rope(qt, kt, 10000.0)
+    pos = np.unique(np.array([0, 1, (1 << 20) - 1, 1 << 20, (1 << 20) + 1, (1 << 21) - 1, 1 << 21,
+                              S - 1] + list(range(0, S, 262_147))))
+    pt = torch.from_numpy(pos).cuda()
+    rp = orc.rope_prog()
+    inc = orc.rope_inc(D, 10000.0)
+    for x, y, H in ((qt, qo, Hq), (kt, ko, Hkv)):
+        xs = to_bits(x[:, pt])                                   # [1, len, H, D]
+        got = to_bits(y[:, :, pt])                               # [1, H, len, D]
+        rows = xs.transpose(0, 2, 1, 3).reshape(-1, D)
+        ref = orc.rope_rows(rp, inc, rows, np.tile(pos, H).astype(np.int64)).reshape(got.shape)
+        nan_g = (got & 0x7FFF) > 0x7C00
+        nan_r = (ref & 0x7FFF) > 0x7C00
+        ok = (got == ref) | (nan_g & nan_r)
+        assert bool(ok.all()), f"{int((~ok).sum())} of {got.size} differ"
+    del qt, kt, qo, ko
+    free()
