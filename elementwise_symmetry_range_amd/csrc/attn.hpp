@@ -673,7 +673,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // pieces (or pair) the scheduler can interleave, filling the stalls
     // between dependent steps of one chain (the exp2 cores 1.035-1.05x and
     // the BF16 softcap 1.03-1.04x faster than with 16 slots, 4 slots no
-    // better; the FP16 softcap 1-2 % slower).  Outputs are bit-identical
+    // better; the FP16 softcap 1-2 % slower).  Reading the operands two or
+    // three slots ahead instead of one made the 16-slot layouts 1-2 % slower
+    // (more registers live across each MFMA).  Outputs are bit-identical
     // either way.
     constexpr int AT_SLOTS = (SOFTCAP && EXP == 0 && MODE != AM_SOFTCAP_POLY_BF16) ? 16 : 8, AT_AHEAD = 1;
     auto slotted = [&](f32x16 &sn, f32x16 &scur, bf16x8 (&pc)[2], const bf16x8 (&pp)[2],
