@@ -112,6 +112,8 @@ def lib() -> C.CDLL:
         L.pa_status_str.restype = C.c_char_p
         L.pa_attn_bwd_workspace_bytes.argtypes = [i32] * 6
         L.pa_attn_bwd_workspace_bytes.restype = C.c_int64
+        L.pa_attn_bwd_ds_limit.argtypes = [C.c_int64]
+        L.pa_attn_bwd_ds_limit.restype = C.c_int64
         L.pa_attn_bwd_static_scratch_bytes.argtypes = []
         L.pa_attn_bwd_static_scratch_bytes.restype = C.c_int64
         L.pa_abi_version.argtypes = []

@@ -19,7 +19,11 @@
 //   dQ = dS K / sqrt(D),  dK = dS^T Q / sqrt(D) (summed over the query heads
 //   that share a key/value head).
 //
-// Two kernels, no atomics:
+// Two forms, no atomics, the same dQ, dK and dV bits.  With the dS blocks
+// stored (while they fit the workspace limit): k_attn_bwd_rows (Delta and
+// -lse log2(e) per row), k_attn_bwd_dkdv, which also stores the BF16 dS it
+// forms (2 KiB per 32 x 32 block), and k_attn_bwd_dq_ds, dQ^T += K^T dS^T
+// over the stored blocks, so the transform runs once.  Without them:
 //   k_attn_bwd_dq    one workgroup per 128 queries of one head (4 waves x 32
 //                    queries, lane = query as in the forward).  It computes
 //                    Delta for its rows first (softcap) and stores it, with
@@ -38,8 +42,9 @@
 //                    transform, dV^T += dO^T P and dK^T += Q^T dS with dO^T
 //                    and Q^T read transposed from the tiles.
 // Both run after the forward has written O and the LSE; dkdv after dq (it
-// reads Delta).  Every MFMA is v_mfma_f32_32x32x16_bf16 with the operand
-// layouts described in attn.hpp; P and dS are rounded to BF16 for the MFMA.
+// reads Delta); in the stored form dkdv after the row pass and dq_ds last.
+// Every MFMA is v_mfma_f32_32x32x16_bf16 with the operand layouts described
+// in attn.hpp; P and dS are rounded to BF16 for the MFMA.
 #pragma once
 #include <type_traits>
 
@@ -53,6 +58,8 @@ struct AttnBwdArgs {
     float *delta;          // softcap: workspace, Delta per query row
     float *nlse;           // softcap: workspace, -lse * log2(e) per query row
     float *part;           // grouped query heads: FP32 dK, dV partials per query head
+    uint16_t *dsb;         // BF16 dS blocks the dK/dV kernel stores for dQ, or nullptr
+    int32_t nqb;           // 32-row blocks per head, ceil(S / 32)
     uint16_t *dq, *dk, *dv;
     int32_t S, H, G;       // G = H / Hkv
     int32_t causal;
@@ -139,6 +146,34 @@ __device__ __forceinline__ void bwd_pair(const AttnBwdArgs &a, float s0, float s
         ds0 = dp0 * (p0 * (1.0f - p0));
         ds1 = dp1 * (p1 * (1.0f - p1));
         pw = pack_bf(p0, p1);
+    }
+}
+
+// Delta_i = dO_i . O_i and -lse_i log2(e) of every query row, for the dK/dV
+// kernel when dQ is formed from stored dS blocks: the dQ kernel's arithmetic
+// (the same FP32 FMAs in the same order, the halves summed by one add), one
+// wave per 32 rows, lane = row and half h of each 16-column chunk.
+__global__ __launch_bounds__(256) void k_attn_bwd_rows(AttnBwdArgs a, int64_t rows)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int col = lane & 31, h = lane >> 5;
+    const int64_t r = ((int64_t)blockIdx.x * 4 + wave) * 32 + col;
+    const bool valid = r < rows;
+    float acc = 0.0f;
+    if (valid) {
+        const uint16_t *orow = a.o + r * AT_D, *drow = a.dout + r * AT_D;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            const bf16x8 dv = ld_bf16x8(drow + ks * 16 + h * 8);
+            const bf16x8 ov = ld_bf16x8(orow + ks * 16 + h * 8);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc = fmaf((float)dv[e], (float)ov[e], acc);
+        }
+    }
+    const float dl = acc + __shfl_xor(acc, 32);
+    if (valid && h == 0) {
+        a.delta[r] = dl;
+        a.nlse[r] = -a.lse[r] * AT_LOG2E;
     }
 }
 
@@ -393,11 +428,24 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     };
 
     load(0, std::integral_constant<int, 0>{});
+    // the dS block of a tile is stored at the start of the next one, after
+    // its wait: that wait counts stores too, and a store issued at the end of
+    // a tile would hold it for the store's whole latency
+    u32x4 pend0 = {}, pend1 = {};
+    uint16_t *pend = nullptr;
+    auto flush = [&]() __attribute__((always_inline)) {
+        if (pend) {
+            __builtin_nontemporal_store(pend0, (u32x4 *)pend);
+            __builtin_nontemporal_store(pend1, (u32x4 *)(pend + 8));
+            pend = nullptr;
+        }
+    };
     auto tile = [&](int t, auto bufc) __attribute__((always_inline)) {
         constexpr int buf = decltype(bufc)::value;
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         if (t + 1 < ntile) load(t + 1, std::integral_constant<int, buf ^ 1>{});
+        flush();
         const int r0 = qstart + (t % nqt) * AT_BQ + qh * 32;   // this wave's first row
         if (a.causal && r0 + 31 < k0) return;   // every row of the half precedes these keys
         if (k0 >= S || r0 >= S) return;
@@ -405,7 +453,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const uint16_t *Db = buf ? Ds1 : Ds0;
         const float *Lb = buf ? Ls1 : Ls0;
         const float *Eb = buf ? Es1 : Es0;
-        const bool need_mask = (a.causal && r0 < k0 + 31) || r0 + 32 > S;
+        // keys past S are masked too: their dS entries are stored for dQ
+        const bool need_mask = (a.causal && r0 < k0 + 31) || r0 + 32 > S || k0 + 32 > S;
         // the lane's byte offsets (per tile, so the compiler does not hold
         // every derived address for the whole loop)
         uint32_t bq = bq0, bkv = bkv0, btr = btr0;
@@ -464,8 +513,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             uint32_t dk2 = pack_bf(d0, d1);
             if constexpr (MASKED) {
                 const int q = r0 + j * 8 + h * 4 + i;
-                const bool vis0 = q < S && (!a.causal || q >= my_k);
-                const bool vis1 = q + 1 < S && (!a.causal || q + 1 >= my_k);
+                const bool vis0 = valid && q < S && (!a.causal || q >= my_k);
+                const bool vis1 = valid && q + 1 < S && (!a.causal || q + 1 >= my_k);
                 const uint32_t keep = (vis0 ? 0x0000FFFFu : 0u) | (vis1 ? 0xFFFF0000u : 0u);
                 pk &= keep;
                 dk2 &= keep;
@@ -481,6 +530,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         // db is the chunk offset XOR (db << 6) and step f adds 8 rows, i.e.
         // XOR (1 << 5) and + 2048 bytes.  The transform of fragment 1 runs
         // one pair per slot beside the MFMAs of fragment 0.
+        // this wave's 32 x 32 dS block for dQ: block (r0 / 32, k0 / 32) of
+        // the head, 2 KiB in lane order (lane: key my_k, dw4[0] then dw4[1])
+        uint16_t *dsp = nullptr;
+        if (a.dsb)
+            dsp = a.dsb + ((head_of(t) * a.nqb + r0 / 32) * a.nqb + k0 / 32) * 1024 + lane * 16;
         bf16x8 oa[AH + 1], qa[AH + 1];
         auto ld = [&](auto nc) __attribute__((always_inline)) {
             constexpr int n = decltype(nc)::value, f = n >> 2, db = n & 3, b = n % (AH + 1);
@@ -521,11 +575,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         };
         if (need_mask) run(std::true_type{});
         else run(std::false_type{});
+        if (dsp) {
+            pend0 = dw4[0];
+            pend1 = dw4[1];
+            pend = dsp;
+        }
     };
     for (int t = 0; t < ntile; t += 2) {
         tile(t, std::integral_constant<int, 0>{});
         if (t + 1 < ntile) tile(t + 1, std::integral_constant<int, 1>{});
     }
+    flush();
 
     // half 1 hands its partials to half 0 through LDS (16 KB per array per
     // key group: the Q / dO buffers take dK, K / V take dV)
@@ -590,6 +650,165 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             w.x = pack_bf(dv[db][j * 4 + 0], dv[db][j * 4 + 1]);
             w.y = pack_bf(dv[db][j * 4 + 2], dv[db][j * 4 + 3]);
             *(u32x2 *)(vrow + d) = w;
+        }
+    }
+}
+
+// dQ from the dS blocks the dK/dV kernel stored: the dQ kernel's workgroups,
+// key tiles and products (dQ^T += K^T dS^T, the same operands in the same
+// order, so the same dQ) with dS^T read from LDS instead of recomputed.
+// The kernel streams 2 KiB of dS per 32 x 32 block, so it is bound by how
+// many bytes it keeps in flight: both operands come through registers (K
+// loaded one tile ahead, dS two tiles ahead) and are written to LDS at the
+// start of their tile, one barrier per tile, 48 KiB of LDS per workgroup.
+// (Loading both with global-to-LDS loads into double buffers measured the
+// same, about 4.4 TB/s of dS at 1 x 16 x 8192 causal.)  A wave's two 32 x 32 blocks of a
+// 64-key tile are stored in the dK/dV kernel's lane order (lane (key c,
+// half h') holds queries 8 f + 4 h' + i and 16 further on in dword group
+// f); each B operand (lane: query q, keys 16 jj + 4 h + r and 8 further on)
+// is two transposed reads: in a 16-lane group, lane m addresses the four
+// consecutive queries 4 (m % 4) + 16 (g16 % 2) .. + 3 of key row
+// 16 jj + 4 h + m / 4 (+ 8), so that lane j receives query j + 16 (g16 % 2)
+// of the four keys.  Causal blocks above the diagonal are neither stored nor
+// multiplied (their dS is zero); their loads read a stored block instead,
+// as do the loads past the last tile, so that every tile issues the same
+// loads.
+__global__ __launch_bounds__(256) void k_attn_bwd_dq_ds(AttnBwdArgs a)
+{
+    __shared__ __attribute__((aligned(16))) uint16_t Ks0[AT_TILE], Ks1[AT_TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t Dl[4][2048];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int col = lane & 31, h = lane >> 5;
+    const int g16 = lane >> 4, i16 = lane & 15;
+    const int S = a.S, nqb = a.nqb;
+    const int ntq = (S + AT_BM - 1) / AT_BM;
+    const int nbh = (int)(gridDim.x / (unsigned)ntq);
+    const int qrank = (int)blockIdx.x / nbh;
+    const int bh = (int)blockIdx.x - qrank * nbh;
+    const int qt = a.causal ? ntq - 1 - qrank : qrank;
+    const int64_t qbase = (int64_t)bh * S * AT_D;
+    const int64_t kvbase = (int64_t)(bh / a.G) * S * AT_D;
+    const uint16_t *K = a.k + kvbase;
+    const int q0 = qt * AT_BM + wave * 32;
+    const int qb = q0 / 32;
+    const int my_q = q0 + col;
+    const bool valid = my_q < S;
+    const int qbc = qb < nqb ? qb : nqb - 1;
+    const int kbmax = a.causal ? qbc : nqb - 1;   // last stored block of the row
+    const uint16_t *dsrow = a.dsb + ((int64_t)bh * nqb + qbc) * nqb * 1024 + lane * 16;
+    auto has_block = [&](int kb) { return q0 < S && kb <= kbmax; };
+
+    const int kend = a.causal ? (qt * AT_BM + AT_BM < S ? qt * AT_BM + AT_BM : S) : S;
+    const int nkt = (kend + AT_BN - 1) / AT_BN;
+
+    // K tile kt (clamped to the last): thread tid holds chunk idx % 16 of
+    // row idx / 16 for idx = tid + 256 i (rows past S repeat row S - 1)
+    auto load_k = [&](int kt, u32x4 (&r)[4]) __attribute__((always_inline)) {
+        kt = kt < nkt ? kt : nkt - 1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int idx = tid + 256 * i, row = idx >> 4, c = idx & 15;
+            int g = kt * AT_BN + row;
+            g = g < S ? g : S - 1;
+            r[i] = *(const u32x4 *)(K + (int64_t)g * AT_D + c * 8);
+        }
+    };
+    auto store_k = [&](uint16_t *lds, const u32x4 (&r)[4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int idx = tid + 256 * i, row = idx >> 4, c = idx & 15;
+            *(u32x4 *)(lds + row * AT_D + swz(row, c) * 8) = r[i];
+        }
+    };
+    // the lane's 32 bytes of this wave's blocks 2 kt and 2 kt + 1 (a stored
+    // block in their place where they do not exist)
+    auto load_d = [&](int kt, u32x4 (&r)[4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            int kb = kt * 2 + b;
+            kb = kb <= kbmax ? kb : kbmax;
+            const uint16_t *p = dsrow + (int64_t)kb * 1024;
+            r[2 * b] = *(const u32x4 *)p;
+            r[2 * b + 1] = *(const u32x4 *)(p + 8);
+        }
+    };
+
+    // byte offset of the lane's transposed read in a block, key row 0
+    const int u = i16 & 3;
+    const uint32_t tr0 = (uint32_t)((32 * (u & 1)) * 32 + ((u >> 1) * 8 + (g16 & 1) * 4) * 2) +
+                         (uint32_t)(h * 4 + (i16 >> 2)) * 32u;
+    uint16_t *dl = Dl[wave];
+
+    f32x16 dq[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db) dq[db] = f32x16{};
+
+    // tiles held in registers (measured on MI355X: 1-3 K tiles and 1-3 dS
+    // tiles within 2 %, more registers slower)
+    constexpr int KD = 1, DD = 2;
+    u32x4 kr[KD][4], dr[DD][4];
+#pragma unroll
+    for (int j = 0; j < KD; ++j) load_k(j, kr[j]);
+#pragma unroll
+    for (int j = 0; j < DD; ++j) load_d(j, dr[j]);
+    auto tile = [&](int kt, auto bufc) __attribute__((always_inline)) {
+        constexpr int buf = decltype(bufc)::value;
+        uint16_t *Kb = buf ? Ks1 : Ks0;
+        store_k(Kb, kr[0]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *(u32x4 *)(dl + (i >> 1) * 1024 + lane * 16 + (i & 1) * 8) = dr[0][i];
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j + 1 < KD; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) kr[j][i] = kr[j + 1][i];
+        load_k(kt + KD, kr[KD - 1]);
+#pragma unroll
+        for (int j = 0; j + 1 < DD; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dr[j][i] = dr[j + 1][i];
+        load_d(kt + DD, dr[DD - 1]);
+        const int key0 = kt * AT_BN;
+        if (a.causal && key0 > q0 + 31) return;
+        if (q0 >= S) return;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            if (!has_block(kt * 2 + kb)) continue;
+            const char *blk = (const char *)dl + kb * 2048;
+            bf16x8 dsf[2];
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                const u32x2 lo = ds_read_tr16((const uint16_t *)(blk + tr0 + jj * 16 * 32));
+                const u32x2 hi = ds_read_tr16((const uint16_t *)(blk + tr0 + (jj * 16 + 8) * 32));
+                dsf[jj] = bc<bf16x8>(u32x4{lo.x, lo.y, hi.x, hi.y});
+            }
+#pragma unroll
+            for (int db = 0; db < 4; ++db) {
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj)
+                    dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_tr_a(Kb, kb * 2 + jj, db, g16, i16),
+                                                                     dsf[jj], dq[db], 0, 0, 0);
+            }
+        }
+    };
+    for (int kt = 0; kt < nkt; kt += 2) {
+        tile(kt, std::integral_constant<int, 0>{});
+        if (kt + 1 < nkt) tile(kt + 1, std::integral_constant<int, 1>{});
+    }
+
+    if (!valid) return;
+    uint16_t *row = a.dq + qbase + (int64_t)my_q * AT_D;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int d = db * 32 + j * 8 + h * 4;
+            u32x2 w;
+            w.x = pack_bf(dq[db][j * 4 + 0] * a.rsd, dq[db][j * 4 + 1] * a.rsd);
+            w.y = pack_bf(dq[db][j * 4 + 2] * a.rsd, dq[db][j * 4 + 3] * a.rsd);
+            *(u32x2 *)(row + d) = w;
         }
     }
 }

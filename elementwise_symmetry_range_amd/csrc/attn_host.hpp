@@ -1,5 +1,6 @@
 // attn_host.hpp -- argument validation and launches of the attention kernels.
 #pragma once
+#include <atomic>
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -176,7 +177,7 @@ inline void attn_fwd_launch(const AttnArgs &a, dim3 grid, hipStream_t stream)
 // softcap program only).
 inline pa_status attn_fwd(int mode, const void *q, const void *k, const void *v, void *o, float *lse,
                           int32_t B, int32_t H, int32_t Hkv, int32_t S, int32_t D, float cap,
-                          int32_t causal, hipStream_t stream, int exp2_core = 0)
+                          int32_t causal, hipStream_t stream, int exp2_core = 0, bool allow_ds = true)
 {
     if (exp2_core < 0 || exp2_core > 4 || (exp2_core && mode != AM_SOFTCAP_POLY_BF16)) return PA_ERR_FUNC;
     if (!q || !k || !v || !o) return PA_ERR_NULL;
@@ -245,15 +246,41 @@ inline pa_status attn_fwd(int mode, const void *q, const void *k, const void *v,
     return attn_launched();
 }
 
+// Bytes of the BF16 dS blocks of a backward: B H ceil(S/32)^2 blocks of
+// 32 x 32 (every block of the square, so the size does not depend on the
+// causal flag; a causal call writes and reads the lower triangle only).
+inline int64_t attn_bwd_ds_bytes(int32_t B, int32_t H, int32_t S)
+{
+    const int64_t nqb = ((int64_t)S + 31) / 32;
+    return (int64_t)B * H * nqb * nqb * 2048;
+}
+
+// The backward stores dS for dQ (dK/dV kernel, then a dQ product over the
+// stored blocks: the score transform runs once) when the blocks take at
+// most the process-wide limit (16 GiB unless pa_attn_bwd_ds_limit changes
+// it); above that the dQ kernel recomputes S, dP and the transform (twice
+// the transform, no quadratic storage).  Both give the same dQ, dK and dV.
+inline std::atomic<int64_t> &attn_ds_limit()
+{
+    static std::atomic<int64_t> limit{int64_t(16) << 30};
+    return limit;
+}
+inline bool attn_bwd_use_ds(int32_t B, int32_t H, int32_t S)
+{
+    return attn_bwd_ds_bytes(B, H, S) <= attn_ds_limit().load(std::memory_order_relaxed);
+}
+
 // Workspace of a backward call, in floats: Delta and -lse log2(e) per query
 // row (softcap; each region padded to 16 bytes), then, for grouped query
-// heads, FP32 dK and dV partials per query head.  0 when none is needed.
+// heads, FP32 dK and dV partials per query head, then (ds) the dS blocks.
+// 0 when none is needed.
 inline int64_t attn_bwd_ws_floats(bool softcap, int32_t B, int32_t H, int32_t Hkv, int32_t S,
-                                  int32_t D)
+                                  int32_t D, bool ds)
 {
     const int64_t rows = (int64_t)B * H * S;
     int64_t n = softcap ? 2 * ((rows + 3) / 4 * 4) : 0;
     if (Hkv > 0 && H > Hkv) n += 2 * rows * D;
+    if (ds) n += attn_bwd_ds_bytes(B, H, S) / 4;
     return n;
 }
 
@@ -262,25 +289,31 @@ inline void attn_bwd_launch(const AttnBwdArgs &a, int32_t B, int32_t H, int32_t 
                             hipStream_t stream)
 {
     const dim3 gq((unsigned)(((S + AT_BM - 1) / AT_BM) * (B * H)));
-    hipLaunchKernelGGL((k_attn_bwd_dq<MODE, EXP>), gq, dim3(256), 0, stream, a);
+    if (!a.dsb) {
+        hipLaunchKernelGGL((k_attn_bwd_dq<MODE, EXP>), gq, dim3(256), 0, stream, a);
+    } else if (am_softcap(MODE)) {
+        const int64_t rows = (int64_t)B * H * S;
+        hipLaunchKernelGGL(k_attn_bwd_rows, dim3((unsigned)((rows + 127) / 128)), dim3(256), 0, stream, a, rows);
+    }
     const int ntk = (S + AT_BK - 1) / AT_BK;
     if (H == Hkv) {
         hipLaunchKernelGGL((k_attn_bwd_dkdv<MODE, false, EXP>), dim3((unsigned)(ntk * B * Hkv)), dim3(512), 0,
                            stream, a);
-        return;
+    } else {
+        hipLaunchKernelGGL((k_attn_bwd_dkdv<MODE, true, EXP>), dim3((unsigned)(ntk * B * H)), dim3(512), 0,
+                           stream, a);
+        const int64_t n8 = (int64_t)B * Hkv * S * AT_D / 8;
+        hipLaunchKernelGGL(k_attn_bwd_reduce, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream, a, n8,
+                           (int64_t)S * AT_D);
     }
-    hipLaunchKernelGGL((k_attn_bwd_dkdv<MODE, true, EXP>), dim3((unsigned)(ntk * B * H)), dim3(512), 0, stream,
-                       a);
-    const int64_t n8 = (int64_t)B * Hkv * S * AT_D / 8;
-    hipLaunchKernelGGL(k_attn_bwd_reduce, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream, a, n8,
-                       (int64_t)S * AT_D);
+    if (a.dsb) hipLaunchKernelGGL(k_attn_bwd_dq_ds, gq, dim3(256), 0, stream, a);
 }
 
 // o, lse and ws are used by the softcap modes only.
 inline pa_status attn_bwd(int mode, const void *q, const void *k, const void *v, const void *o,
                           const void *dout, const float *lse, void *dq, void *dk, void *dv, float *ws,
                           int32_t B, int32_t H, int32_t Hkv, int32_t S, int32_t D, float cap,
-                          int32_t causal, hipStream_t stream, int exp2_core = 0)
+                          int32_t causal, hipStream_t stream, int exp2_core = 0, bool allow_ds = true)
 {
     if (exp2_core < 0 || exp2_core > 4 || (exp2_core && mode != AM_SOFTCAP_POLY_BF16)) return PA_ERR_FUNC;
     const bool softcap = am_softcap(mode);
@@ -288,7 +321,9 @@ inline pa_status attn_bwd(int mode, const void *q, const void *k, const void *v,
     if (softcap && (!o || !lse)) return PA_ERR_NULL;
     pa_status st = attn_shape(B, H, Hkv, S, D);
     if (st != PA_OK) return st;
-    const int64_t wsn = attn_bwd_ws_floats(softcap, B, H, Hkv, S, D);
+    // no workspace (allowed for sigmoid with H == Hkv): the recompute form
+    const bool ds = allow_ds && ws && attn_bwd_use_ds(B, H, S);
+    const int64_t wsn = attn_bwd_ws_floats(softcap, B, H, Hkv, S, D, ds);
     if (wsn > 0 && !ws) return PA_ERR_NULL;
     if (!aligned16({q, k, v, dout, dq, dk, dv, ws}) || (softcap && !aligned16({o})) ||
         ((uintptr_t)lse & 3u))
@@ -313,6 +348,8 @@ inline pa_status attn_bwd(int mode, const void *q, const void *k, const void *v,
     a.delta = softcap ? ws : nullptr;
     a.nlse = softcap ? ws + rows4 : nullptr;
     a.part = H > Hkv ? ws + (softcap ? 2 * rows4 : 0) : nullptr;
+    a.dsb = ds ? (uint16_t *)(ws + attn_bwd_ws_floats(softcap, B, H, Hkv, S, D, false)) : nullptr;
+    a.nqb = (S + 31) / 32;
     a.dq = (uint16_t *)dq;
     a.dk = (uint16_t *)dk;
     a.dv = (uint16_t *)dv;

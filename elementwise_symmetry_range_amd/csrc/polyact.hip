@@ -671,7 +671,13 @@ int64_t pa_attn_bwd_workspace_bytes(int32_t softcap, int32_t B, int32_t H, int32
                                     int32_t S, int32_t D)
 {
     if (attn_shape(B, H, Hkv, S, D) != PA_OK) return -1;
-    return 4 * attn_bwd_ws_floats(softcap != 0, B, H, Hkv, S, D);
+    return 4 * attn_bwd_ws_floats(softcap != 0, B, H, Hkv, S, D, attn_bwd_use_ds(B, H, S));
+}
+
+int64_t pa_attn_bwd_ds_limit(int64_t bytes)
+{
+    if (bytes < 0) return attn_ds_limit().load();
+    return attn_ds_limit().exchange(bytes);
 }
 
 pa_status poly_sigmoid_attn_program(pa_sigmoid_attn_program *out)
@@ -781,14 +787,14 @@ pa_status poly_softcap_attn_bwd_static(const void *q, const void *k, const void 
 {
     pa_status st = attn_shape(B, H, Hkv, S, D);
     if (st != PA_OK) return st;
-    const int64_t need = attn_bwd_ws_floats(true, B, H, Hkv, S, D);
+    const int64_t need = attn_bwd_ws_floats(true, B, H, Hkv, S, D, false);
     if (need > kStaticScratchFloats) return PA_ERR_SHAPE;
     if ((int64_t)B * H == 0 || S == 0) {
         return attn_bwd(AM_SOFTCAP_POLY_BF16, q, k, v, o, dout, lse, dq, dk, dv, nullptr, B, H, Hkv,
-                        S, D, cap, causal, stream);
+                        S, D, cap, causal, stream, 0, false);
     }
     float *ws = static_scratch(st);
     if (!ws) return st;
     return attn_bwd(AM_SOFTCAP_POLY_BF16, q, k, v, o, dout, lse, dq, dk, dv, ws, B, H, Hkv, S, D,
-                    cap, causal, stream);
+                    cap, causal, stream, 0, false);
 }

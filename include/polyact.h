@@ -61,7 +61,7 @@ extern "C" {
 /* HIP's stream handle (the same typedef as hip_runtime_api.h). */
 typedef struct ihipStream_t *hipStream_t;
 
-#define PA_ABI_VERSION 4
+#define PA_ABI_VERSION 5
 
 typedef enum {
     PA_OK = 0,
@@ -240,9 +240,12 @@ pa_status poly_softcap_attn_fwd_exp2(const void *q, const void *k, const void *v
  * rounded to BF16 for the MFMA.  workspace: caller-owned scratch, 16-byte
  * aligned, of pa_attn_bwd_workspace_bytes(1, B, H, Hkv, S, D) bytes: B * H * S
  * floats each for Delta and for -lse log2(e) (each region rounded up to 16
- * bytes) and, when H > Hkv, FP32 dK and dV partials of every query head
- * (summed per group by a final pass in a fixed order); contents on return
- * unspecified.
+ * bytes); when H > Hkv, FP32 dK and dV partials of every query head (summed
+ * per group by a final pass in a fixed order); and, while they fit the limit
+ * of pa_attn_bwd_ds_limit, the BF16 dS of every 32 x 32 block (B H
+ * ceil(S/32)^2 x 2 KiB), which the dK/dV kernel stores so that dQ is one
+ * product over them instead of a second pass of S, dP and the transform
+ * (the same dQ either way); contents on return unspecified.
  * Paper: Eq. 12 and section 5.2.2 (the differentiated D3 at the recomputed
  * scaled score), section 3.3 (differentiated-polynomial backward). */
 pa_status poly_softcap_attn_bwd(const void *q, const void *k, const void *v, const void *o,
@@ -307,8 +310,8 @@ pa_status poly_sigmoid_attn_fwd(const void *q, const void *k, const void *v, voi
  * dQ = dS K / sqrt(D), dK = dS^T Q / sqrt(D), with g the factored derivative
  * surrogate P~(x) (a + b x) of the same region and clamped x (BF16 per
  * stage).  Same length guard.  workspace: as for the softcap backward,
- * pa_attn_bwd_workspace_bytes(0, ...) bytes (none, and NULL allowed, when
- * H == Hkv).  Paper: section 3.4 (the coupled value / derivative
+ * pa_attn_bwd_workspace_bytes(0, ...) bytes; with H == Hkv NULL is allowed
+ * too and selects the recompute form, which needs none.  Paper: section 3.4 (the coupled value / derivative
  * evaluator), Appendix C (Listing 2). */
 pa_status poly_sigmoid_attn_bwd(const void *q, const void *k, const void *v, const void *dout,
                                 void *dq, void *dk, void *dv, float *workspace, int32_t B,
@@ -457,11 +460,22 @@ pa_status poly_rope_program(pa_rope_program *out);
 /* Bytes of caller-owned workspace an attention backward needs (softcap != 0
  * for the softcap backward, 0 for sigmoid); -1 for an invalid shape.  The
  * paper defines the gradients (Eq. 12, section 3.3), not their storage: the
- * workspace is this library's split of the backward into a dQ kernel and a
- * dK/dV kernel (the row terms Delta and -lse log2 e, and FP32 dK / dV partials
- * per query head when Hkv < H). */
+ * workspace is this library's split of the backward into kernels (the row
+ * terms Delta and -lse log2 e, FP32 dK / dV partials per query head when
+ * Hkv < H, and the stored dS blocks while B H ceil(S/32)^2 x 2 KiB is within
+ * pa_attn_bwd_ds_limit).  The size depends on the limit in force: size the
+ * workspace under the limit the call will see. */
 int64_t pa_attn_bwd_workspace_bytes(int32_t softcap, int32_t B, int32_t H, int32_t Hkv,
                                     int32_t S, int32_t D);
+
+/* The process-wide limit, in bytes, on the dS blocks an attention backward
+ * stores (default 16 GiB; 0 makes every backward recompute S, dP and the
+ * transform for dQ instead).  bytes >= 0 sets it and returns the previous
+ * value; bytes < 0 only returns it.  Results do not depend on it; the
+ * workspace size does, so a caller that raises it must size workspaces
+ * after the change (a workspace sized under a higher limit serves any lower
+ * one).  A storage choice of this library, not a passage of the paper. */
+int64_t pa_attn_bwd_ds_limit(int64_t bytes);
 
 /* Static description of a status code. */
 const char *pa_status_str(pa_status s);

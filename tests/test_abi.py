@@ -29,11 +29,11 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(pa):
     names = declared_functions()
-    assert len(names) == 33, names
+    assert len(names) == 34, names
     L = pa.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert L.pa_abi_version() == 4
+    assert L.pa_abi_version() == 5
 
 
 def test_program_table_matches_oracle(pa, orc):
@@ -186,11 +186,28 @@ def test_error_paths_attention(pa):
     assert sb(Q, K, V, DO, DQ, DK, DV, DQ, 1, 4, 2, 4096, 128, 1, None) == 5        # ws over dq
     assert L.native_sigmoid_attn_bwd(Q, K, V, DO, DQ, DK, DV, None, 1, 2, 2, 0, 128, 1, None) == 0
     wb = L.pa_attn_bwd_workspace_bytes
-    assert wb(0, 1, 8, 8, 4096, 128) == 0
-    assert wb(1, 1, 8, 8, 4095, 128) == 4 * 2 * 8 * 4095            # Delta, -lse log2(e)
-    assert wb(0, 1, 8, 2, 100, 128) == 4 * 2 * 8 * 100 * 128
-    assert wb(1, 1, 3, 1, 5, 128) == 4 * (2 * 16 + 2 * 3 * 5 * 128)   # regions padded to 16 B
+
+    def ds(B, H, S):      # BF16 dS blocks of 32 x 32, the whole square
+        return B * H * ((S + 31) // 32) ** 2 * 2048
+    assert wb(0, 1, 8, 8, 4096, 128) == ds(1, 8, 4096)
+    assert wb(1, 1, 8, 8, 4095, 128) == 4 * 2 * 8 * 4095 + ds(1, 8, 4095)   # Delta, -lse log2(e)
+    assert wb(0, 1, 8, 2, 100, 128) == 4 * 2 * 8 * 100 * 128 + ds(1, 8, 100)
+    assert wb(1, 1, 3, 1, 5, 128) == 4 * (2 * 16 + 2 * 3 * 5 * 128) + ds(1, 3, 5)   # regions padded to 16 B
     assert wb(1, 1, 3, 2, 5, 128) == -1
+    # above 16 GiB of dS blocks the backward recomputes instead of storing
+    assert ds(1, 32, 16384) == 16 << 30 and wb(1, 1, 32, 32, 16384, 128) == 4 * 2 * 32 * 16384 + (16 << 30)
+    assert wb(1, 1, 32, 32, 16385, 128) == 4 * 2 * 32 * 16385
+    assert wb(0, 2, 32, 32, 16384, 128) == 0
+    # the limit: queried, lowered to 0 (recompute form, no dS blocks), restored
+    lim = L.pa_attn_bwd_ds_limit(-1)
+    assert lim == 16 << 30
+    try:
+        assert L.pa_attn_bwd_ds_limit(0) == lim
+        assert wb(1, 1, 8, 8, 4095, 128) == 4 * 2 * 8 * 4095
+        assert wb(0, 1, 8, 8, 4096, 128) == 0
+    finally:
+        assert L.pa_attn_bwd_ds_limit(lim) == 0
+    assert L.pa_attn_bwd_ds_limit(-5) == lim
 
 
 def test_rope_program_matches_oracle(pa, orc):
