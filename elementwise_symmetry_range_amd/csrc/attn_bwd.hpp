@@ -436,7 +436,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     auto flush = [&]() __attribute__((always_inline)) {
         if (pend) {
             __builtin_nontemporal_store(pend0, (u32x4 *)pend);
-            __builtin_nontemporal_store(pend1, (u32x4 *)(pend + 8));
+            __builtin_nontemporal_store(pend1, (u32x4 *)(pend + 512));
             pend = nullptr;
         }
     };
@@ -531,10 +531,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         // XOR (1 << 5) and + 2048 bytes.  The transform of fragment 1 runs
         // one pair per slot beside the MFMAs of fragment 0.
         // this wave's 32 x 32 dS block for dQ: block (r0 / 32, k0 / 32) of
-        // the head, 2 KiB in lane order (lane: key my_k, dw4[0] then dw4[1])
+        // the head, 2 KiB: dw4[0] of lanes 0..63, then dw4[1] (16 bytes per
+        // lane, so each store fills 1 KiB)
         uint16_t *dsp = nullptr;
         if (a.dsb)
-            dsp = a.dsb + ((head_of(t) * a.nqb + r0 / 32) * a.nqb + k0 / 32) * 1024 + lane * 16;
+            dsp = a.dsb + ((head_of(t) * a.nqb + r0 / 32) * a.nqb + k0 / 32) * 1024 + lane * 8;
         bf16x8 oa[AH + 1], qa[AH + 1];
         auto ld = [&](auto nc) __attribute__((always_inline)) {
             constexpr int n = decltype(nc)::value, f = n >> 2, db = n & 3, b = n % (AH + 1);
@@ -662,11 +663,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // loaded one tile ahead, dS two tiles ahead) and are written to LDS at the
 // start of their tile, one barrier per tile, 48 KiB of LDS per workgroup.
 // (Loading both with global-to-LDS loads into double buffers measured the
-// same, about 4.4 TB/s of dS at 1 x 16 x 8192 causal.)  A wave's two 32 x 32 blocks of a
-// 64-key tile are stored in the dK/dV kernel's lane order (lane (key c,
-// half h') holds queries 8 f + 4 h' + i and 16 further on in dword group
-// f); each B operand (lane: query q, keys 16 jj + 4 h + r and 8 further on)
-// is two transposed reads: in a 16-lane group, lane m addresses the four
+// same.)  A wave's two 32 x 32 blocks of a 64-key tile are stored as the
+// dK/dV kernel's fragments: 1 KiB per dword group f, 16 bytes per lane,
+// lane (key c, half h') holding queries 8 f + 4 h' + i and 16 further on.
+// Each B operand (lane: query q, keys 16 jj + 4 h + r and 8 further on) is
+// two transposed reads: in a 16-lane group, lane m addresses the four
 // consecutive queries 4 (m % 4) + 16 (g16 % 2) .. + 3 of key row
 // 16 jj + 4 h + m / 4 (+ 8), so that lane j receives query j + 16 (g16 % 2)
 // of the four keys.  Causal blocks above the diagonal are neither stored nor
@@ -697,7 +698,7 @@ __global__ __launch_bounds__(256) void k_attn_bwd_dq_ds(AttnBwdArgs a)
     const bool valid = my_q < S;
     const int qbc = qb < nqb ? qb : nqb - 1;
     const int kbmax = a.causal ? qbc : nqb - 1;   // last stored block of the row
-    const uint16_t *dsrow = a.dsb + ((int64_t)bh * nqb + qbc) * nqb * 1024 + lane * 16;
+    const uint16_t *dsrow = a.dsb + ((int64_t)bh * nqb + qbc) * nqb * 1024 + lane * 8;
     auto has_block = [&](int kb) { return q0 < S && kb <= kbmax; };
 
     const int kend = a.causal ? (qt * AT_BM + AT_BM < S ? qt * AT_BM + AT_BM : S) : S;
@@ -722,8 +723,8 @@ __global__ __launch_bounds__(256) void k_attn_bwd_dq_ds(AttnBwdArgs a)
             *(u32x4 *)(lds + row * AT_D + swz(row, c) * 8) = r[i];
         }
     };
-    // the lane's 32 bytes of this wave's blocks 2 kt and 2 kt + 1 (a stored
-    // block in their place where they do not exist)
+    // the lane's 2 x 16 bytes of this wave's blocks 2 kt and 2 kt + 1 (a
+    // stored block in their place where they do not exist)
     auto load_d = [&](int kt, u32x4 (&r)[4]) __attribute__((always_inline)) {
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
@@ -731,14 +732,15 @@ __global__ __launch_bounds__(256) void k_attn_bwd_dq_ds(AttnBwdArgs a)
             kb = kb <= kbmax ? kb : kbmax;
             const uint16_t *p = dsrow + (int64_t)kb * 1024;
             r[2 * b] = *(const u32x4 *)p;
-            r[2 * b + 1] = *(const u32x4 *)(p + 8);
+            r[2 * b + 1] = *(const u32x4 *)(p + 512);
         }
     };
 
-    // byte offset of the lane's transposed read in a block, key row 0
+    // byte offset of the lane's transposed read in a block, key row 0:
+    // dword group (u / 2), stored lane (key + 32 (u % 2)), half g16 % 2
     const int u = i16 & 3;
-    const uint32_t tr0 = (uint32_t)((32 * (u & 1)) * 32 + ((u >> 1) * 8 + (g16 & 1) * 4) * 2) +
-                         (uint32_t)(h * 4 + (i16 >> 2)) * 32u;
+    const uint32_t tr0 = (uint32_t)((u >> 1) * 1024 + (32 * (u & 1)) * 16 + (g16 & 1) * 8) +
+                         (uint32_t)(h * 4 + (i16 >> 2)) * 16u;
     uint16_t *dl = Dl[wave];
 
     f32x16 dq[4];
@@ -758,7 +760,7 @@ __global__ __launch_bounds__(256) void k_attn_bwd_dq_ds(AttnBwdArgs a)
         uint16_t *Kb = buf ? Ks1 : Ks0;
         store_k(Kb, kr[0]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) *(u32x4 *)(dl + (i >> 1) * 1024 + lane * 16 + (i & 1) * 8) = dr[0][i];
+        for (int i = 0; i < 4; ++i) *(u32x4 *)(dl + (i >> 1) * 1024 + (i & 1) * 512 + lane * 8) = dr[0][i];
         __syncthreads();
 #pragma unroll
         for (int j = 0; j + 1 < KD; ++j)
@@ -780,8 +782,8 @@ __global__ __launch_bounds__(256) void k_attn_bwd_dq_ds(AttnBwdArgs a)
             bf16x8 dsf[2];
 #pragma unroll
             for (int jj = 0; jj < 2; ++jj) {
-                const u32x2 lo = ds_read_tr16((const uint16_t *)(blk + tr0 + jj * 16 * 32));
-                const u32x2 hi = ds_read_tr16((const uint16_t *)(blk + tr0 + (jj * 16 + 8) * 32));
+                const u32x2 lo = ds_read_tr16((const uint16_t *)(blk + tr0 + jj * 16 * 16));
+                const u32x2 hi = ds_read_tr16((const uint16_t *)(blk + tr0 + (jj * 16 + 8) * 16));
                 dsf[jj] = bc<bf16x8>(u32x4{lo.x, lo.y, hi.x, hi.y});
             }
 #pragma unroll
