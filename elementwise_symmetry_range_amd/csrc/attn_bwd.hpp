@@ -336,6 +336,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
 }
 
+// Index of the stored dS block (query block qb, key block kb) of head bh:
+// four query blocks (a dQ workgroup's 128 rows) side by side per key block,
+// so that a dQ workgroup's two key blocks are 16 KiB in one piece and a
+// dK/dV workgroup's tile is four pieces of 4 KiB.  ceil(nqb / 4) groups of
+// four rows per head (the last group padded).
+__device__ __forceinline__ int64_t ds_block(int64_t bh, int qb, int kb, int nqb)
+{
+    const int64_t nqg = (nqb + 3) / 4;
+    return ((bh * nqg + (qb >> 2)) * nqb + kb) * 4 + (qb & 3);
+}
+
 constexpr int AT_BK = 128;   // keys per dK/dV workgroup
 constexpr int AT_BQ = 64;    // query rows per streamed tile
 
@@ -531,11 +542,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         // XOR (1 << 5) and + 2048 bytes.  The transform of fragment 1 runs
         // one pair per slot beside the MFMAs of fragment 0.
         // this wave's 32 x 32 dS block for dQ: block (r0 / 32, k0 / 32) of
-        // the head, 2 KiB: dw4[0] of lanes 0..63, then dw4[1] (16 bytes per
-        // lane, so each store fills 1 KiB)
+        // the head, at ds_block; 2 KiB: dw4[0] of lanes 0..63, then dw4[1]
+        // (16 bytes per lane, so each store fills 1 KiB)
         uint16_t *dsp = nullptr;
-        if (a.dsb)
-            dsp = a.dsb + ((head_of(t) * a.nqb + r0 / 32) * a.nqb + k0 / 32) * 1024 + lane * 8;
+        if (a.dsb) dsp = a.dsb + ds_block(head_of(t), r0 / 32, k0 / 32, a.nqb) * 1024 + lane * 8;
         bf16x8 oa[AH + 1], qa[AH + 1];
         auto ld = [&](auto nc) __attribute__((always_inline)) {
             constexpr int n = decltype(nc)::value, f = n >> 2, db = n & 3, b = n % (AH + 1);
@@ -663,7 +673,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // loaded one tile ahead, dS two tiles ahead) and are written to LDS at the
 // start of their tile, one barrier per tile, 48 KiB of LDS per workgroup.
 // (Loading both with global-to-LDS loads into double buffers measured the
-// same.)  A wave's two 32 x 32 blocks of a 64-key tile are stored as the
+// same.)  The workgroup's dS of a tile is 16 KiB in one piece (ds_block).
+// A wave's two 32 x 32 blocks of a 64-key tile are stored as the
 // dK/dV kernel's fragments: 1 KiB per dword group f, 16 bytes per lane,
 // lane (key c, half h') holding queries 8 f + 4 h' + i and 16 further on.
 // Each B operand (lane: query q, keys 16 jj + 4 h + r and 8 further on) is
@@ -674,17 +685,20 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // multiplied (their dS is zero); their loads read a stored block instead,
 // as do the loads past the last tile, so that every tile issues the same
 // loads.
-__global__ __launch_bounds__(256) void k_attn_bwd_dq_ds(AttnBwdArgs a)
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void k_attn_bwd_dq_ds(AttnBwdArgs a)
 {
+    constexpr int QBM = NW * 32;              // queries per workgroup
+    constexpr int CH = AT_TILE / 8 / (NW * 64);   // 16-byte K chunks per thread
     __shared__ __attribute__((aligned(16))) uint16_t Ks0[AT_TILE], Ks1[AT_TILE];
-    __shared__ __attribute__((aligned(16))) uint16_t Dl[4][2048];
+    __shared__ __attribute__((aligned(16))) uint16_t Dl[NW][2048];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int col = lane & 31, h = lane >> 5;
     const int g16 = lane >> 4, i16 = lane & 15;
     const int S = a.S, nqb = a.nqb;
-    const int ntq = (S + AT_BM - 1) / AT_BM;
+    const int ntq = (S + QBM - 1) / QBM;
     const int nbh = (int)(gridDim.x / (unsigned)ntq);
     const int qrank = (int)blockIdx.x / nbh;
     const int bh = (int)blockIdx.x - qrank * nbh;
@@ -692,34 +706,34 @@ __global__ __launch_bounds__(256) void k_attn_bwd_dq_ds(AttnBwdArgs a)
     const int64_t qbase = (int64_t)bh * S * AT_D;
     const int64_t kvbase = (int64_t)(bh / a.G) * S * AT_D;
     const uint16_t *K = a.k + kvbase;
-    const int q0 = qt * AT_BM + wave * 32;
+    const int q0 = qt * QBM + wave * 32;
     const int qb = q0 / 32;
     const int my_q = q0 + col;
     const bool valid = my_q < S;
     const int qbc = qb < nqb ? qb : nqb - 1;
     const int kbmax = a.causal ? qbc : nqb - 1;   // last stored block of the row
-    const uint16_t *dsrow = a.dsb + ((int64_t)bh * nqb + qbc) * nqb * 1024 + lane * 8;
+    const uint16_t *dsrow = a.dsb + ds_block(bh, qb, 0, nqb) * 1024 + lane * 8;   // key block 0
     auto has_block = [&](int kb) { return q0 < S && kb <= kbmax; };
 
-    const int kend = a.causal ? (qt * AT_BM + AT_BM < S ? qt * AT_BM + AT_BM : S) : S;
+    const int kend = a.causal ? (qt * QBM + QBM < S ? qt * QBM + QBM : S) : S;
     const int nkt = (kend + AT_BN - 1) / AT_BN;
 
     // K tile kt (clamped to the last): thread tid holds chunk idx % 16 of
-    // row idx / 16 for idx = tid + 256 i (rows past S repeat row S - 1)
-    auto load_k = [&](int kt, u32x4 (&r)[4]) __attribute__((always_inline)) {
+    // row idx / 16 for idx = tid + 64 NW i (rows past S repeat row S - 1)
+    auto load_k = [&](int kt, u32x4 (&r)[CH]) __attribute__((always_inline)) {
         kt = kt < nkt ? kt : nkt - 1;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int idx = tid + 256 * i, row = idx >> 4, c = idx & 15;
+        for (int i = 0; i < CH; ++i) {
+            const int idx = tid + NW * 64 * i, row = idx >> 4, c = idx & 15;
             int g = kt * AT_BN + row;
             g = g < S ? g : S - 1;
             r[i] = *(const u32x4 *)(K + (int64_t)g * AT_D + c * 8);
         }
     };
-    auto store_k = [&](uint16_t *lds, const u32x4 (&r)[4]) __attribute__((always_inline)) {
+    auto store_k = [&](uint16_t *lds, const u32x4 (&r)[CH]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int idx = tid + 256 * i, row = idx >> 4, c = idx & 15;
+        for (int i = 0; i < CH; ++i) {
+            const int idx = tid + NW * 64 * i, row = idx >> 4, c = idx & 15;
             *(u32x4 *)(lds + row * AT_D + swz(row, c) * 8) = r[i];
         }
     };
@@ -730,9 +744,9 @@ __global__ __launch_bounds__(256) void k_attn_bwd_dq_ds(AttnBwdArgs a)
         for (int b = 0; b < 2; ++b) {
             int kb = kt * 2 + b;
             kb = kb <= kbmax ? kb : kbmax;
-            const uint16_t *p = dsrow + (int64_t)kb * 1024;
-            r[2 * b] = *(const u32x4 *)p;
-            r[2 * b + 1] = *(const u32x4 *)(p + 512);
+            const uint16_t *p = dsrow + (int64_t)kb * 4096;
+            r[2 * b] = __builtin_nontemporal_load((const u32x4 *)p);
+            r[2 * b + 1] = __builtin_nontemporal_load((const u32x4 *)(p + 512));
         }
     };
 
@@ -750,7 +764,7 @@ __global__ __launch_bounds__(256) void k_attn_bwd_dq_ds(AttnBwdArgs a)
     // tiles held in registers (measured on MI355X: 1-3 K tiles and 1-3 dS
     // tiles within 2 %, more registers slower)
     constexpr int KD = 1, DD = 2;
-    u32x4 kr[KD][4], dr[DD][4];
+    u32x4 kr[KD][CH], dr[DD][4];
 #pragma unroll
     for (int j = 0; j < KD; ++j) load_k(j, kr[j]);
 #pragma unroll
@@ -765,7 +779,7 @@ __global__ __launch_bounds__(256) void k_attn_bwd_dq_ds(AttnBwdArgs a)
 #pragma unroll
         for (int j = 0; j + 1 < KD; ++j)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) kr[j][i] = kr[j + 1][i];
+            for (int i = 0; i < CH; ++i) kr[j][i] = kr[j + 1][i];
         load_k(kt + KD, kr[KD - 1]);
 #pragma unroll
         for (int j = 0; j + 1 < DD; ++j)

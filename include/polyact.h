@@ -242,10 +242,10 @@ pa_status poly_softcap_attn_fwd_exp2(const void *q, const void *k, const void *v
  * floats each for Delta and for -lse log2(e) (each region rounded up to 16
  * bytes); when H > Hkv, FP32 dK and dV partials of every query head (summed
  * per group by a final pass in a fixed order); and, while they fit the limit
- * of pa_attn_bwd_ds_limit, the BF16 dS of every 32 x 32 block (B H
- * ceil(S/32)^2 x 2 KiB), which the dK/dV kernel stores so that dQ is one
- * product over them instead of a second pass of S, dP and the transform
- * (the same dQ either way); contents on return unspecified.
+ * of pa_attn_bwd_ds_limit, the BF16 dS of every 32 x 32 block (B H x
+ * 4 ceil(S/128) x ceil(S/32) x 2 KiB), which the dK/dV kernel stores so
+ * that dQ is one product over them instead of a second pass of S, dP and
+ * the transform (the same dQ either way); contents on return unspecified.
  * Paper: Eq. 12 and section 5.2.2 (the differentiated D3 at the recomputed
  * scaled score), section 3.3 (differentiated-polynomial backward). */
 pa_status poly_softcap_attn_bwd(const void *q, const void *k, const void *v, const void *o,
@@ -462,9 +462,10 @@ pa_status poly_rope_program(pa_rope_program *out);
  * paper defines the gradients (Eq. 12, section 3.3), not their storage: the
  * workspace is this library's split of the backward into kernels (the row
  * terms Delta and -lse log2 e, FP32 dK / dV partials per query head when
- * Hkv < H, and the stored dS blocks while B H ceil(S/32)^2 x 2 KiB is within
- * pa_attn_bwd_ds_limit).  The size depends on the limit in force: size the
- * workspace under the limit the call will see. */
+ * Hkv < H, and the stored dS blocks while their B H x 4 ceil(S/128) x
+ * ceil(S/32) x 2 KiB is within pa_attn_bwd_ds_limit).  The size depends on
+ * the limit in force: size the workspace under the limit the call will
+ * see. */
 int64_t pa_attn_bwd_workspace_bytes(int32_t softcap, int32_t B, int32_t H, int32_t Hkv,
                                     int32_t S, int32_t D);
 

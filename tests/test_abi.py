@@ -187,8 +187,9 @@ def test_error_paths_attention(pa):
     assert L.native_sigmoid_attn_bwd(Q, K, V, DO, DQ, DK, DV, None, 1, 2, 2, 0, 128, 1, None) == 0
     wb = L.pa_attn_bwd_workspace_bytes
 
-    def ds(B, H, S):      # BF16 dS blocks of 32 x 32, the whole square
-        return B * H * ((S + 31) // 32) ** 2 * 2048
+    def ds(B, H, S):      # BF16 dS blocks of 32 x 32, the whole square, query blocks in fours
+        nqb = (S + 31) // 32
+        return B * H * ((nqb + 3) // 4 * 4) * nqb * 2048
     assert wb(0, 1, 8, 8, 4096, 128) == ds(1, 8, 4096)
     assert wb(1, 1, 8, 8, 4095, 128) == 4 * 2 * 8 * 4095 + ds(1, 8, 4095)   # Delta, -lse log2(e)
     assert wb(0, 1, 8, 2, 100, 128) == 4 * 2 * 8 * 100 * 128 + ds(1, 8, 100)

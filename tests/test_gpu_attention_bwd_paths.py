@@ -1,7 +1,7 @@
 """The attention backward's two forms give the same bits.
 
-With the dS blocks stored (the default while B H ceil(S/32)^2 x 2 KiB is
-within pa_attn_bwd_ds_limit) the dK/dV kernel writes the BF16 dS it forms
+With the dS blocks stored (the default while they fit
+pa_attn_bwd_ds_limit) the dK/dV kernel writes the BF16 dS it forms
 and dQ is a product over those blocks; with the limit at 0 a dQ kernel
 recomputes S, dP and the transform.  Both use the same products in the same
 order, so dQ, dK and dV must agree bit for bit, for every score transform,
