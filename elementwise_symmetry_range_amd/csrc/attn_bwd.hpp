@@ -750,11 +750,16 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bwd_dq_ds(AttnBwdArgs a)
         }
     };
 
-    // byte offset of the lane's transposed read in a block, key row 0:
-    // dword group (u / 2), stored lane (key + 32 (u % 2)), half g16 % 2
+    // In LDS a fragment (dword group f, 16 bytes of stored lane L) sits at
+    // 16-byte slot L ^ ((2 f + L / 32) << 2) of its 1 KiB (bits 2-3 of the
+    // slot swizzled, so that the 16 lanes of a transposed read hit 16
+    // different slots: without it four of them shared each bank).  The
+    // lane's read for key row 16 jj + 8 half + 4 h + r (r = i16 / 4) of
+    // stored lane key + 32 (u % 2) in group f = u / 2 (u = i16 % 4), half
+    // g16 % 2: slot bits 2-3 are (2 half + h) ^ u.
     const int u = i16 & 3;
-    const uint32_t tr0 = (uint32_t)((u >> 1) * 1024 + (32 * (u & 1)) * 16 + (g16 & 1) * 8) +
-                         (uint32_t)(h * 4 + (i16 >> 2)) * 16u;
+    const uint32_t trb = (uint32_t)((u >> 1) * 1024 + (32 * (u & 1) + (i16 >> 2)) * 16 + (g16 & 1) * 8);
+    const uint32_t tlo = trb + (uint32_t)((h ^ u) * 64), thi = trb + (uint32_t)(((h ^ u) ^ 2) * 64);
     uint16_t *dl = Dl[wave];
 
     f32x16 dq[4];
@@ -774,7 +779,9 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bwd_dq_ds(AttnBwdArgs a)
         uint16_t *Kb = buf ? Ks1 : Ks0;
         store_k(Kb, kr[0]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) *(u32x4 *)(dl + (i >> 1) * 1024 + (i & 1) * 512 + lane * 8) = dr[0][i];
+        for (int i = 0; i < 4; ++i)
+            *(u32x4 *)(dl + (i >> 1) * 1024 + (i & 1) * 512 + (lane ^ ((2 * (i & 1) + (lane >> 5)) << 2)) * 8) =
+                dr[0][i];
         __syncthreads();
 #pragma unroll
         for (int j = 0; j + 1 < KD; ++j)
@@ -796,8 +803,8 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bwd_dq_ds(AttnBwdArgs a)
             bf16x8 dsf[2];
 #pragma unroll
             for (int jj = 0; jj < 2; ++jj) {
-                const u32x2 lo = ds_read_tr16((const uint16_t *)(blk + tr0 + jj * 16 * 16));
-                const u32x2 hi = ds_read_tr16((const uint16_t *)(blk + tr0 + (jj * 16 + 8) * 16));
+                const u32x2 lo = ds_read_tr16((const uint16_t *)(blk + tlo + jj * 256));
+                const u32x2 hi = ds_read_tr16((const uint16_t *)(blk + thi + jj * 256));
                 dsf[jj] = bc<bf16x8>(u32x4{lo.x, lo.y, hi.x, hi.y});
             }
 #pragma unroll

@@ -75,20 +75,61 @@ SCORES = {"softcap": 16 * 8192 * 8193 // 2, "sigmoid": 32 * 4096 * 4097 // 2}
 def attn_parts(name):
     """(kind, mode, exp2 core or None) of an attention kernel's template
     instance: k_attn_fwd<MODE, EXP, SREF>, k_attn_bwd_dq<MODE, EXP>,
-    k_attn_bwd_dkdv<MODE, SPLIT, EXP>, k_attn_bwd_reduce."""
+    k_attn_bwd_dkdv<MODE, SPLIT, EXP>, k_attn_bwd_reduce; the stored-dS
+    passes k_attn_bwd_rows and k_attn_bwd_dq_ds<NW> carry no mode."""
     import re
-    m = re.search(r"k_attn_(fwd|bwd_dq|bwd_dkdv|bwd_reduce)(?:<([^>]*)>)?", name)
+    m = re.search(r"k_attn_(fwd|bwd_dq_ds|bwd_dq|bwd_dkdv|bwd_reduce|bwd_rows)(?:<([^>]*)>)?", name)
     if not m:
         return None
     kind = m.group(1)
     args = [a.strip() for a in (m.group(2) or "").split(",") if a.strip()]
     mode = args[0] if args else None
+    if kind in ("bwd_dq_ds", "bwd_rows"):
+        return kind, None, None
     core = {"fwd": 1, "bwd_dq": 1, "bwd_dkdv": 2}.get(kind)
     exp = args[core] if core is not None and len(args) > core else None
     return kind, mode, exp if exp in EXP_CORES else None
 
 
+def attn_trace_means(trace):
+    """{(short name, kind, mode, exp): [ns, ...]} from a kernel trace in
+    launch order.  The stored-dS passes take the mode and exp2 core of the
+    dK/dV kernel of their backward call: the row pass runs just before it,
+    the dQ pass just after it."""
+    rows = sorted(csv.DictReader(open(trace)), key=lambda r: int(r["Start_Timestamp"]))
+    out = collections.defaultdict(list)
+    pending, last = [], None
+    for r in rows:
+        name = r["Kernel_Name"]
+        ns = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        short_name = name.split("(")[0].replace("void ", "")
+        parts = attn_parts(name)
+        if parts is None:
+            if "swiglu" in name:
+                out[(short_name, "swiglu", None, None)].append(ns)
+            continue
+        kind, mode, exp = parts
+        if kind == "bwd_rows":
+            pending.append((short_name, ns))
+            continue
+        if kind == "bwd_dkdv":
+            last = (mode, exp)
+            for sn, v in pending:
+                out[(sn, "bwd_rows", mode, exp)].append(v)
+            pending = []
+        if kind == "bwd_dq_ds":
+            mode, exp = last if last else (None, None)
+        out[(short_name, kind, mode, exp)].append(ns)
+    return out
+
+
+# BF16 dS bytes the dQ pass over stored blocks reads per launch: 2 KiB per
+# causal 32 x 32 block
+DS_BYTES = {"softcap": 16 * (256 * 257 // 2) * 2048, "sigmoid": 32 * (128 * 129 // 2) * 2048}
+
+
 def components(path, command, out):
+    """Kernel table of the components run from its kernel trace CSV."""
     lines = ["# SwiGLU and attention components", "",
              "Kernel trace of `bench.py --components-only --component-set main` "
              "(alternating poly / comparator rounds; softcap attention 1 x 16 x 8192 x 128 "
@@ -97,33 +138,35 @@ def components(path, command, out):
              "", "```", command, "```", "",
              "| kernel | what | calls | mean us | MFMA TFLOP/s | % of 2.5 PF |",
              "|---|---|---|---|---|---|"]
-    import re
-    for r in sorted(csv.DictReader(open(path)), key=lambda r: r["Name"]):
-        name = r["Name"]
-        avg = float(r["AverageNs"])
-        what, tfl = "", ""
-        parts = attn_parts(name)
-        if parts:
-            kind, mode, exp = parts
+    ds_rates = []
+    means = attn_trace_means(path)
+    for (short_name, kind, mode, exp), v in sorted(means.items(), key=lambda kv: (kv[0][0], str(kv[0][2]), str(kv[0][3]))):
+        avg = sum(v) / len(v)
+        tfl = ""
+        if kind == "swiglu":
+            what = "SwiGLU " + ("poly" if "Poly" in short_name else "comparator")
+        else:
             what = ATTN_MODES.get(mode, "") if mode else "sum of dK/dV partials"
             if exp:
                 what += f", exp2 core {EXP_CORES[exp]}"
-            if kind != "bwd_reduce" and mode:
-                sc = SCORES["softcap" if mode in "014" else "sigmoid"]
-                prods = {"fwd": 2, "bwd_dq": 3, "bwd_dkdv": 4}[kind]
-                t = prods * 2 * 128 * sc / (avg * 1e-9) / 1e12
+            if kind not in ("bwd_reduce", "bwd_rows") and mode:
+                fam = "softcap" if mode in "014" else "sigmoid"
+                prods = {"fwd": 2, "bwd_dq": 3, "bwd_dkdv": 4, "bwd_dq_ds": 1}[kind]
+                t = prods * 2 * 128 * SCORES[fam] / (avg * 1e-9) / 1e12
                 tfl = f"{t:.0f} | {100 * t / 2500:.1f}"
+                if kind == "bwd_dq_ds":
+                    ds_rates.append(f"{what}: {DS_BYTES[fam] / avg:.0f} GB/s")
             what = f"{kind} {what}"
-        elif "swiglu" in name:
-            what = "SwiGLU " + ("poly" if "Poly" in name else "comparator")
-        else:
-            continue
-        short_name = name.split("(")[0].replace("void ", "")
-        lines.append(f"| `{short_name}` | {what} | {r['Calls']} | {avg / 1e3:.1f} | "
+        lines.append(f"| `{short_name}` | {what} | {len(v)} | {avg / 1e3:.1f} | "
                      f"{tfl if tfl else '- | -'} |")
     lines += ["", "MFMA FLOP per launch counts the products each kernel performs (forward: "
-              "S and PV; dq kernel: S, dP, dQ; dK/dV kernel: S, dP, dV, dK), 2 x 128 flop "
-              "per causal score each."]
+              "S and PV; dq kernel: S, dP, dQ; dK/dV kernel: S, dP, dV, dK; dq_ds, the dQ pass "
+              "over the stored dS blocks: dQ), 2 x 128 flop per causal score each. The "
+              "stored-dS passes (bwd_rows before the dK/dV kernel, bwd_dq_ds after it) are "
+              "listed under the dK/dV kernel's mode of the same backward call."]
+    if ds_rates:
+        lines += ["", "dS read by the dQ pass (2 KiB per causal 32 x 32 block; 1,077,936,128 bytes "
+                  "softcap, 541,065,216 sigmoid): " + "; ".join(ds_rates) + "."]
     with open(os.path.join(out, "attention_components.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -228,11 +271,7 @@ CLOCK_HZ = 2.4e9      # MI355X peak engine clock (MFMA-busy fractions assume it)
 SIMDS = 256 * 4
 
 
-def attn_label(name):
-    parts = attn_parts(name)
-    if not parts or parts[0] == "bwd_reduce":
-        return None
-    kind, mode, exp = parts
+def attn_label(kind, mode, exp):
     what = ATTN_MODES.get(mode, "")
     if exp:
         what += f", exp2 core {EXP_CORES[exp]}"
@@ -240,11 +279,29 @@ def attn_label(name):
 
 
 def attn_pass(path):
-    """{label: (summed counters over the label's dispatches, summed ns)} of one PMC pass"""
+    """{label: (summed counters over the label's dispatches, summed ns)} of one
+    PMC pass; the dQ pass over stored dS takes the mode of the dK/dV kernel
+    dispatched before it (the row pass is left out: no MFMA)"""
+    rows = list(csv.DictReader(open(path)))
+    kinds = {}
+    for r in rows:
+        parts = attn_parts(r["Kernel_Name"])
+        if parts and parts[0] not in ("bwd_reduce", "bwd_rows"):
+            kinds[int(r["Dispatch_Id"])] = parts
+    labels, last = {}, None
+    for d in sorted(kinds):
+        kind, mode, exp = kinds[d]
+        if kind == "bwd_dkdv":
+            last = (mode, exp)
+        if kind == "bwd_dq_ds":
+            if last is None:
+                continue
+            mode, exp = last
+        labels[d] = attn_label(kind, mode, exp)
     per = collections.defaultdict(lambda: collections.defaultdict(float))
     span = {}
-    for r in csv.DictReader(open(path)):
-        lab = attn_label(r["Kernel_Name"])
+    for r in rows:
+        lab = labels.get(int(r["Dispatch_Id"]))
         if not lab:
             continue
         per[lab][r["Counter_Name"]] += float(r["Counter_Value"])
