@@ -75,6 +75,24 @@ def test_softcap_forms_agree(pa, shape, variant):
         assert np.array_equal(a, b), f"{name}: {int(np.sum(a != b))} of {a.size} differ"
 
 
+@pytest.mark.parametrize("fmt", ["bf16", "f16"])
+def test_softcap_forms_agree_at_scale(pa, fmt):
+    """A longer causal run (1 x 16 x 4096, 2048 workgroups per kernel), where
+    waves drift far out of step: a missing wait or barrier shows up as bits
+    that differ between the forms or between repeats."""
+    B, H, S = 1, 16, 4096
+    note(f"softcap backward forms at scale {fmt}")
+    q, k, v = si.t_attn_inputs(B, H, S)
+    do = si.t_attn_grad(B, H, S)
+    o, lse = pa.poly_softcap_attn_fwd(q, k, v, 50.0, True, fmt=fmt, with_lse=True)
+    run = lambda: pa.poly_softcap_attn_bwd(q, k, v, o, do, lse, 50.0, True, fmt=fmt)  # noqa: E731
+    first = [bits(t) for t in run()]
+    stored, recomputed = both_forms(pa, run)
+    for name, a, b, c in zip(("dq", "dk", "dv"), first, stored, recomputed):
+        assert np.array_equal(a, b), f"{name}: repeat differs in {int(np.sum(a != b))} of {a.size}"
+        assert np.array_equal(b, c), f"{name}: {int(np.sum(b != c))} of {b.size} differ"
+
+
 @pytest.mark.parametrize("shape", [(1, 4, 2, 4096, True), (1, 2, 2, 4096, False)])
 @pytest.mark.parametrize("poly", [True, False])
 def test_sigmoid_forms_agree(pa, shape, poly):
