@@ -28,7 +28,8 @@ __all__ = [
     "poly_softcap_attn_fwd_exp2", "poly_softcap_attn_bwd", "native_softcap_attn_bwd",
     "poly_sigmoid_attn_fwd",
     "native_sigmoid_attn_fwd", "poly_sigmoid_attn_bwd", "native_sigmoid_attn_bwd",
-    "sigmoid_attn_program", "attn_bwd_workspace", "stream_copy", "FUNCS", "poly_rope",
+    "sigmoid_attn_program", "attn_bwd_workspace", "attn_bwd_ds_limit", "stream_copy", "FUNCS",
+    "poly_rope",
     "native_rope", "native_rope_table", "rope_table", "rope_program",
 ]
 
@@ -362,6 +363,14 @@ def native_softcap_attn_fwd(q, k, v, cap: float = 50.0, causal: bool = True, out
 
 def _grads(q, k, dq, dk, dv):
     return _like(dq, q, "dq"), _like(dk, k, "dk"), _like(dv, k, "dv")
+
+
+def attn_bwd_ds_limit(nbytes: int | None = None) -> int:
+    """The process-wide limit on the dS blocks an attention backward stores
+    (the library's pa_attn_bwd_ds_limit): with nbytes, set it and return the
+    previous value; without, return it.  0 makes every backward recompute
+    for dQ; size workspaces after a change."""
+    return int(lib().pa_attn_bwd_ds_limit(-1 if nbytes is None else int(nbytes)))
 
 
 def attn_bwd_workspace(softcap: bool, B, H, Hkv, S, D=128, device=None):

@@ -34,17 +34,16 @@ def bits(t):
 def both_forms(pa, run):
     """run() under the default limit, then with the limit at 0; the limit is
     restored whatever happens."""
-    L = pa.lib()
-    lim = L.pa_attn_bwd_ds_limit(-1)
+    lim = pa.attn_bwd_ds_limit()
     assert lim > 0
     stored = [bits(t) for t in run()]
     torch.cuda.synchronize()
-    L.pa_attn_bwd_ds_limit(0)
+    pa.attn_bwd_ds_limit(0)
     try:
         recomputed = [bits(t) for t in run()]
         torch.cuda.synchronize()
     finally:
-        L.pa_attn_bwd_ds_limit(lim)
+        pa.attn_bwd_ds_limit(lim)
     return stored, recomputed
 
 
