@@ -277,13 +277,16 @@ pa_status poly_softcap_attn_bwd_exp2(const void *q, const void *k, const void *v
  * cannot allocate device memory (code under graph capture, serving loops,
  * harnesses that forbid allocation).  The scratch lives in one device array
  * of pa_attn_bwd_static_scratch_bytes() bytes (8 MiB) inside the library,
- * held by each GPU the library runs on until the process ends; shapes whose
- * workspace (pa_attn_bwd_workspace_bytes(1, ...)) exceeds it return
+ * held by each GPU the library runs on until the process ends.  It runs the
+ * recompute form of the backward (no stored dS blocks), whose scratch is
+ * Delta and -lse log2(e) per query row and, with grouped heads, the FP32
+ * dK / dV partials; shapes whose scratch exceeds the array return
  * PA_ERR_SHAPE (for example B H S <= 1,048,576 query rows when H == Hkv, and
  * B H S <= 8,128 rows with grouped heads).  The call allocates nothing.  Every
  * call on a GPU shares that GPU's array: calls that overlap in time on one
  * GPU (other streams, other threads) race and must be serialised by the
- * caller.  Results equal poly_softcap_attn_bwd's. */
+ * caller.  Results equal poly_softcap_attn_bwd's (bit for bit: both forms
+ * give the same bits). */
 pa_status poly_softcap_attn_bwd_static(const void *q, const void *k, const void *v,
                                        const void *o, const void *dout, const float *lse,
                                        void *dq, void *dk, void *dv, int32_t B, int32_t H,
