@@ -668,12 +668,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // dQ from the dS blocks the dK/dV kernel stored: the dQ kernel's workgroups,
 // key tiles and products (dQ^T += K^T dS^T, the same operands in the same
 // order, so the same dQ) with dS^T read from LDS instead of recomputed.
-// The kernel streams 2 KiB of dS per 32 x 32 block, so it is bound by how
-// many bytes it keeps in flight: both operands come through registers (K
-// loaded one tile ahead, dS two tiles ahead) and are written to LDS at the
-// start of their tile, one barrier per tile, 48 KiB of LDS per workgroup.
-// (Loading both with global-to-LDS loads into double buffers measured the
-// same.)  The workgroup's dS of a tile is 16 KiB in one piece (ds_block).
+// The kernel streams 2 KiB of dS per 32 x 32 block (nontemporal, so the
+// stream does not push K out of L2) and is bound by that stream, about
+// 5 TB/s on MI355X.  Both operands come through registers (K loaded one
+// tile ahead, dS two tiles ahead) and are written to LDS at the start of
+// their tile, one barrier per tile, 48 KiB of LDS per workgroup: K double
+// buffered (all waves read it), the dS blocks single buffered per wave (a
+// wave reads only the blocks it wrote, in program order).  (Loading both
+// with global-to-LDS loads into double buffers measured the same.)  The
+// workgroup's dS of a tile is 16 KiB in one piece (ds_block).
 // A wave's two 32 x 32 blocks of a 64-key tile are stored as the
 // dK/dV kernel's fragments: 1 KiB per dword group f, 16 bytes per lane,
 // lane (key c, half h') holding queries 8 f + 4 h' + i and 16 further on.
