@@ -534,6 +534,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             dw4[f][w] = dk2;
         };
 
+        // this wave's 32 x 32 dS block for dQ: block (r0 / 32, k0 / 32) of
+        // the head, at ds_block; 2 KiB: dw4[0] of lanes 0..63, then dw4[1]
+        // (16 bytes per lane, so each store fills 1 KiB)
+        uint16_t *dsp = nullptr;
+        if (a.dsb) dsp = a.dsb + ds_block(head_of(t), r0 / 32, k0 / 32, a.nqb) * 1024 + lane * 8;
+
         // dV^T += dO^T P,  dK^T += Q^T dS over the half's two contraction
         // steps f, in slots (d block db) with the operands read one slot
         // ahead.  A transposed read covers rows 8 f + .. of the half and the
@@ -541,11 +547,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         // db is the chunk offset XOR (db << 6) and step f adds 8 rows, i.e.
         // XOR (1 << 5) and + 2048 bytes.  The transform of fragment 1 runs
         // one pair per slot beside the MFMAs of fragment 0.
-        // this wave's 32 x 32 dS block for dQ: block (r0 / 32, k0 / 32) of
-        // the head, at ds_block; 2 KiB: dw4[0] of lanes 0..63, then dw4[1]
-        // (16 bytes per lane, so each store fills 1 KiB)
-        uint16_t *dsp = nullptr;
-        if (a.dsb) dsp = a.dsb + ds_block(head_of(t), r0 / 32, k0 / 32, a.nqb) * 1024 + lane * 8;
         bf16x8 oa[AH + 1], qa[AH + 1];
         auto ld = [&](auto nc) __attribute__((always_inline)) {
             constexpr int n = decltype(nc)::value, f = n >> 2, db = n & 3, b = n % (AH + 1);
