@@ -19,9 +19,13 @@
 // one packed FMA: y0 = RN16(x0 c - RN16(x1 s)), y1 = RN16(x1 c + RN16(x0 s)).
 // Layouts: Q [B, S, Hq, D] and K [B, S, Hkv, D] in, Q [B, Hq, S, D] and
 // K [B, Hkv, S, D] out (FP16).  A thread takes one position, 8 consecutive
-// head dimensions and a group of 4 heads (queries, then keys); consecutive
-// threads take consecutive 16-byte chunks of a row, so every head's loads
-// and stores are runs of whole rows.
+// head dimensions and a group of 8 heads (queries, then keys); consecutive
+// threads take the 16-byte chunks of a row, then consecutive positions of
+// the same head group, so a workgroup (16 positions at D = 128) reads runs
+// of 8 whole head rows per position and writes 4 KiB runs of each output
+// head.  Measured on MI355X at 1 x 4096 x 32 (8) x 128: 13.7 us, the rate of
+// a plain copy of the same bytes, against 15.3 us with the positions outer
+// (each output head written in 256-byte runs) and 4 heads per thread.
 #pragma once
 #include <cmath>
 
@@ -77,7 +81,7 @@ __device__ __forceinline__ uint32_t rope_rot(uint32_t xw, _Float16 sn, _Float16 
     return bc<uint32_t>(y);
 }
 
-constexpr int RP_HPG = 4;   // heads per thread (of the Hq query then Hkv key heads)
+constexpr int RP_HPG = 8;   // heads per thread (of the Hq query then Hkv key heads)
 
 template <int VAR>
 __global__ __launch_bounds__(256) void k_rope(RopeArgs a)
@@ -85,13 +89,14 @@ __global__ __launch_bounds__(256) void k_rope(RopeArgs a)
     const int ch = a.D >> 3;                                   // 16-byte chunks per row
     const int ng = (a.Hq + a.Hkv + RP_HPG - 1) / RP_HPG;       // head groups
     const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t rg = gid / ch;                               // (b S + s) ng + g
-    const int64_t row = rg / ng;                               // b S + s
-    if (row >= a.rows) return;
-    const int c = (int)(gid - rg * ch);
-    const int g = (int)(rg - row * ng);
-    const int64_t b = row / a.S;
-    const int s = (int)(row - b * a.S);
+    const int64_t ps = gid / ch;                               // (b ng + g) S + s
+    const int64_t bg = ps / a.S;
+    const int64_t b = bg / ng;
+    if (b * a.S >= a.rows) return;
+    const int c = (int)(gid - ps * ch);
+    const int s = (int)(ps - bg * a.S);
+    const int g = (int)(bg - b * ng);
+    const int64_t row = b * a.S + s;
 
     // (cos, sin) of frequencies 4c .. 4c + 3 as FP16 pairs: lane l of word j
     // is frequency 4c + 2j + l
