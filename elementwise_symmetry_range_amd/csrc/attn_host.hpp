@@ -50,9 +50,10 @@ inline bool aligned16(std::initializer_list<const void *> ps)
 // Shape rules shared by every attention entry point.
 inline pa_status attn_shape(int32_t B, int32_t H, int32_t Hkv, int32_t S, int32_t D)
 {
-    if (B < 0 || H < 0 || Hkv < 0 || S < 0 || D != AT_D) return PA_ERR_SHAPE;
+    // S + 255 must fit int32 (the kernels' tile counts)
+    if (B < 0 || H < 0 || Hkv < 0 || S < 0 || S > 0x7FFFFFFF - 256 || D != AT_D) return PA_ERR_SHAPE;
     if ((int64_t)B * H > 0 && (Hkv == 0 || H % Hkv != 0)) return PA_ERR_SHAPE;
-    const int64_t tiles = (int64_t)(S + AT_BM - 1) / AT_BM;
+    const int64_t tiles = ((int64_t)S + AT_BM - 1) / AT_BM;
     if ((int64_t)B * H * tiles > 0x7FFFFFFF) return PA_ERR_SHAPE;
     return PA_OK;
 }
@@ -177,7 +178,7 @@ inline void attn_fwd_launch(const AttnArgs &a, dim3 grid, hipStream_t stream)
 // softcap program only).
 inline pa_status attn_fwd(int mode, const void *q, const void *k, const void *v, void *o, float *lse,
                           int32_t B, int32_t H, int32_t Hkv, int32_t S, int32_t D, float cap,
-                          int32_t causal, hipStream_t stream, int exp2_core = 0, bool allow_ds = true)
+                          int32_t causal, hipStream_t stream, int exp2_core = 0)
 {
     if (exp2_core < 0 || exp2_core > 4 || (exp2_core && mode != AM_SOFTCAP_POLY_BF16)) return PA_ERR_FUNC;
     if (!q || !k || !v || !o) return PA_ERR_NULL;
@@ -253,6 +254,8 @@ inline pa_status attn_fwd(int mode, const void *q, const void *k, const void *v,
 inline int64_t attn_bwd_ds_bytes(int32_t B, int32_t H, int32_t S)
 {
     const int64_t nqb = ((int64_t)S + 31) / 32;
+    const double est = (double)B * H * (double)((nqb + 3) / 4 * 4) * (double)nqb * 2048.0;
+    if (est > 4.0e18) return INT64_MAX;   // beyond any limit (and int64)
     return (int64_t)B * H * ((nqb + 3) / 4 * 4) * nqb * 2048;
 }
 
@@ -268,7 +271,8 @@ inline std::atomic<int64_t> &attn_ds_limit()
 }
 inline bool attn_bwd_use_ds(int32_t B, int32_t H, int32_t S)
 {
-    return attn_bwd_ds_bytes(B, H, S) <= attn_ds_limit().load(std::memory_order_relaxed);
+    const int64_t b = attn_bwd_ds_bytes(B, H, S);
+    return b != INT64_MAX && b <= attn_ds_limit().load(std::memory_order_relaxed);
 }
 
 // Workspace of a backward call, in floats: Delta and -lse log2(e) per query

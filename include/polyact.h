@@ -174,7 +174,8 @@ pa_status poly_swiglu_bwd(int32_t t, const void *gate, const void *up, const voi
  * Layout: q, o, dout, dq: [B, H, S, D]; k, v, dk, dv: [B, Hkv, S, D], all
  * contiguous BF16 and 16-byte aligned; H must be a multiple of Hkv (query head
  * h uses key/value head h / (H / Hkv): grouped-query attention; Hkv = H is
- * plain multi-head attention).  D must be 128; any S >= 0; causal != 0 masks
+ * plain multi-head attention).  D must be 128; 0 <= S <= 2^31 - 257 (the
+ * kernels' tile counts stay in int32); causal != 0 masks
  * key j from query i when j > i.  lse and workspace: [B, H, S] FP32, 4-byte
  * aligned.  No output may overlap another output or an input
  * (PA_ERR_OVERLAP).  B * H * ceil(S / 128) must fit in int32. */

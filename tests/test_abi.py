@@ -209,6 +209,14 @@ def test_error_paths_attention(pa):
     finally:
         assert L.pa_attn_bwd_ds_limit(lim) == 0
     assert L.pa_attn_bwd_ds_limit(-5) == lim
+    # no overflow at the largest shapes, whatever the limit
+    big = (1 << 31) - 257           # the largest S the attention entry points take
+    assert wb(1, 1, 1, 1, big + 1, 128) == -1
+    try:
+        L.pa_attn_bwd_ds_limit((1 << 63) - 1)
+        assert wb(1, 1, 1, 1, big, 128) == 4 * 2 * ((big + 3) // 4 * 4)
+    finally:
+        L.pa_attn_bwd_ds_limit(lim)
 
 
 def test_rope_program_matches_oracle(pa, orc):
