@@ -148,6 +148,37 @@ def test_softcap_full_size_sampled(pa, orc, tp):
                 f"softcap bwd full fmt={fmt}", cap=50.0, tanh_prog=tp, **kw)
 
 
+def test_softcap_b2_geometry_sampled(pa, orc, tp):
+    """The pages' B2 geometry, 1 x 32 query heads on 8 key/value heads x
+    4096 x 128, causal, BF16 program: the grouped dK/dV kernel with FP32
+    partials and their sum, and the dQ pass over stored dS blocks.  Query
+    heads 1 and 13 get the oracle's O and lse (the others lse = 1e4, P = 0,
+    in the kernel and the oracle alike); sampled query rows of both and key
+    rows of their key/value heads 0 and 3."""
+    B, H, Hkv, S = 1, 32, 8, 4096
+    heads = (1, 13)
+    note("softcap bwd B2 geometry draw")
+    qt, kt, vt = si.t_attn_inputs(B, H, S, Hkv=Hkv)
+    dot = si.t_attn_grad(B, H, S)
+    q, k, v, do = to_bits(qt), to_bits(kt), to_bits(vt), to_bits(dot)
+    rng = np.random.default_rng(65)
+    qrows = np.unique(np.concatenate([[h * S, h * S + S - 1] for h in heads] + [heads[1] * S + rng.integers(0, S, 24)]))
+    krows = np.unique(np.concatenate([[g * S, g * S + S - 1] for g in (0, 3)] + [3 * S + rng.integers(0, S, 24)]))
+    call, kind, kw = softcap_variant(pa, orc, "bf16")
+    o = np.zeros((B, H, S, 128), np.uint16)
+    lse = np.full((B, H, S), 1e4, np.float32)
+    for h in heads:
+        note(f"softcap bwd B2 geometry: oracle forward of head {h}")
+        g = h // (H // Hkv)
+        o[:, h:h + 1], lse[:, h:h + 1] = fwd_for_bwd(orc, kind, q[:, h:h + 1], k[:, g:g + 1], v[:, g:g + 1],
+                                                     True, tanh_prog=tp, **kw)
+    note("softcap bwd B2 geometry: kernel")
+    dq, dk, dv = call(qt, kt, vt, to_dev(o, BF), dot, torch.from_numpy(lse).cuda(), 50.0, True)
+    dq, dk, dv = to_bits(dq), to_bits(dk), to_bits(dv)
+    compare(orc, kind, q, k, v, o, do, lse, dq, dk, dv, qrows, krows, True, "softcap bwd B2 geometry",
+            cap=50.0, tanh_prog=tp, **kw)
+
+
 def sigmoid_case(pa, orc, sp, B, H, Hkv, S, causal, poly, seed, qrows=None, krows=None):
     q, k, v, do = draw(B, H, Hkv, S, seed)
     kind = orc.ATTN_SIGMOID_POLY if poly else orc.ATTN_SIGMOID_EXACT
