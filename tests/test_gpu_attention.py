@@ -145,6 +145,27 @@ def test_softcap_full_size_sampled(pa, orc, tp):
         check_lse(lse[rows], ref_lse, f"full fmt={fmt}")
 
 
+def test_softcap_b2_geometry_sampled(pa, orc, tp):
+    """The pages' B2 geometry: 1 x 32 query heads on 8 key/value heads x
+    4096 x 128, causal, alpha = 50, BF16 program and comparator; 40 sampled
+    rows (every key/value group's first and last rows, random)."""
+    B, H, Hkv, S = 1, 32, 8, 4096
+    note("softcap B2 geometry draw")
+    qt, kt, vt = si.t_attn_inputs(B, H, S, Hkv=Hkv)
+    rng = np.random.default_rng(33)
+    rows = np.unique(np.concatenate([np.arange(0, H, 4) * S, np.arange(3, H, 4) * S + S - 1,
+                                     rng.integers(0, B * H * S, 24)]))
+    q, k, v = to_bits(qt), to_bits(kt), to_bits(vt)
+    for fmt in ("bf16", "native"):
+        note(f"softcap B2 geometry fmt={fmt}")
+        call, kind, kw = softcap_entry(pa, fmt)
+        o, lse = call(qt, kt, vt, 50.0, True)
+        o, lse = to_bits(o).reshape(-1, 128), lse.cpu().numpy().ravel()
+        ref, ref_lse, spread = orc.attn_fwd_rows(kind, q, k, v, rows, tanh_prog=tp, **kw)
+        check(o[rows], ref, spread, f"B2 geometry fmt={fmt}")
+        check_lse(lse[rows], ref_lse, f"B2 geometry fmt={fmt}")
+
+
 def sigmoid_case(pa, orc, sp, q, k, v, causal, poly, rows=None, label=""):
     B, H, S, D = q.shape
     note(f"sigmoid fwd {label} B={B} H={H} Hkv={k.shape[1]} S={S} causal={causal} poly={poly}")
