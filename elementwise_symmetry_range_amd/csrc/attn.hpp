@@ -707,9 +707,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 mfma_op(std::integral_constant<int, t * MPS + decltype(ic)::value>{});
             });
             constexpr int p0 = t * NPC / AT_SLOTS, p1 = (t + 1) * NPC / AT_SLOTS;
+            // FP16 softcap: the slot's transform piece at raised wave
+            // priority, so the SIMD's other wave yields to it (measured on
+            // MI355X: 1.025x; the BF16 program, sigmoid, the comparator and
+            // the exp2 cores are slower with it, and so is raising it for
+            // the MFMAs instead)
+            if constexpr (MODE == AM_SOFTCAP_POLY) __builtin_amdgcn_s_setprio(1);
             static_for<p1 - p0>([&](auto ic) __attribute__((always_inline)) {
                 piece(std::integral_constant<int, p0 + decltype(ic)::value>{}, scur, st, ukey0, std::false_type{});
             });
+            if constexpr (MODE == AM_SOFTCAP_POLY) __builtin_amdgcn_s_setprio(0);
             __builtin_amdgcn_sched_barrier(0);
         });
         finish(st, pc);
